@@ -1,0 +1,36 @@
+"""LoRA linear: y = x W^T + s (x A^T) B^T with a frozen W and trainable A [r x in], B [out x r].
+
+The pages train low-rank adapters on a frozen base ("Exact Layer Streaming ...",
+abstract; "Soup CLI ...", "How Layer Streaming Works": the base stays frozen).
+The adapter form y = x W^T + (alpha/r) x A^T B^T is the standard LoRA
+parametrisation (Hu et al. 2021, section 4.1); no dropout (reading).
+
+bf16 mode rounds t = x A^T, u = dy B and the outputs y, dx once each; the
+adapter gradients are float outputs (no rounding). W has no gradient.
+"""
+import numpy as np
+
+from .bf16 import round_bf16
+
+
+def lora_linear_fwd(x, w, a, b, scale, rnd=round_bf16):
+    """Returns (y, t). x [T x in], w [out x in], a [r x in], b [out x r]."""
+    t = rnd(x @ a.T)
+    y = rnd(x @ w.T + scale * (t @ b.T))
+    return y, t
+
+
+def lora_linear_bwd(x, t, dy, w, a, b, scale, rnd=round_bf16, round_dx=True):
+    """Returns (dx, dA, dB, u) for the loss gradient dy [T x out].
+
+    dx = dy W + s (dy B) A;  dA = s (dy B)^T x;  dB = s dy^T t.
+    With round_dx=False dx is returned unrounded so callers can sum several
+    projections that read the same input before rounding once.
+    """
+    u = rnd(dy @ b)
+    dx = dy @ w + scale * (u @ a)
+    if round_dx:
+        dx = rnd(dx)
+    da = scale * (u.T @ x)
+    db = scale * (dy.T @ t)
+    return dx, da, db, u

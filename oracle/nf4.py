@@ -1,0 +1,81 @@
+"""NF4: 4-bit NormalFloat with blockwise absmax scaling (block 64, float32 absmax).
+
+The pages name NF4 as the format of the frozen 8B base ("Exact Layer
+Streaming ...", abstract; "Soup CLI ...", "Key Takeaways"). Its definition is
+QLoRA's NormalFloat (Dettmers et al. 2023, section 3): the code values are
+quantiles of the standard normal distribution, split so that zero is exactly
+representable, scaled to [-1, 1].
+
+Readings taken here (the pages are silent on all of them):
+  * offset delta = ((1 - 1/30) + (1 - 1/32)) / 2 = 929/960, evaluated in float64;
+  * 8 positive values: Phi^-1 at 8 evenly spaced probabilities from delta down
+    to (but excluding) 1/2 (9-point grid, last point dropped); 7 negative values:
+    the same with an 8-point grid, negated; plus an exact 0; every value is
+    divided by the largest (Phi^-1(delta)) in float64 and rounded once to float32;
+  * quantisation: w is the bf16 weight read as float32; absmax per block of 64
+    consecutive row-major elements; n = w / absmax (float32, IEEE division;
+    n = 0 when absmax = 0); code = number of float32 midpoints
+    m_i = (c_i + c_{i+1}) / 2 with n > m_i (nearest code, ties to the lower index);
+  * packing: element 2j in the high nibble of byte j, element 2j+1 in the low nibble;
+  * dequantisation: w' = bf16(float32(c[code]) * absmax), one float32 multiply.
+"""
+from statistics import NormalDist
+
+import numpy as np
+
+from .bf16 import round_bf16
+
+BLOCK = 64
+
+
+def nf4_codebook() -> np.ndarray:
+    """The 16 NF4 code values, ascending, float32."""
+    delta = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0))
+    nd = NormalDist()
+    pos = [nd.inv_cdf(p) for p in np.linspace(delta, 0.5, 9)[:-1]]
+    neg = [-nd.inv_cdf(p) for p in np.linspace(delta, 0.5, 8)[:-1]]
+    vals = sorted(pos + neg + [0.0])
+    top = max(vals)
+    return np.array([v / top for v in vals], dtype=np.float64).astype(np.float32)
+
+
+def _midpoints(cb: np.ndarray) -> np.ndarray:
+    cb = cb.astype(np.float32)
+    return ((cb[:-1] + cb[1:]) * np.float32(0.5)).astype(np.float32)
+
+
+def nf4_quantize(w: np.ndarray):
+    """Quantise w [rows x cols] (cols % 64 == 0) -> (codes uint8 [rows x cols/2], absmax float32 [rows x cols/64])."""
+    w = np.asarray(w)
+    rows, cols = w.shape
+    if cols % BLOCK:
+        raise ValueError("in-features must be a multiple of 64")
+    f = w.astype(np.float32).reshape(-1, BLOCK)
+    absmax = np.max(np.abs(f), axis=1).astype(np.float32)
+    safe = np.where(absmax > 0, absmax, np.float32(1.0)).astype(np.float32)
+    n = (f / safe[:, None]).astype(np.float32)
+    n[absmax == 0] = np.float32(0.0)
+    mids = _midpoints(nf4_codebook())
+    code = np.sum(n[..., None] > mids[None, None, :], axis=-1).astype(np.uint8)
+    code = code.reshape(rows, cols)
+    packed = ((code[:, 0::2] << 4) | code[:, 1::2]).astype(np.uint8)
+    return packed, absmax.reshape(rows, cols // BLOCK)
+
+
+def nf4_unpack(packed: np.ndarray) -> np.ndarray:
+    """Codes uint8 [rows x cols] from packed bytes [rows x cols/2]."""
+    rows, half = packed.shape
+    code = np.empty((rows, 2 * half), np.uint8)
+    code[:, 0::2] = packed >> 4
+    code[:, 1::2] = packed & 0xF
+    return code
+
+
+def nf4_dequant(packed: np.ndarray, absmax: np.ndarray, rnd=round_bf16) -> np.ndarray:
+    """w' = rnd(float32(c[code]) * absmax) as float64 [rows x cols]."""
+    code = nf4_unpack(packed)
+    rows, cols = code.shape
+    cb = nf4_codebook()
+    c = cb[code].reshape(-1, BLOCK)
+    prod = (c * absmax.reshape(-1)[:, None].astype(np.float32)).astype(np.float32)
+    return rnd(prod.astype(np.float64)).reshape(rows, cols)

@@ -1,0 +1,455 @@
+"""Pins of the CPU oracle to things other than itself: library routines (torch
+CPU float64 ops, scipy), closed forms, brute force on tiny inputs, invariants
+and central finite differences. A plausible slip in the oracle (a dropped term,
+a wrong sign, a transposed operand, a wrong head mapping) fails one of these."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+from oracle.bf16 import round_bf16, identity, bf16_bits, from_bf16_bits
+from oracle.nf4 import nf4_codebook, nf4_quantize, nf4_dequant, nf4_unpack
+from synth.configs import TINY_LAYER, PROJ_IN_OUT
+
+RNG = np.random.default_rng(1234)
+
+
+def t64(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+
+
+# ------------------------------------------------------------------ bf16
+def test_bf16_matches_torch_conversion():
+    x = np.concatenate([RNG.standard_normal(20000) * 10.0 ** RNG.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1.0, -1.0, 3.0e38, -3.0e38, 1e-40, -1e-40]])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = bf16_bits(x32.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_ties_to_even():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to the even mantissa (1.0)
+    assert round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: ties to 1 + 2^-6 (even)
+    assert round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert round_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -20]))[0] == 1.0 + 2.0 ** -7
+    assert np.isnan(round_bf16(np.array([np.nan]))[0])
+    assert np.array_equal(from_bf16_bits(np.array([0x3F80, 0xC000], np.uint16)), [1.0, -2.0])
+
+
+# ------------------------------------------------------------------ NF4
+def test_nf4_codebook_invariants():
+    cb = nf4_codebook()
+    assert cb.dtype == np.float32 and cb.shape == (16,)
+    assert np.all(np.diff(cb) > 0)
+    assert cb[0] == -1.0 and cb[7] == 0.0 and cb[15] == 1.0
+    assert np.sum(cb < 0) == 7 and np.sum(cb > 0) == 8
+
+
+def test_nf4_codebook_is_normal_quantiles():
+    """Each code value times Phi^-1(delta) maps back (through scipy's normal CDF)
+    onto the evenly spaced probability grid of the NormalFloat construction."""
+    from scipy.stats import norm
+    cb = nf4_codebook().astype(np.float64)
+    delta = 0.5 * ((1 - 1 / 30) + (1 - 1 / 32))
+    top = norm.ppf(delta)
+    pos_p = norm.cdf(cb[8:] * top)          # ascending
+    neg_p = norm.cdf(-cb[:7] * top)         # for negated values, ascending after reversal
+    assert np.allclose(np.sort(pos_p), np.linspace(delta, 0.5, 9)[:-1][::-1], atol=2e-7)
+    assert np.allclose(np.sort(neg_p), np.linspace(delta, 0.5, 8)[:-1][::-1], atol=2e-7)
+    # scipy's ppf gives the same float32 table
+    v = sorted(list(norm.ppf(np.linspace(delta, 0.5, 9)[:-1])) +
+               list(-norm.ppf(np.linspace(delta, 0.5, 8)[:-1])) + [0.0])
+    assert np.array_equal((np.array(v) / max(v)).astype(np.float32), nf4_codebook())
+
+
+def _brute_codes(w):
+    cb = nf4_codebook()
+    f = w.astype(np.float32).reshape(-1, 64)
+    out = np.empty(f.shape, np.uint8)
+    am = np.abs(f).max(axis=1)
+    for b in range(f.shape[0]):
+        for i in range(64):
+            n = np.float32(0.0) if am[b] == 0 else np.float32(f[b, i] / am[b])
+            d = [abs(float(n) - float(c)) for c in cb]
+            best = min(d)
+            # nearest; on an exact tie the lower index
+            out[b, i] = [j for j in range(16) if d[j] == best][0]
+    return out.reshape(w.shape), am
+
+
+def test_nf4_quantize_brute_force():
+    w = round_bf16(RNG.standard_normal((4, 128)) * 0.02)
+    w[1, :64] = 0.0                      # all-zero block
+    w[2, 64:] = 0.0
+    w[2, 70] = -0.5                      # single non-zero (negative) element
+    packed, absmax = nf4_quantize(w)
+    codes = nf4_unpack(packed)
+    bc, bam = _brute_codes(w)
+    assert np.array_equal(absmax.reshape(-1), bam)
+    # exact ties (n equal to a float32 midpoint) are the only place nearest can differ
+    assert np.array_equal(codes, bc)
+    assert np.all(codes[1, :64] == 7)
+    assert codes[2, 70] == 0 and np.all(codes[2, 64:70] == 7)
+
+
+def test_nf4_midpoint_ties_go_low():
+    cb = nf4_codebook()
+    mids = ((cb[:-1] + cb[1:]) * np.float32(0.5)).astype(np.float32)
+    # a block whose absmax is 1 makes n == w exactly
+    for i in (0, 6, 7, 12):
+        blk = np.zeros(64)
+        blk[0] = 1.0
+        blk[1] = float(mids[i])
+        if round_bf16(np.array([blk[1]]))[0] != blk[1]:
+            continue                     # only bf16-representable midpoints can occur
+        c = nf4_unpack(nf4_quantize(blk[None, :])[0])[0]
+        assert c[1] == i
+
+
+def test_nf4_pack_order_and_roundtrip():
+    blk = np.zeros((1, 64))
+    blk[0, 0], blk[0, 1] = 1.0, -1.0
+    packed, absmax = nf4_quantize(blk)
+    assert packed[0, 0] == 0xF0 and packed[0, 1] == 0x77 and absmax[0, 0] == 1.0
+    w = round_bf16(RNG.standard_normal((8, 256)) * 0.05)
+    packed, absmax = nf4_quantize(w)
+    deq32 = nf4_dequant(packed, absmax, rnd=identity)
+    ratio = deq32.reshape(-1, 64) / absmax.reshape(-1, 1).astype(np.float64)
+    cb = nf4_codebook().astype(np.float64)
+    # dequant(quant(w)) / absmax is a code value (exact float32 product, no rounding)
+    assert np.all(np.isin(np.round(ratio, 6), np.round(cb, 6)))
+    # the element holding absmax comes back exactly
+    deq = nf4_dequant(packed, absmax)
+    fb = np.abs(w.reshape(-1, 64))
+    am_idx = fb.argmax(axis=1)
+    got = np.abs(deq.reshape(-1, 64)[np.arange(fb.shape[0]), am_idx])
+    assert np.array_equal(got, fb.max(axis=1))
+    # quant o dequant o quant == quant
+    p2, a2 = nf4_quantize(deq)
+    assert np.array_equal(p2, packed) and np.array_equal(a2, absmax)
+
+
+def test_nf4_dequant_single_fp32_multiply():
+    w = round_bf16(RNG.standard_normal((2, 64)) * 0.02)
+    packed, absmax = nf4_quantize(w)
+    codes = nf4_unpack(packed)
+    cb = nf4_codebook()
+    exp = (torch.from_numpy(cb[codes]) * torch.from_numpy(absmax.repeat(64, axis=1))).to(torch.bfloat16)
+    assert np.array_equal(nf4_dequant(packed, absmax), exp.double().numpy())
+
+
+# ------------------------------------------------------------------ finite differences
+def fd_grad(f, x, idx_list, eps=1e-6):
+    out = []
+    for idx in idx_list:
+        xp = x.copy(); xp[idx] += eps
+        xm = x.copy(); xm[idx] -= eps
+        out.append((f(xp) - f(xm)) / (2 * eps))
+    return np.array(out)
+
+
+def sample_idx(shape, n, rng):
+    return [tuple(int(rng.integers(0, s)) for s in shape) for _ in range(n)]
+
+
+def assert_fd(analytic, f, x, n=12, rtol=1e-6, atol=1e-9):
+    rng = np.random.default_rng(7)
+    idx = sample_idx(x.shape, n, rng)
+    num = fd_grad(f, x, idx)
+    ana = np.array([analytic[i] for i in idx])
+    # central differences carry roundoff of about 1e-16 * |f| / eps
+    atol = atol + 1e-7 * max(1.0, float(np.max(np.abs(num))))
+    assert np.allclose(ana, num, rtol=rtol, atol=atol), (ana, num)
+
+
+# ------------------------------------------------------------------ LoRA linear
+def _lora_inputs(T=6, fin=64, fout=32, r=4):
+    x = RNG.standard_normal((T, fin))
+    w = RNG.standard_normal((fout, fin)) * 0.1
+    a = RNG.uniform(-0.2, 0.2, (r, fin))
+    b = RNG.standard_normal((fout, r)) * 0.1
+    return x, w, a, b
+
+
+def test_lora_zero_b_is_plain_linear():
+    x, w, a, _ = _lora_inputs()
+    xb, wb, ab = round_bf16(x), round_bf16(w), round_bf16(a)
+    y, _ = O.lora_linear_fwd(xb, wb, ab, np.zeros((32, 4)), 2.0)
+    ref = F.linear(t64(xb), t64(wb)).to(torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(y, ref)
+
+
+def test_lora_merged_weight_identity():
+    x, w, a, b = _lora_inputs()
+    y, _ = O.lora_linear_fwd(x, w, a, b, 2.0, rnd=identity)
+    ref = F.linear(t64(x), t64(w) + 2.0 * (t64(b) @ t64(a))).numpy()
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_lora_bwd_finite_differences():
+    x, w, a, b = _lora_inputs()
+    dy = RNG.standard_normal((6, 32))
+    s = 2.0
+    y, t = O.lora_linear_fwd(x, w, a, b, s, rnd=identity)
+    dx, da, db, _ = O.lora_linear_bwd(x, t, dy, w, a, b, s, rnd=identity)
+    L = lambda **kw: float(np.sum(dy * O.lora_linear_fwd(kw.get("x", x), w, kw.get("a", a), kw.get("b", b), s, rnd=identity)[0]))
+    assert_fd(dx, lambda v: L(x=v), x)
+    assert_fd(da, lambda v: L(a=v), a)
+    assert_fd(db, lambda v: L(b=v), b)
+
+
+# ------------------------------------------------------------------ RMSNorm
+def test_rmsnorm_matches_torch():
+    x = RNG.standard_normal((5, 48))
+    w = 1 + RNG.uniform(-0.1, 0.1, 48)
+    y = O.rmsnorm_fwd(x, w, 1e-5, rnd=identity)
+    ref = F.rms_norm(t64(x), (48,), t64(w), eps=1e-5).numpy()
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rmsnorm_bwd_fd_and_invariance():
+    x = RNG.standard_normal((3, 16))
+    w = 1 + RNG.uniform(-0.1, 0.1, 16)
+    dy = RNG.standard_normal((3, 16))
+    dx = O.rmsnorm_bwd(x, w, 1e-5, dy)
+    assert_fd(dx, lambda v: float(np.sum(dy * O.rmsnorm_fwd(v, w, 1e-5, rnd=identity))), x)
+    y1 = O.rmsnorm_fwd(x, w, 0.0, rnd=identity)
+    y2 = O.rmsnorm_fwd(3.7 * x, w, 0.0, rnd=identity)
+    assert np.allclose(y1, y2, rtol=1e-13)
+    c = O.rmsnorm_fwd(np.full((1, 16), -2.5), w, 0.0, rnd=identity)
+    assert np.allclose(c, -w)
+
+
+# ------------------------------------------------------------------ RoPE
+def test_rope_is_complex_rotation():
+    T, H, d, theta = 7, 3, 16, 10000.0
+    x = RNG.standard_normal((T, H, d))
+    pos = np.array([0, 1, 2, 3, 0, 1, 2])
+    y = O.rope_apply(x, pos, theta, rnd=identity)
+    z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    freq = np.array([theta ** (-(2 * i) / d) for i in range(d // 2)])
+    rot = np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    zr = z * rot
+    assert np.allclose(y, np.concatenate([zr.real, zr.imag], -1), atol=1e-13)
+    assert np.allclose(y[0], x[0]) and np.allclose(y[4], x[4])     # position 0 restarts per sequence
+    back = O.rope_apply(y, pos, theta, inverse=True, rnd=identity)
+    assert np.allclose(back, x, atol=1e-13)
+
+
+def test_rope_relative_position():
+    d, theta = 32, 500000.0
+    q, k = RNG.standard_normal((1, 1, d)), RNG.standard_normal((1, 1, d))
+    dots = []
+    for m, n in ((5, 2), (9, 6), (103, 100)):
+        qr = O.rope_apply(q, [m], theta, rnd=identity)
+        kr = O.rope_apply(k, [n], theta, rnd=identity)
+        dots.append(float(np.sum(qr * kr)))
+    assert np.allclose(dots, dots[0], rtol=1e-10)
+
+
+# ------------------------------------------------------------------ attention
+def _sdpa_ref(q, k, v, batch, seq):
+    T, nq, d = q.shape
+    grp = nq // k.shape[1]
+    qt = t64(q).view(batch, seq, nq, d).transpose(1, 2)
+    kt = t64(k).view(batch, seq, -1, d).transpose(1, 2).repeat_interleave(grp, dim=1)
+    vt = t64(v).view(batch, seq, -1, d).transpose(1, 2).repeat_interleave(grp, dim=1)
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    return o.transpose(1, 2).reshape(T, nq, d).numpy()
+
+
+@pytest.mark.parametrize("nq,nkv", [(4, 4), (4, 2), (6, 1)])
+def test_attention_matches_sdpa(nq, nkv):
+    batch, seq, d = 2, 9, 8
+    q = RNG.standard_normal((batch * seq, nq, d))
+    k = RNG.standard_normal((batch * seq, nkv, d))
+    v = RNG.standard_normal((batch * seq, nkv, d))
+    o, lse = O.attention_fwd(q, k, v, batch, seq, rnd=identity)
+    assert np.allclose(o, _sdpa_ref(q, k, v, batch, seq), atol=1e-12)
+    # lse of the first row of every sequence is its single score
+    assert np.allclose(lse[:, :, 0], np.einsum("bhd,bhd->bh",
+                       q.reshape(batch, seq, nq, d)[:, 0],
+                       np.repeat(k.reshape(batch, seq, nkv, d)[:, 0], nq // nkv, axis=1)) / np.sqrt(d))
+
+
+def test_attention_causal_and_bwd_fd():
+    batch, seq, nq, nkv, d = 2, 5, 4, 2, 4
+    q = RNG.standard_normal((batch * seq, nq, d))
+    k = RNG.standard_normal((batch * seq, nkv, d))
+    v = RNG.standard_normal((batch * seq, nkv, d))
+    do = RNG.standard_normal((batch * seq, nq, d))
+    o, _ = O.attention_fwd(q, k, v, batch, seq, rnd=identity)
+    k2 = k.copy(); k2[3] += 1.0                      # key at position 3 of sequence 0
+    o2, _ = O.attention_fwd(q, k2, v, batch, seq, rnd=identity)
+    assert np.allclose(o2[:3], o[:3]) and not np.allclose(o2[3:5], o[3:5]) and np.allclose(o2[5:], o[5:])
+    dq, dk, dv = O.attention_bwd(q, k, v, do, batch, seq, rnd=identity)
+    L = lambda qq, kk, vv: float(np.sum(do * O.attention_fwd(qq, kk, vv, batch, seq, rnd=identity)[0]))
+    assert_fd(dq, lambda z: L(z, k, v), q)
+    assert_fd(dk, lambda z: L(q, z, v), k)
+    assert_fd(dv, lambda z: L(q, k, z), v)
+
+
+# ------------------------------------------------------------------ SwiGLU
+def test_swiglu_matches_torch_and_fd():
+    g, u, da = (RNG.standard_normal((4, 6)) * 3 for _ in range(3))
+    a = O.swiglu_fwd(g, u, rnd=identity)
+    assert np.allclose(a, (F.silu(t64(g)) * t64(u)).numpy(), atol=1e-14)
+    dg, du = O.swiglu_bwd(g, u, da, rnd=identity)
+    assert_fd(dg, lambda z: float(np.sum(da * O.swiglu_fwd(z, u, rnd=identity))), g)
+    assert_fd(du, lambda z: float(np.sum(da * O.swiglu_fwd(g, z, rnd=identity))), u)
+
+
+# ------------------------------------------------------------------ decoder layer
+def tiny_layer_params(shape=TINY_LAYER, seed=3):
+    rng = np.random.default_rng(seed)
+    w = {p: rng.standard_normal((fout, fin)) * 0.1 for p, (fin, fout) in PROJ_IN_OUT(shape).items()}
+    w["norm1"] = 1 + rng.uniform(-0.1, 0.1, shape.hidden)
+    w["norm2"] = 1 + rng.uniform(-0.1, 0.1, shape.hidden)
+    lora = {}
+    for p, (fin, fout) in PROJ_IN_OUT(shape).items():
+        lora["A_" + p] = rng.uniform(-0.3, 0.3, (shape.lora_r, fin))
+        lora["B_" + p] = rng.standard_normal((fout, shape.lora_r)) * 0.1
+    return w, lora
+
+
+def _torch_layer(x, w, lora, shape, batch, seq):
+    """Independent composition from torch library ops (merged LoRA weights, SDPA)."""
+    s = shape.lora_scale
+    W = {p: t64(w[p]) + s * (t64(lora["B_" + p]) @ t64(lora["A_" + p])) for p in PROJ_IN_OUT(shape)}
+    xt = t64(x)
+    n1 = F.rms_norm(xt, (shape.hidden,), t64(w["norm1"]), eps=shape.rms_eps)
+    T, d = x.shape[0], shape.head_dim
+    q, k, v = (F.linear(n1, W[p]).numpy() for p in ("q", "k", "v"))
+    pos = np.tile(np.arange(seq), batch)
+
+    def rot(a, nh):
+        a = a.reshape(T, nh, d)
+        z = a[..., : d // 2] + 1j * a[..., d // 2:]
+        fr = shape.rope_theta ** (-(2 * np.arange(d // 2)) / d)
+        z = z * np.exp(1j * pos[:, None, None] * fr[None, None, :])
+        return np.concatenate([z.real, z.imag], -1)
+    o = _sdpa_ref(rot(q, shape.n_q), rot(k, shape.n_kv), v.reshape(T, shape.n_kv, d), batch, seq)
+    h1 = xt + F.linear(t64(o.reshape(T, -1)), W["o"])
+    n2 = F.rms_norm(h1, (shape.hidden,), t64(w["norm2"]), eps=shape.rms_eps)
+    a = F.silu(F.linear(n2, W["gate"])) * F.linear(n2, W["up"])
+    return (h1 + F.linear(a, W["down"])).numpy()
+
+
+def test_decoder_layer_fwd_matches_torch_composition():
+    shape, batch, seq = TINY_LAYER, 2, 8
+    w, lora = tiny_layer_params()
+    x = RNG.standard_normal((batch * seq, shape.hidden))
+    out, _ = O.decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=identity)
+    assert np.allclose(out, _torch_layer(x, w, lora, shape, batch, seq), atol=1e-11)
+
+
+def test_decoder_layer_bwd_finite_differences():
+    shape, batch, seq = TINY_LAYER, 1, 8
+    w, lora = tiny_layer_params()
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((batch * seq, shape.hidden))
+    dout = rng.standard_normal((batch * seq, shape.hidden))
+    dx, gr = O.decoder_layer_bwd(x, dout, w, lora, shape, batch, seq, rnd=identity)
+
+    def L(xx=x, ll=lora):
+        return float(np.sum(dout * O.decoder_layer_fwd(xx, w, ll, shape, batch, seq, rnd=identity)[0]))
+    assert_fd(dx, lambda v: L(xx=v), x, n=8, rtol=1e-5, atol=1e-8)
+    for key in ("A_q", "B_k", "A_v", "B_o", "A_gate", "B_up", "A_down", "B_down"):
+        def Lk(v, key=key):
+            ll = dict(lora); ll[key] = v
+            return L(ll=ll)
+        assert_fd(gr[key], Lk, lora[key], n=4, rtol=1e-5, atol=1e-8)
+
+
+def test_decoder_layer_zero_b_gives_zero_da():
+    shape, batch, seq = TINY_LAYER, 1, 8
+    w, lora = tiny_layer_params()
+    for p in PROJ_IN_OUT(shape):
+        lora["B_" + p] = np.zeros_like(lora["B_" + p])
+    x = RNG.standard_normal((seq, shape.hidden))
+    dout = RNG.standard_normal((seq, shape.hidden))
+    _, gr = O.decoder_layer_bwd(x, dout, w, lora, shape, batch, seq, rnd=identity)
+    for p in PROJ_IN_OUT(shape):
+        assert np.all(gr["A_" + p] == 0) and np.any(gr["B_" + p] != 0)
+
+
+# ------------------------------------------------------------------ cross-entropy
+def test_ce_matches_torch():
+    T, H, V = 12, 16, 50
+    h = RNG.standard_normal((T, H))
+    W = RNG.standard_normal((V, H)) * 0.3
+    labels = RNG.integers(0, V, T)
+    labels[[3, 7]] = -100
+    loss, lse, nv = O.ce_loss_fwd(h, W, labels)
+    ht = t64(h).requires_grad_(True)
+    ref = F.cross_entropy(ht @ t64(W).T, torch.from_numpy(labels), ignore_index=-100)
+    assert nv == 10 and abs(loss - ref.item()) < 1e-12
+    assert np.allclose(lse, torch.logsumexp(t64(h) @ t64(W).T, dim=1).numpy())
+    ref.backward()
+    dh = O.ce_loss_bwd(h, W, labels, rnd=identity)
+    assert np.allclose(dh, ht.grad.numpy(), atol=1e-13)
+    assert np.all(dh[[3, 7]] == 0)
+    dh2 = O.ce_loss_bwd(h, W, labels, grad_scale=0.25, rnd=identity)
+    assert np.allclose(dh2, 0.25 * dh)
+
+
+def test_ce_zero_weights_closed_form():
+    T, H, V = 5, 8, 37
+    h = RNG.standard_normal((T, H))
+    loss, lse, _ = O.ce_loss_fwd(h, np.zeros((V, H)), RNG.integers(0, V, T))
+    assert abs(loss - math.log(V)) < 1e-14 and np.allclose(lse, math.log(V))
+    assert np.all(O.ce_loss_bwd(h, np.zeros((V, H)), RNG.integers(0, V, T)) == 0)
+
+
+def test_ce_bwd_fd():
+    T, H, V = 4, 6, 11
+    h = RNG.standard_normal((T, H))
+    W = RNG.standard_normal((V, H))
+    labels = np.array([1, 5, -100, 10])
+    dh = O.ce_loss_bwd(h, W, labels, rnd=identity)
+    assert_fd(dh, lambda v: O.ce_loss_fwd(v, W, labels)[0], h)
+
+
+# ------------------------------------------------------------------ AdamW
+def test_adamw_matches_torch_and_first_step():
+    p0 = RNG.standard_normal(10)
+    pt = t64(p0).clone().requires_grad_(True)
+    opt = torch.optim.AdamW([pt], lr=2e-4, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    p, m, v = p0.copy(), np.zeros(10), np.zeros(10)
+    for step in range(1, 5):
+        g = RNG.standard_normal(10)
+        pt.grad = t64(g)
+        opt.step()
+        p_prev = p
+        p, m, v = O.adamw_step(p, g, m, v, step, lr=2e-4, wd=0.01)
+        if step == 1:
+            # p1 = p0 (1 - lr wd) - lr g / (|g| + eps)
+            assert np.allclose(p, p_prev * (1 - 2e-6) - 2e-4 * g / (np.abs(g) + 1e-8), rtol=1e-12, atol=1e-15)
+    assert np.allclose(p, pt.detach().numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------------ whole model
+def test_model_grad_reaches_layer0_fd():
+    """The gradient of the mean loss with respect to a layer-0 adapter equals its
+    finite difference (a severed path upstream would make it zero or wrong)."""
+    from oracle.model import model_step
+    shape, batch, seq, V = TINY_LAYER, 1, 6, 23
+    rng = np.random.default_rng(5)
+    layers = [tiny_layer_params(seed=s) for s in (21, 22)]
+    emb = rng.standard_normal((V, shape.hidden)) * 0.5
+    fn = np.ones(shape.hidden)
+    ids = [rng.integers(0, V, seq), rng.integers(0, V, seq)]
+    loss, grads, _ = model_step(ids, emb, fn, None, layers, shape, batch, seq, rnd=identity)
+    key = "A_q"
+    a0 = layers[0][1][key]
+
+    def L(v):
+        ll = [(layers[0][0], {**layers[0][1], key: v}), layers[1]]
+        return model_step(ids, emb, fn, None, ll, shape, batch, seq, rnd=identity)[0]
+    assert_fd(grads[0][key], L, a0, n=4, rtol=1e-5, atol=1e-9)
+    assert np.any(grads[0][key] != 0)
