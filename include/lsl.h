@@ -1,0 +1,279 @@
+/*
+ * lsl.h - C ABI of the layer-streamed LoRA training library for AMD MI355X (gfx950).
+ *
+ * What the library computes: LoRA fine-tuning of a frozen decoder-only base whose
+ * layers live in pinned host memory and are streamed, one layer per visit, into a
+ * two-slot HBM pool, for the forward and the backward pass ("Exact Layer
+ * Streaming: LoRA Fine-Tuning of an 8B Model on a 4 GB Laptop GPU", abstract;
+ * "Soup CLI Lets You Fine-Tune an 8B LLM on a 4 GB Laptop GPU", section "How
+ * Layer Streaming Works"; "Soup: Fine-Tuning an 8B LLM on a 4 GB Laptop GPU with
+ * One YAML File", section "Layer Streaming: The Mechanism Behind the 4 GB Claim",
+ * which describes a pinned host base store and two VRAM layer buffers).
+ *
+ * Conventions shared by every call:
+ *  - Every call returns lsl_status. On any error nothing has been enqueued and
+ *    lsl_last_error() returns a message (thread-local, valid until the next call
+ *    on the same thread). No C++ exception crosses this boundary.
+ *  - Compute calls are asynchronous on the caller's stream (a hipStream_t passed
+ *    as lsl_stream; NULL is the null stream). They never synchronise the host and
+ *    never allocate device memory: scratch space is a caller-provided workspace
+ *    whose size the matching *_workspace_bytes call returns.
+ *  - bfloat16 tensors are passed as uint16_t bit patterns, row-major, densely
+ *    packed unless a leading dimension is given. Device pointers must be 16-byte
+ *    aligned (INVALID_ARG otherwise; there is no slower fallback path).
+ *  - Kernel selection (tile shapes, splits, chunking) depends only on the shapes
+ *    passed, never on pointer values, residency or the stream, so a streamed and
+ *    a resident run execute identical arithmetic and produce identical bits.
+ *    No result is reduced with floating-point atomics.
+ *  - The caller owns every buffer. The library keeps no device state; a pool
+ *    object owns only its HIP events.
+ */
+#ifndef LSL_H
+#define LSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lsl_status;
+enum {
+  LSL_OK = 0,
+  LSL_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size */
+  LSL_ERR_UNSUPPORTED = 2,  /* a shape this build does not support */
+  LSL_ERR_NOT_PINNED = 3,   /* host pointer is not page-locked */
+  LSL_ERR_WORKSPACE = 4,    /* workspace smaller than *_workspace_bytes */
+  LSL_ERR_STATE = 5,        /* pool slot used out of order */
+  LSL_ERR_HIP = 6           /* a HIP runtime call failed */
+};
+
+typedef void* lsl_stream; /* hipStream_t */
+
+/* Message of the last error on this thread ("" when none). */
+const char* lsl_last_error(void);
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t lsl_abi_version(void);
+
+typedef struct {
+  int32_t cu_count;
+  int32_t clock_khz;       /* peak shader clock */
+  int32_t mem_clock_khz;
+  int32_t mem_bus_bits;
+  int64_t hbm_bytes;
+  int32_t lds_bytes_per_cu;
+  int32_t pad;
+  char arch[64];           /* e.g. "gfx950:sramecc+:xnack-" */
+} lsl_device_props;
+/* Properties of `device`, for roofline arithmetic. */
+lsl_status lsl_device_info(int32_t device, lsl_device_props* out);
+
+/* ------------------------------------------------------------------ NF4
+ * NF4 is the 4-bit NormalFloat format the pages quantise the 8B base to
+ * ("Exact Layer Streaming ...", abstract). Definition (QLoRA, Dettmers et al.
+ * 2023, section 3): 16 code values = standard-normal quantiles scaled to
+ * [-1, 1] with an exact 0; blockwise absmax scaling over 64 consecutive
+ * row-major elements, absmax stored as float32.
+ * Packing: element 2j in the high nibble of byte j, element 2j+1 in the low one.
+ */
+/* The 16 float32 code values, ascending (host call, no GPU needed). */
+lsl_status lsl_nf4_codebook(float out[16]);
+/* Quantise w [rows x cols] bf16 (cols % 64 == 0) into codes [rows x cols/2] and
+ * absmax [rows x cols/64]: n = w / absmax (IEEE float32 division; 0 when absmax
+ * is 0), code = nearest code value, ties to the lower code. Device pointers. */
+lsl_status lsl_nf4_quantize(const uint16_t* w, int64_t rows, int64_t cols,
+                            uint8_t* codes, float* absmax, lsl_stream stream);
+/* w' = bf16(code_value * absmax) (one float32 multiply, round to nearest even). */
+lsl_status lsl_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t rows,
+                           int64_t cols, uint16_t* w, lsl_stream stream);
+
+/* ------------------------------------------------------------------ weights */
+enum { LSL_WFMT_NF4 = 0, LSL_WFMT_BF16 = 1 };
+/* A frozen weight [n_out x k_in] (n_out and k_in multiples of 64): NF4 (nf4
+ * codes + absmax) or bf16. Pointers not used by the format must be NULL. */
+typedef struct {
+  int32_t fmt;
+  int32_t pad;
+  int64_t n_out;
+  int64_t k_in;
+  const uint8_t* nf4;
+  const float* absmax;
+  const uint16_t* bf16;
+} lsl_weight;
+
+/* ------------------------------------------------------------------ LoRA linear
+ * y = x W^T + s (x A^T) B^T with frozen W and trainable A [r x k_in],
+ * B [n_out x r] (LoRA, Hu et al. 2021; the pages train such adapters on the
+ * frozen base: "Exact Layer Streaming ...", abstract).
+ * Rounding: t = bf16(x A^T); y = bf16(x W^T + s t B^T) (float32 accumulation,
+ * one rounding). r is a multiple of 8 in [8, 64]; T >= 0 is any token count.
+ */
+size_t lsl_lora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in, int32_t r);
+/* x [T x k_in], y [T x n_out], t_out [T x r] (kept for the backward). */
+lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                           uint16_t* y, uint16_t* t_out, void* ws, size_t ws_bytes,
+                           lsl_stream stream);
+/* u = bf16(dy B); dx = bf16(dy W + s u A) (dx may be NULL);
+ * dA += s u^T x and dB += s dy^T t (float32, accumulated into the caller's
+ * buffers in a fixed order). W gets no gradient. */
+lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, const uint16_t* dy, int64_t T,
+                           const lsl_weight* W, const uint16_t* A, const uint16_t* B, int32_t r,
+                           float scale, uint16_t* dx, float* dA, float* dB, void* ws,
+                           size_t ws_bytes, lsl_stream stream);
+
+/* ------------------------------------------------------------------ decoder layer
+ * Pre-norm Llama/Qwen2 decoder layer: h = x + o(attn(rope(q(n1)), rope(k(n1)), v(n1))),
+ * out = h + down(silu(gate(n2)) * up(n2)), n1 = rmsnorm(x), n2 = rmsnorm(h);
+ * GQA causal attention (query head j reads kv head j / (n_q / n_kv)), scale
+ * 1/sqrt(head_dim); rotate-half RoPE with angle pos * theta^(-2i/d), positions
+ * restarting at 0 in each sequence; LoRA on all seven projections.
+ * The pages stream exactly these "decoder layers" ("Soup CLI ...", section "How
+ * Layer Streaming Works").
+ */
+typedef struct {
+  int32_t hidden, n_q, n_kv, head_dim, inter;
+  float rms_eps, rope_theta;
+  int32_t wfmt;      /* LSL_WFMT_NF4 or LSL_WFMT_BF16 */
+  int32_t lora_r;
+  float lora_scale;  /* alpha / r */
+} lsl_layer_cfg;
+
+/* Byte offsets inside one packed layer blob (every offset 256-byte aligned).
+ * Matrices are stacked per fused GEMM: qkv = [Wq; Wk; Wv] [(n_q+2 n_kv) d x hidden],
+ * o [hidden x n_q d], gu = [Wgate; Wup] [2 inter x hidden], down [hidden x inter].
+ * For NF4 each matrix is codes at w_off[i] and float32 absmax at absmax_off[i];
+ * for bf16 the matrix is at w_off[i] and absmax_off[i] is 0.
+ * norm1/norm2 are bf16 [hidden]. The pinned host store and a resident copy use
+ * this same layout, so a slot holds a byte-identical copy of one layer. */
+enum { LSL_M_QKV = 0, LSL_M_O = 1, LSL_M_GU = 2, LSL_M_DOWN = 3 };
+typedef struct {
+  uint64_t norm1_off, norm2_off;
+  uint64_t w_off[4];
+  uint64_t absmax_off[4];
+  uint64_t total_bytes;
+} lsl_layer_layout;
+lsl_status lsl_layer_layout_get(const lsl_layer_cfg* cfg, lsl_layer_layout* out);
+
+/* Trainable adapters of one layer, grouped like the fused GEMMs:
+ *   A[QKV] = [A_q; A_k; A_v]   [3r x hidden]    B[QKV] = [B_q; B_k; B_v] [(n_q+2n_kv)d x r]
+ *   A[O]                       [r x n_q d]      B[O]                     [hidden x r]
+ *   A[GU]  = [A_gate; A_up]    [2r x hidden]    B[GU]  = [B_gate; B_up]  [2 inter x r]
+ *   A[DOWN]                    [r x inter]      B[DOWN]                  [hidden x r]
+ * bf16 working copies; gradients have the same shapes in float32. */
+typedef struct { const uint16_t* A[4]; const uint16_t* B[4]; } lsl_lora_set;
+typedef struct { float* dA[4]; float* dB[4]; } lsl_lora_grads;
+
+enum { LSL_MODE_FWD = 0, LSL_MODE_BWD = 1 };
+size_t lsl_layer_workspace_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode);
+/* x_in, x_out [batch*seq x hidden] bf16. Nothing is saved: the caller keeps
+ * x_in as the layer-boundary checkpoint for the backward. */
+lsl_status decoder_layer_fwd(const lsl_layer_cfg* cfg, const void* layer_blob,
+                             const lsl_lora_set* lora, const uint16_t* x_in, int32_t batch,
+                             int32_t seq, uint16_t* x_out, void* ws, size_t ws_bytes,
+                             lsl_stream stream);
+/* Recomputes the forward from x_in, then back-propagates dy. dx may be NULL
+ * (first layer); adapter gradients are accumulated (+=) into grads. */
+lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* layer_blob,
+                             const lsl_lora_set* lora, const uint16_t* x_in, const uint16_t* dy,
+                             int32_t batch, int32_t seq, uint16_t* dx,
+                             const lsl_lora_grads* grads, void* ws, size_t ws_bytes,
+                             lsl_stream stream);
+
+/* ------------------------------------------------------------------ layer pool
+ * Two (or more) HBM slots, each holding one layer blob, filled from the pinned
+ * host store by hipMemcpyAsync on a copy stream and ordered against compute by
+ * events ("Soup: ...", section "Layer Streaming: The Mechanism Behind the 4 GB
+ * Claim": a pinned base store and two VRAM buffers).
+ * Slot life cycle: load_layer_async -> lsl_pool_acquire -> lsl_pool_release ->
+ * load_layer_async ... . A load waits (on the copy stream) until the slot's
+ * previous user released it; acquire makes the compute stream wait for the load.
+ * The caller owns the slot memory and the copy stream. */
+typedef struct lsl_pool lsl_pool;
+lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, int32_t n_slots,
+                           size_t slot_bytes, lsl_stream copy_stream);
+lsl_status lsl_pool_destroy(lsl_pool* pool);
+/* Enqueue host->slot copy of `bytes` (<= slot_bytes) from page-locked host_ptr.
+ * NOT_PINNED if host_ptr is pageable; STATE if the slot is loaded or acquired. */
+lsl_status load_layer_async(lsl_pool* pool, int32_t slot, const void* host_ptr, size_t bytes);
+/* Make `compute` wait for the slot's load; returns the slot's device pointer.
+ * STATE unless the slot has been loaded and not yet acquired. */
+lsl_status lsl_pool_acquire(lsl_pool* pool, int32_t slot, lsl_stream compute, void** slot_ptr);
+/* Record on `compute` that the slot's contents are no longer needed.
+ * STATE unless the slot is acquired. */
+lsl_status lsl_pool_release(lsl_pool* pool, int32_t slot, lsl_stream compute);
+/* Mark a released slot as still holding `host_ptr`'s layer, so it can be
+ * acquired again without a copy (the layers kept across the turn of a sweep). */
+lsl_status lsl_pool_reuse(lsl_pool* pool, int32_t slot);
+/* Seconds the copy engine spent on the slot's most recent load (waits for it). */
+lsl_status lsl_pool_last_copy_seconds(lsl_pool* pool, int32_t slot, double* seconds);
+
+/* ------------------------------------------------------------------ cross-entropy
+ * Token cross-entropy over the vocabulary, fused with the lm_head product and
+ * chunked over the vocabulary so no [T x V] logits tensor is ever stored (the
+ * pages measure that tensor's cost: "Exact Layer Streaming ...", abstract).
+ * z = hN W^T (float32, never rounded); lse_t = log sum_v exp(z_tv);
+ * loss = mean over labels != ignore_index of (lse_t - z_t,label).
+ * hN [T x H] bf16, w_lm [V x H] bf16, labels int32 [T].
+ */
+size_t lsl_ce_workspace_bytes(int64_t T, int64_t H, int64_t V);
+/* loss: one float (device); lse: float [T] (device). */
+lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm, const int32_t* labels,
+                             int64_t T, int64_t H, int64_t V, int32_t ignore_index, float* loss,
+                             float* lse, void* ws, size_t ws_bytes, lsl_stream stream);
+/* dhN = bf16(grad_scale / N_valid * (softmax(z) - onehot(label)) W), zero rows for
+ * ignored tokens; lse from fused_ce_loss_fwd. */
+lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm, const int32_t* labels,
+                             const float* lse, int64_t T, int64_t H, int64_t V,
+                             int32_t ignore_index, float grad_scale, uint16_t* dhN, void* ws,
+                             size_t ws_bytes, lsl_stream stream);
+
+/* ------------------------------------------------------------------ support ops
+ * The individual steps of the decoder layer, exported so each can be checked on
+ * its own (same kernels the layer calls). */
+/* y = bf16(x / sqrt(mean(x^2) + eps) * w), x, y [T x H]. */
+lsl_status lsl_rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps,
+                           uint16_t* y, lsl_stream stream);
+/* dx = bf16(dres + r (w dy - xh mean(xh w dy))), xh = x r; dres may be NULL. */
+lsl_status lsl_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy,
+                           const uint16_t* dres, int64_t T, int64_t H, float eps, uint16_t* dx,
+                           lsl_stream stream);
+/* In-place rotate-half RoPE on x [T rows, row stride ld elements], heads
+ * [n_heads x head_dim] starting at column 0 of each row; position = row % seq.
+ * inverse != 0 rotates by -angle (the backward). */
+lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_heads, int32_t head_dim,
+                    int32_t seq, float theta, int32_t inverse, lsl_stream stream);
+/* Causal GQA attention. q [T x ldq] (n_q heads of d), k, v [T x ldk] (n_kv heads),
+ * o [T x ldo]; lse float [batch x n_q x seq]. T = batch * seq. head_dim 64 or 128. */
+lsl_status lsl_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             int64_t ldq, int64_t ldk, int32_t batch, int32_t seq, int32_t n_q,
+                             int32_t n_kv, int32_t head_dim, uint16_t* o, int64_t ldo, float* lse,
+                             lsl_stream stream);
+size_t lsl_attention_workspace_bytes(int32_t batch, int32_t seq, int32_t n_q, int32_t n_kv,
+                                     int32_t head_dim);
+/* Gradients of sum(do * o): dq [T x ldq], dk, dv [T x ldk] (dk, dv summed over
+ * the heads of each group). */
+lsl_status lsl_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* o, const uint16_t* dout, const float* lse,
+                             int64_t ldq, int64_t ldk, int32_t batch, int32_t seq, int32_t n_q,
+                             int32_t n_kv, int32_t head_dim, uint16_t* dq, uint16_t* dk,
+                             uint16_t* dv, void* ws, size_t ws_bytes, lsl_stream stream);
+/* gu [T x 2I] = [gate | up]; a = bf16(silu(gate) * up) [T x I]. */
+lsl_status lsl_swiglu_fwd(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, lsl_stream stream);
+/* dgu [T x 2I] = [bf16(da up s(g)(1 + g(1 - s(g)))) | bf16(da silu(g))]. */
+lsl_status lsl_swiglu_bwd(const uint16_t* gu, const uint16_t* da, int64_t T, int64_t I,
+                          uint16_t* dgu, lsl_stream stream);
+/* out[t] = table[ids[t]] (frozen, resident embedding; ids outside [0, V) give zeros). */
+lsl_status lsl_embed_fwd(const uint16_t* table, const int32_t* ids, int64_t T, int64_t H,
+                         int64_t V, uint16_t* out, lsl_stream stream);
+/* AdamW (decoupled decay) on n float32 master parameters; refreshes the bf16
+ * working copy p_bf16 (may be NULL). step counts from 1. */
+lsl_status lsl_adamw_step(float* p, uint16_t* p_bf16, const float* g, float* m, float* v,
+                          int64_t n, int32_t step, float lr, float beta1, float beta2, float eps,
+                          float weight_decay, lsl_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSL_H */

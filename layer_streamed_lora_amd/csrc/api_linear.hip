@@ -1,0 +1,161 @@
+// C-ABI entry points of the LoRA linear and of the standalone support ops.
+// Every entry validates all arguments before enqueueing anything.
+#include "common.h"
+#include "gemm.h"
+#include "small.h"
+#include "api_util.h"
+
+using namespace lsl;
+
+namespace lsl {
+
+bool lora_rank_ok(int32_t r) { return r >= 8 && r <= 64 && r % 8 == 0; }
+
+size_t linear_ws_fwd(int64_t T, int64_t K) { return lora_nt_ws_bytes(T, K); }
+
+size_t linear_ws_bwd(int64_t T, int64_t N, int64_t K, int r) {
+  size_t part = lora_nt_ws_bytes(T, N);
+  part = std::max(part, lora_tn_ws_bytes(T, K));
+  part = std::max(part, lora_tn_ws_bytes(T, N));
+  return align256((size_t)T * r * 2) + part;
+}
+
+static lsl_status check_weight(const lsl_weight* W, const char* fn) {
+  if (!W) return set_error(LSL_ERR_INVALID_ARG, "%s: W is NULL", fn);
+  if (W->n_out <= 0 || W->k_in <= 0 || W->k_in % 64 || W->n_out % 64)
+    return set_error(LSL_ERR_UNSUPPORTED, "%s: weight [%lld x %lld] needs k_in and n_out multiples of 64", fn,
+                     (long long)W->n_out, (long long)W->k_in);
+  if (W->fmt == LSL_WFMT_NF4) {
+    if (!W->nf4 || !W->absmax || W->bf16 || !aligned(W->nf4, 16) || !aligned(W->absmax, 4))
+      return set_error(LSL_ERR_INVALID_ARG, "%s: NF4 weight needs 16-byte aligned codes and absmax, bf16 NULL", fn);
+  } else if (W->fmt == LSL_WFMT_BF16) {
+    if (!W->bf16 || W->nf4 || W->absmax || !aligned(W->bf16, 16))
+      return set_error(LSL_ERR_INVALID_ARG, "%s: bf16 weight needs a 16-byte aligned pointer, NF4 pointers NULL", fn);
+  } else {
+    return set_error(LSL_ERR_INVALID_ARG, "%s: unknown weight format %d", fn, W->fmt);
+  }
+  return LSL_OK;
+}
+
+static void weight_into(GemmDesc& g, const lsl_weight* W) {
+  g.wfmt = W->fmt;
+  g.wb = W->bf16; g.wq = W->nf4; g.wa = W->absmax;
+}
+
+}  // namespace lsl
+
+extern "C" size_t lsl_lora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in, int32_t r) {
+  if (T < 0 || n_out <= 0 || k_in <= 0 || !lora_rank_ok(r)) return 0;
+  return std::max(linear_ws_fwd(T, k_in), linear_ws_bwd(T, n_out, k_in, r));
+}
+
+extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W, const uint16_t* A,
+                                      const uint16_t* B, int32_t r, float scale, uint16_t* y, uint16_t* t_out,
+                                      void* ws, size_t ws_bytes, lsl_stream stream) {
+  const char* fn = "lora_linear_fwd";
+  LSL_TRY(check_weight(W, fn));
+  if (T < 0) return set_error(LSL_ERR_INVALID_ARG, "%s: T < 0", fn);
+  if (!lora_rank_ok(r)) return set_error(LSL_ERR_UNSUPPORTED, "%s: rank %d must be a multiple of 8 in [8, 64]", fn, r);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {x, A, B, y, t_out}));
+  if (ws_bytes < linear_ws_fwd(T, W->k_in) || (!ws && linear_ws_fwd(T, W->k_in)))
+    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, linear_ws_fwd(T, W->k_in));
+  hipStream_t s = (hipStream_t)stream;
+  LoraNt nt;
+  nt.p = x; nt.ldp = W->k_in; nt.T = T; nt.K = W->k_in; nt.kl = r; nt.a_full = A;
+  nt.out = t_out; nt.ldo = r; nt.ws = (float*)ws;
+  LSL_TRY(lora_nt_launch(nt, s));
+  GemmDesc g;
+  g.x = x; g.ldx = W->k_in; weight_into(g, W); g.kn = false;
+  g.M = T; g.N = W->n_out; g.K = W->k_in;
+  g.lora = 1; g.la = t_out; g.ldla = r; g.kl = r; g.lb = B; g.r = r; g.nseg = 1; g.seg_end[0] = W->n_out;
+  g.scale = scale; g.y = y; g.ldy = W->n_out;
+  return gemm_launch(g, s);
+}
+
+extern "C" lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, const uint16_t* dy, int64_t T,
+                                      const lsl_weight* W, const uint16_t* A, const uint16_t* B, int32_t r,
+                                      float scale, uint16_t* dx, float* dA, float* dB, void* ws, size_t ws_bytes,
+                                      lsl_stream stream) {
+  const char* fn = "lora_linear_bwd";
+  LSL_TRY(check_weight(W, fn));
+  if (T < 0) return set_error(LSL_ERR_INVALID_ARG, "%s: T < 0", fn);
+  if (!lora_rank_ok(r)) return set_error(LSL_ERR_UNSUPPORTED, "%s: rank %d must be a multiple of 8 in [8, 64]", fn, r);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {x, t, dy, A, B, dA, dB}));
+  if (dx && !aligned(dx, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: dx misaligned", fn);
+  size_t need = linear_ws_bwd(T, W->n_out, W->k_in, r);
+  if (!ws || ws_bytes < need || !aligned(ws, 256))
+    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t N = W->n_out, K = W->k_in;
+  uint16_t* u = (uint16_t*)ws;
+  float* part = (float*)((char*)ws + align256((size_t)T * r * 2));
+  LoraNt nt;
+  nt.p = dy; nt.ldp = N; nt.T = T; nt.K = N; nt.kl = r; nt.b_full = B; nt.r = r; nt.nseg = 1; nt.seg_end[0] = N;
+  nt.out = u; nt.ldo = r; nt.ws = part;
+  LSL_TRY(lora_nt_launch(nt, s));
+  if (dx) {
+    GemmDesc g;
+    g.x = dy; g.ldx = N; weight_into(g, W); g.kn = true;
+    g.M = T; g.N = K; g.K = N;
+    g.lora = 2; g.la = u; g.ldla = r; g.kl = r; g.lb = A; g.r = r;
+    g.scale = scale; g.y = dx; g.ldy = K;
+    LSL_TRY(gemm_launch(g, s));
+  }
+  LoraTn ta;
+  ta.p = x; ta.ldp = K; ta.q = u; ta.ldq = r; ta.T = T; ta.W = K; ta.kl = r; ta.scale = scale; ta.dA = dA; ta.ws = part;
+  LSL_TRY(lora_tn_launch(ta, s));
+  LoraTn tb;
+  tb.p = dy; tb.ldp = N; tb.q = t; tb.ldq = r; tb.T = T; tb.W = N; tb.kl = r; tb.scale = scale; tb.dB = dB;
+  tb.r = r; tb.nseg = 1; tb.seg_end[0] = N; tb.ws = part;
+  return lora_tn_launch(tb, s);
+}
+
+// ---------------------------------------------------------------- support ops
+extern "C" lsl_status lsl_rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps,
+                                      uint16_t* y, lsl_stream stream) {
+  const char* fn = "lsl_rmsnorm_fwd";
+  if (T < 0 || H <= 0 || H % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes (H %% 8 == 0)", fn);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {x, w, y}));
+  return rmsnorm_fwd_launch(x, w, T, H, eps, y, (hipStream_t)stream);
+}
+
+extern "C" lsl_status lsl_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,
+                                      int64_t T, int64_t H, float eps, uint16_t* dx, lsl_stream stream) {
+  const char* fn = "lsl_rmsnorm_bwd";
+  if (T < 0 || H <= 0 || H % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes (H %% 8 == 0)", fn);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {x, w, dy, dx}));
+  if (dres && !aligned(dres, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: dres misaligned", fn);
+  return rmsnorm_bwd_launch(x, w, dy, dres, T, H, eps, dx, (hipStream_t)stream);
+}
+
+extern "C" lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_heads, int32_t head_dim, int32_t seq,
+                               float theta, int32_t inverse, lsl_stream stream) {
+  const char* fn = "lsl_rope";
+  if (T < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 || seq <= 0 || ld < (int64_t)n_heads * head_dim ||
+      !(theta > 0.f))
+    return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {x}));
+  return rope_launch(x, T, ld, n_heads, head_dim, seq, theta, inverse, (hipStream_t)stream);
+}
+
+extern "C" lsl_status lsl_swiglu_fwd(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, lsl_stream stream) {
+  const char* fn = "lsl_swiglu_fwd";
+  if (T < 0 || I <= 0 || I % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes (I %% 8 == 0)", fn);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {gu, a}));
+  return swiglu_fwd_launch(gu, T, I, a, (hipStream_t)stream);
+}
+
+extern "C" lsl_status lsl_swiglu_bwd(const uint16_t* gu, const uint16_t* da, int64_t T, int64_t I, uint16_t* dgu,
+                                     lsl_stream stream) {
+  const char* fn = "lsl_swiglu_bwd";
+  if (T < 0 || I <= 0 || I % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes (I %% 8 == 0)", fn);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {gu, da, dgu}));
+  return swiglu_bwd_launch(gu, da, T, I, dgu, (hipStream_t)stream);
+}

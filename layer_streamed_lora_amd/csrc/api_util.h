@@ -1,0 +1,25 @@
+// Validation helpers shared by the C-ABI translation units.
+#pragma once
+#include "common.h"
+#include <algorithm>
+#include <initializer_list>
+
+#define LSL_TRY(expr)                         \
+  do {                                        \
+    lsl_status _st = (expr);                  \
+    if (_st != LSL_OK) return _st;            \
+  } while (0)
+
+namespace lsl {
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+inline lsl_status check_ptrs(const char* fn, std::initializer_list<const void*> ps) {
+  int i = 0;
+  for (const void* p : ps) {
+    if (!p) return set_error(LSL_ERR_INVALID_ARG, "%s: pointer argument %d is NULL", fn, i);
+    if (!aligned(p, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: pointer argument %d is not 16-byte aligned", fn, i);
+    ++i;
+  }
+  return LSL_OK;
+}
+bool lora_rank_ok(int32_t r);
+}  // namespace lsl

@@ -1,0 +1,18 @@
+// Host-side descriptor of one LoRA GEMM launch (see gemm.hip).
+#pragma once
+#include "common.h"
+namespace lsl {
+struct GemmDesc {
+  const uint16_t* x = nullptr; int64_t ldx = 0;    // [M x K]
+  int wfmt = LSL_WFMT_BF16; bool kn = false;        // weight format; stored [K x N] when kn
+  const uint16_t* wb = nullptr; const uint8_t* wq = nullptr; const float* wa = nullptr;
+  int64_t M = 0, N = 0, K = 0;
+  int lora = 0;                                     // 0 none, 1 forward (masked B), 2 backward (A^T)
+  const uint16_t* la = nullptr; int64_t ldla = 0; int kl = 0;
+  const uint16_t* lb = nullptr; int r = 0; int nseg = 1; int64_t seg_end[4] = {0, 0, 0, 0};
+  float scale = 0.f;
+  uint16_t* y = nullptr; int64_t ldy = 0;
+  const uint16_t* res = nullptr; int64_t ldres = 0;
+};
+lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
+}  // namespace lsl

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/lsl.h declares, and rejects bad arguments with the
+documented status before touching a device."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "lsl.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import layer_streamed_lora_amd as lsl
+    return lsl
+
+
+def test_header_lists_entry_points():
+    names = header_functions()
+    for n in ("load_layer_async", "lora_linear_fwd", "lora_linear_bwd", "decoder_layer_fwd", "decoder_layer_bwd",
+              "fused_ce_loss_fwd", "fused_ce_loss_bwd", "lsl_pool_create", "lsl_nf4_quantize"):
+        assert n in names
+    assert len(names) >= 30
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    from layer_streamed_lora_amd import _abi
+    assert set(_abi.PROTOS) == set(header_functions())
+
+
+def test_codebook_matches_oracle_bitwise(L):
+    from oracle.nf4 import nf4_codebook
+    got = np.array(L.nf4_codebook(), np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4_codebook().view(np.uint32))
+
+
+def test_abi_version(L):
+    assert L.abi_version() == 1
+
+
+def _status(L, name, *args):
+    return getattr(L.lib(), name)(*args)
+
+
+def test_validation_rejects_before_enqueue(L):
+    from layer_streamed_lora_amd import _abi
+    lib = L.lib()
+    # non-multiple-of-64 columns
+    assert lib.lsl_nf4_quantize(None, 4, 63, None, None, None) == _abi.LSL_ERR_INVALID_ARG
+    assert b"multiple of 64" in lib.lsl_last_error()
+    # null weight
+    assert lib.lora_linear_fwd(None, 8, None, None, None, 8, 2.0, None, None, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
+    # rank not a multiple of 8
+    w = _abi.Weight(_abi.WFMT_BF16, 0, 64, 64, None, None, 16)
+    assert lib.lora_linear_fwd(16, 8, C.byref(w), 16, 16, 12, 2.0, 16, 16, None, 0, None) == _abi.LSL_ERR_UNSUPPORTED
+    # k_in not a multiple of 64
+    w = _abi.Weight(_abi.WFMT_BF16, 0, 64, 96, None, None, 16)
+    assert lib.lora_linear_fwd(16, 8, C.byref(w), 16, 16, 8, 2.0, 16, 16, None, 0, None) == _abi.LSL_ERR_UNSUPPORTED
+    w = _abi.Weight(_abi.WFMT_BF16, 0, 72, 64, None, None, 16)
+    assert lib.lora_linear_fwd(16, 8, C.byref(w), 16, 16, 8, 2.0, 16, 16, None, 0, None) == _abi.LSL_ERR_UNSUPPORTED
+    # NF4 weight with a bf16 pointer set
+    w = _abi.Weight(_abi.WFMT_NF4, 0, 64, 64, 256, 256, 256)
+    assert lib.lora_linear_fwd(16, 8, C.byref(w), 16, 16, 8, 2.0, 16, 16, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
+    # misaligned activation pointer
+    w = _abi.Weight(_abi.WFMT_BF16, 0, 64, 64, None, None, 256)
+    assert lib.lora_linear_fwd(18, 8, C.byref(w), 256, 256, 8, 2.0, 256, 256, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.lora_linear_fwd(256, 8, C.byref(w), 256, 256, 8, 2.0, 256, 256, 256, 0, None) == _abi.LSL_ERR_WORKSPACE
+    # empty input is a no-op
+    assert lib.lora_linear_fwd(None, 0, C.byref(w), None, None, 8, 2.0, None, None, None, 0, None) == _abi.LSL_OK
+    # pool arguments
+    out = C.c_void_p()
+    assert lib.lsl_pool_create(C.byref(out), None, 2, 1024, None) == _abi.LSL_ERR_INVALID_ARG
+    slots = (C.c_void_p * 2)(256, 300)
+    assert lib.lsl_pool_create(C.byref(out), slots, 2, 1024, None) == _abi.LSL_ERR_INVALID_ARG
+    assert lib.load_layer_async(None, 0, 4096, 16) == _abi.LSL_ERR_INVALID_ARG
+    assert lib.lsl_adamw_step(None, None, None, None, None, 10, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == _abi.LSL_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_are_deterministic(L):
+    a = L.lora_linear_workspace_bytes(512, 4096, 4096, 16)
+    b = L.lora_linear_workspace_bytes(512, 4096, 4096, 16)
+    assert a == b and a > 0
+    assert L.lora_linear_workspace_bytes(512, 4096, 4096, 12) == 0

@@ -1,0 +1,102 @@
+"""GPU parity of NF4 quantise/dequant and of the LoRA linear forward/backward
+against the CPU oracle, on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth.configs import WORKLOADS
+from tests.gpu_util import dev_bf16, dev, host, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+def test_nf4_quantize_dequant_bitwise(gpu):
+    w = synth.normal_bf16((192, 512), 0.02, 9, 0, 1)
+    w[3, :64] = 0.0
+    w[5, 64:128] = 0.0
+    w[5, 100] = -0.375
+    codes, absmax = gpu.nf4_quantize(dev_bf16(w))
+    oc, oa = O.nf4_quantize(w.astype(np.float64))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), oa.view(np.uint32))
+    deq = gpu.nf4_dequant(codes, absmax)
+    od = O.nf4_dequant(oc, oa)
+    assert np.array_equal(host(deq), od)
+
+
+def test_nf4_quantize_large_bitwise(gpu):
+    # one Llama-8B-shaped o projection (4096 x 4096)
+    w = synth.normal_bf16((4096, 4096), 0.02, 2, 0, 4)
+    codes, absmax = gpu.nf4_quantize(dev_bf16(w))
+    oc, oa = O.nf4_quantize(w.astype(np.float64))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(absmax.cpu().numpy(), oa)
+
+
+def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
+    x = synth.activation((T, fin), wid, "x")
+    dy = synth.activation((T, fout), wid, "dy")
+    w = synth.normal_bf16((fout, fin), 0.02, wid, 0, 1)
+    a = synth.uniform_bf16((r, fin), -1 / np.sqrt(fin), 1 / np.sqrt(fin), wid, 0, 10)
+    b = np.zeros((fout, r), np.float32) if b_zero else synth.normal_bf16((fout, r), 0.01, wid, 0, 11)
+    return x, dy, w, a, b, alpha / r
+
+
+@pytest.mark.parametrize("T,fin,fout,r,fmt", [
+    (128, 256, 256, 8, "nf4"),        # single NF4 LoRA linear 256 -> 256, 128 tokens
+    (200, 320, 448, 16, "nf4"),       # ragged: several tiles and a partial tile in T and both widths
+    (200, 320, 448, 16, "bf16"),
+    (1, 64, 64, 8, "nf4"),            # a single token, smallest shapes
+    (300, 1024, 1152, 16, "bf16"),
+])
+def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
+    x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
+    if fmt == "nf4":
+        oc, oa = O.nf4_quantize(w.astype(np.float64))
+        wd = O.nf4_dequant(oc, oa)
+        W = gpu.FrozenWeight.nf4(dev_bf16(w))
+    else:
+        wd = w.astype(np.float64)
+        W = gpu.FrozenWeight.dense(dev_bf16(w))
+    xd, ad, bd, dyd = (v.astype(np.float64) for v in (x, a, b, dy))
+    y_ref, t_ref = O.lora_linear_fwd(xd, wd, ad, bd, s)
+    dx_ref, da_ref, db_ref, _ = O.lora_linear_bwd(xd, t_ref, dyd, wd, ad, bd, s)
+    X, A, B, DY = dev_bf16(x), dev_bf16(a), dev_bf16(b), dev_bf16(dy)
+    y, t = gpu.lora_linear_fwd(X, W, A, B, s)
+    dA = torch.zeros((r, fin), dtype=torch.float32, device="cuda")
+    dB = torch.zeros((fout, r), dtype=torch.float32, device="cuda")
+    dx = gpu.lora_linear_bwd(X, t, DY, W, A, B, s, dA, dB)
+    torch.cuda.synchronize()
+    assert_close(host(t), t_ref, "t")
+    assert_close(host(y), y_ref, "y")
+    assert_close(host(dx), dx_ref, "dx")
+    assert_close(host(dA), da_ref, "dA")
+    assert_close(host(dB), db_ref, "dB")
+    # gradients accumulate (+=) in a fixed order: a second call doubles them exactly
+    dA1, dB1 = dA.clone(), dB.clone()
+    gpu.lora_linear_bwd(X, t, DY, W, A, B, s, dA, dB, need_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dA, dA1 * 2) and torch.equal(dB, dB1 * 2)
+
+
+def test_zero_b_is_plain_dequant_gemm(gpu):
+    """B = 0 (LoRA init): y equals the product with the dequantised weight; the
+    fused NF4 path and the dense path over the dequantised weight agree bitwise."""
+    T, fin, fout, r = 256, 512, 384, 16
+    x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 32.0, 3, "nf4", b_zero=True)
+    Wn = gpu.FrozenWeight.nf4(dev_bf16(w))
+    Wd = gpu.FrozenWeight.dense(gpu.nf4_dequant(Wn.codes, Wn.absmax))
+    X, A, B = dev_bf16(x), dev_bf16(a), dev_bf16(b)
+    y1, _ = gpu.lora_linear_fwd(X, Wn, A, B, s)
+    y2, _ = gpu.lora_linear_fwd(X, Wd, A, B, s)
+    y3, _ = gpu.lora_linear_fwd(X, Wn, dev_bf16(a * 0.5), B, s)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    oc, oa = O.nf4_quantize(w.astype(np.float64))
+    ref = O.round_bf16(x.astype(np.float64) @ O.nf4_dequant(oc, oa).T)
+    assert_close(host(y1), ref, "y(B=0)")
+    exact = np.mean(host(y1) == ref)
+    print("fraction bitwise equal to the float64 product rounded once:", exact)
+    assert exact > 0.95
