@@ -245,18 +245,22 @@ lsl_status lsl_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t*
 lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_heads, int32_t head_dim,
                     int32_t seq, float theta, int32_t inverse, lsl_stream stream);
 /* Causal GQA attention. q [T x ldq] (n_q heads of d), k, v [T x ldk] (n_kv heads),
- * o [T x ldo]; lse float [batch x n_q x seq]. T = batch * seq. head_dim 64 or 128. */
+ * o [T x ldo]; lse float [batch x n_q x seq]. T = batch * seq. head_dim 64 or 128,
+ * at most 8 query heads per kv head. o32 (may be NULL) receives the unrounded
+ * output as float [T x n_q d], which the backward uses for rowsum(dout * o). */
 lsl_status lsl_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              int64_t ldq, int64_t ldk, int32_t batch, int32_t seq, int32_t n_q,
                              int32_t n_kv, int32_t head_dim, uint16_t* o, int64_t ldo, float* lse,
-                             lsl_stream stream);
+                             float* o32, lsl_stream stream);
 size_t lsl_attention_workspace_bytes(int32_t batch, int32_t seq, int32_t n_q, int32_t n_kv,
                                      int32_t head_dim);
-/* Gradients of sum(do * o): dq [T x ldq], dk, dv [T x ldk] (dk, dv summed over
- * the heads of each group). */
+/* Gradients of sum(dout * o): o, dout [T x ldo]; dq [T x ldq] like q; dk, dv
+ * [T x ldk] like k (dk, dv summed over the heads of each group). o32 (may be
+ * NULL) is the forward's float output; without it rowsum(dout * o) uses o. */
 lsl_status lsl_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* o, const uint16_t* dout, const float* lse,
-                             int64_t ldq, int64_t ldk, int32_t batch, int32_t seq, int32_t n_q,
+                             const float* o32, int64_t ldq, int64_t ldk, int64_t ldo, int32_t batch,
+                             int32_t seq, int32_t n_q,
                              int32_t n_kv, int32_t head_dim, uint16_t* dq, uint16_t* dk,
                              uint16_t* dv, void* ws, size_t ws_bytes, lsl_stream stream);
 /* gu [T x 2I] = [gate | up]; a = bf16(silu(gate) * up) [T x I]. */

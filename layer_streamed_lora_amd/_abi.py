@@ -71,9 +71,9 @@ PROTOS = {
     "lsl_rmsnorm_fwd": (i32, [vp, vp, i64, i64, f32, vp, vp]),
     "lsl_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, f32, vp, vp]),
     "lsl_rope": (i32, [vp, i64, i64, i32, i32, i32, f32, i32, vp]),
-    "lsl_attention_fwd": (i32, [vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, vp, i64, vp, vp]),
+    "lsl_attention_fwd": (i32, [vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, vp, i64, vp, vp, vp]),
     "lsl_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
-    "lsl_attention_bwd": (i32, [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+    "lsl_attention_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
     "lsl_swiglu_fwd": (i32, [vp, i64, i64, vp, vp]),
     "lsl_swiglu_bwd": (i32, [vp, vp, i64, i64, vp, vp]),
     "lsl_embed_fwd": (i32, [vp, vp, i64, i64, i64, vp, vp]),

@@ -26,6 +26,7 @@ struct AttnArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
   int64_t ldq, ldk;
   const uint16_t* o; const uint16_t* dout;   // backward
+  float* o32;                                // optional float32 copy of the output [T x n_q d]
   const float* lse; const float* dsum;       // [batch][n_q][seq]
   uint16_t* out; int64_t ldo;                // forward output o, or dq
   float* lse_out; float* dsum_out;
@@ -46,6 +47,15 @@ LSL_DEV bf16x8 ld4x2(const uint16_t* p0, const uint16_t* p1) {
 }
 LSL_DEV bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
   return __builtin_bit_cast(bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])});
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits
+// through two bf16 MFMAs, used where a reduction cancels (dS in dK and dQ).
+LSL_DEV void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+  hi = pack8(a, b);
+  u32x4 h = __builtin_bit_cast(u32x4, hi);
+  f32x4 ra = f32x4{a[0] - lo_bf(h[0]), a[1] - hi_bf(h[0]), a[2] - lo_bf(h[1]), a[3] - hi_bf(h[1])};
+  f32x4 rb = f32x4{b[0] - lo_bf(h[2]), b[1] - hi_bf(h[2]), b[2] - lo_bf(h[3]), b[3] - hi_bf(h[3])};
+  lo = pack8(ra, rb);
 }
 
 // Stage rows [r0, r0+nrows) x D of a strided bf16 matrix (zero beyond `valid` rows)
@@ -71,7 +81,7 @@ LSL_DEV void stage_rows(const uint16_t* __restrict__ src, int64_t ld, int r0, in
 // ---------------------------------------------------------------- forward
 // grid (ceil(seq/32), n_kv, batch), block group*64 threads.
 template <int D>
-__global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * 72];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = blockDim.x;
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
         s[kvs][1] = mfma(kf, qf[1][ks], s[kvs][1]);
       }
     }
-    bf16x8 pf[2][2];
+    bf16x8 pf[2][2], pl[2][2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int q = q0 + qs * 16 + c16;
@@ -149,8 +159,8 @@ __global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
       for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[ds][qs][i] *= alpha;
-      pf[qs][0] = pack8(s[0][qs], s[1][qs]);
-      pf[qs][1] = pack8(s[2][qs], s[3][qs]);
+      split8(s[0][qs], s[1][qs], pf[qs][0], pl[qs][0]);
+      split8(s[2][qs], s[3][qs], pf[qs][1], pl[qs][1]);
     }
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
@@ -159,7 +169,9 @@ __global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 vf = ld4x2(vr + kk * 32 + g * 4, vr + kk * 32 + 16 + g * 4);
         o[ds][0] = mfma(vf, pf[0][kk], o[ds][0]);
+        o[ds][0] = mfma(vf, pl[0][kk], o[ds][0]);
         o[ds][1] = mfma(vf, pf[1][kk], o[ds][1]);
+        o[ds][1] = mfma(vf, pl[1][kk], o[ds][1]);
       }
     }
     __syncthreads();
@@ -176,6 +188,9 @@ __global__ __launch_bounds__(1024) void attn_fwd_kernel(const AttnArgs a) {
     for (int ds = 0; ds < D / 16; ++ds) {
       const f32x4& r = o[ds][qs];
       *reinterpret_cast<u32x2*>(op + ds * 16 + g * 4) = u32x2{pack2(r[0] * inv, r[1] * inv), pack2(r[2] * inv, r[3] * inv)};
+      if (a.o32)
+        *reinterpret_cast<f32x4*>(a.o32 + (rowbase + q) * ((int64_t)a.n_q * D) + (int64_t)h * D + ds * 16 + g * 4) =
+            f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
     }
     if (g == 0) a.lse_out[((int64_t)b * a.n_q + h) * a.seq + q] = (m[qs] + log2f(lt)) * LN2;
   }
@@ -194,9 +209,17 @@ __global__ void attn_dsum_kernel(const AttnArgs a) {
   const uint16_t* op = a.o + row * a.ldo + (int64_t)h * D;
   const uint16_t* dp = a.dout + row * a.ldo + (int64_t)h * D;
   float s = 0.f;
-  for (int c = lane * 2; c < D; c += 128) {
-    uint32_t ov = *reinterpret_cast<const uint32_t*>(op + c), dv = *reinterpret_cast<const uint32_t*>(dp + c);
-    s += lo_bf(ov) * lo_bf(dv) + hi_bf(ov) * hi_bf(dv);
+  if (a.o32) {
+    const float* o32 = a.o32 + row * ((int64_t)a.n_q * D) + (int64_t)h * D;
+    for (int c = lane * 2; c < D; c += 128) {
+      uint32_t dv = *reinterpret_cast<const uint32_t*>(dp + c);
+      s += o32[c] * lo_bf(dv) + o32[c + 1] * hi_bf(dv);
+    }
+  } else {
+    for (int c = lane * 2; c < D; c += 128) {
+      uint32_t ov = *reinterpret_cast<const uint32_t*>(op + c), dv = *reinterpret_cast<const uint32_t*>(dp + c);
+      s += lo_bf(ov) * lo_bf(dv) + hi_bf(ov) * hi_bf(dv);
+    }
   }
   s = wave_sum(s);
   if (lane == 0) {
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const AttnArgs a) {
           dp[qs] = mfma(oa, vf[ks], dp[qs]);
         }
       }
-      bf16x8 pb[2], dsb[2];
+      bf16x8 pb[2], pbl[2], dsb[2], dsl[2];
       f32x4 p[2], ds[2];
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs)
@@ -280,9 +303,9 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const AttnArgs a) {
           p[qs][i] = pv;
           ds[qs][i] = pv * (dp[qs][i] - dsum_s[ql]);
         }
-      pb[0] = pack8(p[0], p[1]);
-      dsb[0] = pack8(ds[0], ds[1]);
-      (void)pb[1]; (void)dsb[1];
+      split8(p[0], p[1], pb[0], pbl[0]);
+      split8(ds[0], ds[1], dsb[0], dsl[0]);
+      (void)pb[1]; (void)pbl[1]; (void)dsb[1]; (void)dsl[1];
       // dV^T += dO^T P ; dK^T += Q^T dS   (reduction over the 32 queries, permuted)
 #pragma unroll
       for (int dd = 0; dd < D / 16; ++dd) {
@@ -291,7 +314,9 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const AttnArgs a) {
         bf16x8 oa = ld4x2(otr + g * 4, otr + 16 + g * 4);
         bf16x8 qa = ld4x2(qtr + g * 4, qtr + 16 + g * 4);
         dv[dd] = mfma(oa, pb[0], dv[dd]);
+        dv[dd] = mfma(oa, pbl[0], dv[dd]);
         dk[dd] = mfma(qa, dsb[0], dk[dd]);
+        dk[dd] = mfma(qa, dsl[0], dk[dd]);
       }
       __syncthreads();
     }
@@ -314,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const AttnArgs a) {
 // dQ for one 32-query tile of each of the group's heads (wave = head), like the forward.
 // grid (ceil(seq/32), n_kv, batch), block group*64 threads.
 template <int D>
-__global__ __launch_bounds__(1024) void attn_dq_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(512) void attn_dq_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * (D + 8)];
   __shared__ __attribute__((aligned(16))) uint16_t Kt[D * 72];
@@ -355,7 +380,7 @@ __global__ __launch_bounds__(1024) void attn_dq_kernel(const AttnArgs a) {
     stage_rows<D>(vp, a.ldk, kv0, 64, a.seq, Vs, nullptr, tid, nthreads);
     __syncthreads();
     // S^T and dP^T: lane holds kv = kvs*16 + 4g + i, q = qs*16 + c16
-    bf16x8 dsf[2][2];
+    bf16x8 dsf[2][2], dsl[2][2];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       f32x4 s[4], dp[4];
@@ -379,8 +404,8 @@ __global__ __launch_bounds__(1024) void attn_dq_kernel(const AttnArgs a) {
           float pv = (kv <= q && kv < a.seq && q < a.seq) ? exp2f(s[kvs][i] * a.scale_log2 - lse2[qs]) : 0.f;
           s[kvs][i] = pv * (dp[kvs][i] - dsm[qs]);
         }
-      dsf[qs][0] = pack8(s[0], s[1]);
-      dsf[qs][1] = pack8(s[2], s[3]);
+      split8(s[0], s[1], dsf[qs][0], dsl[qs][0]);
+      split8(s[2], s[3], dsf[qs][1], dsl[qs][1]);
     }
     // dQ^T += K^T dS^T (reduction over 64 keys, permuted like the forward's P V)
 #pragma unroll
@@ -390,7 +415,9 @@ __global__ __launch_bounds__(1024) void attn_dq_kernel(const AttnArgs a) {
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 ka = ld4x2(kr + kk * 32 + g * 4, kr + kk * 32 + 16 + g * 4);
         dq[dd][0] = mfma(ka, dsf[0][kk], dq[dd][0]);
+        dq[dd][0] = mfma(ka, dsl[0][kk], dq[dd][0]);
         dq[dd][1] = mfma(ka, dsf[1][kk], dq[dd][1]);
+        dq[dd][1] = mfma(ka, dsl[1][kk], dq[dd][1]);
       }
     }
     __syncthreads();
@@ -414,7 +441,7 @@ static lsl_status attn_check(const char* fn, int64_t ldq, int64_t ldk, int batch
   if (batch < 0 || seq < 0 || n_q <= 0 || n_kv <= 0 || n_q % n_kv)
     return set_error(LSL_ERR_INVALID_ARG, "%s: bad head counts (n_q %% n_kv must be 0)", fn);
   if (d != 64 && d != 128) return set_error(LSL_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, d);
-  if (n_q / n_kv > 16) return set_error(LSL_ERR_UNSUPPORTED, "%s: more than 16 query heads per kv head", fn);
+  if (n_q / n_kv > 8) return set_error(LSL_ERR_UNSUPPORTED, "%s: more than 8 query heads per kv head", fn);
   if (ldq < (int64_t)n_q * d || ldk < (int64_t)n_kv * d || ldq % 8 || ldk % 8)
     return set_error(LSL_ERR_INVALID_ARG, "%s: leading dimensions too small or not multiples of 8", fn);
   return LSL_OK;
@@ -455,14 +482,15 @@ using namespace lsl;
 
 extern "C" lsl_status lsl_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ldq,
                                         int64_t ldk, int32_t batch, int32_t seq, int32_t n_q, int32_t n_kv,
-                                        int32_t head_dim, uint16_t* o, int64_t ldo, float* lse, lsl_stream stream) {
+                                        int32_t head_dim, uint16_t* o, int64_t ldo, float* lse, float* o32,
+                                        lsl_stream stream) {
   const char* fn = "lsl_attention_fwd";
   LSL_TRY(attn_check(fn, ldq, ldk, batch, seq, n_q, n_kv, head_dim));
   if (ldo < (int64_t)n_q * head_dim || ldo % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad ldo", fn);
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {q, k, v, o, lse}));
   AttnArgs a{};
-  a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.out = o; a.ldo = ldo; a.lse_out = lse;
+  a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk; a.out = o; a.ldo = ldo; a.lse_out = lse; a.o32 = o32;
   a.batch = batch; a.seq = seq; a.n_q = n_q; a.n_kv = n_kv; a.group = n_q / n_kv;
   a.scale = 1.0f / sqrtf((float)head_dim);
   a.scale_log2 = a.scale * LOG2E;
@@ -475,18 +503,20 @@ extern "C" size_t lsl_attention_workspace_bytes(int32_t batch, int32_t seq, int3
 }
 
 extern "C" lsl_status lsl_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-                                        const uint16_t* dout, const float* lse, int64_t ldq, int64_t ldk, int32_t batch,
-                                        int32_t seq, int32_t n_q, int32_t n_kv, int32_t head_dim, uint16_t* dq,
-                                        uint16_t* dk, uint16_t* dv, void* ws, size_t ws_bytes, lsl_stream stream) {
+                                        const uint16_t* dout, const float* lse, const float* o32, int64_t ldq,
+                                        int64_t ldk, int64_t ldo, int32_t batch, int32_t seq, int32_t n_q,
+                                        int32_t n_kv, int32_t head_dim, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                                        void* ws, size_t ws_bytes, lsl_stream stream) {
   const char* fn = "lsl_attention_bwd";
   LSL_TRY(attn_check(fn, ldq, ldk, batch, seq, n_q, n_kv, head_dim));
+  if (ldo < (int64_t)n_q * head_dim || ldo % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad ldo", fn);
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {q, k, v, o, dout, lse, dq, dk, dv}));
   size_t need = attention_ws_bytes(batch, seq, n_q);
   if (!ws || ws_bytes < need) return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, need);
   AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk;
-  a.o = o; a.dout = dout; a.ldo = ldq; a.lse = lse; a.dsum_out = (float*)ws;
+  a.o = o; a.dout = dout; a.ldo = ldo; a.lse = lse; a.dsum_out = (float*)ws; a.o32 = (float*)o32;
   a.out = dq; a.dk = dk; a.dv = dv;
   a.batch = batch; a.seq = seq; a.n_q = n_q; a.n_kv = n_kv; a.group = n_q / n_kv;
   a.scale = 1.0f / sqrtf((float)head_dim);

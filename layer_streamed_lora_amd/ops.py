@@ -182,25 +182,29 @@ def adamw_step(p, p_bf16, g, m, v, step, lr=2e-4, beta1=0.9, beta2=0.999, eps=1e
                                                   beta1, beta2, eps, weight_decay, _s(stream)))
 
 
-def attention_fwd(q, k, v, batch, seq, n_q, n_kv, head_dim, stream=None):
-    """q [T x ldq], k, v [T x ldk] views with unit column stride -> (o [T x n_q d], lse [batch x n_q x seq])."""
+def attention_fwd(q, k, v, batch, seq, n_q, n_kv, head_dim, want_o32=False, stream=None):
+    """q [T x ldq], k, v [T x ldk] views with unit column stride -> (o [T x n_q d], lse [batch x n_q x seq], o32)."""
     T = batch * seq
     o = torch.empty((T, n_q * head_dim), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((batch, n_q, seq), dtype=torch.float32, device=q.device)
+    o32 = torch.empty((T, n_q * head_dim), dtype=torch.float32, device=q.device) if want_o32 else None
     _check("lsl_attention_fwd", lib().lsl_attention_fwd(_p(q), _p(k), _p(v), q.stride(0), k.stride(0), batch, seq,
-                                                        n_q, n_kv, head_dim, _p(o), o.stride(0), _p(lse), _s(stream)))
-    return o, lse
+                                                        n_q, n_kv, head_dim, _p(o), o.stride(0), _p(lse), _p(o32),
+                                                        _s(stream)))
+    return o, lse, o32
 
 
-def attention_bwd(q, k, v, o, do, lse, batch, seq, n_q, n_kv, head_dim, stream=None):
+def attention_bwd(q, k, v, o, do, lse, batch, seq, n_q, n_kv, head_dim, o32=None, stream=None):
     T = batch * seq
     dq = torch.empty((T, n_q * head_dim), dtype=torch.bfloat16, device=q.device)
     dk = torch.empty((T, n_kv * head_dim), dtype=torch.bfloat16, device=q.device)
     dv = torch.empty((T, n_kv * head_dim), dtype=torch.bfloat16, device=q.device)
     ws = _ws(lib().lsl_attention_workspace_bytes(batch, seq, n_q, n_kv, head_dim), q.device)
-    if q.stride(0) != dq.stride(0) or k.stride(0) != dk.stride(0):
+    if q.stride(0) != dq.stride(0) or k.stride(0) != dk.stride(0) or o.stride(0) != do.stride(0):
         raise ValueError("attention_bwd: q/k must be densely packed for this wrapper")
-    _check("lsl_attention_bwd", lib().lsl_attention_bwd(_p(q), _p(k), _p(v), _p(o), _p(do), _p(lse), q.stride(0),
-                                                        k.stride(0), batch, seq, n_q, n_kv, head_dim, _p(dq), _p(dk),
+    _check("lsl_attention_bwd", lib().lsl_attention_bwd(_p(q), _p(k), _p(v), _p(o), _p(do), _p(lse), _p(o32),
+                                                        q.stride(0),
+                                                        k.stride(0), o.stride(0), batch, seq, n_q, n_kv, head_dim,
+                                                        _p(dq), _p(dk),
                                                         _p(dv), _p(ws), ws.numel(), _s(stream)))
     return dq, dk, dv

@@ -38,3 +38,32 @@ def assert_close(got, ref, name="", atol=ATOL, rtol=RTOL):
     assert not bad.any(), msg
     assert np.all(np.isfinite(got)), name + ": non-finite values"
     return fro
+
+
+# Outputs of a chain of several bf16 rounding points (a whole decoder layer or
+# model) cannot meet the per-element bound for every element: a one-ulp flip at
+# an intermediate rounding point propagates. Two CPU evaluations of the Llama-8B
+# layer that differ only in matmul accumulation (float32 vs float64) already put
+# 0.23% of the layer outputs outside the per-element bound, with a largest error
+# of 4.6% of the tensor RMS. For such outputs the bound is read normwise
+# (relative Frobenius error <= RTOL) together with a per-element bound whose
+# absolute term is CHAIN_ABS_RMS times the tensor RMS (about twice the spread
+# between those two faithful evaluations).
+CHAIN_ABS_RMS = 0.1
+
+
+def assert_close_chain(got, ref, name=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), name + ": non-finite values"
+    err = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+    frac = float(np.mean(err > ATOL + RTOL * np.abs(ref)))
+    fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    worst = float(np.max(err / (RTOL * np.abs(ref) + CHAIN_ABS_RMS * rms)))
+    msg = (f"{name}: rel Frobenius err {fro:.3g}, {frac:.2%} outside the per-element bound, "
+           f"max err {err.max():.3g} = {err.max() / rms:.3g} x RMS, chain-bound ratio {worst:.3g}")
+    print(msg)
+    assert fro <= RTOL and worst <= 1.0, msg
+    return fro

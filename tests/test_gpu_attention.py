@@ -1,0 +1,54 @@
+"""GPU parity of causal GQA attention forward/backward against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import dev_bf16, host, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("batch,seq,nq,nkv,d", [
+    (2, 77, 8, 2, 128),     # ragged sequence, two sequences
+    (1, 128, 4, 1, 64),
+    (2, 64, 7, 1, 64),      # group of 7 (Qwen2.5-0.5B: 14 q / 2 kv heads)
+    (1, 96, 8, 1, 128),     # group of 8 (Qwen2.5-3B: 16 q / 2 kv heads)
+    (1, 512, 32, 8, 128),   # one Llama-3.1-8B layer at seq 512
+    (3, 1, 4, 2, 64),       # one token per sequence
+])
+def test_attention_parity(gpu, batch, seq, nq, nkv, d):
+    T = batch * seq
+    q = synth.activation((T, nq * d), 20 + d, "x", std=1.2)
+    k = synth.activation((T, nkv * d), 20 + d, "x", salt=1, std=1.2)
+    v = synth.activation((T, nkv * d), 20 + d, "x", salt=2)
+    do = synth.activation((T, nq * d), 20 + d, "dy")
+    qd, kd, vd, dod = (a.astype(np.float64) for a in (q, k, v, do))
+    o_ref, lse_ref = O.attention_fwd(qd.reshape(T, nq, d), kd.reshape(T, nkv, d), vd.reshape(T, nkv, d), batch, seq)
+    dq_ref, dk_ref, dv_ref = O.attention_bwd(qd.reshape(T, nq, d), kd.reshape(T, nkv, d), vd.reshape(T, nkv, d),
+                                             dod.reshape(T, nq, d), batch, seq)
+    Q, K, V, DO = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(do)
+    o, lse, o32 = gpu.attention_fwd(Q, K, V, batch, seq, nq, nkv, d, want_o32=True)
+    dq, dk, dv = gpu.attention_bwd(Q, K, V, o, DO, lse, batch, seq, nq, nkv, d, o32=o32)
+    torch.cuda.synchronize()
+    assert_close(host(o), o_ref.reshape(T, -1), "attn o")
+    assert np.allclose(host(lse), lse_ref, rtol=1e-5, atol=1e-5), np.abs(host(lse) - lse_ref).max()
+    assert_close(host(dq), dq_ref.reshape(T, -1), "attn dq")
+    assert_close(host(dk), dk_ref.reshape(T, -1), "attn dk")
+    assert_close(host(dv), dv_ref.reshape(T, -1), "attn dv")
+
+
+def test_attention_strided_views(gpu):
+    """q, k, v as column slices of one fused qkv row (the layout the layer uses)."""
+    batch, seq, nq, nkv, d = 1, 80, 4, 2, 64
+    T, W = batch * seq, (nq + 2 * nkv) * d
+    qkv = synth.activation((T, W), 31, "x")
+    X = dev_bf16(qkv)
+    Q, K, V = X[:, : nq * d], X[:, nq * d:(nq + nkv) * d], X[:, (nq + nkv) * d:]
+    o, lse, _ = gpu.attention_fwd(Q, K, V, batch, seq, nq, nkv, d)
+    torch.cuda.synchronize()
+    qd = qkv.astype(np.float64)
+    o_ref, _ = O.attention_fwd(qd[:, : nq * d].reshape(T, nq, d), qd[:, nq * d:(nq + nkv) * d].reshape(T, nkv, d),
+                               qd[:, (nq + nkv) * d:].reshape(T, nkv, d), batch, seq)
+    assert_close(host(o), o_ref.reshape(T, -1), "attn o (strided)")

@@ -1,0 +1,104 @@
+"""GPU parity of the whole decoder layer (forward, and backward with recompute)
+against the oracle, plus the determinism properties streaming relies on."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth.configs import SMALL_LAYER_NF4, SMALL_LAYER_BF16, LLAMA8B_LAYER, PROJ_IN_OUT
+from tests.gpu_util import dev_bf16, host, assert_close, assert_close_chain
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(gpu, shape, batch, seq, wid, ones_norm=False):
+    from layer_streamed_lora_amd import model as M
+    T = batch * seq
+    w = synth.layer_weights(shape, wid, 0, ones_norm=ones_norm)
+    lora = synth.layer_lora(shape, wid, 0)
+    x = synth.activation((T, shape.hidden), wid, "x")
+    dy = synth.activation((T, shape.hidden), wid, "dy")
+    cfg = M.layer_cfg(shape)
+    L = M.layer_layout(cfg)
+    blob = torch.zeros(L.total_bytes, dtype=torch.uint8, device="cuda")
+    M.write_layer_blob(shape, cfg, blob, {k: dev_bf16(v) for k, v in w.items()})
+    lp = M.LoraParams(shape, 1)
+    lp.set_from(0, lora)
+    return M, cfg, blob, lp, w, lora, x, dy
+
+
+def _oracle(shape, w, lora, x, dy, batch, seq):
+    wd = {}
+    for p in PROJ_IN_OUT(shape):
+        if shape.wfmt == "nf4":
+            c, a = O.nf4_quantize(w[p].astype(np.float64))
+            wd[p] = O.nf4_dequant(c, a)
+        else:
+            wd[p] = w[p].astype(np.float64)
+    wd["norm1"], wd["norm2"] = w["norm1"].astype(np.float64), w["norm2"].astype(np.float64)
+    ld = {k: v.astype(np.float64) for k, v in lora.items()}
+    xd, dyd = x.astype(np.float64), dy.astype(np.float64)
+    out, _ = O.decoder_layer_fwd(xd, wd, ld, shape, batch, seq)
+    dx, gr = O.decoder_layer_bwd(xd, dyd, wd, ld, shape, batch, seq)
+    return out, dx, gr
+
+
+def _run_and_compare(gpu, shape, batch, seq, wid):
+    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, wid)
+    X, DY = dev_bf16(x), dev_bf16(dy)
+    out = M.decoder_layer_fwd(cfg, blob, lp.lora_set(0), X, batch, seq)
+    dx = M.decoder_layer_bwd(cfg, blob, lp.lora_set(0), X, DY, batch, seq, lp.lora_grads(0))
+    torch.cuda.synchronize()
+    out_ref, dx_ref, gr_ref = _oracle(shape, w, lora, x, dy, batch, seq)
+    assert_close_chain(host(out), out_ref, "layer out")
+    assert_close_chain(host(dx), dx_ref, "layer dx")
+    got = lp.grads_np(0)
+    for k in gr_ref:
+        assert_close_chain(got[k], gr_ref[k], "grad " + k)
+    return M, cfg, blob, lp, X, DY, out, dx
+
+
+@pytest.mark.parametrize("shape,batch,seq", [
+    (SMALL_LAYER_NF4, 2, 40),     # NF4, two sequences, partial tiles everywhere
+    (SMALL_LAYER_BF16, 1, 150),   # bf16 base, group of 3, rank 8
+])
+def test_layer_parity_small(gpu, shape, batch, seq):
+    _run_and_compare(gpu, shape, batch, seq, 41)
+
+
+@pytest.mark.timeout(900)
+def test_layer_parity_llama8b_seq512(gpu):
+    """One Llama-3.1-8B-shaped NF4 layer, batch 1 x seq 512, every output and gradient."""
+    _run_and_compare(gpu, LLAMA8B_LAYER, 1, 512, 2)
+
+
+def test_layer_deterministic_and_address_independent(gpu):
+    """Same bits from a second run and from a copy of the blob at another address
+    (a streamed slot vs a resident copy)."""
+    shape, batch, seq = SMALL_LAYER_NF4, 1, 96
+    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 43)
+    X, DY = dev_bf16(x), dev_bf16(dy)
+    other = torch.empty(blob.numel() + 4096, dtype=torch.uint8, device="cuda")[1024:1024 + blob.numel()]
+    other.copy_(blob)
+    outs, dxs, grads = [], [], []
+    for b in (blob, blob, other):
+        lp.grad.zero_()
+        outs.append(M.decoder_layer_fwd(cfg, b, lp.lora_set(0), X, batch, seq))
+        dxs.append(M.decoder_layer_bwd(cfg, b, lp.lora_set(0), X, DY, batch, seq, lp.lora_grads(0)))
+        grads.append(lp.grad.clone())
+    torch.cuda.synchronize()
+    for i in (1, 2):
+        assert torch.equal(outs[0], outs[i]) and torch.equal(dxs[0], dxs[i]) and torch.equal(grads[0], grads[i])
+
+
+def test_layer_zero_b_gives_zero_dA(gpu):
+    shape, batch, seq = SMALL_LAYER_BF16, 1, 64
+    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 44)
+    for i in range(4):
+        lp.view(lp.bf16, 0, i, "B").zero_()
+    M.decoder_layer_bwd(cfg, blob, lp.lora_set(0), dev_bf16(x), dev_bf16(dy), batch, seq, lp.lora_grads(0))
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.count_nonzero(lp.view(lp.grad, 0, i, "A")) == 0
+        assert torch.count_nonzero(lp.view(lp.grad, 0, i, "B")) > 0
