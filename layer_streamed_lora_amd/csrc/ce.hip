@@ -1,0 +1,178 @@
+// Fused, vocabulary-chunked token cross-entropy (forward and backward).
+//
+// The pages measure what the naive logits term costs (bytes per logit element,
+// "Exact Layer Streaming ...", abstract); here no [T x V] logits tensor is ever
+// written. Forward: one MFMA GEMM pass z = hN W^T whose epilogue reduces every
+// 128-wide vocabulary tile to a (max, sum exp) pair per token and picks the
+// label logit; a second kernel merges the tile pairs in index order into the
+// log-sum-exp, and a single workgroup sums the loss in a fixed order.
+// Backward: per vocabulary chunk, the GEMM recomputes z and writes
+// G = s (softmax - onehot) for that chunk only (hi + lo bf16, L2/MALL resident),
+// then dH += G W_chunk accumulates in float32 across chunks in chunk order.
+#include "common.h"
+#include "gemm.h"
+#include "api_util.h"
+
+namespace lsl {
+
+constexpr int64_t CE_CHUNK = 8192;  // vocabulary columns per backward chunk
+
+struct CePlan {
+  size_t nvalid, part, zlab, lossv, g, dh32, total;
+};
+
+static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
+  CePlan p{};
+  size_t off = 0;
+  auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
+  p.nvalid = take(4);
+  size_t common = off;
+  int64_t ntiles = (V + 127) / 128;
+  p.part = take((size_t)ntiles * T * 8);
+  p.zlab = take((size_t)T * 4);
+  p.lossv = take((size_t)T * 4);
+  size_t fwd_end = off;
+  off = common;
+  int64_t vc = V < CE_CHUNK ? V : CE_CHUNK;
+  p.g = take((size_t)T * 2 * vc * 2);
+  p.dh32 = take((size_t)T * H * 4);
+  p.total = std::max(fwd_end, off);
+  return p;
+}
+
+__global__ void ce_count_valid_kernel(const int32_t* __restrict__ labels, int64_t T, int ignore, int64_t V,
+                                      float* __restrict__ nvalid) {
+  __shared__ int cnt[256];
+  int c = 0;
+  for (int64_t t = threadIdx.x; t < T; t += 256) {
+    int l = labels[t];
+    c += (l != ignore && l >= 0 && l < V) ? 1 : 0;
+  }
+  cnt[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) cnt[threadIdx.x] += cnt[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *nvalid = (float)cnt[0];
+}
+
+// lse[t] = log sum over tiles (merged in tile order); lossv[t] = lse - z_label (0 if ignored)
+__global__ void ce_lse_kernel(const float2* __restrict__ part, int64_t ntiles, int64_t T,
+                              const int32_t* __restrict__ labels, const float* __restrict__ zlab, int ignore,
+                              int64_t V, float* __restrict__ lse, float* __restrict__ lossv) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float mx = -INFINITY;
+  for (int64_t i = 0; i < ntiles; ++i) mx = fmaxf(mx, part[i * T + t].x);
+  float s = 0.f;
+  for (int64_t i = 0; i < ntiles; ++i) {
+    float2 p = part[i * T + t];
+    if (p.x != -INFINITY) s += p.y * expf(p.x - mx);
+  }
+  float l = mx + logf(s);
+  lse[t] = l;
+  int lab = labels[t];
+  lossv[t] = (lab != ignore && lab >= 0 && lab < V) ? l - zlab[t] : 0.f;
+}
+
+// loss = sum(lossv) / nvalid, one workgroup, fixed summation order
+__global__ void ce_loss_kernel(const float* __restrict__ lossv, int64_t T, const float* __restrict__ nvalid,
+                               float* __restrict__ loss) {
+  __shared__ float acc[256];
+  float s = 0.f;
+  for (int64_t t = threadIdx.x; t < T; t += 256) s += lossv[t];
+  acc[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) acc[threadIdx.x] += acc[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = *nvalid > 0.f ? acc[0] / *nvalid : 0.f;
+}
+
+static lsl_status ce_check(const char* fn, int64_t T, int64_t H, int64_t V) {
+  if (T < 0 || H <= 0 || V <= 0) return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (H % 64 || V % 64) return set_error(LSL_ERR_UNSUPPORTED, "%s: hidden and vocab must be multiples of 64", fn);
+  if (V > (int64_t)1 << 31) return set_error(LSL_ERR_UNSUPPORTED, "%s: vocab too large", fn);
+  return LSL_OK;
+}
+
+}  // namespace lsl
+
+using namespace lsl;
+
+extern "C" size_t lsl_ce_workspace_bytes(int64_t T, int64_t H, int64_t V) {
+  if (ce_check("lsl_ce_workspace_bytes", T, H, V) != LSL_OK) return 0;
+  return ce_plan(T, H, V).total;
+}
+
+extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm, const int32_t* labels, int64_t T,
+                                        int64_t H, int64_t V, int32_t ignore_index, float* loss, float* lse, void* ws,
+                                        size_t ws_bytes, lsl_stream stream) {
+  const char* fn = "fused_ce_loss_fwd";
+  LSL_TRY(ce_check(fn, T, H, V));
+  LSL_TRY(check_ptrs(fn, {w_lm, loss}));
+  CePlan p = ce_plan(T, H, V);
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256))
+    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, p.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* nvalid = (float*)(w + p.nvalid);
+  if (T == 0) {
+    hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(256), 0, s, (const float*)nullptr, (int64_t)0,
+                       (const float*)nvalid, loss);
+    return check_launch(fn);
+  }
+  LSL_TRY(check_ptrs(fn, {hN, labels, lse}));
+  hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
+  GemmDesc g;
+  g.x = hN; g.ldx = H; g.wfmt = LSL_WFMT_BF16; g.wb = w_lm; g.M = T; g.N = V; g.K = H;
+  g.epi = 1; g.labels = labels; g.part = w + p.part; g.zlab = (float*)(w + p.zlab); g.ignore = ignore_index;
+  g.vocab = V;
+  LSL_TRY(gemm_launch(g, s));
+  int64_t ntiles = (V + 127) / 128;
+  hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, (const float2*)(w + p.part),
+                     ntiles, T, labels, (const float*)(w + p.zlab), ignore_index, V, lse, (float*)(w + p.lossv));
+  hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(256), 0, s, (const float*)(w + p.lossv), T, (const float*)nvalid,
+                     loss);
+  return check_launch(fn);
+}
+
+extern "C" lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm, const int32_t* labels,
+                                        const float* lse, int64_t T, int64_t H, int64_t V, int32_t ignore_index,
+                                        float grad_scale, uint16_t* dhN, void* ws, size_t ws_bytes,
+                                        lsl_stream stream) {
+  const char* fn = "fused_ce_loss_bwd";
+  LSL_TRY(ce_check(fn, T, H, V));
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {hN, w_lm, labels, lse, dhN}));
+  CePlan p = ce_plan(T, H, V);
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256))
+    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, p.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* nvalid = (float*)(w + p.nvalid);
+  hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
+  uint16_t* G = (uint16_t*)(w + p.g);
+  float* dh32 = (float*)(w + p.dh32);
+  const int64_t nchunks = (V + CE_CHUNK - 1) / CE_CHUNK;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t v0 = c * CE_CHUNK;
+    const int64_t vc = std::min(CE_CHUNK, V - v0);
+    const uint16_t* wc = w_lm + v0 * H;
+    GemmDesc g1;
+    g1.x = hN; g1.ldx = H; g1.wfmt = LSL_WFMT_BF16; g1.wb = wc; g1.M = T; g1.N = vc; g1.K = H;
+    g1.epi = 2; g1.labels = labels; g1.lse = lse; g1.nvalid = nvalid; g1.gscale = grad_scale;
+    g1.ignore = ignore_index; g1.vocab_off = v0; g1.vocab = V;
+    g1.y = G; g1.y2 = G + vc; g1.ldy = 2 * vc;
+    LSL_TRY(gemm_launch(g1, s));
+    GemmDesc g2;
+    g2.x = G; g2.ldx = 2 * vc; g2.wfmt = LSL_WFMT_BF16; g2.kn = true; g2.wb = wc; g2.kwrap = vc;
+    g2.M = T; g2.N = H; g2.K = 2 * vc;
+    g2.epi = 3; g2.out32 = dh32; g2.ldo32 = H; g2.first = c == 0 ? 1 : 0;
+    g2.y = c == nchunks - 1 ? dhN : nullptr; g2.ldy = H;
+    LSL_TRY(gemm_launch(g2, s));
+  }
+  return LSL_OK;
+}

@@ -13,6 +13,15 @@ struct GemmDesc {
   float scale = 0.f;
   uint16_t* y = nullptr; int64_t ldy = 0;
   const uint16_t* res = nullptr; int64_t ldres = 0;
+  // epilogue selection: 0 bf16 store (+ residual); 1 cross-entropy max/sum-exp
+  // partials; 2 cross-entropy gradient chunk (hi into y, lo into y2);
+  // 3 float accumulate into out32 (bf16 copy into y when y != NULL)
+  int epi = 0;
+  const int32_t* labels = nullptr; const float* lse = nullptr; const float* nvalid = nullptr;
+  void* part = nullptr; float* zlab = nullptr; uint16_t* y2 = nullptr;
+  float gscale = 1.f; int ignore = -100; int64_t vocab_off = 0, vocab = 0;
+  float* out32 = nullptr; int64_t ldo32 = 0; int first = 1;
+  int64_t kwrap = 0;
 };
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
 }  // namespace lsl

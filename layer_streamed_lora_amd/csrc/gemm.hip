@@ -40,7 +40,16 @@ struct GemmKArgs {
   const uint16_t* res; int64_t ldres;
   int tiles_m, tiles_n;
   float cb[16];
+  // cross-entropy epilogues
+  const int32_t* labels; const float* lse; const float* nvalid;
+  float2* part; float* zlab;
+  uint16_t* y2;              // low half of the hi + lo gradient pair
+  float gscale; int ignore; int64_t vocab_off, vocab;
+  float* out32; int64_t ldo32; int first;
+  int64_t kwrap;             // KN operand: reduction index k reads weight row k mod kwrap
 };
+
+enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_CEGRAD = 2, EPI_ACC32 = 3 };
 
 template <int WFMT, bool KN>
 struct WLoader;
@@ -125,6 +134,7 @@ struct WLoader<LSL_WFMT_BF16, true> {
   LSL_DEV void load(const GemmKArgs& a, int64_t n0, int64_t k0, int tid) {
     int q = tid >> 4, o = tid & 15;
     int64_t n = n0 + o * 8;
+    if (a.kwrap) k0 %= a.kwrap;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       u32x4 v = n < a.N ? *reinterpret_cast<const u32x4*>(a.wb + (k0 + q * 4 + rr) * a.N + n) : u32x4{0, 0, 0, 0};
@@ -198,7 +208,7 @@ LSL_DEV void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   tm = t - tn * tiles_m;
 }
 
-template <int WFMT, bool KN, int LORA>
+template <int WFMT, bool KN, int LORA, int EPI>
 __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDSW];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM * LDSW];
@@ -294,6 +304,55 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
   }
 
   // ---- epilogue: lane holds C[m][n..n+3]
+  if constexpr (EPI == EPI_LSE) {
+    // Cross-entropy forward: per token m, max and sum of exp over this tile's
+    // vocabulary entries n < N, and the label's logit if it falls in the tile.
+    float2* red = reinterpret_cast<float2*>(Xs[0]);  // [2 (wn)][128 (m)]
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
+      const int lab = m < a.M ? a.labels[m] : -1;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < a.N) {
+            mx = fmaxf(mx, acc[ni][mi][e]);
+            if (n + e == lab) a.zlab[m] = acc[ni][mi][e];
+          }
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float sm = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.N) sm += expf(acc[ni][mi][e] - mx);
+        }
+      }
+      sm += __shfl_xor(sm, 16, 64);
+      sm += __shfl_xor(sm, 32, 64);
+      if ((lane >> 4) == 0) red[wn * BM + wm * 64 + mi * 16 + (lane & 15)] = make_float2(mx, sm);
+    }
+    __syncthreads();
+    if (tid < BM && m0 + tid < a.M) {
+      float2 p0 = red[tid], p1 = red[BM + tid];
+      float mx = fmaxf(p0.x, p1.x);
+      float sm = 0.f;
+      if (mx != -INFINITY) {
+        if (p0.x != -INFINITY) sm += p0.y * expf(p0.x - mx);
+        if (p1.x != -INFINITY) sm += p1.y * expf(p1.x - mx);
+      }
+      a.part[(int64_t)tn * a.M + m0 + tid] = make_float2(mx, sm);
+    }
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
@@ -303,23 +362,47 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
       const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
       if (m >= a.M) continue;
       float v0 = acc[ni][mi][0], v1 = acc[ni][mi][1], v2 = acc[ni][mi][2], v3 = acc[ni][mi][3];
-      if (a.res) {
-        u32x2 r = *reinterpret_cast<const u32x2*>(a.res + m * a.ldres + n);
-        v0 = bf2f(f2bf(v0)) + lo_bf(r[0]);
-        v1 = bf2f(f2bf(v1)) + hi_bf(r[0]);
-        v2 = bf2f(f2bf(v2)) + lo_bf(r[1]);
-        v3 = bf2f(f2bf(v3)) + hi_bf(r[1]);
+      if constexpr (EPI == EPI_CEGRAD) {
+        // G = coef * (softmax - onehot) for this vocabulary chunk, as a hi + lo
+        // pair of bf16 matrices (about 16 significant bits for the dH product)
+        const int lab = a.labels[m];
+        const float nv = *a.nvalid;
+        const bool valid = lab != a.ignore && lab >= 0 && lab < a.vocab;
+        const float coef = (valid && nv > 0.f) ? a.gscale / nv : 0.f;
+        const float l = a.lse[m];
+        const int64_t nl = n + a.vocab_off;
+        float g[4] = {v0, v1, v2, v3};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) g[e] = coef * (expf(g[e] - l) - (nl + e == lab ? 1.f : 0.f));
+        const uint32_t h0 = pack2(g[0], g[1]), h1 = pack2(g[2], g[3]);
+        *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(a.y2 + m * a.ldy + n) =
+            u32x2{pack2(g[0] - lo_bf(h0), g[1] - hi_bf(h0)), pack2(g[2] - lo_bf(h1), g[3] - hi_bf(h1))};
+      } else if constexpr (EPI == EPI_ACC32) {
+        float* o = a.out32 + m * a.ldo32 + n;
+        f32x4 prev = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(o);
+        f32x4 r = f32x4{prev[0] + v0, prev[1] + v1, prev[2] + v2, prev[3] + v3};
+        *reinterpret_cast<f32x4*>(o) = r;
+        if (a.y) *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
+      } else {
+        if (a.res) {
+          u32x2 r = *reinterpret_cast<const u32x2*>(a.res + m * a.ldres + n);
+          v0 = bf2f(f2bf(v0)) + lo_bf(r[0]);
+          v1 = bf2f(f2bf(v1)) + hi_bf(r[0]);
+          v2 = bf2f(f2bf(v2)) + lo_bf(r[1]);
+          v3 = bf2f(f2bf(v3)) + hi_bf(r[1]);
+        }
+        *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(v0, v1), pack2(v2, v3)};
       }
-      *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(v0, v1), pack2(v2, v3)};
     }
   }
 }
 
 template <int WFMT, bool KN>
 static void launch_lora_variant(const GemmKArgs& a, int lora, hipStream_t s, dim3 grid) {
-  if (lora == 0) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 0>), grid, dim3(NTHREADS), 0, s, a);
-  else if (lora == 1) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 1>), grid, dim3(NTHREADS), 0, s, a);
-  else hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 2>), grid, dim3(NTHREADS), 0, s, a);
+  if (lora == 0) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 0, EPI_BF16>), grid, dim3(NTHREADS), 0, s, a);
+  else if (lora == 1) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 1, EPI_BF16>), grid, dim3(NTHREADS), 0, s, a);
+  else hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 2, EPI_BF16>), grid, dim3(NTHREADS), 0, s, a);
 }
 
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
@@ -343,7 +426,18 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   a.tiles_n = (int)((d.N + BN - 1) / BN);
   const Nf4Table& t = nf4_table();
   for (int i = 0; i < 16; ++i) a.cb[i] = t.cb[i];
+  a.labels = d.labels; a.lse = d.lse; a.nvalid = d.nvalid; a.part = (float2*)d.part; a.zlab = d.zlab;
+  a.y2 = d.y2; a.gscale = d.gscale; a.ignore = d.ignore; a.vocab_off = d.vocab_off; a.vocab = d.vocab;
+  a.out32 = d.out32; a.ldo32 = d.ldo32; a.first = d.first; a.kwrap = d.kwrap;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  if (d.epi != EPI_BF16) {
+    if (d.wfmt != LSL_WFMT_BF16 || d.lora) return set_error(LSL_ERR_UNSUPPORTED, "gemm: CE epilogues take a bf16 weight");
+    if (d.epi == EPI_LSE && !d.kn) hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, false, 0, EPI_LSE>), grid, dim3(NTHREADS), 0, s, a);
+    else if (d.epi == EPI_CEGRAD && !d.kn) hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, false, 0, EPI_CEGRAD>), grid, dim3(NTHREADS), 0, s, a);
+    else if (d.epi == EPI_ACC32 && d.kn) hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, true, 0, EPI_ACC32>), grid, dim3(NTHREADS), 0, s, a);
+    else return set_error(LSL_ERR_UNSUPPORTED, "gemm: epilogue %d with layout %d", d.epi, (int)d.kn);
+    return check_launch("gemm(ce)");
+  }
   if (d.wfmt == LSL_WFMT_NF4) {
     if (d.kn) launch_lora_variant<LSL_WFMT_NF4, true>(a, d.lora, s, grid);
     else launch_lora_variant<LSL_WFMT_NF4, false>(a, d.lora, s, grid);

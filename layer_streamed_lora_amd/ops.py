@@ -208,3 +208,32 @@ def attention_bwd(q, k, v, o, do, lse, batch, seq, n_q, n_kv, head_dim, o32=None
                                                         _p(dq), _p(dk),
                                                         _p(dv), _p(ws), ws.numel(), _s(stream)))
     return dq, dk, dv
+
+
+# ------------------------------------------------------------------ cross-entropy
+def ce_workspace_bytes(T, H, V):
+    return lib().lsl_ce_workspace_bytes(T, H, V)
+
+
+def fused_ce_loss_fwd(hN, w_lm, labels, ignore_index=-100, ws=None, stream=None):
+    """-> (loss float32 [1] on device, lse float32 [T])."""
+    T, H = hN.shape
+    V = w_lm.shape[0]
+    loss = torch.empty(1, dtype=torch.float32, device=hN.device)
+    lse = torch.empty(T, dtype=torch.float32, device=hN.device)
+    if ws is None:
+        ws = _ws(ce_workspace_bytes(T, H, V), hN.device)
+    _check("fused_ce_loss_fwd", lib().fused_ce_loss_fwd(_p(hN), _p(w_lm), _p(labels), T, H, V, ignore_index, _p(loss),
+                                                        _p(lse), _p(ws), ws.numel(), _s(stream)))
+    return loss, lse
+
+
+def fused_ce_loss_bwd(hN, w_lm, labels, lse, grad_scale=1.0, ignore_index=-100, ws=None, out=None, stream=None):
+    T, H = hN.shape
+    V = w_lm.shape[0]
+    dh = torch.empty_like(hN) if out is None else out
+    if ws is None:
+        ws = _ws(ce_workspace_bytes(T, H, V), hN.device)
+    _check("fused_ce_loss_bwd", lib().fused_ce_loss_bwd(_p(hN), _p(w_lm), _p(labels), _p(lse), T, H, V, ignore_index,
+                                                        grad_scale, _p(dh), _p(ws), ws.numel(), _s(stream)))
+    return dh

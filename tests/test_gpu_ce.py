@@ -1,0 +1,90 @@
+"""GPU parity of the fused, vocabulary-chunked cross-entropy against the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.gpu_util import dev_bf16, dev, host, assert_close, assert_close_chain
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(T, H, V, wid, n_ignore=3):
+    h = synth.activation((T, H), wid, "x")
+    w = synth.normal_bf16((V, H), 0.05, wid, 1000, 52)
+    labels = synth.token_ids(T, V, wid).astype(np.int64)
+    labels[np.arange(n_ignore) * 7 % T] = -100
+    return h, w, labels
+
+
+@pytest.mark.parametrize("T,H,V,gs", [
+    (100, 128, 16576, 1.0),     # three vocabulary chunks, the last one partial; ragged T
+    (37, 256, 1088, 0.25),      # one chunk with a partial vocabulary tile, a gradient scale
+    (1, 64, 64, 1.0),
+])
+def test_ce_parity(gpu, T, H, V, gs):
+    h, w, labels = _case(T, H, V, 50 + T)
+    hd, wd = h.astype(np.float64), w.astype(np.float64)
+    loss_ref, lse_ref, nv = O.ce_loss_fwd(hd, wd, labels)
+    dh_ref = O.ce_loss_bwd(hd, wd, labels, grad_scale=gs)
+    Hh, W, L = dev_bf16(h), dev_bf16(w), dev(labels.astype(np.int32))
+    loss, lse = gpu.fused_ce_loss_fwd(Hh, W, L)
+    dh = gpu.fused_ce_loss_bwd(Hh, W, L, lse, grad_scale=gs)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - loss_ref) <= 1e-5 * abs(loss_ref), (loss.item(), loss_ref)
+    assert np.allclose(host(lse), lse_ref, rtol=1e-5, atol=0)
+    # dh is O(grad_scale / N_valid): judged scale-free (normwise and RMS-scaled) and by the plain bound
+    assert_close(host(dh), dh_ref, "ce dh")
+    assert_close_chain(host(dh), dh_ref, "ce dh (scale-free)")
+    assert_close_chain(host(dh) * nv, dh_ref * nv, "ce dh * N_valid")
+
+
+def test_ce_zero_weights_closed_form(gpu):
+    T, H, V = 50, 128, 4096
+    h, _, labels = _case(T, H, V, 61)
+    W = torch.zeros((V, H), dtype=torch.bfloat16, device="cuda")
+    loss, lse = gpu.fused_ce_loss_fwd(dev_bf16(h), W, dev(labels.astype(np.int32)))
+    dh = gpu.fused_ce_loss_bwd(dev_bf16(h), W, dev(labels.astype(np.int32)), lse)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - math.log(V)) < 1e-5 * math.log(V)
+    assert np.allclose(host(lse), math.log(V), rtol=1e-6)
+    assert torch.count_nonzero(dh) == 0
+
+
+def test_ce_all_ignored(gpu):
+    T, H, V = 16, 64, 128
+    h, w, _ = _case(T, H, V, 62)
+    labels = np.full(T, -100, np.int32)
+    loss, lse = gpu.fused_ce_loss_fwd(dev_bf16(h), dev_bf16(w), dev(labels))
+    dh = gpu.fused_ce_loss_bwd(dev_bf16(h), dev_bf16(w), dev(labels), lse)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and torch.count_nonzero(dh) == 0
+
+
+@pytest.mark.timeout(900)
+def test_ce_llama8b_head_sampled_rows(gpu):
+    """Full Llama-3.1-8B head (1024 tokens, hidden 4096, vocab 128256) on the GPU;
+    the oracle checks 48 sampled tokens (each token's lse and dh row depend only
+    on its own row and on the number of valid labels)."""
+    T, H, V = 1024, 4096, 128256
+    h = synth.activation((T, H), 5, "x")
+    w = synth.normal_bf16((V, H), 0.02, 5, 1000, 52)
+    labels = synth.token_ids(T, V, 5).astype(np.int64)
+    labels[T - 1] = -100
+    Hh, W, L = dev_bf16(h), dev_bf16(w), dev(labels.astype(np.int32))
+    loss, lse = gpu.fused_ce_loss_fwd(Hh, W, L)
+    dh = gpu.fused_ce_loss_bwd(Hh, W, L, lse)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(0).choice(T, 48, replace=False))
+    rows[-1] = T - 1
+    hd, wd = h[rows].astype(np.float64), w.astype(np.float64)
+    _, lse_ref, _ = O.ce_loss_fwd(hd, wd, labels[rows])
+    nv_all = int(np.sum(labels != -100))
+    dh_ref = O.ce_loss_bwd(hd, wd, labels[rows], grad_scale=len(np.nonzero(labels[rows] != -100)[0]) / nv_all)
+    assert np.allclose(host(lse)[rows], lse_ref, rtol=1e-5, atol=0)
+    assert_close(host(dh)[rows], dh_ref, "ce dh rows")
+    assert_close_chain(host(dh)[rows] * nv_all, dh_ref * nv_all, "ce dh rows * N_valid")
+    assert np.all(host(dh)[T - 1] == 0)
