@@ -19,7 +19,8 @@
  *    never allocate device memory: scratch space is a caller-provided workspace
  *    whose size the matching *_workspace_bytes call returns.
  *  - bfloat16 tensors are passed as uint16_t bit patterns, row-major, densely
- *    packed unless a leading dimension is given. Device pointers must be 16-byte
+ *    packed unless a leading dimension is given. Device pointers to bf16 data
+ *    must be 16-byte aligned, float/int32 vectors (labels, lse, loss) 4-byte
  *    aligned (INVALID_ARG otherwise; there is no slower fallback path).
  *  - Kernel selection (tile shapes, splits, chunking) depends only on the shapes
  *    passed, never on pointer values, residency or the stream, so a streamed and

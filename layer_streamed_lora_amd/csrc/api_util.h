@@ -12,11 +12,12 @@
 
 namespace lsl {
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-inline lsl_status check_ptrs(const char* fn, std::initializer_list<const void*> ps) {
+inline lsl_status check_ptrs(const char* fn, std::initializer_list<const void*> ps, size_t align = 16) {
   int i = 0;
   for (const void* p : ps) {
     if (!p) return set_error(LSL_ERR_INVALID_ARG, "%s: pointer argument %d is NULL", fn, i);
-    if (!aligned(p, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: pointer argument %d is not 16-byte aligned", fn, i);
+    if (!aligned(p, align))
+      return set_error(LSL_ERR_INVALID_ARG, "%s: pointer argument %d is not %zu-byte aligned", fn, i, align);
     ++i;
   }
   return LSL_OK;

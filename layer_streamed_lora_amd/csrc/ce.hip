@@ -112,7 +112,8 @@ extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm
                                         size_t ws_bytes, lsl_stream stream) {
   const char* fn = "fused_ce_loss_fwd";
   LSL_TRY(ce_check(fn, T, H, V));
-  LSL_TRY(check_ptrs(fn, {w_lm, loss}));
+  LSL_TRY(check_ptrs(fn, {w_lm}));
+  LSL_TRY(check_ptrs(fn, {loss}, 4));
   CePlan p = ce_plan(T, H, V);
   if (!ws || ws_bytes < p.total || !aligned(ws, 256))
     return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, p.total);
@@ -124,7 +125,8 @@ extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm
                        (const float*)nvalid, loss);
     return check_launch(fn);
   }
-  LSL_TRY(check_ptrs(fn, {hN, labels, lse}));
+  LSL_TRY(check_ptrs(fn, {hN}));
+  LSL_TRY(check_ptrs(fn, {labels, lse}, 4));
   hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
   GemmDesc g;
   g.x = hN; g.ldx = H; g.wfmt = LSL_WFMT_BF16; g.wb = w_lm; g.M = T; g.N = V; g.K = H;
@@ -146,7 +148,8 @@ extern "C" lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm
   const char* fn = "fused_ce_loss_bwd";
   LSL_TRY(ce_check(fn, T, H, V));
   if (T == 0) return LSL_OK;
-  LSL_TRY(check_ptrs(fn, {hN, w_lm, labels, lse, dhN}));
+  LSL_TRY(check_ptrs(fn, {hN, w_lm, dhN}));
+  LSL_TRY(check_ptrs(fn, {labels, lse}, 4));
   CePlan p = ce_plan(T, H, V);
   if (!ws || ws_bytes < p.total || !aligned(ws, 256))
     return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, p.total);

@@ -1,0 +1,137 @@
+"""Whole training steps: the streamed model against the oracle (small shapes),
+and streamed against resident bit for bit (the pages' correctness protocol:
+"Exact Layer Streaming ...", abstract; "Soup CLI ...", section "How Layer
+Streaming Works")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth.configs import LayerShape, PROJ_IN_OUT, QWEN05B_LAYER
+from tests.gpu_util import dev_bf16, host, assert_close_chain
+
+pytestmark = pytest.mark.gpu
+
+SMALL_NF4 = LayerShape(128, 2, 1, 64, 192, 1e-5, 500000.0, "nf4", 8, 16.0)
+SMALL_BF16 = LayerShape(192, 3, 1, 64, 256, 1e-6, 1000000.0, "bf16", 16, 32.0)
+
+
+def build(shape, n_layers, vocab, tied, batch, seq, mode, wid):
+    from layer_streamed_lora_amd.trainer import StreamedLoraModel
+    m = StreamedLoraModel(shape, n_layers, vocab, tied, batch, seq, mode=mode)
+    weights, loras = [], []
+    for l in range(n_layers):
+        w = synth.layer_weights(shape, wid, l, ones_norm=False)
+        lo = synth.layer_lora(shape, wid, l)
+        m.set_layer_weights(l, {k: dev_bf16(v) for k, v in w.items()})
+        m.lora.set_from(l, lo)
+        weights.append(w)
+        loras.append(lo)
+    emb, fn, lm = synth.model_head(shape.hidden, vocab, tied, wid, std=0.05, ones_norm=False)
+    m.embed.copy_(dev_bf16(emb))
+    m.final_norm.copy_(dev_bf16(fn))
+    if not tied:
+        m.lm_head.copy_(dev_bf16(lm))
+    torch.cuda.synchronize()
+    return m, weights, loras, (emb, fn, lm)
+
+
+def ids_for(vocab, batch, seq, n_micro, wid):
+    return [synth.token_ids(batch * seq, vocab, wid, salt=i) for i in range(n_micro)]
+
+
+@pytest.mark.parametrize("shape,tied", [(SMALL_NF4, False), (SMALL_BF16, True)])
+def test_model_step_matches_oracle(gpu, shape, tied):
+    n_layers, vocab, batch, seq, n_micro, wid = 3, 640, 2, 40, 2, 70
+    m, weights, loras, (emb, fn, lm) = build(shape, n_layers, vocab, tied, batch, seq, "streamed", wid)
+    chunks = ids_for(vocab, batch, seq, n_micro, wid)
+    losses = m.step(m.prepare_inputs(chunks), adamw=False)
+    torch.cuda.synchronize()
+    layers = []
+    for l in range(n_layers):
+        wd = {}
+        for p in PROJ_IN_OUT(shape):
+            if shape.wfmt == "nf4":
+                c, a = O.nf4_quantize(weights[l][p].astype(np.float64))
+                wd[p] = O.nf4_dequant(c, a)
+            else:
+                wd[p] = weights[l][p].astype(np.float64)
+        wd["norm1"] = weights[l]["norm1"].astype(np.float64)
+        wd["norm2"] = weights[l]["norm2"].astype(np.float64)
+        layers.append((wd, {k: v.astype(np.float64) for k, v in loras[l].items()}))
+    loss_ref, grads_ref, outs = O.model_step(chunks, emb.astype(np.float64), fn.astype(np.float64),
+                                             None if tied else lm.astype(np.float64), layers, shape, batch, seq)
+    got_losses = host(losses)
+    for i in range(n_micro):
+        assert abs(got_losses[i] - outs[i]["loss"]) <= 1e-3 * abs(outs[i]["loss"]), (got_losses[i], outs[i]["loss"])
+    for l in range(n_layers):
+        g = m.lora.grads_np(l)
+        for k in grads_ref[l]:
+            assert_close_chain(g[k], grads_ref[l][k], f"layer {l} {k}")
+
+
+def _assert_same_state(a, b):
+    for name in ("grad", "master", "bf16", "m", "v"):
+        assert torch.equal(getattr(a.lora, name), getattr(b.lora, name)), name
+
+
+@pytest.mark.parametrize("shape", [SMALL_NF4, SMALL_BF16])
+def test_streamed_equals_resident_small(gpu, shape):
+    n_layers, vocab, batch, seq, n_micro = 4, 640, 2, 64, 3
+    s, *_ = build(shape, n_layers, vocab, False, batch, seq, "streamed", 71)
+    r, *_ = build(shape, n_layers, vocab, False, batch, seq, "resident", 71)
+    for step in range(2):
+        chunks = ids_for(vocab, batch, seq, n_micro, 71 + step)
+        ls = s.step(s.prepare_inputs(chunks))
+        lr = r.step(r.prepare_inputs(chunks))
+        torch.cuda.synchronize()
+        assert torch.equal(ls, lr)
+        assert torch.equal(s.ckpt, r.ckpt) and torch.equal(s.lse, r.lse)
+        _assert_same_state(s, r)
+    # every layer's adapters received gradient (no severed path)
+    for l in range(n_layers):
+        for i in range(4):
+            assert torch.count_nonzero(s.lora.view(s.lora.grad, l, i, "A")) > 0
+            assert torch.count_nonzero(s.lora.view(s.lora.grad, l, i, "B")) > 0
+    # layer copies: 2L - 2 for the first microbatch, 2L - 4 for every later one
+    # (the two layers at each turn of the sweep are reused from the slots)
+    assert s.loads == (2 * n_layers - 2) + (2 * n_micro - 1) * (2 * n_layers - 4)
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_qwen05b(gpu):
+    """Qwen2.5-0.5B-shaped model (24 layers, hidden 896, 14/2 heads, MLP 4864,
+    vocab 151936, tied), 4 microbatches of 4 x 512 tokens, one AdamW step:
+    streamed and resident runs give identical bits."""
+    from layer_streamed_lora_amd.trainer import StreamedLoraModel
+    shape, L, V, batch, seq, n_micro = QWEN05B_LAYER, 24, 151936, 4, 512, 4
+    models = {}
+    for mode in ("resident", "streamed"):
+        m = StreamedLoraModel(shape, L, V, True, batch, seq, mode=mode)
+        g = torch.Generator(device="cuda").manual_seed(3)
+        for l in range(L):
+            w = {}
+            for p, (fin, fout) in PROJ_IN_OUT(shape).items():
+                w[p] = (torch.randn((fout, fin), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+            w["norm1"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
+            w["norm2"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
+            m.set_layer_weights(l, w)
+        m.embed.copy_((torch.randn((V, shape.hidden), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+        m.lora.master.copy_(torch.randn(m.lora.numel, generator=g, device="cuda") * 0.01)
+        m.lora.bf16.copy_(m.lora.master.to(torch.bfloat16))
+        models[mode] = m
+    chunks = ids_for(V, batch, seq, n_micro, 3)
+    out = {}
+    for mode, m in models.items():
+        out[mode] = m.step(m.prepare_inputs(chunks))
+    torch.cuda.synchronize()
+    s, r = models["streamed"], models["resident"]
+    assert torch.equal(out["streamed"], out["resident"])
+    assert torch.equal(s.ckpt, r.ckpt) and torch.equal(s.lse, r.lse)
+    _assert_same_state(s, r)
+    loss = host(out["streamed"]).mean()
+    # random N(0, 0.02) weights: the loss sits near ln V
+    assert abs(loss - np.log(V)) < 1.0, loss
+    for l in (0, L - 1):
+        assert torch.count_nonzero(s.lora.view(s.lora.grad, l, 0, "A")) > 0
