@@ -1,0 +1,292 @@
+"""Benchmark: layer-streamed LoRA training steps on one MI355X.
+
+Workload: Llama-3.1-8B-shaped decoder (32 layers, hidden 4096, 32/8 heads of
+128, SwiGLU 14336, vocab 128256, separate bf16 lm_head), frozen NF4 base
+(block 64, float32 absmax) streamed layer by layer from a pinned host store
+into 2 HBM slots, LoRA r=16 alpha=32 on all seven projections, batch 1 x seq
+1024 uniform random tokens, fused chunked cross-entropy, full forward +
+backward (recompute) + AdamW on the adapters. Synthetic random weights of that
+architecture (no checkpoint): N(0, 0.02) base and embeddings.
+
+Prints one JSON line. Other output goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LoRA train tok/s (streamed fwd+bwd) + % bf16 MFMA peak + achieved H2D GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+COUNTERS = os.path.join(ROOT, "profiles", "gemm_gu_fwd_nf4_llama8b_s1024_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload(name):
+    from synth.configs import WORKLOADS
+    w = WORKLOADS[name]
+    m = w.model
+    return w, m.layer, m
+
+
+def build_model(shape, ms, mode, seed=1234):
+    import torch
+    from synth.configs import PROJ_IN_OUT
+    from layer_streamed_lora_amd.trainer import StreamedLoraModel
+    m = StreamedLoraModel(shape, ms.n_layers, ms.vocab, ms.tied, ms.batch, ms.seq, mode=mode)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    for l in range(ms.n_layers):
+        w = {p: (torch.randn((fout, fin), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+             for p, (fin, fout) in PROJ_IN_OUT(shape).items()}
+        w["norm1"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
+        w["norm2"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
+        m.set_layer_weights(l, w)
+        del w
+    m.embed.copy_((torch.randn(m.embed.shape, generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    if m.lm_head is not None:
+        m.lm_head.copy_((torch.randn(m.lm_head.shape, generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+    lp = m.lora
+    for l in range(ms.n_layers):
+        for i in range(4):
+            A = lp.view(lp.master, l, i, "A")
+            A.copy_((torch.rand(A.shape, generator=g, device="cuda") * 2 - 1) / A.shape[1] ** 0.5)
+            B = lp.view(lp.master, l, i, "B")
+            B.copy_(torch.randn(B.shape, generator=g, device="cuda") * 0.01)
+    lp.bf16.copy_(lp.master.to(torch.bfloat16))
+    torch.cuda.synchronize()
+    return m
+
+
+def step_flops(shape, ms):
+    """Algorithmic FLOPs of one optimizer step (per microbatch x n_micro):
+    forward GEMMs, their recompute, input-gradient GEMMs, LoRA side products,
+    attention (causal: half the dense score/value work), cross-entropy 3 passes."""
+    T, H, I, r = ms.batch * ms.seq, shape.hidden, shape.inter, shape.lora_r
+    q, kv, d = shape.n_q * shape.head_dim, shape.n_kv * shape.head_dim, shape.head_dim
+    mats = [(q + 2 * kv, H, 3), (H, q, 1), (2 * I, H, 2), (H, I, 1)]   # (N, K, projections)
+    base = sum(2 * T * n * k for n, k, _ in mats)
+    lora = sum(2 * T * r * p * (k + n) for n, k, p in mats)        # t = xA^T and t B^T
+    lora_bwd = sum(2 * T * r * p * (n + k) * 2 for n, k, p in mats)  # u, dx-term, dA, dB
+    attn_fwd = 2 * 2 * ms.batch * shape.n_q * ms.seq * ms.seq * d / 2
+    per_layer = 2 * (base + lora + attn_fwd) + (base + lora_bwd + 2.5 * attn_fwd)
+    ce = 3 * 2 * T * H * ms.vocab
+    return ms.n_micro * (ms.n_layers * per_layer + ce)
+
+
+def pinned_h2d_peak(nbytes, reps=20):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            dst.copy_(src, non_blocking=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        e1.record(s)
+    e1.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def time_steps(m, inputs, steps, warmup, timing_which=0, stats=False):
+    import ctypes as C
+    import torch
+    from layer_streamed_lora_amd.ops import lib, _check
+    for _ in range(warmup):
+        m.step(inputs)
+    torch.cuda.synchronize()
+    if timing_which:
+        n_launch = steps * m.n_layers * inputs[0].shape[0] * 2
+        _check("lsl_timing_enable", lib().lsl_timing_enable(timing_which, n_launch))
+    if stats and m.pool is not None:
+        _check("lsl_pool_stats_enable", lib().lsl_pool_stats_enable(m.pool.handle, steps * 4 * m.n_layers * 8))
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        losses = m.step(inputs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    out = {"ms_per_step": ms, "wall_s": wall, "loss": float(losses.mean().item())}
+    if timing_which:
+        tot, n = C.c_double(), C.c_int32()
+        _check("lsl_timing_read", lib().lsl_timing_read(C.byref(tot), C.byref(n)))
+        lib().lsl_timing_disable()
+        out["kernel_ms_total"], out["kernel_launches"] = tot.value, n.value
+    if stats and m.pool is not None:
+        loads, b, s = C.c_int32(), C.c_double(), C.c_double()
+        _check("lsl_pool_stats_read", lib().lsl_pool_stats_read(m.pool.handle, C.byref(loads), C.byref(b), C.byref(s)))
+        lib().lsl_pool_stats_enable(m.pool.handle, 0)
+        out["h2d_loads"], out["h2d_bytes"], out["h2d_copy_s"] = loads.value, b.value, s.value
+    return out
+
+
+def counters_traffic():
+    """HBM bytes per launch of the timed GEMM from committed rocprofv3 counters,
+    if they were taken on the current kernel source (else None)."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+        src = open(os.path.join(ROOT, "layer_streamed_lora_amd", "csrc", "gemm.hip"), "rb").read()
+        if hashlib.sha256(src).hexdigest() != c.get("gemm_hip_sha256"):
+            return None
+        return c["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, ms):
+    """The CPU oracle on a bounded sample of the same step: one Llama-8B layer
+    forward + backward (recompute) at all 1024 tokens, that layer's NF4 dequant
+    (done on every visit, forward and backward), and the cross-entropy forward +
+    backward for 32 of the 1024 tokens; scaled to 32 layers and 1024 tokens."""
+    import numpy as np
+    import oracle as O
+    import synth
+    from synth.configs import PROJ_IN_OUT
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T = ms.batch * ms.seq
+    w = synth.layer_weights(shape, 5, 0, ones_norm=True)
+    lora = {k: v.astype(np.float64) for k, v in synth.layer_lora(shape, 5, 0).items()}
+    x = synth.activation((T, shape.hidden), 5, "x").astype(np.float64)
+    dy = synth.activation((T, shape.hidden), 5, "dy").astype(np.float64) * 1e-3
+    q = {p: O.nf4_quantize(w[p].astype(np.float64)) for p in PROJ_IN_OUT(shape)}
+    t0 = time.perf_counter()
+    wd = {p: O.nf4_dequant(*q[p]) for p in PROJ_IN_OUT(shape)}
+    t_deq = time.perf_counter() - t0
+    wd["norm1"], wd["norm2"] = w["norm1"].astype(np.float64), w["norm2"].astype(np.float64)
+    t0 = time.perf_counter()
+    O.decoder_layer_fwd(x, wd, lora, shape, ms.batch, ms.seq)
+    O.decoder_layer_bwd(x, dy, wd, lora, shape, ms.batch, ms.seq)
+    t_layer = time.perf_counter() - t0
+    ntok = 32
+    h = synth.activation((ntok, shape.hidden), 5, "x", salt=3).astype(np.float64)
+    wlm = synth.normal_bf16((ms.vocab, shape.hidden), 0.02, 5, 1000, 52).astype(np.float64)
+    labels = synth.token_ids(ntok, ms.vocab, 5)
+    t0 = time.perf_counter()
+    O.ce_loss_fwd(h, wlm, labels)
+    O.ce_loss_bwd(h, wlm, labels)
+    t_ce = time.perf_counter() - t0
+    step_s = ms.n_layers * (t_layer + 2 * t_deq) + t_ce * (T / ntok)
+    return {"value": T * ms.n_micro / (step_s * ms.n_micro), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"1 of {ms.n_layers} layers fwd+bwd at {T} tokens ({t_layer:.1f} s) + its NF4 dequant x2 "
+                       f"({2 * t_deq:.1f} s) + cross-entropy fwd+bwd on {ntok} of {T} tokens ({t_ce:.1f} s), "
+                       f"scaled to {ms.n_layers} layers and {T} tokens (float64 numpy)"),
+            "est_step_s": step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b_nf4")
+    ap.add_argument("--no-resident", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (one process, one MI355X); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import layer_streamed_lora_amd as lsl
+    import synth
+    lsl.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl, shape, ms = workload(args.workload)
+    T = ms.batch * ms.seq
+    log(f"building {args.workload}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.wfmt} base")
+    t0 = time.perf_counter()
+    s_model = build_model(shape, ms, "streamed")
+    log(f"  streamed model built in {time.perf_counter() - t0:.1f} s; blob {s_model.blob_bytes} B, "
+        f"store {s_model.blob_bytes * ms.n_layers / 1e9:.3f} GB pinned")
+    chunks = [synth.token_ids(T, ms.vocab, wl.wid, salt=i) for i in range(ms.n_micro)]
+    inputs = s_model.prepare_inputs(chunks)
+
+    bit_exact = None
+    r_model = None
+    if not args.no_resident:
+        from layer_streamed_lora_amd.trainer import StreamedLoraModel
+        r_model = StreamedLoraModel(shape, ms.n_layers, ms.vocab, ms.tied, ms.batch, ms.seq, mode="resident")
+        r_model.copy_base_from(s_model)
+        ls = s_model.step(inputs)
+        lr_ = r_model.step(inputs)
+        torch.cuda.synchronize()
+        bit_exact = bool(torch.equal(ls, lr_) and torch.equal(s_model.lora.grad, r_model.lora.grad)
+                         and torch.equal(s_model.lora.master, r_model.lora.master)
+                         and torch.equal(s_model.ckpt, r_model.ckpt) and torch.equal(s_model.lse, r_model.lse))
+        log(f"  streamed vs resident bit-exact: {bit_exact}")
+
+    peak_h2d = pinned_h2d_peak(s_model.blob_bytes)
+    log(f"  pinned H2D (hipMemcpyAsync, {s_model.blob_bytes} B): {peak_h2d:.1f} GB/s")
+    res = time_steps(s_model, inputs, args.steps, args.warmup, timing_which=3, stats=True)
+    log(f"  streamed: {res['ms_per_step']:.2f} ms/step, loss {res['loss']:.4f}")
+    resident = None
+    if r_model is not None:
+        resident = time_steps(r_model, inputs, args.steps, args.warmup)
+        log(f"  resident: {resident['ms_per_step']:.2f} ms/step")
+
+    tok_s = T * ms.n_micro / (res["ms_per_step"] * 1e-3)
+    flops = step_flops(shape, ms)
+    # the timed kernel: forward gate|up GEMM, NF4 dequant fused, LoRA-up K-step fused
+    K, N, kl = shape.hidden, 2 * shape.inter, 2 * shape.lora_r
+    g_flops = 2.0 * T * K * N + 2.0 * T * kl * N
+    g_ms = res["kernel_ms_total"] / max(res["kernel_launches"], 1)
+    achieved = g_flops / (g_ms * 1e-3) / 1e12
+    h2d_copy = res["h2d_bytes"] / res["h2d_copy_s"] / 1e9 if res.get("h2d_copy_s") else None
+    h2d_eff = res["h2d_bytes"] / (res["ms_per_step"] * 1e-3 * args.steps) / 1e9 if res.get("h2d_bytes") else None
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: Llama-3.1-8B-shaped, 32 layers, NF4 base (block 64, fp32 absmax) "
+                               f"streamed through 2 HBM slots, LoRA r16 a32 on all projections, "
+                               f"{ms.batch}x{ms.seq} tokens, fused CE, AdamW",
+                   "batch": ms.batch, "seq_len": ms.seq, "n_micro": ms.n_micro, "layers": ms.n_layers,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<NF4, NK, LoRA-fwd> gate|up 1024x28672x4096",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(),
+                     "avg_launch_ms": round(g_ms, 4), "launches": res["kernel_launches"]},
+        "mfma_frac_step": round(flops / (res["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "h2d": {"achieved_GBps_copy_engine": h2d_copy and round(h2d_copy, 2),
+                "achieved_GBps_over_step": h2d_eff and round(h2d_eff, 2),
+                "pinned_peak_GBps": round(peak_h2d, 2),
+                "frac_of_pinned_peak": h2d_copy and round(h2d_copy / peak_h2d, 3),
+                "bytes_per_step": res.get("h2d_bytes", 0) / args.steps},
+        "resident": resident and {"ms_per_step": round(resident["ms_per_step"], 3),
+                                  "tok_s": round(T * ms.n_micro / (resident["ms_per_step"] * 1e-3), 2)},
+        "streamed_over_resident": resident and round(res["ms_per_step"] / resident["ms_per_step"], 3),
+        "bit_exact_vs_resident": bit_exact,
+        "loss": round(res["loss"], 5),
+        "context": {"pages_tok_s": 119.6, "pages_hardware": "RTX 3050 Laptop 4 GB, seq/batch not stated"},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample ...")
+        cb = cpu_baseline(shape, ms)
+        cb["value"] = round(cb["value"], 4)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,7 +27,8 @@
  *    a resident run execute identical arithmetic and produce identical bits.
  *    No result is reduced with floating-point atomics.
  *  - The caller owns every buffer. The library keeps no device state; a pool
- *    object owns only its HIP events.
+ *    object owns only its HIP events (the optional GEMM timing below is the one
+ *    piece of process-global state).
  */
 #ifndef LSL_H
 #define LSL_H
@@ -209,6 +210,23 @@ lsl_status lsl_pool_release(lsl_pool* pool, int32_t slot, lsl_stream compute);
 lsl_status lsl_pool_reuse(lsl_pool* pool, int32_t slot);
 /* Seconds the copy engine spent on the slot's most recent load (waits for it). */
 lsl_status lsl_pool_last_copy_seconds(lsl_pool* pool, int32_t slot, double* seconds);
+/* Copy statistics: after enable, each of the next max_loads loads records a
+ * start/end event pair on the copy stream; read waits for them and returns the
+ * number of loads, bytes and summed copy seconds, then clears the record. */
+lsl_status lsl_pool_stats_enable(lsl_pool* pool, int32_t max_loads);
+lsl_status lsl_pool_stats_read(lsl_pool* pool, int32_t* loads, double* bytes, double* seconds);
+
+/* ------------------------------------------------------------------ timing
+ * Optional measurement of one GEMM of the decoder layer for roofline reports:
+ * while enabled, decoder_layer_fwd/bwd record HIP events on their stream
+ * around each launch of the selected GEMM (at most max_launches). This is the
+ * only process-global state of the library; it is off by default.
+ * which: 1..4 forward GEMM of group LSL_M_QKV..LSL_M_DOWN (+1),
+ *        5..8 input-gradient GEMM of the same groups. */
+lsl_status lsl_timing_enable(int32_t which, int32_t max_launches);
+/* Waits for the recorded events; total milliseconds and launch count. */
+lsl_status lsl_timing_read(double* total_ms, int32_t* launches);
+lsl_status lsl_timing_disable(void);
 
 /* ------------------------------------------------------------------ cross-entropy
  * Token cross-entropy over the vocabulary, fused with the lm_head product and

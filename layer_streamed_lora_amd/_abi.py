@@ -65,6 +65,11 @@ PROTOS = {
     "lsl_pool_release": (i32, [vp, i32, vp]),
     "lsl_pool_reuse": (i32, [vp, i32]),
     "lsl_pool_last_copy_seconds": (i32, [vp, i32, C.POINTER(C.c_double)]),
+    "lsl_pool_stats_enable": (i32, [vp, i32]),
+    "lsl_pool_stats_read": (i32, [vp, C.POINTER(i32), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "lsl_timing_enable": (i32, [i32, i32]),
+    "lsl_timing_read": (i32, [C.POINTER(C.c_double), C.POINTER(i32)]),
+    "lsl_timing_disable": (i32, []),
     "lsl_ce_workspace_bytes": (sz, [i64, i64, i64]),
     "fused_ce_loss_fwd": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]),
     "fused_ce_loss_bwd": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp, sz, vp]),

@@ -10,6 +10,7 @@
 #include "gemm.h"
 #include "small.h"
 #include "api_util.h"
+#include <vector>
 
 namespace lsl {
 struct AttnArgs;
@@ -26,6 +27,24 @@ extern "C" lsl_status lsl_attention_bwd(const uint16_t*, const uint16_t*, const 
 extern "C" size_t lsl_attention_workspace_bytes(int32_t, int32_t, int32_t, int32_t, int32_t);
 
 namespace lsl {
+
+// Optional GEMM timing (see lsl_timing_enable).
+struct Timing {
+  int which = 0;
+  std::vector<hipEvent_t> start, stop;
+  int count = 0;
+};
+static Timing g_timing;
+
+static void timing_mark(int which, bool begin, hipStream_t s) {
+  if (g_timing.which != which || g_timing.count >= (int)g_timing.start.size()) return;
+  if (begin) {
+    hipEventRecord(g_timing.start[g_timing.count], s);
+  } else {
+    hipEventRecord(g_timing.stop[g_timing.count], s);
+    ++g_timing.count;
+  }
+}
 
 struct Dims {
   int64_t T, H, Q, KV, NQKV, I;
@@ -186,7 +205,10 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   else g.seg_end[0] = n;
   g.scale = c->lora_scale;
   g.y = y; g.ldy = n; g.res = res; g.ldres = n;
-  return gemm_launch(g, s);
+  timing_mark(1 + i, true, s);
+  lsl_status st = gemm_launch(g, s);
+  timing_mark(1 + i, false, s);
+  return st;
 }
 
 // Backward of one fused LoRA linear: u = dy B (per projection); dx = dy W + s u A;
@@ -213,7 +235,10 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
     g.M = d.T; g.N = k; g.K = n;
     g.lora = 2; g.la = u; g.ldla = kl; g.kl = kl; g.lb = lo->A[i]; g.r = d.r;
     g.scale = c->lora_scale; g.y = dx; g.ldy = k;
-    LSL_TRY(gemm_launch(g, s));
+    timing_mark(5 + i, true, s);
+    lsl_status st = gemm_launch(g, s);
+    timing_mark(5 + i, false, s);
+    LSL_TRY(st);
   }
   LoraTn ta;
   ta.p = x; ta.ldp = k; ta.q = u; ta.ldq = kl; ta.T = d.T; ta.W = k; ta.kl = kl;
@@ -338,5 +363,50 @@ extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* la
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
                            (uint16_t*)(w + p.uqkv), dn1, part, s));
   if (dx) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
+  return LSL_OK;
+}
+
+static void timing_free() {
+  for (auto e : g_timing.start) hipEventDestroy(e);
+  for (auto e : g_timing.stop) hipEventDestroy(e);
+  g_timing = Timing();
+}
+
+extern "C" lsl_status lsl_timing_enable(int32_t which, int32_t max_launches) {
+  if (which < 1 || which > 8 || max_launches < 1 || max_launches > (1 << 20))
+    return set_error(LSL_ERR_INVALID_ARG, "lsl_timing_enable: which in [1, 8], max_launches > 0");
+  timing_free();
+  g_timing.start.assign(max_launches, nullptr);
+  g_timing.stop.assign(max_launches, nullptr);
+  for (int i = 0; i < max_launches; ++i) {
+    hipError_t e;
+    if ((e = hipEventCreate(&g_timing.start[i])) != hipSuccess || (e = hipEventCreate(&g_timing.stop[i])) != hipSuccess) {
+      timing_free();
+      return set_error(LSL_ERR_HIP, "lsl_timing_enable: %s", hipGetErrorString(e));
+    }
+  }
+  g_timing.which = which;
+  return LSL_OK;
+}
+
+extern "C" lsl_status lsl_timing_read(double* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return set_error(LSL_ERR_INVALID_ARG, "lsl_timing_read: NULL argument");
+  double t = 0.0;
+  for (int i = 0; i < g_timing.count; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.stop[i]);
+    if (e != hipSuccess) return set_error(LSL_ERR_HIP, "lsl_timing_read: %s", hipGetErrorString(e));
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i])) != hipSuccess)
+      return set_error(LSL_ERR_HIP, "lsl_timing_read: %s", hipGetErrorString(e));
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = g_timing.count;
+  g_timing.count = 0;
+  return LSL_OK;
+}
+
+extern "C" lsl_status lsl_timing_disable(void) {
+  timing_free();
   return LSL_OK;
 }

@@ -26,6 +26,10 @@ struct lsl_pool {
   std::vector<hipEvent_t> ready, freed, start;
   std::vector<int> state;
   std::vector<bool> free_recorded;
+  // optional copy statistics
+  std::vector<hipEvent_t> st_start, st_end;
+  std::vector<size_t> st_bytes;
+  int st_count = 0;
 };
 
 using namespace lsl;
@@ -63,6 +67,15 @@ extern "C" lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, in
   return LSL_OK;
 }
 
+static void stats_free(lsl_pool* p) {
+  for (auto e : p->st_start) hipEventDestroy(e);
+  for (auto e : p->st_end) hipEventDestroy(e);
+  p->st_start.clear();
+  p->st_end.clear();
+  p->st_bytes.clear();
+  p->st_count = 0;
+}
+
 extern "C" lsl_status lsl_pool_destroy(lsl_pool* p) {
   if (!p) return LSL_OK;
   for (int i = 0; i < p->n; ++i) {
@@ -70,7 +83,43 @@ extern "C" lsl_status lsl_pool_destroy(lsl_pool* p) {
     if (p->freed[i]) hipEventDestroy(p->freed[i]);
     if (p->start[i]) hipEventDestroy(p->start[i]);
   }
+  stats_free(p);
   delete p;
+  return LSL_OK;
+}
+
+extern "C" lsl_status lsl_pool_stats_enable(lsl_pool* p, int32_t max_loads) {
+  if (!p || max_loads < 0 || max_loads > (1 << 20))
+    return set_error(LSL_ERR_INVALID_ARG, "lsl_pool_stats_enable: bad arguments");
+  stats_free(p);
+  p->st_start.assign(max_loads, nullptr);
+  p->st_end.assign(max_loads, nullptr);
+  p->st_bytes.assign(max_loads, 0);
+  for (int i = 0; i < max_loads; ++i) {
+    hipError_t e;
+    if ((e = hipEventCreate(&p->st_start[i])) != hipSuccess || (e = hipEventCreate(&p->st_end[i])) != hipSuccess) {
+      stats_free(p);
+      return hip_fail("lsl_pool_stats_enable: hipEventCreate", e);
+    }
+  }
+  return LSL_OK;
+}
+
+extern "C" lsl_status lsl_pool_stats_read(lsl_pool* p, int32_t* loads, double* bytes, double* seconds) {
+  if (!p || !loads || !bytes || !seconds) return set_error(LSL_ERR_INVALID_ARG, "lsl_pool_stats_read: NULL argument");
+  double b = 0.0, s = 0.0;
+  for (int i = 0; i < p->st_count; ++i) {
+    hipError_t e = hipEventSynchronize(p->st_end[i]);
+    if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+    float ms = 0.f;
+    if ((e = hipEventElapsedTime(&ms, p->st_start[i], p->st_end[i])) != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+    s += ms * 1e-3;
+    b += (double)p->st_bytes[i];
+  }
+  *loads = p->st_count;
+  *bytes = b;
+  *seconds = s;
+  p->st_count = 0;
   return LSL_OK;
 }
 
@@ -97,9 +146,15 @@ extern "C" lsl_status load_layer_async(lsl_pool* p, int32_t slot, const void* ho
   if (p->free_recorded[slot] && (e = hipStreamWaitEvent(p->copy, p->freed[slot], 0)) != hipSuccess)
     return hip_fail("load_layer_async: hipStreamWaitEvent", e);
   if ((e = hipEventRecord(p->start[slot], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  const bool stat = p->st_count < (int)p->st_start.size();
+  if (stat && (e = hipEventRecord(p->st_start[p->st_count], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if ((e = hipMemcpyAsync(p->ptr[slot], host_ptr, bytes, hipMemcpyHostToDevice, p->copy)) != hipSuccess)
     return hip_fail("load_layer_async: hipMemcpyAsync", e);
   if ((e = hipEventRecord(p->ready[slot], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  if (stat) {
+    if ((e = hipEventRecord(p->st_end[p->st_count], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
+    p->st_bytes[p->st_count++] = bytes;
+  }
   p->state[slot] = SLOT_LOADED;
   return LSL_OK;
 }
