@@ -3,7 +3,7 @@
 // The pages measure what the naive logits term costs (bytes per logit element,
 // "Exact Layer Streaming ...", abstract); here no [T x V] logits tensor is ever
 // written. Forward: one MFMA GEMM pass z = hN W^T whose epilogue reduces every
-// 128-wide vocabulary tile to a (max, sum exp) pair per token and picks the
+// vocabulary tile to a (max, sum exp) pair per token and picks the
 // label logit; a second kernel merges the tile pairs in index order into the
 // log-sum-exp, and a single workgroup sums the loss in a fixed order.
 // Backward: per vocabulary chunk, the GEMM recomputes z and writes
@@ -27,7 +27,9 @@ static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
   auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
   p.nvalid = take(4);
   size_t common = off;
-  int64_t ntiles = (V + 127) / 128;
+  int bn, bm;
+  gemm_tile_shape(T, V, bn, bm);
+  int64_t ntiles = (V + bn - 1) / bn;
   p.part = take((size_t)ntiles * T * 8);
   p.zlab = take((size_t)T * 4);
   p.lossv = take((size_t)T * 4);
@@ -133,7 +135,9 @@ extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm
   g.epi = 1; g.labels = labels; g.part = w + p.part; g.zlab = (float*)(w + p.zlab); g.ignore = ignore_index;
   g.vocab = V;
   LSL_TRY(gemm_launch(g, s));
-  int64_t ntiles = (V + 127) / 128;
+  int bn, bm;
+  gemm_tile_shape(T, V, bn, bm);
+  int64_t ntiles = (V + bn - 1) / bn;
   hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, (const float2*)(w + p.part),
                      ntiles, T, labels, (const float*)(w + p.zlab), ignore_index, V, lse, (float*)(w + p.lossv));
   hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(256), 0, s, (const float*)(w + p.lossv), T, (const float*)nvalid,

@@ -24,4 +24,6 @@ struct GemmDesc {
   int64_t kwrap = 0;
 };
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
+// Tile shape gemm_launch picks for an M x N output (bn weight rows, bm tokens).
+void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm);
 }  // namespace lsl

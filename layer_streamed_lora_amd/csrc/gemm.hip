@@ -12,20 +12,28 @@
 // L = u = dy B, Lt = A^T. Accumulation is float32 in MFMA registers; the output
 // is rounded to bf16 once (plus once more after a fused residual add).
 //
-// Tiling: 128(n) x 128(m) per workgroup of 4 waves, 64 x 64 per wave, K-step 64,
-// LDS double-buffered with one barrier per K-step. The MFMA A operand is the
-// weight tile (rows n) and the B operand the activation tile (rows m), so each
-// lane's four accumulators are four consecutive n of one output row m and the
-// epilogue writes 8-byte chunks. Workgroups are mapped so that each XCD (L2)
-// owns a contiguous range of weight tiles and all m-tiles of each: a weight
-// tile is fetched from HBM by one XCD only.
+// Tiling: BN (weight rows) x BM (tokens) per workgroup of 4 waves; a wave owns
+// 64 weight rows x BM/(4*64/BN) tokens, K-step 64; the next tile's global loads
+// are issued into registers before the current tile's MFMAs and stored to LDS
+// after them. The MFMA A operand is the weight tile
+// and the B operand the token tile, so each lane's four accumulators are four
+// consecutive n of one output row m and the epilogue writes 8-byte chunks.
+// Loader addresses are set up once; a K-step only adds a uniform offset.
+// NF4 dequantisation cost per weight is amortised over the BM tokens of the
+// tile. Workgroups are mapped so that each XCD (L2) owns a contiguous range of
+// weight tiles and all token tiles of each: a weight tile is fetched from HBM
+// by one XCD only. The tile shape is a function of (M, N) only.
 #include "common.h"
 #include "gemm.h"
 #include "nf4.h"
 
 namespace lsl {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDSW = BK + 8;  // LDS row stride in elements
+#ifndef LSL_GEMM_PIPE
+#define LSL_GEMM_PIPE 0
+#endif
+constexpr int PIPE = LSL_GEMM_PIPE;  // K-loop pipeline structure (see the main loop)
+constexpr int BK = 64, LDSW = BK + 8;  // LDS row stride in elements
 constexpr int NTHREADS = 256;
 
 struct GemmKArgs {
@@ -46,132 +54,185 @@ struct GemmKArgs {
   uint16_t* y2;              // low half of the hi + lo gradient pair
   float gscale; int ignore; int64_t vocab_off, vocab;
   float* out32; int64_t ldo32; int first;
-  int64_t kwrap;             // KN operand: reduction index k reads weight row k mod kwrap
+  int64_t kwrap;             // KN operand: reduction index k reads weight row k mod kwrap (K <= 2 kwrap)
 };
 
 enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_CEGRAD = 2, EPI_ACC32 = 3 };
 
-template <int WFMT, bool KN>
-struct WLoader;
+// 2 x bf16 halves: (lo of a, lo of b) and (hi of a, hi of b)
+LSL_DEV uint32_t lo_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+LSL_DEV uint32_t hi_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// ---- activation / bf16-NK loader: 128 rows x 64 k; 4 x 16B per thread
+// Buffer resource over [base, base + bytes): loads past the end return zeros,
+// so partial tiles need no branches. The fourth descriptor word is the gfx9
+// raw-buffer format.
+LSL_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+LSL_DEV u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+LSL_DEV u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+LSL_DEV uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// ---- row-major bf16 tile loader: ROWS rows x 64 k, 16 B chunks, 8 chunks per
+// row; thread -> rows tid/8 + 32 i. Per K-step only the scalar offset changes.
+template <int ROWS>
 struct RowLoader {
-  u32x4 v[4];
-  LSL_DEV void load(const uint16_t* __restrict__ base, int64_t ld, int64_t rows, int64_t r0, int64_t k0, int tid) {
+  static constexpr int CH = ROWS / 32;
+  uint32_t voff;
+  u32x4 v[CH];
+  LSL_DEV void init(int64_t ld, int64_t r0, int tid) {
+    voff = (uint32_t)(((r0 + (tid >> 3)) * ld + (tid & 7) * 8) * 2);
+  }
+  // base/ld/rows come straight from the kernel arguments, so the descriptor is uniform
+  LSL_DEV void load(const uint16_t* base, int64_t ld, int64_t rows, int64_t k0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows * ld * 2);
+    const uint32_t rstride = (uint32_t)(32 * ld * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + i * NTHREADS;
-      int row = c >> 3, col = (c & 7) * 8;
-      int64_t gr = r0 + row;
-      v[i] = gr < rows ? *reinterpret_cast<const u32x4*>(base + gr * ld + k0 + col) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < CH; ++i) v[i] = bload16(rs, voff, (uint32_t)(i * rstride + k0 * 2));
   }
   LSL_DEV void store(uint16_t* lds, int tid) const {
+    const int r = tid >> 3, c = (tid & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + i * NTHREADS;
-      int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(lds + row * LDSW + col) = v[i];
-    }
+    for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(lds + (r + 32 * i) * LDSW + c) = v[i];
   }
 };
 
-template <>
-struct WLoader<LSL_WFMT_BF16, false> {
-  RowLoader r;
-  LSL_DEV void load(const GemmKArgs& a, int64_t n0, int64_t k0, int tid) { r.load(a.wb, a.K, a.N, n0, k0, tid); }
+template <int WFMT, bool KN, int BN>
+struct WLoader;
+
+template <int BN>
+struct WLoader<LSL_WFMT_BF16, false, BN> {
+  RowLoader<BN> r;
+  LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) { r.init(a.K, n0, tid); }
+  LSL_DEV void load(const GemmKArgs& a, int64_t k0) { r.load(a.wb, a.K, a.N, k0); }
   LSL_DEV void store(uint16_t* lds, const float2*, int tid) const { r.store(lds, tid); }
 };
 
-// NF4 [N x K]: thread -> row tid/2, 32 consecutive k (16 code bytes)
-template <>
-struct WLoader<LSL_WFMT_NF4, false> {
-  u32x4 c; float am;
-  LSL_DEV void load(const GemmKArgs& a, int64_t n0, int64_t k0, int tid) {
-    int row = tid >> 1, half = tid & 1;
-    int64_t n = n0 + row;
-    if (n < a.N) {
-      c = *reinterpret_cast<const u32x4*>(a.wq + n * (a.K >> 1) + (k0 >> 1) + half * 16);
-      am = a.wa[n * (a.K >> 6) + (k0 >> 6)];
+// NF4 [N x K]: each of the BN rows has 32 code bytes per K-step; TPR threads per
+// row, BPT bytes (2 BPT weights) each. Rows past N are clamped to the last row:
+// their outputs are never stored.
+template <int BN>
+struct WLoader<LSL_WFMT_NF4, false, BN> {
+  static constexpr int TPR = 256 / BN, BPT = 32 / TPR;
+  const uint8_t* pc;
+  const float* pa;
+  uint32_t c[BPT / 4];
+  float am;
+  LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) {
+    const int row = tid / TPR, part = tid % TPR;
+    const int64_t n = n0 + row < a.N ? n0 + row : a.N - 1;
+    pc = a.wq + n * (a.K >> 1) + part * BPT;
+    pa = a.wa + n * (a.K >> 6);
+  }
+  LSL_DEV void load(const GemmKArgs&, int64_t k0) {
+    if constexpr (BPT == 16) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(pc + (k0 >> 1));
+      c[0] = v[0]; c[1] = v[1]; c[2] = v[2]; c[3] = v[3];
     } else {
-      c = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      am = 0.f;
+      u32x2 v = *reinterpret_cast<const u32x2*>(pc + (k0 >> 1));
+      c[0] = v[0]; c[1] = v[1];
     }
+    am = pa[k0 >> 6];
   }
   LSL_DEV void store(uint16_t* lds, const float2* lut, int tid) const {
-    int row = tid >> 1, half = tid & 1;
-    uint32_t o[16];
+    const int row = tid / TPR, part = tid % TPR;
+    uint32_t o[BPT];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < BPT; ++j) {
       float2 cv = lut[(c[j >> 2] >> ((j & 3) * 8)) & 0xFF];
       o[j] = pack2(cv.x * am, cv.y * am);
     }
-    u32x4* d = reinterpret_cast<u32x4*>(lds + row * LDSW + half * 32);
-    d[0] = u32x4{o[0], o[1], o[2], o[3]};
-    d[1] = u32x4{o[4], o[5], o[6], o[7]};
-    d[2] = u32x4{o[8], o[9], o[10], o[11]};
-    d[3] = u32x4{o[12], o[13], o[14], o[15]};
+    u32x4* d = reinterpret_cast<u32x4*>(lds + row * LDSW + part * 2 * BPT);
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) d[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
 };
 
-// Transposing store shared by the KN loaders: vals[r][c] = element (kk = 4q + r, j = 8o + c)
-LSL_DEV void store_transposed_4x8(uint16_t* lds, const uint32_t w[4][4], int tid) {
-  int q = tid >> 4, o = tid & 15;
+// Transposing store shared by the KN loaders. w[rr][j] holds n-columns 2j (low
+// half) and 2j+1 (high half) of reduction row rr; Ws[n][k] wants KR consecutive
+// k per n-column.
+template <int KR>
+LSL_DEV void store_transposed(uint16_t* lds, const uint32_t (&w)[KR][4], int q, int o) {
 #pragma unroll
-  for (int cc = 0; cc < 8; ++cc) {
-    uint32_t e[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) e[rr] = (cc & 1) ? (w[rr][cc >> 1] >> 16) : (w[rr][cc >> 1] & 0xFFFFu);
-    u32x2 v = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-    *reinterpret_cast<u32x2*>(lds + (o * 8 + cc) * LDSW + q * 4) = v;
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (KR == 4) {
+      *reinterpret_cast<u32x2*>(lds + (o * 8 + 2 * j) * LDSW + q * 4) =
+          u32x2{lo_lo(w[0][j], w[1][j]), lo_lo(w[2][j], w[3][j])};
+      *reinterpret_cast<u32x2*>(lds + (o * 8 + 2 * j + 1) * LDSW + q * 4) =
+          u32x2{hi_hi(w[0][j], w[1][j]), hi_hi(w[2][j], w[3][j])};
+    } else {
+      *reinterpret_cast<uint32_t*>(lds + (o * 8 + 2 * j) * LDSW + q * 2) = lo_lo(w[0][j], w[1][j]);
+      *reinterpret_cast<uint32_t*>(lds + (o * 8 + 2 * j + 1) * LDSW + q * 2) = hi_hi(w[0][j], w[1][j]);
+    }
   }
 }
 
-// bf16 stored [K x N] (row = reduction index): thread -> 4 k-rows x 8 n-cols
-template <>
-struct WLoader<LSL_WFMT_BF16, true> {
-  uint32_t w[4][4];
-  LSL_DEV void load(const GemmKArgs& a, int64_t n0, int64_t k0, int tid) {
-    int q = tid >> 4, o = tid & 15;
-    int64_t n = n0 + o * 8;
-    if (a.kwrap) k0 %= a.kwrap;
+// bf16 stored [K x N] (row = reduction index): thread -> KR k-rows x 8 n-cols.
+// Columns past N read neighbouring data or zeros; their outputs are never stored.
+template <int BN>
+struct WLoader<LSL_WFMT_BF16, true, BN> {
+  static constexpr int KR = BN / 32, OG = BN / 8;  // k-rows per thread, n-groups per tile
+  uint32_t voff;
+  uint32_t w[KR][4];
+  LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) {
+    const int q = tid / OG, o = tid % OG;
+    voff = (uint32_t)(((int64_t)(q * KR) * a.N + n0 + o * 8) * 2);
+  }
+  LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
+    const int64_t rows = a.kwrap ? a.kwrap : a.K;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb, rows * a.N * 2);
+    const uint32_t rowb = (uint32_t)(a.N * 2);
+    if (a.kwrap && k0 >= a.kwrap) k0 -= a.kwrap;  // K <= 2 kwrap (checked on the host)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      u32x4 v = n < a.N ? *reinterpret_cast<const u32x4*>(a.wb + (k0 + q * 4 + rr) * a.N + n) : u32x4{0, 0, 0, 0};
+    for (int rr = 0; rr < KR; ++rr) {
+      u32x4 v = bload16(rs, voff, (uint32_t)((k0 + rr) * rowb));
       w[rr][0] = v[0]; w[rr][1] = v[1]; w[rr][2] = v[2]; w[rr][3] = v[3];
     }
   }
-  LSL_DEV void store(uint16_t* lds, const float2*, int tid) const { store_transposed_4x8(lds, w, tid); }
+  LSL_DEV void store(uint16_t* lds, const float2*, int tid) const { store_transposed<KR>(lds, w, tid / OG, tid % OG); }
 };
 
-// NF4 stored [K x N]: thread -> 4 k-rows x 8 n-cols (4 code bytes + absmax per row)
-template <>
-struct WLoader<LSL_WFMT_NF4, true> {
-  uint32_t c[4]; float am[4];
-  LSL_DEV void load(const GemmKArgs& a, int64_t n0, int64_t k0, int tid) {
-    int q = tid >> 4, o = tid & 15;
-    int64_t n = n0 + o * 8;
+// NF4 stored [K x N]: thread -> KR k-rows x 8 n-cols (4 code bytes + absmax per
+// row); column groups past N are clamped to the last group (outputs not stored).
+template <int BN>
+struct WLoader<LSL_WFMT_NF4, true, BN> {
+  static constexpr int KR = BN / 32, OG = BN / 8;
+  const uint8_t* pc;
+  const float* pa;
+  int64_t rowc, rowa;
+  uint32_t c[KR];
+  float am[KR];
+  LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) {
+    const int q = tid / OG, o = tid % OG;
+    const int64_t n = n0 + o * 8 < a.N ? n0 + o * 8 : a.N - 8;
+    rowc = a.N >> 1;
+    rowa = a.N >> 6;
+    pc = a.wq + (int64_t)(q * KR) * rowc + (n >> 1);
+    pa = a.wa + (int64_t)(q * KR) * rowa + (n >> 6);
+  }
+  LSL_DEV void load(const GemmKArgs&, int64_t k0) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      int64_t kk = k0 + q * 4 + rr;
-      if (n < a.N) {
-        c[rr] = *reinterpret_cast<const uint32_t*>(a.wq + kk * (a.N >> 1) + (n >> 1));
-        am[rr] = a.wa[kk * (a.N >> 6) + (n >> 6)];
-      } else {
-        c[rr] = 0x77777777u; am[rr] = 0.f;
-      }
+    for (int rr = 0; rr < KR; ++rr) {
+      c[rr] = *reinterpret_cast<const uint32_t*>(pc + (k0 + rr) * rowc);
+      am[rr] = pa[(k0 + rr) * rowa];
     }
   }
   LSL_DEV void store(uint16_t* lds, const float2* lut, int tid) const {
-    uint32_t w[4][4];
+    uint32_t w[KR][4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
+    for (int rr = 0; rr < KR; ++rr)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float2 cv = lut[(c[rr] >> (8 * j)) & 0xFF];
         w[rr][j] = pack2(cv.x * am[rr], cv.y * am[rr]);
       }
-    store_transposed_4x8(lds, w, tid);
+    store_transposed<KR>(lds, w, tid / OG, tid % OG);
   }
 };
 
@@ -179,20 +240,29 @@ LSL_DEV f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One 64-deep K-step on LDS tiles: acc[ni][mi] += Wt-frag[ni] x X-frag[mi]
-LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x4 acc[4][4], int wn, int wm, int lane, int ksteps) {
+// Tile geometry: WN x WM waves, each 64 (n) x WTM (m), MS 16-row m-subtiles.
+template <int BN, int BM>
+struct Geo {
+  static constexpr int WN = BN / 64, WM = 4 / WN, WTM = BM / WM, MS = WTM / 16;
+};
+
+// ksteps x 32-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-frag[ni] x X-frag[mi]
+template <int MS>
+LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x4 (&acc)[4][MS], int wn, int wm0, int lane,
+                      int ksteps) {
   for (int ks = 0; ks < ksteps; ++ks) {
-    bf16x8 af[4], bfr[4];
-    int kofs = ks * 32 + (lane >> 4) * 8;
+    const int kofs = ks * 32 + (lane >> 4) * 8;
+    bf16x8 af[4], bfr[MS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
       af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + i * 16 + (lane & 15)) * LDSW + kofs);
-      bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm * 64 + i * 16 + (lane & 15)) * LDSW + kofs);
-    }
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int i = 0; i < MS; ++i)
+      bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm0 + i * 16 + (lane & 15)) * LDSW + kofs);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = mfma16(af[ni], bfr[mi], acc[ni][mi]);
+    for (int mi = 0; mi < MS; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) acc[ni][mi] = mfma16(af[ni], bfr[mi], acc[ni][mi]);
   }
 }
 
@@ -208,56 +278,108 @@ LSL_DEV void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
   tm = t - tn * tiles_m;
 }
 
-template <int WFMT, bool KN, int LORA, int EPI>
-__global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM * LDSW];
+template <int WFMT, bool KN, int LORA, int EPI, int BN, int BM>
+__global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
+  using G = Geo<BN, BM>;
+  constexpr int MS = G::MS;
+  constexpr int NBUF = PIPE == 0 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[NBUF][BN * LDSW];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[NBUF][BM * LDSW];
   __shared__ float2 lut[WFMT == LSL_WFMT_NF4 ? 256 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % G::WN, wm = wave / G::WN;
+  const int wm0 = wm * G::WTM;
   int tm, tn;
   tile_coords(a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   if constexpr (WFMT == LSL_WFMT_NF4) lut[tid] = make_float2(a.cb[tid >> 4], a.cb[tid & 15]);
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][MS];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = (int)(a.K / BK);
-  RowLoader xl;
-  WLoader<WFMT, KN> wl;
-  xl.load(a.x, a.ldx, a.M, m0, 0, tid);
-  wl.load(a, n0, 0, tid);
-  __syncthreads();  // lut visible
-  xl.store(Xs[0], tid);
-  wl.store(Ws[0], lut, tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      xl.load(a.x, a.ldx, a.M, m0, (int64_t)(kt + 1) * BK, tid);
-      wl.load(a, n0, (int64_t)(kt + 1) * BK, tid);
+  if constexpr (PIPE == 2) {
+    // tile k computes from LDS buffer k % 2 while tile k + 1 waits in registers
+    // (set (k + 1) % 2) for its LDS store and tile k + 2 is in flight
+    RowLoader<BM> xl0, xl1;
+    WLoader<WFMT, KN, BN> wl0, wl1;
+    xl0.init(a.ldx, m0, tid);
+    wl0.init(a, n0, tid);
+    xl1 = xl0;
+    wl1 = wl0;
+    xl0.load(a.x, a.ldx, a.M, 0);
+    wl0.load(a, 0);
+    if (KT > 1) {
+      xl1.load(a.x, a.ldx, a.M, BK);
+      wl1.load(a, BK);
     }
-    mma_tile(Ws[cur], Xs[cur], acc, wn, wm, lane, 2);
-    if (more) {
-      xl.store(Xs[cur ^ 1], tid);
-      wl.store(Ws[cur ^ 1], lut, tid);
-    }
+    __syncthreads();  // lut visible
+    xl0.store(Xs[0], tid);
+    wl0.store(Ws[0], lut, tid);
     __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+      if (kt + 2 < KT) {
+        xl0.load(a.x, a.ldx, a.M, (int64_t)(kt + 2) * BK);
+        wl0.load(a, (int64_t)(kt + 2) * BK);
+      }
+      mma_tile<MS>(Ws[0], Xs[0], acc, wn, wm0, lane, 2);
+      if (kt + 1 < KT) {
+        xl1.store(Xs[1], tid);
+        wl1.store(Ws[1], lut, tid);
+      }
+      __syncthreads();
+      if (kt + 1 >= KT) break;
+      if (kt + 3 < KT) {
+        xl1.load(a.x, a.ldx, a.M, (int64_t)(kt + 3) * BK);
+        wl1.load(a, (int64_t)(kt + 3) * BK);
+      }
+      mma_tile<MS>(Ws[1], Xs[1], acc, wn, wm0, lane, 2);
+      if (kt + 2 < KT) {
+        xl0.store(Xs[0], tid);
+        wl0.store(Ws[0], lut, tid);
+      }
+      __syncthreads();
+    }
+  } else {
+    // tile k + 1 is loaded into registers while tile k computes from LDS; with
+    // PIPE == 1 LDS is double-buffered (one barrier per K-step), with PIPE == 0
+    // single-buffered (two barriers, half the LDS, more workgroups per CU)
+    RowLoader<BM> xl;
+    WLoader<WFMT, KN, BN> wl;
+    xl.init(a.ldx, m0, tid);
+    wl.init(a, n0, tid);
+    xl.load(a.x, a.ldx, a.M, 0);
+    wl.load(a, 0);
+    __syncthreads();  // lut visible
+    xl.store(Xs[0], tid);
+    wl.store(Ws[0], lut, tid);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = PIPE == 1 ? (kt & 1) : 0;
+      const bool more = kt + 1 < KT;
+      if (more) {
+        xl.load(a.x, a.ldx, a.M, (int64_t)(kt + 1) * BK);
+        wl.load(a, (int64_t)(kt + 1) * BK);
+      }
+      mma_tile<MS>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 2);
+      if constexpr (PIPE == 0) __syncthreads();
+      if (more) {
+        xl.store(Xs[PIPE == 1 ? cur ^ 1 : 0], tid);
+        wl.store(Ws[PIPE == 1 ? cur ^ 1 : 0], lut, tid);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- LoRA K-step (kl <= 64, zero padded to 64) into separate accumulators
   if constexpr (LORA != 0) {
     uint16_t* Ls = Xs[0];
     uint16_t* Lt = Ws[0];
-    // L side: [128 m x kl]
     for (int c = tid; c < BM * 8; c += NTHREADS) {
       int row = c >> 3, col = (c & 7) * 8;
       int64_t gm = m0 + row;
@@ -281,7 +403,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
     } else {
       // Lt[n][j] = A_full[j][n]
       for (int c = tid; c < BN * 64; c += NTHREADS) {
-        int j = c >> 7, row = c & 127;
+        int j = c / BN, row = c % BN;
         int64_t gn = n0 + row;
         uint16_t v = 0;
         if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
@@ -289,16 +411,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
       }
     }
     __syncthreads();
-    f32x4 lacc[4][4];
+    f32x4 lacc[4][MS];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_tile(Lt, Ls, lacc, wn, wm, lane, (a.kl + 31) / 32);
+      for (int j = 0; j < MS; ++j) lacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mma_tile<MS>(Lt, Ls, lacc, wn, wm0, lane, (a.kl + 31) / 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < MS; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][e] += a.scale * lacc[i][j][e];
   }
@@ -307,10 +429,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
   if constexpr (EPI == EPI_LSE) {
     // Cross-entropy forward: per token m, max and sum of exp over this tile's
     // vocabulary entries n < N, and the label's logit if it falls in the tile.
-    float2* red = reinterpret_cast<float2*>(Xs[0]);  // [2 (wn)][128 (m)]
+    float2* red = reinterpret_cast<float2*>(Xs[0]);  // [WN][BM]
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
+    for (int mi = 0; mi < MS; ++mi) {
+      const int64_t m = m0 + wm0 + mi * 16 + (lane & 15);
       const int lab = m < a.M ? a.labels[m] : -1;
       float mx = -INFINITY;
 #pragma unroll
@@ -338,18 +460,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
       }
       sm += __shfl_xor(sm, 16, 64);
       sm += __shfl_xor(sm, 32, 64);
-      if ((lane >> 4) == 0) red[wn * BM + wm * 64 + mi * 16 + (lane & 15)] = make_float2(mx, sm);
+      if ((lane >> 4) == 0) red[wn * BM + wm0 + mi * 16 + (lane & 15)] = make_float2(mx, sm);
     }
     __syncthreads();
-    if (tid < BM && m0 + tid < a.M) {
-      float2 p0 = red[tid], p1 = red[BM + tid];
-      float mx = fmaxf(p0.x, p1.x);
+    for (int t = tid; t < BM; t += NTHREADS) {
+      if (m0 + t >= a.M) continue;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < G::WN; ++w) mx = fmaxf(mx, red[w * BM + t].x);
       float sm = 0.f;
       if (mx != -INFINITY) {
-        if (p0.x != -INFINITY) sm += p0.y * expf(p0.x - mx);
-        if (p1.x != -INFINITY) sm += p1.y * expf(p1.x - mx);
+#pragma unroll
+        for (int w = 0; w < G::WN; ++w) {
+          float2 p = red[w * BM + t];
+          if (p.x != -INFINITY) sm += p.y * expf(p.x - mx);
+        }
       }
-      a.part[(int64_t)tn * a.M + m0 + tid] = make_float2(mx, sm);
+      a.part[(int64_t)tn * a.M + m0 + t] = make_float2(mx, sm);
     }
     return;
   }
@@ -358,8 +485,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
     const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
     if (n >= a.N) continue;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int64_t m = m0 + wm * 64 + mi * 16 + (lane & 15);
+    for (int mi = 0; mi < MS; ++mi) {
+      const int64_t m = m0 + wm0 + mi * 16 + (lane & 15);
       if (m >= a.M) continue;
       float v0 = acc[ni][mi][0], v1 = acc[ni][mi][1], v2 = acc[ni][mi][2], v3 = acc[ni][mi][3];
       if constexpr (EPI == EPI_CEGRAD) {
@@ -398,11 +525,49 @@ __global__ __launch_bounds__(NTHREADS, 2) void gemm_kernel(const GemmKArgs a) {
   }
 }
 
-template <int WFMT, bool KN>
+template <int WFMT, bool KN, int BN, int BM>
 static void launch_lora_variant(const GemmKArgs& a, int lora, hipStream_t s, dim3 grid) {
-  if (lora == 0) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 0, EPI_BF16>), grid, dim3(NTHREADS), 0, s, a);
-  else if (lora == 1) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 1, EPI_BF16>), grid, dim3(NTHREADS), 0, s, a);
-  else hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 2, EPI_BF16>), grid, dim3(NTHREADS), 0, s, a);
+  if (lora == 0) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 0, EPI_BF16, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
+  else if (lora == 1) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 1, EPI_BF16, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
+  else hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 2, EPI_BF16, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
+}
+
+template <int BN, int BM>
+static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
+  a.tiles_m = (int)((d.M + BM - 1) / BM);
+  a.tiles_n = (int)((d.N + BN - 1) / BN);
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  if (d.epi != EPI_BF16) {
+    if (d.wfmt != LSL_WFMT_BF16 || d.lora) return set_error(LSL_ERR_UNSUPPORTED, "gemm: CE epilogues take a bf16 weight");
+    if (d.epi == EPI_LSE && !d.kn)
+      hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, false, 0, EPI_LSE, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
+    else if (d.epi == EPI_CEGRAD && !d.kn)
+      hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, false, 0, EPI_CEGRAD, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
+    else if (d.epi == EPI_ACC32 && d.kn)
+      hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, true, 0, EPI_ACC32, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
+    else
+      return set_error(LSL_ERR_UNSUPPORTED, "gemm: epilogue %d with layout %d", d.epi, (int)d.kn);
+    return check_launch("gemm(ce)");
+  }
+  if (d.wfmt == LSL_WFMT_NF4) {
+    if (d.kn) launch_lora_variant<LSL_WFMT_NF4, true, BN, BM>(a, d.lora, s, grid);
+    else launch_lora_variant<LSL_WFMT_NF4, false, BN, BM>(a, d.lora, s, grid);
+  } else {
+    if (d.kn) launch_lora_variant<LSL_WFMT_BF16, true, BN, BM>(a, d.lora, s, grid);
+    else launch_lora_variant<LSL_WFMT_BF16, false, BN, BM>(a, d.lora, s, grid);
+  }
+  return check_launch("gemm");
+}
+
+// Tile shape from the problem shape only: 64 weight rows, 256 tokens once there
+// are at least 1024 tokens (128 below). Measured on MI355X at the Llama-8B
+// layer shapes, this beat 128-row weight tiles and two-deep prefetching: with
+// 64 x 64 wave tiles the loop is bound by LDS bandwidth, and the small LDS
+// footprint (single buffer, 46 KB) lets three workgroups share a CU.
+void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
+  (void)N;
+  bm = M >= 1024 ? 256 : 128;
+  bn = 64;
 }
 
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
@@ -414,6 +579,12 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: LoRA width %d must be a multiple of 8 in [8, 64]", d.kl);
   if (d.wfmt == LSL_WFMT_NF4 && d.kn && d.N % 64)
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: NF4 transposed operand needs N %% 64 == 0");
+  if (d.kwrap && (d.kwrap % BK || d.K > 2 * d.kwrap || !d.kn))
+    return set_error(LSL_ERR_UNSUPPORTED, "gemm: wrapped reduction needs kn, kwrap %% 64 == 0 and K <= 2 kwrap");
+  // every operand is addressed through 32-bit buffer offsets (with one tile of slack)
+  const int64_t lim = ((int64_t)1 << 32) - 1;
+  if ((d.M + 256) * d.ldx * 2 > lim || (d.N + 128) * d.K * 2 > lim)
+    return set_error(LSL_ERR_UNSUPPORTED, "gemm: operand larger than 4 GiB");
   GemmKArgs a{};
   a.x = d.x; a.ldx = d.ldx;
   a.wb = d.wb; a.wq = d.wq; a.wa = d.wa;
@@ -422,30 +593,14 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   for (int i = 0; i < 4; ++i) a.seg_end[i] = d.seg_end[i];
   a.scale = d.scale;
   a.y = d.y; a.ldy = d.ldy; a.res = d.res; a.ldres = d.ldres;
-  a.tiles_m = (int)((d.M + BM - 1) / BM);
-  a.tiles_n = (int)((d.N + BN - 1) / BN);
   const Nf4Table& t = nf4_table();
   for (int i = 0; i < 16; ++i) a.cb[i] = t.cb[i];
   a.labels = d.labels; a.lse = d.lse; a.nvalid = d.nvalid; a.part = (float2*)d.part; a.zlab = d.zlab;
   a.y2 = d.y2; a.gscale = d.gscale; a.ignore = d.ignore; a.vocab_off = d.vocab_off; a.vocab = d.vocab;
   a.out32 = d.out32; a.ldo32 = d.ldo32; a.first = d.first; a.kwrap = d.kwrap;
-  dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
-  if (d.epi != EPI_BF16) {
-    if (d.wfmt != LSL_WFMT_BF16 || d.lora) return set_error(LSL_ERR_UNSUPPORTED, "gemm: CE epilogues take a bf16 weight");
-    if (d.epi == EPI_LSE && !d.kn) hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, false, 0, EPI_LSE>), grid, dim3(NTHREADS), 0, s, a);
-    else if (d.epi == EPI_CEGRAD && !d.kn) hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, false, 0, EPI_CEGRAD>), grid, dim3(NTHREADS), 0, s, a);
-    else if (d.epi == EPI_ACC32 && d.kn) hipLaunchKernelGGL((gemm_kernel<LSL_WFMT_BF16, true, 0, EPI_ACC32>), grid, dim3(NTHREADS), 0, s, a);
-    else return set_error(LSL_ERR_UNSUPPORTED, "gemm: epilogue %d with layout %d", d.epi, (int)d.kn);
-    return check_launch("gemm(ce)");
-  }
-  if (d.wfmt == LSL_WFMT_NF4) {
-    if (d.kn) launch_lora_variant<LSL_WFMT_NF4, true>(a, d.lora, s, grid);
-    else launch_lora_variant<LSL_WFMT_NF4, false>(a, d.lora, s, grid);
-  } else {
-    if (d.kn) launch_lora_variant<LSL_WFMT_BF16, true>(a, d.lora, s, grid);
-    else launch_lora_variant<LSL_WFMT_BF16, false>(a, d.lora, s, grid);
-  }
-  return check_launch("gemm");
+  int bn, bm;
+  gemm_tile_shape(d.M, d.N, bn, bm);
+  return bm == 256 ? launch_cfg<64, 256>(d, a, s) : launch_cfg<64, 128>(d, a, s);
 }
 
 }  // namespace lsl
