@@ -192,6 +192,107 @@ def cpu_baseline(shape, ms):
             "est_step_s": step_s}
 
 
+# ---------------------------------------------------------------- profiling
+# The timed kernel is recognised in rocprofv3 output by its name and its grid:
+# one 256-thread workgroup per 256 x 64 (or 128 x 64 below 1024 rows) output tile.
+CALIB_MIB = 256
+
+
+def gu_grid_items(shape, ms):
+    T = ms.batch * ms.seq
+    bm = 256 if T >= 1024 else 128
+    return -(-T // bm) * -(-2 * shape.inter // 64) * 256
+
+
+def gu_algorithmic_bytes(shape, ms):
+    """Bytes the gate|up forward launch must move at least once: x, the NF4
+    codes and absmax, the LoRA B rows and x A^T, and the bf16 output."""
+    T, K, N, kl = ms.batch * ms.seq, shape.hidden, 2 * shape.inter, 2 * shape.lora_r
+    return T * K * 2 + N * K // 2 + N * K // 64 * 4 + N * kl * 2 + T * kl * 2 + T * N * 2
+
+
+def calib_copy():
+    """A plain copy kernel of known size for scaling the HBM byte counters:
+    elementwise negation of CALIB_MIB MiB of bf16 (reads and writes that much)."""
+    import torch
+    n = CALIB_MIB << 20
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, pattern):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not hits:
+        sys.exit(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def _grid_items(r):
+    if "Grid_Size" in r:
+        return int(float(r["Grid_Size"]))
+    return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+
+
+def summarize_trace(d, args):
+    """Markdown summary of a `rocprofv3 --kernel-trace --stats -f csv` run: the
+    top kernels by total time, and the timed GEMM's dispatches (by grid)."""
+    wl, shape, ms = workload(args.workload)
+    stats = _rows(_find(d, "*kernel_stats.csv"))
+    out = ["| kernel | calls | total ms | avg us | % |", "|---|---:|---:|---:|---:|"]
+    for r in stats[:25]:
+        name = r["Name"] if len(r["Name"]) < 110 else r["Name"][:107] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    trace = _rows(_find(d, "*kernel_trace.csv"))
+    g = gu_grid_items(shape, ms)
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+            if "gemm_kernel" in r["Kernel_Name"] and _grid_items(r) == g]
+    out.append("")
+    if durs:
+        out.append(f"gate|up forward GEMM dispatches (gemm_kernel, {g} work-items): {len(durs)} calls, "
+                   f"average {sum(durs) / len(durs):.1f} us, min {min(durs):.1f} us, max {max(durs):.1f} us")
+    print("\n".join(out))
+
+
+def summarize_counters(fetch_dir, write_dir, args):
+    """Scale the timed GEMM's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what
+    the same counters read for the calibration copy, and write the counters file
+    the benchmark reports as roofline traffic."""
+    wl, shape, ms = workload(args.workload)
+    g = gu_grid_items(shape, ms)
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _rows(_find(d, "*counter_collection.csv")) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]
+                and _grid_items(r) >= 1 << 20]
+        gemm = [float(r["Counter_Value"]) for r in rows if "gemm_kernel" in r["Kernel_Name"] and _grid_items(r) == g]
+        if not copy or not gemm:
+            sys.exit(f"{counter}: copy dispatches {len(copy)}, gemm dispatches {len(gemm)}")
+        kib_copy = sum(copy) / len(copy)
+        scale = (CALIB_MIB << 20) / (kib_copy * 1024.0)
+        res[counter] = {"gemm_kib_per_dispatch": sum(gemm) / len(gemm), "dispatches": len(gemm),
+                        "copy_kib_per_dispatch": kib_copy, "copy_bytes_known": CALIB_MIB << 20, "scale": scale,
+                        "gemm_bytes_per_dispatch": sum(gemm) / len(gemm) * 1024.0 * scale}
+    src = open(os.path.join(ROOT, "layer_streamed_lora_amd", "csrc", "gemm.hip"), "rb").read()
+    hbm = res["FETCH_SIZE"]["gemm_bytes_per_dispatch"] + res["WRITE_SIZE"]["gemm_bytes_per_dispatch"]
+    doc = {"kernel": "gemm_kernel<NF4, NK, LoRA-fwd> gate|up", "workload": args.workload,
+           "gemm_hip_sha256": hashlib.sha256(src).hexdigest(), "counters": res,
+           "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": gu_algorithmic_bytes(shape, ms),
+           "commands": args.commands}
+    with open(COUNTERS, "w") as f:
+        json.dump(doc, f, indent=1)
+    print(json.dumps(doc, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,7 +301,17 @@ def main():
     ap.add_argument("--workload", default="llama8b_nf4")
     ap.add_argument("--no-resident", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one plain copy kernel of known size first (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="summarise a rocprofv3 kernel-trace csv run and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc csv runs into the committed counters file and exit")
+    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the counters file")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU only (one process, one MI355X); "
@@ -212,6 +323,8 @@ def main():
     import synth
     lsl.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calib_copy:
+        calib_copy()
     wl, shape, ms = workload(args.workload)
     T = ms.batch * ms.seq
     log(f"building {args.workload}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.wfmt} base")
