@@ -184,6 +184,8 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
 }
 
 // y = x W_i^T + s t B_i^T (+ res); t = x A_i^T computed first.
+// Forward of one fused LoRA linear: t = x A^T, y = x W^T + s t B^T (+ res).
+// With y == nullptr only t is computed.
 static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    int i, const uint16_t* x, uint16_t* t, uint16_t* y, const uint16_t* res,
                                    float* part, hipStream_t s) {
@@ -195,6 +197,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   nt.p = x; nt.ldp = k; nt.T = d.T; nt.K = k; nt.kl = kl; nt.a_full = lo->A[i];
   nt.out = t; nt.ldo = kl; nt.ws = part;
   LSL_TRY(lora_nt_launch(nt, s));
+  if (!y) return LSL_OK;
   GemmDesc g;
   g.x = x; g.ldx = k; g.wfmt = c->wfmt; g.kn = false;
   g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i];
@@ -273,6 +276,8 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
   LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, s));
   LSL_TRY(swiglu_fwd_launch(gu, d.T, d.I, a, s));
+  // out == nullptr (the backward's recompute): the layer output itself is not
+  // needed, only the LoRA product t of the down projection (for its dB)
   return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, s);
 }
 
@@ -333,9 +338,10 @@ extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* la
   char* w = (char*)ws;
   LayerPtrs W = ptrs_of(cfg, layer_blob);
   Dims d = dims_of(cfg, batch, seq);
-  // recompute the forward; its output row block is not needed, so it lands in dn1 (overwritten later)
+  // recompute the forward up to what the backward reads (every intermediate
+  // except the layer output, whose down-projection GEMM is skipped)
   uint16_t* dn1 = (uint16_t*)(w + p.dn1);
-  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, dn1, w, p, (float*)(w + p.o32), s));
+  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, (float*)(w + p.o32), s));
   float* part = (float*)(w + p.part);
   uint16_t* qkv = (uint16_t*)(w + p.qkv);
   uint16_t* dqkv = (uint16_t*)(w + p.dqkv);

@@ -7,13 +7,15 @@
 // owns one query column: the running max/sum of the online softmax need one
 // value per lane, and the probabilities feed the P V product straight from
 // registers (the reduction index of an MFMA may be permuted freely as long as
-// both operands use the same permutation; V^T is staged in LDS to match).
+// both operands use the same permutation; the V^T operand is read in that order
+// from the row-major V tile with transposing LDS reads).
 // The log-sum-exp per query row is saved for the backward.
 //
 // Backward (the standard gradient of softmax attention, recomputing P from the
-// saved log-sum-exp): D_q = sum_d dO O; a dK/dV kernel owns a 64-key tile (one
-// 16-key slice per wave) and sums over the G query heads and all query tiles in
-// a fixed order; a dQ kernel owns query tiles like the forward. No atomics.
+// saved log-sum-exp): D_q = sum_d dO O; a dK/dV kernel owns a 32-key tile and
+// sums over the G query heads (split over up to four head groups of waves,
+// added in a fixed order at the end) and all query tiles; a dQ kernel owns
+// query tiles like the forward. No atomics; every tile is staged row-major.
 #include "common.h"
 #include "api_util.h"
 
@@ -39,12 +41,10 @@ struct AttnArgs {
 LSL_DEV f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// 2^x on the hardware exponential (results below 2^-126 flush to zero, which
+// a probability of that size may); exp2_ftz(-inf) = 0.
+LSL_DEV float exp2_ftz(float x) { return __builtin_amdgcn_exp2f(x); }
 LSL_DEV bf16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-// two 4-element (8-byte) pieces -> one fragment (the permuted reduction index)
-LSL_DEV bf16x8 ld4x2(const uint16_t* p0, const uint16_t* p1) {
-  u32x2 a = *reinterpret_cast<const u32x2*>(p0), b = *reinterpret_cast<const u32x2*>(p1);
-  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-}
 LSL_DEV bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
   return __builtin_bit_cast(bf16x8, u32x4{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])});
 }
@@ -58,126 +58,170 @@ LSL_DEV void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   lo = pack8(ra, rb);
 }
 
-// Stage rows [r0, r0+nrows) x D of a strided bf16 matrix (zero beyond `valid` rows)
-// into LDS row-major [row][D + 8] and/or transposed [D][nrows + 8].
-template <int D>
-LSL_DEV void stage_rows(const uint16_t* __restrict__ src, int64_t ld, int r0, int nrows, int valid, uint16_t* rm,
-                        uint16_t* tr, int tid, int nthreads) {
-  const int chunks = nrows * (D / 8);
-  for (int c = tid; c < chunks; c += nthreads) {
-    int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    u32x4 v = (r0 + row) < valid ? *reinterpret_cast<const u32x4*>(src + (int64_t)(r0 + row) * ld + col) : u32x4{0, 0, 0, 0};
-    if (rm) *reinterpret_cast<u32x4*>(rm + row * (D + 8) + col) = v;
-    if (tr) {
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
+// lane j passes the address of row (j >> 2), columns 4 (j & 3) .. +3 of a 4 x 16
+// block and receives column j of the block, rows 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+LSL_DEV u32x2 ld_tr4(const uint16_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+// MFMA operand whose reduction index runs down the rows of a row-major LDS tile:
+// lane l (g = l >> 4) gets column c0 + l % 16 at rows r0 + 4g + s (slots 0..3)
+// and r0 + 16 + 4g + s (slots 4..7) -- the permuted reduction order in which
+// two 16-row MFMA results are packed into one operand (pack8 / split8).
+LSL_DEV bf16x8 ld_tr8(const uint16_t* tile, int ld, int r0, int c0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = tile + (r0 + 4 * g + (j >> 2)) * ld + c0 + 4 * (j & 3);
+  const u32x2 x = ld_tr4(p), y = ld_tr4(p + 16 * ld);
+  return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// A 64-row x D tile of a strided bf16 matrix moved global -> registers -> LDS
+// (row-major, row stride D + 8) by the NT threads of a workgroup. Rows past
+// `valid` read a clamped in-range row (callers mask them out), so the loads are
+// branch-free and are only waited for at the LDS store: load() for the next
+// tile is issued before the current one is computed.
+template <int D, int NT>
+struct TileStage {
+  static constexpr int CHUNKS = 64 * D / 8;
+  static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  u32x4 v[CPT];
+  LSL_DEV void load(const uint16_t* __restrict__ src, int64_t ld, int r0, int valid, int tid) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t w = v[e >> 1];
-        tr[(col + e) * (nrows + 8) + row] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFF));
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        const int64_t r = min(r0 + row, valid - 1);
+        v[i] = *reinterpret_cast<const u32x4*>(src + r * ld + col);
       }
     }
   }
-}
+  LSL_DEV void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(dst + row * (D + 8) + col) = v[i];
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------- forward
-// grid (ceil(seq/32), n_kv, batch), block group*64 threads.
-template <int D>
-__global__ __launch_bounds__(512) void attn_fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * 72];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = blockDim.x;
+// grid (ceil(seq / (16 NQS)), n_kv, batch), block group*64 threads; wave = query
+// head, 16 NQS queries per wave.
+template <int D, int NQS, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int QT = 16 * NQS, LD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (latest) query tiles first
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int h = kvh * a.group + wave;
-  const int q0 = qt * 32;
+  const int q0 = qt * QT;
   const int64_t rowbase = (int64_t)b * a.seq;
   const uint16_t* qp = a.q + rowbase * a.ldq + (int64_t)h * D;
   const uint16_t* kp = a.k + rowbase * a.ldk + (int64_t)kvh * D;
   const uint16_t* vp = a.v + rowbase * a.ldk + (int64_t)kvh * D;
   const int g = lane >> 4, c16 = lane & 15;
 
-  bf16x8 qf[2][D / 32];
+  bf16x8 qf[NQS][D / 32];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    int q = q0 + qs * 16 + c16;
+  for (int qs = 0; qs < NQS; ++qs) {
+    const int64_t q = min(q0 + qs * 16 + c16, a.seq - 1);
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-      qf[qs][ks] = q < a.seq ? ld8(qp + (int64_t)q * a.ldq + ks * 32 + g * 8) : bf16x8{};
+    for (int ks = 0; ks < D / 32; ++ks) qf[qs][ks] = ld8(qp + q * a.ldq + ks * 32 + g * 8);
   }
-  f32x4 o[D / 16][2];
+  f32x4 o[D / 16][NQS];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) o[i][0] = o[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs) o[i][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[NQS], l[NQS];
+#pragma unroll
+  for (int qs = 0; qs < NQS; ++qs) m[qs] = -INFINITY, l[qs] = 0.f;
 
-  const int qmax = min(q0 + 31, a.seq - 1);
+  const int qmax = min(q0 + QT - 1, a.seq - 1);
   const int ntiles = qmax / 64 + 1;
+  TileStage<D, 64 * NW> kst, vst;
+  kst.load(kp, a.ldk, 0, a.seq, tid);
+  vst.load(vp, a.ldk, 0, a.seq, tid);
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * 64;
-    stage_rows<D>(kp, a.ldk, kv0, 64, a.seq, Ks, nullptr, tid, nthreads);
-    stage_rows<D>(vp, a.ldk, kv0, 64, a.seq, nullptr, Vt, tid, nthreads);
+    kst.store(Ks, tid);
+    vst.store(Vs, tid);
     __syncthreads();
-    f32x4 s[4][2];
+    if (j + 1 < ntiles) {
+      kst.load(kp, a.ldk, kv0 + 64, a.seq, tid);
+      vst.load(vp, a.ldk, kv0 + 64, a.seq, tid);
+    }
+    // S^T: lane holds kv = kv0 + kvs*16 + 4g + i, q = q0 + qs*16 + c16
+    f32x4 sc[4][NQS];
 #pragma unroll
     for (int kvs = 0; kvs < 4; ++kvs) {
-      s[kvs][0] = s[kvs][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qs = 0; qs < NQS; ++qs) sc[kvs][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        bf16x8 kf = ld8(Ks + (kvs * 16 + c16) * (D + 8) + ks * 32 + g * 8);
-        s[kvs][0] = mfma(kf, qf[0][ks], s[kvs][0]);
-        s[kvs][1] = mfma(kf, qf[1][ks], s[kvs][1]);
+        const bf16x8 kf = ld8(Ks + (kvs * 16 + c16) * LD + ks * 32 + g * 8);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) sc[kvs][qs] = mfma(kf, qf[qs][ks], sc[kvs][qs]);
       }
     }
-    bf16x8 pf[2][2], pl[2][2];
+    bf16x8 pf[NQS][2];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
+    for (int qs = 0; qs < NQS; ++qs) {
       const int q = q0 + qs * 16 + c16;
       float mt = -INFINITY;
 #pragma unroll
       for (int kvs = 0; kvs < 4; ++kvs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int kv = kv0 + kvs * 16 + g * 4 + i;
-          float x = (kv <= q && kv < a.seq) ? s[kvs][qs][i] * a.scale_log2 : -INFINITY;
-          s[kvs][qs][i] = x;
+          const int kv = kv0 + kvs * 16 + g * 4 + i;
+          const float x = (kv <= q && kv < a.seq) ? sc[kvs][qs][i] * a.scale_log2 : -INFINITY;
+          sc[kvs][qs][i] = x;
           mt = fmaxf(mt, x);
         }
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m[qs], mt);
-      const float alpha = exp2f(m[qs] - mn);
+      const float mn = fmaxf(m[qs], mt);  // finite: key 0 is visible to every query
+      const float alpha = exp2_ftz(m[qs] - mn);
       m[qs] = mn;
       float ls = 0.f;
 #pragma unroll
       for (int kvs = 0; kvs < 4; ++kvs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p = exp2f(s[kvs][qs][i] - mn);
-          s[kvs][qs][i] = p;
-          ls += p;
+          const float pv = exp2_ftz(sc[kvs][qs][i] - mn);
+          sc[kvs][qs][i] = pv;
+          ls += pv;
         }
       l[qs] = l[qs] * alpha + ls;
 #pragma unroll
       for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[ds][qs][i] *= alpha;
-      split8(s[0][qs], s[1][qs], pf[qs][0], pl[qs][0]);
-      split8(s[2][qs], s[3][qs], pf[qs][1], pl[qs][1]);
+      pf[qs][0] = pack8(sc[0][qs], sc[1][qs]);
+      pf[qs][1] = pack8(sc[2][qs], sc[3][qs]);
     }
+    // O^T += V^T P^T (reduction over the 64 keys in the permuted order of pf)
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
-      const uint16_t* vr = Vt + (ds * 16 + c16) * 72;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 vf = ld4x2(vr + kk * 32 + g * 4, vr + kk * 32 + 16 + g * 4);
-        o[ds][0] = mfma(vf, pf[0][kk], o[ds][0]);
-        o[ds][0] = mfma(vf, pl[0][kk], o[ds][0]);
-        o[ds][1] = mfma(vf, pf[1][kk], o[ds][1]);
-        o[ds][1] = mfma(vf, pl[1][kk], o[ds][1]);
+        const bf16x8 vf = ld_tr8(Vs, LD, kk * 32, ds * 16, lane);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) o[ds][qs] = mfma(vf, pf[qs][kk], o[ds][qs]);
       }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < NQS; ++qs) {
     float lt = l[qs] + __shfl_xor(l[qs], 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     const int q = q0 + qs * 16 + c16;
@@ -228,24 +272,29 @@ __global__ void attn_dsum_kernel(const AttnArgs a) {
   }
 }
 
-// dK, dV for one 64-key tile of one kv head. grid (ceil(seq/64), n_kv, batch), 4 waves;
-// wave w owns keys kv0 + 16w .. +15. Loops over the group's query heads and over
-// 32-query tiles from the diagonal down, in a fixed order.
+// dK, dV for one 32-key tile of one kv head. grid (ceil(seq/32), n_kv, batch),
+// block 128 * HG threads with HG = min(group, 4) head groups of two waves; wave
+// (hg, w) owns keys kv0 + 16w .. +15 and the query heads hg, hg + HG, ... of the
+// kv head. Each head group walks 64-query tiles from the diagonal down (the next
+// tile is fetched into registers while the current one is computed); at the end
+// the head groups' partial dK/dV are added in head-group order through LDS.
+constexpr int DKV_QT = 64;
 template <int D>
-__global__ __launch_bounds__(256) void attn_dkv_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * 40];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[32 * (D + 8)];   // dO
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * 40];         // dO^T
-  __shared__ float lse_s[32], dsum_s[32];
+__global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
+  constexpr int LD = D + 8;
+  constexpr int CH = DKV_QT * D / 8 / 128;  // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 2 * DKV_QT * LD];
+  __shared__ float lse_s[4][DKV_QT], dsum_s[4][DKV_QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kt = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int kv0 = kt * 64;
+  const int HG = blockDim.x >> 7, hg = wave >> 1, ws = wave & 1, htid = tid & 127;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int kv0 = blockIdx.x * 32;  // heaviest (earliest) key tiles are dispatched first
   const int64_t rowbase = (int64_t)b * a.seq;
   const int g = lane >> 4, c16 = lane & 15;
-  const int mykv = kv0 + wave * 16 + c16;  // the key this lane's B-operand column is
+  const int mykv = kv0 + ws * 16 + c16;
+  uint16_t* Qs = lds + hg * 2 * DKV_QT * LD;
+  uint16_t* Os = Qs + DKV_QT * LD;
 
-  // K and V rows of this wave's 16 keys as B operands (rows kv, reduction d)
   bf16x8 kf[D / 32], vf[D / 32];
   {
     const uint16_t* kp = a.k + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
@@ -256,98 +305,140 @@ __global__ __launch_bounds__(256) void attn_dkv_kernel(const AttnArgs a) {
       vf[ks] = mykv < a.seq ? ld8(vp + ks * 32 + g * 8) : bf16x8{};
     }
   }
-  f32x4 dk[D / 16], dv[D / 16];  // dK^T, dV^T: lane holds [d = ds*16 + 4g + i][kv = mykv]
+  f32x4 dk[D / 16], dv[D / 16];  // dK^T, dV^T: lane holds [d = dd*16 + 4g + i][kv = mykv]
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) dk[i] = dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int qt_begin = kv0 / 32;
-  const int qt_end = (a.seq + 31) / 32;
-  for (int hh = 0; hh < a.group; ++hh) {
-    const int h = kvh * a.group + hh;
-    const uint16_t* qp = a.q + rowbase * a.ldq + (int64_t)h * D;
-    const uint16_t* dop = a.dout + rowbase * a.ldo + (int64_t)h * D;
-    const float* lsep = a.lse + ((int64_t)b * a.n_q + h) * a.seq;
-    const float* dsp = a.dsum + ((int64_t)b * a.n_q + h) * a.seq;
-    for (int qt = qt_begin; qt < qt_end; ++qt) {
-      const int q0 = qt * 32;
-      stage_rows<D>(qp, a.ldq, q0, 32, a.seq, Qs, Qt, tid, 256);
-      stage_rows<D>(dop, a.ldo, q0, 32, a.seq, Os, Ot, tid, 256);
-      if (tid < 32) {
-        int q = q0 + tid;
-        lse_s[tid] = q < a.seq ? lsep[q] * LOG2E : 0.f;
-        dsum_s[tid] = q < a.seq ? dsp[q] : 0.f;
-      }
-      __syncthreads();
-      // S[q][kv] and dP[q][kv]: lane holds q = qs*16 + 4g + i, kv = mykv
-      f32x4 s[2], dp[2];
+  const int qt_begin = kv0 / DKV_QT;
+  const int nq = (a.seq + DKV_QT - 1) / DKV_QT - qt_begin;
+  const int iters = (a.group + HG - 1) / HG * nq;  // the same count for every head group
+  u32x4 pq[CH], po[CH];
+  float plse = 0.f, pds = 0.f;
+  // Prefetch into registers. Rows past the sequence and inactive head groups
+  // load a clamped in-range row (masked out in the compute), so the loads need
+  // no branches and nothing waits for them until the LDS store.
+  auto fetch = [&](int it) {
+    const int hl = min(hg + (it / nq) * HG, a.group - 1);
+    const int q0 = (qt_begin + it % nq) * DKV_QT;
+    const int h = kvh * a.group + hl;
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        s[qs] = dp[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CH; ++c) {
+      const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
+      const int64_t q = min(q0 + row, a.seq - 1);
+      pq[c] = *reinterpret_cast<const u32x4*>(a.q + (rowbase + q) * a.ldq + (int64_t)h * D + col);
+      po[c] = *reinterpret_cast<const u32x4*>(a.dout + (rowbase + q) * a.ldo + (int64_t)h * D + col);
+    }
+    if (htid < DKV_QT) {
+      const int q = min(q0 + htid, a.seq - 1);
+      plse = a.lse[((int64_t)b * a.n_q + h) * a.seq + q];
+      pds = a.dsum[((int64_t)b * a.n_q + h) * a.seq + q];
+    }
+  };
+
+  fetch(0);
+  for (int it = 0; it < iters; ++it) {
+    const bool act = hg + (it / nq) * HG < a.group;
+    const int q0 = (qt_begin + it % nq) * DKV_QT;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Qs + row * LD + col) = pq[c];
+      *reinterpret_cast<u32x4*>(Os + row * LD + col) = po[c];
+    }
+    if (htid < DKV_QT) {
+      lse_s[hg][htid] = plse * LOG2E;
+      dsum_s[hg][htid] = pds;
+    }
+    __syncthreads();
+    if (it + 1 < iters) fetch(it + 1);
+    if (act) {
+      // S[q][kv], dP[q][kv] for 64 queries: lane holds q = qs*16 + 4g + i, kv = mykv
+      f32x4 p[4], ds[4];
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) {
+        f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          bf16x8 qa = ld8(Qs + (qs * 16 + c16) * (D + 8) + ks * 32 + g * 8);
-          bf16x8 oa = ld8(Os + (qs * 16 + c16) * (D + 8) + ks * 32 + g * 8);
-          s[qs] = mfma(qa, kf[ks], s[qs]);
-          dp[qs] = mfma(oa, vf[ks], dp[qs]);
+          sv = mfma(ld8(Qs + (qs * 16 + c16) * LD + ks * 32 + g * 8), kf[ks], sv);
+          dp = mfma(ld8(Os + (qs * 16 + c16) * LD + ks * 32 + g * 8), vf[ks], dp);
         }
-      }
-      bf16x8 pb[2], pbl[2], dsb[2], dsl[2];
-      f32x4 p[2], ds[2];
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ql = qs * 16 + g * 4 + i;
           const int q = q0 + ql;
-          float pv = (mykv <= q && q < a.seq && mykv < a.seq) ? exp2f(s[qs][i] * a.scale_log2 - lse_s[ql]) : 0.f;
+          const bool keep = mykv <= q && q < a.seq && mykv < a.seq;
+          const float pv = exp2_ftz(keep ? sv[i] * a.scale_log2 - lse_s[hg][ql] : -INFINITY);
           p[qs][i] = pv;
-          ds[qs][i] = pv * (dp[qs][i] - dsum_s[ql]);
+          ds[qs][i] = pv * (dp[i] - dsum_s[hg][ql]);
         }
-      split8(p[0], p[1], pb[0], pbl[0]);
-      split8(ds[0], ds[1], dsb[0], dsl[0]);
-      (void)pb[1]; (void)pbl[1]; (void)dsb[1]; (void)dsl[1];
-      // dV^T += dO^T P ; dK^T += Q^T dS   (reduction over the 32 queries, permuted)
-#pragma unroll
-      for (int dd = 0; dd < D / 16; ++dd) {
-        const uint16_t* otr = Ot + (dd * 16 + c16) * 40;
-        const uint16_t* qtr = Qt + (dd * 16 + c16) * 40;
-        bf16x8 oa = ld4x2(otr + g * 4, otr + 16 + g * 4);
-        bf16x8 qa = ld4x2(qtr + g * 4, qtr + 16 + g * 4);
-        dv[dd] = mfma(oa, pb[0], dv[dd]);
-        dv[dd] = mfma(oa, pbl[0], dv[dd]);
-        dk[dd] = mfma(qa, dsb[0], dk[dd]);
-        dk[dd] = mfma(qa, dsl[0], dk[dd]);
       }
-      __syncthreads();
+      // dV^T += dO^T P, dK^T += Q^T dS: reduction over the 64 queries in two
+      // 32-steps; the transposed operands come from the row-major tiles through
+      // transposing LDS reads, in the permuted order of the P / dS registers.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pb, pl, sb, sl;
+        split8(p[2 * kk], p[2 * kk + 1], pb, pl);
+        split8(ds[2 * kk], ds[2 * kk + 1], sb, sl);
+#pragma unroll
+        for (int dd = 0; dd < D / 16; ++dd) {
+          const bf16x8 oa = ld_tr8(Os, LD, kk * 32, dd * 16, lane);
+          const bf16x8 qa = ld_tr8(Qs, LD, kk * 32, dd * 16, lane);
+          dv[dd] = mfma(oa, pb, dv[dd]);
+          dv[dd] = mfma(oa, pl, dv[dd]);
+          dk[dd] = mfma(qa, sb, dk[dd]);
+          dk[dd] = mfma(qa, sl, dk[dd]);
+        }
+      }
     }
+    __syncthreads();
   }
-  if (mykv < a.seq) {
-    uint16_t* dkp = a.dk + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
-    uint16_t* dvp = a.dv + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
-    // lane holds d = dd*16 + 4g + i for key mykv: scatter 4 consecutive d
+  // add the head groups' partial sums in head-group order (LDS reused)
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+  auto slot = [&](int h, int which, int dd) { return (((h - 1) * 2 + ws) * 2 + which) * (D / 16) * 64 + dd * 64 + lane; };
+  if (hg > 0) {
 #pragma unroll
     for (int dd = 0; dd < D / 16; ++dd) {
-      const f32x4& rk = dk[dd];
-      const f32x4& rv = dv[dd];
-      *reinterpret_cast<u32x2*>(dkp + dd * 16 + g * 4) =
-          u32x2{pack2(rk[0] * a.scale, rk[1] * a.scale), pack2(rk[2] * a.scale, rk[3] * a.scale)};
-      *reinterpret_cast<u32x2*>(dvp + dd * 16 + g * 4) = u32x2{pack2(rv[0], rv[1]), pack2(rv[2], rv[3])};
+      red[slot(hg, 0, dd)] = dk[dd];
+      red[slot(hg, 1, dd)] = dv[dd];
     }
+  }
+  __syncthreads();
+  if (hg != 0 || mykv >= a.seq) return;
+  for (int h = 1; h < HG; ++h)
+#pragma unroll
+    for (int dd = 0; dd < D / 16; ++dd) {
+      const f32x4 rk = red[slot(h, 0, dd)], rv = red[slot(h, 1, dd)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dk[dd][i] += rk[i];
+        dv[dd][i] += rv[i];
+      }
+    }
+  uint16_t* dkp = a.dk + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
+  uint16_t* dvp = a.dv + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) {
+    const f32x4& rk = dk[dd];
+    const f32x4& rv = dv[dd];
+    *reinterpret_cast<u32x2*>(dkp + dd * 16 + g * 4) =
+        u32x2{pack2(rk[0] * a.scale, rk[1] * a.scale), pack2(rk[2] * a.scale, rk[3] * a.scale)};
+    *reinterpret_cast<u32x2*>(dvp + dd * 16 + g * 4) = u32x2{pack2(rv[0], rv[1]), pack2(rv[2], rv[3])};
   }
 }
 
-// dQ for one 32-query tile of each of the group's heads (wave = head), like the forward.
-// grid (ceil(seq/32), n_kv, batch), block group*64 threads.
-template <int D>
-__global__ __launch_bounds__(512) void attn_dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * 72];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = blockDim.x;
+// dQ for one 16 NQS-query tile of each of the group's heads (wave = head), like
+// the forward. grid (ceil(seq / (16 NQS)), n_kv, batch), block group*64 threads.
+template <int D, int NQS, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_dq_kernel(const AttnArgs a) {
+  constexpr int QT = 16 * NQS, LD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qt = gridDim.x - 1 - blockIdx.x;
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int h = kvh * a.group + wave;
-  const int q0 = qt * 32;
+  const int q0 = qt * QT;
   const int64_t rowbase = (int64_t)b * a.seq;
   const int g = lane >> 4, c16 = lane & 15;
   const uint16_t* qp = a.q + rowbase * a.ldq + (int64_t)h * D;
@@ -355,88 +446,132 @@ __global__ __launch_bounds__(512) void attn_dq_kernel(const AttnArgs a) {
   const uint16_t* kp = a.k + rowbase * a.ldk + (int64_t)kvh * D;
   const uint16_t* vp = a.v + rowbase * a.ldk + (int64_t)kvh * D;
 
-  bf16x8 qf[2][D / 32], of[2][D / 32];
-  float lse2[2], dsm[2];
+  bf16x8 qf[NQS][D / 32], of[NQS][D / 32];
+  float lse2[NQS], dsm[NQS];
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    int q = q0 + qs * 16 + c16;
+  for (int qs = 0; qs < NQS; ++qs) {
+    const int64_t q = min(q0 + qs * 16 + c16, a.seq - 1);
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      qf[qs][ks] = q < a.seq ? ld8(qp + (int64_t)q * a.ldq + ks * 32 + g * 8) : bf16x8{};
-      of[qs][ks] = q < a.seq ? ld8(dop + (int64_t)q * a.ldo + ks * 32 + g * 8) : bf16x8{};
+      qf[qs][ks] = ld8(qp + q * a.ldq + ks * 32 + g * 8);
+      of[qs][ks] = ld8(dop + q * a.ldo + ks * 32 + g * 8);
     }
-    lse2[qs] = q < a.seq ? a.lse[((int64_t)b * a.n_q + h) * a.seq + q] * LOG2E : 0.f;
-    dsm[qs] = q < a.seq ? a.dsum[((int64_t)b * a.n_q + h) * a.seq + q] : 0.f;
+    lse2[qs] = a.lse[((int64_t)b * a.n_q + h) * a.seq + q] * LOG2E;
+    dsm[qs] = a.dsum[((int64_t)b * a.n_q + h) * a.seq + q];
   }
-  f32x4 dq[D / 16][2];
+  f32x4 dq[D / 16][NQS];
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) dq[i][0] = dq[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < D / 16; ++i)
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs) dq[i][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int qmax = min(q0 + 31, a.seq - 1);
+  const int qmax = min(q0 + QT - 1, a.seq - 1);
   const int ntiles = qmax / 64 + 1;
+  TileStage<D, 64 * NW> kst, vst;
+  kst.load(kp, a.ldk, 0, a.seq, tid);
+  vst.load(vp, a.ldk, 0, a.seq, tid);
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * 64;
-    stage_rows<D>(kp, a.ldk, kv0, 64, a.seq, Ks, Kt, tid, nthreads);
-    stage_rows<D>(vp, a.ldk, kv0, 64, a.seq, Vs, nullptr, tid, nthreads);
+    kst.store(Ks, tid);
+    vst.store(Vs, tid);
     __syncthreads();
-    // S^T and dP^T: lane holds kv = kvs*16 + 4g + i, q = qs*16 + c16
-    bf16x8 dsf[2][2], dsl[2][2];
+    if (j + 1 < ntiles) {
+      kst.load(kp, a.ldk, kv0 + 64, a.seq, tid);
+      vst.load(vp, a.ldk, kv0 + 64, a.seq, tid);
+    }
+    // S^T and dP^T: lane holds kv = kv0 + kvs*16 + 4g + i, q = q0 + qs*16 + c16
+    bf16x8 dsf[NQS][2], dsl[NQS][2];
+    f32x4 sc[4][NQS], dp[4][NQS];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      f32x4 s[4], dp[4];
+    for (int kvs = 0; kvs < 4; ++kvs) {
 #pragma unroll
-      for (int kvs = 0; kvs < 4; ++kvs) {
-        s[kvs] = dp[kvs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qs = 0; qs < NQS; ++qs) sc[kvs][qs] = dp[kvs][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          bf16x8 ka = ld8(Ks + (kvs * 16 + c16) * (D + 8) + ks * 32 + g * 8);
-          bf16x8 va = ld8(Vs + (kvs * 16 + c16) * (D + 8) + ks * 32 + g * 8);
-          s[kvs] = mfma(ka, qf[qs][ks], s[kvs]);
-          dp[kvs] = mfma(va, of[qs][ks], dp[kvs]);
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const bf16x8 ka = ld8(Ks + (kvs * 16 + c16) * LD + ks * 32 + g * 8);
+        const bf16x8 va = ld8(Vs + (kvs * 16 + c16) * LD + ks * 32 + g * 8);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+          sc[kvs][qs] = mfma(ka, qf[qs][ks], sc[kvs][qs]);
+          dp[kvs][qs] = mfma(va, of[qs][ks], dp[kvs][qs]);
         }
       }
+    }
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs) {
       const int q = q0 + qs * 16 + c16;
 #pragma unroll
       for (int kvs = 0; kvs < 4; ++kvs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kv = kv0 + kvs * 16 + g * 4 + i;
-          float pv = (kv <= q && kv < a.seq && q < a.seq) ? exp2f(s[kvs][i] * a.scale_log2 - lse2[qs]) : 0.f;
-          s[kvs][i] = pv * (dp[kvs][i] - dsm[qs]);
+          const bool keep = kv <= q && kv < a.seq && q < a.seq;
+          const float pv = exp2_ftz(keep ? sc[kvs][qs][i] * a.scale_log2 - lse2[qs] : -INFINITY);
+          sc[kvs][qs][i] = pv * (dp[kvs][qs][i] - dsm[qs]);
         }
-      split8(s[0], s[1], dsf[qs][0], dsl[qs][0]);
-      split8(s[2], s[3], dsf[qs][1], dsl[qs][1]);
+      split8(sc[0][qs], sc[1][qs], dsf[qs][0], dsl[qs][0]);
+      split8(sc[2][qs], sc[3][qs], dsf[qs][1], dsl[qs][1]);
     }
     // dQ^T += K^T dS^T (reduction over 64 keys, permuted like the forward's P V)
 #pragma unroll
     for (int dd = 0; dd < D / 16; ++dd) {
-      const uint16_t* kr = Kt + (dd * 16 + c16) * 72;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 ka = ld4x2(kr + kk * 32 + g * 4, kr + kk * 32 + 16 + g * 4);
-        dq[dd][0] = mfma(ka, dsf[0][kk], dq[dd][0]);
-        dq[dd][0] = mfma(ka, dsl[0][kk], dq[dd][0]);
-        dq[dd][1] = mfma(ka, dsf[1][kk], dq[dd][1]);
-        dq[dd][1] = mfma(ka, dsl[1][kk], dq[dd][1]);
+        const bf16x8 ka = ld_tr8(Ks, LD, kk * 32, dd * 16, lane);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+          dq[dd][qs] = mfma(ka, dsf[qs][kk], dq[dd][qs]);
+          dq[dd][qs] = mfma(ka, dsl[qs][kk], dq[dd][qs]);
+        }
       }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
+  for (int qs = 0; qs < NQS; ++qs) {
     const int q = q0 + qs * 16 + c16;
     if (q >= a.seq) continue;
-    uint16_t* dp = a.out + (rowbase + q) * a.ldq + (int64_t)h * D;
+    uint16_t* dqp = a.out + (rowbase + q) * a.ldq + (int64_t)h * D;
 #pragma unroll
     for (int dd = 0; dd < D / 16; ++dd) {
       const f32x4& r = dq[dd][qs];
-      *reinterpret_cast<u32x2*>(dp + dd * 16 + g * 4) =
+      *reinterpret_cast<u32x2*>(dqp + dd * 16 + g * 4) =
           u32x2{pack2(r[0] * a.scale, r[1] * a.scale), pack2(r[2] * a.scale, r[3] * a.scale)};
     }
   }
 }
 
 // ---------------------------------------------------------------- host
+#ifndef LSL_ATT_QT
+#define LSL_ATT_QT 16
+#endif
+constexpr int ATT_QT = LSL_ATT_QT;  // queries per wave in the forward and dQ kernels (16 or 32)
+
+struct FwdKernel {
+  template <int D, int NW> static void launch(dim3 g, dim3 b, hipStream_t s, const AttnArgs& a) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, ATT_QT / 16, NW>), g, b, 0, s, a);
+  }
+};
+struct DqKernel {
+  template <int D, int NW> static void launch(dim3 g, dim3 b, hipStream_t s, const AttnArgs& a) {
+    hipLaunchKernelGGL((attn_dq_kernel<D, ATT_QT / 16, NW>), g, b, 0, s, a);
+  }
+};
+// one instantiation per group size (1..8 query heads per kv head, checked by attn_check)
+template <class K, int D>
+static void launch_by_group(int group, dim3 g, dim3 b, hipStream_t s, const AttnArgs& a) {
+  switch (group) {
+    case 1: K::template launch<D, 1>(g, b, s, a); break;
+    case 2: K::template launch<D, 2>(g, b, s, a); break;
+    case 3: K::template launch<D, 3>(g, b, s, a); break;
+    case 4: K::template launch<D, 4>(g, b, s, a); break;
+    case 5: K::template launch<D, 5>(g, b, s, a); break;
+    case 6: K::template launch<D, 6>(g, b, s, a); break;
+    case 7: K::template launch<D, 7>(g, b, s, a); break;
+    default: K::template launch<D, 8>(g, b, s, a); break;
+  }
+}
+
 static lsl_status attn_check(const char* fn, int64_t ldq, int64_t ldk, int batch, int seq, int n_q, int n_kv, int d) {
   if (batch < 0 || seq < 0 || n_q <= 0 || n_kv <= 0 || n_q % n_kv)
     return set_error(LSL_ERR_INVALID_ARG, "%s: bad head counts (n_q %% n_kv must be 0)", fn);
@@ -450,10 +585,10 @@ static lsl_status attn_check(const char* fn, int64_t ldq, int64_t ldk, int batch
 lsl_status attention_fwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
   AttnArgs a = a0;
   if ((int64_t)a.batch * a.seq == 0) return LSL_OK;
-  dim3 grid((unsigned)((a.seq + 31) / 32), (unsigned)a.n_kv, (unsigned)a.batch);
+  dim3 grid((unsigned)((a.seq + ATT_QT - 1) / ATT_QT), (unsigned)a.n_kv, (unsigned)a.batch);
   dim3 block((unsigned)(64 * a.group));
-  if (d == 128) hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, s, a);
+  if (d == 128) launch_by_group<FwdKernel, 128>(a.group, grid, block, s, a);
+  else launch_by_group<FwdKernel, 64>(a.group, grid, block, s, a);
   return check_launch("attention_fwd");
 }
 
@@ -465,12 +600,13 @@ lsl_status attention_bwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
   if (d == 128) hipLaunchKernelGGL(attn_dsum_kernel<128>, gs, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_dsum_kernel<64>, gs, dim3(256), 0, s, a);
   a.dsum = a.dsum_out;
-  dim3 gk((unsigned)((a.seq + 63) / 64), (unsigned)a.n_kv, (unsigned)a.batch);
-  if (d == 128) hipLaunchKernelGGL(attn_dkv_kernel<128>, gk, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(attn_dkv_kernel<64>, gk, dim3(256), 0, s, a);
-  dim3 gq((unsigned)((a.seq + 31) / 32), (unsigned)a.n_kv, (unsigned)a.batch);
-  if (d == 128) hipLaunchKernelGGL(attn_dq_kernel<128>, gq, dim3(64 * a.group), 0, s, a);
-  else hipLaunchKernelGGL(attn_dq_kernel<64>, gq, dim3(64 * a.group), 0, s, a);
+  dim3 gk((unsigned)((a.seq + 31) / 32), (unsigned)a.n_kv, (unsigned)a.batch);
+  dim3 bk((unsigned)(128 * std::min(a.group, 4)));
+  if (d == 128) hipLaunchKernelGGL(attn_dkv_kernel<128>, gk, bk, 0, s, a);
+  else hipLaunchKernelGGL(attn_dkv_kernel<64>, gk, bk, 0, s, a);
+  dim3 gq((unsigned)((a.seq + ATT_QT - 1) / ATT_QT), (unsigned)a.n_kv, (unsigned)a.batch);
+  if (d == 128) launch_by_group<DqKernel, 128>(a.group, gq, dim3(64 * a.group), s, a);
+  else launch_by_group<DqKernel, 64>(a.group, gq, dim3(64 * a.group), s, a);
   return check_launch("attention_bwd");
 }
 

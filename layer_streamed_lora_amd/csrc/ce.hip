@@ -59,22 +59,43 @@ __global__ void ce_count_valid_kernel(const int32_t* __restrict__ labels, int64_
   if (threadIdx.x == 0) *nvalid = (float)cnt[0];
 }
 
-// lse[t] = log sum over tiles (merged in tile order); lossv[t] = lse - z_label (0 if ignored)
-__global__ void ce_lse_kernel(const float2* __restrict__ part, int64_t ntiles, int64_t T,
-                              const int32_t* __restrict__ labels, const float* __restrict__ zlab, int ignore,
-                              int64_t V, float* __restrict__ lse, float* __restrict__ lossv) {
-  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float mx = -INFINITY;
-  for (int64_t i = 0; i < ntiles; ++i) mx = fmaxf(mx, part[i * T + t].x);
-  float s = 0.f;
-  for (int64_t i = 0; i < ntiles; ++i) {
-    float2 p = part[i * T + t];
-    if (p.x != -INFINITY) s += p.y * expf(p.x - mx);
+// lse[t] = log sum over the per-tile partials (max, sum of exp); lossv[t] = lse - z_label
+// (0 if ignored). A workgroup takes 64 rows; its 16 waves take every 16th tile
+// (online max/sum merge), then wave 0 merges the 16 results in wave order, so
+// the result depends on the tile count only.
+constexpr int LSE_WAVES = 16;
+__global__ __launch_bounds__(64 * LSE_WAVES) void ce_lse_kernel(const float2* __restrict__ part, int64_t ntiles,
+                                                               int64_t T, const int32_t* __restrict__ labels,
+                                                               const float* __restrict__ zlab, int ignore, int64_t V,
+                                                               float* __restrict__ lse, float* __restrict__ lossv) {
+  __shared__ float sm[LSE_WAVES][64], ss[LSE_WAVES][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 64 + lane;
+  float m = -INFINITY, sum = 0.f;
+  if (t < T) {
+    for (int64_t i = w; i < ntiles; i += LSE_WAVES) {
+      const float2 p = part[i * T + t];
+      if (p.x == -INFINITY) continue;
+      if (p.x > m) {
+        sum = sum * expf(m - p.x) + p.y;
+        m = p.x;
+      } else {
+        sum += p.y * expf(p.x - m);
+      }
+    }
   }
-  float l = mx + logf(s);
+  sm[w][lane] = m;
+  ss[w][lane] = sum;
+  __syncthreads();
+  if (w != 0 || t >= T) return;
+  float mx = -INFINITY;
+  for (int j = 0; j < LSE_WAVES; ++j) mx = fmaxf(mx, sm[j][lane]);
+  float s = 0.f;
+  for (int j = 0; j < LSE_WAVES; ++j)
+    if (sm[j][lane] != -INFINITY) s += ss[j][lane] * expf(sm[j][lane] - mx);
+  const float l = mx + logf(s);
   lse[t] = l;
-  int lab = labels[t];
+  const int lab = labels[t];
   lossv[t] = (lab != ignore && lab >= 0 && lab < V) ? l - zlab[t] : 0.f;
 }
 
@@ -138,7 +159,7 @@ extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm
   int bn, bm;
   gemm_tile_shape(T, V, bn, bm);
   int64_t ntiles = (V + bn - 1) / bn;
-  hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, (const float2*)(w + p.part),
+  hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 63) / 64)), dim3(64 * LSE_WAVES), 0, s, (const float2*)(w + p.part),
                      ntiles, T, labels, (const float*)(w + p.zlab), ignore_index, V, lse, (float*)(w + p.lossv));
   hipLaunchKernelGGL(ce_loss_kernel, dim3(1), dim3(256), 0, s, (const float*)(w + p.lossv), T, (const float*)nvalid,
                      loss);
