@@ -26,7 +26,7 @@ struct NtArgs {
   const uint16_t* rB; int r; int nseg; int64_t seg_end[4];  // B_full [K x r] (mode 1)
   int64_t T, K; int kl;
   int64_t k_per_split;
-  float* part;                      // [S][T][64]
+  float* part;                      // [S][T][kl]
 };
 
 // grid: (ceil(T/128), S); 4 waves, wave w owns rows 32w..32w+31 of the tile.
@@ -88,14 +88,16 @@ __global__ __launch_bounds__(256) void lora_nt_kernel(const NtArgs a) {
     __syncthreads();
   }
   // lane holds C[t][j..j+3], j = 16 i + 4 (lane >> 4)
-  float* dst = a.part + (int64_t)blockIdx.y * a.T * 64;
+  float* dst = a.part + (int64_t)blockIdx.y * a.T * a.kl;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int64_t t = t0 + wave * 32 + j * 16 + (lane & 15);
     if (t >= a.T) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<f32x4*>(dst + t * 64 + i * 16 + (lane >> 4) * 4) = acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int c = i * 16 + (lane >> 4) * 4;
+      if (c < a.kl) *reinterpret_cast<f32x4*>(dst + t * a.kl + c) = acc[i][j];
+    }
   }
 }
 
@@ -105,7 +107,7 @@ __global__ void nt_reduce_kernel(const float* __restrict__ part, int S, int64_t 
   if (i >= T * kl) return;
   int64_t t = i / kl; int j = (int)(i - t * kl);
   float s = 0.f;
-  for (int k = 0; k < S; ++k) s += part[((int64_t)k * T + t) * 64 + j];
+  for (int k = 0; k < S; ++k) s += part[((int64_t)k * T + t) * kl + j];
   out[t * ldo + j] = f2bf(s);
 }
 
@@ -114,10 +116,13 @@ struct TnArgs {
   const uint16_t* q; int64_t ldq;  // [T x kl]
   int64_t T, W; int kl;
   int64_t t_per_split;
-  float* part;                     // [S][W][64]
+  float* part;                     // [S][W][kl] (S > 1)
+  // S == 1: the result goes straight to dA [kl x W] or dB [W x r] (+= scale C)
+  float* dA; float* dB; float scale; int r; int nseg; SegEnds seg;
 };
 
 // grid: (ceil(W/128), S). 4 waves, wave w owns columns a = 32w..32w+31 of the tile.
+template <bool DIRECT>
 __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ps[128 * SK_LDS];  // [a][t]
   __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * SK_LDS];   // [j][t]
@@ -180,15 +185,32 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
     }
     __syncthreads();
   }
-  // lane holds C[a][j..j+3]
-  float* dst = a.part + (int64_t)blockIdx.y * a.W * 64;
+  // lane holds C[a][c..c+3], c = 16 i + 4 (lane >> 4)
+  float* dst = a.part + (int64_t)blockIdx.y * a.W * a.kl;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int64_t ac = a0 + wave * 32 + j * 16 + (lane & 15);
     if (ac >= a.W) continue;
+    int p = 0;
+    if (DIRECT && a.dB)
+      while (p < a.nseg - 1 && ac >= a.seg.e[p]) ++p;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<f32x4*>(dst + ac * 64 + i * 16 + (lane >> 4) * 4) = acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int c = i * 16 + (lane >> 4) * 4;
+      if (c >= a.kl) continue;
+      if (!DIRECT) {
+        *reinterpret_cast<f32x4*>(dst + ac * a.kl + c) = acc[i][j];
+      } else if (a.dA) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.dA[(int64_t)(c + e) * a.W + ac] += a.scale * acc[i][j][e];
+      } else if (c >= p * a.r && c < (p + 1) * a.r) {
+        f32x4* d = reinterpret_cast<f32x4*>(a.dB + ac * a.r + (c - p * a.r));
+        f32x4 v = *d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += a.scale * acc[i][j][e];
+        *d = v;
+      }
+    }
   }
 }
 
@@ -198,12 +220,12 @@ __global__ void tn_reduce_dA_kernel(const float* __restrict__ part, int S, int64
   if (i >= W * kl) return;
   int j = (int)(i / W); int64_t k = i - (int64_t)j * W;
   float s = 0.f;
-  for (int q = 0; q < S; ++q) s += part[((int64_t)q * W + k) * 64 + j];
+  for (int q = 0; q < S; ++q) s += part[((int64_t)q * W + k) * kl + j];
   dA[i] += scale * s;
 }
 
 // dB[n][i] += s * sum_s part[s][n][p(n) r + i]
-__global__ void tn_reduce_dB_kernel(const float* __restrict__ part, int S, int64_t W, int r, int nseg,
+__global__ void tn_reduce_dB_kernel(const float* __restrict__ part, int S, int64_t W, int kl, int r, int nseg,
                                     SegEnds seg, float scale, float* __restrict__ dB) {
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= W * r) return;
@@ -212,29 +234,33 @@ __global__ void tn_reduce_dB_kernel(const float* __restrict__ part, int S, int64
   while (p < nseg - 1 && n >= seg.e[p]) ++p;
   int j = p * r + i;
   float s = 0.f;
-  for (int q = 0; q < S; ++q) s += part[((int64_t)q * W + n) * 64 + j];
+  for (int q = 0; q < S; ++q) s += part[((int64_t)q * W + n) * kl + j];
   dB[idx] += scale * s;
 }
 
 // ---------------------------------------------------------------- host side
-static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks) {
+// Splits of the reduction so that about `target_blocks` workgroups run, each
+// taking at least `min_steps` 64-wide steps of the reduction.
+static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks, int64_t min_steps) {
   int64_t steps = (red + 63) / 64;
   int64_t s = (target_blocks + tiles - 1) / tiles;
-  if (s > steps) s = steps;
+  int64_t cap = steps / min_steps;
+  if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int)s;
 }
+constexpr int64_t NT_TARGET = 256, NT_MIN_STEPS = 4, TN_TARGET = 256, TN_MIN_STEPS = 4;
 
 size_t lora_nt_ws_bytes(int64_t T, int64_t K) {
   int64_t tiles = (T + 127) / 128;
-  int S = pick_splits(tiles, K, 512);
+  int S = pick_splits(tiles, K, NT_TARGET, NT_MIN_STEPS);
   return (size_t)S * T * 64 * sizeof(float);
 }
 
 size_t lora_tn_ws_bytes(int64_t T, int64_t W) {
   int64_t tiles = (W + 127) / 128;
-  int S = pick_splits(tiles, T, 512);
-  return (size_t)S * W * 64 * sizeof(float);
+  int S = pick_splits(tiles, T, TN_TARGET, TN_MIN_STEPS);
+  return S > 1 ? (size_t)S * W * 64 * sizeof(float) : 0;
 }
 
 lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
@@ -242,7 +268,7 @@ lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
   if (d.K % 64 || d.kl <= 0 || d.kl > 64 || d.kl % 8)
     return set_error(LSL_ERR_UNSUPPORTED, "lora side product: K %% 64 and kl in [8, 64] multiple of 8 required");
   int64_t tiles = (d.T + 127) / 128;
-  int S = pick_splits(tiles, d.K, 512);
+  int S = pick_splits(tiles, d.K, NT_TARGET, NT_MIN_STEPS);
   int64_t steps = d.K / 64;
   int64_t per = ((steps + S - 1) / S) * 64;
   S = (int)((d.K + per - 1) / per);
@@ -265,24 +291,28 @@ lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
     return set_error(LSL_ERR_UNSUPPORTED, "lora grad: kl in [8, 64] multiple of 8 and W %% 8 required");
   if (d.T == 0) return LSL_OK;
   int64_t tiles = (d.W + 127) / 128;
-  int S = pick_splits(tiles, d.T, 512);
+  int S = pick_splits(tiles, d.T, TN_TARGET, TN_MIN_STEPS);
   int64_t steps = (d.T + 63) / 64;
   int64_t per = ((steps + S - 1) / S) * 64;
   S = (int)((d.T + per - 1) / per);
   TnArgs a{};
   a.p = d.p; a.ldp = d.ldp; a.q = d.q; a.ldq = d.ldq; a.T = d.T; a.W = d.W; a.kl = d.kl;
   a.t_per_split = per; a.part = d.ws;
-  hipLaunchKernelGGL(lora_tn_kernel, dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
+  a.dA = d.dA; a.dB = d.dA ? nullptr : d.dB; a.scale = d.scale; a.r = d.r; a.nseg = d.nseg;
+  for (int i = 0; i < 4; ++i) a.seg.e[i] = d.seg_end[i];
+  if (S == 1) {
+    hipLaunchKernelGGL(lora_tn_kernel<true>, dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
+    return check_launch("lora_tn");
+  }
+  hipLaunchKernelGGL(lora_tn_kernel<false>, dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
   if (d.dA) {
     int64_t n = d.W * d.kl;
     hipLaunchKernelGGL(tn_reduce_dA_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        (const float*)d.ws, S, d.W, d.kl, d.scale, d.dA);
   } else {
     int64_t n = d.W * d.r;
-    SegEnds se;
-    for (int i = 0; i < 4; ++i) se.e[i] = d.seg_end[i];
     hipLaunchKernelGGL(tn_reduce_dB_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float*)d.ws, S, d.W, d.r, d.nseg, se, d.scale, d.dB);
+                       (const float*)d.ws, S, d.W, d.kl, d.r, d.nseg, a.seg, d.scale, d.dB);
   }
   return check_launch("lora_tn");
 }
