@@ -136,7 +136,10 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
   p.gu = take(T * 2 * d.I * 2);
   p.a = take(T * d.I * 2);
   p.td = take(T * d.r * 2);
-  size_t part = std::max({lora_nt_ws_bytes(d.T, d.H), lora_nt_ws_bytes(d.T, d.Q), lora_nt_ws_bytes(d.T, d.I)});
+  // one region reused in turn by LoRA split partials and GEMM split-K partials
+  size_t part = std::max({lora_nt_ws_bytes(d.T, d.H), lora_nt_ws_bytes(d.T, d.Q), lora_nt_ws_bytes(d.T, d.I),
+                          gemm_split_bytes(d.T, d.NQKV, d.H), gemm_split_bytes(d.T, d.H, d.Q),
+                          gemm_split_bytes(d.T, 2 * d.I, d.H), gemm_split_bytes(d.T, d.H, d.I)});
   if (mode == LSL_MODE_BWD) {
     p.ud = take(T * d.r * 2);
     p.da = take(T * d.I * 2);
@@ -153,7 +156,9 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
     p.o32 = take(T * d.Q * 4);
     part = std::max({part, lora_nt_ws_bytes(d.T, d.NQKV), lora_nt_ws_bytes(d.T, 2 * d.I),
                      lora_tn_ws_bytes(d.T, d.H), lora_tn_ws_bytes(d.T, d.Q), lora_tn_ws_bytes(d.T, d.I),
-                     lora_tn_ws_bytes(d.T, d.NQKV), lora_tn_ws_bytes(d.T, 2 * d.I)});
+                     lora_tn_ws_bytes(d.T, d.NQKV), lora_tn_ws_bytes(d.T, 2 * d.I),
+                     gemm_split_bytes(d.T, d.H, d.NQKV), gemm_split_bytes(d.T, d.Q, d.H),
+                     gemm_split_bytes(d.T, d.H, 2 * d.I), gemm_split_bytes(d.T, d.I, d.H)});
   }
   p.part = take(part);
   p.total = off;
@@ -207,7 +212,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   else if (i == LSL_M_GU) { g.seg_end[0] = d.I; g.seg_end[1] = 2 * d.I; }
   else g.seg_end[0] = n;
   g.scale = c->lora_scale;
-  g.y = y; g.ldy = n; g.res = res; g.ldres = n;
+  g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part;
   timing_mark(1 + i, true, s);
   lsl_status st = gemm_launch(g, s);
   timing_mark(1 + i, false, s);
@@ -237,7 +242,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
     g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i];
     g.M = d.T; g.N = k; g.K = n;
     g.lora = 2; g.la = u; g.ldla = kl; g.kl = kl; g.lb = lo->A[i]; g.r = d.r;
-    g.scale = c->lora_scale; g.y = dx; g.ldy = k;
+    g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part;
     timing_mark(5 + i, true, s);
     lsl_status st = gemm_launch(g, s);
     timing_mark(5 + i, false, s);

@@ -11,10 +11,16 @@ namespace lsl {
 
 bool lora_rank_ok(int32_t r) { return r >= 8 && r <= 64 && r % 8 == 0; }
 
-size_t linear_ws_fwd(int64_t T, int64_t K) { return lora_nt_ws_bytes(T, K); }
+// fwd: the t = x A^T partials, then the GEMM's split-K partials (in turn)
+size_t linear_ws_fwd(int64_t T, int64_t N, int64_t K) {
+  return std::max(lora_nt_ws_bytes(T, K), gemm_split_bytes(T, N, K));
+}
 
+// bwd: u = dy B [T x r] bf16, then one region reused in turn by the u partials,
+// the dX GEMM's split-K partials and the dA / dB partials
 size_t linear_ws_bwd(int64_t T, int64_t N, int64_t K, int r) {
   size_t part = lora_nt_ws_bytes(T, N);
+  part = std::max(part, gemm_split_bytes(T, K, N));
   part = std::max(part, lora_tn_ws_bytes(T, K));
   part = std::max(part, lora_tn_ws_bytes(T, N));
   return align256((size_t)T * r * 2) + part;
@@ -46,7 +52,7 @@ static void weight_into(GemmDesc& g, const lsl_weight* W) {
 
 extern "C" size_t lsl_lora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in, int32_t r) {
   if (T < 0 || n_out <= 0 || k_in <= 0 || !lora_rank_ok(r)) return 0;
-  return std::max(linear_ws_fwd(T, k_in), linear_ws_bwd(T, n_out, k_in, r));
+  return std::max(linear_ws_fwd(T, n_out, k_in), linear_ws_bwd(T, n_out, k_in, r));
 }
 
 extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W, const uint16_t* A,
@@ -58,8 +64,9 @@ extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_we
   if (!lora_rank_ok(r)) return set_error(LSL_ERR_UNSUPPORTED, "%s: rank %d must be a multiple of 8 in [8, 64]", fn, r);
   if (T == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x, A, B, y, t_out}));
-  if (ws_bytes < linear_ws_fwd(T, W->k_in) || (!ws && linear_ws_fwd(T, W->k_in)))
-    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, linear_ws_fwd(T, W->k_in));
+  const size_t need = linear_ws_fwd(T, W->n_out, W->k_in);
+  if (ws_bytes < need || (need && (!ws || !aligned(ws, 256))))
+    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   LoraNt nt;
   nt.p = x; nt.ldp = W->k_in; nt.T = T; nt.K = W->k_in; nt.kl = r; nt.a_full = A;
@@ -69,7 +76,7 @@ extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_we
   g.x = x; g.ldx = W->k_in; weight_into(g, W); g.kn = false;
   g.M = T; g.N = W->n_out; g.K = W->k_in;
   g.lora = 1; g.la = t_out; g.ldla = r; g.kl = r; g.lb = B; g.r = r; g.nseg = 1; g.seg_end[0] = W->n_out;
-  g.scale = scale; g.y = y; g.ldy = W->n_out;
+  g.scale = scale; g.y = y; g.ldy = W->n_out; g.split_ws = (float*)ws;
   return gemm_launch(g, s);
 }
 
@@ -100,7 +107,7 @@ extern "C" lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, cons
     g.x = dy; g.ldx = N; weight_into(g, W); g.kn = true;
     g.M = T; g.N = K; g.K = N;
     g.lora = 2; g.la = u; g.ldla = r; g.kl = r; g.lb = A; g.r = r;
-    g.scale = scale; g.y = dx; g.ldy = K;
+    g.scale = scale; g.y = dx; g.ldy = K; g.split_ws = part;
     LSL_TRY(gemm_launch(g, s));
   }
   LoraTn ta;

@@ -22,8 +22,14 @@ struct GemmDesc {
   float gscale = 1.f; int ignore = -100; int64_t vocab_off = 0, vocab = 0;
   float* out32 = nullptr; int64_t ldo32 = 0; int first = 1;
   int64_t kwrap = 0;
+  // split-K scratch for the bf16 epilogue: gemm_split_bytes(M, N, K) bytes
+  float* split_ws = nullptr;
 };
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
+// Reduction splits gemm_launch uses for a bf16-epilogue GEMM of this shape, and
+// the float32 scratch they need (0 when the GEMM is not split).
+int gemm_splits(int64_t M, int64_t N, int64_t K);
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
 // Tile shape gemm_launch picks for an M x N output (bn weight rows, bm tokens).
 void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm);
 }  // namespace lsl

@@ -55,6 +55,8 @@ struct GemmKArgs {
   float gscale; int ignore; int64_t vocab_off, vocab;
   float* out32; int64_t ldo32; int first;
   int64_t kwrap;             // KN operand: reduction index k reads weight row k mod kwrap (K <= 2 kwrap)
+  int ksplit; int kt_per_split;  // split-K: workgroup b takes split b / (tiles_m tiles_n)
+  float* spart;                  // float32 partials [ksplit][M][N]
 };
 
 enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_CEGRAD = 2, EPI_ACC32 = 3 };
@@ -268,9 +270,8 @@ LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x4 (&acc)[4][MS
 
 // Tile index remap: XCD x (= workgroup id mod 8) gets a contiguous range of
 // tiles, ordered m-fastest so that the tiles sharing a weight tile run together.
-LSL_DEV void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+LSL_DEV void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   int nt = tiles_m * tiles_n;
-  int b = blockIdx.x;
   int per = nt / 8;
   int t = b;
   if (b < per * 8) t = (b & 7) * per + (b >> 3);
@@ -291,7 +292,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
   const int wn = wave % G::WN, wm = wave / G::WN;
   const int wm0 = wm * G::WTM;
   int tm, tn;
-  tile_coords(a.tiles_m, a.tiles_n, tm, tn);
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int split = (int)blockIdx.x / ntiles;
+  tile_coords((int)blockIdx.x - split * ntiles, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   if constexpr (WFMT == LSL_WFMT_NF4) lut[tid] = make_float2(a.cb[tid >> 4], a.cb[tid & 15]);
@@ -302,7 +305,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
 #pragma unroll
     for (int j = 0; j < MS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = (int)(a.K / BK);
+  // this workgroup's reduction steps [kt0, kt0 + KT); the LoRA step goes with the last split
+  const int kt0 = split * a.kt_per_split;
+  const int KT = min((int)(a.K / BK) - kt0, a.kt_per_split);
+  const bool last_split = split == a.ksplit - 1;
   if constexpr (PIPE == 2) {
     // tile k computes from LDS buffer k % 2 while tile k + 1 waits in registers
     // (set (k + 1) % 2) for its LDS store and tile k + 2 is in flight
@@ -312,11 +318,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
     wl0.init(a, n0, tid);
     xl1 = xl0;
     wl1 = wl0;
-    xl0.load(a.x, a.ldx, a.M, 0);
-    wl0.load(a, 0);
+    xl0.load(a.x, a.ldx, a.M, (int64_t)kt0 * BK);
+    wl0.load(a, (int64_t)kt0 * BK);
     if (KT > 1) {
-      xl1.load(a.x, a.ldx, a.M, BK);
-      wl1.load(a, BK);
+      xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + 1) * BK);
+      wl1.load(a, (int64_t)(kt0 + 1) * BK);
     }
     __syncthreads();  // lut visible
     xl0.store(Xs[0], tid);
@@ -324,8 +330,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
     __syncthreads();
     for (int kt = 0; kt < KT; kt += 2) {
       if (kt + 2 < KT) {
-        xl0.load(a.x, a.ldx, a.M, (int64_t)(kt + 2) * BK);
-        wl0.load(a, (int64_t)(kt + 2) * BK);
+        xl0.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 2) * BK);
+        wl0.load(a, (int64_t)(kt0 + kt + 2) * BK);
       }
       mma_tile<MS>(Ws[0], Xs[0], acc, wn, wm0, lane, 2);
       if (kt + 1 < KT) {
@@ -335,8 +341,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
       __syncthreads();
       if (kt + 1 >= KT) break;
       if (kt + 3 < KT) {
-        xl1.load(a.x, a.ldx, a.M, (int64_t)(kt + 3) * BK);
-        wl1.load(a, (int64_t)(kt + 3) * BK);
+        xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 3) * BK);
+        wl1.load(a, (int64_t)(kt0 + kt + 3) * BK);
       }
       mma_tile<MS>(Ws[1], Xs[1], acc, wn, wm0, lane, 2);
       if (kt + 2 < KT) {
@@ -353,8 +359,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
     WLoader<WFMT, KN, BN> wl;
     xl.init(a.ldx, m0, tid);
     wl.init(a, n0, tid);
-    xl.load(a.x, a.ldx, a.M, 0);
-    wl.load(a, 0);
+    xl.load(a.x, a.ldx, a.M, (int64_t)kt0 * BK);
+    wl.load(a, (int64_t)kt0 * BK);
     __syncthreads();  // lut visible
     xl.store(Xs[0], tid);
     wl.store(Ws[0], lut, tid);
@@ -363,8 +369,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
       const int cur = PIPE == 1 ? (kt & 1) : 0;
       const bool more = kt + 1 < KT;
       if (more) {
-        xl.load(a.x, a.ldx, a.M, (int64_t)(kt + 1) * BK);
-        wl.load(a, (int64_t)(kt + 1) * BK);
+        xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
+        wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
       }
       mma_tile<MS>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 2);
       if constexpr (PIPE == 0) __syncthreads();
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
   }
 
   // ---- LoRA K-step (kl <= 64, zero padded to 64) into separate accumulators
-  if constexpr (LORA != 0) {
+  if constexpr (LORA != 0) if (last_split) {
     uint16_t* Ls = Xs[0];
     uint16_t* Lt = Ws[0];
     for (int c = tid; c < BM * 8; c += NTHREADS) {
@@ -480,6 +486,21 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
     }
     return;
   }
+  if (EPI == EPI_BF16 && a.ksplit > 1) {
+    // split-K: float32 partial of this split; gemm_split_reduce adds the splits
+    float* dst = a.spart + (int64_t)split * a.M * a.N;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int mi = 0; mi < MS; ++mi) {
+        const int64_t m = m0 + wm0 + mi * 16 + (lane & 15);
+        if (m < a.M) *reinterpret_cast<f32x4*>(dst + m * a.N + n) = acc[ni][mi];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
@@ -525,6 +546,27 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
   }
 }
 
+// y[m][n] = bf16(sum over splits in index order) (+ residual, rounded again),
+// the same rounding as the unsplit bf16 epilogue. One thread per 4 outputs.
+__global__ void gemm_split_reduce(const float* __restrict__ part, int S, int64_t M, int64_t N,
+                                  const uint16_t* __restrict__ res, int64_t ldres, uint16_t* __restrict__ y,
+                                  int64_t ldy) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= M * N) return;
+  const int64_t m = i / N, n = i - m * N;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 p = *reinterpret_cast<const f32x4*>(part + (int64_t)s * M * N + i);
+    v = f32x4{v[0] + p[0], v[1] + p[1], v[2] + p[2], v[3] + p[3]};
+  }
+  if (res) {
+    const u32x2 r = *reinterpret_cast<const u32x2*>(res + m * ldres + n);
+    v = f32x4{bf2f(f2bf(v[0])) + lo_bf(r[0]), bf2f(f2bf(v[1])) + hi_bf(r[0]), bf2f(f2bf(v[2])) + lo_bf(r[1]),
+              bf2f(f2bf(v[3])) + hi_bf(r[1])};
+  }
+  *reinterpret_cast<u32x2*>(y + m * ldy + n) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+}
+
 template <int WFMT, bool KN, int BN, int BM>
 static void launch_lora_variant(const GemmKArgs& a, int lora, hipStream_t s, dim3 grid) {
   if (lora == 0) hipLaunchKernelGGL((gemm_kernel<WFMT, KN, 0, EPI_BF16, BN, BM>), grid, dim3(NTHREADS), 0, s, a);
@@ -536,7 +578,19 @@ template <int BN, int BM>
 static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
   a.tiles_m = (int)((d.M + BM - 1) / BM);
   a.tiles_n = (int)((d.N + BN - 1) / BN);
-  dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  const int KT = (int)(d.K / BK);
+  a.ksplit = 1;
+  a.kt_per_split = KT;
+  if (d.epi == EPI_BF16) {
+    const int S = gemm_splits(d.M, d.N, d.K);
+    if (S > 1) {
+      if (!d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
+      a.kt_per_split = (KT + S - 1) / S;
+      a.ksplit = (KT + a.kt_per_split - 1) / a.kt_per_split;
+      a.spart = d.split_ws;
+    }
+  }
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.ksplit));
   if (d.epi != EPI_BF16) {
     if (d.wfmt != LSL_WFMT_BF16 || d.lora) return set_error(LSL_ERR_UNSUPPORTED, "gemm: CE epilogues take a bf16 weight");
     if (d.epi == EPI_LSE && !d.kn)
@@ -556,6 +610,11 @@ static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
     if (d.kn) launch_lora_variant<LSL_WFMT_BF16, true, BN, BM>(a, d.lora, s, grid);
     else launch_lora_variant<LSL_WFMT_BF16, false, BN, BM>(a, d.lora, s, grid);
   }
+  if (a.ksplit > 1) {
+    const int64_t n4 = d.M * d.N / 4;
+    hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
+                       a.ksplit, d.M, d.N, d.res, d.ldres, d.y, d.ldy);
+  }
   return check_launch("gemm");
 }
 
@@ -570,9 +629,34 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
   bn = 64;
 }
 
+// Split-K for GEMMs with few output tiles: enough reduction splits to give
+// about SPLIT_TARGET workgroups, each taking at least SPLIT_MIN_STEPS K-steps.
+#ifndef LSL_SPLIT_TARGET
+#define LSL_SPLIT_TARGET 512
+#endif
+#ifndef LSL_SPLIT_MIN_STEPS
+#define LSL_SPLIT_MIN_STEPS 32
+#endif
+int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  int bn, bm;
+  gemm_tile_shape(M, N, bn, bm);
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int64_t steps = K / BK;
+  int64_t S = (LSL_SPLIT_TARGET + tiles - 1) / tiles;
+  if (S > steps / LSL_SPLIT_MIN_STEPS) S = steps / LSL_SPLIT_MIN_STEPS;
+  if (S < 2) return 1;
+  const int64_t per = (steps + S - 1) / S;
+  return (int)((steps + per - 1) / per);
+}
+
+size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = gemm_splits(M, N, K);
+  return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
+}
+
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   if (d.M == 0 || d.N == 0) return LSL_OK;
-  if (d.K % BK || d.N % 8)
+  if (d.K % BK || d.N % 8 || d.K == 0)
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: K (%lld) must be a multiple of 64 and N (%lld) of 8",
                      (long long)d.K, (long long)d.N);
   if (d.lora && (d.kl <= 0 || d.kl > 64 || d.kl % 8))
