@@ -58,25 +58,6 @@ LSL_DEV void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   lo = pack8(ra, rb);
 }
 
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group,
-// lane j passes the address of row (j >> 2), columns 4 (j & 3) .. +3 of a 4 x 16
-// block and receives column j of the block, rows 0..3.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-LSL_DEV u32x2 ld_tr4(const uint16_t* p) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
-}
-// MFMA operand whose reduction index runs down the rows of a row-major LDS tile:
-// lane l (g = l >> 4) gets column c0 + l % 16 at rows r0 + 4g + s (slots 0..3)
-// and r0 + 16 + 4g + s (slots 4..7) -- the permuted reduction order in which
-// two 16-row MFMA results are packed into one operand (pack8 / split8).
-LSL_DEV bf16x8 ld_tr8(const uint16_t* tile, int ld, int r0, int c0, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const uint16_t* p = tile + (r0 + 4 * g + (j >> 2)) * ld + c0 + 4 * (j & 3);
-  const u32x2 x = ld_tr4(p), y = ld_tr4(p + 16 * ld);
-  return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
-}
-
 // A 64-row x D tile of a strided bf16 matrix moved global -> registers -> LDS
 // (row-major, row stride D + 8) by the NT threads of a workgroup. Rows past
 // `valid` read a clamped in-range row (callers mask them out), so the loads are

@@ -103,6 +103,19 @@ struct RowLoader {
 #pragma unroll
     for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(lds + (r + 32 * i) * LDSW + c) = v[i];
   }
+  // Same tile with the reduction index permuted inside each 32-group: position
+  // 8g + s holds k = 4g + s and position 8g + 4 + s holds k = 16 + 4g + s, the
+  // order in which ld_tr8 delivers the other operand.
+  LSL_DEV void store_perm(uint16_t* lds, int tid) const {
+    const int r = tid >> 3, cc = tid & 3;
+    const int c = (tid & 4) * 8 + (cc & 1) * 16 + (cc >> 1) * 4;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      uint16_t* d = lds + (r + 32 * i) * LDSW + c;
+      *reinterpret_cast<u32x2*>(d) = u32x2{v[i][0], v[i][1]};
+      *reinterpret_cast<u32x2*>(d + 8) = u32x2{v[i][2], v[i][3]};
+    }
+  }
 };
 
 template <int WFMT, bool KN, int BN>
@@ -113,7 +126,7 @@ struct WLoader<LSL_WFMT_BF16, false, BN> {
   RowLoader<BN> r;
   LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) { r.init(a.K, n0, tid); }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) { r.load(a.wb, a.K, a.N, k0); }
-  LSL_DEV void store(uint16_t* lds, const float2*, int tid) const { r.store(lds, tid); }
+  LSL_DEV void store(uint16_t* lds, const float*, int tid) const { r.store(lds, tid); }
 };
 
 // NF4 [N x K]: each of the BN rows has 32 code bytes per K-step; TPR threads per
@@ -142,38 +155,19 @@ struct WLoader<LSL_WFMT_NF4, false, BN> {
     }
     am = pa[k0 >> 6];
   }
-  LSL_DEV void store(uint16_t* lds, const float2* lut, int tid) const {
+  LSL_DEV void store(uint16_t* lds, const float* lut, int tid) const {
     const int row = tid / TPR, part = tid % TPR;
     uint32_t o[BPT];
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      float2 cv = lut[(c[j >> 2] >> ((j & 3) * 8)) & 0xFF];
-      o[j] = pack2(cv.x * am, cv.y * am);
+      const uint32_t b = c[j >> 2] >> ((j & 3) * 8);  // element 2j in the high nibble
+      o[j] = pack2(lut[(b >> 4) & 15] * am, lut[b & 15] * am);
     }
     u32x4* d = reinterpret_cast<u32x4*>(lds + row * LDSW + part * 2 * BPT);
 #pragma unroll
     for (int i = 0; i < BPT / 4; ++i) d[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
 };
-
-// Transposing store shared by the KN loaders. w[rr][j] holds n-columns 2j (low
-// half) and 2j+1 (high half) of reduction row rr; Ws[n][k] wants KR consecutive
-// k per n-column.
-template <int KR>
-LSL_DEV void store_transposed(uint16_t* lds, const uint32_t (&w)[KR][4], int q, int o) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (KR == 4) {
-      *reinterpret_cast<u32x2*>(lds + (o * 8 + 2 * j) * LDSW + q * 4) =
-          u32x2{lo_lo(w[0][j], w[1][j]), lo_lo(w[2][j], w[3][j])};
-      *reinterpret_cast<u32x2*>(lds + (o * 8 + 2 * j + 1) * LDSW + q * 4) =
-          u32x2{hi_hi(w[0][j], w[1][j]), hi_hi(w[2][j], w[3][j])};
-    } else {
-      *reinterpret_cast<uint32_t*>(lds + (o * 8 + 2 * j) * LDSW + q * 2) = lo_lo(w[0][j], w[1][j]);
-      *reinterpret_cast<uint32_t*>(lds + (o * 8 + 2 * j + 1) * LDSW + q * 2) = hi_hi(w[0][j], w[1][j]);
-    }
-  }
-}
 
 // bf16 stored [K x N] (row = reduction index): thread -> KR k-rows x 8 n-cols.
 // Columns past N read neighbouring data or zeros; their outputs are never stored.
@@ -197,7 +191,13 @@ struct WLoader<LSL_WFMT_BF16, true, BN> {
       w[rr][0] = v[0]; w[rr][1] = v[1]; w[rr][2] = v[2]; w[rr][3] = v[3];
     }
   }
-  LSL_DEV void store(uint16_t* lds, const float2*, int tid) const { store_transposed<KR>(lds, w, tid / OG, tid % OG); }
+  // row-major [k][n] tile (row stride BN + 8); the MFMA reads it transposed
+  LSL_DEV void store(uint16_t* lds, const float*, int tid) const {
+    const int q = tid / OG, o = tid % OG;
+#pragma unroll
+    for (int rr = 0; rr < KR; ++rr)
+      *reinterpret_cast<u32x4*>(lds + (q * KR + rr) * (BN + 8) + o * 8) = u32x4{w[rr][0], w[rr][1], w[rr][2], w[rr][3]};
+  }
 };
 
 // NF4 stored [K x N]: thread -> KR k-rows x 8 n-cols (4 code bytes + absmax per
@@ -225,16 +225,19 @@ struct WLoader<LSL_WFMT_NF4, true, BN> {
       am[rr] = pa[(k0 + rr) * rowa];
     }
   }
-  LSL_DEV void store(uint16_t* lds, const float2* lut, int tid) const {
-    uint32_t w[KR][4];
+  // row-major [k][n] tile (row stride BN + 8); the MFMA reads it transposed
+  LSL_DEV void store(uint16_t* lds, const float* lut, int tid) const {
+    const int q = tid / OG, o = tid % OG;
 #pragma unroll
-    for (int rr = 0; rr < KR; ++rr)
+    for (int rr = 0; rr < KR; ++rr) {
+      uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float2 cv = lut[(c[rr] >> (8 * j)) & 0xFF];
-        w[rr][j] = pack2(cv.x * am[rr], cv.y * am[rr]);
+        const uint32_t b = c[rr] >> (8 * j);  // element 2j in the high nibble
+        w[j] = pack2(lut[(b >> 4) & 15] * am[rr], lut[b & 15] * am[rr]);
       }
-    store_transposed<KR>(lds, w, tid / OG, tid % OG);
+      *reinterpret_cast<u32x4*>(lds + (q * KR + rr) * (BN + 8) + o * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
   }
 };
 
@@ -248,16 +251,20 @@ struct Geo {
   static constexpr int WN = BN / 64, WM = 4 / WN, WTM = BM / WM, MS = WTM / 16;
 };
 
-// ksteps x 32-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-frag[ni] x X-frag[mi]
-template <int MS>
+// ksteps x 32-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-frag[ni] x X-frag[mi].
+// TRW: the weight tile is row-major [k][n] (row stride WLD) and read transposed,
+// and the token tile holds its reduction index in the matching permuted order.
+template <int MS, bool TRW = false, int WLD = LDSW>
 LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x4 (&acc)[4][MS], int wn, int wm0, int lane,
                       int ksteps) {
   for (int ks = 0; ks < ksteps; ++ks) {
     const int kofs = ks * 32 + (lane >> 4) * 8;
     bf16x8 af[4], bfr[MS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + i * 16 + (lane & 15)) * LDSW + kofs);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (TRW) af[i] = ld_tr8(Ws, WLD, ks * 32, wn * 64 + i * 16, lane);
+      else af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + i * 16 + (lane & 15)) * LDSW + kofs);
+    }
 #pragma unroll
     for (int i = 0; i < MS; ++i)
       bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm0 + i * 16 + (lane & 15)) * LDSW + kofs);
@@ -284,9 +291,13 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
   using G = Geo<BN, BM>;
   constexpr int MS = G::MS;
   constexpr int NBUF = PIPE == 0 ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[NBUF][BN * LDSW];
+  // weight tile: [BN][LDSW] (NK), or row-major [BK][BN + 8] read transposed (KN);
+  // the LoRA step reuses buffer 0 as [BN][LDSW]
+  constexpr int WSZ = BN * LDSW > BK * (BN + 8) ? BN * LDSW : BK * (BN + 8);
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[NBUF][WSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[NBUF][BM * LDSW];
-  __shared__ float2 lut[WFMT == LSL_WFMT_NF4 ? 256 : 1];
+  // NF4 codebook: 16 floats, so every lookup is a conflict-free broadcast read
+  __shared__ float lut[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % G::WN, wm = wave / G::WN;
@@ -297,7 +308,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
   tile_coords((int)blockIdx.x - split * ntiles, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  if constexpr (WFMT == LSL_WFMT_NF4) lut[tid] = make_float2(a.cb[tid >> 4], a.cb[tid & 15]);
+  if constexpr (WFMT == LSL_WFMT_NF4)
+    if (tid < 16) lut[tid] = a.cb[tid];
 
   f32x4 acc[4][MS];
 #pragma unroll
@@ -305,6 +317,11 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
 #pragma unroll
     for (int j = 0; j < MS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // token tile store: natural k order, or (KN) the order of the transposed weight reads
+  auto xstore = [&](const RowLoader<BM>& l, uint16_t* d) {
+    if constexpr (KN) l.store_perm(d, tid);
+    else l.store(d, tid);
+  };
   // this workgroup's reduction steps [kt0, kt0 + KT); the LoRA step goes with the last split
   const int kt0 = split * a.kt_per_split;
   const int KT = min((int)(a.K / BK) - kt0, a.kt_per_split);
@@ -325,7 +342,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
       wl1.load(a, (int64_t)(kt0 + 1) * BK);
     }
     __syncthreads();  // lut visible
-    xl0.store(Xs[0], tid);
+    xstore(xl0, Xs[0]);
     wl0.store(Ws[0], lut, tid);
     __syncthreads();
     for (int kt = 0; kt < KT; kt += 2) {
@@ -333,9 +350,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
         xl0.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 2) * BK);
         wl0.load(a, (int64_t)(kt0 + kt + 2) * BK);
       }
-      mma_tile<MS>(Ws[0], Xs[0], acc, wn, wm0, lane, 2);
+      mma_tile<MS, KN, BN + 8>(Ws[0], Xs[0], acc, wn, wm0, lane, 2);
       if (kt + 1 < KT) {
-        xl1.store(Xs[1], tid);
+        xstore(xl1, Xs[1]);
         wl1.store(Ws[1], lut, tid);
       }
       __syncthreads();
@@ -344,9 +361,9 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
         xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 3) * BK);
         wl1.load(a, (int64_t)(kt0 + kt + 3) * BK);
       }
-      mma_tile<MS>(Ws[1], Xs[1], acc, wn, wm0, lane, 2);
+      mma_tile<MS, KN, BN + 8>(Ws[1], Xs[1], acc, wn, wm0, lane, 2);
       if (kt + 2 < KT) {
-        xl0.store(Xs[0], tid);
+        xstore(xl0, Xs[0]);
         wl0.store(Ws[0], lut, tid);
       }
       __syncthreads();
@@ -362,7 +379,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
     xl.load(a.x, a.ldx, a.M, (int64_t)kt0 * BK);
     wl.load(a, (int64_t)kt0 * BK);
     __syncthreads();  // lut visible
-    xl.store(Xs[0], tid);
+    xstore(xl, Xs[0]);
     wl.store(Ws[0], lut, tid);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
@@ -372,10 +389,10 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
         xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
         wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
       }
-      mma_tile<MS>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 2);
+      mma_tile<MS, KN, BN + 8>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 2);
       if constexpr (PIPE == 0) __syncthreads();
       if (more) {
-        xl.store(Xs[PIPE == 1 ? cur ^ 1 : 0], tid);
+        xstore(xl, Xs[PIPE == 1 ? cur ^ 1 : 0]);
         wl.store(Ws[PIPE == 1 ? cur ^ 1 : 0], lut, tid);
       }
       __syncthreads();
