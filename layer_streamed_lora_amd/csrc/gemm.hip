@@ -35,6 +35,11 @@ namespace lsl {
 constexpr int PIPE = LSL_GEMM_PIPE;  // K-loop pipeline structure (see the main loop)
 constexpr int BK = 64, LDSW = BK + 8;  // LDS row stride in elements
 constexpr int NTHREADS = 256;
+// at least two workgroups per CU: keeps each wave within 168 registers, so three
+// workgroups (12 waves) fit on a CU, which hides the staging latency better
+#ifndef LSL_GEMM_MINB
+#define LSL_GEMM_MINB 2
+#endif
 
 struct GemmKArgs {
   const uint16_t* x; int64_t ldx;
@@ -287,7 +292,7 @@ LSL_DEV void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
 }
 
 template <int WFMT, bool KN, int LORA, int EPI, int BN, int BM>
-__global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
+__global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const GemmKArgs a) {
   using G = Geo<BN, BM>;
   constexpr int MS = G::MS;
   constexpr int NBUF = PIPE == 0 ? 1 : 2;
@@ -322,10 +327,56 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
     if constexpr (KN) l.store_perm(d, tid);
     else l.store(d, tid);
   };
-  // this workgroup's reduction steps [kt0, kt0 + KT); the LoRA step goes with the last split
+  // ---- LoRA K-step first (kl <= 64, zero padded to 64), by split 0: the
+  // accumulators start as s * (L Lt^T), so no second set of accumulators is live
+  // during the main loop
+  if constexpr (LORA != 0) if (split == 0) {
+    uint16_t* Ls = Xs[0];
+    uint16_t* Lt = Ws[0];
+    for (int c = tid; c < BM * 8; c += NTHREADS) {
+      int row = c >> 3, col = (c & 7) * 8;
+      int64_t gm = m0 + row;
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (gm < a.M && col < a.kl) v = *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col);
+      *reinterpret_cast<u32x4*>(Ls + row * LDSW + col) = v;
+    }
+    if constexpr (LORA == 1) {
+      // Lt[n][j] = B[n][j % r] if j / r is the projection owning column n
+      for (int c = tid; c < BN * 64; c += NTHREADS) {
+        int row = c >> 6, j = c & 63;
+        int64_t gn = n0 + row;
+        uint16_t v = 0;
+        if (gn < a.N && j < a.kl) {
+          int seg = 0;
+          while (seg < a.nseg - 1 && gn >= a.seg_end[seg]) ++seg;
+          if (j / a.r == seg) v = a.lb[gn * a.r + (j % a.r)];
+        }
+        Lt[row * LDSW + j] = v;
+      }
+    } else {
+      // Lt[n][j] = A_full[j][n]
+      for (int c = tid; c < BN * 64; c += NTHREADS) {
+        int j = c / BN, row = c % BN;
+        int64_t gn = n0 + row;
+        uint16_t v = 0;
+        if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
+        Lt[row * LDSW + j] = v;
+      }
+    }
+    __syncthreads();
+    mma_tile<MS>(Lt, Ls, acc, wn, wm0, lane, (a.kl + 31) / 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < MS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] *= a.scale;
+    // the main loop's first barrier (before any tile store) orders these LDS reads
+  }
+
+  // this workgroup's reduction steps [kt0, kt0 + KT)
   const int kt0 = split * a.kt_per_split;
   const int KT = min((int)(a.K / BK) - kt0, a.kt_per_split);
-  const bool last_split = split == a.ksplit - 1;
   if constexpr (PIPE == 2) {
     // tile k computes from LDS buffer k % 2 while tile k + 1 waits in registers
     // (set (k + 1) % 2) for its LDS store and tile k + 2 is in flight
@@ -397,55 +448,6 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(const GemmKArgs a) {
       }
       __syncthreads();
     }
-  }
-
-  // ---- LoRA K-step (kl <= 64, zero padded to 64) into separate accumulators
-  if constexpr (LORA != 0) if (last_split) {
-    uint16_t* Ls = Xs[0];
-    uint16_t* Lt = Ws[0];
-    for (int c = tid; c < BM * 8; c += NTHREADS) {
-      int row = c >> 3, col = (c & 7) * 8;
-      int64_t gm = m0 + row;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (gm < a.M && col < a.kl) v = *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col);
-      *reinterpret_cast<u32x4*>(Ls + row * LDSW + col) = v;
-    }
-    if constexpr (LORA == 1) {
-      // Lt[n][j] = B[n][j % r] if j / r is the projection owning column n
-      for (int c = tid; c < BN * 64; c += NTHREADS) {
-        int row = c >> 6, j = c & 63;
-        int64_t gn = n0 + row;
-        uint16_t v = 0;
-        if (gn < a.N && j < a.kl) {
-          int seg = 0;
-          while (seg < a.nseg - 1 && gn >= a.seg_end[seg]) ++seg;
-          if (j / a.r == seg) v = a.lb[gn * a.r + (j % a.r)];
-        }
-        Lt[row * LDSW + j] = v;
-      }
-    } else {
-      // Lt[n][j] = A_full[j][n]
-      for (int c = tid; c < BN * 64; c += NTHREADS) {
-        int j = c / BN, row = c % BN;
-        int64_t gn = n0 + row;
-        uint16_t v = 0;
-        if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
-        Lt[row * LDSW + j] = v;
-      }
-    }
-    __syncthreads();
-    f32x4 lacc[4][MS];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MS; ++j) lacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mma_tile<MS>(Lt, Ls, lacc, wn, wm0, lane, (a.kl + 31) / 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MS; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] += a.scale * lacc[i][j][e];
   }
 
   // ---- epilogue: lane holds C[m][n..n+3]
