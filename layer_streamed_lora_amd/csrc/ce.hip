@@ -15,11 +15,25 @@
 
 namespace lsl {
 
-constexpr int64_t CE_CHUNK = 8192;  // vocabulary columns per backward chunk
+constexpr int64_t CE_CHUNK = 16384;  // vocabulary columns per backward chunk
 
 struct CePlan {
   size_t nvalid, part, zlab, lossv, g, dh32, total;
+  int splits;
 };
+
+// dH = sum over chunks of G_c W_c is accumulated in `splits` float32 partial
+// sums, each over its own share of every chunk's reduction (so that enough
+// workgroups run on the T x H output), added in split order at the end.
+static int ce_acc_splits(int64_t T, int64_t H, int64_t vc) {
+  int bn, bm;
+  gemm_tile_shape(T, H, bn, bm);
+  const int64_t tiles = ((T + bm - 1) / bm) * ((H + bn - 1) / bn);
+  const int64_t steps = vc / 64;
+  int64_t S = (768 + tiles - 1) / tiles;
+  if (S > steps / 32) S = steps / 32;
+  return S < 1 ? 1 : (int)S;
+}
 
 static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
   CePlan p{};
@@ -36,8 +50,9 @@ static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
   size_t fwd_end = off;
   off = common;
   int64_t vc = V < CE_CHUNK ? V : CE_CHUNK;
-  p.g = take((size_t)T * 2 * vc * 2);
-  p.dh32 = take((size_t)T * H * 4);
+  p.g = take((size_t)T * vc * 2);
+  p.splits = ce_acc_splits(T, H, vc);
+  p.dh32 = take((size_t)p.splits * T * H * 4);
   p.total = std::max(fwd_end, off);
   return p;
 }
@@ -97,6 +112,18 @@ __global__ __launch_bounds__(64 * LSE_WAVES) void ce_lse_kernel(const float2* __
   lse[t] = l;
   const int lab = labels[t];
   lossv[t] = (lab != ignore && lab >= 0 && lab < V) ? l - zlab[t] : 0.f;
+}
+
+// dH = bf16(sum of the split partial sums, in split order); 4 values per thread
+__global__ void ce_dh_reduce_kernel(const float* __restrict__ part, int S, int64_t n, uint16_t* __restrict__ dh) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(part + (int64_t)s * n + i);
+    v = f32x4{v[0] + q[0], v[1] + q[1], v[2] + q[2], v[3] + q[3]};
+  }
+  *reinterpret_cast<u32x2*>(dh + i) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
 }
 
 // loss = sum(lossv) / nvalid, one workgroup, fixed summation order
@@ -189,18 +216,27 @@ extern "C" lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm
     const int64_t v0 = c * CE_CHUNK;
     const int64_t vc = std::min(CE_CHUNK, V - v0);
     const uint16_t* wc = w_lm + v0 * H;
+    // G = coef (softmax - onehot) for this chunk, bf16 [T x vc]
     GemmDesc g1;
     g1.x = hN; g1.ldx = H; g1.wfmt = LSL_WFMT_BF16; g1.wb = wc; g1.M = T; g1.N = vc; g1.K = H;
     g1.epi = 2; g1.labels = labels; g1.lse = lse; g1.nvalid = nvalid; g1.gscale = grad_scale;
     g1.ignore = ignore_index; g1.vocab_off = v0; g1.vocab = V;
-    g1.y = G; g1.y2 = G + vc; g1.ldy = 2 * vc;
+    g1.y = G; g1.ldy = vc;
     LSL_TRY(gemm_launch(g1, s));
+    // dH (+)= G W_c in float32
     GemmDesc g2;
-    g2.x = G; g2.ldx = 2 * vc; g2.wfmt = LSL_WFMT_BF16; g2.kn = true; g2.wb = wc; g2.kwrap = vc;
-    g2.M = T; g2.N = H; g2.K = 2 * vc;
+    g2.x = G; g2.ldx = vc; g2.wfmt = LSL_WFMT_BF16; g2.kn = true; g2.wb = wc;
+    g2.M = T; g2.N = H; g2.K = vc;
     g2.epi = 3; g2.out32 = dh32; g2.ldo32 = H; g2.first = c == 0 ? 1 : 0;
-    g2.y = c == nchunks - 1 ? dhN : nullptr; g2.ldy = H;
+    g2.acc_splits = p.splits; g2.o32_split = T * H;
+    g2.y = (p.splits == 1 && c == nchunks - 1) ? dhN : nullptr; g2.ldy = H;
     LSL_TRY(gemm_launch(g2, s));
+  }
+  if (p.splits > 1) {
+    const int64_t n4 = T * H / 4;
+    hipLaunchKernelGGL(ce_dh_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dh32, p.splits,
+                       T * H, dhN);
+    return check_launch(fn);
   }
   return LSL_OK;
 }

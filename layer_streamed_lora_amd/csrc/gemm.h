@@ -21,6 +21,9 @@ struct GemmDesc {
   void* part = nullptr; float* zlab = nullptr; uint16_t* y2 = nullptr;
   float gscale = 1.f; int ignore = -100; int64_t vocab_off = 0, vocab = 0;
   float* out32 = nullptr; int64_t ldo32 = 0; int first = 1;
+  // epilogue 3 only: the reduction is split acc_splits ways, split s accumulating
+  // into out32 + s * o32_split (y must be NULL; the caller adds the splits)
+  int acc_splits = 1; int64_t o32_split = 0;
   int64_t kwrap = 0;
   // split-K scratch for the bf16 epilogue: gemm_split_bytes(M, N, K) bytes
   float* split_ws = nullptr;

@@ -58,7 +58,7 @@ struct GemmKArgs {
   float2* part; float* zlab;
   uint16_t* y2;              // low half of the hi + lo gradient pair
   float gscale; int ignore; int64_t vocab_off, vocab;
-  float* out32; int64_t ldo32; int first;
+  float* out32; int64_t ldo32; int first; int64_t o32_split;  // split s accumulates at out32 + s o32_split
   int64_t kwrap;             // KN operand: reduction index k reads weight row k mod kwrap (K <= 2 kwrap)
   int ksplit; int kt_per_split;  // split-K: workgroup b takes split b / (tiles_m tiles_n)
   float* spart;                  // float32 partials [ksplit][M][N]
@@ -543,10 +543,11 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         for (int e = 0; e < 4; ++e) g[e] = coef * (expf(g[e] - l) - (nl + e == lab ? 1.f : 0.f));
         const uint32_t h0 = pack2(g[0], g[1]), h1 = pack2(g[2], g[3]);
         *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{h0, h1};
-        *reinterpret_cast<u32x2*>(a.y2 + m * a.ldy + n) =
-            u32x2{pack2(g[0] - lo_bf(h0), g[1] - hi_bf(h0)), pack2(g[2] - lo_bf(h1), g[3] - hi_bf(h1))};
+        if (a.y2)
+          *reinterpret_cast<u32x2*>(a.y2 + m * a.ldy + n) =
+              u32x2{pack2(g[0] - lo_bf(h0), g[1] - hi_bf(h0)), pack2(g[2] - lo_bf(h1), g[3] - hi_bf(h1))};
       } else if constexpr (EPI == EPI_ACC32) {
-        float* o = a.out32 + m * a.ldo32 + n;
+        float* o = a.out32 + split * a.o32_split + m * a.ldo32 + n;
         f32x4 prev = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(o);
         f32x4 r = f32x4{prev[0] + v0, prev[1] + v1, prev[2] + v2, prev[3] + v3};
         *reinterpret_cast<f32x4*>(o) = r;
@@ -600,6 +601,14 @@ static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
   const int KT = (int)(d.K / BK);
   a.ksplit = 1;
   a.kt_per_split = KT;
+  if (d.epi == EPI_ACC32 && d.acc_splits > 1) {
+    if (d.y) return set_error(LSL_ERR_UNSUPPORTED, "gemm: split float accumulation has no bf16 copy");
+    a.kt_per_split = (KT + d.acc_splits - 1) / d.acc_splits;
+    a.ksplit = (KT + a.kt_per_split - 1) / a.kt_per_split;
+    if (d.first && a.ksplit != d.acc_splits)  // the first pass must initialise every split
+      return set_error(LSL_ERR_UNSUPPORTED, "gemm: %d accumulation splits of %d steps", d.acc_splits, KT);
+    a.o32_split = d.o32_split;
+  }
   if (d.epi == EPI_BF16) {
     const int S = gemm_splits(d.M, d.N, d.K);
     if (S > 1) {
@@ -651,7 +660,7 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
 // Split-K for GEMMs with few output tiles: enough reduction splits to give
 // about SPLIT_TARGET workgroups, each taking at least SPLIT_MIN_STEPS K-steps.
 #ifndef LSL_SPLIT_TARGET
-#define LSL_SPLIT_TARGET 512
+#define LSL_SPLIT_TARGET 768
 #endif
 #ifndef LSL_SPLIT_MIN_STEPS
 #define LSL_SPLIT_MIN_STEPS 32
