@@ -208,8 +208,6 @@ lsl_status lsl_pool_release(lsl_pool* pool, int32_t slot, lsl_stream compute);
 /* Mark a released slot as still holding `host_ptr`'s layer, so it can be
  * acquired again without a copy (the layers kept across the turn of a sweep). */
 lsl_status lsl_pool_reuse(lsl_pool* pool, int32_t slot);
-/* Seconds the copy engine spent on the slot's most recent load (waits for it). */
-lsl_status lsl_pool_last_copy_seconds(lsl_pool* pool, int32_t slot, double* seconds);
 /* Copy statistics: after enable, each of the next max_loads loads records a
  * start/end event pair on the copy stream; read waits for them and returns the
  * number of loads, bytes and summed copy seconds, then clears the record. */

@@ -64,7 +64,6 @@ PROTOS = {
     "lsl_pool_acquire": (i32, [vp, i32, vp, C.POINTER(vp)]),
     "lsl_pool_release": (i32, [vp, i32, vp]),
     "lsl_pool_reuse": (i32, [vp, i32]),
-    "lsl_pool_last_copy_seconds": (i32, [vp, i32, C.POINTER(C.c_double)]),
     "lsl_pool_stats_enable": (i32, [vp, i32]),
     "lsl_pool_stats_read": (i32, [vp, C.POINTER(i32), C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     "lsl_timing_enable": (i32, [i32, i32]),

@@ -23,7 +23,7 @@ struct lsl_pool {
   size_t slot_bytes = 0;
   hipStream_t copy = nullptr;
   std::vector<void*> ptr;
-  std::vector<hipEvent_t> ready, freed, start;
+  std::vector<hipEvent_t> ready, freed;
   std::vector<int> state;
   std::vector<bool> free_recorded;
   // optional copy statistics
@@ -52,12 +52,12 @@ extern "C" lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, in
   p->ptr.assign(slot_ptrs, slot_ptrs + n_slots);
   p->ready.assign(n_slots, nullptr);
   p->freed.assign(n_slots, nullptr);
-  p->start.assign(n_slots, nullptr);
   p->state.assign(n_slots, SLOT_EMPTY);
   p->free_recorded.assign(n_slots, false);
   for (int i = 0; i < n_slots; ++i) {
     hipError_t e;
-    if ((e = hipEventCreate(&p->ready[i])) != hipSuccess || (e = hipEventCreate(&p->start[i])) != hipSuccess ||
+    // ordering only: no timestamps on the per-layer events (statistics use their own)
+    if ((e = hipEventCreateWithFlags(&p->ready[i], hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&p->freed[i], hipEventDisableTiming)) != hipSuccess) {
       lsl_pool_destroy(p);
       return hip_fail("lsl_pool_create: hipEventCreate", e);
@@ -81,7 +81,6 @@ extern "C" lsl_status lsl_pool_destroy(lsl_pool* p) {
   for (int i = 0; i < p->n; ++i) {
     if (p->ready[i]) hipEventDestroy(p->ready[i]);
     if (p->freed[i]) hipEventDestroy(p->freed[i]);
-    if (p->start[i]) hipEventDestroy(p->start[i]);
   }
   stats_free(p);
   delete p;
@@ -145,7 +144,6 @@ extern "C" lsl_status load_layer_async(lsl_pool* p, int32_t slot, const void* ho
   }
   if (p->free_recorded[slot] && (e = hipStreamWaitEvent(p->copy, p->freed[slot], 0)) != hipSuccess)
     return hip_fail("load_layer_async: hipStreamWaitEvent", e);
-  if ((e = hipEventRecord(p->start[slot], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
   const bool stat = p->st_count < (int)p->st_start.size();
   if (stat && (e = hipEventRecord(p->st_start[p->st_count], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if ((e = hipMemcpyAsync(p->ptr[slot], host_ptr, bytes, hipMemcpyHostToDevice, p->copy)) != hipSuccess)
@@ -189,18 +187,5 @@ extern "C" lsl_status lsl_pool_reuse(lsl_pool* p, int32_t slot) {
   if (p->state[slot] != SLOT_RELEASED)
     return set_error(LSL_ERR_STATE, "%s: slot %d holds no released layer (state %d)", fn, slot, p->state[slot]);
   p->state[slot] = SLOT_LOADED;
-  return LSL_OK;
-}
-
-extern "C" lsl_status lsl_pool_last_copy_seconds(lsl_pool* p, int32_t slot, double* seconds) {
-  const char* fn = "lsl_pool_last_copy_seconds";
-  LSL_TRY(check_slot(p, slot, fn));
-  if (!seconds) return set_error(LSL_ERR_INVALID_ARG, "%s: seconds is NULL", fn);
-  if (p->state[slot] == SLOT_EMPTY) return set_error(LSL_ERR_STATE, "%s: slot %d was never loaded", fn, slot);
-  hipError_t e = hipEventSynchronize(p->ready[slot]);
-  if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
-  float ms = 0.f;
-  if ((e = hipEventElapsedTime(&ms, p->start[slot], p->ready[slot])) != hipSuccess) return hip_fail("hipEventElapsedTime", e);
-  *seconds = ms * 1e-3;
   return LSL_OK;
 }

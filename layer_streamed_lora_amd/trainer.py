@@ -62,11 +62,6 @@ class LayerPool:
     def reuse(self, slot):
         _check("lsl_pool_reuse", lib().lsl_pool_reuse(self.handle, slot))
 
-    def last_copy_seconds(self, slot):
-        s = C.c_double()
-        _check("lsl_pool_last_copy_seconds", lib().lsl_pool_last_copy_seconds(self.handle, slot, C.byref(s)))
-        return s.value
-
     def close(self):
         if self.handle:
             lib().lsl_pool_destroy(self.handle)
