@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 import synth
-from synth.configs import LayerShape, PROJ_IN_OUT, QWEN05B_LAYER
+from synth.configs import LayerShape, PROJ_IN_OUT, QWEN05B_LAYER, QWEN3B_LAYER, LLAMA8B_LAYER
 from tests.gpu_util import dev_bf16, host, assert_close_chain
 
 pytestmark = pytest.mark.gpu
@@ -99,17 +99,15 @@ def test_streamed_equals_resident_small(gpu, shape):
     assert s.loads == (2 * n_layers - 2) + (2 * n_micro - 1) * (2 * n_layers - 4)
 
 
-@pytest.mark.timeout(900)
-def test_streamed_equals_resident_qwen05b(gpu):
-    """Qwen2.5-0.5B-shaped model (24 layers, hidden 896, 14/2 heads, MLP 4864,
-    vocab 151936, tied), 4 microbatches of 4 x 512 tokens, one AdamW step:
-    streamed and resident runs give identical bits."""
+def _streamed_vs_resident(shape, L, V, tied, batch, seq, n_micro, seed):
+    """Build a resident and a streamed model with the same random base
+    (N(0, 0.02), unit norms), run one optimizer step on the same tokens and
+    require identical bits everywhere."""
     from layer_streamed_lora_amd.trainer import StreamedLoraModel
-    shape, L, V, batch, seq, n_micro = QWEN05B_LAYER, 24, 151936, 4, 512, 4
     models = {}
     for mode in ("resident", "streamed"):
-        m = StreamedLoraModel(shape, L, V, True, batch, seq, mode=mode)
-        g = torch.Generator(device="cuda").manual_seed(3)
+        m = StreamedLoraModel(shape, L, V, tied, batch, seq, mode=mode)
+        g = torch.Generator(device="cuda").manual_seed(seed)
         for l in range(L):
             w = {}
             for p, (fin, fout) in PROJ_IN_OUT(shape).items():
@@ -118,10 +116,12 @@ def test_streamed_equals_resident_qwen05b(gpu):
             w["norm2"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
             m.set_layer_weights(l, w)
         m.embed.copy_((torch.randn((V, shape.hidden), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
+        if not tied:
+            m.lm_head.copy_((torch.randn((V, shape.hidden), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
         m.lora.master.copy_(torch.randn(m.lora.numel, generator=g, device="cuda") * 0.01)
         m.lora.bf16.copy_(m.lora.master.to(torch.bfloat16))
         models[mode] = m
-    chunks = ids_for(V, batch, seq, n_micro, 3)
+    chunks = ids_for(V, batch, seq, n_micro, seed)
     out = {}
     for mode, m in models.items():
         out[mode] = m.step(m.prepare_inputs(chunks))
@@ -130,8 +130,34 @@ def test_streamed_equals_resident_qwen05b(gpu):
     assert torch.equal(out["streamed"], out["resident"])
     assert torch.equal(s.ckpt, r.ckpt) and torch.equal(s.lse, r.lse)
     _assert_same_state(s, r)
+    # one step: 2L - 2 copies for the first microbatch, 2L - 4 for each later one
+    assert s.loads == (2 * L - 2) + (n_micro - 1) * (2 * L - 4)
     loss = host(out["streamed"]).mean()
     # random N(0, 0.02) weights: the loss sits near ln V
     assert abs(loss - np.log(V)) < 1.0, loss
     for l in (0, L - 1):
         assert torch.count_nonzero(s.lora.view(s.lora.grad, l, 0, "A")) > 0
+    return s
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_qwen05b(gpu):
+    """Qwen2.5-0.5B-shaped model (24 layers, hidden 896, 14/2 heads, MLP 4864,
+    vocab 151936, tied), 4 microbatches of 4 x 512 tokens, one AdamW step:
+    streamed and resident runs give identical bits."""
+    _streamed_vs_resident(QWEN05B_LAYER, 24, 151936, True, 4, 512, 4, 3)
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_qwen3b(gpu):
+    """Qwen2.5-3B-shaped model with an un-quantized bf16 base (36 layers,
+    hidden 2048, 16/2 heads of 128, MLP 11008, vocab 151936, tied), 1 x 1024
+    tokens: streamed (5.5 GB pinned store, two 154 MB slots) equals resident."""
+    _streamed_vs_resident(QWEN3B_LAYER, 36, 151936, True, 1, 1024, 1, 4)
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_llama8b_nf4(gpu):
+    """Llama-3.1-8B-shaped model, NF4 base (32 layers, 122.7 MB blobs, 3.9 GB
+    pinned store), separate bf16 lm_head, vocab 128256, 1 x 1024 tokens."""
+    _streamed_vs_resident(LLAMA8B_LAYER, 32, 128256, False, 1, 1024, 1, 5)
