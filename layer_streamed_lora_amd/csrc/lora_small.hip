@@ -11,6 +11,7 @@
 // reduction; the second adds the splits in index order and writes the result.
 #include "common.h"
 #include "small.h"
+#include "api_util.h"
 
 namespace lsl {
 
@@ -22,93 +23,122 @@ LSL_DEV f32x4 mfma16s(const bf16x8& a, const bf16x8& b, const f32x4& c) {
 
 struct NtArgs {
   const uint16_t* p; int64_t ldp;   // [T x K]
-  const uint16_t* rA;               // A_full [kl x K]  (mode 0)
-  const uint16_t* rB; int r; int nseg; int64_t seg_end[4];  // B_full [K x r] (mode 1)
+  const uint16_t* rt;               // R [kl x K], row stride K (A_full, or the masked B transposed)
   int64_t T, K; int kl;
-  int64_t k_per_split;
-  float* part;                      // [S][T][kl]
+  int64_t k_per_split;              // multiple of 256
+  float* part;                      // [S][T][kl] float32 partial sums (S > 1)
+  uint16_t* out; int64_t ldo;       // S == 1: the bf16 result [T x kl]
 };
 
-// grid: (ceil(T/128), S); 4 waves, wave w owns rows 32w..32w+31 of the tile.
-template <int MODE>
+// Raw buffer loads: bytes past the descriptor's end read as zeros.
+LSL_DEV __amdgpu_buffer_rsrc_t small_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+// C[t][j] = sum_k P[t][k] R[j][k] for a 64-row tile and one split of K.
+// grid (ceil(T/64), S), 4 waves; wave w takes the split's 64-wide K-steps
+// w, w + 4, ... for all 64 rows and all kl columns, loading both operands from
+// global memory (L2) straight into MFMA registers (each P element is read once;
+// R is small and shared). The four waves' sums are added in wave order in LDS.
+template <bool DIRECT>
 __global__ __launch_bounds__(256) void lora_nt_kernel(const NtArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[128 * SK_LDS];
-  __shared__ __attribute__((aligned(16))) uint16_t Rs[64 * SK_LDS];
+  __shared__ f32x4 red[3][4][4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * 128;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int64_t kbeg = (int64_t)blockIdx.y * a.k_per_split;
   const int64_t kend = kbeg + a.k_per_split < a.K ? kbeg + a.k_per_split : a.K;
-  f32x4 acc[4][2];
+  const __amdgpu_buffer_rsrc_t rp = small_rsrc(a.p, a.T * a.ldp * 2);
+  const __amdgpu_buffer_rsrc_t rr = small_rsrc(a.rt, (int64_t)a.kl * a.K * 2);
+  uint32_t po[4], ro[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t k0 = kbeg; k0 < kend; k0 += 64) {
+  for (int i = 0; i < 4; ++i) {
+    po[i] = (uint32_t)(((t0 + i * 16 + c16) * a.ldp + g * 8) * 2);   // rows >= T read zeros
+    ro[i] = (uint32_t)(((int64_t)(i * 16 + c16) * a.K + g * 8) * 2);  // rows >= kl read zeros
+  }
+  f32x4 acc[4][4];  // [j block][row block]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + i * 256, row = c >> 3, col = (c & 7) * 8;
-      int64_t gt = t0 + row;
-      u32x4 v = gt < a.T ? *reinterpret_cast<const u32x4*>(a.p + gt * a.ldp + k0 + col) : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(Ps + row * SK_LDS + col) = v;
-    }
-    if constexpr (MODE == 0) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int c = tid + i * 256, row = c >> 3, col = (c & 7) * 8;
-        u32x4 v = row < a.kl ? *reinterpret_cast<const u32x4*>(a.rA + (int64_t)row * a.K + k0 + col) : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(Rs + row * SK_LDS + col) = v;
-      }
-    } else {
-      // Rs[j][kk] = B[k0+kk][j % r] masked by projection; thread -> one kk, 16 j's
-      int kk = tid & 63, jq = tid >> 6;  // jq: 16-wide j group
-      int64_t n = k0 + kk;
-      int seg = 0;
-      while (seg < a.nseg - 1 && n >= a.seg_end[seg]) ++seg;
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        int j = jq * 16 + jj;
-        uint16_t v = 0;
-        if (j < a.kl && j / a.r == seg) v = a.rB[n * a.r + (j % a.r)];
-        Rs[j * SK_LDS + kk] = v;
-      }
-    }
-    __syncthreads();
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int64_t k0 = kbeg + wave * 64; k0 < kend; k0 += 256) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      int kofs = ks * 32 + (lane >> 4) * 8;
-      bf16x8 rf[4], pf[2];
+      const uint32_t so = (uint32_t)((k0 + ks * 32) * 2);
+      bf16x8 pf[4], rf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rf[i] = *reinterpret_cast<const bf16x8*>(Rs + (i * 16 + (lane & 15)) * SK_LDS + kofs);
+      for (int i = 0; i < 4; ++i) {
+        pf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rp, po[i], so, 0));
+        rf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rr, ro[i], so, 0));
+      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) pf[i] = *reinterpret_cast<const bf16x8*>(Ps + (wave * 32 + i * 16 + (lane & 15)) * SK_LDS + kofs);
+      for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16s(rf[i], pf[j], acc[i][j]);
+        for (int rb = 0; rb < 4; ++rb) acc[jb][rb] = mfma16s(rf[jb], pf[rb], acc[jb][rb]);
     }
-    __syncthreads();
   }
-  // lane holds C[t][j..j+3], j = 16 i + 4 (lane >> 4)
-  float* dst = a.part + (int64_t)blockIdx.y * a.T * a.kl;
+  if (wave > 0)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int64_t t = t0 + wave * 32 + j * 16 + (lane & 15);
-    if (t >= a.T) continue;
+    for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = i * 16 + (lane >> 4) * 4;
-      if (c < a.kl) *reinterpret_cast<f32x4*>(dst + t * a.kl + c) = acc[i][j];
+      for (int rb = 0; rb < 4; ++rb) red[wave - 1][jb][rb][lane] = acc[jb][rb];
+  __syncthreads();
+  if (wave != 0) return;
+  // lane holds C[j = 16 jb + 4 g + i][t = t0 + 16 rb + c16]
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    const int j = jb * 16 + g * 4;
+    if (j >= a.kl) continue;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int64_t t = t0 + rb * 16 + c16;
+      f32x4 v = acc[jb][rb];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const f32x4 q = red[w][jb][rb][lane];
+        v = f32x4{v[0] + q[0], v[1] + q[1], v[2] + q[2], v[3] + q[3]};
+      }
+      if (t >= a.T) continue;
+      if (DIRECT) *reinterpret_cast<u32x2*>(a.out + t * a.ldo + j) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      else *reinterpret_cast<f32x4*>(a.part + ((int64_t)blockIdx.y * a.T + t) * a.kl + j) = v;
     }
   }
 }
 
-// out[t][j] = bf16(sum_s part[s][t][j]) for j < kl
-__global__ void nt_reduce_kernel(const float* __restrict__ part, int S, int64_t T, int kl, uint16_t* __restrict__ out, int64_t ldo) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// out[t][j] = bf16(sum over splits in order); 4 values per thread
+__global__ void nt_reduce_kernel(const float* __restrict__ part, int S, int64_t T, int kl, uint16_t* __restrict__ out,
+                                 int64_t ldo) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= T * kl) return;
-  int64_t t = i / kl; int j = (int)(i - t * kl);
-  float s = 0.f;
-  for (int k = 0; k < S; ++k) s += part[((int64_t)k * T + t) * kl + j];
-  out[t * ldo + j] = f2bf(s);
+  const int64_t t = i / kl;
+  const int j = (int)(i - t * kl);
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int k = 1; k < S; ++k) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(part + (int64_t)k * T * kl + i);
+    v = f32x4{v[0] + q[0], v[1] + q[1], v[2] + q[2], v[3] + q[3]};
+  }
+  *reinterpret_cast<u32x2*>(out + t * ldo + j) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+}
+
+// Masked transpose of B_full [K x r] for u = dy B: bt[j][k] = B[k][j % r] when
+// j / r is the projection owning row k (else 0), j < kl. 8 k per thread.
+__global__ void lora_bt_kernel(const uint16_t* __restrict__ b, int r, int kl, int64_t K, int nseg, SegEnds seg,
+                               uint16_t* __restrict__ bt) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t kc = K / 8;
+  if (idx >= kl * kc) return;
+  const int j = (int)(idx / kc);
+  const int64_t k = (idx - (int64_t)j * kc) * 8;
+  int p = 0;
+  while (p < nseg - 1 && k >= seg.e[p]) ++p;  // segment ends are multiples of 8
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (j / r == p) {
+    const uint16_t* src = b + k * r + (j % r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (uint32_t)src[(2 * e) * r] | ((uint32_t)src[(2 * e + 1) * r] << 16);
+  }
+  *reinterpret_cast<u32x4*>(bt + (int64_t)j * K + k) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
 struct TnArgs {
@@ -251,10 +281,19 @@ static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks, int64_
 }
 constexpr int64_t NT_TARGET = 256, NT_MIN_STEPS = 4, TN_TARGET = 256, TN_MIN_STEPS = 4;
 
+// NT splits: about 256 workgroups of 64 rows, each split at least 1024 of K
+// (so each of its four waves takes four or more 64-wide steps)
+static int nt_splits(int64_t T, int64_t K) {
+  const int64_t tiles = (T + 63) / 64;
+  int64_t S = (256 + tiles - 1) / tiles;
+  if (S > K / 1024) S = K / 1024;
+  return S < 1 ? 1 : (int)S;
+}
+
+// [masked B^T, kl <= 64 rows] + [S][T][kl] partials
 size_t lora_nt_ws_bytes(int64_t T, int64_t K) {
-  int64_t tiles = (T + 127) / 128;
-  int S = pick_splits(tiles, K, NT_TARGET, NT_MIN_STEPS);
-  return (size_t)S * T * 64 * sizeof(float);
+  const int S = nt_splits(T, K);
+  return align256((size_t)64 * K * 2) + (S > 1 ? (size_t)S * T * 64 * sizeof(float) : 0);
 }
 
 size_t lora_tn_ws_bytes(int64_t T, int64_t W) {
@@ -267,21 +306,36 @@ lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
   if (d.T == 0) return LSL_OK;
   if (d.K % 64 || d.kl <= 0 || d.kl > 64 || d.kl % 8)
     return set_error(LSL_ERR_UNSUPPORTED, "lora side product: K %% 64 and kl in [8, 64] multiple of 8 required");
-  int64_t tiles = (d.T + 127) / 128;
-  int S = pick_splits(tiles, d.K, NT_TARGET, NT_MIN_STEPS);
-  int64_t steps = d.K / 64;
-  int64_t per = ((steps + S - 1) / S) * 64;
-  S = (int)((d.K + per - 1) / per);
+  if ((d.T + 64) * d.ldp * 2 >= ((int64_t)1 << 32))
+    return set_error(LSL_ERR_UNSUPPORTED, "lora side product: operand larger than 4 GiB");
+  char* ws = (char*)d.ws;
   NtArgs a{};
-  a.p = d.p; a.ldp = d.ldp; a.rA = d.a_full; a.rB = d.b_full; a.r = d.r; a.nseg = d.nseg;
-  for (int i = 0; i < 4; ++i) a.seg_end[i] = d.seg_end[i];
-  a.T = d.T; a.K = d.K; a.kl = d.kl; a.k_per_split = per; a.part = d.ws;
-  dim3 grid((unsigned)tiles, (unsigned)S);
-  if (d.b_full) hipLaunchKernelGGL(lora_nt_kernel<1>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(lora_nt_kernel<0>, grid, dim3(256), 0, s, a);
-  int64_t n = d.T * d.kl;
-  hipLaunchKernelGGL(nt_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const float*)d.ws, S, d.T, d.kl, d.out, d.ldo);
+  a.p = d.p; a.ldp = d.ldp; a.T = d.T; a.K = d.K; a.kl = d.kl; a.out = d.out; a.ldo = d.ldo;
+  if (d.b_full) {
+    uint16_t* bt = (uint16_t*)ws;
+    SegEnds se;
+    for (int i = 0; i < 4; ++i) se.e[i] = d.seg_end[i];
+    const int64_t n = (int64_t)d.kl * (d.K / 8);
+    hipLaunchKernelGGL(lora_bt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, d.b_full, d.r, d.kl, d.K,
+                       d.nseg, se, bt);
+    a.rt = bt;
+  } else {
+    a.rt = d.a_full;
+  }
+  a.part = (float*)(ws + align256((size_t)64 * d.K * 2));
+  const int64_t tiles = (d.T + 63) / 64;
+  int S = nt_splits(d.T, d.K);
+  const int64_t per = (d.K / S + 255) / 256 * 256;
+  S = (int)((d.K + per - 1) / per);
+  a.k_per_split = per;
+  if (S == 1) {
+    hipLaunchKernelGGL(lora_nt_kernel<true>, dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
+    return check_launch("lora_nt");
+  }
+  hipLaunchKernelGGL(lora_nt_kernel<false>, dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
+  const int64_t n4 = d.T * d.kl / 4;
+  hipLaunchKernelGGL(nt_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.part, S,
+                     d.T, d.kl, d.out, d.ldo);
   return check_launch("lora_nt");
 }
 
