@@ -108,19 +108,6 @@ struct RowLoader {
 #pragma unroll
     for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(lds + (r + 32 * i) * LDSW + c) = v[i];
   }
-  // Same tile with the reduction index permuted inside each 32-group: position
-  // 8g + s holds k = 4g + s and position 8g + 4 + s holds k = 16 + 4g + s, the
-  // order in which ld_tr8 delivers the other operand.
-  LSL_DEV void store_perm(uint16_t* lds, int tid) const {
-    const int r = tid >> 3, cc = tid & 3;
-    const int c = (tid & 4) * 8 + (cc & 1) * 16 + (cc >> 1) * 4;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      uint16_t* d = lds + (r + 32 * i) * LDSW + c;
-      *reinterpret_cast<u32x2*>(d) = u32x2{v[i][0], v[i][1]};
-      *reinterpret_cast<u32x2*>(d + 8) = u32x2{v[i][2], v[i][3]};
-    }
-  }
 };
 
 template <int WFMT, bool KN, int BN>
@@ -246,37 +233,49 @@ struct WLoader<LSL_WFMT_NF4, true, BN> {
   }
 };
 
-LSL_DEV f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// 32 x 32 x 16 bf16 MFMA (on gfx950 twice the throughput of 16 x 16 x 32). Lane l
+// holds A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; accumulator
+// element i is C[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
+LSL_DEV f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Tile geometry: WN x WM waves, each 64 (n) x WTM (m), MS 16-row m-subtiles.
+// Tile geometry: WN x WM waves, each 64 (n) x WTM (m): 2 x MI blocks of 32 x 32.
 template <int BN, int BM>
 struct Geo {
-  static constexpr int WN = BN / 64, WM = 4 / WN, WTM = BM / WM, MS = WTM / 16;
+  static constexpr int WN = BN / 64, WM = 4 / WN, WTM = BM / WM, MI = WTM / 32;
 };
 
-// ksteps x 32-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-frag[ni] x X-frag[mi].
-// TRW: the weight tile is row-major [k][n] (row stride WLD) and read transposed,
-// and the token tile holds its reduction index in the matching permuted order.
-template <int MS, bool TRW = false, int WLD = LDSW>
-LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x4 (&acc)[4][MS], int wn, int wm0, int lane,
+// ksteps x 16-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-block[ni] x X-block[mi].
+// TRW: the weight tile is row-major [k][n] (row stride WLD) and read with
+// transposing LDS reads (natural k order, so the token tile is unchanged).
+template <int MI, bool TRW = false, int WLD = LDSW>
+LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x16 (&acc)[2][MI], int wn, int wm0, int lane,
                       int ksteps) {
+  const int h8 = (lane >> 5) * 8, r32 = lane & 31;
   for (int ks = 0; ks < ksteps; ++ks) {
-    const int kofs = ks * 32 + (lane >> 4) * 8;
-    bf16x8 af[4], bfr[MS];
+    const int kofs = ks * 16 + h8;
+    bf16x8 af[2], bfr[MI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (TRW) af[i] = ld_tr8(Ws, WLD, ks * 32, wn * 64 + i * 16, lane);
-      else af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + i * 16 + (lane & 15)) * LDSW + kofs);
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (TRW) {
+        // lanes 16-31 / 48-63 take columns 16..31 of the block; each 16-lane group
+        // reads rows kofs .. kofs + 3 and kofs + 4 .. kofs + 7 of its 16 columns
+        const int j = lane & 15;
+        const uint16_t* p = Ws + (kofs + (j >> 2)) * WLD + wn * 64 + i * 32 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+        const u32x2 x = ld_tr4(p), y = ld_tr4(p + 4 * WLD);
+        af[i] = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+      } else {
+        af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + i * 32 + r32) * LDSW + kofs);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < MS; ++i)
-      bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm0 + i * 16 + (lane & 15)) * LDSW + kofs);
+    for (int i = 0; i < MI; ++i)
+      bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm0 + i * 32 + r32) * LDSW + kofs);
 #pragma unroll
-    for (int mi = 0; mi < MS; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) acc[ni][mi] = mfma16(af[ni], bfr[mi], acc[ni][mi]);
+      for (int ni = 0; ni < 2; ++ni) acc[ni][mi] = mfma32(af[ni], bfr[mi], acc[ni][mi]);
   }
 }
 
@@ -294,7 +293,7 @@ LSL_DEV void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
 template <int WFMT, bool KN, int LORA, int EPI, int BN, int BM>
 __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const GemmKArgs a) {
   using G = Geo<BN, BM>;
-  constexpr int MS = G::MS;
+  constexpr int MI = G::MI;
   constexpr int NBUF = PIPE == 0 ? 1 : 2;
   // weight tile: [BN][LDSW] (NK), or row-major [BK][BN + 8] read transposed (KN);
   // the LoRA step reuses buffer 0 as [BN][LDSW]
@@ -316,17 +315,15 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   if constexpr (WFMT == LSL_WFMT_NF4)
     if (tid < 16) lut[tid] = a.cb[tid];
 
-  f32x4 acc[4][MS];
+  f32x16 acc[2][MI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < MS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MI; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // token tile store: natural k order, or (KN) the order of the transposed weight reads
-  auto xstore = [&](const RowLoader<BM>& l, uint16_t* d) {
-    if constexpr (KN) l.store_perm(d, tid);
-    else l.store(d, tid);
-  };
+  auto xstore = [&](const RowLoader<BM>& l, uint16_t* d) { l.store(d, tid); };
   // ---- LoRA K-step first (kl <= 64, zero padded to 64), by split 0: the
   // accumulators start as s * (L Lt^T), so no second set of accumulators is live
   // during the main loop
@@ -364,13 +361,13 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
       }
     }
     __syncthreads();
-    mma_tile<MS>(Lt, Ls, acc, wn, wm0, lane, (a.kl + 31) / 32);
+    mma_tile<MI>(Lt, Ls, acc, wn, wm0, lane, (a.kl + 15) / 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < MS; ++j)
+      for (int j = 0; j < MI; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] *= a.scale;
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= a.scale;
     // the main loop's first barrier (before any tile store) orders these LDS reads
   }
 
@@ -401,7 +398,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         xl0.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 2) * BK);
         wl0.load(a, (int64_t)(kt0 + kt + 2) * BK);
       }
-      mma_tile<MS, KN, BN + 8>(Ws[0], Xs[0], acc, wn, wm0, lane, 2);
+      mma_tile<MI, KN, BN + 8>(Ws[0], Xs[0], acc, wn, wm0, lane, 4);
       if (kt + 1 < KT) {
         xstore(xl1, Xs[1]);
         wl1.store(Ws[1], lut, tid);
@@ -412,7 +409,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 3) * BK);
         wl1.load(a, (int64_t)(kt0 + kt + 3) * BK);
       }
-      mma_tile<MS, KN, BN + 8>(Ws[1], Xs[1], acc, wn, wm0, lane, 2);
+      mma_tile<MI, KN, BN + 8>(Ws[1], Xs[1], acc, wn, wm0, lane, 4);
       if (kt + 2 < KT) {
         xstore(xl0, Xs[0]);
         wl0.store(Ws[0], lut, tid);
@@ -440,7 +437,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
         wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
       }
-      mma_tile<MS, KN, BN + 8>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 2);
+      mma_tile<MI, KN, BN + 8>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 4);
       if constexpr (PIPE == 0) __syncthreads();
       if (more) {
         xstore(xl, Xs[PIPE == 1 ? cur ^ 1 : 0]);
@@ -450,42 +447,42 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
     }
   }
 
-  // ---- epilogue: lane holds C[m][n..n+3]
+  // ---- epilogue: for block (ni, mi) and q < 4, the lane holds C[m][n .. n+3] with
+  // m = m0 + wm0 + 32 mi + lane % 32, n = n0 + 64 wn + 32 ni + 8 q + 4 (lane / 32)
+  const int64_t mb = m0 + wm0 + (lane & 31);
+  const int64_t nb = n0 + wn * 64 + (lane >> 5) * 4;
   if constexpr (EPI == EPI_LSE) {
     // Cross-entropy forward: per token m, max and sum of exp over this tile's
     // vocabulary entries n < N, and the label's logit if it falls in the tile.
     float2* red = reinterpret_cast<float2*>(Xs[0]);  // [WN][BM]
 #pragma unroll
-    for (int mi = 0; mi < MS; ++mi) {
-      const int64_t m = m0 + wm0 + mi * 16 + (lane & 15);
+    for (int mi = 0; mi < MI; ++mi) {
+      const int64_t m = mb + mi * 32;
       const int lab = m < a.M ? a.labels[m] : -1;
       float mx = -INFINITY;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
+      for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (n + e < a.N) {
-            mx = fmaxf(mx, acc[ni][mi][e]);
-            if (n + e == lab) a.zlab[m] = acc[ni][mi][e];
+        for (int i = 0; i < 16; ++i) {
+          const int64_t n = nb + ni * 32 + 8 * (i >> 2) + (i & 3);
+          if (n < a.N) {
+            mx = fmaxf(mx, acc[ni][mi][i]);
+            if (n == lab) a.zlab[m] = acc[ni][mi][i];
           }
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       float sm = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < a.N) sm += expf(acc[ni][mi][e] - mx);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const int64_t n = nb + ni * 32 + 8 * (i >> 2) + (i & 3);
+            if (n < a.N) sm += expf(acc[ni][mi][i] - mx);
+          }
       }
-      sm += __shfl_xor(sm, 16, 64);
       sm += __shfl_xor(sm, 32, 64);
-      if ((lane >> 4) == 0) red[wn * BM + wm0 + mi * 16 + (lane & 15)] = make_float2(mx, sm);
+      if ((lane >> 5) == 0) red[wn * BM + wm0 + mi * 32 + (lane & 31)] = make_float2(mx, sm);
     }
     __syncthreads();
     for (int t = tid; t < BM; t += NTHREADS) {
@@ -509,26 +506,32 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
     // split-K: float32 partial of this split; gemm_split_reduce adds the splits
     float* dst = a.spart + (int64_t)split * a.M * a.N;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
-      if (n >= a.N) continue;
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < MS; ++mi) {
-        const int64_t m = m0 + wm0 + mi * 16 + (lane & 15);
-        if (m < a.M) *reinterpret_cast<f32x4*>(dst + m * a.N + n) = acc[ni][mi];
+      for (int mi = 0; mi < MI; ++mi) {
+        const int64_t m = mb + mi * 32;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = nb + ni * 32 + 8 * q;
+          if (n < a.N)
+            *reinterpret_cast<f32x4*>(dst + m * a.N + n) =
+                f32x4{acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2], acc[ni][mi][4 * q + 3]};
+        }
       }
-    }
     return;
   }
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int64_t n = n0 + wn * 64 + ni * 16 + (lane >> 4) * 4;
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t n = nb + ni * 32 + 8 * q;
     if (n >= a.N) continue;
 #pragma unroll
-    for (int mi = 0; mi < MS; ++mi) {
-      const int64_t m = m0 + wm0 + mi * 16 + (lane & 15);
+    for (int mi = 0; mi < MI; ++mi) {
+      const int64_t m = mb + mi * 32;
       if (m >= a.M) continue;
-      float v0 = acc[ni][mi][0], v1 = acc[ni][mi][1], v2 = acc[ni][mi][2], v3 = acc[ni][mi][3];
+      float v0 = acc[ni][mi][4 * q], v1 = acc[ni][mi][4 * q + 1], v2 = acc[ni][mi][4 * q + 2], v3 = acc[ni][mi][4 * q + 3];
       if constexpr (EPI == EPI_CEGRAD) {
         // G = coef * (softmax - onehot) for this vocabulary chunk, as a hi + lo
         // pair of bf16 matrices (about 16 significant bits for the dH product)

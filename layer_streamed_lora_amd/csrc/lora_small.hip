@@ -281,12 +281,18 @@ static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks, int64_
 }
 constexpr int64_t NT_TARGET = 256, NT_MIN_STEPS = 4, TN_TARGET = 256, TN_MIN_STEPS = 4;
 
-// NT splits: about 256 workgroups of 64 rows, each split at least 1024 of K
-// (so each of its four waves takes four or more 64-wide steps)
+// NT splits: about NT_BLOCKS workgroups of 64 rows, each split at least
+// NT_MIN_K of K (so that each of its four waves takes NT_MIN_K / 256 steps)
+#ifndef LSL_NT_BLOCKS
+#define LSL_NT_BLOCKS 256
+#endif
+#ifndef LSL_NT_MIN_K
+#define LSL_NT_MIN_K 1024
+#endif
 static int nt_splits(int64_t T, int64_t K) {
   const int64_t tiles = (T + 63) / 64;
-  int64_t S = (256 + tiles - 1) / tiles;
-  if (S > K / 1024) S = K / 1024;
+  int64_t S = (LSL_NT_BLOCKS + tiles - 1) / tiles;
+  if (S > K / LSL_NT_MIN_K) S = K / LSL_NT_MIN_K;
   return S < 1 ? 1 : (int)S;
 }
 
