@@ -86,6 +86,9 @@ LSL_DEV uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) 
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Chunk swizzle of the unpadded token tile (8 chunks of 16 B per 128-B row).
+LSL_DEV int xswz(int r) { return (r ^ (r >> 3)) & 7; }
+
 // ---- row-major bf16 tile loader: ROWS rows x 64 k, 16 B chunks, 8 chunks per
 // row; thread -> rows tid/8 + 32 i. Per K-step only the scalar offset changes.
 template <int ROWS>
@@ -107,6 +110,17 @@ struct RowLoader {
     const int r = tid >> 3, c = (tid & 7) * 8;
 #pragma unroll
     for (int i = 0; i < CH; ++i) *reinterpret_cast<u32x4*>(lds + (r + 32 * i) * LDSW + c) = v[i];
+  }
+  // unpadded [ROWS][64] layout, chunk c of row r at position c ^ xswz(r): each
+  // wave store fills 8 whole rows (1 KB, no bank conflicts) and the 32-row MFMA
+  // operand reads spread over all banks
+  LSL_DEV void store_swz(uint16_t* lds, int tid) const {
+    const int r = tid >> 3, c = tid & 7;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int row = r + 32 * i;
+      *reinterpret_cast<u32x4*>(lds + row * 64 + 8 * (c ^ xswz(row))) = v[i];
+    }
   }
 };
 
@@ -249,7 +263,8 @@ struct Geo {
 // ksteps x 16-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-block[ni] x X-block[mi].
 // TRW: the weight tile is row-major [k][n] (row stride WLD) and read with
 // transposing LDS reads (natural k order, so the token tile is unchanged).
-template <int MI, bool TRW = false, int WLD = LDSW>
+// XSW: the token tile is the unpadded, swizzled [BM][64] layout (else [BM][LDSW]).
+template <int MI, bool TRW = false, int WLD = LDSW, bool XSW = false>
 LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x16 (&acc)[2][MI], int wn, int wm0, int lane,
                       int ksteps) {
   const int h8 = (lane >> 5) * 8, r32 = lane & 31;
@@ -270,8 +285,13 @@ LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x16 (&acc)[2][M
       }
     }
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + (wm0 + i * 32 + r32) * LDSW + kofs);
+    for (int i = 0; i < MI; ++i) {
+      const int row = wm0 + i * 32 + r32;
+      if constexpr (XSW)
+        bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + row * 64 + 8 * ((2 * ks + (lane >> 5)) ^ xswz(row)));
+      else
+        bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + row * LDSW + kofs);
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -323,7 +343,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto xstore = [&](const RowLoader<BM>& l, uint16_t* d) { l.store(d, tid); };
+  auto xstore = [&](const RowLoader<BM>& l, uint16_t* d) { l.store_swz(d, tid); };
   // ---- LoRA K-step first (kl <= 64, zero padded to 64), by split 0: the
   // accumulators start as s * (L Lt^T), so no second set of accumulators is live
   // during the main loop
@@ -398,7 +418,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         xl0.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 2) * BK);
         wl0.load(a, (int64_t)(kt0 + kt + 2) * BK);
       }
-      mma_tile<MI, KN, BN + 8>(Ws[0], Xs[0], acc, wn, wm0, lane, 4);
+      mma_tile<MI, KN, BN + 8, true>(Ws[0], Xs[0], acc, wn, wm0, lane, 4);
       if (kt + 1 < KT) {
         xstore(xl1, Xs[1]);
         wl1.store(Ws[1], lut, tid);
@@ -409,7 +429,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 3) * BK);
         wl1.load(a, (int64_t)(kt0 + kt + 3) * BK);
       }
-      mma_tile<MI, KN, BN + 8>(Ws[1], Xs[1], acc, wn, wm0, lane, 4);
+      mma_tile<MI, KN, BN + 8, true>(Ws[1], Xs[1], acc, wn, wm0, lane, 4);
       if (kt + 2 < KT) {
         xstore(xl0, Xs[0]);
         wl0.store(Ws[0], lut, tid);
@@ -437,7 +457,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
         wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
       }
-      mma_tile<MI, KN, BN + 8>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 4);
+      mma_tile<MI, KN, BN + 8, true>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 4);
       if constexpr (PIPE == 0) __syncthreads();
       if (more) {
         xstore(xl, Xs[PIPE == 1 ? cur ^ 1 : 0]);
