@@ -79,3 +79,70 @@ def nf4_dequant(packed: np.ndarray, absmax: np.ndarray, rnd=round_bf16) -> np.nd
     c = cb[code].reshape(-1, BLOCK)
     prod = (c * absmax.reshape(-1)[:, None].astype(np.float32)).astype(np.float32)
     return rnd(prod.astype(np.float64)).reshape(rows, cols)
+
+
+# ---------------------------------------------------------------- double quantisation
+# QLoRA's "double quantization" (Dettmers et al. 2023, section 3) quantises the
+# float32 absmax constants themselves with 8 bits in blocks of 256, keeping one
+# float32 constant per block. That is the storage the pages' sizes imply ("Soup:
+# ...", section "Layer Streaming: The Mechanism Behind the 4 GB Claim": a 3.60 GB
+# base store over 32 layers and two 113 MB buffers for Llama-3.1-8B). The pages
+# give only those sizes; the 8-bit map read here is the plainest one that fits:
+#   * s = float32(max of the 256 absmax values / 255) (float32 division);
+#   * q = round-half-even(absmax / s) (float32 division), clamped to [0, 255];
+#     q = 0 when s = 0;
+#   * absmax' = float32(q) * s (one float32 multiply); absmax values are
+#     flattened in row-major order and the last block may be short;
+#   * the 4-bit codes are those of nf4_quantize (chosen with the exact absmax);
+#     dequantisation uses absmax': w' = bf16(float32(c[code]) * absmax').
+DQ_BLOCK = 256
+
+
+def nf4dq_quantize_absmax(absmax: np.ndarray):
+    """float32 absmax [rows x nb] -> (q uint8 [rows x nb], scale float32 [ceil(rows*nb/256)])."""
+    a = np.asarray(absmax, np.float32).reshape(-1)
+    nblk = (a.size + DQ_BLOCK - 1) // DQ_BLOCK
+    scale = np.empty(nblk, np.float32)
+    q = np.empty(a.size, np.uint8)
+    for b in range(nblk):
+        blk = a[b * DQ_BLOCK:(b + 1) * DQ_BLOCK]
+        s = np.float32(np.max(blk) / np.float32(255.0))
+        scale[b] = s
+        if s > 0:
+            r = np.rint((blk / s).astype(np.float32))
+            q[b * DQ_BLOCK:(b + 1) * DQ_BLOCK] = np.clip(r, 0, 255).astype(np.uint8)
+        else:
+            q[b * DQ_BLOCK:(b + 1) * DQ_BLOCK] = 0
+    return q.reshape(np.shape(absmax)), scale
+
+
+def nf4dq_absmax(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """absmax' = float32(q) * s of its 256-block, same shape as q."""
+    qf = np.asarray(q, np.uint8).reshape(-1).astype(np.float32)
+    s = np.repeat(np.asarray(scale, np.float32), DQ_BLOCK)[:qf.size]
+    return (qf * s).astype(np.float32).reshape(np.shape(q))
+
+
+def nf4dq_quantize(w: np.ndarray):
+    """w [rows x cols] -> (codes uint8 [rows x cols/2], q uint8 [rows x cols/64], scale float32)."""
+    packed, absmax = nf4_quantize(w)
+    q, scale = nf4dq_quantize_absmax(absmax)
+    return packed, q, scale
+
+
+def nf4dq_dequant(packed: np.ndarray, q: np.ndarray, scale: np.ndarray, rnd=round_bf16) -> np.ndarray:
+    """w' = rnd(float32(c[code]) * absmax') as float64 [rows x cols]."""
+    return nf4_dequant(packed, nf4dq_absmax(q, scale), rnd)
+
+
+def nf4dq_layer_bytes(hidden, n_q, n_kv, head_dim, inter):
+    """Bytes of one decoder layer stored this way: 4-bit codes, 8-bit absmax,
+    float32 block constants for the seven projections, and the two bf16 norm
+    weights (no alignment padding)."""
+    q, kv = n_q * head_dim, n_kv * head_dim
+    mats = [(q, hidden), (kv, hidden), (kv, hidden), (hidden, q), (inter, hidden), (inter, hidden), (hidden, inter)]
+    total = 2 * 2 * hidden
+    for n, k in mats:
+        nb = n * k // BLOCK
+        total += n * k // 2 + nb + 4 * ((nb + DQ_BLOCK - 1) // DQ_BLOCK)
+    return total

@@ -12,9 +12,11 @@ import torch.nn.functional as F
 import oracle as O
 from oracle.bf16 import round_bf16, identity, bf16_bits, from_bf16_bits
 from oracle.nf4 import nf4_codebook, nf4_quantize, nf4_dequant, nf4_unpack
+from oracle.nf4 import nf4dq_quantize, nf4dq_quantize_absmax, nf4dq_absmax, nf4dq_dequant, nf4dq_layer_bytes
 from synth.configs import TINY_LAYER, PROJ_IN_OUT
 
 RNG = np.random.default_rng(1234)
+GOLDEN = __import__('os').path.join(__import__('os').path.dirname(__file__), 'golden')
 
 
 def t64(a):
@@ -165,6 +167,71 @@ def assert_fd(analytic, f, x, n=12, rtol=1e-6, atol=1e-9):
     # central differences carry roundoff of about 1e-16 * |f| / eps
     atol = atol + 1e-7 * max(1.0, float(np.max(np.abs(num))))
     assert np.allclose(ana, num, rtol=rtol, atol=atol), (ana, num)
+
+
+# ------------------------------------------------------------------ NF4 double quantisation
+def test_nf4dq_store_sizes_match_the_pages():
+    """The page's pre-flight sizes for Llama-3.1-8B (tests/golden/pages_store_sizes.json)
+    are those of 4-bit codes + 8-bit absmax + one float32 per 256 absmax values."""
+    import json
+    g = json.load(open(__import__("os").path.join(GOLDEN, "pages_store_sizes.json")))
+    m = g["model"]
+    b = nf4dq_layer_bytes(m["hidden"], m["n_q"], m["n_kv"], m["head_dim"], m["inter"])
+    assert round(b / 1e6) == g["buffer_MB"]
+    assert round(m["layers"] * b / 1e9, 2) == g["store_GB"]
+    # float32 absmax (one per 64 weights) would not fit those sizes
+    fp32_absmax = b + sum(n * k // 64 * 3 for n, k in [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096),
+                                                       (14336, 4096), (14336, 4096), (4096, 14336)])
+    assert round(m["layers"] * fp32_absmax / 1e9, 2) != g["store_GB"]
+
+
+def _brute_q(a, s):
+    """Nearest integer in [0, 255] to a / s in exact arithmetic (ties to even)."""
+    out = np.zeros(a.size, np.int64)
+    for i, v in enumerate(a.astype(np.float64)):
+        if s == 0:
+            continue
+        x = v / float(s)
+        best = min(range(256), key=lambda q: (abs(q - x), q % 2))
+        out[i] = best
+    return out
+
+
+def test_nf4dq_absmax_brute_force_and_bounds():
+    a = np.abs(RNG.standard_normal(600) * 0.03).astype(np.float32)   # blocks of 256, 256, 88
+    a[256:512] = 0.0                                                   # an all-zero block
+    a[300] = 0.0
+    q, s = nf4dq_quantize_absmax(a.reshape(6, 100))
+    q = q.reshape(-1)
+    assert s.shape == (3,) and s[1] == 0.0 and np.all(q[256:512] == 0)
+    for b in range(3):
+        blk = a[b * 256:(b + 1) * 256]
+        assert s[b] == np.float32(np.max(blk) / np.float32(255.0))
+        assert np.array_equal(q[b * 256:(b + 1) * 256], _brute_q(blk, s[b]))
+        if s[b] > 0:
+            assert q[b * 256 + int(np.argmax(blk))] == 255
+    a2 = nf4dq_absmax(q.reshape(6, 100), s).reshape(-1).astype(np.float64)
+    err = np.abs(a2 - a)
+    bound = np.repeat(s.astype(np.float64), 256)[:600] * (0.5 + 1e-5)
+    assert np.all(err <= bound)
+
+
+def test_nf4dq_dequant_values_and_error():
+    w = round_bf16(RNG.standard_normal((32, 512)) * 0.02)
+    w[3, :] = 0.0
+    packed, q, s = nf4dq_quantize(w)
+    p2, absmax = nf4_quantize(w)
+    assert np.array_equal(packed, p2)                       # codes chosen with the exact absmax
+    deq = nf4dq_dequant(packed, q, s, rnd=identity)
+    a2 = nf4dq_absmax(q, s).reshape(-1).astype(np.float64)
+    ratio = deq.reshape(-1, 64) / np.where(a2 > 0, a2, 1.0)[:, None]
+    cb = nf4_codebook().astype(np.float64)
+    assert np.all(np.isin(np.round(ratio, 5), np.round(cb, 5)))   # every value is code * absmax'
+    assert np.all(deq[3] == 0.0)
+    # error: NF4 rounding (half the widest code gap) plus the absmax error
+    gap = np.max(np.diff(cb)) / 2
+    tol = absmax.reshape(-1, 1) * gap + np.repeat(s, 256)[:absmax.size].reshape(-1, 1) * 0.5 * 1.0001
+    assert np.all(np.abs(deq - w).reshape(-1, 64) <= tol + 1e-12)
 
 
 # ------------------------------------------------------------------ LoRA linear
