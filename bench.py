@@ -134,6 +134,33 @@ def time_steps(m, inputs, steps, warmup, timing_which=0, stats=False):
     return out
 
 
+def nf4dq_leg(args, T_inputs_seed):
+    """The same model with double-quantized absmax (8-bit absmax codes, one
+    float32 per 256): streamed step time, gate|up GEMM time and bytes moved."""
+    import torch
+    import synth
+    wl, shape, ms = workload("llama8b_nf4dq")
+    T = ms.batch * ms.seq
+    log(f"building llama8b_nf4dq: {ms.n_layers} layers, {shape.wfmt} base")
+    m = build_model(shape, ms, "streamed")
+    chunks = [synth.token_ids(T, ms.vocab, T_inputs_seed, salt=i) for i in range(ms.n_micro)]
+    inputs = m.prepare_inputs(chunks)
+    res = time_steps(m, inputs, args.steps, args.warmup, timing_which=3)
+    cs = time_steps(m, inputs, 1, 0, stats=True)
+    g_ms = res["kernel_ms_total"] / max(res["kernel_launches"], 1)
+    log(f"  nf4dq streamed: {res['ms_per_step']:.2f} ms/step, gate|up GEMM {g_ms * 1e3:.1f} us")
+    out = {"workload": "llama8b_nf4dq: the same model, NF4 with double-quantized absmax",
+           "ms_per_step": round(res["ms_per_step"], 3),
+           "tok_s": round(T * ms.n_micro / (res["ms_per_step"] * 1e-3), 2),
+           "blob_bytes": m.blob_bytes, "store_GB": round(m.blob_bytes * ms.n_layers / 1e9, 3),
+           "h2d_bytes_per_step": cs.get("h2d_bytes"),
+           "h2d_GBps_copy_engine": cs.get("h2d_copy_s") and round(cs["h2d_bytes"] / cs["h2d_copy_s"] / 1e9, 2),
+           "gu_gemm_avg_launch_ms": round(g_ms, 4), "loss": round(res["loss"], 5)}
+    del m, inputs
+    torch.cuda.synchronize()
+    return out
+
+
 def counters_traffic():
     """HBM bytes per launch of the timed GEMM from committed rocprofv3 counters,
     if they were taken on the current kernel source (else None)."""
@@ -301,6 +328,7 @@ def main():
     ap.add_argument("--workload", default="llama8b_nf4")
     ap.add_argument("--no-resident", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-nf4dq", action="store_true", help="skip the double-quantized-absmax variant")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain copy kernel of known size first (for scaling HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="summarise a rocprofv3 kernel-trace csv run and exit")
@@ -361,6 +389,13 @@ def main():
         resident = time_steps(r_model, inputs, args.steps, args.warmup)
         log(f"  resident: {resident['ms_per_step']:.2f} ms/step")
 
+    variant = None
+    if not args.no_nf4dq and args.workload == "llama8b_nf4":
+        del r_model
+        r_model = None
+        torch.cuda.empty_cache()
+        variant = nf4dq_leg(args, wl.wid)
+
     tok_s = T * ms.n_micro / (res["ms_per_step"] * 1e-3)
     flops = step_flops(shape, ms)
     # the timed kernel: forward gate|up GEMM, NF4 dequant fused, LoRA-up K-step fused
@@ -395,6 +430,7 @@ def main():
         "streamed_over_resident": resident and round(res["ms_per_step"] / resident["ms_per_step"], 3),
         "bit_exact_vs_resident": bit_exact,
         "loss": round(res["loss"], 5),
+        "nf4dq": variant,
         "context": {"pages_tok_s": 119.6, "pages_hardware": "RTX 3050 Laptop 4 GB, seq/batch not stated"},
     }
     if not args.no_cpu_baseline:

@@ -90,10 +90,26 @@ lsl_status lsl_nf4_quantize(const uint16_t* w, int64_t rows, int64_t cols,
 lsl_status lsl_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t rows,
                            int64_t cols, uint16_t* w, lsl_stream stream);
 
+/* NF4 with double-quantized absmax: QLoRA's double quantization (section 3),
+ * the storage behind the 3.60 GB store and 113 MB layer buffers the pages
+ * report for Llama-3.1-8B ("Soup: ...", section "Layer Streaming: The Mechanism
+ * Behind the 4 GB Claim"). The float32 absmax values, flattened row-major, are
+ * split into blocks of 256 (the last may be short); per block
+ * s = float32(max / 255), q = round-half-even(absmax / s) (float32 division)
+ * clamped to [0, 255], q = 0 when s = 0; absmax' = float32(q) * s. The 4-bit
+ * codes stay those of lsl_nf4_quantize. */
+/* absmax [n] float32 -> q [n] uint8, scale [ceil(n / 256)] float32. Device pointers. */
+lsl_status lsl_nf4dq_quantize_absmax(const float* absmax, int64_t n, uint8_t* q, float* scale,
+                                     lsl_stream stream);
+/* w' = bf16(code_value * absmax') with absmax' = float32(q) * s of its block. */
+lsl_status lsl_nf4dq_dequant(const uint8_t* codes, const uint8_t* q, const float* scale, int64_t rows,
+                             int64_t cols, uint16_t* w, lsl_stream stream);
+
 /* ------------------------------------------------------------------ weights */
-enum { LSL_WFMT_NF4 = 0, LSL_WFMT_BF16 = 1 };
+enum { LSL_WFMT_NF4 = 0, LSL_WFMT_BF16 = 1, LSL_WFMT_NF4DQ = 2 };
 /* A frozen weight [n_out x k_in] (n_out and k_in multiples of 64): NF4 (nf4
- * codes + absmax) or bf16. Pointers not used by the format must be NULL. */
+ * codes + absmax), bf16, or NF4 with double-quantized absmax (nf4 codes +
+ * absmax_q + absmax_scale). Pointers not used by the format must be NULL. */
 typedef struct {
   int32_t fmt;
   int32_t pad;
@@ -102,6 +118,8 @@ typedef struct {
   const uint8_t* nf4;
   const float* absmax;
   const uint16_t* bf16;
+  const uint8_t* absmax_q;
+  const float* absmax_scale;
 } lsl_weight;
 
 /* ------------------------------------------------------------------ LoRA linear
@@ -137,7 +155,7 @@ lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, const uint16_t*
 typedef struct {
   int32_t hidden, n_q, n_kv, head_dim, inter;
   float rms_eps, rope_theta;
-  int32_t wfmt;      /* LSL_WFMT_NF4 or LSL_WFMT_BF16 */
+  int32_t wfmt;      /* LSL_WFMT_NF4, LSL_WFMT_BF16 or LSL_WFMT_NF4DQ */
   int32_t lora_r;
   float lora_scale;  /* alpha / r */
 } lsl_layer_cfg;
@@ -146,7 +164,9 @@ typedef struct {
  * Matrices are stacked per fused GEMM: qkv = [Wq; Wk; Wv] [(n_q+2 n_kv) d x hidden],
  * o [hidden x n_q d], gu = [Wgate; Wup] [2 inter x hidden], down [hidden x inter].
  * For NF4 each matrix is codes at w_off[i] and float32 absmax at absmax_off[i];
- * for bf16 the matrix is at w_off[i] and absmax_off[i] is 0.
+ * for NF4DQ codes at w_off[i], uint8 absmax codes at absmax_off[i] and float32
+ * block constants at scale_off[i]; for bf16 the matrix is at w_off[i] and
+ * absmax_off[i] (and scale_off[i]) are 0.
  * norm1/norm2 are bf16 [hidden]. The pinned host store and a resident copy use
  * this same layout, so a slot holds a byte-identical copy of one layer. */
 enum { LSL_M_QKV = 0, LSL_M_O = 1, LSL_M_GU = 2, LSL_M_DOWN = 3 };
@@ -155,6 +175,7 @@ typedef struct {
   uint64_t w_off[4];
   uint64_t absmax_off[4];
   uint64_t total_bytes;
+  uint64_t scale_off[4];
 } lsl_layer_layout;
 lsl_status lsl_layer_layout_get(const lsl_layer_cfg* cfg, lsl_layer_layout* out);
 

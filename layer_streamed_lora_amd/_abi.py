@@ -7,7 +7,7 @@ LIB_PATH = os.path.join(HERE, "liblsl.so")
 
 LSL_OK, LSL_ERR_INVALID_ARG, LSL_ERR_UNSUPPORTED, LSL_ERR_NOT_PINNED, LSL_ERR_WORKSPACE, LSL_ERR_STATE, LSL_ERR_HIP = range(7)
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "NOT_PINNED", 4: "WORKSPACE", 5: "STATE", 6: "HIP"}
-WFMT_NF4, WFMT_BF16 = 0, 1
+WFMT_NF4, WFMT_BF16, WFMT_NF4DQ = 0, 1, 2
 M_QKV, M_O, M_GU, M_DOWN = 0, 1, 2, 3
 MODE_FWD, MODE_BWD = 0, 1
 
@@ -17,7 +17,7 @@ i32, i64, f32, sz = C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
 class Weight(C.Structure):
     _fields_ = [("fmt", i32), ("pad", i32), ("n_out", i64), ("k_in", i64),
-                ("nf4", vp), ("absmax", vp), ("bf16", vp)]
+                ("nf4", vp), ("absmax", vp), ("bf16", vp), ("absmax_q", vp), ("absmax_scale", vp)]
 
 
 class LayerCfg(C.Structure):
@@ -27,7 +27,8 @@ class LayerCfg(C.Structure):
 
 class LayerLayout(C.Structure):
     _fields_ = [("norm1_off", C.c_uint64), ("norm2_off", C.c_uint64), ("w_off", C.c_uint64 * 4),
-                ("absmax_off", C.c_uint64 * 4), ("total_bytes", C.c_uint64)]
+                ("absmax_off", C.c_uint64 * 4), ("total_bytes", C.c_uint64),
+                ("scale_off", C.c_uint64 * 4)]
 
 
 class LoraSet(C.Structure):
@@ -50,6 +51,8 @@ PROTOS = {
     "lsl_nf4_codebook": (i32, [C.POINTER(C.c_float)]),
     "lsl_nf4_quantize": (i32, [vp, i64, i64, vp, vp, vp]),
     "lsl_nf4_dequant": (i32, [vp, vp, i64, i64, vp, vp]),
+    "lsl_nf4dq_quantize_absmax": (i32, [vp, i64, vp, vp, vp]),
+    "lsl_nf4dq_dequant": (i32, [vp, vp, vp, i64, i64, vp, vp]),
     "lsl_lora_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
     "lora_linear_fwd": (i32, [vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, sz, vp]),
     "lora_linear_bwd": (i32, [vp, vp, vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),

@@ -75,7 +75,7 @@ static lsl_status check_cfg(const lsl_layer_cfg* c, const char* fn) {
     return set_error(LSL_ERR_UNSUPPORTED, "%s: hidden and inter must be multiples of 64", fn);
   if (c->lora_r != 8 && c->lora_r != 16)
     return set_error(LSL_ERR_UNSUPPORTED, "%s: fused layer supports LoRA rank 8 or 16 (got %d)", fn, c->lora_r);
-  if (c->wfmt != LSL_WFMT_NF4 && c->wfmt != LSL_WFMT_BF16)
+  if (c->wfmt != LSL_WFMT_NF4 && c->wfmt != LSL_WFMT_BF16 && c->wfmt != LSL_WFMT_NF4DQ)
     return set_error(LSL_ERR_INVALID_ARG, "%s: unknown weight format %d", fn, c->wfmt);
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return set_error(LSL_ERR_INVALID_ARG, "%s: bad eps/theta", fn);
   return LSL_OK;
@@ -100,9 +100,15 @@ static void layout_of(const lsl_layer_cfg* c, lsl_layer_layout* L) {
   for (int i = 0; i < 4; ++i) {
     int64_t n, k;
     mat_shape(d, i, n, k);
+    L->scale_off[i] = 0;
     if (c->wfmt == LSL_WFMT_NF4) {
       L->w_off[i] = take((uint64_t)n * k / 2);
       L->absmax_off[i] = take((uint64_t)n * k / 64 * 4);
+    } else if (c->wfmt == LSL_WFMT_NF4DQ) {
+      const uint64_t nb = (uint64_t)n * k / 64;
+      L->w_off[i] = take((uint64_t)n * k / 2);
+      L->absmax_off[i] = take(nb);
+      L->scale_off[i] = take((nb + 255) / 256 * 4);
     } else {
       L->w_off[i] = take((uint64_t)n * k * 2);
       L->absmax_off[i] = 0;
@@ -168,6 +174,7 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
 struct LayerPtrs {
   const uint16_t* norm1; const uint16_t* norm2;
   const uint16_t* wb[4]; const uint8_t* wq[4]; const float* wa[4];
+  const uint8_t* wq8[4]; const float* wsc[4];  // NF4DQ absmax codes and block constants
 };
 
 static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
@@ -181,6 +188,10 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
     if (c->wfmt == LSL_WFMT_NF4) {
       p.wq[i] = (const uint8_t*)(b + L.w_off[i]);
       p.wa[i] = (const float*)(b + L.absmax_off[i]);
+    } else if (c->wfmt == LSL_WFMT_NF4DQ) {
+      p.wq[i] = (const uint8_t*)(b + L.w_off[i]);
+      p.wq8[i] = (const uint8_t*)(b + L.absmax_off[i]);
+      p.wsc[i] = (const float*)(b + L.scale_off[i]);
     } else {
       p.wb[i] = (const uint16_t*)(b + L.w_off[i]);
     }
@@ -205,7 +216,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   if (!y) return LSL_OK;
   GemmDesc g;
   g.x = x; g.ldx = k; g.wfmt = c->wfmt; g.kn = false;
-  g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i];
+  g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i]; g.wq8 = W.wq8[i]; g.wsc = W.wsc[i];
   g.M = d.T; g.N = n; g.K = k;
   g.lora = 1; g.la = t; g.ldla = kl; g.kl = kl; g.lb = lo->B[i]; g.r = d.r; g.nseg = nseg;
   if (i == LSL_M_QKV) { g.seg_end[0] = d.Q; g.seg_end[1] = d.Q + d.KV; g.seg_end[2] = d.NQKV; }
@@ -239,7 +250,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
   if (dx) {
     GemmDesc g;
     g.x = dy; g.ldx = n; g.wfmt = c->wfmt; g.kn = true;
-    g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i];
+    g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i]; g.wq8 = W.wq8[i]; g.wsc = W.wsc[i];
     g.M = d.T; g.N = k; g.K = n;
     g.lora = 2; g.la = u; g.ldla = kl; g.kl = kl; g.lb = lo->A[i]; g.r = d.r;
     g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part;

@@ -32,10 +32,16 @@ static lsl_status check_weight(const lsl_weight* W, const char* fn) {
     return set_error(LSL_ERR_UNSUPPORTED, "%s: weight [%lld x %lld] needs k_in and n_out multiples of 64", fn,
                      (long long)W->n_out, (long long)W->k_in);
   if (W->fmt == LSL_WFMT_NF4) {
-    if (!W->nf4 || !W->absmax || W->bf16 || !aligned(W->nf4, 16) || !aligned(W->absmax, 4))
+    if (!W->nf4 || !W->absmax || W->bf16 || W->absmax_q || W->absmax_scale || !aligned(W->nf4, 16) ||
+        !aligned(W->absmax, 4))
       return set_error(LSL_ERR_INVALID_ARG, "%s: NF4 weight needs 16-byte aligned codes and absmax, bf16 NULL", fn);
+  } else if (W->fmt == LSL_WFMT_NF4DQ) {
+    if (!W->nf4 || !W->absmax_q || !W->absmax_scale || W->absmax || W->bf16 || !aligned(W->nf4, 16) ||
+        !aligned(W->absmax_scale, 4))
+      return set_error(LSL_ERR_INVALID_ARG,
+                       "%s: NF4DQ weight needs 16-byte aligned codes, absmax_q and absmax_scale; absmax, bf16 NULL", fn);
   } else if (W->fmt == LSL_WFMT_BF16) {
-    if (!W->bf16 || W->nf4 || W->absmax || !aligned(W->bf16, 16))
+    if (!W->bf16 || W->nf4 || W->absmax || W->absmax_q || W->absmax_scale || !aligned(W->bf16, 16))
       return set_error(LSL_ERR_INVALID_ARG, "%s: bf16 weight needs a 16-byte aligned pointer, NF4 pointers NULL", fn);
   } else {
     return set_error(LSL_ERR_INVALID_ARG, "%s: unknown weight format %d", fn, W->fmt);
@@ -45,7 +51,7 @@ static lsl_status check_weight(const lsl_weight* W, const char* fn) {
 
 static void weight_into(GemmDesc& g, const lsl_weight* W) {
   g.wfmt = W->fmt;
-  g.wb = W->bf16; g.wq = W->nf4; g.wa = W->absmax;
+  g.wb = W->bf16; g.wq = W->nf4; g.wa = W->absmax; g.wq8 = W->absmax_q; g.wsc = W->absmax_scale;
 }
 
 }  // namespace lsl

@@ -6,6 +6,7 @@ struct GemmDesc {
   const uint16_t* x = nullptr; int64_t ldx = 0;    // [M x K]
   int wfmt = LSL_WFMT_BF16; bool kn = false;        // weight format; stored [K x N] when kn
   const uint16_t* wb = nullptr; const uint8_t* wq = nullptr; const float* wa = nullptr;
+  const uint8_t* wq8 = nullptr; const float* wsc = nullptr;  // NF4DQ absmax codes and block constants
   int64_t M = 0, N = 0, K = 0;
   int lora = 0;                                     // 0 none, 1 forward (masked B), 2 backward (A^T)
   const uint16_t* la = nullptr; int64_t ldla = 0; int kl = 0;

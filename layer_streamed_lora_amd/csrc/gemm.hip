@@ -44,6 +44,7 @@ constexpr int NTHREADS = 256;
 struct GemmKArgs {
   const uint16_t* x; int64_t ldx;
   const uint16_t* wb; const uint8_t* wq; const float* wa;
+  const uint8_t* wq8; const float* wsc;  // NF4DQ: 8-bit absmax codes, float32 block constants
   int64_t M, N, K;
   const uint16_t* la; int64_t ldla; int kl;   // LoRA A-side [M x kl]
   const uint16_t* lb;                         // fwd: B_full [N x r]; bwd: A_full [kl x N]
@@ -138,20 +139,27 @@ struct WLoader<LSL_WFMT_BF16, false, BN> {
 // NF4 [N x K]: each of the BN rows has 32 code bytes per K-step; TPR threads per
 // row, BPT bytes (2 BPT weights) each. Rows past N are clamped to the last row:
 // their outputs are never stored.
-template <int BN>
-struct WLoader<LSL_WFMT_NF4, false, BN> {
+// absmax of NF4 block idx (flattened row-major): float32, or (NF4DQ) q * s
+template <int WFMT>
+LSL_DEV float block_absmax(const GemmKArgs& a, int64_t idx) {
+  if constexpr (WFMT == LSL_WFMT_NF4DQ) return (float)a.wq8[idx] * a.wsc[idx >> 8];
+  else return a.wa[idx];
+}
+
+template <int WFMT, int BN>
+struct Nf4NkLoader {
   static constexpr int TPR = 256 / BN, BPT = 32 / TPR;
   const uint8_t* pc;
-  const float* pa;
+  int64_t ai;  // absmax index of the row's first block
   uint32_t c[BPT / 4];
   float am;
   LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) {
     const int row = tid / TPR, part = tid % TPR;
     const int64_t n = n0 + row < a.N ? n0 + row : a.N - 1;
     pc = a.wq + n * (a.K >> 1) + part * BPT;
-    pa = a.wa + n * (a.K >> 6);
+    ai = n * (a.K >> 6);
   }
-  LSL_DEV void load(const GemmKArgs&, int64_t k0) {
+  LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
     if constexpr (BPT == 16) {
       u32x4 v = *reinterpret_cast<const u32x4*>(pc + (k0 >> 1));
       c[0] = v[0]; c[1] = v[1]; c[2] = v[2]; c[3] = v[3];
@@ -159,7 +167,7 @@ struct WLoader<LSL_WFMT_NF4, false, BN> {
       u32x2 v = *reinterpret_cast<const u32x2*>(pc + (k0 >> 1));
       c[0] = v[0]; c[1] = v[1];
     }
-    am = pa[k0 >> 6];
+    am = block_absmax<WFMT>(a, ai + (k0 >> 6));
   }
   LSL_DEV void store(uint16_t* lds, const float* lut, int tid) const {
     const int row = tid / TPR, part = tid % TPR;
@@ -174,6 +182,10 @@ struct WLoader<LSL_WFMT_NF4, false, BN> {
     for (int i = 0; i < BPT / 4; ++i) d[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
 };
+template <int BN>
+struct WLoader<LSL_WFMT_NF4, false, BN> : Nf4NkLoader<LSL_WFMT_NF4, BN> {};
+template <int BN>
+struct WLoader<LSL_WFMT_NF4DQ, false, BN> : Nf4NkLoader<LSL_WFMT_NF4DQ, BN> {};
 
 // bf16 stored [K x N] (row = reduction index): thread -> KR k-rows x 8 n-cols.
 // Columns past N read neighbouring data or zeros; their outputs are never stored.
@@ -208,11 +220,11 @@ struct WLoader<LSL_WFMT_BF16, true, BN> {
 
 // NF4 stored [K x N]: thread -> KR k-rows x 8 n-cols (4 code bytes + absmax per
 // row); column groups past N are clamped to the last group (outputs not stored).
-template <int BN>
-struct WLoader<LSL_WFMT_NF4, true, BN> {
+template <int WFMT, int BN>
+struct Nf4KnLoader {
   static constexpr int KR = BN / 32, OG = BN / 8;
   const uint8_t* pc;
-  const float* pa;
+  int64_t ai;  // absmax index of this thread's first row and column block
   int64_t rowc, rowa;
   uint32_t c[KR];
   float am[KR];
@@ -222,13 +234,13 @@ struct WLoader<LSL_WFMT_NF4, true, BN> {
     rowc = a.N >> 1;
     rowa = a.N >> 6;
     pc = a.wq + (int64_t)(q * KR) * rowc + (n >> 1);
-    pa = a.wa + (int64_t)(q * KR) * rowa + (n >> 6);
+    ai = (int64_t)(q * KR) * rowa + (n >> 6);
   }
-  LSL_DEV void load(const GemmKArgs&, int64_t k0) {
+  LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
 #pragma unroll
     for (int rr = 0; rr < KR; ++rr) {
       c[rr] = *reinterpret_cast<const uint32_t*>(pc + (k0 + rr) * rowc);
-      am[rr] = pa[(k0 + rr) * rowa];
+      am[rr] = block_absmax<WFMT>(a, ai + (k0 + rr) * rowa);
     }
   }
   // row-major [k][n] tile (row stride BN + 8); the MFMA reads it transposed
@@ -246,6 +258,10 @@ struct WLoader<LSL_WFMT_NF4, true, BN> {
     }
   }
 };
+template <int BN>
+struct WLoader<LSL_WFMT_NF4, true, BN> : Nf4KnLoader<LSL_WFMT_NF4, BN> {};
+template <int BN>
+struct WLoader<LSL_WFMT_NF4DQ, true, BN> : Nf4KnLoader<LSL_WFMT_NF4DQ, BN> {};
 
 // 32 x 32 x 16 bf16 MFMA (on gfx950 twice the throughput of 16 x 16 x 32). Lane l
 // holds A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; accumulator
@@ -332,7 +348,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   tile_coords((int)blockIdx.x - split * ntiles, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  if constexpr (WFMT == LSL_WFMT_NF4)
+  if constexpr (WFMT != LSL_WFMT_BF16)
     if (tid < 16) lut[tid] = a.cb[tid];
 
   f32x16 acc[2][MI];
@@ -657,6 +673,9 @@ static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
   if (d.wfmt == LSL_WFMT_NF4) {
     if (d.kn) launch_lora_variant<LSL_WFMT_NF4, true, BN, BM>(a, d.lora, s, grid);
     else launch_lora_variant<LSL_WFMT_NF4, false, BN, BM>(a, d.lora, s, grid);
+  } else if (d.wfmt == LSL_WFMT_NF4DQ) {
+    if (d.kn) launch_lora_variant<LSL_WFMT_NF4DQ, true, BN, BM>(a, d.lora, s, grid);
+    else launch_lora_variant<LSL_WFMT_NF4DQ, false, BN, BM>(a, d.lora, s, grid);
   } else {
     if (d.kn) launch_lora_variant<LSL_WFMT_BF16, true, BN, BM>(a, d.lora, s, grid);
     else launch_lora_variant<LSL_WFMT_BF16, false, BN, BM>(a, d.lora, s, grid);
@@ -712,7 +731,7 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
                      (long long)d.K, (long long)d.N);
   if (d.lora && (d.kl <= 0 || d.kl > 64 || d.kl % 8))
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: LoRA width %d must be a multiple of 8 in [8, 64]", d.kl);
-  if (d.wfmt == LSL_WFMT_NF4 && d.kn && d.N % 64)
+  if (d.wfmt != LSL_WFMT_BF16 && d.kn && d.N % 64)
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: NF4 transposed operand needs N %% 64 == 0");
   if (d.kwrap && (d.kwrap % BK || d.K > 2 * d.kwrap || !d.kn))
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: wrapped reduction needs kn, kwrap %% 64 == 0 and K <= 2 kwrap");
@@ -722,7 +741,7 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: operand larger than 4 GiB");
   GemmKArgs a{};
   a.x = d.x; a.ldx = d.ldx;
-  a.wb = d.wb; a.wq = d.wq; a.wa = d.wa;
+  a.wb = d.wb; a.wq = d.wq; a.wa = d.wa; a.wq8 = d.wq8; a.wsc = d.wsc;
   a.M = d.M; a.N = d.N; a.K = d.K;
   a.la = d.la; a.ldla = d.ldla; a.kl = d.kl; a.lb = d.lb; a.r = d.r; a.nseg = d.nseg;
   for (int i = 0; i < 4; ++i) a.seg_end[i] = d.seg_end[i];

@@ -108,9 +108,66 @@ __global__ void nf4_dequant_kernel(const uint8_t* __restrict__ codes, const floa
   reinterpret_cast<u32x4*>(w)[i] = o;
 }
 
+// Double quantisation of the absmax values: one workgroup per block of 256.
+__global__ __launch_bounds__(256) void nf4dq_absmax_kernel(const float* __restrict__ absmax, int64_t n,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float a = i < n ? absmax[i] : 0.f;
+  float m = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(m, 255.0f);
+  if (threadIdx.x == 0) scale[blockIdx.x] = s;
+  if (i < n) q[i] = s > 0.f ? (uint8_t)fminf(fmaxf(rintf(__fdiv_rn(a, s)), 0.f), 255.f) : (uint8_t)0;
+}
+
+// One thread per 8 elements, absmax' = float(q) * s of its 256-block.
+__global__ void nf4dq_dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ qa,
+                                     const float* __restrict__ scale, int64_t n8, uint16_t* __restrict__ w,
+                                     Nf4Table tab) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  uint32_t c = reinterpret_cast<const uint32_t*>(codes)[i];
+  const int64_t b = i >> 3;
+  const float am = (float)qa[b] * scale[b >> 8];
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t byte = (c >> (8 * j)) & 0xFF;
+    o[j] = pack2(tab.cb[byte >> 4] * am, tab.cb[byte & 15] * am);
+  }
+  reinterpret_cast<u32x4*>(w)[i] = o;
+}
+
 }  // namespace lsl
 
 using namespace lsl;
+
+extern "C" lsl_status lsl_nf4dq_quantize_absmax(const float* absmax, int64_t n, uint8_t* q, float* scale,
+                                                lsl_stream stream) {
+  if (n < 0) return set_error(LSL_ERR_INVALID_ARG, "lsl_nf4dq_quantize_absmax: n < 0");
+  if (n == 0) return LSL_OK;
+  if (!absmax || !q || !scale || !aligned(absmax, 4) || !aligned(scale, 4))
+    return set_error(LSL_ERR_INVALID_ARG, "lsl_nf4dq_quantize_absmax: null or misaligned pointer");
+  hipLaunchKernelGGL(nf4dq_absmax_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     absmax, n, q, scale);
+  return check_launch("nf4dq_quantize_absmax");
+}
+
+extern "C" lsl_status lsl_nf4dq_dequant(const uint8_t* codes, const uint8_t* q, const float* scale, int64_t rows,
+                                        int64_t cols, uint16_t* w, lsl_stream stream) {
+  if (rows < 0 || cols < 0 || cols % 64)
+    return set_error(LSL_ERR_INVALID_ARG, "lsl_nf4dq_dequant: cols must be a multiple of 64");
+  if (rows * cols == 0) return LSL_OK;
+  if (!w || !codes || !q || !scale || !aligned(w, 16) || !aligned(codes, 16) || !aligned(scale, 4))
+    return set_error(LSL_ERR_INVALID_ARG, "lsl_nf4dq_dequant: null or misaligned pointer");
+  int64_t n8 = rows * cols / 8;
+  hipLaunchKernelGGL(nf4dq_dequant_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     codes, q, scale, n8, w, nf4_table());
+  return check_launch("nf4dq_dequant");
+}
 
 extern "C" lsl_status lsl_nf4_codebook(float out[16]) {
   if (!out) return set_error(LSL_ERR_INVALID_ARG, "lsl_nf4_codebook: out is NULL");

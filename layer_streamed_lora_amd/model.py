@@ -9,12 +9,13 @@ from . import _abi
 from .ops import lib, _check, _p, _s
 
 PROJ_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+WFMT_CODES = {"nf4": _abi.WFMT_NF4, "bf16": _abi.WFMT_BF16, "nf4dq": _abi.WFMT_NF4DQ}
 
 
 def layer_cfg(shape):
     """ctypes lsl_layer_cfg from a synth LayerShape-like object."""
     return _abi.LayerCfg(shape.hidden, shape.n_q, shape.n_kv, shape.head_dim, shape.inter, shape.rms_eps,
-                         shape.rope_theta, _abi.WFMT_NF4 if shape.wfmt == "nf4" else _abi.WFMT_BF16,
+                         shape.rope_theta, WFMT_CODES[shape.wfmt],
                          shape.lora_r, shape.lora_alpha / shape.lora_r)
 
 
@@ -47,6 +48,15 @@ def write_layer_blob(shape, cfg, blob, w, stream=None):
             codes = region(L.w_off[i], n * k // 2)
             absmax = region(L.absmax_off[i], n * k // 64 * 4).view(torch.float32)
             _check("lsl_nf4_quantize", lib().lsl_nf4_quantize(_p(m), n, k, _p(codes), _p(absmax), _s(stream)))
+        elif cfg.wfmt == _abi.WFMT_NF4DQ:
+            nb = n * k // 64
+            codes = region(L.w_off[i], n * k // 2)
+            absmax = torch.empty(nb, dtype=torch.float32, device=blob.device)
+            _check("lsl_nf4_quantize", lib().lsl_nf4_quantize(_p(m), n, k, _p(codes), _p(absmax), _s(stream)))
+            q = region(L.absmax_off[i], nb)
+            scale = region(L.scale_off[i], (nb + 255) // 256 * 4).view(torch.float32)
+            _check("lsl_nf4dq_quantize_absmax",
+                   lib().lsl_nf4dq_quantize_absmax(_p(absmax), nb, _p(q), _p(scale), _s(stream)))
         else:
             region(L.w_off[i], n * k * 2).view(torch.bfloat16).copy_(m.view(-1))
     return L

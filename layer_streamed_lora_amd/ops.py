@@ -81,20 +81,54 @@ def nf4_dequant(codes, absmax, stream=None):
     return w
 
 
+def nf4dq_quantize_absmax(absmax, stream=None):
+    """float32 absmax (any shape, flattened row-major) -> (uint8 codes, float32
+    per-256-block constants)."""
+    _need(absmax, torch.float32, "absmax")
+    n = absmax.numel()
+    q = torch.empty(absmax.shape, dtype=torch.uint8, device=absmax.device)
+    scale = torch.empty(((n + 255) // 256,), dtype=torch.float32, device=absmax.device)
+    _check("lsl_nf4dq_quantize_absmax",
+           lib().lsl_nf4dq_quantize_absmax(_p(absmax), n, _p(q), _p(scale), _s(stream)))
+    return q, scale
+
+
+def nf4dq_dequant(codes, q, scale, stream=None):
+    rows, half = codes.shape
+    w = torch.empty((rows, 2 * half), dtype=torch.bfloat16, device=codes.device)
+    _check("lsl_nf4dq_dequant",
+           lib().lsl_nf4dq_dequant(_p(codes), _p(q), _p(scale), rows, 2 * half, _p(w), _s(stream)))
+    return w
+
+
 # ------------------------------------------------------------------ weights
 class FrozenWeight:
-    """A frozen [n_out x k_in] weight: NF4 (codes, absmax) or bf16."""
+    """A frozen [n_out x k_in] weight: NF4 (codes, absmax), NF4 with
+    double-quantized absmax (codes, absmax_q, absmax_scale) or bf16."""
 
-    def __init__(self, n_out, k_in, codes=None, absmax=None, bf16=None):
+    def __init__(self, n_out, k_in, codes=None, absmax=None, bf16=None, absmax_q=None, absmax_scale=None):
         self.n_out, self.k_in = n_out, k_in
         self.codes, self.absmax, self.bf16 = codes, absmax, bf16
-        self.fmt = _abi.WFMT_BF16 if bf16 is not None else _abi.WFMT_NF4
-        self.struct = _abi.Weight(self.fmt, 0, n_out, k_in, _p(codes), _p(absmax), _p(bf16))
+        self.absmax_q, self.absmax_scale = absmax_q, absmax_scale
+        if bf16 is not None:
+            self.fmt = _abi.WFMT_BF16
+        elif absmax_q is not None:
+            self.fmt = _abi.WFMT_NF4DQ
+        else:
+            self.fmt = _abi.WFMT_NF4
+        self.struct = _abi.Weight(self.fmt, 0, n_out, k_in, _p(codes), _p(absmax), _p(bf16),
+                                  _p(absmax_q), _p(absmax_scale))
 
     @classmethod
     def nf4(cls, w_bf16, stream=None):
         codes, absmax = nf4_quantize(w_bf16, stream)
         return cls(w_bf16.shape[0], w_bf16.shape[1], codes=codes, absmax=absmax)
+
+    @classmethod
+    def nf4dq(cls, w_bf16, stream=None):
+        codes, absmax = nf4_quantize(w_bf16, stream)
+        q, scale = nf4dq_quantize_absmax(absmax, stream)
+        return cls(w_bf16.shape[0], w_bf16.shape[1], codes=codes, absmax_q=q, absmax_scale=scale)
 
     @classmethod
     def dense(cls, w_bf16):

@@ -146,3 +146,23 @@ def nf4dq_layer_bytes(hidden, n_q, n_kv, head_dim, inter):
         nb = n * k // BLOCK
         total += n * k // 2 + nb + 4 * ((nb + DQ_BLOCK - 1) // DQ_BLOCK)
     return total
+
+
+def nf4dq_quantize_fused(mats):
+    """Double quantization of several matrices with the same column count that
+    are stored one under another as one fused matrix (the q, k and v weights;
+    gate and up): the 4-bit codes and absmax are those of each matrix alone,
+    and the absmax values of the stacked matrix, flattened row-major, are cut
+    into blocks of 256 as one vector, so a block may straddle two matrices.
+    This is the same as double-quantizing each matrix alone whenever every
+    matrix holds a multiple of 256 absmax values (any rows x cols with both
+    multiples of 128). Returns the dequantised matrices (float64, as
+    nf4dq_dequant)."""
+    stacked = np.concatenate([np.asarray(m, np.float64) for m in mats], axis=0)
+    packed, q, scale = nf4dq_quantize(stacked)
+    w = nf4dq_dequant(packed, q, scale)
+    out, r = [], 0
+    for m in mats:
+        out.append(w[r:r + m.shape[0]])
+        r += m.shape[0]
+    return out

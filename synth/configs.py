@@ -34,7 +34,7 @@ class LayerShape:
     inter: int
     rms_eps: float
     rope_theta: float
-    wfmt: str            # "nf4" or "bf16"
+    wfmt: str            # "nf4", "nf4dq" (double-quantized absmax) or "bf16"
     lora_r: int
     lora_alpha: float
 
@@ -89,6 +89,7 @@ class Workload:
 
 
 LLAMA8B_LAYER = LayerShape(4096, 32, 8, 128, 14336, 1e-5, 500000.0, "nf4", 16, 32.0)
+LLAMA8B_LAYER_DQ = LayerShape(4096, 32, 8, 128, 14336, 1e-5, 500000.0, "nf4dq", 16, 32.0)
 QWEN05B_LAYER = LayerShape(896, 14, 2, 64, 4864, 1e-6, 1000000.0, "bf16", 16, 32.0)
 QWEN3B_LAYER = LayerShape(2048, 16, 2, 128, 11008, 1e-6, 1000000.0, "bf16", 16, 32.0)
 
@@ -109,9 +110,13 @@ WORKLOADS = {
     # Llama-3.1-8B-shaped model, NF4 base, bf16 lm_head, 1 x 1024 tokens, AdamW step
     "llama8b_nf4": Workload("llama8b_nf4", 5, "model", layer=LLAMA8B_LAYER,
                             model=ModelShape(LLAMA8B_LAYER, 32, 128256, False, 1, 1024, 1)),
+    # the same model with double-quantized absmax (the layer format of the pages' 4 GB runs)
+    "llama8b_nf4dq": Workload("llama8b_nf4dq", 6, "model", layer=LLAMA8B_LAYER_DQ,
+                              model=ModelShape(LLAMA8B_LAYER_DQ, 32, 128256, False, 1, 1024, 1)),
 }
 
 # small shapes for the oracle's own checks and for quick GPU parity cases
 TINY_LAYER = LayerShape(64, 4, 2, 16, 128, 1e-5, 10000.0, "nf4", 4, 8.0)
 SMALL_LAYER_NF4 = LayerShape(256, 4, 2, 64, 512, 1e-5, 500000.0, "nf4", 16, 32.0)
 SMALL_LAYER_BF16 = LayerShape(192, 3, 1, 64, 320, 1e-6, 1000000.0, "bf16", 8, 16.0)
+SMALL_LAYER_NF4DQ = LayerShape(320, 5, 1, 64, 448, 1e-5, 500000.0, "nf4dq", 8, 16.0)

@@ -67,3 +67,32 @@ def assert_close_chain(got, ref, name=""):
     print(msg)
     assert fro <= RTOL and worst <= 1.0, msg
     return fro
+
+
+def oracle_weight(w, fmt):
+    """The frozen weight as the oracle sees it (float64): NF4 and NF4DQ are
+    quantised and dequantised by the oracle, bf16 is taken as is."""
+    import oracle as O
+    w = np.asarray(w, np.float64)
+    if fmt == "nf4":
+        return O.nf4_dequant(*O.nf4_quantize(w))
+    if fmt == "nf4dq":
+        from oracle.nf4 import nf4dq_quantize, nf4dq_dequant
+        return nf4dq_dequant(*nf4dq_quantize(w))
+    assert fmt == "bf16", fmt
+    return w
+
+
+def oracle_layer_weights(w, shape):
+    """All seven projections of a layer as the oracle sees them. NF4DQ blocks its
+    absmax over each fused matrix (q, k, v stacked; gate, up stacked), as the
+    layer blob stores them."""
+    from synth.configs import PROJ_IN_OUT
+    if shape.wfmt != "nf4dq":
+        return {p: oracle_weight(w[p], shape.wfmt) for p in PROJ_IN_OUT(shape)}
+    from oracle.nf4 import nf4dq_quantize_fused
+    out = {}
+    for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+        for p, d in zip(group, nf4dq_quantize_fused([np.asarray(w[p], np.float64) for p in group])):
+            out[p] = d
+    return out

@@ -94,3 +94,55 @@ def test_workspace_sizes_are_deterministic(L):
     b = L.lora_linear_workspace_bytes(512, 4096, 4096, 16)
     assert a == b and a > 0
     assert L.lora_linear_workspace_bytes(512, 4096, 4096, 12) == 0
+
+
+def test_nf4dq_validation(L):
+    from layer_streamed_lora_amd import _abi
+    lib = L.lib()
+    assert lib.lsl_nf4dq_quantize_absmax(None, -1, None, None, None) == _abi.LSL_ERR_INVALID_ARG
+    assert lib.lsl_nf4dq_quantize_absmax(None, 0, None, None, None) == _abi.LSL_OK
+    assert lib.lsl_nf4dq_quantize_absmax(256, 10, 256, None, None) == _abi.LSL_ERR_INVALID_ARG
+    assert lib.lsl_nf4dq_dequant(256, 256, 256, 4, 96, 256, None) == _abi.LSL_ERR_INVALID_ARG
+    # NF4DQ weight: codes + absmax_q + absmax_scale, float32 absmax and bf16 NULL
+    w = _abi.Weight(_abi.WFMT_NF4DQ, 0, 64, 64, 256, 256, None, 256, 256)
+    assert lib.lora_linear_fwd(256, 8, C.byref(w), 256, 256, 8, 2.0, 256, 256, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
+    w = _abi.Weight(_abi.WFMT_NF4DQ, 0, 64, 64, 256, None, None, 256, None)
+    assert lib.lora_linear_fwd(256, 8, C.byref(w), 256, 256, 8, 2.0, 256, 256, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
+    w = _abi.Weight(_abi.WFMT_NF4DQ, 0, 64, 64, 256, None, None, 256, 256)
+    assert lib.lora_linear_fwd(None, 0, C.byref(w), None, None, 8, 2.0, None, None, None, 0, None) == _abi.LSL_OK
+
+
+@pytest.mark.parametrize("wfmt", ["nf4", "nf4dq", "bf16"])
+def test_layer_layout_regions(L, wfmt):
+    """The packed layer blob: every region 256-byte aligned, disjoint, inside
+    total_bytes, and sized for its format; for Llama-3.1-8B NF4DQ the blob is
+    the oracle's byte count plus alignment padding only (under the pages'
+    113 MB buffer)."""
+    import dataclasses
+    from layer_streamed_lora_amd import model as M
+    from synth.configs import LLAMA8B_LAYER
+    from oracle.nf4 import nf4dq_layer_bytes
+    shape = dataclasses.replace(LLAMA8B_LAYER, wfmt=wfmt)
+    lay = M.layer_layout(M.layer_cfg(shape))
+    H, I, Q, KV = shape.hidden, shape.inter, shape.q_dim, shape.kv_dim
+    mats = [(Q + 2 * KV, H), (H, Q), (2 * I, H), (H, I)]
+    regions = [(lay.norm1_off, 2 * H), (lay.norm2_off, 2 * H)]
+    for i, (n, k) in enumerate(mats):
+        nb = n * k // 64
+        if wfmt == "bf16":
+            regions.append((lay.w_off[i], 2 * n * k))
+            assert lay.absmax_off[i] == 0 and lay.scale_off[i] == 0
+        elif wfmt == "nf4":
+            regions += [(lay.w_off[i], n * k // 2), (lay.absmax_off[i], 4 * nb)]
+            assert lay.scale_off[i] == 0
+        else:
+            regions += [(lay.w_off[i], n * k // 2), (lay.absmax_off[i], nb), (lay.scale_off[i], 4 * ((nb + 255) // 256))]
+    regions.sort()
+    for (o, b), (o2, _) in zip(regions, regions[1:]):
+        assert o % 256 == 0 and o + b <= o2
+    assert regions[-1][0] + regions[-1][1] <= lay.total_bytes
+    payload = sum(b for _, b in regions)
+    assert lay.total_bytes - payload < 256 * len(regions)
+    if wfmt == "nf4dq":
+        assert payload == nf4dq_layer_bytes(H, shape.n_q, shape.n_kv, shape.head_dim, I)
+        assert lay.total_bytes < 113_000_000

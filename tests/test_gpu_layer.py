@@ -6,8 +6,8 @@ import torch
 
 import oracle as O
 import synth
-from synth.configs import SMALL_LAYER_NF4, SMALL_LAYER_BF16, LLAMA8B_LAYER, PROJ_IN_OUT
-from tests.gpu_util import dev_bf16, host, assert_close, assert_close_chain
+from synth.configs import SMALL_LAYER_NF4, SMALL_LAYER_BF16, SMALL_LAYER_NF4DQ, LLAMA8B_LAYER, PROJ_IN_OUT
+from tests.gpu_util import dev_bf16, host, assert_close, assert_close_chain, oracle_layer_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -30,12 +30,7 @@ def _setup(gpu, shape, batch, seq, wid, ones_norm=False):
 
 def _oracle(shape, w, lora, x, dy, batch, seq):
     wd = {}
-    for p in PROJ_IN_OUT(shape):
-        if shape.wfmt == "nf4":
-            c, a = O.nf4_quantize(w[p].astype(np.float64))
-            wd[p] = O.nf4_dequant(c, a)
-        else:
-            wd[p] = w[p].astype(np.float64)
+    wd.update(oracle_layer_weights(w, shape))
     wd["norm1"], wd["norm2"] = w["norm1"].astype(np.float64), w["norm2"].astype(np.float64)
     ld = {k: v.astype(np.float64) for k, v in lora.items()}
     xd, dyd = x.astype(np.float64), dy.astype(np.float64)
@@ -62,6 +57,7 @@ def _run_and_compare(gpu, shape, batch, seq, wid):
 @pytest.mark.parametrize("shape,batch,seq", [
     (SMALL_LAYER_NF4, 2, 40),     # NF4, two sequences, partial tiles everywhere
     (SMALL_LAYER_BF16, 1, 150),   # bf16 base, group of 3, rank 8
+    (SMALL_LAYER_NF4DQ, 1, 72),   # NF4 with double-quantized absmax, short last 256-block
 ])
 def test_layer_parity_small(gpu, shape, batch, seq):
     _run_and_compare(gpu, shape, batch, seq, 41)

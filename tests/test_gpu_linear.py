@@ -7,7 +7,7 @@ import torch
 import oracle as O
 import synth
 from synth.configs import WORKLOADS
-from tests.gpu_util import dev_bf16, dev, host, assert_close
+from tests.gpu_util import dev_bf16, dev, host, assert_close, oracle_weight
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,39 @@ def test_nf4_quantize_large_bitwise(gpu):
     assert np.array_equal(absmax.cpu().numpy(), oa)
 
 
+def test_nf4dq_absmax_quantize_dequant_bitwise(gpu):
+    """Double quantization of the absmax on the GPU gives the oracle's bits: the
+    8-bit codes, the per-256-block constants (a short last block, an all-zero
+    block) and the dequantised weight."""
+    from oracle.nf4 import nf4dq_quantize, nf4dq_dequant
+    w = synth.normal_bf16((320, 448), 0.02, 12, 0, 1)     # 2240 absmax values: 8 full blocks + 192
+    w[:37, :] = 0.0                                       # absmax block 0 all zero -> s = 0, q = 0
+    w[40, 64:128] = 0.0                                   # a zero absmax inside a block
+    codes, absmax = gpu.nf4_quantize(dev_bf16(w))
+    q, scale = gpu.nf4dq_quantize_absmax(absmax)
+    oc, oq, osc = nf4dq_quantize(w.astype(np.float64))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    assert osc[0] == 0 and osc.size == 9
+    deq = gpu.nf4dq_dequant(codes, q, scale)
+    assert np.array_equal(host(deq), nf4dq_dequant(oc, oq, osc))
+
+
+def test_nf4dq_absmax_rounding_ties(gpu):
+    """absmax values that land exactly halfway between two 8-bit codes round to
+    the even code on both sides (float32 division, then round-half-even)."""
+    from oracle.nf4 import nf4dq_quantize_absmax
+    s = np.float32(0.5) / np.float32(255.0)
+    a = (np.arange(256, dtype=np.float32) + np.float32(0.5)) * s
+    a[-1] = np.float32(0.5)                                # the block max -> code 255
+    a = np.concatenate([a, np.float32([0.25, 0.0, 3e-3])]) # a short second block
+    q, sc = gpu.nf4dq_quantize_absmax(dev(a))
+    oq, osc = nf4dq_quantize_absmax(a)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+
+
 def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     x = synth.activation((T, fin), wid, "x")
     dy = synth.activation((T, fout), wid, "dy")
@@ -49,14 +82,15 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (200, 320, 448, 16, "nf4"),       # ragged: several tiles and a partial tile in T and both widths
     (200, 320, 448, 16, "bf16"),
     (1, 64, 64, 8, "nf4"),            # a single token, smallest shapes
+    (200, 320, 448, 16, "nf4dq"),     # double-quantized absmax, short last 256-block
+    (96, 1024, 1600, 8, "nf4dq"),
     (300, 1024, 1152, 16, "bf16"),
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
-    if fmt == "nf4":
-        oc, oa = O.nf4_quantize(w.astype(np.float64))
-        wd = O.nf4_dequant(oc, oa)
-        W = gpu.FrozenWeight.nf4(dev_bf16(w))
+    if fmt in ("nf4", "nf4dq"):
+        wd = oracle_weight(w, fmt)
+        W = getattr(gpu.FrozenWeight, fmt)(dev_bf16(w))
     else:
         wd = w.astype(np.float64)
         W = gpu.FrozenWeight.dense(dev_bf16(w))

@@ -8,13 +8,14 @@ import torch
 
 import oracle as O
 import synth
-from synth.configs import LayerShape, PROJ_IN_OUT, QWEN05B_LAYER, QWEN3B_LAYER, LLAMA8B_LAYER
-from tests.gpu_util import dev_bf16, host, assert_close_chain
+from synth.configs import LayerShape, PROJ_IN_OUT, QWEN05B_LAYER, QWEN3B_LAYER, LLAMA8B_LAYER, LLAMA8B_LAYER_DQ
+from tests.gpu_util import dev_bf16, host, assert_close_chain, oracle_layer_weights
 
 pytestmark = pytest.mark.gpu
 
 SMALL_NF4 = LayerShape(128, 2, 1, 64, 192, 1e-5, 500000.0, "nf4", 8, 16.0)
 SMALL_BF16 = LayerShape(192, 3, 1, 64, 256, 1e-6, 1000000.0, "bf16", 16, 32.0)
+SMALL_NF4DQ = LayerShape(192, 4, 1, 64, 320, 1e-5, 500000.0, "nf4dq", 16, 32.0)
 
 
 def build(shape, n_layers, vocab, tied, batch, seq, mode, wid):
@@ -41,7 +42,7 @@ def ids_for(vocab, batch, seq, n_micro, wid):
     return [synth.token_ids(batch * seq, vocab, wid, salt=i) for i in range(n_micro)]
 
 
-@pytest.mark.parametrize("shape,tied", [(SMALL_NF4, False), (SMALL_BF16, True)])
+@pytest.mark.parametrize("shape,tied", [(SMALL_NF4, False), (SMALL_BF16, True), (SMALL_NF4DQ, False)])
 def test_model_step_matches_oracle(gpu, shape, tied):
     n_layers, vocab, batch, seq, n_micro, wid = 3, 640, 2, 40, 2, 70
     m, weights, loras, (emb, fn, lm) = build(shape, n_layers, vocab, tied, batch, seq, "streamed", wid)
@@ -51,12 +52,7 @@ def test_model_step_matches_oracle(gpu, shape, tied):
     layers = []
     for l in range(n_layers):
         wd = {}
-        for p in PROJ_IN_OUT(shape):
-            if shape.wfmt == "nf4":
-                c, a = O.nf4_quantize(weights[l][p].astype(np.float64))
-                wd[p] = O.nf4_dequant(c, a)
-            else:
-                wd[p] = weights[l][p].astype(np.float64)
+        wd.update(oracle_layer_weights(weights[l], shape))
         wd["norm1"] = weights[l]["norm1"].astype(np.float64)
         wd["norm2"] = weights[l]["norm2"].astype(np.float64)
         layers.append((wd, {k: v.astype(np.float64) for k, v in loras[l].items()}))
@@ -76,7 +72,7 @@ def _assert_same_state(a, b):
         assert torch.equal(getattr(a.lora, name), getattr(b.lora, name)), name
 
 
-@pytest.mark.parametrize("shape", [SMALL_NF4, SMALL_BF16])
+@pytest.mark.parametrize("shape", [SMALL_NF4, SMALL_BF16, SMALL_NF4DQ])
 def test_streamed_equals_resident_small(gpu, shape):
     n_layers, vocab, batch, seq, n_micro = 4, 640, 2, 64, 3
     s, *_ = build(shape, n_layers, vocab, False, batch, seq, "streamed", 71)
@@ -161,3 +157,11 @@ def test_streamed_equals_resident_llama8b_nf4(gpu):
     """Llama-3.1-8B-shaped model, NF4 base (32 layers, 122.7 MB blobs, 3.9 GB
     pinned store), separate bf16 lm_head, vocab 128256, 1 x 1024 tokens."""
     _streamed_vs_resident(LLAMA8B_LAYER, 32, 128256, False, 1, 1024, 1, 5)
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_llama8b_nf4dq(gpu):
+    """Llama-3.1-8B-shaped model with double-quantized absmax (112.5 MB layer
+    blobs, 3.6 GB pinned store), 1 x 1024 tokens: streamed equals resident."""
+    s = _streamed_vs_resident(LLAMA8B_LAYER_DQ, 32, 128256, False, 1, 1024, 1, 6)
+    assert s.blob_bytes < 113_000_000

@@ -13,6 +13,7 @@ import oracle as O
 from oracle.bf16 import round_bf16, identity, bf16_bits, from_bf16_bits
 from oracle.nf4 import nf4_codebook, nf4_quantize, nf4_dequant, nf4_unpack
 from oracle.nf4 import nf4dq_quantize, nf4dq_quantize_absmax, nf4dq_absmax, nf4dq_dequant, nf4dq_layer_bytes
+from oracle.nf4 import nf4dq_quantize_fused
 from synth.configs import TINY_LAYER, PROJ_IN_OUT
 
 RNG = np.random.default_rng(1234)
@@ -232,6 +233,34 @@ def test_nf4dq_dequant_values_and_error():
     gap = np.max(np.diff(cb)) / 2
     tol = absmax.reshape(-1, 1) * gap + np.repeat(s, 256)[:absmax.size].reshape(-1, 1) * 0.5 * 1.0001
     assert np.all(np.abs(deq - w).reshape(-1, 64) <= tol + 1e-12)
+
+
+def test_nf4dq_fused_equals_separate_on_whole_blocks():
+    """Stacked matrices whose absmax counts are multiples of 256 (rows x cols both
+    multiples of 128) double-quantize exactly as each matrix alone."""
+    mats = [round_bf16(RNG.standard_normal((r, 256)) * sd) for r, sd in ((128, 0.02), (64 * 2, 0.5), (128, 0.001))]
+    fused = nf4dq_quantize_fused(mats)
+    for m, f in zip(mats, fused):
+        assert np.array_equal(f, nf4dq_dequant(*nf4dq_quantize(m)))
+
+
+def test_nf4dq_fused_block_straddles_matrices():
+    """With 64 x 320 (320 absmax, not a multiple of 256) on top of a matrix of a
+    much larger scale, the second 256-block holds the tail of the first matrix
+    and the head of the second: its constant is the largest absmax of both
+    parts / 255, so the small matrix's tail loses precision that quantizing it
+    alone keeps."""
+    a = round_bf16(RNG.standard_normal((64, 320)) * 0.001)
+    b = round_bf16(RNG.standard_normal((64, 320)) * 1.0)
+    fa, fb = nf4dq_quantize_fused([a, b])
+    assert np.array_equal(fa[:51], nf4dq_dequant(*nf4dq_quantize(a))[:51])   # rows 0..50 sit in block 0 only
+    _, absmax_b = nf4_quantize(b)
+    _, absmax_a = nf4_quantize(a)
+    s1 = np.float32(max(absmax_a.reshape(-1)[256:].max(), absmax_b.reshape(-1)[:192].max()) / np.float32(255.0))
+    _, q, scale = nf4dq_quantize(np.concatenate([a, b], 0))
+    assert scale[1] == s1
+    # a's tail shares block 1 with b's head: fused and separate differ for a
+    assert not np.array_equal(fa, nf4dq_dequant(*nf4dq_quantize(a)))
 
 
 # ------------------------------------------------------------------ LoRA linear
