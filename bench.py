@@ -22,6 +22,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LoRA train tok/s (streamed fwd+bwd) + % bf16 MFMA peak + achieved H2D GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+# the timed kernel's instantiation: NF4 weight, [N x K] layout, forward LoRA step, bf16 epilogue
+GU_KERNEL = "gemm_kernel<0, false, 1, 0,"
 COUNTERS = os.path.join(ROOT, "profiles", "gemm_gu_fwd_nf4_llama8b_s1024_counters.json")
 
 
@@ -282,11 +284,47 @@ def summarize_trace(d, args):
     trace = _rows(_find(d, "*kernel_trace.csv"))
     g = gu_grid_items(shape, ms)
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
-            if "gemm_kernel" in r["Kernel_Name"] and _grid_items(r) == g]
+            if GU_KERNEL in r["Kernel_Name"] and _grid_items(r) == g]
     out.append("")
     if durs:
         out.append(f"gate|up forward GEMM dispatches (gemm_kernel, {g} work-items): {len(durs)} calls, "
                    f"average {sum(durs) / len(durs):.1f} us, min {min(durs):.1f} us, max {max(durs):.1f} us")
+    print("\n".join(out))
+
+
+def summarize_copies(d, args):
+    """Copy-engine timeline of a `rocprofv3 --kernel-trace --memory-copy-trace`
+    run of `bench.py --no-resident --steps K`: for each of the K timed steps
+    (the layer copies before the final statistics step), copy-engine busy time,
+    the idle gap at the turn of the sweep and at the step boundary, and the
+    kernel time inside each gap."""
+    wl, shape, ms = workload(args.workload)
+    per_step = (2 * ms.n_layers - 4) * ms.n_micro
+    cps = [r for r in _rows(_find(d, "*memory_copy_trace.csv")) if r["Direction"].endswith("HOST_TO_DEVICE")]
+    kts = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in _rows(_find(d, "*kernel_trace.csv")))
+    # layer copies: the pool's copies are the only ones taking over a millisecond
+    big = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in cps
+                 if int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) > 1_000_000)
+    steps = args.steps
+    timed = big[len(big) - (steps + 1) * per_step:len(big) - per_step]
+
+    def kernel_ns(a, b):
+        return sum(max(0, min(e, b) - max(s, a)) for s, e in kts if e > a and s < b)
+    out = ["| step | span ms | copies | copy busy ms | GB/s while copying | largest gaps ms (kernel ms inside) | "
+           "other gaps ms |", "|---|---:|---:|---:|---:|---|---:|"]
+    for k in range(steps):
+        c = timed[k * per_step:(k + 1) * per_step]
+        nxt = timed[(k + 1) * per_step][0] if k + 1 < steps else None
+        busy = sum(e - s for s, e in c) / 1e6
+        gaps = [(c[i + 1][0] - c[i][1], c[i][1], c[i + 1][0]) for i in range(len(c) - 1)]
+        if nxt is not None:
+            gaps.append((nxt - c[-1][1], c[-1][1], nxt))
+        gaps.sort(reverse=True)
+        big2 = ", ".join(f"{g / 1e6:.2f} ({kernel_ns(a, b) / 1e6:.2f})" for g, a, b in gaps[:2])
+        rest = sum(g for g, _, _ in gaps[2:]) / 1e6
+        span = ((nxt if nxt is not None else c[-1][1]) - c[0][0]) / 1e6  # the last step ends at its last copy
+        gbs = len(c) * args.blob_bytes / (busy * 1e-3) / 1e9 if args.blob_bytes else float("nan")
+        out.append(f"| {k} | {span:.2f} | {len(c)} | {busy:.2f} | {gbs:.1f} | {big2} | {rest:.2f} |")
     print("\n".join(out))
 
 
@@ -301,7 +339,7 @@ def summarize_counters(fetch_dir, write_dir, args):
         rows = [r for r in _rows(_find(d, "*counter_collection.csv")) if r["Counter_Name"] == counter]
         copy = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]
                 and _grid_items(r) >= 1 << 20]
-        gemm = [float(r["Counter_Value"]) for r in rows if "gemm_kernel" in r["Kernel_Name"] and _grid_items(r) == g]
+        gemm = [float(r["Counter_Value"]) for r in rows if GU_KERNEL in r["Kernel_Name"] and _grid_items(r) == g]
         if not copy or not gemm:
             sys.exit(f"{counter}: copy dispatches {len(copy)}, gemm dispatches {len(gemm)}")
         kib_copy = sum(copy) / len(copy)
@@ -335,9 +373,14 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc csv runs into the committed counters file and exit")
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the counters file")
+    ap.add_argument("--summarize-copies", metavar="DIR",
+                    help="summarise a rocprofv3 kernel + memory-copy trace of a --no-resident run and exit")
+    ap.add_argument("--blob-bytes", type=int, default=0, help="layer blob size, for --summarize-copies")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args)
+    if args.summarize_copies:
+        return summarize_copies(args.summarize_copies, args)
     if args.summarize_counters:
         return summarize_counters(*args.summarize_counters, args)
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -1,4 +1,4 @@
-// LoRA GEMM family on gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16).
+// LoRA GEMM family on gfx950 bf16 MFMA (v_mfma_f32_32x32x16_bf16).
 //
 //   C[m][n] = sum_k X[m][k] * Wt[n][k]  (+ s * sum_j L[m][j] * Lt[n][j])  (+ residual)
 //
@@ -6,8 +6,9 @@
 // [N x K]: either stored that way (forward, y = x W^T: layout NK) or stored
 // [K x N] (input gradient, dx = dy W: layout KN). It is bf16 or NF4; NF4 codes
 // are dequantised while the tile is staged into LDS, w = bf16(code * absmax)
-// (QLoRA NormalFloat with blockwise absmax, block 64), so the dense bf16 weight
-// never exists in HBM. The LoRA term is one extra short K-step on the same
+// (QLoRA NormalFloat with blockwise absmax, block 64; the absmax itself is
+// float32, or 8-bit codes times a float32 constant per 256 blocks), so the
+// dense bf16 weight never exists in HBM. The LoRA term is one extra short K-step on the same
 // tiles: forward L = t = x A^T, Lt = B masked per fused projection; backward
 // L = u = dy B, Lt = A^T. Accumulation is float32 in MFMA registers; the output
 // is rounded to bf16 once (plus once more after a fused residual add).
@@ -15,7 +16,9 @@
 // Tiling: BN (weight rows) x BM (tokens) per workgroup of 4 waves; a wave owns
 // 64 weight rows x BM/(4*64/BN) tokens, K-step 64; the next tile's global loads
 // are issued into registers before the current tile's MFMAs and stored to LDS
-// after them. The MFMA A operand is the weight tile
+// after them. The token tile is stored unpadded with a chunk swizzle, so its
+// stores and the MFMA operand reads are free of bank conflicts. GEMMs with few
+// output tiles split the reduction (float32 partials added in split order). The MFMA A operand is the weight tile
 // and the B operand the token tile, so each lane's four accumulators are four
 // consecutive n of one output row m and the epilogue writes 8-byte chunks.
 // Loader addresses are set up once; a K-step only adds a uniform offset.
