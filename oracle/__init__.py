@@ -25,14 +25,15 @@ Sources (the pages are cited by title and section):
 
 Parity status: every function here is pinned by tests against closed forms,
 library routines (torch CPU float64 ops, scipy), brute force or finite
-differences; none is "parity unpinned". The pages themselves print no worked
-example, so no value here is pinned to a number printed on the pages.
+differences; none is "parity unpinned". The pages print no worked example of
+the arithmetic; the one set of printed numbers that fixes a step is the byte
+count of the double-quantized NF4 store (tests/golden/pages_store_sizes.json).
 """
 from .bf16 import round_bf16, identity, bf16_bits, from_bf16_bits  # noqa: F401
 from .nf4 import nf4_codebook, nf4_quantize, nf4_dequant  # noqa: F401
 from .lora import lora_linear_fwd, lora_linear_bwd  # noqa: F401
 from .layer import (  # noqa: F401
-    rmsnorm_fwd, rmsnorm_bwd, rope_apply, attention_fwd, attention_bwd,
+    rmsnorm_fwd, rmsnorm_bwd, rope_apply, rope_inv_freq, attention_fwd, attention_bwd,
     swiglu_fwd, swiglu_bwd, decoder_layer_fwd, decoder_layer_bwd,
 )
 from .ce import ce_loss_fwd, ce_loss_bwd  # noqa: F401

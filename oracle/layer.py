@@ -13,8 +13,17 @@ Works"); the layer itself is the published architecture of those bases:
     query i iff j <= i within the same sequence;
   * SwiGLU MLP (Shazeer 2020): down(silu(gate(x)) * up(x)).
   * h' = x + o(attn(...)); out = h' + down(...).
-Readings: no q/k/v bias; no RoPE frequency rescaling; the backward recomputes
-the forward from the layer input (nothing but the layer input is kept).
+Model-fidelity options (off unless the shape asks for them):
+  * q/k/v bias (Qwen2 bases): frozen bf16 vectors added to those three
+    projections before their single rounding; no gradient;
+  * Llama-3.1 RoPE frequency scaling (the rope_type "llama3" configuration
+    published with Llama-3.1: factor, low/high frequency factors and the
+    original context length): inverse frequencies whose wavelength 2 pi / f is
+    shorter than original / high_factor stay; those longer than
+    original / low_factor are divided by factor; in between the two are blended
+    linearly in original / wavelength.
+Reading: the backward recomputes the forward from the layer input (nothing but
+the layer input is kept).
 
 bf16 mode rounds (with rnd) every tensor the GPU path stores in bfloat16; all
 arithmetic is float64.
@@ -40,16 +49,36 @@ def rmsnorm_bwd(x, w, eps, dy):
 
 
 # ---------------------------------------------------------------- RoPE
-def rope_angles(positions, head_dim, theta):
+def rope_inv_freq(head_dim, theta, scaling=None):
+    """Inverse frequencies theta^(-2i/d), i < d/2; scaling = (factor,
+    low_freq_factor, high_freq_factor, original_max_position) or None."""
     i = np.arange(head_dim // 2, dtype=np.float64)
     inv = theta ** (-2.0 * i / head_dim)
+    if scaling is None:
+        return inv
+    factor, low, high, orig = (float(v) for v in scaling)
+    out = np.empty_like(inv)
+    for j, f in enumerate(inv):
+        wavelen = 2.0 * np.pi / f
+        if wavelen < orig / high:          # high frequencies: unchanged
+            out[j] = f
+        elif wavelen > orig / low:         # low frequencies: slowed by factor
+            out[j] = f / factor
+        else:                              # the band between: linear blend in orig / wavelen
+            mix = (orig / wavelen - low) / (high - low)
+            out[j] = (1.0 - mix) * f / factor + mix * f
+    return out
+
+
+def rope_angles(positions, head_dim, theta, scaling=None):
+    inv = rope_inv_freq(head_dim, theta, scaling)
     return np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
 
 
-def rope_apply(x, positions, theta, inverse=False, rnd=round_bf16):
+def rope_apply(x, positions, theta, inverse=False, rnd=round_bf16, scaling=None):
     """x [T x heads x d]; rotate pairs (x[i], x[i + d/2]) by +angle (or -angle)."""
     d = x.shape[-1]
-    ang = rope_angles(positions, d, theta)[:, None, :]
+    ang = rope_angles(positions, d, theta, scaling)[:, None, :]
     c, s = np.cos(ang), np.sin(ang)
     if inverse:
         s = -s
@@ -142,10 +171,12 @@ def decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=round_bf16):
     pos = positions_of(batch, seq)
     c = {"x": x}
     c["n1"] = n1 = rmsnorm_fwd(x, w["norm1"], shape.rms_eps, rnd)
+    sc = getattr(shape, "rope_scaling", None)
     for p in ("q", "k", "v"):
-        c[p], c["t_" + p] = lora_linear_fwd(n1, w[p], lora["A_" + p], lora["B_" + p], s, rnd)
-    c["qr"] = rope_apply(c["q"].reshape(T, nq, d), pos, shape.rope_theta, rnd=rnd)
-    c["kr"] = rope_apply(c["k"].reshape(T, nkv, d), pos, shape.rope_theta, rnd=rnd)
+        c[p], c["t_" + p] = lora_linear_fwd(n1, w[p], lora["A_" + p], lora["B_" + p], s, rnd,
+                                            bias=w.get(p + "_bias"))
+    c["qr"] = rope_apply(c["q"].reshape(T, nq, d), pos, shape.rope_theta, rnd=rnd, scaling=sc)
+    c["kr"] = rope_apply(c["k"].reshape(T, nkv, d), pos, shape.rope_theta, rnd=rnd, scaling=sc)
     vv = c["v"].reshape(T, nkv, d)
     o, c["lse"] = attention_fwd(c["qr"], c["kr"], vv, batch, seq, rnd)
     c["attn"] = o = o.reshape(T, nq * d)
@@ -185,8 +216,9 @@ def decoder_layer_bwd(x, dout, w, lora, shape, batch, seq, rnd=round_bf16):
         c["attn"], c["t_o"], dh1, w["o"], lora["A_o"], lora["B_o"], s, rnd)
     dqr, dkr, dv = attention_bwd(c["qr"], c["kr"], c["v"].reshape(T, nkv, d),
                                  dattn.reshape(T, nq, d), batch, seq, rnd)
-    dq = rope_apply(dqr, pos, shape.rope_theta, inverse=True, rnd=rnd).reshape(T, nq * d)
-    dk = rope_apply(dkr, pos, shape.rope_theta, inverse=True, rnd=rnd).reshape(T, nkv * d)
+    sc = getattr(shape, "rope_scaling", None)
+    dq = rope_apply(dqr, pos, shape.rope_theta, inverse=True, rnd=rnd, scaling=sc).reshape(T, nq * d)
+    dk = rope_apply(dkr, pos, shape.rope_theta, inverse=True, rnd=rnd, scaling=sc).reshape(T, nkv * d)
     dv = dv.reshape(T, nkv * d)
     dn1 = 0.0
     for p, dp in (("q", dq), ("k", dk), ("v", dv)):

@@ -13,11 +13,15 @@ import numpy as np
 from .bf16 import round_bf16
 
 
-def lora_linear_fwd(x, w, a, b, scale, rnd=round_bf16):
-    """Returns (y, t). x [T x in], w [out x in], a [r x in], b [out x r]."""
+def lora_linear_fwd(x, w, a, b, scale, rnd=round_bf16, bias=None):
+    """Returns (y, t). x [T x in], w [out x in], a [r x in], b [out x r].
+    bias [out] (optional, frozen like W: the q/k/v projections of Qwen2 bases)
+    joins the sum before the single rounding of y."""
     t = rnd(x @ a.T)
-    y = rnd(x @ w.T + scale * (t @ b.T))
-    return y, t
+    y = x @ w.T + scale * (t @ b.T)
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return rnd(y), t
 
 
 def lora_linear_bwd(x, t, dy, w, a, b, scale, rnd=round_bf16, round_dx=True):

@@ -21,6 +21,8 @@ TENSOR_IDS = {
     "x": 40, "dy": 41, "tokens": 42,
     # model head (used with layer_id = HEAD_LAYER_ID)
     "embed": 50, "final_norm": 51, "lm_head": 52,
+    # q/k/v bias (Qwen2 bases)
+    "q_bias": 60, "k_bias": 61, "v_bias": 62,
 }
 HEAD_LAYER_ID = 1000
 
@@ -37,6 +39,8 @@ class LayerShape:
     wfmt: str            # "nf4", "nf4dq" (double-quantized absmax) or "bf16"
     lora_r: int
     lora_alpha: float
+    qkv_bias: bool = False          # Qwen2: frozen bias on q, k, v
+    rope_scaling: tuple = None      # Llama-3.1: (factor, low_freq_factor, high_freq_factor, original_max_position)
 
     @property
     def lora_scale(self) -> float:
@@ -114,6 +118,9 @@ WORKLOADS = {
     "llama8b_nf4dq": Workload("llama8b_nf4dq", 6, "model", layer=LLAMA8B_LAYER_DQ,
                               model=ModelShape(LLAMA8B_LAYER_DQ, 32, 128256, False, 1, 1024, 1)),
 }
+
+# the published Llama-3.1 RoPE frequency scaling (rope_type "llama3")
+LLAMA31_ROPE_SCALING = (8.0, 1.0, 4.0, 8192.0)
 
 # small shapes for the oracle's own checks and for quick GPU parity cases
 TINY_LAYER = LayerShape(64, 4, 2, 16, 128, 1e-5, 10000.0, "nf4", 4, 8.0)

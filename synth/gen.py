@@ -54,13 +54,17 @@ def activation(shape, wid, name, salt=0, std=1.0):
     return normal_bf16(shape, std, wid, 0, TENSOR_IDS[name], salt)
 
 
-def layer_weights(shape: LayerShape, wid: int, layer_id: int, w_std=0.02, ones_norm=False):
-    """Frozen base weights of one decoder layer, unquantised bf16 values [out x in]."""
+def layer_weights(shape: LayerShape, wid: int, layer_id: int, w_std=0.02, ones_norm=False, bias_std=0.1):
+    """Frozen base weights of one decoder layer, unquantised bf16 values [out x in]
+    (plus 'q_bias', 'k_bias', 'v_bias' ~ N(0, bias_std) when the shape has them)."""
     out = {}
     for p, (fin, fout) in PROJ_IN_OUT(shape).items():
         out[p] = normal_bf16((fout, fin), w_std, wid, layer_id, TENSOR_IDS[p])
     out["norm1"] = norm_weight_bf16(shape.hidden, wid, layer_id, TENSOR_IDS["norm1"], ones_norm)
     out["norm2"] = norm_weight_bf16(shape.hidden, wid, layer_id, TENSOR_IDS["norm2"], ones_norm)
+    if getattr(shape, "qkv_bias", False):
+        for p, n in (("q", shape.q_dim), ("k", shape.kv_dim), ("v", shape.kv_dim)):
+            out[p + "_bias"] = normal_bf16((n,), bias_std, wid, layer_id, TENSOR_IDS[p + "_bias"])
     return out
 
 

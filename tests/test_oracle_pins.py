@@ -348,6 +348,37 @@ def test_rope_relative_position():
     assert np.allclose(dots, dots[0], rtol=1e-10)
 
 
+def test_rope_llama3_scaling_shape():
+    """Llama-3.1 frequency scaling, checked by the properties that fix it: the
+    ratio r = scaled / unscaled frequency is 1 where the wavelength is shorter
+    than original / high_factor, 1 / factor where it is longer than
+    original / low_factor, affine in x = original / wavelength in between, and
+    continuous at both ends of that band."""
+    factor, low, high, orig = 8.0, 1.0, 4.0, 8192.0
+    d, theta = 4096, 500000.0                      # 2048 frequencies spread over the three regimes
+    inv = O.rope_inv_freq(d, theta)
+    r = O.rope_inv_freq(d, theta, (factor, low, high, orig)) / inv
+    x = orig * inv / (2 * np.pi)                   # original / wavelength
+    hi_f, lo_f, band = x > high, x < low, (x >= low) & (x <= high)
+    assert hi_f.sum() > 10 and lo_f.sum() > 10 and band.sum() > 10
+    assert np.all(r[hi_f] == 1.0)
+    assert np.allclose(r[lo_f], 1.0 / factor, rtol=1e-15)
+    xb, rb = x[band], r[band]
+    slope = np.diff(rb) / np.diff(xb)
+    assert np.allclose(slope, slope[0], rtol=1e-9)                       # affine in x
+    assert np.isclose(rb[np.argmin(xb)] + slope[0] * (low - xb.min()), 1.0 / factor, rtol=1e-9)   # meets 1/factor at x = low
+    assert np.isclose(rb[np.argmax(xb)] + slope[0] * (high - xb.max()), 1.0, rtol=1e-9)         # meets 1 at x = high
+    assert np.all(np.diff(r * inv) < 0)            # frequencies stay strictly ordered
+    # factor 1 changes nothing; the scaled rotation is still a rotation
+    assert np.allclose(O.rope_inv_freq(128, theta, (1.0, low, high, orig)), O.rope_inv_freq(128, theta),
+                       rtol=1e-15, atol=0)
+    xx = RNG.standard_normal((5, 2, 128))
+    y = O.rope_apply(xx, [0, 9000, 3, 40000, 7], theta, rnd=identity, scaling=(factor, low, high, orig))
+    assert np.allclose(np.sum(y * y, -1), np.sum(xx * xx, -1), rtol=1e-12)
+    back = O.rope_apply(y, [0, 9000, 3, 40000, 7], theta, inverse=True, rnd=identity, scaling=(factor, low, high, orig))
+    assert np.allclose(back, xx, atol=1e-12)
+
+
 # ------------------------------------------------------------------ attention
 def _sdpa_ref(q, k, v, batch, seq):
     T, nq, d = q.shape
@@ -414,13 +445,15 @@ def tiny_layer_params(shape=TINY_LAYER, seed=3):
 
 
 def _torch_layer(x, w, lora, shape, batch, seq):
-    """Independent composition from torch library ops (merged LoRA weights, SDPA)."""
+    """Independent composition from torch library ops (merged LoRA weights, SDPA,
+    F.linear's own bias)."""
     s = shape.lora_scale
     W = {p: t64(w[p]) + s * (t64(lora["B_" + p]) @ t64(lora["A_" + p])) for p in PROJ_IN_OUT(shape)}
     xt = t64(x)
     n1 = F.rms_norm(xt, (shape.hidden,), t64(w["norm1"]), eps=shape.rms_eps)
     T, d = x.shape[0], shape.head_dim
-    q, k, v = (F.linear(n1, W[p]).numpy() for p in ("q", "k", "v"))
+    q, k, v = (F.linear(n1, W[p], t64(w[p + "_bias"]) if p + "_bias" in w else None).numpy()
+               for p in ("q", "k", "v"))
     pos = np.tile(np.arange(seq), batch)
 
     def rot(a, nh):
@@ -442,6 +475,50 @@ def test_decoder_layer_fwd_matches_torch_composition():
     x = RNG.standard_normal((batch * seq, shape.hidden))
     out, _ = O.decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=identity)
     assert np.allclose(out, _torch_layer(x, w, lora, shape, batch, seq), atol=1e-11)
+
+
+def test_decoder_layer_qkv_bias_matches_torch_and_shifts_v():
+    """q/k/v bias: the layer equals torch's composition with F.linear's bias, and
+    a v bias alone moves the attention output by exactly that bias (softmax rows
+    sum to one)."""
+    import dataclasses
+    shape, batch, seq = dataclasses.replace(TINY_LAYER, qkv_bias=True), 2, 8
+    w, lora = tiny_layer_params()
+    rng = np.random.default_rng(5)
+    for p, n in (("q", shape.q_dim), ("k", shape.kv_dim), ("v", shape.kv_dim)):
+        w[p + "_bias"] = rng.standard_normal(n) * 0.5
+    x = RNG.standard_normal((batch * seq, shape.hidden))
+    out, c = O.decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=identity)
+    assert np.allclose(out, _torch_layer(x, w, lora, shape, batch, seq), atol=1e-11)
+    w0 = dict(w); w0["v_bias"] = np.zeros(shape.kv_dim)
+    _, c0 = O.decoder_layer_fwd(x, w0, lora, shape, batch, seq, rnd=identity)
+    grp = shape.n_q // shape.n_kv
+    shift = np.repeat(w["v_bias"].reshape(shape.n_kv, shape.head_dim), grp, axis=0).reshape(-1)
+    assert np.allclose(c["attn"] - c0["attn"], shift[None, :], atol=1e-12)
+
+
+def test_decoder_layer_bwd_finite_differences_with_bias_and_scaling():
+    """The backward stays the gradient of the forward with q/k/v bias and
+    Llama-3.1 RoPE scaling switched on (positions past the original context)."""
+    import dataclasses
+    shape = dataclasses.replace(TINY_LAYER, qkv_bias=True, rope_scaling=(8.0, 1.0, 4.0, 64.0))
+    batch, seq = 1, 8
+    w, lora = tiny_layer_params()
+    rng = np.random.default_rng(13)
+    for p, n in (("q", shape.q_dim), ("k", shape.kv_dim), ("v", shape.kv_dim)):
+        w[p + "_bias"] = rng.standard_normal(n) * 0.5
+    x = rng.standard_normal((batch * seq, shape.hidden))
+    dout = rng.standard_normal((batch * seq, shape.hidden))
+    dx, gr = O.decoder_layer_bwd(x, dout, w, lora, shape, batch, seq, rnd=identity)
+
+    def L(xx=x, ll=lora):
+        return float(np.sum(dout * O.decoder_layer_fwd(xx, w, ll, shape, batch, seq, rnd=identity)[0]))
+    assert_fd(dx, lambda v: L(xx=v), x, n=8, rtol=1e-5, atol=1e-8)
+    for key in ("A_q", "B_k", "B_v"):
+        def Lk(v, key=key):
+            ll = dict(lora); ll[key] = v
+            return L(ll=ll)
+        assert_fd(gr[key], Lk, lora[key], n=4, rtol=1e-5, atol=1e-8)
 
 
 def test_decoder_layer_bwd_finite_differences():
