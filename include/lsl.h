@@ -109,7 +109,10 @@ lsl_status lsl_nf4dq_dequant(const uint8_t* codes, const uint8_t* q, const float
 enum { LSL_WFMT_NF4 = 0, LSL_WFMT_BF16 = 1, LSL_WFMT_NF4DQ = 2 };
 /* A frozen weight [n_out x k_in] (n_out and k_in multiples of 64): NF4 (nf4
  * codes + absmax), bf16, or NF4 with double-quantized absmax (nf4 codes +
- * absmax_q + absmax_scale). Pointers not used by the format must be NULL. */
+ * absmax_q + absmax_scale). Pointers not used by the format must be NULL.
+ * bias (optional, NULL for none): a frozen bf16 vector [n_out] added to the
+ * forward output before its rounding, as in the q/k/v projections of Qwen2
+ * bases; it has no gradient and does not enter the backward. */
 typedef struct {
   int32_t fmt;
   int32_t pad;
@@ -120,14 +123,15 @@ typedef struct {
   const uint16_t* bf16;
   const uint8_t* absmax_q;
   const float* absmax_scale;
+  const uint16_t* bias;
 } lsl_weight;
 
 /* ------------------------------------------------------------------ LoRA linear
  * y = x W^T + s (x A^T) B^T with frozen W and trainable A [r x k_in],
  * B [n_out x r] (LoRA, Hu et al. 2021; the pages train such adapters on the
  * frozen base: "Exact Layer Streaming ...", abstract).
- * Rounding: t = bf16(x A^T); y = bf16(x W^T + s t B^T) (float32 accumulation,
- * one rounding). r is a multiple of 8 in [8, 64]; T >= 0 is any token count.
+ * Rounding: t = bf16(x A^T); y = bf16(x W^T + s t B^T (+ bias)) (float32
+ * accumulation, one rounding). r is a multiple of 8 in [8, 64]; T >= 0 is any token count.
  */
 size_t lsl_lora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in, int32_t r);
 /* x [T x k_in], y [T x n_out], t_out [T x r] (kept for the backward). */
@@ -147,17 +151,33 @@ lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, const uint16_t*
  * Pre-norm Llama/Qwen2 decoder layer: h = x + o(attn(rope(q(n1)), rope(k(n1)), v(n1))),
  * out = h + down(silu(gate(n2)) * up(n2)), n1 = rmsnorm(x), n2 = rmsnorm(h);
  * GQA causal attention (query head j reads kv head j / (n_q / n_kv)), scale
- * 1/sqrt(head_dim); rotate-half RoPE with angle pos * theta^(-2i/d), positions
- * restarting at 0 in each sequence; LoRA on all seven projections.
+ * 1/sqrt(head_dim); rotate-half RoPE with angle pos * theta^(-2i/d) (frequencies
+ * optionally rescaled, rope_scaling), positions restarting at 0 in each sequence;
+ * optional frozen q/k/v bias; LoRA on all seven projections.
  * The pages stream exactly these "decoder layers" ("Soup CLI ...", section "How
  * Layer Streaming Works").
  */
+/* RoPE frequency scaling of Llama-3.1 checkpoints (their published rope_type
+ * "llama3" configuration: 8, 1, 4, 8192). With f = theta^(-2i/d) and
+ * wavelength 2 pi / f: f stays if the wavelength is below
+ * original_max_position / high_freq_factor, becomes f / factor above
+ * original_max_position / low_freq_factor, and in between
+ * (1 - m) f / factor + m f with m = (original_max_position / wavelength -
+ * low_freq_factor) / (high_freq_factor - low_freq_factor). factor == 0 means
+ * no scaling; otherwise factor >= 1, 0 < low_freq_factor < high_freq_factor and
+ * original_max_position > 0 are required. Computed in float64. */
+typedef struct {
+  float factor, low_freq_factor, high_freq_factor, original_max_position;
+} lsl_rope_scaling;
+
 typedef struct {
   int32_t hidden, n_q, n_kv, head_dim, inter;
   float rms_eps, rope_theta;
   int32_t wfmt;      /* LSL_WFMT_NF4, LSL_WFMT_BF16 or LSL_WFMT_NF4DQ */
   int32_t lora_r;
   float lora_scale;  /* alpha / r */
+  int32_t qkv_bias;  /* 1: the blob holds a bf16 q|k|v bias [(n_q + 2 n_kv) d] (Qwen2 bases) */
+  lsl_rope_scaling rope_scaling;  /* factor 0: none */
 } lsl_layer_cfg;
 
 /* Byte offsets inside one packed layer blob (every offset 256-byte aligned).
@@ -166,7 +186,8 @@ typedef struct {
  * For NF4 each matrix is codes at w_off[i] and float32 absmax at absmax_off[i];
  * for NF4DQ codes at w_off[i], uint8 absmax codes at absmax_off[i] and float32
  * block constants at scale_off[i]; for bf16 the matrix is at w_off[i] and
- * absmax_off[i] (and scale_off[i]) are 0.
+ * absmax_off[i] (and scale_off[i]) are 0. With qkv_bias the bf16 bias of the
+ * stacked q|k|v rows is at bias_off (else bias_off is 0).
  * norm1/norm2 are bf16 [hidden]. The pinned host store and a resident copy use
  * this same layout, so a slot holds a byte-identical copy of one layer. */
 enum { LSL_M_QKV = 0, LSL_M_O = 1, LSL_M_GU = 2, LSL_M_DOWN = 3 };
@@ -176,6 +197,7 @@ typedef struct {
   uint64_t absmax_off[4];
   uint64_t total_bytes;
   uint64_t scale_off[4];
+  uint64_t bias_off;
 } lsl_layer_layout;
 lsl_status lsl_layer_layout_get(const lsl_layer_cfg* cfg, lsl_layer_layout* out);
 
@@ -279,9 +301,10 @@ lsl_status lsl_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t*
                            lsl_stream stream);
 /* In-place rotate-half RoPE on x [T rows, row stride ld elements], heads
  * [n_heads x head_dim] starting at column 0 of each row; position = row % seq.
- * inverse != 0 rotates by -angle (the backward). */
+ * inverse != 0 rotates by -angle (the backward). scaling may be NULL (none). */
 lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_heads, int32_t head_dim,
-                    int32_t seq, float theta, int32_t inverse, lsl_stream stream);
+                    int32_t seq, float theta, const lsl_rope_scaling* scaling, int32_t inverse,
+                    lsl_stream stream);
 /* Causal GQA attention. q [T x ldq] (n_q heads of d), k, v [T x ldk] (n_kv heads),
  * o [T x ldo]; lse float [batch x n_q x seq]. T = batch * seq. head_dim 64 or 128,
  * at most 8 query heads per kv head. o32 (may be NULL) receives the unrounded

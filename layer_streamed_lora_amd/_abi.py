@@ -17,18 +17,25 @@ i32, i64, f32, sz = C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
 class Weight(C.Structure):
     _fields_ = [("fmt", i32), ("pad", i32), ("n_out", i64), ("k_in", i64),
-                ("nf4", vp), ("absmax", vp), ("bf16", vp), ("absmax_q", vp), ("absmax_scale", vp)]
+                ("nf4", vp), ("absmax", vp), ("bf16", vp), ("absmax_q", vp), ("absmax_scale", vp),
+                ("bias", vp)]
+
+
+class RopeScaling(C.Structure):
+    _fields_ = [("factor", f32), ("low_freq_factor", f32), ("high_freq_factor", f32),
+                ("original_max_position", f32)]
 
 
 class LayerCfg(C.Structure):
     _fields_ = [("hidden", i32), ("n_q", i32), ("n_kv", i32), ("head_dim", i32), ("inter", i32),
-                ("rms_eps", f32), ("rope_theta", f32), ("wfmt", i32), ("lora_r", i32), ("lora_scale", f32)]
+                ("rms_eps", f32), ("rope_theta", f32), ("wfmt", i32), ("lora_r", i32), ("lora_scale", f32),
+                ("qkv_bias", i32), ("rope_scaling", RopeScaling)]
 
 
 class LayerLayout(C.Structure):
     _fields_ = [("norm1_off", C.c_uint64), ("norm2_off", C.c_uint64), ("w_off", C.c_uint64 * 4),
                 ("absmax_off", C.c_uint64 * 4), ("total_bytes", C.c_uint64),
-                ("scale_off", C.c_uint64 * 4)]
+                ("scale_off", C.c_uint64 * 4), ("bias_off", C.c_uint64)]
 
 
 class LoraSet(C.Structure):
@@ -77,7 +84,7 @@ PROTOS = {
     "fused_ce_loss_bwd": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp, sz, vp]),
     "lsl_rmsnorm_fwd": (i32, [vp, vp, i64, i64, f32, vp, vp]),
     "lsl_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, f32, vp, vp]),
-    "lsl_rope": (i32, [vp, i64, i64, i32, i32, i32, f32, i32, vp]),
+    "lsl_rope": (i32, [vp, i64, i64, i32, i32, i32, f32, C.POINTER(RopeScaling), i32, vp]),
     "lsl_attention_fwd": (i32, [vp, vp, vp, i64, i64, i32, i32, i32, i32, i32, vp, i64, vp, vp, vp]),
     "lsl_attention_workspace_bytes": (sz, [i32, i32, i32, i32, i32]),
     "lsl_attention_bwd": (i32, [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),

@@ -78,7 +78,8 @@ static lsl_status check_cfg(const lsl_layer_cfg* c, const char* fn) {
   if (c->wfmt != LSL_WFMT_NF4 && c->wfmt != LSL_WFMT_BF16 && c->wfmt != LSL_WFMT_NF4DQ)
     return set_error(LSL_ERR_INVALID_ARG, "%s: unknown weight format %d", fn, c->wfmt);
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return set_error(LSL_ERR_INVALID_ARG, "%s: bad eps/theta", fn);
-  return LSL_OK;
+  if (c->qkv_bias != 0 && c->qkv_bias != 1) return set_error(LSL_ERR_INVALID_ARG, "%s: qkv_bias must be 0 or 1", fn);
+  return check_rope_scaling(fn, &c->rope_scaling);
 }
 
 // Matrix shapes [n_out x k_in] of the four fused GEMMs.
@@ -97,6 +98,7 @@ static void layout_of(const lsl_layer_cfg* c, lsl_layer_layout* L) {
   auto take = [&](uint64_t bytes) { uint64_t o = off; off = align256(off + bytes); return o; };
   L->norm1_off = take(2 * d.H);
   L->norm2_off = take(2 * d.H);
+  L->bias_off = c->qkv_bias ? take(2 * d.NQKV) : 0;
   for (int i = 0; i < 4; ++i) {
     int64_t n, k;
     mat_shape(d, i, n, k);
@@ -175,6 +177,7 @@ struct LayerPtrs {
   const uint16_t* norm1; const uint16_t* norm2;
   const uint16_t* wb[4]; const uint8_t* wq[4]; const float* wa[4];
   const uint8_t* wq8[4]; const float* wsc[4];  // NF4DQ absmax codes and block constants
+  const uint16_t* qkv_bias;                     // bf16 [NQKV] or NULL
 };
 
 static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
@@ -184,6 +187,7 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
   LayerPtrs p{};
   p.norm1 = (const uint16_t*)(b + L.norm1_off);
   p.norm2 = (const uint16_t*)(b + L.norm2_off);
+  p.qkv_bias = c->qkv_bias ? (const uint16_t*)(b + L.bias_off) : nullptr;
   for (int i = 0; i < 4; ++i) {
     if (c->wfmt == LSL_WFMT_NF4) {
       p.wq[i] = (const uint8_t*)(b + L.w_off[i]);
@@ -224,6 +228,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   else g.seg_end[0] = n;
   g.scale = c->lora_scale;
   g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part;
+  if (i == LSL_M_QKV) g.bias = W.qkv_bias;
   timing_mark(1 + i, true, s);
   lsl_status st = gemm_launch(g, s);
   timing_mark(1 + i, false, s);
@@ -284,8 +289,8 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   uint16_t* a = (uint16_t*)(ws + p.a);
   LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s));
   LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s));
-  LSL_TRY(rope_launch(qkv, d.T, d.NQKV, c->n_q, d.d, seq, c->rope_theta, 0, s));
-  LSL_TRY(rope_launch(qkv + d.Q, d.T, d.NQKV, c->n_kv, d.d, seq, c->rope_theta, 0, s));
+  LSL_TRY(rope_launch(qkv, d.T, d.NQKV, c->n_q, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
+  LSL_TRY(rope_launch(qkv + d.Q, d.T, d.NQKV, c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(lsl_attention_fwd(qkv, qkv + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
   LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s));
@@ -380,8 +385,8 @@ extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* la
                             (const float*)(w + p.o32), d.NQKV,
                             d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d, dqkv, dqkv + d.Q, dqkv + d.Q + d.KV,
                             w + p.attn_ws, p.o32 - p.attn_ws, s));
-  LSL_TRY(rope_launch(dqkv, d.T, d.NQKV, cfg->n_q, d.d, seq, cfg->rope_theta, 1, s));
-  LSL_TRY(rope_launch(dqkv + d.Q, d.T, d.NQKV, cfg->n_kv, d.d, seq, cfg->rope_theta, 1, s));
+  LSL_TRY(rope_launch(dqkv, d.T, d.NQKV, cfg->n_q, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
+  LSL_TRY(rope_launch(dqkv + d.Q, d.T, d.NQKV, cfg->n_kv, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
                            (uint16_t*)(w + p.uqkv), dn1, part, s));
   if (dx) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));

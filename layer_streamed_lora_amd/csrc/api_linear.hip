@@ -46,6 +46,7 @@ static lsl_status check_weight(const lsl_weight* W, const char* fn) {
   } else {
     return set_error(LSL_ERR_INVALID_ARG, "%s: unknown weight format %d", fn, W->fmt);
   }
+  if (W->bias && !aligned(W->bias, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: bias not 16-byte aligned", fn);
   return LSL_OK;
 }
 
@@ -82,7 +83,7 @@ extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_we
   g.x = x; g.ldx = W->k_in; weight_into(g, W); g.kn = false;
   g.M = T; g.N = W->n_out; g.K = W->k_in;
   g.lora = 1; g.la = t_out; g.ldla = r; g.kl = r; g.lb = B; g.r = r; g.nseg = 1; g.seg_end[0] = W->n_out;
-  g.scale = scale; g.y = y; g.ldy = W->n_out; g.split_ws = (float*)ws;
+  g.scale = scale; g.y = y; g.ldy = W->n_out; g.split_ws = (float*)ws; g.bias = W->bias;
   return gemm_launch(g, s);
 }
 
@@ -146,14 +147,15 @@ extern "C" lsl_status lsl_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, cons
 }
 
 extern "C" lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_heads, int32_t head_dim, int32_t seq,
-                               float theta, int32_t inverse, lsl_stream stream) {
+                               float theta, const lsl_rope_scaling* scaling, int32_t inverse, lsl_stream stream) {
   const char* fn = "lsl_rope";
   if (T < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 || seq <= 0 || ld < (int64_t)n_heads * head_dim ||
       !(theta > 0.f))
     return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  LSL_TRY(check_rope_scaling(fn, scaling));
   if (T == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x}));
-  return rope_launch(x, T, ld, n_heads, head_dim, seq, theta, inverse, (hipStream_t)stream);
+  return rope_launch(x, T, ld, n_heads, head_dim, seq, theta, scaling, inverse, (hipStream_t)stream);
 }
 
 extern "C" lsl_status lsl_swiglu_fwd(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, lsl_stream stream) {

@@ -23,4 +23,12 @@ inline lsl_status check_ptrs(const char* fn, std::initializer_list<const void*> 
   return LSL_OK;
 }
 bool lora_rank_ok(int32_t r);
+// NULL or factor 0: no scaling; otherwise factor >= 1, 0 < low < high, original > 0
+inline lsl_status check_rope_scaling(const char* fn, const lsl_rope_scaling* sc) {
+  if (!sc || sc->factor == 0.f) return LSL_OK;
+  if (!(sc->factor >= 1.f) || !(sc->low_freq_factor > 0.f) || !(sc->high_freq_factor > sc->low_freq_factor) ||
+      !(sc->original_max_position > 0.f))
+    return set_error(LSL_ERR_INVALID_ARG, "%s: bad RoPE scaling (factor >= 1, 0 < low < high, original > 0)", fn);
+  return LSL_OK;
+}
 }  // namespace lsl

@@ -87,18 +87,33 @@ lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16
 }
 
 // ---------------------------------------------------------------- RoPE
-// Thread per (row, frequency index i); the angle pos * theta^(-2i/d) and its
-// sine/cosine are evaluated in float64, then every head's pair (i, i + d/2) is
-// rotated in float32 and rounded to bf16 in place.
+// Thread per (row, frequency index i); the inverse frequency theta^(-2i/d)
+// (optionally rescaled the Llama-3.1 way), the angle and its sine/cosine are
+// evaluated in float64, then every head's pair (i, i + d/2) is rotated in
+// float32 and rounded to bf16 in place.
+struct RopeScale {
+  double factor, low, high, orig;  // factor 0: none
+};
+
+LSL_DEV double rope_inv_freq(int i, int head_dim, double theta, const RopeScale& sc) {
+  const double f = pow(theta, -2.0 * (double)i / (double)head_dim);
+  if (sc.factor == 0.0) return f;
+  const double wavelen = 2.0 * 3.141592653589793 / f;
+  if (wavelen < sc.orig / sc.high) return f;
+  if (wavelen > sc.orig / sc.low) return f / sc.factor;
+  const double m = (sc.orig / wavelen - sc.low) / (sc.high - sc.low);
+  return (1.0 - m) * f / sc.factor + m * f;
+}
+
 __global__ void rope_kernel(uint16_t* __restrict__ x, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,
-                            double theta, int inverse) {
+                            double theta, RopeScale sc, int inverse) {
   int half = head_dim >> 1;
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * half) return;
   int64_t row = idx / half;
   int i = (int)(idx - row * half);
   int pos = (int)(row % seq);
-  double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)head_dim);
+  double ang = (double)pos * rope_inv_freq(i, head_dim, theta, sc);
   double sd, cd;
   sincos(ang, &sd, &cd);
   float c = (float)cd, sn = inverse ? -(float)sd : (float)sd;
@@ -112,11 +127,15 @@ __global__ void rope_kernel(uint16_t* __restrict__ x, int64_t T, int64_t ld, int
 }
 
 lsl_status rope_launch(uint16_t* x, int64_t T, int64_t ld, int n_heads, int head_dim, int seq, float theta,
-                       int inverse, hipStream_t s) {
+                       const lsl_rope_scaling* scaling, int inverse, hipStream_t s) {
   if (T == 0) return LSL_OK;
   int64_t n = T * (head_dim / 2);
+  RopeScale sc{0.0, 0.0, 0.0, 0.0};
+  if (scaling && scaling->factor != 0.f)
+    sc = RopeScale{scaling->factor, scaling->low_freq_factor, scaling->high_freq_factor,
+                   scaling->original_max_position};
   hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, T, ld, n_heads, head_dim,
-                     seq, (double)theta, inverse);
+                     seq, (double)theta, sc, inverse);
   return check_launch("rope");
 }
 

@@ -14,6 +14,7 @@ struct GemmDesc {
   float scale = 0.f;
   uint16_t* y = nullptr; int64_t ldy = 0;
   const uint16_t* res = nullptr; int64_t ldres = 0;
+  const uint16_t* bias = nullptr;                   // bf16 [N], added before the rounding (bf16 epilogue)
   // epilogue selection: 0 bf16 store (+ residual); 1 cross-entropy max/sum-exp
   // partials; 2 cross-entropy gradient chunk (hi into y, lo into y2);
   // 3 float accumulate into out32 (bf16 copy into y when y != NULL)

@@ -55,6 +55,7 @@ struct GemmKArgs {
   float scale;
   uint16_t* y; int64_t ldy;
   const uint16_t* res; int64_t ldres;
+  const uint16_t* bias;      // bf16 [N] or NULL
   int tiles_m, tiles_n;
   float cb[16];
   // cross-entropy epilogues
@@ -595,6 +596,10 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         *reinterpret_cast<f32x4*>(o) = r;
         if (a.y) *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
       } else {
+        if (a.bias) {
+          const u32x2 b = *reinterpret_cast<const u32x2*>(a.bias + n);
+          v0 += lo_bf(b[0]); v1 += hi_bf(b[0]); v2 += lo_bf(b[1]); v3 += hi_bf(b[1]);
+        }
         if (a.res) {
           u32x2 r = *reinterpret_cast<const u32x2*>(a.res + m * a.ldres + n);
           v0 = bf2f(f2bf(v0)) + lo_bf(r[0]);
@@ -608,11 +613,11 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   }
 }
 
-// y[m][n] = bf16(sum over splits in index order) (+ residual, rounded again),
-// the same rounding as the unsplit bf16 epilogue. One thread per 4 outputs.
+// y[m][n] = bf16(sum over splits in index order (+ bias)) (+ residual, rounded
+// again), the same rounding as the unsplit bf16 epilogue. One thread per 4 outputs.
 __global__ void gemm_split_reduce(const float* __restrict__ part, int S, int64_t M, int64_t N,
-                                  const uint16_t* __restrict__ res, int64_t ldres, uint16_t* __restrict__ y,
-                                  int64_t ldy) {
+                                  const uint16_t* __restrict__ bias, const uint16_t* __restrict__ res, int64_t ldres,
+                                  uint16_t* __restrict__ y, int64_t ldy) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= M * N) return;
   const int64_t m = i / N, n = i - m * N;
@@ -620,6 +625,10 @@ __global__ void gemm_split_reduce(const float* __restrict__ part, int S, int64_t
   for (int s = 1; s < S; ++s) {
     const f32x4 p = *reinterpret_cast<const f32x4*>(part + (int64_t)s * M * N + i);
     v = f32x4{v[0] + p[0], v[1] + p[1], v[2] + p[2], v[3] + p[3]};
+  }
+  if (bias) {
+    const u32x2 b = *reinterpret_cast<const u32x2*>(bias + n);
+    v = f32x4{v[0] + lo_bf(b[0]), v[1] + hi_bf(b[0]), v[2] + lo_bf(b[1]), v[3] + hi_bf(b[1])};
   }
   if (res) {
     const u32x2 r = *reinterpret_cast<const u32x2*>(res + m * ldres + n);
@@ -686,7 +695,7 @@ static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
   if (a.ksplit > 1) {
     const int64_t n4 = d.M * d.N / 4;
     hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
-                       a.ksplit, d.M, d.N, d.res, d.ldres, d.y, d.ldy);
+                       a.ksplit, d.M, d.N, d.bias, d.res, d.ldres, d.y, d.ldy);
   }
   return check_launch("gemm");
 }
@@ -749,7 +758,7 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   a.la = d.la; a.ldla = d.ldla; a.kl = d.kl; a.lb = d.lb; a.r = d.r; a.nseg = d.nseg;
   for (int i = 0; i < 4; ++i) a.seg_end[i] = d.seg_end[i];
   a.scale = d.scale;
-  a.y = d.y; a.ldy = d.ldy; a.res = d.res; a.ldres = d.ldres;
+  a.y = d.y; a.ldy = d.ldy; a.res = d.res; a.ldres = d.ldres; a.bias = d.bias;
   const Nf4Table& t = nf4_table();
   for (int i = 0; i < 16; ++i) a.cb[i] = t.cb[i];
   a.labels = d.labels; a.lse = d.lse; a.nvalid = d.nvalid; a.part = (float2*)d.part; a.zlab = d.zlab;

@@ -26,7 +26,7 @@ lsl_status check_launch(const char* what) {
 }  // namespace lsl
 
 extern "C" const char* lsl_last_error(void) { return lsl::g_err.c_str(); }
-extern "C" int32_t lsl_abi_version(void) { return 1; }
+extern "C" int32_t lsl_abi_version(void) { return 2; }
 
 extern "C" lsl_status lsl_device_info(int32_t device, lsl_device_props* out) {
   if (!out) return lsl::set_error(LSL_ERR_INVALID_ARG, "lsl_device_info: out is NULL");

@@ -14,9 +14,12 @@ WFMT_CODES = {"nf4": _abi.WFMT_NF4, "bf16": _abi.WFMT_BF16, "nf4dq": _abi.WFMT_N
 
 def layer_cfg(shape):
     """ctypes lsl_layer_cfg from a synth LayerShape-like object."""
+    from .ops import rope_scaling
     return _abi.LayerCfg(shape.hidden, shape.n_q, shape.n_kv, shape.head_dim, shape.inter, shape.rms_eps,
                          shape.rope_theta, WFMT_CODES[shape.wfmt],
-                         shape.lora_r, shape.lora_alpha / shape.lora_r)
+                         shape.lora_r, shape.lora_alpha / shape.lora_r,
+                         int(bool(getattr(shape, "qkv_bias", False))),
+                         rope_scaling(getattr(shape, "rope_scaling", None)))
 
 
 def layer_layout(cfg):
@@ -41,6 +44,9 @@ def write_layer_blob(shape, cfg, blob, w, stream=None):
         return blob[off:off + nbytes]
     region(L.norm1_off, 2 * shape.hidden).view(torch.bfloat16).copy_(w["norm1"])
     region(L.norm2_off, 2 * shape.hidden).view(torch.bfloat16).copy_(w["norm2"])
+    if cfg.qkv_bias:
+        b = torch.cat([w["q_bias"], w["k_bias"], w["v_bias"]]).contiguous()
+        region(L.bias_off, 2 * b.numel()).view(torch.bfloat16).copy_(b)
     for i, (names, (n, k)) in enumerate(zip(PROJ_GROUPS, mat_shapes(shape))):
         m = torch.cat([w[nm] for nm in names], dim=0).contiguous()
         assert m.shape == (n, k)

@@ -106,10 +106,11 @@ class FrozenWeight:
     """A frozen [n_out x k_in] weight: NF4 (codes, absmax), NF4 with
     double-quantized absmax (codes, absmax_q, absmax_scale) or bf16."""
 
-    def __init__(self, n_out, k_in, codes=None, absmax=None, bf16=None, absmax_q=None, absmax_scale=None):
+    def __init__(self, n_out, k_in, codes=None, absmax=None, bf16=None, absmax_q=None, absmax_scale=None,
+                 bias=None):
         self.n_out, self.k_in = n_out, k_in
         self.codes, self.absmax, self.bf16 = codes, absmax, bf16
-        self.absmax_q, self.absmax_scale = absmax_q, absmax_scale
+        self.absmax_q, self.absmax_scale, self.bias = absmax_q, absmax_scale, bias
         if bf16 is not None:
             self.fmt = _abi.WFMT_BF16
         elif absmax_q is not None:
@@ -117,7 +118,12 @@ class FrozenWeight:
         else:
             self.fmt = _abi.WFMT_NF4
         self.struct = _abi.Weight(self.fmt, 0, n_out, k_in, _p(codes), _p(absmax), _p(bf16),
-                                  _p(absmax_q), _p(absmax_scale))
+                                  _p(absmax_q), _p(absmax_scale), _p(bias))
+
+    def with_bias(self, bias):
+        """The same weight with a frozen bf16 bias [n_out] added to its forward output."""
+        return FrozenWeight(self.n_out, self.k_in, self.codes, self.absmax, self.bf16, self.absmax_q,
+                            self.absmax_scale, bias)
 
     @classmethod
     def nf4(cls, w_bf16, stream=None):
@@ -182,10 +188,18 @@ def rmsnorm_bwd(x, w, dy, eps, dres=None, stream=None):
     return dx
 
 
-def rope(x, n_heads, head_dim, seq, theta, inverse=False, stream=None):
+def rope_scaling(scaling):
+    """(factor, low_freq_factor, high_freq_factor, original_max_position) or None
+    -> ctypes lsl_rope_scaling (factor 0 = none)."""
+    return _abi.RopeScaling(*(scaling if scaling else (0.0, 0.0, 0.0, 0.0)))
+
+
+def rope(x, n_heads, head_dim, seq, theta, inverse=False, stream=None, scaling=None):
     """In place on x [T x ld] (bf16)."""
     T, ld = x.shape
-    _check("lsl_rope", lib().lsl_rope(_p(x), T, ld, n_heads, head_dim, seq, theta, int(inverse), _s(stream)))
+    sc = rope_scaling(scaling)
+    _check("lsl_rope", lib().lsl_rope(_p(x), T, ld, n_heads, head_dim, seq, theta, C.byref(sc), int(inverse),
+                                      _s(stream)))
     return x
 
 

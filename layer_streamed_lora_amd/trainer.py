@@ -119,7 +119,8 @@ class StreamedLoraModel:
         return self.store[layer * self.stride: layer * self.stride + self.blob_bytes]
 
     def set_layer_weights(self, layer, w):
-        """w: dict of cuda bf16 tensors ('q'.. 'down' [out x in], 'norm1', 'norm2')."""
+        """w: dict of cuda bf16 tensors ('q'.. 'down' [out x in], 'norm1', 'norm2', and
+        'q_bias', 'k_bias', 'v_bias' when the shape has them)."""
         if self.mode == "resident":
             write_layer_blob(self.shape, self.cfg, self.blob_view(layer), w)
         else:

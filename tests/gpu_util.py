@@ -84,15 +84,16 @@ def oracle_weight(w, fmt):
 
 
 def oracle_layer_weights(w, shape):
-    """All seven projections of a layer as the oracle sees them. NF4DQ blocks its
-    absmax over each fused matrix (q, k, v stacked; gate, up stacked), as the
-    layer blob stores them."""
+    """All seven projections of a layer as the oracle sees them (and the q/k/v
+    biases, if any). NF4DQ blocks its absmax over each fused matrix (q, k, v
+    stacked; gate, up stacked), as the layer blob stores them."""
     from synth.configs import PROJ_IN_OUT
+    biases = {k: np.asarray(v, np.float64) for k, v in w.items() if k.endswith("_bias")}
     if shape.wfmt != "nf4dq":
-        return {p: oracle_weight(w[p], shape.wfmt) for p in PROJ_IN_OUT(shape)}
+        return {**{p: oracle_weight(w[p], shape.wfmt) for p in PROJ_IN_OUT(shape)}, **biases}
     from oracle.nf4 import nf4dq_quantize_fused
     out = {}
     for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
         for p, d in zip(group, nf4dq_quantize_fused([np.asarray(w[p], np.float64) for p in group])):
             out[p] = d
-    return out
+    return {**out, **biases}

@@ -47,7 +47,7 @@ def test_codebook_matches_oracle_bitwise(L):
 
 
 def test_abi_version(L):
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
 
 
 def _status(L, name, *args):
@@ -146,3 +146,35 @@ def test_layer_layout_regions(L, wfmt):
     if wfmt == "nf4dq":
         assert payload == nf4dq_layer_bytes(H, shape.n_q, shape.n_kv, shape.head_dim, I)
         assert lay.total_bytes < 113_000_000
+
+
+def test_fidelity_options_validation_and_layout(L):
+    """q/k/v bias and RoPE scaling: bad options are rejected before anything is
+    enqueued; the bias region is 256-byte aligned and sized [(n_q + 2 n_kv) d]."""
+    import dataclasses
+    from layer_streamed_lora_amd import _abi
+    from layer_streamed_lora_amd import model as M
+    from synth.configs import QWEN05B_LAYER, LLAMA31_ROPE_SCALING
+    lib = L.lib()
+    shape = dataclasses.replace(QWEN05B_LAYER, qkv_bias=True, rope_scaling=LLAMA31_ROPE_SCALING)
+    cfg = M.layer_cfg(shape)
+    lay = M.layer_layout(cfg)
+    plain = M.layer_layout(M.layer_cfg(QWEN05B_LAYER))
+    nqkv = shape.q_dim + 2 * shape.kv_dim
+    assert lay.bias_off % 256 == 0 and lay.bias_off >= plain.norm2_off + 2 * shape.hidden
+    assert lay.total_bytes - plain.total_bytes == (2 * nqkv + 255) // 256 * 256 and plain.bias_off == 0
+    for bad in ((0.5, 1.0, 4.0, 8192.0), (8.0, 4.0, 1.0, 8192.0), (8.0, 0.0, 4.0, 8192.0), (8.0, 1.0, 4.0, 0.0)):
+        c = M.layer_cfg(dataclasses.replace(shape, rope_scaling=bad))
+        out = _abi.LayerLayout()
+        assert lib.lsl_layer_layout_get(C.byref(c), C.byref(out)) == _abi.LSL_ERR_INVALID_ARG
+        assert b"RoPE scaling" in lib.lsl_last_error()
+        sc = _abi.RopeScaling(*bad)
+        assert lib.lsl_rope(256, 4, 128, 1, 128, 4, 1e4, C.byref(sc), 0, None) == _abi.LSL_ERR_INVALID_ARG
+    c = M.layer_cfg(shape)
+    c.qkv_bias = 2
+    assert lib.lsl_layer_layout_get(C.byref(c), C.byref(_abi.LayerLayout())) == _abi.LSL_ERR_INVALID_ARG
+    # a misaligned bias on a weight
+    w = _abi.Weight(_abi.WFMT_BF16, 0, 64, 64, None, None, 256, None, None, 258)
+    assert lib.lora_linear_fwd(256, 8, C.byref(w), 256, 256, 8, 2.0, 256, 256, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
+    # scaling off (NULL or factor 0) is accepted with an empty input
+    assert lib.lsl_rope(None, 0, 128, 1, 128, 4, 1e4, None, 0, None) == _abi.LSL_OK

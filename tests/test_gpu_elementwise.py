@@ -43,6 +43,26 @@ def test_rope(gpu, batch, seq, nh, d, theta):
     assert_close(host(X2), back, "rope inverse")
 
 
+@pytest.mark.parametrize("seq,scaling", [
+    (1024, (8.0, 1.0, 4.0, 8192.0)),   # Llama-3.1's published scaling, all three frequency regimes at d 128
+    (300, (4.0, 1.0, 2.0, 256.0)),     # positions past the original context, ragged rows
+])
+def test_rope_llama3_scaling(gpu, seq, scaling):
+    T, nh, d, theta = seq, 4, 128, 500000.0
+    x = synth.activation((T, nh * d), 11, "x")
+    pos = np.arange(seq)
+    xd = x.astype(np.float64).reshape(T, nh, d)
+    for inverse in (False, True):
+        ref = O.rope_apply(xd, pos, theta, inverse=inverse, scaling=scaling).reshape(T, nh * d)
+        X = dev_bf16(x)
+        gpu.rope(X, nh, d, seq, theta, inverse=inverse, scaling=scaling)
+        torch.cuda.synchronize()
+        assert_close(host(X), ref, "rope scaled")
+        # the rescaled low frequencies really differ from unscaled RoPE
+        plain = O.rope_apply(xd, pos, theta, inverse=inverse).reshape(T, nh * d)
+        assert np.abs(host(X) - plain).max() > 0.1
+
+
 def test_rope_strided_heads_leave_other_columns(gpu):
     # q heads inside a wider qkv row: only the first n_heads*d columns change
     T, nh, d, ld = 24, 2, 64, 320

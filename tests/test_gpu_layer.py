@@ -1,5 +1,7 @@
 """GPU parity of the whole decoder layer (forward, and backward with recompute)
 against the oracle, plus the determinism properties streaming relies on."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -7,6 +9,7 @@ import torch
 import oracle as O
 import synth
 from synth.configs import SMALL_LAYER_NF4, SMALL_LAYER_BF16, SMALL_LAYER_NF4DQ, LLAMA8B_LAYER, PROJ_IN_OUT
+from synth.configs import LLAMA31_ROPE_SCALING
 from tests.gpu_util import dev_bf16, host, assert_close, assert_close_chain, oracle_layer_weights
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +61,10 @@ def _run_and_compare(gpu, shape, batch, seq, wid):
     (SMALL_LAYER_NF4, 2, 40),     # NF4, two sequences, partial tiles everywhere
     (SMALL_LAYER_BF16, 1, 150),   # bf16 base, group of 3, rank 8
     (SMALL_LAYER_NF4DQ, 1, 72),   # NF4 with double-quantized absmax, short last 256-block
+    # Qwen2-style q/k/v bias with RoPE scaling past a 64-position original context
+    (dataclasses.replace(SMALL_LAYER_BF16, qkv_bias=True, rope_scaling=(8.0, 1.0, 4.0, 64.0)), 1, 150),
+    # NF4 with Llama-3.1's published RoPE scaling
+    (dataclasses.replace(SMALL_LAYER_NF4, rope_scaling=LLAMA31_ROPE_SCALING), 2, 40),
 ])
 def test_layer_parity_small(gpu, shape, batch, seq):
     _run_and_compare(gpu, shape, batch, seq, 41)

@@ -115,6 +115,34 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     assert torch.equal(dA, dA1 * 2) and torch.equal(dB, dB1 * 2)
 
 
+@pytest.mark.parametrize("T,fin,fout,r,fmt", [
+    (200, 320, 448, 16, "bf16"),      # ragged, unsplit GEMM
+    (64, 4096, 512, 16, "nf4"),       # few output tiles: split-K path, bias added in the split reduce
+])
+def test_lora_linear_bias(gpu, T, fin, fout, r, fmt):
+    """A frozen bias joins the forward sum before its single rounding; the
+    backward ignores it."""
+    x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 4, fmt)
+    bias = synth.normal_bf16((fout,), 0.5, 4, 0, 60)
+    wd = oracle_weight(w, fmt)
+    W0 = gpu.FrozenWeight.nf4(dev_bf16(w)) if fmt == "nf4" else gpu.FrozenWeight.dense(dev_bf16(w))
+    W = W0.with_bias(dev_bf16(bias))
+    xd, ad, bd = (v.astype(np.float64) for v in (x, a, b))
+    y_ref, t_ref = O.lora_linear_fwd(xd, wd, ad, bd, s, bias=bias.astype(np.float64))
+    X, A, B, DY = dev_bf16(x), dev_bf16(a), dev_bf16(b), dev_bf16(dy)
+    y, t = gpu.lora_linear_fwd(X, W, A, B, s)
+    y0, _ = gpu.lora_linear_fwd(X, W0, A, B, s)
+    dA = torch.zeros((r, fin), dtype=torch.float32, device="cuda")
+    dB = torch.zeros((fout, r), dtype=torch.float32, device="cuda")
+    dA0, dB0 = dA.clone(), dB.clone()
+    dx = gpu.lora_linear_bwd(X, t, DY, W, A, B, s, dA, dB)
+    dx0 = gpu.lora_linear_bwd(X, t, DY, W0, A, B, s, dA0, dB0)
+    torch.cuda.synchronize()
+    assert_close(host(y), y_ref, "y with bias")
+    assert not torch.equal(y, y0)
+    assert torch.equal(dx, dx0) and torch.equal(dA, dA0) and torch.equal(dB, dB0)
+
+
 def test_zero_b_is_plain_dequant_gemm(gpu):
     """B = 0 (LoRA init): y equals the product with the dequantised weight; the
     fused NF4 path and the dense path over the dequantised weight agree bitwise."""

@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 SMALL_NF4 = LayerShape(128, 2, 1, 64, 192, 1e-5, 500000.0, "nf4", 8, 16.0)
 SMALL_BF16 = LayerShape(192, 3, 1, 64, 256, 1e-6, 1000000.0, "bf16", 16, 32.0)
 SMALL_NF4DQ = LayerShape(192, 4, 1, 64, 320, 1e-5, 500000.0, "nf4dq", 16, 32.0)
+# Qwen2-style q/k/v bias; Llama-3.1-style RoPE scaling with a short original context
+SMALL_BF16_BIAS = LayerShape(192, 3, 1, 64, 256, 1e-6, 1000000.0, "bf16", 16, 32.0, qkv_bias=True)
+SMALL_NF4_SCALED = LayerShape(128, 2, 1, 64, 192, 1e-5, 500000.0, "nf4", 8, 16.0,
+                              rope_scaling=(8.0, 1.0, 4.0, 32.0))
 
 
 def build(shape, n_layers, vocab, tied, batch, seq, mode, wid):
@@ -42,7 +46,8 @@ def ids_for(vocab, batch, seq, n_micro, wid):
     return [synth.token_ids(batch * seq, vocab, wid, salt=i) for i in range(n_micro)]
 
 
-@pytest.mark.parametrize("shape,tied", [(SMALL_NF4, False), (SMALL_BF16, True), (SMALL_NF4DQ, False)])
+@pytest.mark.parametrize("shape,tied", [(SMALL_NF4, False), (SMALL_BF16, True), (SMALL_NF4DQ, False),
+                                        (SMALL_BF16_BIAS, True), (SMALL_NF4_SCALED, False)])
 def test_model_step_matches_oracle(gpu, shape, tied):
     n_layers, vocab, batch, seq, n_micro, wid = 3, 640, 2, 40, 2, 70
     m, weights, loras, (emb, fn, lm) = build(shape, n_layers, vocab, tied, batch, seq, "streamed", wid)
@@ -72,7 +77,7 @@ def _assert_same_state(a, b):
         assert torch.equal(getattr(a.lora, name), getattr(b.lora, name)), name
 
 
-@pytest.mark.parametrize("shape", [SMALL_NF4, SMALL_BF16, SMALL_NF4DQ])
+@pytest.mark.parametrize("shape", [SMALL_NF4, SMALL_BF16, SMALL_NF4DQ, SMALL_BF16_BIAS])
 def test_streamed_equals_resident_small(gpu, shape):
     n_layers, vocab, batch, seq, n_micro = 4, 640, 2, 64, 3
     s, *_ = build(shape, n_layers, vocab, False, batch, seq, "streamed", 71)
@@ -110,6 +115,9 @@ def _streamed_vs_resident(shape, L, V, tied, batch, seq, n_micro, seed):
                 w[p] = (torch.randn((fout, fin), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
             w["norm1"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
             w["norm2"] = torch.ones(shape.hidden, dtype=torch.bfloat16, device="cuda")
+            if shape.qkv_bias:
+                for p, n in (("q", shape.q_dim), ("k", shape.kv_dim), ("v", shape.kv_dim)):
+                    w[p + "_bias"] = (torch.randn(n, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
             m.set_layer_weights(l, w)
         m.embed.copy_((torch.randn((V, shape.hidden), generator=g, device="cuda") * 0.02).to(torch.bfloat16))
         if not tied:
@@ -165,3 +173,20 @@ def test_streamed_equals_resident_llama8b_nf4dq(gpu):
     blobs, 3.6 GB pinned store), 1 x 1024 tokens: streamed equals resident."""
     s = _streamed_vs_resident(LLAMA8B_LAYER_DQ, 32, 128256, False, 1, 1024, 1, 6)
     assert s.blob_bytes < 113_000_000
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_qwen05b_bias(gpu):
+    """Qwen2.5-0.5B-shaped model as the real checkpoints are built: q/k/v bias
+    (24 layers, tied head, 1 x 512 tokens, 2 microbatches)."""
+    import dataclasses
+    _streamed_vs_resident(dataclasses.replace(QWEN05B_LAYER, qkv_bias=True), 24, 151936, True, 1, 512, 2, 7)
+
+
+@pytest.mark.timeout(900)
+def test_streamed_equals_resident_llama8b_rope_scaled(gpu):
+    """Llama-3.1-8B-shaped NF4 model with the published RoPE frequency scaling."""
+    import dataclasses
+    from synth.configs import LLAMA31_ROPE_SCALING
+    _streamed_vs_resident(dataclasses.replace(LLAMA8B_LAYER, rope_scaling=LLAMA31_ROPE_SCALING), 32, 128256, False,
+                          1, 1024, 1, 8)
