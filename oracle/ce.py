@@ -8,6 +8,13 @@ never stores logits; what it computes is the plain definition:
   loss = mean over tokens with label != ignore_index of (lse_t - z_t,label),
   dh = rnd(grad_scale / N_valid * (softmax(z) - onehot(label)) W)  (zero rows for ignored tokens).
 W (the lm_head or the tied embedding) is frozen, so it gets no gradient.
+
+Per-token log-probabilities (the reference model's scores that preference
+training compares against, computed with the adapters off on the same streamed
+base: "Soup: ...", section on the layer-streaming mechanism, and the news
+article's key takeaways on preference training): logp_t = z_t,label - lse_t for
+tokens with a label, 0 for ignored ones; a sequence's score is the sum over its
+tokens.
 """
 import numpy as np
 
@@ -46,3 +53,18 @@ def ce_loss_bwd(h, w, labels, ignore_index=-100, grad_scale=1.0, rnd=round_bf16)
     if nv:
         p *= grad_scale / nv
     return rnd(p @ w)
+
+
+def ce_token_logprobs(h, w, labels, ignore_index=-100):
+    """logp [T] = z_label - lse (0 where the label is ignore_index)."""
+    labels = np.asarray(labels)
+    z, lse = _logits_lse(h, w)
+    out = np.zeros(len(labels))
+    idx = np.nonzero(labels != ignore_index)[0]
+    out[idx] = z[idx, labels[idx]] - lse[idx]
+    return out
+
+
+def sequence_logprobs(logp, batch, seq):
+    """Sum of the token log-probabilities of each sequence [batch]."""
+    return np.asarray(logp).reshape(batch, seq).sum(axis=1)

@@ -31,7 +31,7 @@ arithmetic is float64.
 import numpy as np
 
 from .bf16 import round_bf16
-from .lora import lora_linear_fwd, lora_linear_bwd
+from .lora import lora_linear_fwd, lora_linear_bwd, base_linear_fwd
 
 
 # ---------------------------------------------------------------- RMSNorm
@@ -163,9 +163,16 @@ def swiglu_bwd(g, u, da, rnd=round_bf16):
 # ---------------------------------------------------------------- decoder layer
 def decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=round_bf16):
     """Forward of one layer. w: dequantised weights ('q','k','v','o','gate','up','down'
-    [out x in], 'norm1', 'norm2'); lora: 'A_p' [r x in], 'B_p' [out x r].
+    [out x in], 'norm1', 'norm2'); lora: 'A_p' [r x in], 'B_p' [out x r], or None
+    for the base alone (adapters off).
     Returns (out, cache) where cache holds every intermediate the backward needs."""
     s = shape.lora_scale
+
+    def proj(xx, p, bias=None):
+        if lora is None:
+            return base_linear_fwd(xx, w[p], rnd, bias), None
+        return lora_linear_fwd(xx, w[p], lora["A_" + p], lora["B_" + p], s, rnd, bias=bias)
+
     nq, nkv, d = shape.n_q, shape.n_kv, shape.head_dim
     T = x.shape[0]
     pos = positions_of(batch, seq)
@@ -173,20 +180,19 @@ def decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=round_bf16):
     c["n1"] = n1 = rmsnorm_fwd(x, w["norm1"], shape.rms_eps, rnd)
     sc = getattr(shape, "rope_scaling", None)
     for p in ("q", "k", "v"):
-        c[p], c["t_" + p] = lora_linear_fwd(n1, w[p], lora["A_" + p], lora["B_" + p], s, rnd,
-                                            bias=w.get(p + "_bias"))
+        c[p], c["t_" + p] = proj(n1, p, bias=w.get(p + "_bias"))
     c["qr"] = rope_apply(c["q"].reshape(T, nq, d), pos, shape.rope_theta, rnd=rnd, scaling=sc)
     c["kr"] = rope_apply(c["k"].reshape(T, nkv, d), pos, shape.rope_theta, rnd=rnd, scaling=sc)
     vv = c["v"].reshape(T, nkv, d)
     o, c["lse"] = attention_fwd(c["qr"], c["kr"], vv, batch, seq, rnd)
     c["attn"] = o = o.reshape(T, nq * d)
-    c["o"], c["t_o"] = lora_linear_fwd(o, w["o"], lora["A_o"], lora["B_o"], s, rnd)
+    c["o"], c["t_o"] = proj(o, "o")
     c["h1"] = h1 = rnd(x + c["o"])
     c["n2"] = n2 = rmsnorm_fwd(h1, w["norm2"], shape.rms_eps, rnd)
     for p in ("gate", "up"):
-        c[p], c["t_" + p] = lora_linear_fwd(n2, w[p], lora["A_" + p], lora["B_" + p], s, rnd)
+        c[p], c["t_" + p] = proj(n2, p)
     c["act"] = a = swiglu_fwd(c["gate"], c["up"], rnd)
-    c["down"], c["t_down"] = lora_linear_fwd(a, w["down"], lora["A_down"], lora["B_down"], s, rnd)
+    c["down"], c["t_down"] = proj(a, "down")
     out = rnd(h1 + c["down"])
     return out, c
 

@@ -24,6 +24,14 @@ def lora_linear_fwd(x, w, a, b, scale, rnd=round_bf16, bias=None):
     return rnd(y), t
 
 
+def base_linear_fwd(x, w, rnd=round_bf16, bias=None):
+    """The frozen projection alone (adapters off): y = rnd(x W^T (+ bias))."""
+    y = x @ w.T
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return rnd(y)
+
+
 def lora_linear_bwd(x, t, dy, w, a, b, scale, rnd=round_bf16, round_dx=True):
     """Returns (dx, dA, dB, u) for the loss gradient dy [T x out].
 

@@ -15,7 +15,7 @@ gradients are summed in microbatch order.
 import numpy as np
 
 from .bf16 import round_bf16
-from .ce import ce_loss_fwd, ce_loss_bwd
+from .ce import ce_loss_fwd, ce_loss_bwd, ce_token_logprobs, sequence_logprobs
 from .layer import decoder_layer_fwd, decoder_layer_bwd, rmsnorm_fwd, rmsnorm_bwd
 
 IGNORE = -100
@@ -70,3 +70,17 @@ def model_step(id_chunks, emb, final_norm, lm_head, layers, shape, batch, seq, r
                     a[k] = a[k] + g[k]
     loss = sum(o["loss"] for o in outs) / n
     return loss, acc, outs
+
+
+def reference_logprobs(ids, emb, final_norm, lm_head, layer_weights, shape, batch, seq, rnd=round_bf16):
+    """Forward of one microbatch through the base alone (adapters off) and the
+    per-token and per-sequence log-probabilities of the shifted labels:
+    (logp [batch*seq], seq_logp [batch])."""
+    ids = np.asarray(ids)
+    wlm = emb if lm_head is None else lm_head
+    h = emb[ids]
+    for w in layer_weights:
+        h, _ = decoder_layer_fwd(h, w, None, shape, batch, seq, rnd)
+    hn = rmsnorm_fwd(h, final_norm, shape.rms_eps, rnd)
+    logp = ce_token_logprobs(hn, wlm, shifted_labels(ids, batch, seq), IGNORE)
+    return logp, sequence_logprobs(logp, batch, seq)

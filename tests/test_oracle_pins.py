@@ -571,6 +571,45 @@ def test_ce_matches_torch():
     assert np.allclose(dh2, 0.25 * dh)
 
 
+def test_ce_token_logprobs_match_torch_log_softmax():
+    """logp = log_softmax(z)[label] from torch, 0 where ignored; W = 0 gives
+    -ln V; over every possible label the probabilities sum to one; the
+    per-sequence score is the sum of its tokens."""
+    from oracle.ce import ce_token_logprobs, sequence_logprobs
+    T, H, V = 12, 16, 50
+    h = RNG.standard_normal((T, H))
+    W = RNG.standard_normal((V, H)) * 0.3
+    labels = RNG.integers(0, V, T)
+    labels[[3, 7]] = -100
+    lp = ce_token_logprobs(h, W, labels)
+    ref = torch.log_softmax(t64(h) @ t64(W).T, dim=1).numpy()
+    ok = labels != -100
+    assert np.allclose(lp[ok], ref[np.nonzero(ok)[0], labels[ok]], atol=1e-13) and np.all(lp[~ok] == 0)
+    assert np.allclose(ce_token_logprobs(h, np.zeros((V, H)), labels)[ok], -np.log(V), atol=1e-13)
+    every = np.array([ce_token_logprobs(h[:1], W, [v])[0] for v in range(V)])
+    assert abs(np.exp(every).sum() - 1.0) < 1e-12
+    assert np.allclose(sequence_logprobs(lp, 3, 4), [lp[0:4].sum(), lp[4:8].sum(), lp[8:12].sum()])
+    loss, _, nv = O.ce_loss_fwd(h, W, labels)
+    assert abs(loss + lp.sum() / nv) < 1e-12          # the training loss is minus their mean
+
+
+def test_adapter_off_layer_equals_zero_b_and_torch():
+    """With the adapters off the layer is the base alone: bit for bit the layer
+    with B = 0 (in bf16 mode, where t B^T = 0 exactly), and torch's
+    composition of the plain weights."""
+    shape, batch, seq = TINY_LAYER, 2, 8
+    w, lora = tiny_layer_params()
+    x = RNG.standard_normal((batch * seq, shape.hidden))
+    off, c = O.decoder_layer_fwd(x, w, None, shape, batch, seq)
+    lora0 = {k: (np.zeros_like(v) if k.startswith("B_") else v) for k, v in lora.items()}
+    zero_b, _ = O.decoder_layer_fwd(x, w, lora0, shape, batch, seq)
+    assert np.array_equal(off, zero_b) and c["t_q"] is None
+    exact, _ = O.decoder_layer_fwd(x, w, None, shape, batch, seq, rnd=identity)
+    assert np.allclose(exact, _torch_layer(x, w, lora0, shape, batch, seq), atol=1e-11)
+    # and it is not the adapted layer
+    assert not np.allclose(exact, O.decoder_layer_fwd(x, w, lora, shape, batch, seq, rnd=identity)[0])
+
+
 def test_ce_zero_weights_closed_form():
     T, H, V = 5, 8, 37
     h = RNG.standard_normal((T, H))
@@ -626,3 +665,24 @@ def test_model_grad_reaches_layer0_fd():
         return model_step(ids, emb, fn, None, ll, shape, batch, seq, rnd=identity)[0]
     assert_fd(grads[0][key], L, a0, n=4, rtol=1e-5, atol=1e-9)
     assert np.any(grads[0][key] != 0)
+
+
+def test_reference_logprobs_agree_with_the_training_loss_at_b_zero():
+    """The adapter-off forward scores each token; with B = 0 the adapted
+    model computes the same forward, so its training loss is minus the mean
+    reference log-probability, and each sequence score is the sum of its own
+    tokens' log-probabilities."""
+    from oracle.model import model_fwd_bwd, reference_logprobs
+    shape, batch, seq, V = TINY_LAYER, 2, 6, 23
+    rng = np.random.default_rng(9)
+    layers = [tiny_layer_params(seed=s) for s in (31, 32)]
+    layers0 = [(w, {k: (np.zeros_like(v) if k.startswith("B_") else v) for k, v in lo.items()}) for w, lo in layers]
+    emb = rng.standard_normal((V, shape.hidden)) * 0.5
+    fn = 1 + rng.uniform(-0.1, 0.1, shape.hidden)
+    ids = rng.integers(0, V, batch * seq)
+    lp, slp = reference_logprobs(ids, emb, fn, None, [w for w, _ in layers], shape, batch, seq)
+    r = model_fwd_bwd(ids, emb, fn, None, layers0, shape, batch, seq)
+    assert r["n_valid"] == batch * (seq - 1)
+    assert abs(r["loss"] + lp.sum() / r["n_valid"]) < 1e-12
+    assert np.all(lp.reshape(batch, seq)[:, -1] == 0) and np.all(lp.reshape(batch, seq)[:, :-1] < 0)
+    assert np.allclose(slp, lp.reshape(batch, seq).sum(1))
