@@ -99,6 +99,25 @@ def pinned_h2d_peak(nbytes, reps=20):
     return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def time_reference(m, inputs, steps, warmup):
+    """The adapter-off streamed forward with per-token log-probabilities (the
+    reference scores of preference training): ms per call over all microbatches."""
+    import torch
+    for _ in range(warmup):
+        m.reference_logprobs(inputs)
+    torch.cuda.synchronize()
+    loads0 = m.loads
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        lp, _ = m.reference_logprobs(inputs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"ms": e0.elapsed_time(e1) / steps, "loads": (m.loads - loads0) // steps,
+            "mean_logp": float(lp[:, :-1].mean().item())}
+
+
 def time_steps(m, inputs, steps, warmup, timing_which=0, stats=False):
     import ctypes as C
     import torch
@@ -431,6 +450,8 @@ def main():
     if r_model is not None:
         resident = time_steps(r_model, inputs, args.steps, args.warmup)
         log(f"  resident: {resident['ms_per_step']:.2f} ms/step")
+    reference = time_reference(s_model, inputs, args.steps, args.warmup)
+    log(f"  reference forward (adapters off, streamed): {reference['ms']:.2f} ms per {T * ms.n_micro} tokens")
 
     variant = None
     if not args.no_nf4dq and args.workload == "llama8b_nf4":
@@ -474,6 +495,10 @@ def main():
         "bit_exact_vs_resident": bit_exact,
         "loss": round(res["loss"], 5),
         "nf4dq": variant,
+        "reference_forward": {"what": "adapter-off streamed forward + per-token log-probs (preference reference)",
+                              "ms": round(reference["ms"], 3),
+                              "tok_s": round(T * ms.n_micro / (reference["ms"] * 1e-3), 2),
+                              "layer_copies": reference["loads"], "mean_logp": round(reference["mean_logp"], 4)},
         "context": {"pages_tok_s": 119.6, "pages_hardware": "RTX 3050 Laptop 4 GB, seq/batch not stated"},
     }
     if not args.no_cpu_baseline:

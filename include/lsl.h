@@ -213,7 +213,9 @@ typedef struct { float* dA[4]; float* dB[4]; } lsl_lora_grads;
 enum { LSL_MODE_FWD = 0, LSL_MODE_BWD = 1 };
 size_t lsl_layer_workspace_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode);
 /* x_in, x_out [batch*seq x hidden] bf16. Nothing is saved: the caller keeps
- * x_in as the layer-boundary checkpoint for the backward. */
+ * x_in as the layer-boundary checkpoint for the backward. lora may be NULL:
+ * the adapters are off and every projection is the frozen base alone (the
+ * reference forward of preference training). */
 lsl_status decoder_layer_fwd(const lsl_layer_cfg* cfg, const void* layer_blob,
                              const lsl_lora_set* lora, const uint16_t* x_in, int32_t batch,
                              int32_t seq, uint16_t* x_out, void* ws, size_t ws_bytes,
@@ -288,6 +290,18 @@ lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm, const int
                              const float* lse, int64_t T, int64_t H, int64_t V,
                              int32_t ignore_index, float grad_scale, uint16_t* dhN, void* ws,
                              size_t ws_bytes, lsl_stream stream);
+/* Per-token log-probabilities of the labels with the fused forward pass (no
+ * logits tensor): logp[t] = z_t,label - lse_t (float32, 0 where the label is
+ * ignore_index or outside the vocabulary), and, when seq_logp is not NULL,
+ * seq_logp[b] = sum of logp over the T / batch tokens of sequence b (fixed
+ * order). This is the reference score of preference training, computed on the
+ * final hidden state of the adapter-off forward (decoder_layer_fwd with lora
+ * NULL) of the same streamed base ("Soup: ...", section "Layer Streaming: The
+ * Mechanism Behind the 4 GB Claim"; "Soup CLI ...", "Key Takeaways").
+ * Workspace: lsl_ce_workspace_bytes(T, H, V). */
+lsl_status fused_ce_logprobs(const uint16_t* hN, const uint16_t* w_lm, const int32_t* labels, int64_t T,
+                             int64_t H, int64_t V, int32_t ignore_index, int32_t batch, float* logp,
+                             float* seq_logp, void* ws, size_t ws_bytes, lsl_stream stream);
 
 /* ------------------------------------------------------------------ support ops
  * The individual steps of the decoder layer, exported so each can be checked on

@@ -82,6 +82,7 @@ PROTOS = {
     "lsl_ce_workspace_bytes": (sz, [i64, i64, i64]),
     "fused_ce_loss_fwd": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, sz, vp]),
     "fused_ce_loss_bwd": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp, sz, vp]),
+    "fused_ce_logprobs": (i32, [vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp, sz, vp]),
     "lsl_rmsnorm_fwd": (i32, [vp, vp, i64, i64, f32, vp, vp]),
     "lsl_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, f32, vp, vp]),
     "lsl_rope": (i32, [vp, i64, i64, i32, i32, i32, f32, C.POINTER(RopeScaling), i32, vp]),

@@ -213,16 +213,18 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
   int kl = nseg * d.r;
-  LoraNt nt;
-  nt.p = x; nt.ldp = k; nt.T = d.T; nt.K = k; nt.kl = kl; nt.a_full = lo->A[i];
-  nt.out = t; nt.ldo = kl; nt.ws = part;
-  LSL_TRY(lora_nt_launch(nt, s));
+  if (lo) {  // adapters on: t = x A^T first, then the GEMM's LoRA K-step
+    LoraNt nt;
+    nt.p = x; nt.ldp = k; nt.T = d.T; nt.K = k; nt.kl = kl; nt.a_full = lo->A[i];
+    nt.out = t; nt.ldo = kl; nt.ws = part;
+    LSL_TRY(lora_nt_launch(nt, s));
+  }
   if (!y) return LSL_OK;
   GemmDesc g;
   g.x = x; g.ldx = k; g.wfmt = c->wfmt; g.kn = false;
   g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i]; g.wq8 = W.wq8[i]; g.wsc = W.wsc[i];
   g.M = d.T; g.N = n; g.K = k;
-  g.lora = 1; g.la = t; g.ldla = kl; g.kl = kl; g.lb = lo->B[i]; g.r = d.r; g.nseg = nseg;
+  g.lora = lo ? 1 : 0; g.la = t; g.ldla = kl; g.kl = kl; g.lb = lo ? lo->B[i] : nullptr; g.r = d.r; g.nseg = nseg;
   if (i == LSL_M_QKV) { g.seg_end[0] = d.Q; g.seg_end[1] = d.Q + d.KV; g.seg_end[2] = d.NQKV; }
   else if (i == LSL_M_GU) { g.seg_end[0] = d.I; g.seg_end[1] = 2 * d.I; }
   else g.seg_end[0] = n;
@@ -318,13 +320,15 @@ extern "C" size_t lsl_layer_workspace_bytes(const lsl_layer_cfg* cfg, int32_t ba
   return plan_of(cfg, batch, seq, mode).total;
 }
 
+// lora may be NULL in the forward only (adapters off)
 static lsl_status check_layer_call(const char* fn, const lsl_layer_cfg* cfg, const void* blob, const lsl_lora_set* lora,
                                    int32_t batch, int32_t seq, void* ws, size_t ws_bytes, int mode) {
   LSL_TRY(check_cfg(cfg, fn));
   if (batch < 0 || seq < 0) return set_error(LSL_ERR_INVALID_ARG, "%s: negative batch/seq", fn);
   if (!blob || !aligned(blob, 256)) return set_error(LSL_ERR_INVALID_ARG, "%s: layer blob NULL or not 256-byte aligned", fn);
-  if (!lora) return set_error(LSL_ERR_INVALID_ARG, "%s: lora set is NULL", fn);
-  for (int i = 0; i < 4; ++i) LSL_TRY(check_ptrs(fn, {lora->A[i], lora->B[i]}));
+  if (!lora && mode == LSL_MODE_BWD) return set_error(LSL_ERR_INVALID_ARG, "%s: lora set is NULL", fn);
+  if (lora)
+    for (int i = 0; i < 4; ++i) LSL_TRY(check_ptrs(fn, {lora->A[i], lora->B[i]}));
   size_t need = plan_of(cfg, batch, seq, mode).total;
   if (!ws || ws_bytes < need || !aligned(ws, 256))
     return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, need);

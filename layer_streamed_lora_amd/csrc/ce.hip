@@ -18,7 +18,7 @@ namespace lsl {
 constexpr int64_t CE_CHUNK = 16384;  // vocabulary columns per backward chunk
 
 struct CePlan {
-  size_t nvalid, part, zlab, lossv, g, dh32, total;
+  size_t nvalid, part, zlab, lossv, lse, g, dh32, total;
   int splits;
 };
 
@@ -47,6 +47,7 @@ static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
   p.part = take((size_t)ntiles * T * 8);
   p.zlab = take((size_t)T * 4);
   p.lossv = take((size_t)T * 4);
+  p.lse = take((size_t)T * 4);  // the log-probability call's own log-sum-exp
   size_t fwd_end = off;
   off = common;
   int64_t vc = V < CE_CHUNK ? V : CE_CHUNK;
@@ -139,6 +140,28 @@ __global__ void ce_loss_kernel(const float* __restrict__ lossv, int64_t T, const
     __syncthreads();
   }
   if (threadIdx.x == 0) *loss = *nvalid > 0.f ? acc[0] / *nvalid : 0.f;
+}
+
+// logp[t] = -lossv[t] (z_label - lse, 0 where ignored); seq_logp[b] = sum of
+// sequence b's tokens, one workgroup per sequence, fixed summation order.
+__global__ void ce_logp_kernel(const float* __restrict__ lossv, int64_t seq, float* __restrict__ logp,
+                               float* __restrict__ seq_logp) {
+  __shared__ float acc[256];
+  const int64_t t0 = (int64_t)blockIdx.x * seq;
+  float s = 0.f;
+  for (int64_t j = threadIdx.x; j < seq; j += 256) {
+    const float v = -lossv[t0 + j];
+    logp[t0 + j] = v;
+    s += v;
+  }
+  if (!seq_logp) return;
+  acc[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (threadIdx.x < k) acc[threadIdx.x] += acc[threadIdx.x + k];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) seq_logp[blockIdx.x] = acc[0];
 }
 
 static lsl_status ce_check(const char* fn, int64_t T, int64_t H, int64_t V) {
@@ -239,4 +262,37 @@ extern "C" lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm
     return check_launch(fn);
   }
   return LSL_OK;
+}
+
+extern "C" lsl_status fused_ce_logprobs(const uint16_t* hN, const uint16_t* w_lm, const int32_t* labels, int64_t T,
+                                        int64_t H, int64_t V, int32_t ignore_index, int32_t batch, float* logp,
+                                        float* seq_logp, void* ws, size_t ws_bytes, lsl_stream stream) {
+  const char* fn = "fused_ce_logprobs";
+  LSL_TRY(ce_check(fn, T, H, V));
+  if (batch <= 0 || T % batch) return set_error(LSL_ERR_INVALID_ARG, "%s: T must be a multiple of batch > 0", fn);
+  if (T == 0) return LSL_OK;
+  LSL_TRY(check_ptrs(fn, {hN, w_lm}));
+  LSL_TRY(check_ptrs(fn, {labels, logp}, 4));
+  if (seq_logp && !aligned(seq_logp, 4)) return set_error(LSL_ERR_INVALID_ARG, "%s: seq_logp misaligned", fn);
+  CePlan p = ce_plan(T, H, V);
+  if (!ws || ws_bytes < p.total || !aligned(ws, 256))
+    return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, p.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  // the forward's first two stages: per-tile (max, sum exp) and the label logit,
+  // then their ordered merge into lse and lossv = lse - z_label
+  GemmDesc g;
+  g.x = hN; g.ldx = H; g.wfmt = LSL_WFMT_BF16; g.wb = w_lm; g.M = T; g.N = V; g.K = H;
+  g.epi = 1; g.labels = labels; g.part = w + p.part; g.zlab = (float*)(w + p.zlab); g.ignore = ignore_index;
+  g.vocab = V;
+  LSL_TRY(gemm_launch(g, s));
+  int bn, bm;
+  gemm_tile_shape(T, V, bn, bm);
+  int64_t ntiles = (V + bn - 1) / bn;
+  hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 63) / 64)), dim3(64 * LSE_WAVES), 0, s,
+                     (const float2*)(w + p.part), ntiles, T, labels, (const float*)(w + p.zlab), ignore_index, V,
+                     (float*)(w + p.lse), (float*)(w + p.lossv));
+  hipLaunchKernelGGL(ce_logp_kernel, dim3((unsigned)batch), dim3(256), 0, s, (const float*)(w + p.lossv),
+                     T / batch, logp, seq_logp);
+  return check_launch(fn);
 }

@@ -159,11 +159,13 @@ def layer_workspace_bytes(cfg, batch, seq, mode):
 
 
 def decoder_layer_fwd(cfg, blob, lora_set, x, batch, seq, out=None, ws=None, stream=None):
+    """lora_set None: adapters off (the frozen base alone)."""
     if out is None:
         out = torch.empty_like(x)
     if ws is None:
         ws = torch.empty(layer_workspace_bytes(cfg, batch, seq, _abi.MODE_FWD), dtype=torch.uint8, device=x.device)
-    _check("decoder_layer_fwd", lib().decoder_layer_fwd(C.byref(cfg), _p(blob), C.byref(lora_set), _p(x), batch, seq,
+    lo = None if lora_set is None else C.byref(lora_set)
+    _check("decoder_layer_fwd", lib().decoder_layer_fwd(C.byref(cfg), _p(blob), lo, _p(x), batch, seq,
                                                         _p(out), _p(ws), ws.numel(), _s(stream)))
     return out
 

@@ -276,6 +276,21 @@ def fused_ce_loss_fwd(hN, w_lm, labels, ignore_index=-100, ws=None, stream=None)
     return loss, lse
 
 
+def fused_ce_logprobs(hN, w_lm, labels, batch, ignore_index=-100, ws=None, logp=None, seq_logp=None, stream=None):
+    """-> (logp float32 [T], seq_logp float32 [batch]) on the device."""
+    T, H = hN.shape
+    V = w_lm.shape[0]
+    if logp is None:
+        logp = torch.empty(T, dtype=torch.float32, device=hN.device)
+    if seq_logp is None:
+        seq_logp = torch.empty(batch, dtype=torch.float32, device=hN.device)
+    if ws is None:
+        ws = _ws(ce_workspace_bytes(T, H, V), hN.device)
+    _check("fused_ce_logprobs", lib().fused_ce_logprobs(_p(hN), _p(w_lm), _p(labels), T, H, V, ignore_index, batch,
+                                                        _p(logp), _p(seq_logp), _p(ws), ws.numel(), _s(stream)))
+    return logp, seq_logp
+
+
 def fused_ce_loss_bwd(hN, w_lm, labels, lse, grad_scale=1.0, ignore_index=-100, ws=None, out=None, stream=None):
     T, H = hN.shape
     V = w_lm.shape[0]

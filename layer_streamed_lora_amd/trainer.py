@@ -226,6 +226,38 @@ class StreamedLoraModel:
             self._done(slot)
             cur = 1 - cur
 
+    def reference_logprobs(self, inputs):
+        """Forward-only sweep of every microbatch through the frozen base with the
+        adapters off (layer calls with no LoRA set), then the per-token and
+        per-sequence log-probabilities of the shifted labels. Returns device
+        tensors (logp [n_micro x T], seq_logp [n_micro x batch]); each microbatch
+        streams every layer once, in order."""
+        ids, labels = inputs
+        n = ids.shape[0]
+        L, T, H = self.n_layers, self.T, self.shape.hidden
+        stream = torch.cuda.current_stream()
+        logp = torch.empty((n, T), dtype=torch.float32, device=self.device)
+        seq_logp = torch.empty((n, self.batch), dtype=torch.float32, device=self.device)
+        visits = list(range(L))
+        cfg = self.cfg
+        for mb in range(n):
+            _check("lsl_embed_fwd", lib().lsl_embed_fwd(_p(self.embed), _p(ids[mb]), T, H, self.vocab,
+                                                        _p(self.ckpt[0]), _s(stream)))
+            for i in range(L):
+                ptr, slot = self._blob_ptr_for_visit(visits, i)
+                # ping-pong between two checkpoint rows: only the last hidden state is needed
+                src, dst = self.ckpt[i % 2], self.ckpt[(i + 1) % 2]
+                _check("decoder_layer_fwd", lib().decoder_layer_fwd(
+                    C.byref(cfg), ptr, None, _p(src), self.batch, self.seq, _p(dst), _p(self.ws), self.ws.numel(),
+                    _s(stream)))
+                self._done(slot)
+            _check("lsl_rmsnorm_fwd", lib().lsl_rmsnorm_fwd(_p(self.ckpt[L % 2]), _p(self.final_norm), T, H,
+                                                            self.shape.rms_eps, _p(self.hn), _s(stream)))
+            _check("fused_ce_logprobs", lib().fused_ce_logprobs(
+                _p(self.hn), _p(self.w_lm), _p(labels[mb]), T, H, self.vocab, IGNORE, self.batch, _p(logp[mb]),
+                _p(seq_logp[mb]), _p(self.ws), self.ws.numel(), _s(stream)))
+        return logp, seq_logp
+
     def step(self, inputs, lr=2e-4, adamw=True):
         """One optimizer step over the microbatches of `inputs` (from
         prepare_inputs). Returns the per-microbatch losses as a device tensor

@@ -88,3 +88,35 @@ def test_ce_llama8b_head_sampled_rows(gpu):
     assert_close(host(dh)[rows], dh_ref, "ce dh rows")
     assert_close_chain(host(dh)[rows] * nv_all, dh_ref * nv_all, "ce dh rows * N_valid")
     assert np.all(host(dh)[T - 1] == 0)
+
+
+@pytest.mark.parametrize("T,H,V,batch", [
+    (100, 128, 16576, 4),       # ragged vocabulary tile, 4 sequences of 25
+    (37, 256, 1088, 1),
+    (1, 64, 64, 1),
+])
+def test_ce_logprobs_parity(gpu, T, H, V, batch):
+    """Per-token log-probabilities z_label - lse (0 where ignored) and their
+    per-sequence sums. float32 outputs: |gpu - oracle| <= 1e-5 (|z_label| +
+    |lse|) per token (the float32 loss bound applied to each of the two terms),
+    and the sum of those bounds per sequence."""
+    from oracle.ce import ce_token_logprobs, sequence_logprobs
+    h, w, labels = _case(T, H, V, 70 + T)
+    hd, wd = h.astype(np.float64), w.astype(np.float64)
+    lp_ref = ce_token_logprobs(hd, wd, labels)
+    _, lse_ref, _ = O.ce_loss_fwd(hd, wd, labels)
+    bound = 1e-5 * (np.abs(lp_ref + lse_ref) + np.abs(lse_ref)) + 1e-7
+    bound[labels == -100] = 0.0
+    lp, slp = gpu.fused_ce_logprobs(dev_bf16(h), dev_bf16(w), dev(labels.astype(np.int32)), batch)
+    torch.cuda.synchronize()
+    err = np.abs(host(lp) - lp_ref)
+    assert np.all(err <= bound), (err.max(), np.argmax(err - bound))
+    assert np.all(host(lp)[labels == -100] == 0)
+    sb = bound.reshape(batch, -1).sum(1) + 1e-6 * np.abs(sequence_logprobs(lp_ref, batch, T // batch))
+    assert np.all(np.abs(host(slp) - sequence_logprobs(lp_ref, batch, T // batch)) <= sb)
+    # same bits as minus the training forward's per-token loss terms: the two share the same pass
+    loss, _ = gpu.fused_ce_loss_fwd(dev_bf16(h), dev_bf16(w), dev(labels.astype(np.int32)))
+    torch.cuda.synchronize()
+    nv = int(np.sum(labels != -100))
+    if nv:
+        assert abs(loss.item() + host(lp).sum() / nv) <= 1e-5 * abs(loss.item()) + 1e-6

@@ -105,3 +105,22 @@ def test_layer_zero_b_gives_zero_dA(gpu):
     for i in range(4):
         assert torch.count_nonzero(lp.view(lp.grad, 0, i, "A")) == 0
         assert torch.count_nonzero(lp.view(lp.grad, 0, i, "B")) > 0
+
+
+def test_layer_adapters_off(gpu):
+    """lora = NULL runs the frozen base alone: the oracle's adapter-off layer,
+    and bit for bit the GPU layer with every B = 0."""
+    from layer_streamed_lora_amd import model as M
+    shape, batch, seq = dataclasses.replace(SMALL_LAYER_BF16, qkv_bias=True), 2, 72
+    M_, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 45)
+    X = dev_bf16(x)
+    off = M.decoder_layer_fwd(cfg, blob, None, X, batch, seq)
+    lp0 = M.LoraParams(shape, 1)
+    lp0.set_from(0, {k: (np.zeros_like(v) if k.startswith("B_") else v) for k, v in lora.items()})
+    zero_b = M.decoder_layer_fwd(cfg, blob, lp0.lora_set(0), X, batch, seq)
+    torch.cuda.synchronize()
+    assert torch.equal(off, zero_b)
+    wd = {"norm1": w["norm1"].astype(np.float64), "norm2": w["norm2"].astype(np.float64)}
+    wd.update(oracle_layer_weights(w, shape))
+    ref, _ = O.decoder_layer_fwd(x.astype(np.float64), wd, None, shape, batch, seq)
+    assert_close_chain(host(off), ref, "adapter-off layer out")

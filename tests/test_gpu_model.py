@@ -190,3 +190,52 @@ def test_streamed_equals_resident_llama8b_rope_scaled(gpu):
     from synth.configs import LLAMA31_ROPE_SCALING
     _streamed_vs_resident(dataclasses.replace(LLAMA8B_LAYER, rope_scaling=LLAMA31_ROPE_SCALING), 32, 128256, False,
                           1, 1024, 1, 8)
+
+
+@pytest.mark.parametrize("shape,tied", [(SMALL_NF4, False), (SMALL_BF16_BIAS, True)])
+def test_reference_logprobs_match_oracle(gpu, shape, tied):
+    """Adapter-off streamed forward + per-token log-probabilities against the
+    oracle's reference forward (the adapters of the model are ignored)."""
+    from oracle.model import reference_logprobs
+    n_layers, vocab, batch, seq, n_micro, wid = 4, 640, 2, 40, 2, 72
+    m, weights, loras, (emb, fn, lm) = build(shape, n_layers, vocab, tied, batch, seq, "streamed", wid)
+    chunks = ids_for(vocab, batch, seq, n_micro, wid)
+    loads0 = m.loads
+    lp, slp = m.reference_logprobs(m.prepare_inputs(chunks))
+    torch.cuda.synchronize()
+    # every layer once per microbatch (a sweep ends holding layers L-2 and L-1, and the next starts at 0)
+    assert m.loads - loads0 == n_micro * n_layers
+    layer_w = []
+    for l in range(n_layers):
+        wd = {"norm1": weights[l]["norm1"].astype(np.float64), "norm2": weights[l]["norm2"].astype(np.float64)}
+        wd.update(oracle_layer_weights(weights[l], shape))
+        layer_w.append(wd)
+    for i, ids in enumerate(chunks):
+        ref, sref = reference_logprobs(ids, emb.astype(np.float64), fn.astype(np.float64),
+                                       None if tied else lm.astype(np.float64), layer_w, shape, batch, seq)
+        got = host(lp[i])
+        # a chain of bf16 rounding points (every layer) precedes the scores: normwise and RMS-scaled bound
+        assert_close_chain(got, ref, f"reference logp microbatch {i}")
+        assert np.all(got.reshape(batch, seq)[:, -1] == 0)
+        assert np.allclose(host(slp[i]), got.reshape(batch, seq).sum(1), rtol=1e-5)
+
+
+def test_reference_logprobs_streamed_equals_resident_llama8b(gpu):
+    """The adapter-off forward of the Llama-3.1-8B-shaped NF4 model, streamed
+    (32 copies) and resident, gives identical bits; B = 0 adapters give the
+    same scores through the training forward's loss."""
+    import dataclasses
+    s = _streamed_vs_resident(LLAMA8B_LAYER, 32, 128256, False, 1, 1024, 1, 5)
+    from layer_streamed_lora_amd.trainer import StreamedLoraModel
+    r = StreamedLoraModel(LLAMA8B_LAYER, 32, 128256, False, 1, 1024, mode="resident")
+    r.copy_base_from(s)
+    chunks = ids_for(128256, 1, 1024, 1, 9)
+    loads0 = s.loads
+    lps, slps = s.reference_logprobs(s.prepare_inputs(chunks))
+    lpr, slpr = r.reference_logprobs(r.prepare_inputs(chunks))
+    torch.cuda.synchronize()
+    assert torch.equal(lps, lpr) and torch.equal(slps, slpr)
+    # after the training step the slots hold layers 1 and 0, which the sweep reuses
+    assert s.loads - loads0 == 32 - 2
+    v = host(lps)[0, :-1]
+    assert np.all(v < 0) and abs(-v.mean() - np.log(128256)) < 1.0
