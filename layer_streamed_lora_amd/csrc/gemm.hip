@@ -330,6 +330,80 @@ LSL_DEV void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   tm = t - tn * tiles_m;
 }
 
+// y[m][n .. n + 3] = bf16(v (+ bias)) (+ residual, rounded again)
+LSL_DEV void store_bf16x4(const GemmKArgs& a, int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
+  if (a.bias) {
+    const u32x2 b = *reinterpret_cast<const u32x2*>(a.bias + n);
+    v0 += lo_bf(b[0]); v1 += hi_bf(b[0]); v2 += lo_bf(b[1]); v3 += hi_bf(b[1]);
+  }
+  if (a.res) {
+    u32x2 r = *reinterpret_cast<const u32x2*>(a.res + m * a.ldres + n);
+    v0 = bf2f(f2bf(v0)) + lo_bf(r[0]);
+    v1 = bf2f(f2bf(v1)) + hi_bf(r[0]);
+    v2 = bf2f(f2bf(v2)) + lo_bf(r[1]);
+    v3 = bf2f(f2bf(v3)) + hi_bf(r[1]);
+  }
+  *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(v0, v1), pack2(v2, v3)};
+}
+
+// split-K: the float32 partial of this split (gemm_split_reduce adds the splits).
+// Block (ni, mi), q < 4: the lane holds C[m][n .. n + 3], m = mb + 32 mi, n = nb + 32 ni + 8 q.
+template <int MI>
+LSL_DEV void store_split_partials(const GemmKArgs& a, const f32x16 (&acc)[2][MI], int64_t mb, int64_t nb, int split) {
+  float* dst = a.spart + (int64_t)split * a.M * a.N;
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int64_t m = mb + mi * 32;
+      if (m >= a.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = nb + ni * 32 + 8 * q;
+        if (n < a.N)
+          *reinterpret_cast<f32x4*>(dst + m * a.N + n) =
+              f32x4{acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2], acc[ni][mi][4 * q + 3]};
+      }
+    }
+}
+
+// LoRA K-step operands in LDS ([rows][LDSW], k zero padded to 64): Ls = the
+// A-side rows m0.. of la; Lt[n][j] = B[n][j % r] if j / r is the projection
+// owning column n (LORA 1, forward), or A_full[j][n] (LORA 2, input gradient).
+template <int LORA, int BN, int BM>
+LSL_DEV void lora_stage(const GemmKArgs& a, uint16_t* Ls, uint16_t* Lt, int64_t m0, int64_t n0, int tid) {
+  for (int c = tid; c < BM * 8; c += NTHREADS) {
+    int row = c >> 3, col = (c & 7) * 8;
+    int64_t gm = m0 + row;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (gm < a.M && col < a.kl) v = *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col);
+    *reinterpret_cast<u32x4*>(Ls + row * LDSW + col) = v;
+  }
+  if constexpr (LORA == 1) {
+    // Lt[n][j] = B[n][j % r] if j / r is the projection owning column n
+    for (int c = tid; c < BN * 64; c += NTHREADS) {
+      int row = c >> 6, j = c & 63;
+      int64_t gn = n0 + row;
+      uint16_t v = 0;
+      if (gn < a.N && j < a.kl) {
+        int seg = 0;
+        while (seg < a.nseg - 1 && gn >= a.seg_end[seg]) ++seg;
+        if (j / a.r == seg) v = a.lb[gn * a.r + (j % a.r)];
+      }
+      Lt[row * LDSW + j] = v;
+    }
+  } else {
+    // Lt[n][j] = A_full[j][n]
+    for (int c = tid; c < BN * 64; c += NTHREADS) {
+      int j = c / BN, row = c % BN;
+      int64_t gn = n0 + row;
+      uint16_t v = 0;
+      if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
+      Lt[row * LDSW + j] = v;
+    }
+  }
+}
+
 template <int WFMT, bool KN, int LORA, int EPI, int BN, int BM>
 __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const GemmKArgs a) {
   using G = Geo<BN, BM>;
@@ -370,36 +444,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   if constexpr (LORA != 0) if (split == 0) {
     uint16_t* Ls = Xs[0];
     uint16_t* Lt = Ws[0];
-    for (int c = tid; c < BM * 8; c += NTHREADS) {
-      int row = c >> 3, col = (c & 7) * 8;
-      int64_t gm = m0 + row;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (gm < a.M && col < a.kl) v = *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col);
-      *reinterpret_cast<u32x4*>(Ls + row * LDSW + col) = v;
-    }
-    if constexpr (LORA == 1) {
-      // Lt[n][j] = B[n][j % r] if j / r is the projection owning column n
-      for (int c = tid; c < BN * 64; c += NTHREADS) {
-        int row = c >> 6, j = c & 63;
-        int64_t gn = n0 + row;
-        uint16_t v = 0;
-        if (gn < a.N && j < a.kl) {
-          int seg = 0;
-          while (seg < a.nseg - 1 && gn >= a.seg_end[seg]) ++seg;
-          if (j / a.r == seg) v = a.lb[gn * a.r + (j % a.r)];
-        }
-        Lt[row * LDSW + j] = v;
-      }
-    } else {
-      // Lt[n][j] = A_full[j][n]
-      for (int c = tid; c < BN * 64; c += NTHREADS) {
-        int j = c / BN, row = c % BN;
-        int64_t gn = n0 + row;
-        uint16_t v = 0;
-        if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
-        Lt[row * LDSW + j] = v;
-      }
-    }
+    lora_stage<LORA, BN, BM>(a, Ls, Lt, m0, n0, tid);
     __syncthreads();
     mma_tile<MI>(Lt, Ls, acc, wn, wm0, lane, (a.kl + 15) / 16);
 #pragma unroll
@@ -543,22 +588,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
     return;
   }
   if (EPI == EPI_BF16 && a.ksplit > 1) {
-    // split-K: float32 partial of this split; gemm_split_reduce adds the splits
-    float* dst = a.spart + (int64_t)split * a.M * a.N;
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int64_t m = mb + mi * 32;
-        if (m >= a.M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = nb + ni * 32 + 8 * q;
-          if (n < a.N)
-            *reinterpret_cast<f32x4*>(dst + m * a.N + n) =
-                f32x4{acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2], acc[ni][mi][4 * q + 3]};
-        }
-      }
+    store_split_partials<MI>(a, acc, mb, nb, split);
     return;
   }
 #pragma unroll
@@ -596,18 +626,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
         *reinterpret_cast<f32x4*>(o) = r;
         if (a.y) *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
       } else {
-        if (a.bias) {
-          const u32x2 b = *reinterpret_cast<const u32x2*>(a.bias + n);
-          v0 += lo_bf(b[0]); v1 += hi_bf(b[0]); v2 += lo_bf(b[1]); v3 += hi_bf(b[1]);
-        }
-        if (a.res) {
-          u32x2 r = *reinterpret_cast<const u32x2*>(a.res + m * a.ldres + n);
-          v0 = bf2f(f2bf(v0)) + lo_bf(r[0]);
-          v1 = bf2f(f2bf(v1)) + hi_bf(r[0]);
-          v2 = bf2f(f2bf(v2)) + lo_bf(r[1]);
-          v3 = bf2f(f2bf(v3)) + hi_bf(r[1]);
-        }
-        *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(v0, v1), pack2(v2, v3)};
+        store_bf16x4(a, m, n, v0, v1, v2, v3);
       }
     }
   }

@@ -65,6 +65,7 @@ def _run_and_compare(gpu, shape, batch, seq, wid):
     (dataclasses.replace(SMALL_LAYER_BF16, qkv_bias=True, rope_scaling=(8.0, 1.0, 4.0, 64.0)), 1, 150),
     # NF4 with Llama-3.1's published RoPE scaling
     (dataclasses.replace(SMALL_LAYER_NF4, rope_scaling=LLAMA31_ROPE_SCALING), 2, 40),
+    (SMALL_LAYER_NF4, 2, 600),    # 1200 tokens: 256-token GEMM tiles, one of them ragged
 ])
 def test_layer_parity_small(gpu, shape, batch, seq):
     _run_and_compare(gpu, shape, batch, seq, 41)

@@ -84,6 +84,10 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1, 64, 64, 8, "nf4"),            # a single token, smallest shapes
     (200, 320, 448, 16, "nf4dq"),     # double-quantized absmax, short last 256-block
     (96, 1024, 1600, 8, "nf4dq"),
+    # from 1024 tokens on, the GEMM tiles take 256 tokens:
+    (1024, 512, 768, 16, "nf4"),      # whole token tiles
+    (1300, 320, 448, 16, "nf4dq"),    # ragged tokens and weight rows
+    (1024, 4096, 1024, 8, "nf4"),     # few output tiles: split-K, reduce in split order
     (300, 1024, 1152, 16, "bf16"),
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
