@@ -290,6 +290,23 @@ def _grid_items(r):
     return int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
 
 
+def hbm_kernels(shape, ms):
+    """Bandwidth-bound kernels of one step at the workload's shapes: (kernel name
+    prefix in the trace, algorithmic HBM bytes per launch, what they are)."""
+    from synth.configs import PROJ_IN_OUT
+    T, H, I = ms.batch * ms.seq, shape.hidden, shape.inter
+    nq, nkv, d = shape.n_q, shape.n_kv, shape.head_dim
+    n_params = ms.n_layers * sum(shape.lora_r * (fin + fout) for fin, fout in PROJ_IN_OUT(shape).values())
+    return [
+        ("lsl::rmsnorm_fwd_kernel", 2 * T * H * 2 + 2 * H, "x read, y written, bf16 [T x H]"),
+        ("lsl::rmsnorm_bwd_kernel", 4 * T * H * 2 + 2 * H, "x, dy, residual gradient read, dx written"),
+        ("lsl::swiglu_fwd_kernel", 3 * T * I * 2, "gate|up read, a written"),
+        ("lsl::swiglu_bwd_kernel", 5 * T * I * 2, "gate|up and da read, dgate|dup written"),
+        ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2 // 2, "q or k heads read and written in place (mean of the two)"),
+        ("lsl::adamw_kernel", n_params * (4 * 4 + 3 * 4 + 2), "master, grad, m, v read; master, m, v, bf16 copy written"),
+    ]
+
+
 def summarize_trace(d, args):
     """Markdown summary of a `rocprofv3 --kernel-trace --stats -f csv` run: the
     top kernels by total time, and the timed GEMM's dispatches (by grid)."""
@@ -308,6 +325,17 @@ def summarize_trace(d, args):
     if durs:
         out.append(f"gate|up forward GEMM dispatches (gemm_kernel, {g} work-items): {len(durs)} calls, "
                    f"average {sum(durs) / len(durs):.1f} us, min {min(durs):.1f} us, max {max(durs):.1f} us")
+    # bandwidth-bound kernels: algorithmic bytes / average duration against the 8 TB/s HBM peak
+    out += ["", "| bandwidth-bound kernel | calls | avg us | algorithmic bytes per launch | GB/s | of 8 TB/s | bytes |",
+            "|---|---:|---:|---:|---:|---:|---|"]
+    for prefix, nbytes, what in hbm_kernels(shape, ms):
+        ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+              if r["Kernel_Name"].startswith(prefix)]
+        if not ds:
+            continue
+        avg = sum(ds) / len(ds)
+        gbs = nbytes / (avg * 1e-6) / 1e9
+        out.append(f"| `{prefix}` | {len(ds)} | {avg:.1f} | {nbytes:,} | {gbs:.0f} | {gbs / 8000:.2f} | {what} |")
     print("\n".join(out))
 
 

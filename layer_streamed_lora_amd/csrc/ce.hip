@@ -30,6 +30,7 @@ static int ce_acc_splits(int64_t T, int64_t H, int64_t vc) {
   gemm_tile_shape(T, H, bn, bm);
   const int64_t tiles = ((T + bm - 1) / bm) * ((H + bn - 1) / bn);
   const int64_t steps = vc / 64;
+  if (tiles == 0) return 1;  // no tokens
   int64_t S = (768 + tiles - 1) / tiles;
   if (S > steps / 32) S = steps / 32;
   return S < 1 ? 1 : (int)S;

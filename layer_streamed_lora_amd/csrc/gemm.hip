@@ -743,6 +743,7 @@ int gemm_splits(int64_t M, int64_t N, int64_t K) {
   gemm_tile_shape(M, N, bn, bm);
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t steps = K / BK;
+  if (tiles == 0) return 1;  // empty output
   int64_t S = (LSL_SPLIT_TARGET + tiles - 1) / tiles;
   if (S > steps / LSL_SPLIT_MIN_STEPS) S = steps / LSL_SPLIT_MIN_STEPS;
   if (S < 2) return 1;

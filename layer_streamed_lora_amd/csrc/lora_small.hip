@@ -272,6 +272,7 @@ __global__ void tn_reduce_dB_kernel(const float* __restrict__ part, int S, int64
 // Splits of the reduction so that about `target_blocks` workgroups run, each
 // taking at least `min_steps` 64-wide steps of the reduction.
 static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks, int64_t min_steps) {
+  if (tiles <= 0) return 1;  // empty output
   int64_t steps = (red + 63) / 64;
   int64_t s = (target_blocks + tiles - 1) / tiles;
   int64_t cap = steps / min_steps;
@@ -291,6 +292,7 @@ constexpr int64_t NT_TARGET = 256, NT_MIN_STEPS = 4, TN_TARGET = 256, TN_MIN_STE
 #endif
 static int nt_splits(int64_t T, int64_t K) {
   const int64_t tiles = (T + 63) / 64;
+  if (tiles == 0) return 1;  // no tokens
   int64_t S = (LSL_NT_BLOCKS + tiles - 1) / tiles;
   if (S > K / LSL_NT_MIN_K) S = K / LSL_NT_MIN_K;
   return S < 1 ? 1 : (int)S;

@@ -178,3 +178,20 @@ def test_fidelity_options_validation_and_layout(L):
     assert lib.lora_linear_fwd(256, 8, C.byref(w), 256, 256, 8, 2.0, 256, 256, None, 0, None) == _abi.LSL_ERR_INVALID_ARG
     # scaling off (NULL or factor 0) is accepted with an empty input
     assert lib.lsl_rope(None, 0, 128, 1, 128, 4, 1e4, None, 0, None) == _abi.LSL_OK
+
+
+def test_workspace_queries_with_zero_tokens(L):
+    """Workspace sizing with no tokens (batch 0 or seq 0) is defined and does not
+    divide by an empty tile count."""
+    from layer_streamed_lora_amd import _abi
+    from layer_streamed_lora_amd import model as M
+    from synth.configs import LLAMA8B_LAYER, QWEN05B_LAYER
+    lib = L.lib()
+    for shape in (LLAMA8B_LAYER, QWEN05B_LAYER):
+        cfg = M.layer_cfg(shape)
+        for batch, seq in ((0, 16), (4, 0), (0, 0)):
+            for mode in (_abi.MODE_FWD, _abi.MODE_BWD):
+                assert lib.lsl_layer_workspace_bytes(C.byref(cfg), batch, seq, mode) >= 0
+    assert lib.lsl_ce_workspace_bytes(0, 4096, 128256) > 0
+    assert L.lora_linear_workspace_bytes(0, 4096, 4096, 16) >= 0
+    assert lib.lsl_attention_workspace_bytes(0, 0, 32, 8, 128) >= 0

@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
     (1, 96, 8, 1, 128),     # group of 8 (Qwen2.5-3B: 16 q / 2 kv heads)
     (1, 512, 32, 8, 128),   # one Llama-3.1-8B layer at seq 512
     (3, 1, 4, 2, 64),       # one token per sequence
+    (1, 2048, 8, 2, 128),   # a long sequence: 32 key tiles in the backward
 ])
 def test_attention_parity(gpu, batch, seq, nq, nkv, d):
     T = batch * seq

@@ -89,6 +89,8 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1300, 320, 448, 16, "nf4dq"),    # ragged tokens and weight rows
     (1024, 4096, 1024, 8, "nf4"),     # few output tiles: split-K, reduce in split order
     (300, 1024, 1152, 16, "bf16"),
+    (128, 512, 256, 64, "bf16"),      # the largest rank of the linear API
+    (64, 256, 384, 64, "nf4"),
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
