@@ -15,7 +15,10 @@
 
 namespace lsl {
 
-constexpr int64_t CE_CHUNK = 16384;  // vocabulary columns per backward chunk
+#ifndef LSL_CE_CHUNK
+#define LSL_CE_CHUNK 32768
+#endif
+constexpr int64_t CE_CHUNK = LSL_CE_CHUNK;  // vocabulary columns per backward chunk
 
 struct CePlan {
   size_t nvalid, part, zlab, lossv, lse, g, dh32, total;

@@ -21,7 +21,8 @@ def _case(T, H, V, wid, n_ignore=3):
 
 
 @pytest.mark.parametrize("T,H,V,gs", [
-    (100, 128, 16576, 1.0),     # three vocabulary chunks, the last one partial; ragged T
+    (100, 128, 69952, 1.0),     # three vocabulary chunks of the backward, the last one partial; ragged T
+    (100, 128, 16576, 1.0),     # one chunk, a partial vocabulary tile
     (37, 256, 1088, 0.25),      # one chunk with a partial vocabulary tile, a gradient scale
     (1, 64, 64, 1.0),
 ])
