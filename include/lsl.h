@@ -155,7 +155,9 @@ lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, const uint16_t*
  * optionally rescaled, rope_scaling), positions restarting at 0 in each sequence;
  * optional frozen q/k/v bias; LoRA on all seven projections.
  * The pages stream exactly these "decoder layers" ("Soup CLI ...", section "How
- * Layer Streaming Works").
+ * Layer Streaming Works"). Supported: hidden and inter multiples of 64, hidden
+ * at most 8192, head_dim 64 or 128, at most 8 query heads per kv head, LoRA
+ * rank 8 or 16 (UNSUPPORTED otherwise).
  */
 /* RoPE frequency scaling of Llama-3.1 checkpoints (their published rope_type
  * "llama3" configuration: 8, 1, 4, 8192). With f = theta^(-2i/d) and
@@ -306,7 +308,7 @@ lsl_status fused_ce_logprobs(const uint16_t* hN, const uint16_t* w_lm, const int
 /* ------------------------------------------------------------------ support ops
  * The individual steps of the decoder layer, exported so each can be checked on
  * its own (same kernels the layer calls). */
-/* y = bf16(x / sqrt(mean(x^2) + eps) * w), x, y [T x H]. */
+/* y = bf16(x / sqrt(mean(x^2) + eps) * w), x, y [T x H], H a multiple of 8, at most 8192. */
 lsl_status lsl_rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps,
                            uint16_t* y, lsl_stream stream);
 /* dx = bf16(dres + r (w dy - xh mean(xh w dy))), xh = x r; dres may be NULL. */
@@ -315,7 +317,8 @@ lsl_status lsl_rmsnorm_bwd(const uint16_t* x, const uint16_t* w, const uint16_t*
                            lsl_stream stream);
 /* In-place rotate-half RoPE on x [T rows, row stride ld elements], heads
  * [n_heads x head_dim] starting at column 0 of each row; position = row % seq.
- * inverse != 0 rotates by -angle (the backward). scaling may be NULL (none). */
+ * inverse != 0 rotates by -angle (the backward). scaling may be NULL (none).
+ * head_dim a multiple of 8, at most 128; ld a multiple of 4. */
 lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_heads, int32_t head_dim,
                     int32_t seq, float theta, const lsl_rope_scaling* scaling, int32_t inverse,
                     lsl_stream stream);

@@ -73,6 +73,7 @@ static lsl_status check_cfg(const lsl_layer_cfg* c, const char* fn) {
   if (c->n_q / c->n_kv > 8) return set_error(LSL_ERR_UNSUPPORTED, "%s: more than 8 query heads per kv head", fn);
   if (c->hidden % 64 || c->inter % 64)
     return set_error(LSL_ERR_UNSUPPORTED, "%s: hidden and inter must be multiples of 64", fn);
+  if (c->hidden > 8192) return set_error(LSL_ERR_UNSUPPORTED, "%s: hidden %d > 8192", fn, c->hidden);
   if (c->lora_r != 8 && c->lora_r != 16)
     return set_error(LSL_ERR_UNSUPPORTED, "%s: fused layer supports LoRA rank 8 or 16 (got %d)", fn, c->lora_r);
   if (c->wfmt != LSL_WFMT_NF4 && c->wfmt != LSL_WFMT_BF16 && c->wfmt != LSL_WFMT_NF4DQ)

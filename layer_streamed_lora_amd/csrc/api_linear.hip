@@ -152,6 +152,8 @@ extern "C" lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_hea
   if (T < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 || seq <= 0 || ld < (int64_t)n_heads * head_dim ||
       !(theta > 0.f))
     return set_error(LSL_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (head_dim % 8 || head_dim > 128 || ld % 4)
+    return set_error(LSL_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 8 up to 128 and ld of 4", fn);
   LSL_TRY(check_rope_scaling(fn, scaling));
   if (T == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x}));

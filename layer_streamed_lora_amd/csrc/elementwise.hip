@@ -8,32 +8,47 @@
 namespace lsl {
 
 // ---------------------------------------------------------------- RMSNorm
-// y = bf16(x * r * w), r = 1 / sqrt(mean(x^2) + eps). One wave per row.
+// One wave per row. The forward holds the lane's 16-byte chunks of the row
+// (chunk c of lane L covers columns 8 (L + 64 c) .. + 7) in registers, so the
+// row is read from HBM once and all of its loads are in flight together (rows
+// up to 512 RMS_CHUNKS columns).
+constexpr int RMS_CHUNKS = 16;
+
+// y = bf16(x * r * w), r = 1 / sqrt(mean(x^2) + eps)
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                           int64_t T, int64_t H, float eps, uint16_t* __restrict__ y) {
   int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (row >= T) return;
   const uint16_t* xr = x + row * H;
-  float ss = 0.f;
-  for (int64_t c = lane * 8; c < H; c += 512) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+  u32x4 v[RMS_CHUNKS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { float a = lo_bf(v[j]), b = hi_bf(v[j]); ss += a * a + b * b; }
+  for (int c = 0; c < RMS_CHUNKS; ++c) {
+    const int64_t col = (int64_t)(lane + 64 * c) * 8;
+    if (col < H) v[c] = *reinterpret_cast<const u32x4*>(xr + col);
   }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < RMS_CHUNKS; ++c)
+    if ((int64_t)(lane + 64 * c) * 8 < H)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { float a = lo_bf(v[c][j]), b = hi_bf(v[c][j]); ss += a * a + b * b; }
   ss = wave_sum(ss);
   float r = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int64_t c = lane * 8; c < H; c += 512) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    u32x4 g = *reinterpret_cast<const u32x4*>(w + c);
+#pragma unroll
+  for (int c = 0; c < RMS_CHUNKS; ++c) {
+    const int64_t col = (int64_t)(lane + 64 * c) * 8;
+    if (col >= H) continue;
+    u32x4 g = *reinterpret_cast<const u32x4*>(w + col);
     u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = pack2(lo_bf(v[j]) * r * lo_bf(g[j]), hi_bf(v[j]) * r * hi_bf(g[j]));
-    *reinterpret_cast<u32x4*>(y + row * H + c) = o;
+    for (int j = 0; j < 4; ++j) o[j] = pack2(lo_bf(v[c][j]) * r * lo_bf(g[j]), hi_bf(v[c][j]) * r * hi_bf(g[j]));
+    *reinterpret_cast<u32x4*>(y + row * H + col) = o;
   }
 }
 
-// dx = bf16(dres + r (w dy - x r^2 sum(x w dy) / H))
+// dx = bf16(dres + r (w dy - x r^2 sum(x w dy) / H)). Two passes over the row
+// (the second from L2): holding x and dy in registers would halve occupancy.
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                           const uint16_t* __restrict__ dy, const uint16_t* __restrict__ dres,
                                                           int64_t T, int64_t H, float eps, uint16_t* __restrict__ dx) {
@@ -75,6 +90,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
 }
 
 lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y, hipStream_t s) {
+  if (H > 512 * RMS_CHUNKS) return set_error(LSL_ERR_UNSUPPORTED, "rmsnorm: hidden %lld > %d", (long long)H, 512 * RMS_CHUNKS);
   if (T == 0) return LSL_OK;
   hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, w, T, H, eps, y);
   return check_launch("rmsnorm_fwd");
@@ -87,55 +103,87 @@ lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16
 }
 
 // ---------------------------------------------------------------- RoPE
-// Thread per (row, frequency index i); the inverse frequency theta^(-2i/d)
-// (optionally rescaled the Llama-3.1 way), the angle and its sine/cosine are
-// evaluated in float64, then every head's pair (i, i + d/2) is rotated in
-// float32 and rounded to bf16 in place.
-struct RopeScale {
-  double factor, low, high, orig;  // factor 0: none
+// The inverse frequencies theta^(-2i/d) (optionally rescaled the Llama-3.1 way)
+// are computed on the host in float64 and passed by value. A workgroup takes
+// ROPE_ROWS rows: first the float64 angle and its sine/cosine for each
+// (row, i) into LDS, then every head's pairs (i, i + d/2) of those rows are
+// rotated in float32 four at a time (8-byte accesses) and rounded to bf16 in
+// place.
+struct RopeFreq {
+  double inv[64];  // head_dim / 2 <= 64
 };
 
-LSL_DEV double rope_inv_freq(int i, int head_dim, double theta, const RopeScale& sc) {
-  const double f = pow(theta, -2.0 * (double)i / (double)head_dim);
-  if (sc.factor == 0.0) return f;
-  const double wavelen = 2.0 * 3.141592653589793 / f;
-  if (wavelen < sc.orig / sc.high) return f;
-  if (wavelen > sc.orig / sc.low) return f / sc.factor;
-  const double m = (sc.orig / wavelen - sc.low) / (sc.high - sc.low);
-  return (1.0 - m) * f / sc.factor + m * f;
+static RopeFreq rope_freq(int head_dim, double theta, const lsl_rope_scaling* sc) {
+  RopeFreq fr{};
+  const double pi = 3.141592653589793;
+  for (int i = 0; i < head_dim / 2; ++i) {
+    double f = std::pow(theta, -2.0 * (double)i / (double)head_dim);
+    if (sc && sc->factor != 0.f) {
+      const double factor = sc->factor, low = sc->low_freq_factor, high = sc->high_freq_factor;
+      const double orig = sc->original_max_position;
+      const double wavelen = 2.0 * pi / f;
+      if (wavelen > orig / low) {
+        f = f / factor;
+      } else if (wavelen >= orig / high) {
+        const double m = (orig / wavelen - low) / (high - low);
+        f = (1.0 - m) * f / factor + m * f;
+      }
+    }
+    fr.inv[i] = f;
+  }
+  return fr;
 }
 
-__global__ void rope_kernel(uint16_t* __restrict__ x, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,
-                            double theta, RopeScale sc, int inverse) {
-  int half = head_dim >> 1;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * half) return;
-  int64_t row = idx / half;
-  int i = (int)(idx - row * half);
-  int pos = (int)(row % seq);
-  double ang = (double)pos * rope_inv_freq(i, head_dim, theta, sc);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  float c = (float)cd, sn = inverse ? -(float)sd : (float)sd;
-  uint16_t* xr = x + row * ld;
-  for (int h = 0; h < n_heads; ++h) {
-    uint16_t* p = xr + (int64_t)h * head_dim;
-    float x1 = bf2f(p[i]), x2 = bf2f(p[i + half]);
-    p[i] = f2bf(x1 * c - x2 * sn);
-    p[i + half] = f2bf(x2 * c + x1 * sn);
+constexpr int ROPE_ROWS = 4;
+
+__global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int64_t T, int64_t ld, int n_heads,
+                                                   int head_dim, int seq, RopeFreq fr, int inverse) {
+  __shared__ float cs[ROPE_ROWS][64], sn[ROPE_ROWS][64];
+  const int half = head_dim >> 1;
+  const int64_t r0 = (int64_t)blockIdx.x * ROPE_ROWS;
+  for (int t = threadIdx.x; t < ROPE_ROWS * half; t += blockDim.x) {
+    const int rr = t / half, i = t - rr * half;
+    const int64_t row = r0 + rr;
+    if (row >= T) continue;
+    const double ang = (double)(row % seq) * fr.inv[i];
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    cs[rr][i] = (float)cd;
+    sn[rr][i] = inverse ? -(float)sd : (float)sd;
+  }
+  __syncthreads();
+  const int q4 = half >> 2;          // groups of 4 pairs per head
+  const int per_row = n_heads * q4;
+  for (int t = threadIdx.x; t < ROPE_ROWS * per_row; t += blockDim.x) {
+    const int rr = t / per_row, rem = t - rr * per_row;
+    const int h = rem / q4, g = rem - h * q4;
+    const int64_t row = r0 + rr;
+    if (row >= T) continue;
+    uint16_t* p = x + row * ld + (int64_t)h * head_dim + 4 * g;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + half);
+    float x1[4] = {lo_bf(a[0]), hi_bf(a[0]), lo_bf(a[1]), hi_bf(a[1])};
+    float x2[4] = {lo_bf(b[0]), hi_bf(b[0]), lo_bf(b[1]), hi_bf(b[1])};
+    float o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = cs[rr][4 * g + e], s = sn[rr][4 * g + e];
+      o1[e] = x1[e] * c - x2[e] * s;
+      o2[e] = x2[e] * c + x1[e] * s;
+    }
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack2(o1[0], o1[1]), pack2(o1[2], o1[3])};
+    *reinterpret_cast<u32x2*>(p + half) = u32x2{pack2(o2[0], o2[1]), pack2(o2[2], o2[3])};
   }
 }
 
 lsl_status rope_launch(uint16_t* x, int64_t T, int64_t ld, int n_heads, int head_dim, int seq, float theta,
                        const lsl_rope_scaling* scaling, int inverse, hipStream_t s) {
+  if (head_dim % 8 || head_dim > 128)
+    return set_error(LSL_ERR_UNSUPPORTED, "rope: head_dim %d (a multiple of 8, at most 128)", head_dim);
   if (T == 0) return LSL_OK;
-  int64_t n = T * (head_dim / 2);
-  RopeScale sc{0.0, 0.0, 0.0, 0.0};
-  if (scaling && scaling->factor != 0.f)
-    sc = RopeScale{scaling->factor, scaling->low_freq_factor, scaling->high_freq_factor,
-                   scaling->original_max_position};
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, T, ld, n_heads, head_dim,
-                     seq, (double)theta, sc, inverse);
+  const RopeFreq fr = rope_freq(head_dim, (double)theta, scaling);
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((T + ROPE_ROWS - 1) / ROPE_ROWS)), dim3(256), 0, s, x, T, ld,
+                     n_heads, head_dim, seq, fr, inverse);
   return check_launch("rope");
 }
 
