@@ -341,7 +341,7 @@ def summarize_trace(d, args):
 
 def summarize_copies(d, args):
     """Copy-engine timeline of a `rocprofv3 --kernel-trace --memory-copy-trace`
-    run of `bench.py --no-resident --steps K`: for each of the K timed steps
+    run of `bench.py --no-resident --no-reference --steps K`: for each of the K timed steps
     (the layer copies before the final statistics step), copy-engine busy time,
     the idle gap at the turn of the sweep and at the step boundary, and the
     kernel time inside each gap."""
@@ -414,6 +414,7 @@ def main():
     ap.add_argument("--no-resident", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-nf4dq", action="store_true", help="skip the double-quantized-absmax variant")
+    ap.add_argument("--no-reference", action="store_true", help="skip the adapter-off reference forward")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain copy kernel of known size first (for scaling HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="summarise a rocprofv3 kernel-trace csv run and exit")
@@ -478,8 +479,10 @@ def main():
     if r_model is not None:
         resident = time_steps(r_model, inputs, args.steps, args.warmup)
         log(f"  resident: {resident['ms_per_step']:.2f} ms/step")
-    reference = time_reference(s_model, inputs, args.steps, args.warmup)
-    log(f"  reference forward (adapters off, streamed): {reference['ms']:.2f} ms per {T * ms.n_micro} tokens")
+    reference = None
+    if not args.no_reference:
+        reference = time_reference(s_model, inputs, args.steps, args.warmup)
+        log(f"  reference forward (adapters off, streamed): {reference['ms']:.2f} ms per {T * ms.n_micro} tokens")
 
     variant = None
     if not args.no_nf4dq and args.workload == "llama8b_nf4":
@@ -523,10 +526,10 @@ def main():
         "bit_exact_vs_resident": bit_exact,
         "loss": round(res["loss"], 5),
         "nf4dq": variant,
-        "reference_forward": {"what": "adapter-off streamed forward + per-token log-probs (preference reference)",
-                              "ms": round(reference["ms"], 3),
-                              "tok_s": round(T * ms.n_micro / (reference["ms"] * 1e-3), 2),
-                              "layer_copies": reference["loads"], "mean_logp": round(reference["mean_logp"], 4)},
+        "reference_forward": reference and {
+            "what": "adapter-off streamed forward + per-token log-probs (preference reference)",
+            "ms": round(reference["ms"], 3), "tok_s": round(T * ms.n_micro / (reference["ms"] * 1e-3), 2),
+            "layer_copies": reference["loads"], "mean_logp": round(reference["mean_logp"], 4)},
         "context": {"pages_tok_s": 119.6, "pages_hardware": "RTX 3050 Laptop 4 GB, seq/batch not stated"},
     }
     if not args.no_cpu_baseline:
