@@ -32,10 +32,6 @@
 
 namespace lsl {
 
-#ifndef LSL_GEMM_PIPE
-#define LSL_GEMM_PIPE 0
-#endif
-constexpr int PIPE = LSL_GEMM_PIPE;  // K-loop pipeline structure (see the main loop)
 constexpr int BK = 64, LDSW = BK + 8;  // LDS row stride in elements
 constexpr int NTHREADS = 256;
 // at least two workgroups per CU: keeps each wave within 168 registers, so three
@@ -408,12 +404,12 @@ template <int WFMT, bool KN, int LORA, int EPI, int BN, int BM>
 __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const GemmKArgs a) {
   using G = Geo<BN, BM>;
   constexpr int MI = G::MI;
-  constexpr int NBUF = PIPE == 0 ? 1 : 2;
   // weight tile: [BN][LDSW] (NK), or row-major [BK][BN + 8] read transposed (KN);
-  // the LoRA step reuses buffer 0 as [BN][LDSW]
+  // the LoRA step reuses it as [BN][LDSW]. Token tile: swizzled [BM][64] (the
+  // LoRA step: [BM][LDSW]).
   constexpr int WSZ = BN * LDSW > BK * (BN + 8) ? BN * LDSW : BK * (BN + 8);
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[NBUF][WSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[NBUF][BM * LDSW];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[WSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[BM * LDSW];
   // NF4 codebook: 16 floats, so every lookup is a conflict-free broadcast read
   __shared__ float lut[16];
 
@@ -442,8 +438,8 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   // accumulators start as s * (L Lt^T), so no second set of accumulators is live
   // during the main loop
   if constexpr (LORA != 0) if (split == 0) {
-    uint16_t* Ls = Xs[0];
-    uint16_t* Lt = Ws[0];
+    uint16_t* Ls = Xs;
+    uint16_t* Lt = Ws;
     lora_stage<LORA, BN, BM>(a, Ls, Lt, m0, n0, tid);
     __syncthreads();
     mma_tile<MI>(Lt, Ls, acc, wn, wm0, lane, (a.kl + 15) / 16);
@@ -459,77 +455,32 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   // this workgroup's reduction steps [kt0, kt0 + KT)
   const int kt0 = split * a.kt_per_split;
   const int KT = min((int)(a.K / BK) - kt0, a.kt_per_split);
-  if constexpr (PIPE == 2) {
-    // tile k computes from LDS buffer k % 2 while tile k + 1 waits in registers
-    // (set (k + 1) % 2) for its LDS store and tile k + 2 is in flight
-    RowLoader<BM> xl0, xl1;
-    WLoader<WFMT, KN, BN> wl0, wl1;
-    xl0.init(a.ldx, m0, tid);
-    wl0.init(a, n0, tid);
-    xl1 = xl0;
-    wl1 = wl0;
-    xl0.load(a.x, a.ldx, a.M, (int64_t)kt0 * BK);
-    wl0.load(a, (int64_t)kt0 * BK);
-    if (KT > 1) {
-      xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + 1) * BK);
-      wl1.load(a, (int64_t)(kt0 + 1) * BK);
+  // tile k + 1 is loaded into registers while tile k computes from the single
+  // LDS buffer (two barriers per K-step; a second LDS buffer, or a second
+  // register set two tiles ahead, measured slower: fewer workgroups per CU)
+  RowLoader<BM> xl;
+  WLoader<WFMT, KN, BN> wl;
+  xl.init(a.ldx, m0, tid);
+  wl.init(a, n0, tid);
+  xl.load(a.x, a.ldx, a.M, (int64_t)kt0 * BK);
+  wl.load(a, (int64_t)kt0 * BK);
+  __syncthreads();  // lut visible
+  xstore(xl, Xs);
+  wl.store(Ws, lut, tid);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool more = kt + 1 < KT;
+    if (more) {
+      xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
+      wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
     }
-    __syncthreads();  // lut visible
-    xstore(xl0, Xs[0]);
-    wl0.store(Ws[0], lut, tid);
+    mma_tile<MI, KN, BN + 8, true>(Ws, Xs, acc, wn, wm0, lane, 4);
     __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-      if (kt + 2 < KT) {
-        xl0.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 2) * BK);
-        wl0.load(a, (int64_t)(kt0 + kt + 2) * BK);
-      }
-      mma_tile<MI, KN, BN + 8, true>(Ws[0], Xs[0], acc, wn, wm0, lane, 4);
-      if (kt + 1 < KT) {
-        xstore(xl1, Xs[1]);
-        wl1.store(Ws[1], lut, tid);
-      }
-      __syncthreads();
-      if (kt + 1 >= KT) break;
-      if (kt + 3 < KT) {
-        xl1.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 3) * BK);
-        wl1.load(a, (int64_t)(kt0 + kt + 3) * BK);
-      }
-      mma_tile<MI, KN, BN + 8, true>(Ws[1], Xs[1], acc, wn, wm0, lane, 4);
-      if (kt + 2 < KT) {
-        xstore(xl0, Xs[0]);
-        wl0.store(Ws[0], lut, tid);
-      }
-      __syncthreads();
+    if (more) {
+      xstore(xl, Xs);
+      wl.store(Ws, lut, tid);
     }
-  } else {
-    // tile k + 1 is loaded into registers while tile k computes from LDS; with
-    // PIPE == 1 LDS is double-buffered (one barrier per K-step), with PIPE == 0
-    // single-buffered (two barriers, half the LDS, more workgroups per CU)
-    RowLoader<BM> xl;
-    WLoader<WFMT, KN, BN> wl;
-    xl.init(a.ldx, m0, tid);
-    wl.init(a, n0, tid);
-    xl.load(a.x, a.ldx, a.M, (int64_t)kt0 * BK);
-    wl.load(a, (int64_t)kt0 * BK);
-    __syncthreads();  // lut visible
-    xstore(xl, Xs[0]);
-    wl.store(Ws[0], lut, tid);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = PIPE == 1 ? (kt & 1) : 0;
-      const bool more = kt + 1 < KT;
-      if (more) {
-        xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
-        wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
-      }
-      mma_tile<MI, KN, BN + 8, true>(Ws[cur], Xs[cur], acc, wn, wm0, lane, 4);
-      if constexpr (PIPE == 0) __syncthreads();
-      if (more) {
-        xstore(xl, Xs[PIPE == 1 ? cur ^ 1 : 0]);
-        wl.store(Ws[PIPE == 1 ? cur ^ 1 : 0], lut, tid);
-      }
-      __syncthreads();
-    }
   }
 
   // ---- epilogue: for block (ni, mi) and q < 4, the lane holds C[m][n .. n+3] with
@@ -539,7 +490,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
   if constexpr (EPI == EPI_LSE) {
     // Cross-entropy forward: per token m, max and sum of exp over this tile's
     // vocabulary entries n < N, and the label's logit if it falls in the tile.
-    float2* red = reinterpret_cast<float2*>(Xs[0]);  // [WN][BM]
+    float2* red = reinterpret_cast<float2*>(Xs);  // [WN][BM]
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int64_t m = mb + mi * 32;
