@@ -155,6 +155,31 @@ def time_steps(m, inputs, steps, warmup, timing_which=0, stats=False):
     return out
 
 
+def gemm_groups(m, inputs, shape, ms, steps=2):
+    """Average duration and achieved TF/s of each of the layer's eight fused
+    GEMMs (forward and input gradient of q|k|v, o, gate|up, down), LoRA K-step
+    included, timed with HIP events around each launch over `steps` steps."""
+    T, H, I, r = ms.batch * ms.seq, shape.hidden, shape.inter, shape.lora_r
+    q, kv = shape.n_q * shape.head_dim, shape.n_kv * shape.head_dim
+    mats = {"qkv": (q + 2 * kv, H, 3), "o": (H, q, 1), "gate|up": (2 * I, H, 2), "down": (H, I, 1)}
+    out = {}
+    for which in range(1, 9):
+        name = list(mats)[(which - 1) % 4]
+        n, k, nseg = mats[name]
+        if which <= 4:   # y = x W^T + s t B^T: M = T, N = n, K = k (+ kl)
+            flops = 2.0 * T * n * k + 2.0 * T * nseg * r * n
+            label = f"fwd {name} {T}x{n}x{k}"
+        else:            # dx = dy W + s u A: M = T, N = k, K = n (+ kl)
+            flops = 2.0 * T * n * k + 2.0 * T * nseg * r * k
+            label = f"dX {name} {T}x{k}x{n}"
+        res = time_steps(m, inputs, steps, 0, timing_which=which)
+        avg = res["kernel_ms_total"] / max(res["kernel_launches"], 1)
+        tf = flops / (avg * 1e-3) / 1e12
+        out[label] = {"avg_launch_ms": round(avg, 4), "TFLOP_s": round(tf, 1),
+                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def nf4dq_leg(args, T_inputs_seed):
     """The same model with double-quantized absmax (8-bit absmax codes, one
     float32 per 256): streamed step time, gate|up GEMM time and bytes moved."""
@@ -476,9 +501,12 @@ def main():
     cs = time_steps(s_model, inputs, 1, 0, stats=True)
     res.update({k: cs[k] for k in ("h2d_loads", "h2d_bytes", "h2d_copy_s") if k in cs})
     resident = None
+    gemms = None
     if r_model is not None:
         resident = time_steps(r_model, inputs, args.steps, args.warmup)
         log(f"  resident: {resident['ms_per_step']:.2f} ms/step")
+        gemms = gemm_groups(r_model, inputs, shape, ms)
+        log("  GEMMs: " + ", ".join(f"{k} {v['TFLOP_s']} TF/s" for k, v in gemms.items()))
     reference = None
     if not args.no_reference:
         reference = time_reference(s_model, inputs, args.steps, args.warmup)
@@ -515,6 +543,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(),
                      "avg_launch_ms": round(g_ms, 4), "launches": res["kernel_launches"]},
         "mfma_frac_step": round(flops / (res["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemms_resident": gemms,
         "h2d": {"achieved_GBps_copy_engine": h2d_copy and round(h2d_copy, 2),
                 "achieved_GBps_over_step": h2d_eff and round(h2d_eff, 2),
                 "pinned_peak_GBps": round(peak_h2d, 2),
