@@ -180,6 +180,34 @@ def gemm_groups(m, inputs, shape, ms, steps=2):
     return out
 
 
+def t_sweep(args, sizes=(1024, 2048, 4096, 8192, 16384)):
+    """Streamed and resident step time of the workload's model at growing token
+    counts per layer visit (batch x 1024 tokens, one microbatch): where the
+    layer copies start to hide behind compute."""
+    import dataclasses
+    import torch
+    import synth
+    from layer_streamed_lora_amd.trainer import StreamedLoraModel
+    wl, shape, ms0 = workload(args.workload)
+    rows = []
+    for T in sizes:
+        ms = dataclasses.replace(ms0, batch=T // 1024, seq=1024, n_micro=1)
+        s_model = build_model(shape, ms, "streamed")
+        r_model = StreamedLoraModel(shape, ms.n_layers, ms.vocab, ms.tied, ms.batch, ms.seq, mode="resident")
+        r_model.copy_base_from(s_model)
+        chunks = [synth.token_ids(T, ms.vocab, wl.wid, salt=0)]
+        inputs = s_model.prepare_inputs(chunks)
+        st = time_steps(s_model, inputs, args.steps, args.warmup)["ms_per_step"]
+        rt = time_steps(r_model, inputs, args.steps, args.warmup)["ms_per_step"]
+        rows.append({"tokens": T, "streamed_ms": round(st, 2), "resident_ms": round(rt, 2),
+                     "streamed_over_resident": round(st / rt, 3), "streamed_tok_s": round(T / (st * 1e-3), 1)})
+        log(f"  T {T}: streamed {st:.1f} ms, resident {rt:.1f} ms, ratio {st / rt:.2f}")
+        del s_model, r_model, inputs
+        torch.cuda.empty_cache()
+    print(json.dumps({"t_sweep": rows, "workload": args.workload, "steps": args.steps, "warmup": args.warmup}),
+          flush=True)
+
+
 def nf4dq_leg(args, T_inputs_seed):
     """The same model with double-quantized absmax (8-bit absmax codes, one
     float32 per 256): streamed step time, gate|up GEMM time and bytes moved."""
@@ -350,6 +378,21 @@ def summarize_trace(d, args):
     if durs:
         out.append(f"gate|up forward GEMM dispatches (gemm_kernel, {g} work-items): {len(durs)} calls, "
                    f"average {sum(durs) / len(durs):.1f} us, min {min(durs):.1f} us, max {max(durs):.1f} us")
+    # attention: algorithmic FLOP / average duration against the bf16 MFMA peak (causal: half the
+    # dense products; forward 2 products, dK/dV 4 (scores and dP recomputed), dQ 3)
+    half = ms.batch * shape.n_q * ms.seq * ms.seq * shape.head_dim  # 2 B nq S^2 d / 2 per product
+    out += ["", "| attention kernel | calls | avg us | algorithmic GFLOP per launch | TF/s | of bf16 peak |",
+            "|---|---:|---:|---:|---:|---:|"]
+    for prefix, nprod in (("void lsl::attn_fwd_kernel", 2), ("void lsl::attn_dkv_kernel", 4),
+                          ("void lsl::attn_dq_kernel", 3)):
+        ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+              if r["Kernel_Name"].startswith(prefix)]
+        if not ds:
+            continue
+        avg = sum(ds) / len(ds)
+        fl = nprod * half
+        out.append(f"| `{prefix[5:]}` | {len(ds)} | {avg:.1f} | {fl / 1e9:.2f} | {fl / (avg * 1e-6) / 1e12:.0f} | "
+                   f"{fl / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.2f} |")
     # bandwidth-bound kernels: algorithmic bytes / average duration against the 8 TB/s HBM peak
     out += ["", "| bandwidth-bound kernel | calls | avg us | algorithmic bytes per launch | GB/s | of 8 TB/s | bytes |",
             "|---|---:|---:|---:|---:|---:|---|"]
@@ -440,6 +483,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-nf4dq", action="store_true", help="skip the double-quantized-absmax variant")
     ap.add_argument("--no-reference", action="store_true", help="skip the adapter-off reference forward")
+    ap.add_argument("--t-sweep", action="store_true",
+                    help="streamed vs resident step time from 1k to 16k tokens per layer visit, then exit")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain copy kernel of known size first (for scaling HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="summarise a rocprofv3 kernel-trace csv run and exit")
@@ -469,6 +514,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calib_copy:
         calib_copy()
+    if args.t_sweep:
+        return t_sweep(args)
     wl, shape, ms = workload(args.workload)
     T = ms.batch * ms.seq
     log(f"building {args.workload}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.wfmt} base")
@@ -478,6 +525,16 @@ def main():
         f"store {s_model.blob_bytes * ms.n_layers / 1e9:.3f} GB pinned")
     chunks = [synth.token_ids(T, ms.vocab, wl.wid, salt=i) for i in range(ms.n_micro)]
     inputs = s_model.prepare_inputs(chunks)
+    # device memory of the streamed model: persistent buffers (2 slots, embedding,
+    # lm_head, checkpoints, adapters and their optimizer state, workspace) and the
+    # peak over one step (no optimizer update, so the state stays untouched)
+    torch.cuda.synchronize()
+    hbm_live = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    s_model.step(inputs, adamw=False)
+    torch.cuda.synchronize()
+    hbm_peak = torch.cuda.max_memory_allocated()
+    log(f"  streamed model device memory: {hbm_live / 1e9:.2f} GB allocated, {hbm_peak / 1e9:.2f} GB peak in a step")
 
     bit_exact = None
     r_model = None
@@ -553,6 +610,8 @@ def main():
                                   "tok_s": round(T * ms.n_micro / (resident["ms_per_step"] * 1e-3), 2)},
         "streamed_over_resident": resident and round(res["ms_per_step"] / resident["ms_per_step"], 3),
         "bit_exact_vs_resident": bit_exact,
+        "hbm_streamed_GB": {"allocated": round(hbm_live / 1e9, 3), "peak_in_step": round(hbm_peak / 1e9, 3),
+                            "pages_peak_vram_GB": 3.32},
         "loss": round(res["loss"], 5),
         "nf4dq": variant,
         "reference_forward": reference and {
