@@ -485,6 +485,8 @@ def main():
     ap.add_argument("--no-reference", action="store_true", help="skip the adapter-off reference forward")
     ap.add_argument("--t-sweep", action="store_true",
                     help="streamed vs resident step time from 1k to 16k tokens per layer visit, then exit")
+    ap.add_argument("--sizes", type=int, nargs="*", default=[1024, 2048, 4096, 8192, 16384],
+                    help="token counts of --t-sweep (multiples of 1024)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one plain copy kernel of known size first (for scaling HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="summarise a rocprofv3 kernel-trace csv run and exit")
@@ -515,7 +517,7 @@ def main():
     if args.calib_copy:
         calib_copy()
     if args.t_sweep:
-        return t_sweep(args)
+        return t_sweep(args, args.sizes)
     wl, shape, ms = workload(args.workload)
     T = ms.batch * ms.seq
     log(f"building {args.workload}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.wfmt} base")

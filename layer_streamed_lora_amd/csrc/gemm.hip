@@ -316,14 +316,23 @@ LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x16 (&acc)[2][M
 }
 
 // Tile index remap: XCD x (= workgroup id mod 8) gets a contiguous range of
-// tiles, ordered m-fastest so that the tiles sharing a weight tile run together.
+// tiles. The tiles go in groups of GROUP_M token tiles: within a group
+// m-fastest, so that the tiles sharing a weight tile run together, and group by
+// group, so that the token rows in use (GROUP_M x BM rows, re-read by every
+// weight tile) stay in L2/MALL however many tokens there are.
+#ifndef LSL_GROUP_M
+#define LSL_GROUP_M 2
+#endif
 LSL_DEV void tile_coords(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   int nt = tiles_m * tiles_n;
   int per = nt / 8;
   int t = b;
   if (b < per * 8) t = (b & 7) * per + (b >> 3);
-  tn = t / tiles_m;
-  tm = t - tn * tiles_m;
+  const int g = t / (LSL_GROUP_M * tiles_n);            // group of token tiles
+  const int gm = min(LSL_GROUP_M, tiles_m - g * LSL_GROUP_M);
+  const int i = t - g * LSL_GROUP_M * tiles_n;
+  tn = i / gm;
+  tm = g * LSL_GROUP_M + (i - tn * gm);
 }
 
 // y[m][n .. n + 3] = bf16(v (+ bias)) (+ residual, rounded again)
