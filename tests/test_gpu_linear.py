@@ -91,6 +91,14 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (300, 1024, 1152, 16, "bf16"),
     (128, 512, 256, 64, "bf16"),      # the largest rank of the linear API
     (64, 256, 384, 64, "nf4"),
+    # at least 384 output tiles of 256 x 256: the large-tile GEMM. Forward:
+    (1024, 256, 24576, 16, "nf4"),
+    (1100, 320, 24576, 16, "bf16"),   # ragged tokens; bf16 weight tile by LDS DMA
+    (1024, 256, 24640, 16, "nf4dq"),  # ragged weight rows (last tile 64 of 256)
+    # input gradient ([K x N] weight layout):
+    (1000, 24640, 192, 8, "nf4"),
+    (1024, 24576, 256, 16, "bf16"),
+    (1100, 24576, 320, 16, "nf4dq"),
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
@@ -124,6 +132,7 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
 @pytest.mark.parametrize("T,fin,fout,r,fmt", [
     (200, 320, 448, 16, "bf16"),      # ragged, unsplit GEMM
     (64, 4096, 512, 16, "nf4"),       # few output tiles: split-K path, bias added in the split reduce
+    (1100, 256, 24576, 16, "nf4"),    # 256 x 256 tiles
 ])
 def test_lora_linear_bias(gpu, T, fin, fout, r, fmt):
     """A frozen bias joins the forward sum before its single rounding; the
