@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA train tok/s (streamed fwd+bwd) + % bf16 MFMA peak + achieved H2D GB/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # the timed kernel's instantiation: NF4 weight, [N x K] layout, forward LoRA step, bf16 epilogue
-GU_KERNEL = "gemm_kernel<0, false, 1, 0,"
+GU_LABEL = "gemm_big_kernel<NF4, NK, LoRA-fwd> gate|up"
 COUNTERS = os.path.join(ROOT, "profiles", "gemm_gu_fwd_nf4_llama8b_s1024_counters.json")
 
 
@@ -299,10 +299,20 @@ def cpu_baseline(shape, ms):
 CALIB_MIB = 256
 
 
-def gu_grid_items(shape, ms):
-    T = ms.batch * ms.seq
+def gu_kernel(shape, ms):
+    """Name prefix and grid (work-items) of the gate|up forward GEMM launch: the
+    library's 256 x 256-tile kernel once the output has at least 384 such tiles,
+    else the 64-row tiles (256 tokens from 1024 tokens on, 128 below)."""
+    T, N = ms.batch * ms.seq, 2 * shape.inter
+    big = -(-T // 256) * -(-N // 256)
+    if big >= 384:
+        return "gemm_big_kernel<0, false, 1>", big * 512
     bm = 256 if T >= 1024 else 128
-    return -(-T // bm) * -(-2 * shape.inter // 64) * 256
+    return "gemm_kernel<0, false, 1, 0,", -(-T // bm) * -(-N // 64) * 256
+
+
+def gu_grid_items(shape, ms):
+    return gu_kernel(shape, ms)[1]
 
 
 def gu_algorithmic_bytes(shape, ms):
@@ -371,12 +381,12 @@ def summarize_trace(d, args):
         out.append(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
                    f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     trace = _rows(_find(d, "*kernel_trace.csv"))
-    g = gu_grid_items(shape, ms)
+    kname, g = gu_kernel(shape, ms)
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
-            if GU_KERNEL in r["Kernel_Name"] and _grid_items(r) == g]
+            if kname in r["Kernel_Name"] and _grid_items(r) == g]
     out.append("")
     if durs:
-        out.append(f"gate|up forward GEMM dispatches (gemm_kernel, {g} work-items): {len(durs)} calls, "
+        out.append(f"gate|up forward GEMM dispatches ({kname.split('<')[0]}, {g} work-items): {len(durs)} calls, "
                    f"average {sum(durs) / len(durs):.1f} us, min {min(durs):.1f} us, max {max(durs):.1f} us")
     # attention: algorithmic FLOP / average duration against the bf16 MFMA peak (causal: half the
     # dense products; forward 2 products, dK/dV 4 (scores and dP recomputed), dQ 3)
@@ -448,13 +458,13 @@ def summarize_counters(fetch_dir, write_dir, args):
     the same counters read for the calibration copy, and write the counters file
     the benchmark reports as roofline traffic."""
     wl, shape, ms = workload(args.workload)
-    g = gu_grid_items(shape, ms)
+    kname, g = gu_kernel(shape, ms)
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _rows(_find(d, "*counter_collection.csv")) if r["Counter_Name"] == counter]
         copy = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]
                 and _grid_items(r) >= 1 << 20]
-        gemm = [float(r["Counter_Value"]) for r in rows if GU_KERNEL in r["Kernel_Name"] and _grid_items(r) == g]
+        gemm = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"] and _grid_items(r) == g]
         if not copy or not gemm:
             sys.exit(f"{counter}: copy dispatches {len(copy)}, gemm dispatches {len(gemm)}")
         kib_copy = sum(copy) / len(copy)
@@ -464,7 +474,7 @@ def summarize_counters(fetch_dir, write_dir, args):
                         "gemm_bytes_per_dispatch": sum(gemm) / len(gemm) * 1024.0 * scale}
     src = open(os.path.join(ROOT, "layer_streamed_lora_amd", "csrc", "gemm.hip"), "rb").read()
     hbm = res["FETCH_SIZE"]["gemm_bytes_per_dispatch"] + res["WRITE_SIZE"]["gemm_bytes_per_dispatch"]
-    doc = {"kernel": "gemm_kernel<NF4, NK, LoRA-fwd> gate|up", "workload": args.workload,
+    doc = {"kernel": GU_LABEL, "workload": args.workload,
            "gemm_hip_sha256": hashlib.sha256(src).hexdigest(), "counters": res,
            "hbm_bytes_per_launch": round(hbm), "algorithmic_bytes_per_launch": gu_algorithmic_bytes(shape, ms),
            "commands": args.commands}
@@ -597,7 +607,7 @@ def main():
                                f"{ms.batch}x{ms.seq} tokens, fused CE, AdamW",
                    "batch": ms.batch, "seq_len": ms.seq, "n_micro": ms.n_micro, "layers": ms.n_layers,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel<NF4, NK, LoRA-fwd> gate|up 1024x28672x4096",
+        "roofline": {"bound": "mfma", "kernel": GU_LABEL + " 1024x28672x4096",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": counters_traffic(),
                      "avg_launch_ms": round(g_ms, 4), "launches": res["kernel_launches"]},
