@@ -99,6 +99,12 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1000, 24640, 192, 8, "nf4"),
     (1024, 24576, 256, 16, "bf16"),
     (1100, 24576, 320, 16, "nf4dq"),
+    # large-tile pipeline edges: one and two K-steps, a single token
+    (1024, 64, 24576, 8, "nf4"),
+    (1100, 128, 24576, 16, "nf4dq"),
+    (1024, 24576, 64, 8, "bf16"),
+    (1, 64, 98304, 8, "nf4"),
+    (1, 98304, 64, 8, "bf16"),
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
