@@ -82,11 +82,15 @@ def step_flops(shape, ms):
     return ms.n_micro * (ms.n_layers * per_layer + ce)
 
 
-def pinned_h2d_peak(nbytes, reps=20):
+def pinned_h2d_peak(nbytes, stream, reps=20):
+    """hipMemcpyAsync rate of a pinned buffer of nbytes on the given stream. The
+    layer pool's own copy stream is passed: HIP maps streams onto a few hardware
+    queues (4 by default), and streams that share one run one after the other,
+    so every extra stream risks putting the copies behind the compute."""
     import torch
     src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    s = torch.cuda.Stream()
+    s = stream
     with torch.cuda.stream(s):
         for _ in range(3):
             dst.copy_(src, non_blocking=True)
@@ -562,8 +566,15 @@ def main():
                          and torch.equal(s_model.ckpt, r_model.ckpt) and torch.equal(s_model.lse, r_model.lse))
         log(f"  streamed vs resident bit-exact: {bit_exact}")
 
-    peak_h2d = pinned_h2d_peak(s_model.blob_bytes)
+    peak_h2d = pinned_h2d_peak(s_model.blob_bytes, s_model.pool.copy_stream)
     log(f"  pinned H2D (hipMemcpyAsync, {s_model.blob_bytes} B): {peak_h2d:.1f} GB/s")
+    # the copy a GPU would make if N GPUs each pulled 1/N of every layer and
+    # exchanged the rest over xGMI (cooperative streaming, not built here)
+    slices = {}
+    for n in (2, 4, 8):
+        nb = (s_model.blob_bytes // n + 255) // 256 * 256
+        slices[f"1/{n}"] = {"bytes": nb, "GBps": round(pinned_h2d_peak(nb, s_model.pool.copy_stream), 2)}
+    log("  pinned H2D of layer slices: " + ", ".join(f"{k} {v['GBps']} GB/s" for k, v in slices.items()))
     res = time_steps(s_model, inputs, args.steps, args.warmup, timing_which=3)
     log(f"  streamed: {res['ms_per_step']:.2f} ms/step, loss {res['loss']:.4f}")
     # copy-engine statistics (an event pair per copy) in a separate, untimed step
@@ -615,7 +626,7 @@ def main():
         "gemms_resident": gemms,
         "h2d": {"achieved_GBps_copy_engine": h2d_copy and round(h2d_copy, 2),
                 "achieved_GBps_over_step": h2d_eff and round(h2d_eff, 2),
-                "pinned_peak_GBps": round(peak_h2d, 2),
+                "pinned_peak_GBps": round(peak_h2d, 2), "pinned_slices": slices,
                 "frac_of_pinned_peak": h2d_copy and round(h2d_copy / peak_h2d, 3),
                 "bytes_per_step": step_bytes},
         "resident": resident and {"ms_per_step": round(resident["ms_per_step"], 3),

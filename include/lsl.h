@@ -238,7 +238,12 @@ lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* layer_blob,
  * Slot life cycle: load_layer_async -> lsl_pool_acquire -> lsl_pool_release ->
  * load_layer_async ... . A load waits (on the copy stream) until the slot's
  * previous user released it; acquire makes the compute stream wait for the load.
- * The caller owns the slot memory and the copy stream. */
+ * The caller owns the slot memory and the copy stream. The copy stream must be
+ * a non-blocking stream (hipStreamNonBlocking) that does not share a hardware
+ * queue with the compute stream: HIP maps streams onto a few hardware queues
+ * (GPU_MAX_HW_QUEUES, 4 by default) and two streams on one queue run one after
+ * the other, which silently removes the overlap. Keeping one copy stream per
+ * process, and few streams in all, avoids that. */
 typedef struct lsl_pool lsl_pool;
 lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, int32_t n_slots,
                            size_t slot_bytes, lsl_stream copy_stream);

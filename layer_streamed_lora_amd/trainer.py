@@ -36,12 +36,39 @@ def shifted_labels(ids, batch, seq):
     return lab.reshape(-1)
 
 
+_COPY_STREAMS = {}
+
+
+def copy_stream(device="cuda"):
+    """The one stream every layer pool of this process copies on (per device).
+
+    HIP maps streams onto a few hardware queues (GPU_MAX_HW_QUEUES, 4 by
+    default); two streams that share a queue run one after the other, so a copy
+    stream that lands on the compute stream's queue stops overlapping with it
+    (a streamed step then costs copies plus compute). This stream is created
+    directly as a non-blocking HIP stream, so torch's pool of 32+ streams is not
+    initialised by this package and the process keeps two streams: the compute
+    stream and this one. It lives until the process ends."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx not in _COPY_STREAMS:
+        hip = C.CDLL("libamdhip64.so")
+        handle = C.c_void_p()
+        with torch.cuda.device(idx):
+            rc = hip.hipStreamCreateWithFlags(C.byref(handle), C.c_uint(1))  # hipStreamNonBlocking
+        if rc != 0:
+            raise RuntimeError(f"hipStreamCreateWithFlags failed with HIP error {rc}")
+        _COPY_STREAMS[idx] = torch.cuda.ExternalStream(handle.value, device=idx)
+    return _COPY_STREAMS[idx]
+
+
 class LayerPool:
     """Python handle of the C pool (slots are device tensors owned here)."""
 
     def __init__(self, n_slots, slot_bytes, device="cuda"):
         self.slot_bytes = slot_bytes
-        self.copy_stream = torch.cuda.Stream(device=device)
+        self.copy_stream = copy_stream(device)
         self.slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=device) for _ in range(n_slots)]
         ptrs = (C.c_void_p * n_slots)(*[s.data_ptr() for s in self.slots])
         self.handle = C.c_void_p()
