@@ -307,11 +307,11 @@ CALIB_MIB = 256
 
 def gu_kernel(shape, ms):
     """Name prefix and grid (work-items) of the gate|up forward GEMM launch: the
-    library's 256 x 256-tile kernel once the output has at least 384 such tiles,
+    library's 256 x 256-tile kernel once the output has at least 192 such tiles,
     else the 64-row tiles (256 tokens from 1024 tokens on, 128 below)."""
     T, N = ms.batch * ms.seq, 2 * shape.inter
     big = -(-T // 256) * -(-N // 256)
-    if big >= 384:
+    if big >= 192:
         return "gemm_big_kernel<0, false, 1>", big * 512
     bm = 256 if T >= 1024 else 128
     return "gemm_kernel<0, false, 1, 0,", -(-T // bm) * -(-N // 64) * 256

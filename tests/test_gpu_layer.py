@@ -79,7 +79,7 @@ def test_layer_parity_llama8b_seq512(gpu):
 
 def test_layer_large_tile_gemms_sampled_rows(gpu):
     """Llama-8B layer over 6144 one-token sequences: every projection GEMM, forward
-    and input gradient, has at least 384 output tiles of 256 x 256 (the large-tile
+    and input gradient, has at least 192 output tiles of 256 x 256 (the large-tile
     kernel, with the residual epilogues of o and down and the LoRA K-steps). With
     one token per sequence each output row depends on its own input row only, so
     the oracle checks sampled rows."""

@@ -91,7 +91,7 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (300, 1024, 1152, 16, "bf16"),
     (128, 512, 256, 64, "bf16"),      # the largest rank of the linear API
     (64, 256, 384, 64, "nf4"),
-    # at least 384 output tiles of 256 x 256: the large-tile GEMM. Forward:
+    # at least 192 output tiles of 256 x 256: the large-tile GEMM. Forward:
     (1024, 256, 24576, 16, "nf4"),
     (1100, 320, 24576, 16, "bf16"),   # ragged tokens; bf16 weight tile by LDS DMA
     (1024, 256, 24640, 16, "nf4dq"),  # ragged weight rows (last tile 64 of 256)
