@@ -372,39 +372,68 @@ LSL_DEV void store_split_partials(const GemmKArgs& a, const f32x16 (&acc)[2][MI]
     }
 }
 
+// segment (fused projection) owning output column n
+LSL_DEV int lora_seg(const GemmKArgs& a, int64_t n) {
+  int seg = 0;
+  while (seg < a.nseg - 1 && n >= a.seg_end[seg]) ++seg;
+  return seg;
+}
+
 // LoRA K-step operands in LDS ([rows][LDSW], k zero padded to 64): Ls = the
 // A-side rows m0.. of la; Lt[n][j] = B[n][j % r] if j / r is the projection
 // owning column n (LORA 1, forward), or A_full[j][n] (LORA 2, input gradient).
+// Every operand moves in 16-byte chunks (kl and r are multiples of 8, so a chunk
+// never straddles a projection), all of a thread's loads issued before its stores.
 template <int LORA, int BN, int BM>
 LSL_DEV void lora_stage(const GemmKArgs& a, uint16_t* Ls, uint16_t* Lt, int64_t m0, int64_t n0, int tid) {
-  for (int c = tid; c < BM * 8; c += NTHREADS) {
-    int row = c >> 3, col = (c & 7) * 8;
-    int64_t gm = m0 + row;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (gm < a.M && col < a.kl) v = *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col);
-    *reinterpret_cast<u32x4*>(Ls + row * LDSW + col) = v;
+  constexpr int LC = BM * 8 / NTHREADS;  // Ls chunks per thread
+  u32x4 lv[LC];
+#pragma unroll
+  for (int i = 0; i < LC; ++i) {
+    const int c = tid + i * NTHREADS, row = c >> 3, col = (c & 7) * 8;
+    const int64_t gm = m0 + row;
+    lv[i] = (gm < a.M && col < a.kl) ? *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col) : u32x4{0, 0, 0, 0};
   }
+  constexpr int TC = BN * 8 / NTHREADS;  // Lt chunks per thread
+  u32x4 tv[TC];
   if constexpr (LORA == 1) {
-    // Lt[n][j] = B[n][j % r] if j / r is the projection owning column n
-    for (int c = tid; c < BN * 64; c += NTHREADS) {
-      int row = c >> 6, j = c & 63;
-      int64_t gn = n0 + row;
-      uint16_t v = 0;
-      if (gn < a.N && j < a.kl) {
-        int seg = 0;
-        while (seg < a.nseg - 1 && gn >= a.seg_end[seg]) ++seg;
-        if (j / a.r == seg) v = a.lb[gn * a.r + (j % a.r)];
-      }
-      Lt[row * LDSW + j] = v;
+    // thread -> row tid / (8 / TC), chunks TC (tid % (8 / TC)) .. + TC - 1
+    const int row = tid / (8 / TC), c0 = (tid % (8 / TC)) * TC;
+    const int64_t gn = n0 + row;
+    const int seg = gn < a.N ? lora_seg(a, gn) : -1;
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      const int j0 = (c0 + q) * 8;
+      tv[q] = (seg >= 0 && j0 < a.kl && j0 / a.r == seg)
+                  ? *reinterpret_cast<const u32x4*>(a.lb + gn * a.r + (j0 - seg * a.r))
+                  : u32x4{0, 0, 0, 0};
     }
   } else {
-    // Lt[n][j] = A_full[j][n]
-    for (int c = tid; c < BN * 64; c += NTHREADS) {
-      int j = c / BN, row = c % BN;
-      int64_t gn = n0 + row;
-      uint16_t v = 0;
-      if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
-      Lt[row * LDSW + j] = v;
+    // thread -> reduction row j = c / (BN / 8), columns 8 (c % (BN / 8)) .. + 7 of A_full
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      const int c = tid + q * NTHREADS, j = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+      const int64_t gn = n0 + nc;
+      tv[q] = (j < a.kl && gn < a.N) ? *reinterpret_cast<const u32x4*>(a.lb + (int64_t)j * a.N + gn)
+                                     : u32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < LC; ++i) {
+    const int c = tid + i * NTHREADS, row = c >> 3, col = (c & 7) * 8;
+    *reinterpret_cast<u32x4*>(Ls + row * LDSW + col) = lv[i];
+  }
+  if constexpr (LORA == 1) {
+    const int row = tid / (8 / TC), c0 = (tid % (8 / TC)) * TC;
+#pragma unroll
+    for (int q = 0; q < TC; ++q) *reinterpret_cast<u32x4*>(Lt + row * LDSW + (c0 + q) * 8) = tv[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {  // transposed: Lt[n][j], eight 2-byte stores
+      const int c = tid + q * NTHREADS, j = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        Lt[(nc + e) * LDSW + j] = (uint16_t)((e & 1) ? (tv[q][e >> 1] >> 16) : (tv[q][e >> 1] & 0xFFFFu));
     }
   }
 }
@@ -817,35 +846,55 @@ LSL_DEV void mma_big(const uint16_t* __restrict__ Ws, const uint16_t* __restrict
 }
 
 // LoRA K-step operands: Ls = rows m0.. of la (k zero padded to 64) in the
-// swizzled token layout, Lt [BN][LDSW] as in lora_stage
+// swizzled token layout; Lt as in lora_stage, [BN][LDSW] for the forward (LORA
+// 1) and, for the input gradient (LORA 2), A_full's rows j < 64 as the row-major
+// [k][BN + 8] tile the KN main loop reads. 16-byte chunks, loads issued first.
 template <int LORA>
 LSL_DEV void lora_stage_big(const GemmKArgs& a, uint16_t* Ls, uint16_t* Lt, int64_t m0, int64_t n0, int tid) {
-  for (int c = tid; c < BM * 8; c += NT) {
-    const int row = c >> 3, ch = c & 7, col = ch * 8;
+  constexpr int LC = BM * 8 / NT, TC = BN * 8 / NT;  // 4 and 4 chunks per thread
+  u32x4 lv[LC], tv[TC];
+#pragma unroll
+  for (int i = 0; i < LC; ++i) {
+    const int c = tid + i * NT, row = c >> 3, col = (c & 7) * 8;
     const int64_t gm = m0 + row;
-    u32x4 v = u32x4{0, 0, 0, 0};
-    if (gm < a.M && col < a.kl) v = *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col);
-    *reinterpret_cast<u32x4*>(Ls + row * BK + 8 * (ch ^ xswz(row))) = v;
+    lv[i] = (gm < a.M && col < a.kl) ? *reinterpret_cast<const u32x4*>(a.la + gm * a.ldla + col) : u32x4{0, 0, 0, 0};
   }
   if constexpr (LORA == 1) {
-    for (int c = tid; c < BN * 64; c += NT) {
-      const int row = c >> 6, j = c & 63;
-      const int64_t gn = n0 + row;
-      uint16_t v = 0;
-      if (gn < a.N && j < a.kl) {
-        int seg = 0;
-        while (seg < a.nseg - 1 && gn >= a.seg_end[seg]) ++seg;
-        if (j / a.r == seg) v = a.lb[gn * a.r + (j % a.r)];
-      }
-      Lt[row * LDSW + j] = v;
+    // thread -> row tid / 2, chunks 4 (tid % 2) .. + 3
+    const int row = tid >> 1, c0 = (tid & 1) * 4;
+    const int64_t gn = n0 + row;
+    const int seg = gn < a.N ? lora_seg(a, gn) : -1;
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      const int j0 = (c0 + q) * 8;
+      tv[q] = (seg >= 0 && j0 < a.kl && j0 / a.r == seg)
+                  ? *reinterpret_cast<const u32x4*>(a.lb + gn * a.r + (j0 - seg * a.r))
+                  : u32x4{0, 0, 0, 0};
     }
   } else {
-    for (int c = tid; c < BN * 64; c += NT) {
-      const int j = c / BN, row = c % BN;
-      const int64_t gn = n0 + row;
-      uint16_t v = 0;
-      if (gn < a.N && j < a.kl) v = a.lb[(int64_t)j * a.N + gn];
-      Lt[row * LDSW + j] = v;
+    // thread -> reduction row j = c / 32, columns 8 (c % 32) .. + 7
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      const int c = tid + q * NT, j = c >> 5, nc = (c & 31) * 8;
+      const int64_t gn = n0 + nc;
+      tv[q] = (j < a.kl && gn < a.N) ? *reinterpret_cast<const u32x4*>(a.lb + (int64_t)j * a.N + gn)
+                                     : u32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < LC; ++i) {
+    const int c = tid + i * NT, row = c >> 3, ch = c & 7;
+    *reinterpret_cast<u32x4*>(Ls + row * BK + 8 * (ch ^ xswz(row))) = lv[i];
+  }
+  if constexpr (LORA == 1) {
+    const int row = tid >> 1, c0 = (tid & 1) * 4;
+#pragma unroll
+    for (int q = 0; q < TC; ++q) *reinterpret_cast<u32x4*>(Lt + row * LDSW + (c0 + q) * 8) = tv[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < TC; ++q) {
+      const int c = tid + q * NT, j = c >> 5, nc = (c & 31) * 8;
+      *reinterpret_cast<u32x4*>(Lt + j * (BN + 8) + nc) = tv[q];
     }
   }
 }
@@ -895,12 +944,22 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  const int KT = (int)(a.K / BK);
+  TileDma xd;
+  xd.init(a.ldx, m0, 0, wave, lane);
+  W wl;
+  wl.init(a, n0, tid, wave, lane);
+  // step 0's tiles are requested first, so their latency overlaps the LoRA step
+  xd.issue(a.x, a.ldx, a.M, 0, Xs0);
+  if constexpr (W::kind == 1) wl.issue(a, 0, Ws0);
+  else wl.load(a, 0);
+
   // LoRA K-step first, on the second stage's buffers: the accumulators start as
   // s * (L Lt^T)
   if constexpr (LORA != 0) {
     lora_stage_big<LORA>(a, Xs1, Ws1, m0, n0, tid);
     __syncthreads();
-    mma_big<0>(Ws1, Xs1, acc, wn, wm, lane, (a.kl + 15) / 16);
+    mma_big<LORA == 1 ? 0 : 2>(Ws1, Xs1, acc, wn, wm, lane, (a.kl + 15) / 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -911,18 +970,9 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
     // reaches only after these reads
   }
 
-  const int KT = (int)(a.K / BK);
-  TileDma xd;
-  xd.init(a.ldx, m0, 0, wave, lane);
-  W wl;
-  wl.init(a, n0, tid, wave, lane);
   // prologue: step 0 into stage 0; codes of step 1 into registers
-  xd.issue(a.x, a.ldx, a.M, 0, Xs0);
-  if constexpr (W::kind == 1) {
-    wl.issue(a, 0, Ws0);
-  } else {
-    wl.load(a, 0);
-    __syncthreads();  // lut visible
+  if constexpr (W::kind == 0) {
+    if constexpr (LORA == 0) __syncthreads();  // lut visible (the LoRA step's barrier did it otherwise)
     wl.store(Ws0, lut, tid);
     if (KT > 1) wl.load(a, BK);
   }
