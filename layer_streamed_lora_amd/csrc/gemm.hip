@@ -931,7 +931,9 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   int tm, tn;
-  tile_coords((int)blockIdx.x, a.tiles_m, a.tiles_n, tm, tn);
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int split = (int)blockIdx.x / ntiles;  // split-K: reduction steps [kt0, kt0 + KT)
+  tile_coords((int)blockIdx.x - split * ntiles, a.tiles_m, a.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   if constexpr (WFMT != LSL_WFMT_BF16)
     if (tid < 16) lut[tid] = a.cb[tid];
@@ -944,19 +946,21 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int KT = (int)(a.K / BK);
+  const int kt0 = split * a.kt_per_split;
+  const int KT = min((int)(a.K / BK) - kt0, a.kt_per_split);
+  const int64_t k0 = (int64_t)kt0 * BK;
   TileDma xd;
   xd.init(a.ldx, m0, 0, wave, lane);
   W wl;
   wl.init(a, n0, tid, wave, lane);
   // step 0's tiles are requested first, so their latency overlaps the LoRA step
-  xd.issue(a.x, a.ldx, a.M, 0, Xs0);
-  if constexpr (W::kind == 1) wl.issue(a, 0, Ws0);
-  else wl.load(a, 0);
+  xd.issue(a.x, a.ldx, a.M, k0, Xs0);
+  if constexpr (W::kind == 1) wl.issue(a, k0, Ws0);
+  else wl.load(a, k0);
 
-  // LoRA K-step first, on the second stage's buffers: the accumulators start as
-  // s * (L Lt^T)
-  if constexpr (LORA != 0) {
+  // LoRA K-step first (split 0), on the second stage's buffers: the
+  // accumulators start as s * (L Lt^T)
+  if constexpr (LORA != 0) if (split == 0) {
     lora_stage_big<LORA>(a, Xs1, Ws1, m0, n0, tid);
     __syncthreads();
     mma_big<LORA == 1 ? 0 : 2>(Ws1, Xs1, acc, wn, wm, lane, (a.kl + 15) / 16);
@@ -972,9 +976,9 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
 
   // prologue: step 0 into stage 0; codes of step 1 into registers
   if constexpr (W::kind == 0) {
-    if constexpr (LORA == 0) __syncthreads();  // lut visible (the LoRA step's barrier did it otherwise)
+    if (LORA == 0 || split != 0) __syncthreads();  // lut visible (the LoRA step's barrier did it otherwise)
     wl.store(Ws0, lut, tid);
-    if (KT > 1) wl.load(a, BK);
+    if (KT > 1) wl.load(a, k0 + BK);
   }
   big::tile_barrier<0>();
   auto step = [&](int kt, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc, uint16_t* __restrict__ xn,
@@ -982,16 +986,16 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
     const bool next = kt + 1 < KT, next2 = kt + 2 < KT;
     if (next) {
       if constexpr (W::kind == 1) {
-        wl.issue(a, (int64_t)(kt + 1) * BK, wnx);
+        wl.issue(a, k0 + (int64_t)(kt + 1) * BK, wnx);
       } else {
         wl.store(wnx, lut, tid);
       }
-      xd.issue(a.x, a.ldx, a.M, (int64_t)(kt + 1) * BK, xn);
+      xd.issue(a.x, a.ldx, a.M, k0 + (int64_t)(kt + 1) * BK, xn);
       if constexpr (W::kind == 0)
         if (next2) {
           // the weight loads must issue after the DMA: the barrier below counts them
           big::order_point();
-          wl.load(a, (int64_t)(kt + 2) * BK);
+          wl.load(a, k0 + (int64_t)(kt + 2) * BK);
         }
     }
     mma_big<WL>(wc, xc, acc, wn, wm, lane, 4);
@@ -1014,6 +1018,8 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
   // m = m0 + 64 wm + 32 mi + lane % 32, n = n0 + 128 wn + 32 ni + 8 q + 4 (lane / 32)
   const int64_t mb = m0 + wm * 64 + (lane & 31);
   const int64_t nb = n0 + wn * 128 + (lane >> 5) * 4;
+  // split-K: this split's float32 partial (gemm_split_reduce adds the splits in order)
+  float* part = a.ksplit > 1 ? a.spart + (int64_t)split * a.M * a.N : nullptr;
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -1024,8 +1030,11 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
       for (int mi = 0; mi < 2; ++mi) {
         const int64_t m = mb + mi * 32;
         if (m >= a.M) continue;
-        store_bf16x4(a, m, n, acc[ni][mi][4 * q], acc[ni][mi][4 * q + 1], acc[ni][mi][4 * q + 2],
-                     acc[ni][mi][4 * q + 3]);
+        const f32x16& v = acc[ni][mi];
+        if (part)
+          *reinterpret_cast<f32x4*>(part + m * a.N + n) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        else
+          store_bf16x4(a, m, n, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       }
     }
 }
@@ -1111,8 +1120,36 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
 #ifndef LSL_BIG_MIN_TILES
 #define LSL_BIG_MIN_TILES 192
 #endif
-static bool gemm_use_big(int64_t M, int64_t N) {
-  return ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN) >= LSL_BIG_MIN_TILES;
+// GEMMs with fewer tiles but a long reduction take the large tile too, with the
+// reduction split so that about BIG_SPLIT_TARGET workgroups run, each at least
+// BIG_SPLIT_MIN_STEPS K-steps. Measured at 1024 tokens on the Llama-8B layer:
+// the down projection forward (K 14336, four splits) 182 -> 156 us and the
+// gate|up input gradient (K 28672, four splits) 355 -> 302 us.
+#ifndef LSL_BIG_SPLIT_MIN_TILES
+#define LSL_BIG_SPLIT_MIN_TILES 32
+#endif
+#ifndef LSL_BIG_SPLIT_MIN_STEPS
+#define LSL_BIG_SPLIT_MIN_STEPS 48
+#endif
+#ifndef LSL_BIG_SPLIT_TARGET
+#define LSL_BIG_SPLIT_TARGET 256
+#endif
+// 0: the 64-row tiles; 1: the large tile, unsplit; S > 1: the large tile, S splits
+static int gemm_big_plan(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
+  if (tiles == 0) return 0;
+  if (tiles >= LSL_BIG_MIN_TILES) return 1;
+  if (tiles < LSL_BIG_SPLIT_MIN_TILES) return 0;
+  const int64_t steps = K / BK;
+  int64_t S = (LSL_BIG_SPLIT_TARGET + tiles - 1) / tiles;
+  if (S > steps / LSL_BIG_SPLIT_MIN_STEPS) S = steps / LSL_BIG_SPLIT_MIN_STEPS;
+  if (S < 2) return 0;
+  const int64_t per = (steps + S - 1) / S;
+  S = (steps + per - 1) / per;
+  // the splits must fill the chip as well as an unsplit large-tile GEMM does
+  // (the input gradient of q|k|v at 1024 tokens, 64 tiles x 2 splits, is
+  // slower than the 64-row tiles)
+  return tiles * S >= LSL_BIG_MIN_TILES ? (int)S : 0;
 }
 
 template <int WFMT, bool KN>
@@ -1122,12 +1159,19 @@ static void launch_big(const GemmKArgs& a, int lora, hipStream_t s, dim3 grid) {
   else hipLaunchKernelGGL((gemm_big_kernel<WFMT, KN, 2>), grid, dim3(big::NT), 0, s, a);
 }
 
-static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
+static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s, int S) {
   a.tiles_m = (int)((d.M + big::BM - 1) / big::BM);
   a.tiles_n = (int)((d.N + big::BN - 1) / big::BN);
+  const int KT = (int)(d.K / BK);
   a.ksplit = 1;
-  a.kt_per_split = (int)(d.K / BK);
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  a.kt_per_split = KT;
+  if (S > 1) {
+    if (!d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
+    a.kt_per_split = (KT + S - 1) / S;
+    a.ksplit = (KT + a.kt_per_split - 1) / a.kt_per_split;
+    a.spart = d.split_ws;
+  }
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.ksplit));
   if (d.wfmt == LSL_WFMT_NF4) {
     if (d.kn) launch_big<LSL_WFMT_NF4, true>(a, d.lora, s, grid);
     else launch_big<LSL_WFMT_NF4, false>(a, d.lora, s, grid);
@@ -1137,6 +1181,11 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s)
   } else {
     if (d.kn) launch_big<LSL_WFMT_BF16, true>(a, d.lora, s, grid);
     else launch_big<LSL_WFMT_BF16, false>(a, d.lora, s, grid);
+  }
+  if (a.ksplit > 1) {
+    const int64_t n4 = d.M * d.N / 4;
+    hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
+                       a.ksplit, d.M, d.N, d.bias, d.res, d.ldres, d.y, d.ldy);
   }
   return check_launch("gemm(256 x 256 tiles)");
 }
@@ -1155,7 +1204,7 @@ int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t steps = K / BK;
   if (tiles == 0) return 1;  // empty output
-  if (gemm_use_big(M, N)) return 1;
+  if (const int b = gemm_big_plan(M, N, K)) return b;
   int64_t S = (LSL_SPLIT_TARGET + tiles - 1) / tiles;
   if (S > steps / LSL_SPLIT_MIN_STEPS) S = steps / LSL_SPLIT_MIN_STEPS;
   if (S < 2) return 1;
@@ -1196,7 +1245,8 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   a.labels = d.labels; a.lse = d.lse; a.nvalid = d.nvalid; a.part = (float2*)d.part; a.zlab = d.zlab;
   a.y2 = d.y2; a.gscale = d.gscale; a.ignore = d.ignore; a.vocab_off = d.vocab_off; a.vocab = d.vocab;
   a.out32 = d.out32; a.ldo32 = d.ldo32; a.first = d.first; a.kwrap = d.kwrap;
-  if (d.epi == EPI_BF16 && !d.kwrap && gemm_use_big(d.M, d.N)) return launch_big_cfg(d, a, s);
+  if (d.epi == EPI_BF16 && !d.kwrap)
+    if (const int b = gemm_big_plan(d.M, d.N, d.K)) return launch_big_cfg(d, a, s, b);
   int bn, bm;
   gemm_tile_shape(d.M, d.N, bn, bm);
   return bm == 256 ? launch_cfg<64, 256>(d, a, s) : launch_cfg<64, 128>(d, a, s);

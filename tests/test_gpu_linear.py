@@ -105,6 +105,11 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1024, 24576, 64, 8, "bf16"),
     (1, 64, 98304, 8, "nf4"),
     (1, 98304, 64, 8, "bf16"),
+    # fewer large tiles but a long reduction: the large tile with split-K (forward
+    # here; the input gradient of the same linear has 224 tiles, unsplit)
+    (1024, 14336, 2048, 16, "nf4"),
+    (1000, 2048, 14336, 8, "bf16"),   # input gradient split, ragged tokens
+    (1100, 12288, 2048, 16, "nf4dq"),
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
@@ -139,6 +144,7 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     (200, 320, 448, 16, "bf16"),      # ragged, unsplit GEMM
     (64, 4096, 512, 16, "nf4"),       # few output tiles: split-K path, bias added in the split reduce
     (1100, 256, 24576, 16, "nf4"),    # 256 x 256 tiles
+    (1024, 14336, 2048, 16, "nf4"),   # 256 x 256 tiles with split-K, bias added in the split reduce
 ])
 def test_lora_linear_bias(gpu, T, fin, fout, r, fmt):
     """A frozen bias joins the forward sum before its single rounding; the
