@@ -43,7 +43,9 @@ LSL_DEV __amdgpu_buffer_rsrc_t small_rsrc(const void* base, int64_t bytes) {
 template <bool DIRECT>
 __global__ __launch_bounds__(256) void lora_nt_kernel(const NtArgs a) {
   __shared__ f32x4 red[3][4][4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform in a wave: as a scalar, the K loop and the buffer
+  // loads' offsets stay scalar (no per-lane loop around every load)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
   const int64_t kbeg = (int64_t)blockIdx.y * a.k_per_split;
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void lora_nt_kernel(const NtArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+#pragma unroll 4
   for (int64_t k0 = kbeg + wave * 64; k0 < kend; k0 += 256) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -164,42 +166,41 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t tt = tbeg; tt < tend; tt += 64) {
-    {  // P: 4 t-rows x 8 a-cols per thread, stored transposed
-      int q = tid >> 4, o = tid & 15;
-      int64_t ac = a0 + o * 8;
-      uint32_t w[4][4];
+  // thread -> P: 4 t-rows x 8 a-cols; Q: 2 t-rows x 8 j-cols. The global loads
+  // of the next 64-token step are issued before the MFMAs of the current one.
+  const int pq = tid >> 4, po = tid & 15, qq = tid >> 3, qo = tid & 7;
+  const int64_t ac = a0 + po * 8;
+  u32x4 rp[4], rq[2];
+  auto gload = [&](int64_t tt) {
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        int64_t t = tt + q * 4 + rr;
-        u32x4 v = (t < tend && ac < a.W) ? *reinterpret_cast<const u32x4*>(a.p + t * a.ldp + ac) : u32x4{0, 0, 0, 0};
-        w[rr][0] = v[0]; w[rr][1] = v[1]; w[rr][2] = v[2]; w[rr][3] = v[3];
-      }
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        uint32_t e[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) e[rr] = (cc & 1) ? (w[rr][cc >> 1] >> 16) : (w[rr][cc >> 1] & 0xFFFFu);
-        *reinterpret_cast<u32x2*>(Ps + (o * 8 + cc) * SK_LDS + q * 4) = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-      }
+    for (int rr = 0; rr < 4; ++rr) {
+      const int64_t t = tt + pq * 4 + rr;
+      rp[rr] = (t < tend && ac < a.W) ? *reinterpret_cast<const u32x4*>(a.p + t * a.ldp + ac) : u32x4{0, 0, 0, 0};
     }
-    {  // Q: 2 t-rows x 8 j-cols per thread, stored transposed
-      int q = tid >> 3, o = tid & 7;
-      uint32_t w[2][4];
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        int64_t t = tt + q * 2 + rr;
-        u32x4 v = (t < tend && o * 8 < a.kl) ? *reinterpret_cast<const u32x4*>(a.q + t * a.ldq + o * 8) : u32x4{0, 0, 0, 0};
-        w[rr][0] = v[0]; w[rr][1] = v[1]; w[rr][2] = v[2]; w[rr][3] = v[3];
-      }
+    for (int rr = 0; rr < 2; ++rr) {
+      const int64_t t = tt + qq * 2 + rr;
+      rq[rr] = (t < tend && qo * 8 < a.kl) ? *reinterpret_cast<const u32x4*>(a.q + t * a.ldq + qo * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  if (tbeg < tend) gload(tbeg);
+  for (int64_t tt = tbeg; tt < tend; tt += 64) {
+    // both tiles stored transposed ([col][t])
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        uint32_t e0 = (cc & 1) ? (w[0][cc >> 1] >> 16) : (w[0][cc >> 1] & 0xFFFFu);
-        uint32_t e1 = (cc & 1) ? (w[1][cc >> 1] >> 16) : (w[1][cc >> 1] & 0xFFFFu);
-        *reinterpret_cast<uint32_t*>(Qs + (o * 8 + cc) * SK_LDS + q * 2) = e0 | (e1 << 16);
-      }
+    for (int cc = 0; cc < 8; ++cc) {
+      uint32_t e[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) e[rr] = (cc & 1) ? (rp[rr][cc >> 1] >> 16) : (rp[rr][cc >> 1] & 0xFFFFu);
+      *reinterpret_cast<u32x2*>(Ps + (po * 8 + cc) * SK_LDS + pq * 4) = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const uint32_t e0 = (cc & 1) ? (rq[0][cc >> 1] >> 16) : (rq[0][cc >> 1] & 0xFFFFu);
+      const uint32_t e1 = (cc & 1) ? (rq[1][cc >> 1] >> 16) : (rq[1][cc >> 1] & 0xFFFFu);
+      *reinterpret_cast<uint32_t*>(Qs + (qo * 8 + cc) * SK_LDS + qq * 2) = e0 | (e1 << 16);
     }
     __syncthreads();
+    if (tt + 64 < tend) gload(tt + 64);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       int kofs = ks * 32 + (lane >> 4) * 8;
