@@ -39,9 +39,9 @@ static Timing g_timing;
 static void timing_mark(int which, bool begin, hipStream_t s) {
   if (g_timing.which != which || g_timing.count >= (int)g_timing.start.size()) return;
   if (begin) {
-    hipEventRecord(g_timing.start[g_timing.count], s);
+    (void)hipEventRecord(g_timing.start[g_timing.count], s);  // diagnostics only
   } else {
-    hipEventRecord(g_timing.stop[g_timing.count], s);
+    (void)hipEventRecord(g_timing.stop[g_timing.count], s);
     ++g_timing.count;
   }
 }
@@ -399,8 +399,8 @@ extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* la
 }
 
 static void timing_free() {
-  for (auto e : g_timing.start) hipEventDestroy(e);
-  for (auto e : g_timing.stop) hipEventDestroy(e);
+  for (auto e : g_timing.start) (void)hipEventDestroy(e);
+  for (auto e : g_timing.stop) (void)hipEventDestroy(e);
   g_timing = Timing();
 }
 

@@ -73,7 +73,7 @@ __global__ void ce_count_valid_kernel(const int32_t* __restrict__ labels, int64_
   cnt[threadIdx.x] = c;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) cnt[threadIdx.x] += cnt[threadIdx.x + s];
+    if ((int)threadIdx.x < s) cnt[threadIdx.x] += cnt[threadIdx.x + s];
     __syncthreads();
   }
   if (threadIdx.x == 0) *nvalid = (float)cnt[0];
@@ -140,7 +140,7 @@ __global__ void ce_loss_kernel(const float* __restrict__ lossv, int64_t T, const
   acc[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
-    if (threadIdx.x < k) acc[threadIdx.x] += acc[threadIdx.x + k];
+    if ((int)threadIdx.x < k) acc[threadIdx.x] += acc[threadIdx.x + k];
     __syncthreads();
   }
   if (threadIdx.x == 0) *loss = *nvalid > 0.f ? acc[0] / *nvalid : 0.f;
@@ -162,7 +162,7 @@ __global__ void ce_logp_kernel(const float* __restrict__ lossv, int64_t seq, flo
   acc[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
-    if (threadIdx.x < k) acc[threadIdx.x] += acc[threadIdx.x + k];
+    if ((int)threadIdx.x < k) acc[threadIdx.x] += acc[threadIdx.x + k];
     __syncthreads();
   }
   if (threadIdx.x == 0) seq_logp[blockIdx.x] = acc[0];

@@ -63,7 +63,6 @@ __global__ __launch_bounds__(256) void lora_nt_kernel(const NtArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
   for (int64_t k0 = kbeg + wave * 64; k0 < kend; k0 += 256) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -281,7 +280,7 @@ static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks, int64_
   if (s < 1) s = 1;
   return (int)s;
 }
-constexpr int64_t NT_TARGET = 256, NT_MIN_STEPS = 4, TN_TARGET = 256, TN_MIN_STEPS = 4;
+constexpr int64_t TN_TARGET = 256, TN_MIN_STEPS = 4;
 
 // NT splits: about NT_BLOCKS workgroups of 64 rows, each split at least
 // NT_MIN_K of K (so that each of its four waves takes NT_MIN_K / 256 steps)

@@ -68,8 +68,8 @@ extern "C" lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, in
 }
 
 static void stats_free(lsl_pool* p) {
-  for (auto e : p->st_start) hipEventDestroy(e);
-  for (auto e : p->st_end) hipEventDestroy(e);
+  for (auto e : p->st_start) (void)hipEventDestroy(e);
+  for (auto e : p->st_end) (void)hipEventDestroy(e);
   p->st_start.clear();
   p->st_end.clear();
   p->st_bytes.clear();
@@ -79,8 +79,8 @@ static void stats_free(lsl_pool* p) {
 extern "C" lsl_status lsl_pool_destroy(lsl_pool* p) {
   if (!p) return LSL_OK;
   for (int i = 0; i < p->n; ++i) {
-    if (p->ready[i]) hipEventDestroy(p->ready[i]);
-    if (p->freed[i]) hipEventDestroy(p->freed[i]);
+    if (p->ready[i]) (void)hipEventDestroy(p->ready[i]);
+    if (p->freed[i]) (void)hipEventDestroy(p->freed[i]);
   }
   stats_free(p);
   delete p;
