@@ -700,6 +700,22 @@ struct TileDma {
 template <int WFMT, bool KN>
 struct BigW;
 
+// codebook values of the 8 NF4 codes in one code dword (byte j: element 2j in
+// the high nibble, 2j + 1 in the low one), and their bf16 products with the
+// block's absmax
+LSL_DEV void nf4_fetch(uint32_t cw, const float* lut, float (&v)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t b = cw >> (j * 8);
+    v[2 * j] = lut[(b >> 4) & 15];
+    v[2 * j + 1] = lut[b & 15];
+  }
+}
+LSL_DEV u32x4 nf4_emit(const float (&v)[8], float am) {
+  return u32x4{pack2(v[0] * am, v[1] * am), pack2(v[2] * am, v[3] * am), pack2(v[4] * am, v[5] * am),
+               pack2(v[6] * am, v[7] * am)};
+}
+
 // NF4 [N x K]: thread -> row tid / 2, 16 code bytes (32 weights) at k 32 (tid % 2);
 // rows past N clamped to the last row (their outputs are never stored)
 template <int WFMT>
@@ -719,17 +735,19 @@ struct BigNf4Nk {
     c = *reinterpret_cast<const u32x4*>(pc + (k0 >> 1));
     am = block_absmax<WFMT>(a, ai + (k0 >> 6));
   }
+  // quarter i of the tile row, code dword i (8 weights): codebook values, then
+  // the scaled bf16 weights as one 16-byte LDS store
+  LSL_DEV void fetch(int i, const float* lut, float (&v)[8]) const { nf4_fetch(c[i], lut, v); }
+  LSL_DEV void emit(int i, const float (&v)[8], uint16_t* __restrict__ lds, int tid) const {
+    reinterpret_cast<u32x4*>(lds + (tid >> 1) * LDSW + (tid & 1) * 32)[i] = nf4_emit(v, am);
+  }
   LSL_DEV void store(uint16_t* __restrict__ lds, const float* lut, int tid) const {
-    const int row = tid >> 1, part = tid & 1;
-    uint32_t o[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t b = c[j >> 2] >> ((j & 3) * 8);  // element 2j in the high nibble
-      o[j] = pack2(lut[(b >> 4) & 15] * am, lut[b & 15] * am);
+    for (int i = 0; i < 4; ++i) {
+      float v[8];
+      fetch(i, lut, v);
+      emit(i, v, lds, tid);
     }
-    u32x4* d = reinterpret_cast<u32x4*>(lds + row * LDSW + part * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
 };
 template <> struct BigW<LSL_WFMT_NF4, false> : BigNf4Nk<LSL_WFMT_NF4> {};
@@ -757,17 +775,17 @@ struct BigNf4Kn {
     c = *reinterpret_cast<const u32x4*>(pc + k0 * rowc);
     am = block_absmax<WFMT>(a, ai + k0 * rowa);
   }
+  LSL_DEV void fetch(int i, const float* lut, float (&v)[8]) const { nf4_fetch(c[i], lut, v); }
+  LSL_DEV void emit(int i, const float (&v)[8], uint16_t* __restrict__ lds, int tid) const {
+    reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32)[i] = nf4_emit(v, am);
+  }
   LSL_DEV void store(uint16_t* __restrict__ lds, const float* lut, int tid) const {
-    const int kr = tid >> 3, part = tid & 7;
-    uint32_t o[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t b = c[j >> 2] >> ((j & 3) * 8);
-      o[j] = pack2(lut[(b >> 4) & 15] * am, lut[b & 15] * am);
+    for (int i = 0; i < 4; ++i) {
+      float v[8];
+      fetch(i, lut, v);
+      emit(i, v, lds, tid);
     }
-    u32x4* d = reinterpret_cast<u32x4*>(lds + kr * (BN + 8) + part * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
 };
 template <> struct BigW<LSL_WFMT_NF4, true> : BigNf4Kn<LSL_WFMT_NF4> {};
@@ -788,10 +806,13 @@ struct BigW<LSL_WFMT_BF16, true> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = bload16(rs, voff + 16 * i, (uint32_t)(k0 * a.N * 2));
   }
+  LSL_DEV void fetch(int, const float*, float (&)[8]) const {}
+  LSL_DEV void emit(int i, const float (&)[8], uint16_t* __restrict__ lds, int tid) const {
+    reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32)[i] = v[i];
+  }
   LSL_DEV void store(uint16_t* __restrict__ lds, const float*, int tid) const {
-    u32x4* d = reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = v[i];
+    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32)[i] = v[i];
   }
 };
 
@@ -809,14 +830,15 @@ struct BigW<LSL_WFMT_BF16, false> {
 // nsub 16-deep MFMA sub-steps: acc[ni][mi] += W-block[ni] x X-block[mi] for the
 // wave's 128 x 64 tile. WL: weight tile layout 0 padded [n][LDSW], 1 swizzled
 // [n][64], 2 row-major [k][BN + 8] read with transposing LDS reads.
-template <int WL>
+struct NoPart {
+  LSL_DEV void begin() const {}
+  LSL_DEV void operator()(int) const {}
+};
+template <int WL, typename Part = NoPart>
 LSL_DEV void mma_big(const uint16_t* __restrict__ Ws, const uint16_t* __restrict__ Xs, f32x16 (&acc)[4][2], int wn,
-                     int wm, int lane, int nsub) {
+                     int wm, int lane, int nsub, Part&& part = Part()) {
   const int h = lane >> 5, r32 = lane & 31;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s >= nsub) break;
-    bf16x8 af[4], bfr[2];
+  auto frag = [&](int s, bf16x8 (&af)[4], bf16x8 (&bfr)[2]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wn * 128 + i * 32 + r32;
@@ -838,10 +860,21 @@ LSL_DEV void mma_big(const uint16_t* __restrict__ Ws, const uint16_t* __restrict
       const int row = wm * 64 + i * 32 + r32;
       bfr[i] = *reinterpret_cast<const bf16x8*>(Xs + row * BK + 8 * ((2 * s + h) ^ xswz(row)));
     }
+  };
+  // sub-step s + 1's fragments are read while sub-step s multiplies
+  bf16x8 af[2][4], bfr[2][2];
+  frag(0, af[0], bfr[0]);
+  part.begin();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s >= nsub) break;
+    if (s + 1 < nsub) frag(s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
+    part(s);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) acc[ni][mi] = mfma32(af[ni], bfr[mi], acc[ni][mi]);
+      for (int ni = 0; ni < 4; ++ni) acc[ni][mi] = mfma32(af[s & 1][ni], bfr[s & 1][mi], acc[ni][mi]);
+    if constexpr (!std::is_same<Part, NoPart>::value) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -984,21 +1017,39 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
   auto step = [&](int kt, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc, uint16_t* __restrict__ xn,
                   uint16_t* __restrict__ wnx) {
     const bool next = kt + 1 < KT, next2 = kt + 2 < KT;
-    if (next) {
-      if constexpr (W::kind == 1) {
+    if constexpr (W::kind == 1) {
+      if (next) {
         wl.issue(a, k0 + (int64_t)(kt + 1) * BK, wnx);
-      } else {
-        wl.store(wnx, lut, tid);
+        xd.issue(a.x, a.ldx, a.M, k0 + (int64_t)(kt + 1) * BK, xn);
       }
-      xd.issue(a.x, a.ldx, a.M, k0 + (int64_t)(kt + 1) * BK, xn);
-      if constexpr (W::kind == 0)
-        if (next2) {
-          // the weight loads must issue after the DMA: the barrier below counts them
-          big::order_point();
-          wl.load(a, k0 + (int64_t)(kt + 2) * BK);
+      mma_big<WL>(wc, xc, acc, wn, wm, lane, 4);
+    } else {
+      // step kt + 1's weights (held in registers) are converted and stored
+      // between this step's MFMAs, a quarter per 16-deep sub-step. After the
+      // last step the store goes to the idle stage and is never read.
+      const W cur = wl;
+      if (next) xd.issue(a.x, a.ldx, a.M, k0 + (int64_t)(kt + 1) * BK, xn);
+      if (next2) {
+        // the weight loads must issue after the DMA: the barrier below counts them
+        big::order_point();
+        wl.load(a, k0 + (int64_t)(kt + 2) * BK);
+      }
+      // quarter q's codebook values are read one sub-step before they are scaled
+      // and stored, so the LDS latency hides behind that sub-step's MFMAs
+      struct Part {
+        const W& w;
+        const float* lut;
+        uint16_t* __restrict__ dst;
+        int tid;
+        float v[2][8];
+        LSL_DEV void begin() { w.fetch(0, lut, v[0]); }
+        LSL_DEV void operator()(int q) {
+          if (q + 1 < 4) w.fetch(q + 1, lut, v[(q + 1) & 1]);
+          w.emit(q, v[q & 1], dst, tid);
         }
+      } part{cur, lut, wnx, tid, {}};
+      mma_big<WL>(wc, xc, acc, wn, wm, lane, 4, part);
     }
-    mma_big<WL>(wc, xc, acc, wn, wm, lane, 4);
     // the DMA of step kt + 1 is complete once at most the weight loads issued
     // after it (step kt + 2) are outstanding
     if constexpr (W::kind == 0 && W::nload == 2) {
