@@ -874,7 +874,19 @@ LSL_DEV void mma_big(const uint16_t* __restrict__ Ws, const uint16_t* __restrict
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) acc[ni][mi] = mfma32(af[s & 1][ni], bfr[s & 1][mi], acc[ni][mi]);
-    if constexpr (!std::is_same<Part, NoPart>::value) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!std::is_same<Part, NoPart>::value) {
+      // issue order within the sub-step: each MFMA followed by two LDS reads
+      // (next fragments, codebook values) and four VALU operations of the
+      // weight conversion, then the weight store; nothing crosses sub-steps
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);    // LDS write
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
