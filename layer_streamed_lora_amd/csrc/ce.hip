@@ -28,16 +28,7 @@ struct CePlan {
 // dH = sum over chunks of G_c W_c is accumulated in `splits` float32 partial
 // sums, each over its own share of every chunk's reduction (so that enough
 // workgroups run on the T x H output), added in split order at the end.
-static int ce_acc_splits(int64_t T, int64_t H, int64_t vc) {
-  int bn, bm;
-  gemm_tile_shape(T, H, bn, bm);
-  const int64_t tiles = ((T + bm - 1) / bm) * ((H + bn - 1) / bn);
-  const int64_t steps = vc / 64;
-  if (tiles == 0) return 1;  // no tokens
-  int64_t S = (768 + tiles - 1) / tiles;
-  if (S > steps / 32) S = steps / 32;
-  return S < 1 ? 1 : (int)S;
-}
+static int ce_acc_splits(int64_t T, int64_t H, int64_t vc) { return gemm_acc32_splits(T, H, vc); }
 
 static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
   CePlan p{};
@@ -45,8 +36,7 @@ static CePlan ce_plan(int64_t T, int64_t H, int64_t V) {
   auto take = [&](size_t b) { size_t o = off; off = align256(off + b); return o; };
   p.nvalid = take(4);
   size_t common = off;
-  int bn, bm;
-  gemm_tile_shape(T, V, bn, bm);
+  const int bn = gemm_ce_tile_n(T, V, H);
   int64_t ntiles = (V + bn - 1) / bn;
   p.part = take((size_t)ntiles * T * 8);
   p.zlab = take((size_t)T * 4);
@@ -210,8 +200,7 @@ extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm
   g.epi = 1; g.labels = labels; g.part = w + p.part; g.zlab = (float*)(w + p.zlab); g.ignore = ignore_index;
   g.vocab = V;
   LSL_TRY(gemm_launch(g, s));
-  int bn, bm;
-  gemm_tile_shape(T, V, bn, bm);
+  const int bn = gemm_ce_tile_n(T, V, H);
   int64_t ntiles = (V + bn - 1) / bn;
   hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 63) / 64)), dim3(64 * LSE_WAVES), 0, s, (const float2*)(w + p.part),
                      ntiles, T, labels, (const float*)(w + p.zlab), ignore_index, V, lse, (float*)(w + p.lossv));
@@ -290,8 +279,7 @@ extern "C" lsl_status fused_ce_logprobs(const uint16_t* hN, const uint16_t* w_lm
   g.epi = 1; g.labels = labels; g.part = w + p.part; g.zlab = (float*)(w + p.zlab); g.ignore = ignore_index;
   g.vocab = V;
   LSL_TRY(gemm_launch(g, s));
-  int bn, bm;
-  gemm_tile_shape(T, V, bn, bm);
+  const int bn = gemm_ce_tile_n(T, V, H);
   int64_t ntiles = (V + bn - 1) / bn;
   hipLaunchKernelGGL(ce_lse_kernel, dim3((unsigned)((T + 63) / 64)), dim3(64 * LSE_WAVES), 0, s,
                      (const float2*)(w + p.part), ntiles, T, labels, (const float*)(w + p.zlab), ignore_index, V,

@@ -37,4 +37,11 @@ int gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
 // Tile shape gemm_launch picks for an M x N output (bn weight rows, bm tokens).
 void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm);
+// cross-entropy GEMMs: whether the logits passes of an M x N x K problem run in
+// the 256 x 256 tiles, the vocabulary tile width of the forward pass (its
+// per-tile (max, sum) partials are [N / width][M]), and the number of
+// reduction splits the float32 dH accumulation uses
+bool gemm_ce_big(int64_t M, int64_t N, int64_t K);
+int gemm_ce_tile_n(int64_t M, int64_t N, int64_t K);
+int gemm_acc32_splits(int64_t M, int64_t N, int64_t K);
 }  // namespace lsl

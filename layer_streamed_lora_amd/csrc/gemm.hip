@@ -351,6 +351,86 @@ LSL_DEV void store_bf16x4(const GemmKArgs& a, int64_t m, int64_t n, float v0, fl
   *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(v0, v1), pack2(v2, v3)};
 }
 
+// Cross-entropy gradient for C[m][n .. n + 3] (logits of one vocabulary chunk):
+// G = coef * (softmax - onehot), as a hi + lo pair of bf16 matrices (about 16
+// significant bits for the dH product; the lo part only when y2 is set)
+LSL_DEV void ce_grad4(const GemmKArgs& a, int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
+  const int lab = a.labels[m];
+  const float nv = *a.nvalid;
+  const bool valid = lab != a.ignore && lab >= 0 && lab < a.vocab;
+  const float coef = (valid && nv > 0.f) ? a.gscale / nv : 0.f;
+  const float l = a.lse[m];
+  const int64_t nl = n + a.vocab_off;
+  float g[4] = {v0, v1, v2, v3};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) g[e] = coef * (expf(g[e] - l) - (nl + e == lab ? 1.f : 0.f));
+  const uint32_t h0 = pack2(g[0], g[1]), h1 = pack2(g[2], g[3]);
+  *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{h0, h1};
+  if (a.y2)
+    *reinterpret_cast<u32x2*>(a.y2 + m * a.ldy + n) =
+        u32x2{pack2(g[0] - lo_bf(h0), g[1] - hi_bf(h0)), pack2(g[2] - lo_bf(h1), g[3] - hi_bf(h1))};
+}
+
+// float32 accumulation into split `split`'s partial sum (first: overwrite), with
+// a bf16 copy of the sum when y is set
+LSL_DEV void acc32_4(const GemmKArgs& a, int split, int64_t m, int64_t n, float v0, float v1, float v2, float v3) {
+  float* o = a.out32 + split * a.o32_split + m * a.ldo32 + n;
+  const f32x4 prev = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(o);
+  const f32x4 r = f32x4{prev[0] + v0, prev[1] + v1, prev[2] + v2, prev[3] + v3};
+  *reinterpret_cast<f32x4*>(o) = r;
+  if (a.y) *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
+}
+
+// Cross-entropy forward, per token row of a tile: the row's max and sum of exp
+// over the lane's logits (columns n < N; the label's logit is recorded where it
+// falls), combined over the two lane halves holding the row. acc[ni][mi]
+// element i is column nb + 32 ni + 8 (i / 4) + i % 4 of row mb + 32 mi.
+template <int NI, int MI>
+LSL_DEV void lse_rows(const GemmKArgs& a, const f32x16 (&acc)[NI][MI], int64_t mb, int64_t nb, float2 (&res)[MI]) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int64_t m = mb + mi * 32;
+    const int lab = m < a.M ? a.labels[m] : -1;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t n = nb + ni * 32 + 8 * (i >> 2) + (i & 3);
+        if (n < a.N) {
+          mx = fmaxf(mx, acc[ni][mi][i]);
+          if (n == lab) a.zlab[m] = acc[ni][mi][i];
+        }
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sm = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t n = nb + ni * 32 + 8 * (i >> 2) + (i & 3);
+          if (n < a.N) sm += expf(acc[ni][mi][i] - mx);
+        }
+    }
+    sm += __shfl_xor(sm, 32, 64);
+    res[mi] = make_float2(mx, sm);
+  }
+}
+
+// (max, sum of exp) pairs of nw partial rows combined into one, in index order
+LSL_DEV float2 lse_combine(const float2* p, int nw, int stride) {
+  float mx = -INFINITY;
+  for (int w = 0; w < nw; ++w) mx = fmaxf(mx, p[w * stride].x);
+  float sm = 0.f;
+  if (mx != -INFINITY)
+    for (int w = 0; w < nw; ++w) {
+      const float2 q = p[w * stride];
+      if (q.x != -INFINITY) sm += q.y * expf(q.x - mx);
+    }
+  return make_float2(mx, sm);
+}
+
 // split-K: the float32 partial of this split (gemm_split_reduce adds the splits).
 // Block (ni, mi), q < 4: the lane holds C[m][n .. n + 3], m = mb + 32 mi, n = nb + 32 ni + 8 q.
 template <int MI>
@@ -529,51 +609,14 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
     // Cross-entropy forward: per token m, max and sum of exp over this tile's
     // vocabulary entries n < N, and the label's logit if it falls in the tile.
     float2* red = reinterpret_cast<float2*>(Xs);  // [WN][BM]
+    float2 rows[MI];
+    lse_rows<2, MI>(a, acc, mb, nb, rows);
+    if ((lane >> 5) == 0)
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int64_t m = mb + mi * 32;
-      const int lab = m < a.M ? a.labels[m] : -1;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t n = nb + ni * 32 + 8 * (i >> 2) + (i & 3);
-          if (n < a.N) {
-            mx = fmaxf(mx, acc[ni][mi][i]);
-            if (n == lab) a.zlab[m] = acc[ni][mi][i];
-          }
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float sm = 0.f;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int64_t n = nb + ni * 32 + 8 * (i >> 2) + (i & 3);
-            if (n < a.N) sm += expf(acc[ni][mi][i] - mx);
-          }
-      }
-      sm += __shfl_xor(sm, 32, 64);
-      if ((lane >> 5) == 0) red[wn * BM + wm0 + mi * 32 + (lane & 31)] = make_float2(mx, sm);
-    }
+      for (int mi = 0; mi < MI; ++mi) red[wn * BM + wm0 + mi * 32 + (lane & 31)] = rows[mi];
     __syncthreads();
-    for (int t = tid; t < BM; t += NTHREADS) {
-      if (m0 + t >= a.M) continue;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < G::WN; ++w) mx = fmaxf(mx, red[w * BM + t].x);
-      float sm = 0.f;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < G::WN; ++w) {
-          float2 p = red[w * BM + t];
-          if (p.x != -INFINITY) sm += p.y * expf(p.x - mx);
-        }
-      }
-      a.part[(int64_t)tn * a.M + m0 + t] = make_float2(mx, sm);
-    }
+    for (int t = tid; t < BM; t += NTHREADS)
+      if (m0 + t < a.M) a.part[(int64_t)tn * a.M + m0 + t] = lse_combine(red + t, G::WN, BM);
     return;
   }
   if (EPI == EPI_BF16 && a.ksplit > 1) {
@@ -592,28 +635,9 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
       if (m >= a.M) continue;
       float v0 = acc[ni][mi][4 * q], v1 = acc[ni][mi][4 * q + 1], v2 = acc[ni][mi][4 * q + 2], v3 = acc[ni][mi][4 * q + 3];
       if constexpr (EPI == EPI_CEGRAD) {
-        // G = coef * (softmax - onehot) for this vocabulary chunk, as a hi + lo
-        // pair of bf16 matrices (about 16 significant bits for the dH product)
-        const int lab = a.labels[m];
-        const float nv = *a.nvalid;
-        const bool valid = lab != a.ignore && lab >= 0 && lab < a.vocab;
-        const float coef = (valid && nv > 0.f) ? a.gscale / nv : 0.f;
-        const float l = a.lse[m];
-        const int64_t nl = n + a.vocab_off;
-        float g[4] = {v0, v1, v2, v3};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) g[e] = coef * (expf(g[e] - l) - (nl + e == lab ? 1.f : 0.f));
-        const uint32_t h0 = pack2(g[0], g[1]), h1 = pack2(g[2], g[3]);
-        *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{h0, h1};
-        if (a.y2)
-          *reinterpret_cast<u32x2*>(a.y2 + m * a.ldy + n) =
-              u32x2{pack2(g[0] - lo_bf(h0), g[1] - hi_bf(h0)), pack2(g[2] - lo_bf(h1), g[3] - hi_bf(h1))};
+        ce_grad4(a, m, n, v0, v1, v2, v3);
       } else if constexpr (EPI == EPI_ACC32) {
-        float* o = a.out32 + split * a.o32_split + m * a.ldo32 + n;
-        f32x4 prev = a.first ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(o);
-        f32x4 r = f32x4{prev[0] + v0, prev[1] + v1, prev[2] + v2, prev[3] + v3};
-        *reinterpret_cast<f32x4*>(o) = r;
-        if (a.y) *reinterpret_cast<u32x2*>(a.y + m * a.ldy + n) = u32x2{pack2(r[0], r[1]), pack2(r[2], r[3])};
+        acc32_4(a, split, m, n, v0, v1, v2, v3);
       } else {
         store_bf16x4(a, m, n, v0, v1, v2, v3);
       }
@@ -962,7 +986,7 @@ LSL_DEV void tile_barrier() {
 
 }  // namespace big
 
-template <int WFMT, bool KN, int LORA>
+template <int WFMT, bool KN, int LORA, int EPI = EPI_BF16>
 __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a) {
   using namespace big;
   using W = BigW<WFMT, KN>;
@@ -1081,6 +1105,39 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
   // m = m0 + 64 wm + 32 mi + lane % 32, n = n0 + 128 wn + 32 ni + 8 q + 4 (lane / 32)
   const int64_t mb = m0 + wm * 64 + (lane & 31);
   const int64_t nb = n0 + wn * 128 + (lane >> 5) * 4;
+  if constexpr (EPI == EPI_LSE) {
+    // cross-entropy forward: per token row, (max, sum of exp) over this tile's
+    // vocabulary columns; the two column halves (wn) are combined through LDS,
+    // which every wave has finished reading at the loop's last barrier
+    float2* red = reinterpret_cast<float2*>(Xs0);  // [2][BM]
+    float2 rows[2];
+    lse_rows<4, 2>(a, acc, mb, nb, rows);
+    if ((lane >> 5) == 0)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) red[wn * BM + wm * 64 + mi * 32 + (lane & 31)] = rows[mi];
+    __syncthreads();
+    for (int t = tid; t < BM; t += NT)
+      if (m0 + t < a.M) a.part[(int64_t)tn * a.M + m0 + t] = lse_combine(red + t, 2, BM);
+    return;
+  }
+  if constexpr (EPI == EPI_CEGRAD || EPI == EPI_ACC32) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = nb + ni * 32 + 8 * q;
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+          const int64_t m = mb + mi * 32;
+          if (m >= a.M) continue;
+          const f32x16& v = acc[ni][mi];
+          if constexpr (EPI == EPI_CEGRAD) ce_grad4(a, m, n, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          else acc32_4(a, split, m, n, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+      }
+    return;
+  }
   // split-K: this split's float32 partial (gemm_split_reduce adds the splits in order)
   float* part = a.ksplit > 1 ? a.spart + (int64_t)split * a.M * a.N : nullptr;
 #pragma unroll
@@ -1253,6 +1310,66 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s,
   return check_launch("gemm(256 x 256 tiles)");
 }
 
+// Cross-entropy GEMMs (bf16 weight, no LoRA) in the large tile: the logits
+// passes (forward log-sum-exp, gradient chunk) when the vocabulary gives enough
+// tiles unsplit, the dH accumulation when its splits fill the chip.
+bool gemm_ce_big(int64_t M, int64_t N, int64_t K) { return gemm_big_plan(M, N, K) == 1; }
+
+int gemm_ce_tile_n(int64_t M, int64_t N, int64_t K) {
+  if (gemm_ce_big(M, N, K)) return big::BN;
+  int bn, bm;
+  gemm_tile_shape(M, N, bn, bm);
+  return bn;
+}
+
+static bool acc32_big(int64_t M, int64_t N, int S) {
+  const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
+  return tiles >= LSL_BIG_SPLIT_MIN_TILES && tiles * S >= LSL_BIG_MIN_TILES;
+}
+
+int gemm_acc32_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t steps = K / BK;
+  const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
+  if (tiles == 0) return 1;
+  if (tiles >= LSL_BIG_SPLIT_MIN_TILES) {
+    int64_t S = (LSL_BIG_SPLIT_TARGET + tiles - 1) / tiles;
+    if (S > steps / LSL_BIG_SPLIT_MIN_STEPS) S = steps / LSL_BIG_SPLIT_MIN_STEPS;
+    if (S < 1) S = 1;
+    if (acc32_big(M, N, (int)S)) return (int)S;
+  }
+  // the 64-row tiles: about 768 workgroups, at least 32 K-steps each
+  int bn, bm;
+  gemm_tile_shape(M, N, bn, bm);
+  const int64_t t64 = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  int64_t S = (768 + t64 - 1) / t64;
+  if (S > steps / 32) S = steps / 32;
+  return S < 1 ? 1 : (int)S;
+}
+
+static lsl_status launch_big_ce(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
+  a.tiles_m = (int)((d.M + big::BM - 1) / big::BM);
+  a.tiles_n = (int)((d.N + big::BN - 1) / big::BN);
+  const int KT = (int)(d.K / BK);
+  a.ksplit = 1;
+  a.kt_per_split = KT;
+  if (d.epi == EPI_ACC32 && d.acc_splits > 1) {
+    if (d.y) return set_error(LSL_ERR_UNSUPPORTED, "gemm: split float accumulation has no bf16 copy");
+    a.kt_per_split = (KT + d.acc_splits - 1) / d.acc_splits;
+    a.ksplit = (KT + a.kt_per_split - 1) / a.kt_per_split;
+    if (d.first && a.ksplit != d.acc_splits)  // the first pass must initialise every split
+      return set_error(LSL_ERR_UNSUPPORTED, "gemm: %d accumulation splits of %d steps", d.acc_splits, KT);
+    a.o32_split = d.o32_split;
+  }
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.ksplit));
+  if (d.epi == EPI_LSE)
+    hipLaunchKernelGGL((gemm_big_kernel<LSL_WFMT_BF16, false, 0, EPI_LSE>), grid, dim3(big::NT), 0, s, a);
+  else if (d.epi == EPI_CEGRAD)
+    hipLaunchKernelGGL((gemm_big_kernel<LSL_WFMT_BF16, false, 0, EPI_CEGRAD>), grid, dim3(big::NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<LSL_WFMT_BF16, true, 0, EPI_ACC32>), grid, dim3(big::NT), 0, s, a);
+  return check_launch("gemm(ce, 256 x 256 tiles)");
+}
+
 // Split-K for GEMMs with few output tiles: enough reduction splits to give
 // about SPLIT_TARGET workgroups, each taking at least SPLIT_MIN_STEPS K-steps.
 #ifndef LSL_SPLIT_TARGET
@@ -1310,6 +1427,11 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   a.out32 = d.out32; a.ldo32 = d.ldo32; a.first = d.first; a.kwrap = d.kwrap;
   if (d.epi == EPI_BF16 && !d.kwrap)
     if (const int b = gemm_big_plan(d.M, d.N, d.K)) return launch_big_cfg(d, a, s, b);
+  if (d.wfmt == LSL_WFMT_BF16 && !d.lora && !d.kwrap) {
+    if ((d.epi == EPI_LSE || d.epi == EPI_CEGRAD) && !d.kn && gemm_ce_big(d.M, d.N, d.K))
+      return launch_big_ce(d, a, s);
+    if (d.epi == EPI_ACC32 && d.kn && acc32_big(d.M, d.N, d.acc_splits)) return launch_big_ce(d, a, s);
+  }
   int bn, bm;
   gemm_tile_shape(d.M, d.N, bn, bm);
   return bm == 256 ? launch_cfg<64, 256>(d, a, s) : launch_cfg<64, 128>(d, a, s);

@@ -22,6 +22,10 @@ def _case(T, H, V, wid, n_ignore=3):
 
 @pytest.mark.parametrize("T,H,V,gs", [
     (100, 128, 69952, 1.0),     # three vocabulary chunks of the backward, the last one partial; ragged T
+    # 256 x 256 tiles: the forward logits, the first gradient chunk (the second,
+    # 7232 columns, in 64-row tiles) and the dH accumulation with 8 reduction
+    # splits; two token tiles, the second ragged; a partial vocabulary tile
+    (300, 4096, 40000, 1.0),
     (100, 128, 16576, 1.0),     # one chunk, a partial vocabulary tile
     (37, 256, 1088, 0.25),      # one chunk with a partial vocabulary tile, a gradient scale
     (1, 64, 64, 1.0),
@@ -93,6 +97,7 @@ def test_ce_llama8b_head_sampled_rows(gpu):
 
 @pytest.mark.parametrize("T,H,V,batch", [
     (100, 128, 16576, 4),       # ragged vocabulary tile, 4 sequences of 25
+    (100, 128, 69952, 2),       # forward logits in 256 x 256 tiles, a partial one at the end
     (37, 256, 1088, 1),
     (1, 64, 64, 1),
 ])
