@@ -312,7 +312,7 @@ def gu_kernel(shape, ms):
     T, N = ms.batch * ms.seq, 2 * shape.inter
     big = -(-T // 256) * -(-N // 256)
     if big >= 192:
-        return "gemm_big_kernel<0, false, 1>", big * 512
+        return "gemm_big_kernel<0, false, 1, 0>", big * 512
     bm = 256 if T >= 1024 else 128
     return "gemm_kernel<0, false, 1, 0,", -(-T // bm) * -(-N // 64) * 256
 
