@@ -153,7 +153,9 @@ struct TnArgs {
 };
 
 // grid: (ceil(W/128), S). 4 waves, wave w owns columns a = 32w..32w+31 of the tile.
-template <bool DIRECT>
+// BUF: the split's rows are read through buffer descriptors (its bytes below
+// 4 GiB): no per-load bounds branches.
+template <bool DIRECT, bool BUF>
 __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ps[128 * SK_LDS];  // [a][t]
   __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * SK_LDS];   // [j][t]
@@ -166,24 +168,51 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
   for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // thread -> P: 4 t-rows x 8 a-cols; Q: 2 t-rows x 8 j-cols. The global loads
-  // of the next 64-token step are issued before the MFMAs of the current one.
+  // run two 64-token steps ahead of the MFMAs, in two register sets. With BUF,
+  // rows past the split's end read zeros (t_per_split is a multiple of 64, so
+  // that happens only past T); columns past W or kl read neighbouring data or
+  // zeros and feed only outputs that are never stored.
   const int pq = tid >> 4, po = tid & 15, qq = tid >> 3, qo = tid & 7;
   const int64_t ac = a0 + po * 8;
-  u32x4 rp[4], rq[2];
-  auto gload = [&](int64_t tt) {
+  // (unused without BUF)
+  const __amdgpu_buffer_rsrc_t rsp = small_rsrc(a.p + tbeg * a.ldp, (tend - tbeg) * a.ldp * 2);
+  const __amdgpu_buffer_rsrc_t rsq = small_rsrc(a.q + tbeg * a.ldq, (tend - tbeg) * a.ldq * 2);
+  uint32_t pofs[4], qofs[2];
+  if constexpr (BUF) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int64_t t = tt + pq * 4 + rr;
-      rp[rr] = (t < tend && ac < a.W) ? *reinterpret_cast<const u32x4*>(a.p + t * a.ldp + ac) : u32x4{0, 0, 0, 0};
-    }
+    for (int rr = 0; rr < 4; ++rr) pofs[rr] = (uint32_t)(((int64_t)(pq * 4 + rr) * a.ldp + ac) * 2);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int64_t t = tt + qq * 2 + rr;
-      rq[rr] = (t < tend && qo * 8 < a.kl) ? *reinterpret_cast<const u32x4*>(a.q + t * a.ldq + qo * 8) : u32x4{0, 0, 0, 0};
+    for (int rr = 0; rr < 2; ++rr) qofs[rr] = (uint32_t)(((int64_t)(qq * 2 + rr) * a.ldq + qo * 8) * 2);
+  }
+  auto gload = [&](int64_t tt, u32x4 (&rp)[4], u32x4 (&rq)[2]) {
+    if constexpr (BUF) {
+      const uint32_t op = (uint32_t)((tt - tbeg) * a.ldp * 2), oq = (uint32_t)((tt - tbeg) * a.ldq * 2);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        rp[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsp, pofs[rr] + op, 0, 0));
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        rq[rr] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsq, qofs[rr] + oq, 0, 0));
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t t = tt + pq * 4 + rr;
+        rp[rr] = (t < tend && ac < a.W) ? *reinterpret_cast<const u32x4*>(a.p + t * a.ldp + ac) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int64_t t = tt + qq * 2 + rr;
+        rq[rr] = (t < tend && qo * 8 < a.kl) ? *reinterpret_cast<const u32x4*>(a.q + t * a.ldq + qo * 8)
+                                             : u32x4{0, 0, 0, 0};
+      }
     }
   };
-  if (tbeg < tend) gload(tbeg);
-  for (int64_t tt = tbeg; tt < tend; tt += 64) {
+  // one 64-token step from the register set (rp, rq), which is then refilled
+  // with the step two ahead
+  auto step = [&](int64_t tt, u32x4 (&rp)[4], u32x4 (&rq)[2]) {
+    // (nothing of this step moves into the previous one, where it would wait for
+    // loads that are still in flight)
+    __builtin_amdgcn_sched_barrier(0);
     // both tiles stored transposed ([col][t])
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
@@ -199,7 +228,9 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
       *reinterpret_cast<uint32_t*>(Qs + (qo * 8 + cc) * SK_LDS + qq * 2) = e0 | (e1 << 16);
     }
     __syncthreads();
-    if (tt + 64 < tend) gload(tt + 64);
+    // unconditional, so that every step has the same loads in flight and each
+    // wait covers only the older register set (past the split: zeros, unused)
+    gload(tt + 128, rp, rq);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       int kofs = ks * 32 + (lane >> 4) * 8;
@@ -214,7 +245,19 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma16s(qf[i], pf[j], acc[i][j]);
     }
     __syncthreads();
+  };
+  u32x4 rpa[4], rqa[2], rpb[4], rqb[2];
+  gload(tbeg, rpa, rqa);
+  __builtin_amdgcn_sched_barrier(0);  // the first set's loads stay the older ones
+  gload(tbeg + 64, rpb, rqb);
+  // pairs of steps with no branch between them (so the loads in flight are the
+  // same on every path into a step), then an odd last step
+  int64_t tt = tbeg;
+  for (; tt + 64 < tend; tt += 128) {
+    step(tt, rpa, rqa);
+    step(tt + 64, rpb, rqb);
   }
+  if (tt < tend) step(tt, rpa, rqa);
   // lane holds C[a][c..c+3], c = 16 i + 4 (lane >> 4)
   float* dst = a.part + (int64_t)blockIdx.y * a.W * a.kl;
 #pragma unroll
@@ -362,11 +405,17 @@ lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
   a.t_per_split = per; a.part = d.ws;
   a.dA = d.dA; a.dB = d.dA ? nullptr : d.dB; a.scale = d.scale; a.r = d.r; a.nseg = d.nseg;
   for (int i = 0; i < 4; ++i) a.seg.e[i] = d.seg_end[i];
+  // buffer descriptors address a split's rows with 32-bit offsets
+  const int64_t lim = (int64_t)1 << 32;
+  // (the loads run up to two steps past a split's rows)
+  const bool buf = (per + 192) * d.ldp * 2 < lim && (per + 192) * d.ldq * 2 < lim;
   if (S == 1) {
-    hipLaunchKernelGGL(lora_tn_kernel<true>, dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
+    if (buf) hipLaunchKernelGGL((lora_tn_kernel<true, true>), dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((lora_tn_kernel<true, false>), dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
     return check_launch("lora_tn");
   }
-  hipLaunchKernelGGL(lora_tn_kernel<false>, dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
+  if (buf) hipLaunchKernelGGL((lora_tn_kernel<false, true>), dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((lora_tn_kernel<false, false>), dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
   if (d.dA) {
     int64_t n = d.W * d.kl;
     hipLaunchKernelGGL(tn_reduce_dA_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
