@@ -90,14 +90,17 @@ lsl_status lsl_nf4_quantize(const uint16_t* w, int64_t rows, int64_t cols,
 lsl_status lsl_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t rows,
                            int64_t cols, uint16_t* w, lsl_stream stream);
 
-/* NF4 with double-quantized absmax: QLoRA's double quantization (section 3),
- * the storage behind the 3.60 GB store and 113 MB layer buffers the pages
- * report for Llama-3.1-8B ("Soup: ...", section "Layer Streaming: The Mechanism
- * Behind the 4 GB Claim"). The float32 absmax values, flattened row-major, are
- * split into blocks of 256 (the last may be short); per block
- * s = float32(max / 255), q = round-half-even(absmax / s) (float32 division)
- * clamped to [0, 255], q = 0 when s = 0; absmax' = float32(q) * s. The 4-bit
- * codes stay those of lsl_nf4_quantize. */
+/* NF4 with 8-bit absmax codes: the storage behind the 3.60 GB store and 113 MB
+ * layer buffers the pages report for Llama-3.1-8B ("Soup: ...", section "Layer
+ * Streaming: The Mechanism Behind the 4 GB Claim"), which equal 4-bit codes +
+ * one byte per 64 weights + one float32 per 256 absmax values. The pages fix
+ * only those sizes; the 8-bit map is this library's reading, a linear one (not
+ * QLoRA's 8-bit-float map of mean-centred constants, which has the same size).
+ * The float32 absmax values, flattened row-major, are split into blocks of 256
+ * (the last may be short); per block s = float32(max / 255),
+ * q = round-half-even(absmax / s) (float32 division) clamped to [0, 255],
+ * q = 0 when s = 0; absmax' = float32(q) * s. The 4-bit codes stay those of
+ * lsl_nf4_quantize. */
 /* absmax [n] float32 -> q [n] uint8, scale [ceil(n / 256)] float32. Device pointers. */
 lsl_status lsl_nf4dq_quantize_absmax(const float* absmax, int64_t n, uint8_t* q, float* scale,
                                      lsl_stream stream);
@@ -108,7 +111,7 @@ lsl_status lsl_nf4dq_dequant(const uint8_t* codes, const uint8_t* q, const float
 /* ------------------------------------------------------------------ weights */
 enum { LSL_WFMT_NF4 = 0, LSL_WFMT_BF16 = 1, LSL_WFMT_NF4DQ = 2 };
 /* A frozen weight [n_out x k_in] (n_out and k_in multiples of 64): NF4 (nf4
- * codes + absmax), bf16, or NF4 with double-quantized absmax (nf4 codes +
+ * codes + absmax), bf16, or NF4 with 8-bit absmax codes (nf4 codes +
  * absmax_q + absmax_scale). Pointers not used by the format must be NULL.
  * bias (optional, NULL for none): a frozen bf16 vector [n_out] added to the
  * forward output before its rounding, as in the q/k/v projections of Qwen2

@@ -25,7 +25,10 @@ Sources (the pages are cited by title and section):
 
 Parity status: every function here is pinned by tests against closed forms,
 library routines (torch CPU float64 ops, scipy), brute force or finite
-differences; none is "parity unpinned". The pages print no worked example of
+differences; none is "parity unpinned". The model step (model.py: label
+shift, embedding -> layers -> final norm -> head -> cross-entropy, and the
+backward into every layer) is pinned against a torch float64 autograd
+composition of library ops. The pages print no worked example of
 the arithmetic; the one set of printed numbers that fixes a step is the byte
 count of the double-quantized NF4 store (tests/golden/pages_store_sizes.json).
 """

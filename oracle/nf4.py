@@ -82,12 +82,14 @@ def nf4_dequant(packed: np.ndarray, absmax: np.ndarray, rnd=round_bf16) -> np.nd
 
 
 # ---------------------------------------------------------------- double quantisation
-# QLoRA's "double quantization" (Dettmers et al. 2023, section 3) quantises the
-# float32 absmax constants themselves with 8 bits in blocks of 256, keeping one
-# float32 constant per block. That is the storage the pages' sizes imply ("Soup:
-# ...", section "Layer Streaming: The Mechanism Behind the 4 GB Claim": a 3.60 GB
-# base store over 32 layers and two 113 MB buffers for Llama-3.1-8B). The pages
-# give only those sizes; the 8-bit map read here is the plainest one that fits:
+# The pages' sizes ("Soup: ...", section "Layer Streaming: The Mechanism Behind
+# the 4 GB Claim": a 3.60 GB base store over 32 layers and two 113 MB buffers
+# for Llama-3.1-8B) equal 4-bit codes plus one 8-bit absmax code per 64 weights
+# plus one float32 constant per 256 absmax values. The pages fix only those byte
+# counts, not the 8-bit map, so the map below is this build's own reading, the
+# plainest linear one that fits the sizes. (It is not QLoRA's double
+# quantization, which maps the mean-centred constants with 8-bit floats; that
+# scheme has the same byte count.)
 #   * s = float32(max of the 256 absmax values / 255) (float32 division);
 #   * q = round-half-even(absmax / s) (float32 division), clamped to [0, 255];
 #     q = 0 when s = 0;

@@ -686,3 +686,75 @@ def test_reference_logprobs_agree_with_the_training_loss_at_b_zero():
     assert abs(r["loss"] + lp.sum() / r["n_valid"]) < 1e-12
     assert np.all(lp.reshape(batch, seq)[:, -1] == 0) and np.all(lp.reshape(batch, seq)[:, :-1] < 0)
     assert np.allclose(slp, lp.reshape(batch, seq).sum(1))
+
+
+# ------------------------------------------------------------------ model composition
+def _torch_model_loss(ids, emb, fn, lm_head, layers, shape, batch, seq):
+    """Loss, per-token LSE and adapter gradients of a whole model built from torch
+    float64 library ops with autograd, independent of the oracle: F.embedding,
+    merged LoRA weights in F.linear, a complex rotation for RoPE, SDPA with
+    repeated kv heads, F.rms_norm, and F.cross_entropy on logits[:, :-1] against
+    ids[:, 1:] (each sequence predicts its own next token). The head is the
+    embedding table when lm_head is None."""
+    s, d, H = shape.lora_scale, shape.head_dim, shape.hidden
+    T = batch * seq
+    pos = torch.from_numpy(np.tile(np.arange(seq), batch).astype(np.float64))
+    fr = torch.from_numpy(shape.rope_theta ** (-(2 * np.arange(d // 2)) / d))
+    phase = torch.exp(1j * pos[:, None, None] * fr[None, None, :])
+    params = []
+    h = F.embedding(torch.from_numpy(np.asarray(ids, np.int64)), t64(emb))
+    for w, lora in layers:
+        A = {p: t64(lora["A_" + p]).requires_grad_(True) for p in PROJ_IN_OUT(shape)}
+        B = {p: t64(lora["B_" + p]).requires_grad_(True) for p in PROJ_IN_OUT(shape)}
+        params.append((A, B))
+        W = {p: t64(w[p]) + s * (B[p] @ A[p]) for p in PROJ_IN_OUT(shape)}
+        n1 = F.rms_norm(h, (H,), t64(w["norm1"]), eps=shape.rms_eps)
+
+        def rot(a, nh):
+            a = a.reshape(T, nh, d)
+            z = torch.complex(a[..., : d // 2], a[..., d // 2:]) * phase
+            return torch.cat([z.real, z.imag], -1)
+        grp = shape.n_q // shape.n_kv
+        q = rot(F.linear(n1, W["q"]), shape.n_q).view(batch, seq, shape.n_q, d).transpose(1, 2)
+        k = rot(F.linear(n1, W["k"]), shape.n_kv).view(batch, seq, shape.n_kv, d).transpose(1, 2)
+        v = F.linear(n1, W["v"]).view(batch, seq, shape.n_kv, d).transpose(1, 2)
+        o = F.scaled_dot_product_attention(q, k.repeat_interleave(grp, 1), v.repeat_interleave(grp, 1),
+                                           is_causal=True)
+        h = h + F.linear(o.transpose(1, 2).reshape(T, -1), W["o"])
+        n2 = F.rms_norm(h, (H,), t64(w["norm2"]), eps=shape.rms_eps)
+        h = h + F.linear(F.silu(F.linear(n2, W["gate"])) * F.linear(n2, W["up"]), W["down"])
+    hn = F.rms_norm(h, (H,), t64(fn), eps=shape.rms_eps)
+    logits = hn @ t64(emb if lm_head is None else lm_head).T
+    V = logits.shape[-1]
+    tgt = torch.from_numpy(np.asarray(ids, np.int64)).view(batch, seq)[:, 1:].reshape(-1)
+    loss = F.cross_entropy(logits.view(batch, seq, V)[:, :-1].reshape(-1, V), tgt)
+    loss.backward()
+    grads = [{**{"A_" + p: A[p].grad.numpy() for p in A}, **{"B_" + p: B[p].grad.numpy() for p in B}}
+             for A, B in params]
+    return float(loss), torch.logsumexp(logits, -1).detach().numpy(), grads
+
+
+@pytest.mark.parametrize("tied", [True, False])
+def test_model_composition_matches_torch(tied):
+    """The oracle's microbatch (embedding gather, layers, final RMSNorm, head,
+    shifted-label cross-entropy) and its backward through every layer equal a
+    torch autograd composition: loss and LSE to 1e-12, adapter gradients to 1e-9.
+    Two sequences, so a label shift across the sequence boundary (or no shift,
+    or a reversed one) fails; distinct emb and lm_head, so a swapped head fails."""
+    from oracle.model import model_fwd_bwd
+    shape, batch, seq, V = TINY_LAYER, 2, 7, 29
+    rng = np.random.default_rng(11 + tied)
+    layers = [tiny_layer_params(seed=s) for s in (41, 42)]
+    emb = rng.standard_normal((V, shape.hidden)) * 0.5
+    lm = None if tied else rng.standard_normal((V, shape.hidden)) * 0.5
+    fn = 1 + rng.uniform(-0.1, 0.1, shape.hidden)
+    ids = rng.integers(0, V, batch * seq)
+    r = model_fwd_bwd(ids, emb, fn, lm, layers, shape, batch, seq, rnd=identity)
+    loss, lse, grads = _torch_model_loss(ids, emb, fn, lm, layers, shape, batch, seq)
+    assert r["n_valid"] == batch * (seq - 1)
+    assert abs(r["loss"] - loss) <= 1e-12 * abs(loss), (r["loss"], loss)
+    assert np.allclose(r["lse"], lse, rtol=0, atol=1e-12)
+    for li in range(len(layers)):
+        for k, g in grads[li].items():
+            assert np.allclose(r["grads"][li][k], g, rtol=1e-9, atol=1e-12), (li, k)
+            assert np.any(g != 0), (li, k)
