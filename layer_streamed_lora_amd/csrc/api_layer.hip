@@ -28,13 +28,14 @@ extern "C" size_t lsl_attention_workspace_bytes(int32_t, int32_t, int32_t, int32
 
 namespace lsl {
 
-// Optional GEMM timing (see lsl_timing_enable).
+// Optional GEMM timing (see lsl_timing_enable). Per calling thread, so layer
+// calls on other threads neither see nor touch it.
 struct Timing {
   int which = 0;
   std::vector<hipEvent_t> start, stop;
   int count = 0;
 };
-static Timing g_timing;
+static thread_local Timing g_timing;
 
 static void timing_mark(int which, bool begin, hipStream_t s) {
   if (g_timing.which != which || g_timing.count >= (int)g_timing.start.size()) return;
@@ -207,9 +208,10 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
 // y = x W_i^T + s t B_i^T (+ res); t = x A_i^T computed first.
 // Forward of one fused LoRA linear: t = x A^T, y = x W^T + s t B^T (+ res).
 // With y == nullptr only t is computed.
+// dry: only check every launch's conditions (nothing is enqueued).
 static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    int i, const uint16_t* x, uint16_t* t, uint16_t* y, const uint16_t* res,
-                                   float* part, hipStream_t s) {
+                                   float* part, hipStream_t s, bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -218,7 +220,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
     LoraNt nt;
     nt.p = x; nt.ldp = k; nt.T = d.T; nt.K = k; nt.kl = kl; nt.a_full = lo->A[i];
     nt.out = t; nt.ldo = kl; nt.ws = part;
-    LSL_TRY(lora_nt_launch(nt, s));
+    LSL_TRY(dry ? lora_nt_check(nt) : lora_nt_launch(nt, s));
   }
   if (!y) return LSL_OK;
   GemmDesc g;
@@ -232,6 +234,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   g.scale = c->lora_scale;
   g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part;
   if (i == LSL_M_QKV) g.bias = W.qkv_bias;
+  if (dry) return gemm_check(g);
   timing_mark(1 + i, true, s);
   lsl_status st = gemm_launch(g, s);
   timing_mark(1 + i, false, s);
@@ -242,7 +245,8 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
 // dA += s u^T x; dB += s dy^T t (per projection).
 static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    const lsl_lora_grads* gr, int i, const uint16_t* x, const uint16_t* t,
-                                   const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, hipStream_t s) {
+                                   const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, hipStream_t s,
+                                   bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -254,7 +258,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
   nt.p = dy; nt.ldp = n; nt.T = d.T; nt.K = n; nt.kl = kl; nt.b_full = lo->B[i]; nt.r = d.r; nt.nseg = nseg;
   for (int q = 0; q < 4; ++q) nt.seg_end[q] = se[q];
   nt.out = u; nt.ldo = kl; nt.ws = part;
-  LSL_TRY(lora_nt_launch(nt, s));
+  LSL_TRY(dry ? lora_nt_check(nt) : lora_nt_launch(nt, s));
   if (dx) {
     GemmDesc g;
     g.x = dy; g.ldx = n; g.wfmt = c->wfmt; g.kn = true;
@@ -262,25 +266,32 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
     g.M = d.T; g.N = k; g.K = n;
     g.lora = 2; g.la = u; g.ldla = kl; g.kl = kl; g.lb = lo->A[i]; g.r = d.r;
     g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part;
-    timing_mark(5 + i, true, s);
-    lsl_status st = gemm_launch(g, s);
-    timing_mark(5 + i, false, s);
-    LSL_TRY(st);
+    if (dry) {
+      LSL_TRY(gemm_check(g));
+    } else {
+      timing_mark(5 + i, true, s);
+      lsl_status st = gemm_launch(g, s);
+      timing_mark(5 + i, false, s);
+      LSL_TRY(st);
+    }
   }
   LoraTn ta;
   ta.p = x; ta.ldp = k; ta.q = u; ta.ldq = kl; ta.T = d.T; ta.W = k; ta.kl = kl;
   ta.scale = c->lora_scale; ta.dA = gr->dA[i]; ta.ws = part;
-  LSL_TRY(lora_tn_launch(ta, s));
+  LSL_TRY(dry ? lora_tn_check(ta) : lora_tn_launch(ta, s));
   LoraTn tb;
   tb.p = dy; tb.ldp = n; tb.q = t; tb.ldq = kl; tb.T = d.T; tb.W = n; tb.kl = kl;
   tb.scale = c->lora_scale; tb.dB = gr->dB[i]; tb.r = d.r; tb.nseg = nseg;
   for (int q = 0; q < 4; ++q) tb.seg_end[q] = se[q];
   tb.ws = part;
-  return lora_tn_launch(tb, s);
+  return dry ? lora_tn_check(tb) : lora_tn_launch(tb, s);
 }
 
+// dry: check the conditions of every GEMM and side product, enqueue nothing
+// (the other kernels' conditions follow from check_cfg)
 static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, const lsl_lora_set* lo, const uint16_t* x,
-                                int batch, int seq, uint16_t* out, char* ws, const Plan& p, float* o32, hipStream_t s) {
+                                int batch, int seq, uint16_t* out, char* ws, const Plan& p, float* o32, hipStream_t s,
+                                bool dry = false) {
   Dims d = dims_of(c, batch, seq);
   float* part = (float*)(ws + p.part);
   uint16_t* n1 = (uint16_t*)(ws + p.n1);
@@ -290,19 +301,67 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   uint16_t* n2 = (uint16_t*)(ws + p.n2);
   uint16_t* gu = (uint16_t*)(ws + p.gu);
   uint16_t* a = (uint16_t*)(ws + p.a);
+  if (dry) {
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s, true));
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s, true));
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, s, true));
+    return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, s, true);
+  }
   LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s, false));
   LSL_TRY(rope_launch(qkv, d.T, d.NQKV, c->n_q, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(rope_launch(qkv + d.Q, d.T, d.NQKV, c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(lsl_attention_fwd(qkv, qkv + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s, false));
   LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, s));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, s, false));
   LSL_TRY(swiglu_fwd_launch(gu, d.T, d.I, a, s));
   // out == nullptr (the backward's recompute): the layer output itself is not
   // needed, only the LoRA product t of the down projection (for its dB)
-  return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, s);
+  return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, s, false);
+}
+
+// Backward with recompute. dry: check every GEMM's and side product's
+// conditions only. With dx == NULL (the first layer) the q|k|v input-gradient
+// GEMM and the first RMSNorm's backward are skipped, as nothing reads dn1.
+static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, const lsl_lora_set* lora,
+                                 const uint16_t* x_in, const uint16_t* dy, int batch, int seq, uint16_t* dx,
+                                 const lsl_lora_grads* grads, char* w, const Plan& p, hipStream_t s, bool dry) {
+  Dims d = dims_of(cfg, batch, seq);
+  // recompute the forward up to what the backward reads (every intermediate
+  // except the layer output, whose down-projection GEMM is skipped)
+  uint16_t* dn1 = (uint16_t*)(w + p.dn1);
+  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, (float*)(w + p.o32), s, dry));
+  float* part = (float*)(w + p.part);
+  uint16_t* qkv = (uint16_t*)(w + p.qkv);
+  uint16_t* dqkv = (uint16_t*)(w + p.dqkv);
+  uint16_t* da = (uint16_t*)(w + p.da);
+  uint16_t* dgu = (uint16_t*)(w + p.dgu);
+  uint16_t* dn2 = (uint16_t*)(w + p.dn2);
+  uint16_t* dh1 = (uint16_t*)(w + p.dh1);
+  uint16_t* dob = (uint16_t*)(w + p.dob);
+  // MLP
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_DOWN, (uint16_t*)(w + p.a), (uint16_t*)(w + p.td), dy,
+                           (uint16_t*)(w + p.ud), da, part, s, dry));
+  if (!dry) LSL_TRY(swiglu_bwd_launch((uint16_t*)(w + p.gu), da, d.T, d.I, dgu, s));
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), (uint16_t*)(w + p.tgu), dgu,
+                           (uint16_t*)(w + p.ugu), dn2, part, s, dry));
+  if (!dry) LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
+  // attention block
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), (uint16_t*)(w + p.to), dh1,
+                           (uint16_t*)(w + p.uo), dob, part, s, dry));
+  if (!dry) {
+    LSL_TRY(lsl_attention_bwd(qkv, qkv + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
+                              (const float*)(w + p.o32), d.NQKV, d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d,
+                              dqkv, dqkv + d.Q, dqkv + d.Q + d.KV, w + p.attn_ws, p.o32 - p.attn_ws, s));
+    LSL_TRY(rope_launch(dqkv, d.T, d.NQKV, cfg->n_q, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
+    LSL_TRY(rope_launch(dqkv + d.Q, d.T, d.NQKV, cfg->n_kv, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
+  }
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
+                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, s, dry));
+  if (dx && !dry) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
+  return LSL_OK;
 }
 
 }  // namespace lsl
@@ -344,8 +403,9 @@ extern "C" lsl_status decoder_layer_fwd(const lsl_layer_cfg* cfg, const void* la
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x_in, x_out}));
   Plan p = plan_of(cfg, batch, seq, LSL_MODE_FWD);
-  return layer_forward(cfg, ptrs_of(cfg, layer_blob), lora, x_in, batch, seq, x_out, (char*)ws, p, nullptr,
-                       (hipStream_t)stream);
+  const LayerPtrs W = ptrs_of(cfg, layer_blob);
+  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, x_out, (char*)ws, p, nullptr, (hipStream_t)stream, true));
+  return layer_forward(cfg, W, lora, x_in, batch, seq, x_out, (char*)ws, p, nullptr, (hipStream_t)stream);
 }
 
 extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* layer_blob, const lsl_lora_set* lora,
@@ -359,43 +419,11 @@ extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* la
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x_in, dy}));
   if (dx && !aligned(dx, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: dx misaligned", fn);
-  hipStream_t s = (hipStream_t)stream;
-  Plan p = plan_of(cfg, batch, seq, LSL_MODE_BWD);
-  char* w = (char*)ws;
-  LayerPtrs W = ptrs_of(cfg, layer_blob);
-  Dims d = dims_of(cfg, batch, seq);
-  // recompute the forward up to what the backward reads (every intermediate
-  // except the layer output, whose down-projection GEMM is skipped)
-  uint16_t* dn1 = (uint16_t*)(w + p.dn1);
-  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, (float*)(w + p.o32), s));
-  float* part = (float*)(w + p.part);
-  uint16_t* qkv = (uint16_t*)(w + p.qkv);
-  uint16_t* dqkv = (uint16_t*)(w + p.dqkv);
-  uint16_t* da = (uint16_t*)(w + p.da);
-  uint16_t* dgu = (uint16_t*)(w + p.dgu);
-  uint16_t* dn2 = (uint16_t*)(w + p.dn2);
-  uint16_t* dh1 = (uint16_t*)(w + p.dh1);
-  uint16_t* dob = (uint16_t*)(w + p.dob);
-  // MLP
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_DOWN, (uint16_t*)(w + p.a), (uint16_t*)(w + p.td), dy,
-                           (uint16_t*)(w + p.ud), da, part, s));
-  LSL_TRY(swiglu_bwd_launch((uint16_t*)(w + p.gu), da, d.T, d.I, dgu, s));
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), (uint16_t*)(w + p.tgu), dgu,
-                           (uint16_t*)(w + p.ugu), dn2, part, s));
-  LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
-  // attention block
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), (uint16_t*)(w + p.to), dh1,
-                           (uint16_t*)(w + p.uo), dob, part, s));
-  LSL_TRY(lsl_attention_bwd(qkv, qkv + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
-                            (const float*)(w + p.o32), d.NQKV,
-                            d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d, dqkv, dqkv + d.Q, dqkv + d.Q + d.KV,
-                            w + p.attn_ws, p.o32 - p.attn_ws, s));
-  LSL_TRY(rope_launch(dqkv, d.T, d.NQKV, cfg->n_q, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
-  LSL_TRY(rope_launch(dqkv + d.Q, d.T, d.NQKV, cfg->n_kv, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
-                           (uint16_t*)(w + p.uqkv), dn1, part, s));
-  if (dx) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
-  return LSL_OK;
+  const Plan p = plan_of(cfg, batch, seq, LSL_MODE_BWD);
+  const LayerPtrs W = ptrs_of(cfg, layer_blob);
+  // every launch's conditions first, so that a rejected call enqueues nothing
+  LSL_TRY(layer_backward(cfg, W, lora, x_in, dy, batch, seq, dx, grads, (char*)ws, p, (hipStream_t)stream, true));
+  return layer_backward(cfg, W, lora, x_in, dy, batch, seq, dx, grads, (char*)ws, p, (hipStream_t)stream, false);
 }
 
 static void timing_free() {

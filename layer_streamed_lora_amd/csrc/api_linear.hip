@@ -78,12 +78,15 @@ extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_we
   LoraNt nt;
   nt.p = x; nt.ldp = W->k_in; nt.T = T; nt.K = W->k_in; nt.kl = r; nt.a_full = A;
   nt.out = t_out; nt.ldo = r; nt.ws = (float*)ws;
-  LSL_TRY(lora_nt_launch(nt, s));
   GemmDesc g;
   g.x = x; g.ldx = W->k_in; weight_into(g, W); g.kn = false;
   g.M = T; g.N = W->n_out; g.K = W->k_in;
   g.lora = 1; g.la = t_out; g.ldla = r; g.kl = r; g.lb = B; g.r = r; g.nseg = 1; g.seg_end[0] = W->n_out;
   g.scale = scale; g.y = y; g.ldy = W->n_out; g.split_ws = (float*)ws; g.bias = W->bias;
+  // every launch's conditions first, so that a rejected call enqueues nothing
+  LSL_TRY(lora_nt_check(nt));
+  LSL_TRY(gemm_check(g));
+  LSL_TRY(lora_nt_launch(nt, s));
   return gemm_launch(g, s);
 }
 
@@ -108,21 +111,24 @@ extern "C" lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, cons
   LoraNt nt;
   nt.p = dy; nt.ldp = N; nt.T = T; nt.K = N; nt.kl = r; nt.b_full = B; nt.r = r; nt.nseg = 1; nt.seg_end[0] = N;
   nt.out = u; nt.ldo = r; nt.ws = part;
-  LSL_TRY(lora_nt_launch(nt, s));
-  if (dx) {
-    GemmDesc g;
-    g.x = dy; g.ldx = N; weight_into(g, W); g.kn = true;
-    g.M = T; g.N = K; g.K = N;
-    g.lora = 2; g.la = u; g.ldla = r; g.kl = r; g.lb = A; g.r = r;
-    g.scale = scale; g.y = dx; g.ldy = K; g.split_ws = part;
-    LSL_TRY(gemm_launch(g, s));
-  }
+  GemmDesc g;
+  g.x = dy; g.ldx = N; weight_into(g, W); g.kn = true;
+  g.M = T; g.N = K; g.K = N;
+  g.lora = 2; g.la = u; g.ldla = r; g.kl = r; g.lb = A; g.r = r;
+  g.scale = scale; g.y = dx; g.ldy = K; g.split_ws = part;
   LoraTn ta;
   ta.p = x; ta.ldp = K; ta.q = u; ta.ldq = r; ta.T = T; ta.W = K; ta.kl = r; ta.scale = scale; ta.dA = dA; ta.ws = part;
-  LSL_TRY(lora_tn_launch(ta, s));
   LoraTn tb;
   tb.p = dy; tb.ldp = N; tb.q = t; tb.ldq = r; tb.T = T; tb.W = N; tb.kl = r; tb.scale = scale; tb.dB = dB;
   tb.r = r; tb.nseg = 1; tb.seg_end[0] = N; tb.ws = part;
+  // every launch's conditions first, so that a rejected call enqueues nothing
+  LSL_TRY(lora_nt_check(nt));
+  if (dx) LSL_TRY(gemm_check(g));
+  LSL_TRY(lora_tn_check(ta));
+  LSL_TRY(lora_tn_check(tb));
+  LSL_TRY(lora_nt_launch(nt, s));
+  if (dx) LSL_TRY(gemm_launch(g, s));
+  LSL_TRY(lora_tn_launch(ta, s));
   return lora_tn_launch(tb, s);
 }
 

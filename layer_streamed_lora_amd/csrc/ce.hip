@@ -194,11 +194,12 @@ extern "C" lsl_status fused_ce_loss_fwd(const uint16_t* hN, const uint16_t* w_lm
   }
   LSL_TRY(check_ptrs(fn, {hN}));
   LSL_TRY(check_ptrs(fn, {labels, lse}, 4));
-  hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
   GemmDesc g;
   g.x = hN; g.ldx = H; g.wfmt = LSL_WFMT_BF16; g.wb = w_lm; g.M = T; g.N = V; g.K = H;
   g.epi = 1; g.labels = labels; g.part = w + p.part; g.zlab = (float*)(w + p.zlab); g.ignore = ignore_index;
   g.vocab = V;
+  LSL_TRY(gemm_check(g));  // before anything is enqueued
+  hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
   LSL_TRY(gemm_launch(g, s));
   const int bn = gemm_ce_tile_n(T, V, H);
   int64_t ntiles = (V + bn - 1) / bn;
@@ -224,28 +225,36 @@ extern "C" lsl_status fused_ce_loss_bwd(const uint16_t* hN, const uint16_t* w_lm
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   float* nvalid = (float*)(w + p.nvalid);
-  hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
   uint16_t* G = (uint16_t*)(w + p.g);
   float* dh32 = (float*)(w + p.dh32);
   const int64_t nchunks = (V + CE_CHUNK - 1) / CE_CHUNK;
-  for (int64_t c = 0; c < nchunks; ++c) {
+  // the two GEMMs of vocabulary chunk c: G = coef (softmax - onehot) for the
+  // chunk, bf16 [T x vc]; then dH (+)= G W_c in float32
+  auto chunk = [&](int64_t c, GemmDesc& g1, GemmDesc& g2) {
     const int64_t v0 = c * CE_CHUNK;
     const int64_t vc = std::min(CE_CHUNK, V - v0);
     const uint16_t* wc = w_lm + v0 * H;
-    // G = coef (softmax - onehot) for this chunk, bf16 [T x vc]
-    GemmDesc g1;
     g1.x = hN; g1.ldx = H; g1.wfmt = LSL_WFMT_BF16; g1.wb = wc; g1.M = T; g1.N = vc; g1.K = H;
     g1.epi = 2; g1.labels = labels; g1.lse = lse; g1.nvalid = nvalid; g1.gscale = grad_scale;
     g1.ignore = ignore_index; g1.vocab_off = v0; g1.vocab = V;
     g1.y = G; g1.ldy = vc;
-    LSL_TRY(gemm_launch(g1, s));
-    // dH (+)= G W_c in float32
-    GemmDesc g2;
     g2.x = G; g2.ldx = vc; g2.wfmt = LSL_WFMT_BF16; g2.kn = true; g2.wb = wc;
     g2.M = T; g2.N = H; g2.K = vc;
     g2.epi = 3; g2.out32 = dh32; g2.ldo32 = H; g2.first = c == 0 ? 1 : 0;
     g2.acc_splits = p.splits; g2.o32_split = T * H;
     g2.y = (p.splits == 1 && c == nchunks - 1) ? dhN : nullptr; g2.ldy = H;
+  };
+  for (int64_t c = 0; c < nchunks; ++c) {  // every chunk's conditions before anything is enqueued
+    GemmDesc g1, g2;
+    chunk(c, g1, g2);
+    LSL_TRY(gemm_check(g1));
+    LSL_TRY(gemm_check(g2));
+  }
+  hipLaunchKernelGGL(ce_count_valid_kernel, dim3(1), dim3(256), 0, s, labels, T, ignore_index, V, nvalid);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    GemmDesc g1, g2;
+    chunk(c, g1, g2);
+    LSL_TRY(gemm_launch(g1, s));
     LSL_TRY(gemm_launch(g2, s));
   }
   if (p.splits > 1) {

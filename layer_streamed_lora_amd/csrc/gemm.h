@@ -31,6 +31,8 @@ struct GemmDesc {
   float* split_ws = nullptr;
 };
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
+// The conditions gemm_launch rejects, checked without launching anything.
+lsl_status gemm_check(const GemmDesc& d);
 // Reduction splits gemm_launch uses for a bf16-epilogue GEMM of this shape, and
 // the float32 scratch they need (0 when the GEMM is not split).
 int gemm_splits(int64_t M, int64_t N, int64_t K);

@@ -29,6 +29,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "nf4.h"
+#include "api_util.h"
 
 namespace lsl {
 
@@ -71,9 +72,12 @@ enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_CEGRAD = 2, EPI_ACC32 = 3 };
 LSL_DEV uint32_t lo_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 LSL_DEV uint32_t hi_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
-// Buffer resource over [base, base + bytes): loads past the end return zeros,
-// so partial tiles need no branches. The fourth descriptor word is the gfx9
-// raw-buffer format.
+// Buffer resource over [base, base + bytes): loads whose per-lane (vector)
+// offset is at or past the end return zeros, so partial tiles need no branches.
+// The scalar offset of a buffer load is not part of that range check, so every
+// loader keeps whatever can run past the end (rows past M or N, columns past N)
+// in the vector offset and starts the descriptor at the uniform part of the
+// address instead. The fourth descriptor word is the gfx9 raw-buffer format.
 LSL_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
@@ -91,7 +95,10 @@ LSL_DEV uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) 
 LSL_DEV int xswz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // ---- row-major bf16 tile loader: ROWS rows x 64 k, 16 B chunks, 8 chunks per
-// row; thread -> rows tid/8 + 32 i. Per K-step only the scalar offset changes.
+// row; thread -> rows tid/8 + 32 i. Chunk i reads through a descriptor that
+// starts 32 i rows further on (and ends with the matrix), so the one per-lane
+// offset covers every chunk and a row at or past `rows` reads zeros; per K-step
+// only the scalar offset (the column k0) changes.
 template <int ROWS>
 struct RowLoader {
   static constexpr int CH = ROWS / 32;
@@ -100,12 +107,14 @@ struct RowLoader {
   LSL_DEV void init(int64_t ld, int64_t r0, int tid) {
     voff = (uint32_t)(((r0 + (tid >> 3)) * ld + (tid & 7) * 8) * 2);
   }
-  // base/ld/rows come straight from the kernel arguments, so the descriptor is uniform
+  // base/ld/rows come straight from the kernel arguments, so the descriptors are uniform
   LSL_DEV void load(const uint16_t* base, int64_t ld, int64_t rows, int64_t k0) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, rows * ld * 2);
-    const uint32_t rstride = (uint32_t)(32 * ld * 2);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) v[i] = bload16(rs, voff, (uint32_t)(i * rstride + k0 * 2));
+    for (int i = 0; i < CH; ++i) {
+      const int64_t left = rows - 32 * i;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + 32 * i * ld, left > 0 ? left * ld * 2 : 0);
+      v[i] = bload16(rs, voff, (uint32_t)(k0 * 2));
+    }
   }
   LSL_DEV void store(uint16_t* lds, int tid) const {
     const int r = tid >> 3, c = (tid & 7) * 8;
@@ -200,12 +209,13 @@ struct WLoader<LSL_WFMT_BF16, true, BN> {
   }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
     const int64_t rows = a.kwrap ? a.kwrap : a.K;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb, rows * a.N * 2);
-    const uint32_t rowb = (uint32_t)(a.N * 2);
     if (a.kwrap && k0 >= a.kwrap) k0 -= a.kwrap;  // K <= 2 kwrap (checked on the host)
+    // descriptor from row k0 + rr to the end of the matrix: the column offset
+    // (in the vector offset) is range-checked
 #pragma unroll
     for (int rr = 0; rr < KR; ++rr) {
-      u32x4 v = bload16(rs, voff, (uint32_t)((k0 + rr) * rowb));
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb + (k0 + rr) * a.N, (rows - k0 - rr) * a.N * 2);
+      u32x4 v = bload16(rs, voff, 0);
       w[rr][0] = v[0]; w[rr][1] = v[1]; w[rr][2] = v[2]; w[rr][3] = v[3];
     }
   }
@@ -826,9 +836,11 @@ struct BigW<LSL_WFMT_BF16, true> {
     voff = (uint32_t)((((int64_t)(tid >> 3)) * a.N + n0 + (tid & 7) * 32) * 2);
   }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb, a.K * a.N * 2);
+    // descriptor from row k0 to the end of the matrix: a column past N in the
+    // last row reads zeros instead of the bytes after the matrix
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb + k0 * a.N, (a.K - k0) * a.N * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = bload16(rs, voff + 16 * i, (uint32_t)(k0 * a.N * 2));
+    for (int i = 0; i < 4; ++i) v[i] = bload16(rs, voff + 16 * i, 0);
   }
   LSL_DEV void fetch(int, const float*, float (&)[8]) const {}
   LSL_DEV void emit(int i, const float (&)[8], uint16_t* __restrict__ lds, int tid) const {
@@ -1397,7 +1409,9 @@ size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
   return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
 }
 
-lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
+// Every condition gemm_launch can reject, checked without launching anything,
+// so that an entry point can validate all of its GEMMs before the first launch.
+lsl_status gemm_check(const GemmDesc& d) {
   if (d.M == 0 || d.N == 0) return LSL_OK;
   if (d.K % BK || d.N % 8 || d.K == 0)
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: K (%lld) must be a multiple of 64 and N (%lld) of 8",
@@ -1412,6 +1426,26 @@ lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
   const int64_t lim = ((int64_t)1 << 32) - 1;
   if ((d.M + 256) * d.ldx * 2 > lim || (d.N + 128) * d.K * 2 > lim)
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: operand larger than 4 GiB");
+  if (d.epi == EPI_BF16) {
+    if (gemm_splits(d.M, d.N, d.K) > 1 && !d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
+    return LSL_OK;
+  }
+  if (d.wfmt != LSL_WFMT_BF16 || d.lora) return set_error(LSL_ERR_UNSUPPORTED, "gemm: CE epilogues take a bf16 weight");
+  if (!((d.epi == EPI_LSE && !d.kn) || (d.epi == EPI_CEGRAD && !d.kn) || (d.epi == EPI_ACC32 && d.kn)))
+    return set_error(LSL_ERR_UNSUPPORTED, "gemm: epilogue %d with layout %d", d.epi, (int)d.kn);
+  if (d.epi == EPI_ACC32 && d.acc_splits > 1) {
+    if (d.y) return set_error(LSL_ERR_UNSUPPORTED, "gemm: split float accumulation has no bf16 copy");
+    const int KT = (int)(d.K / BK);
+    const int per = (KT + d.acc_splits - 1) / d.acc_splits;
+    if (d.first && (KT + per - 1) / per != d.acc_splits)  // the first pass must initialise every split
+      return set_error(LSL_ERR_UNSUPPORTED, "gemm: %d accumulation splits of %d steps", d.acc_splits, KT);
+  }
+  return LSL_OK;
+}
+
+lsl_status gemm_launch(const GemmDesc& d, hipStream_t s) {
+  if (d.M == 0 || d.N == 0) return LSL_OK;
+  LSL_TRY(gemm_check(d));
   GemmKArgs a{};
   a.x = d.x; a.ldx = d.ldx;
   a.wb = d.wb; a.wq = d.wq; a.wa = d.wa; a.wq8 = d.wq8; a.wsc = d.wsc;

@@ -353,12 +353,25 @@ size_t lora_tn_ws_bytes(int64_t T, int64_t W) {
   return S > 1 ? (size_t)S * W * 64 * sizeof(float) : 0;
 }
 
-lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
+lsl_status lora_nt_check(const LoraNt& d) {
   if (d.T == 0) return LSL_OK;
   if (d.K % 64 || d.kl <= 0 || d.kl > 64 || d.kl % 8)
     return set_error(LSL_ERR_UNSUPPORTED, "lora side product: K %% 64 and kl in [8, 64] multiple of 8 required");
   if ((d.T + 64) * d.ldp * 2 >= ((int64_t)1 << 32))
     return set_error(LSL_ERR_UNSUPPORTED, "lora side product: operand larger than 4 GiB");
+  return LSL_OK;
+}
+
+lsl_status lora_tn_check(const LoraTn& d) {
+  if (d.W == 0) return LSL_OK;
+  if (d.kl <= 0 || d.kl > 64 || d.kl % 8 || d.W % 8)
+    return set_error(LSL_ERR_UNSUPPORTED, "lora grad: kl in [8, 64] multiple of 8 and W %% 8 required");
+  return LSL_OK;
+}
+
+lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
+  if (d.T == 0) return LSL_OK;
+  LSL_TRY(lora_nt_check(d));
   char* ws = (char*)d.ws;
   NtArgs a{};
   a.p = d.p; a.ldp = d.ldp; a.T = d.T; a.K = d.K; a.kl = d.kl; a.out = d.out; a.ldo = d.ldo;
@@ -392,8 +405,7 @@ lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
 
 lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
   if (d.W == 0) return LSL_OK;
-  if (d.kl <= 0 || d.kl > 64 || d.kl % 8 || d.W % 8)
-    return set_error(LSL_ERR_UNSUPPORTED, "lora grad: kl in [8, 64] multiple of 8 and W %% 8 required");
+  LSL_TRY(lora_tn_check(d));
   if (d.T == 0) return LSL_OK;
   int64_t tiles = (d.W + 127) / 128;
   int S = pick_splits(tiles, d.T, TN_TARGET, TN_MIN_STEPS);

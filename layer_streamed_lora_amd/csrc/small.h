@@ -25,6 +25,9 @@ size_t lora_nt_ws_bytes(int64_t T, int64_t K);
 size_t lora_tn_ws_bytes(int64_t T, int64_t W);
 lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s);
 lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s);
+// the conditions the launches reject, checked without launching anything
+lsl_status lora_nt_check(const LoraNt& d);
+lsl_status lora_tn_check(const LoraTn& d);
 
 lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y, hipStream_t s);
 lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,

@@ -195,3 +195,43 @@ def test_workspace_queries_with_zero_tokens(L):
     assert lib.lsl_ce_workspace_bytes(0, 4096, 128256) > 0
     assert L.lora_linear_workspace_bytes(0, 4096, 4096, 16) >= 0
     assert lib.lsl_attention_workspace_bytes(0, 0, 32, 8, 128) >= 0
+
+
+def test_size_limits_rejected_before_any_launch(L):
+    """Shapes past the 32-bit buffer-offset limits are rejected by every entry
+    point before its first launch (these calls would fail on any launch here,
+    where there is no GPU): the LoRA linear's side product and GEMM, the
+    cross-entropy's lm_head GEMM (ahead of its label count), and a decoder
+    layer whose down-projection GEMM is the first to exceed the limit."""
+    from layer_streamed_lora_amd import _abi
+    from layer_streamed_lora_amd import model as M
+    from synth.configs import LLAMA8B_LAYER
+    lib = L.lib()
+    big = 1 << 62
+    T = 1 << 20  # (T + 64) x 2048 bf16 activations exceed 4 GiB
+    w = _abi.Weight(_abi.WFMT_BF16, 0, 64, 2048, None, None, 256)
+    assert lib.lora_linear_fwd(256, T, C.byref(w), 256, 256, 8, 2.0, 256, 256, 256, big, None) == \
+        _abi.LSL_ERR_UNSUPPORTED
+    assert b"4 GiB" in lib.lsl_last_error()
+    # the backward's u = dy B reads dy [T x n_out]: n_out 2048 exceeds the limit
+    w2 = _abi.Weight(_abi.WFMT_BF16, 0, 2048, 64, None, None, 256)
+    assert lib.lora_linear_bwd(256, 256, 256, T, C.byref(w2), 256, 256, 8, 2.0, 256, 256, 256, 256, big, None) == \
+        _abi.LSL_ERR_UNSUPPORTED
+    # vocabulary 2^21 x hidden 1024 bf16 head: (V + 128) H 2 bytes > 4 GiB; ce_check allows it
+    V, H = 1 << 21, 1024
+    assert lib.fused_ce_loss_fwd(256, 256, 256, 64, H, V, -100, 256, 256, 256, big, None) == _abi.LSL_ERR_UNSUPPORTED
+    assert b"4 GiB" in lib.lsl_last_error()
+    # the backward works per 32768-column chunk, so that head is fine there; its
+    # gradient chunk G [T x 32768] bf16 exceeds the limit from T = 65280 tokens
+    assert lib.fused_ce_loss_bwd(256, 256, 256, 256, 70000, 64, 65536, -100, 1.0, 256, 256, big, None) == \
+        _abi.LSL_ERR_UNSUPPORTED
+    assert lib.fused_ce_logprobs(256, 256, 256, 64, H, V, -100, 1, 256, 256, 256, big, None) == _abi.LSL_ERR_UNSUPPORTED
+    # one Llama-8B layer over 160000 tokens: the inter-wide operands exceed 4 GiB
+    cfg = M.layer_cfg(LLAMA8B_LAYER)
+    lo = _abi.LoraSet((C.c_void_p * 4)(*[256] * 4), (C.c_void_p * 4)(*[256] * 4))
+    gr = _abi.LoraGrads((C.c_void_p * 4)(*[256] * 4), (C.c_void_p * 4)(*[256] * 4))
+    assert lib.decoder_layer_fwd(C.byref(cfg), 256, C.byref(lo), 256, 1, 160000, 256, 256, big, None) == \
+        _abi.LSL_ERR_UNSUPPORTED
+    assert b"4 GiB" in lib.lsl_last_error()
+    assert lib.decoder_layer_bwd(C.byref(cfg), 256, C.byref(lo), 256, 256, 1, 160000, 256, C.byref(gr), 256, big,
+                                 None) == _abi.LSL_ERR_UNSUPPORTED
