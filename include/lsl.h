@@ -217,6 +217,47 @@ typedef struct { float* dA[4]; float* dB[4]; } lsl_lora_grads;
 
 enum { LSL_MODE_FWD = 0, LSL_MODE_BWD = 1 };
 size_t lsl_layer_workspace_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode);
+/* Where decoder_layer_fwd / decoder_layer_bwd keep each intermediate inside
+ * their workspace (byte offsets from ws; T = batch * seq, r = lora_r,
+ * d = head_dim, NQKV = (n_q + 2 n_kv) d), so that every rounding point of the
+ * layer can be read back and checked on its own. After decoder_layer_fwd the
+ * forward entries hold that call's values; after decoder_layer_bwd the forward
+ * entries hold the recomputed forward (the down projection's output is not
+ * recomputed) and the backward entries the backward's values. They stay valid
+ * until the workspace is used again. Backward entries are 0 in mode
+ * LSL_MODE_FWD; with the adapters off the t_* entries are not written. */
+typedef struct {
+  /* forward */
+  uint64_t n1;        /* bf16 [T x hidden]  rmsnorm(x_in, norm1) */
+  uint64_t t_qkv;     /* bf16 [T x 3r]      n1 [A_q; A_k; A_v]^T */
+  uint64_t qkv;       /* bf16 [T x NQKV]    q|k|v projections (before RoPE) */
+  uint64_t qk_rope;   /* bf16, row stride NQKV: the RoPE'd q and k columns (v columns unused) */
+  uint64_t attn;      /* bf16 [T x n_q d]   attention output */
+  uint64_t lse;       /* float [batch x n_q x seq] attention log-sum-exp */
+  uint64_t t_o;       /* bf16 [T x r]       attn A_o^T */
+  uint64_t h1;        /* bf16 [T x hidden]  x_in + o projection */
+  uint64_t n2;        /* bf16 [T x hidden]  rmsnorm(h1, norm2) */
+  uint64_t t_gu;      /* bf16 [T x 2r]      n2 [A_gate; A_up]^T */
+  uint64_t gu;        /* bf16 [T x 2 inter] gate | up projections */
+  uint64_t act;       /* bf16 [T x inter]   silu(gate) * up */
+  uint64_t t_down;    /* bf16 [T x r]       act A_down^T */
+  /* backward */
+  uint64_t u_down;    /* bf16 [T x r]       dy B_down */
+  uint64_t d_act;     /* bf16 [T x inter]   gradient of act */
+  uint64_t d_gu;      /* bf16 [T x 2 inter] gradients of gate | up */
+  uint64_t u_gu;      /* bf16 [T x 2r]      d_gate B_gate | d_up B_up */
+  uint64_t d_n2;      /* bf16 [T x hidden] */
+  uint64_t d_h1;      /* bf16 [T x hidden] */
+  uint64_t u_o;       /* bf16 [T x r]       d_h1 B_o */
+  uint64_t d_attn;    /* bf16 [T x n_q d]   gradient of the attention output */
+  uint64_t d_qk_rope; /* bf16, row stride NQKV: gradients of the RoPE'd q and k columns */
+  uint64_t d_qkv;     /* bf16 [T x NQKV]    dq, dk (inverse RoPE applied) and dv */
+  uint64_t u_qkv;     /* bf16 [T x 3r]      per projection d_p B_p */
+  uint64_t d_n1;      /* bf16 [T x hidden]  (written only when dx is not NULL) */
+  uint64_t attn32;    /* float [T x n_q d]  attention output before its rounding */
+} lsl_layer_ws_map;
+lsl_status lsl_layer_workspace_map(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode,
+                                   lsl_layer_ws_map* out);
 /* x_in, x_out [batch*seq x hidden] bf16. Nothing is saved: the caller keeps
  * x_in as the layer-boundary checkpoint for the backward. lora may be NULL:
  * the adapters are off and every projection is the frozen base alone (the
@@ -246,7 +287,14 @@ lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* layer_blob,
  * queue with the compute stream: HIP maps streams onto a few hardware queues
  * (GPU_MAX_HW_QUEUES, 4 by default) and two streams on one queue run one after
  * the other, which silently removes the overlap. Keeping one copy stream per
- * process, and few streams in all, avoids that. */
+ * process, and few streams in all, avoids that.
+ * Debugging aid: with the environment variable LSL_POISON_SLOTS set to a
+ * non-zero value when the pool is created, every load first fills the whole
+ * slot with 0xFF bytes on the copy stream (after the wait for the slot's
+ * release), so a read outside the load/acquire/release window, or past the
+ * layer's bytes, yields NaN weights instead of a silently stale layer (the
+ * pages warn that streaming failures are silent: "Exact Layer Streaming ...",
+ * abstract). Results are unchanged when the slots are used in order. */
 typedef struct lsl_pool lsl_pool;
 lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, int32_t n_slots,
                            size_t slot_bytes, lsl_stream copy_stream);

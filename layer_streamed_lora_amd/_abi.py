@@ -38,6 +38,15 @@ class LayerLayout(C.Structure):
                 ("scale_off", C.c_uint64 * 4), ("bias_off", C.c_uint64)]
 
 
+WS_MAP_FIELDS = ("n1", "t_qkv", "qkv", "qk_rope", "attn", "lse", "t_o", "h1", "n2", "t_gu", "gu", "act", "t_down",
+                 "u_down", "d_act", "d_gu", "u_gu", "d_n2", "d_h1", "u_o", "d_attn", "d_qk_rope", "d_qkv", "u_qkv",
+                 "d_n1", "attn32")
+
+
+class LayerWsMap(C.Structure):
+    _fields_ = [(n, C.c_uint64) for n in WS_MAP_FIELDS]
+
+
 class LoraSet(C.Structure):
     _fields_ = [("A", vp * 4), ("B", vp * 4)]
 
@@ -65,6 +74,7 @@ PROTOS = {
     "lora_linear_bwd": (i32, [vp, vp, vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
     "lsl_layer_layout_get": (i32, [C.POINTER(LayerCfg), C.POINTER(LayerLayout)]),
     "lsl_layer_workspace_bytes": (sz, [C.POINTER(LayerCfg), i32, i32, i32]),
+    "lsl_layer_workspace_map": (i32, [C.POINTER(LayerCfg), i32, i32, i32, C.POINTER(LayerWsMap)]),
     "decoder_layer_fwd": (i32, [C.POINTER(LayerCfg), vp, C.POINTER(LoraSet), vp, i32, i32, vp, vp, sz, vp]),
     "decoder_layer_bwd": (i32, [C.POINTER(LayerCfg), vp, C.POINTER(LoraSet), vp, vp, i32, i32, vp,
                                 C.POINTER(LoraGrads), vp, sz, vp]),

@@ -122,9 +122,13 @@ static void layout_of(const lsl_layer_cfg* c, lsl_layer_layout* L) {
 }
 
 // Workspace plan (byte offsets, all 256-aligned).
+// qkv holds the q|k|v GEMM output and qkr its RoPE'd q and k columns (same
+// row stride; the v columns of qkr are unused); in the backward the attention
+// writes dq and dk into dqkr and dv into dqkv, whose q and k columns then take
+// the inverse RoPE of dqkr. So every rounding point keeps its own tensor.
 struct Plan {
-  size_t n1, tqkv, qkv, o, lse, to, h1, n2, tgu, gu, a, td;                  // forward
-  size_t ud, da, dgu, ugu, dn2, dh1, uo, dob, dqkv, uqkv, dn1, attn_ws, o32;  // backward
+  size_t n1, tqkv, qkv, qkr, o, lse, to, h1, n2, tgu, gu, a, td;                    // forward
+  size_t ud, da, dgu, ugu, dn2, dh1, uo, dob, dqkr, dqkv, uqkv, dn1, attn_ws, o32;  // backward
   size_t part, total;
 };
 
@@ -137,6 +141,7 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
   p.n1 = take(T * d.H * 2);
   p.tqkv = take(T * 3 * d.r * 2);
   p.qkv = take(T * d.NQKV * 2);
+  p.qkr = take(T * d.NQKV * 2);
   p.o = take(T * d.Q * 2);
   p.lse = take((size_t)batch * c->n_q * seq * 4);
   p.to = take(T * d.r * 2);
@@ -159,6 +164,7 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
     p.dh1 = take(T * d.H * 2);
     p.uo = take(T * d.r * 2);
     p.dob = take(T * d.Q * 2);
+    p.dqkr = take(T * d.NQKV * 2);
     p.dqkv = take(T * d.NQKV * 2);
     p.uqkv = take(T * 3 * d.r * 2);
     p.dn1 = take(T * d.H * 2);
@@ -309,9 +315,10 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   }
   LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s));
   LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s, false));
-  LSL_TRY(rope_launch(qkv, d.T, d.NQKV, c->n_q, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
-  LSL_TRY(rope_launch(qkv + d.Q, d.T, d.NQKV, c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
-  LSL_TRY(lsl_attention_fwd(qkv, qkv + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
+  // q and k heads are adjacent in each row and share the frequencies: one launch
+  uint16_t* qkr = (uint16_t*)(ws + p.qkr);
+  LSL_TRY(rope_launch(qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
+  LSL_TRY(lsl_attention_fwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
   LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s, false));
   LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
@@ -335,6 +342,8 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
   LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, (float*)(w + p.o32), s, dry));
   float* part = (float*)(w + p.part);
   uint16_t* qkv = (uint16_t*)(w + p.qkv);
+  uint16_t* qkr = (uint16_t*)(w + p.qkr);
+  uint16_t* dqkr = (uint16_t*)(w + p.dqkr);
   uint16_t* dqkv = (uint16_t*)(w + p.dqkv);
   uint16_t* da = (uint16_t*)(w + p.da);
   uint16_t* dgu = (uint16_t*)(w + p.dgu);
@@ -352,11 +361,11 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), (uint16_t*)(w + p.to), dh1,
                            (uint16_t*)(w + p.uo), dob, part, s, dry));
   if (!dry) {
-    LSL_TRY(lsl_attention_bwd(qkv, qkv + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
+    LSL_TRY(lsl_attention_bwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
                               (const float*)(w + p.o32), d.NQKV, d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d,
-                              dqkv, dqkv + d.Q, dqkv + d.Q + d.KV, w + p.attn_ws, p.o32 - p.attn_ws, s));
-    LSL_TRY(rope_launch(dqkv, d.T, d.NQKV, cfg->n_q, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
-    LSL_TRY(rope_launch(dqkv + d.Q, d.T, d.NQKV, cfg->n_kv, d.d, seq, cfg->rope_theta, &cfg->rope_scaling, 1, s));
+                              dqkr, dqkr + d.Q, dqkv + d.Q + d.KV, w + p.attn_ws, p.o32 - p.attn_ws, s));
+    LSL_TRY(rope_launch(dqkr, dqkv, d.T, d.NQKV, cfg->n_q + cfg->n_kv, d.d, seq, cfg->rope_theta, &cfg->rope_scaling,
+                        1, s));
   }
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
                            (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, s, dry));
@@ -378,6 +387,24 @@ extern "C" lsl_status lsl_layer_layout_get(const lsl_layer_cfg* cfg, lsl_layer_l
 extern "C" size_t lsl_layer_workspace_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode) {
   if (check_cfg(cfg, "lsl_layer_workspace_bytes") != LSL_OK || batch < 0 || seq < 0) return 0;
   return plan_of(cfg, batch, seq, mode).total;
+}
+
+extern "C" lsl_status lsl_layer_workspace_map(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode,
+                                              lsl_layer_ws_map* out) {
+  const char* fn = "lsl_layer_workspace_map";
+  LSL_TRY(check_cfg(cfg, fn));
+  if (!out || batch < 0 || seq < 0 || (mode != LSL_MODE_FWD && mode != LSL_MODE_BWD))
+    return set_error(LSL_ERR_INVALID_ARG, "%s: bad arguments", fn);
+  const Plan p = plan_of(cfg, batch, seq, mode);
+  *out = lsl_layer_ws_map{};
+  out->n1 = p.n1; out->t_qkv = p.tqkv; out->qkv = p.qkv; out->qk_rope = p.qkr; out->attn = p.o; out->lse = p.lse;
+  out->t_o = p.to; out->h1 = p.h1; out->n2 = p.n2; out->t_gu = p.tgu; out->gu = p.gu; out->act = p.a; out->t_down = p.td;
+  if (mode == LSL_MODE_BWD) {
+    out->u_down = p.ud; out->d_act = p.da; out->d_gu = p.dgu; out->u_gu = p.ugu; out->d_n2 = p.dn2; out->d_h1 = p.dh1;
+    out->u_o = p.uo; out->d_attn = p.dob; out->d_qk_rope = p.dqkr; out->d_qkv = p.dqkv; out->u_qkv = p.uqkv;
+    out->d_n1 = p.dn1; out->attn32 = p.o32;
+  }
+  return LSL_OK;
 }
 
 // lora may be NULL in the forward only (adapters off)

@@ -163,7 +163,7 @@ extern "C" lsl_status lsl_rope(uint16_t* x, int64_t T, int64_t ld, int32_t n_hea
   LSL_TRY(check_rope_scaling(fn, scaling));
   if (T == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x}));
-  return rope_launch(x, T, ld, n_heads, head_dim, seq, theta, scaling, inverse, (hipStream_t)stream);
+  return rope_launch(x, x, T, ld, n_heads, head_dim, seq, theta, scaling, inverse, (hipStream_t)stream);
 }
 
 extern "C" lsl_status lsl_swiglu_fwd(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, lsl_stream stream) {

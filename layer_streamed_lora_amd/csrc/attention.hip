@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
         for (int qs = 0; qs < NQS; ++qs) sc[kvs][qs] = mfma(kf, qf[qs][ks], sc[kvs][qs]);
       }
     }
-    bf16x8 pf[NQS][2];
+    bf16x8 pf[NQS][2], pl[NQS][2];
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       const int q = q0 + qs * 16 + c16;
@@ -186,17 +186,23 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
       for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[ds][qs][i] *= alpha;
-      pf[qs][0] = pack8(sc[0][qs], sc[1][qs]);
-      pf[qs][1] = pack8(sc[2][qs], sc[3][qs]);
+      split8(sc[0][qs], sc[1][qs], pf[qs][0], pl[qs][0]);
+      split8(sc[2][qs], sc[3][qs], pf[qs][1], pl[qs][1]);
     }
-    // O^T += V^T P^T (reduction over the 64 keys in the permuted order of pf)
+    // O^T += V^T P^T (reduction over the 64 keys in the permuted order of pf),
+    // with P as a hi + lo pair of bf16 values: O then carries about 16
+    // significant bits of P, so the backward's rowsum(dO O) is accurate where
+    // dP - rowsum cancels
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const bf16x8 vf = ld_tr8(Vs, LD, kk * 32, ds * 16, lane);
 #pragma unroll
-        for (int qs = 0; qs < NQS; ++qs) o[ds][qs] = mfma(vf, pf[qs][kk], o[ds][qs]);
+        for (int qs = 0; qs < NQS; ++qs) {
+          o[ds][qs] = mfma(vf, pf[qs][kk], o[ds][qs]);
+          o[ds][qs] = mfma(vf, pl[qs][kk], o[ds][qs]);
+        }
       }
     }
     __syncthreads();

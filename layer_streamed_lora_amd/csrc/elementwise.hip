@@ -107,8 +107,8 @@ lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16
 // are computed on the host in float64 and passed by value. A workgroup takes
 // ROPE_ROWS rows: first the float64 angle and its sine/cosine for each
 // (row, i) into LDS, then every head's pairs (i, i + d/2) of those rows are
-// rotated in float32 four at a time (8-byte accesses) and rounded to bf16 in
-// place.
+// rotated in float32 four at a time (8-byte accesses) and rounded to bf16 into
+// y (the same row layout as x; y may be x).
 struct RopeFreq {
   double inv[64];  // head_dim / 2 <= 64
 };
@@ -136,7 +136,7 @@ static RopeFreq rope_freq(int head_dim, double theta, const lsl_rope_scaling* sc
 
 constexpr int ROPE_ROWS = 4;
 
-__global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int64_t T, int64_t ld, int n_heads,
+__global__ __launch_bounds__(256) void rope_kernel(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads,
                                                    int head_dim, int seq, RopeFreq fr, int inverse) {
   __shared__ float cs[ROPE_ROWS][64], sn[ROPE_ROWS][64];
   const int half = head_dim >> 1;
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int
     const int h = rem / q4, g = rem - h * q4;
     const int64_t row = r0 + rr;
     if (row >= T) continue;
-    uint16_t* p = x + row * ld + (int64_t)h * head_dim + 4 * g;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(p + half);
+    const int64_t off = row * ld + (int64_t)h * head_dim + 4 * g;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(x + off);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(x + off + half);
     float x1[4] = {lo_bf(a[0]), hi_bf(a[0]), lo_bf(a[1]), hi_bf(a[1])};
     float x2[4] = {lo_bf(b[0]), hi_bf(b[0]), lo_bf(b[1]), hi_bf(b[1])};
     float o1[4], o2[4];
@@ -171,18 +171,18 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int
       o1[e] = x1[e] * c - x2[e] * s;
       o2[e] = x2[e] * c + x1[e] * s;
     }
-    *reinterpret_cast<u32x2*>(p) = u32x2{pack2(o1[0], o1[1]), pack2(o1[2], o1[3])};
-    *reinterpret_cast<u32x2*>(p + half) = u32x2{pack2(o2[0], o2[1]), pack2(o2[2], o2[3])};
+    *reinterpret_cast<u32x2*>(y + off) = u32x2{pack2(o1[0], o1[1]), pack2(o1[2], o1[3])};
+    *reinterpret_cast<u32x2*>(y + off + half) = u32x2{pack2(o2[0], o2[1]), pack2(o2[2], o2[3])};
   }
 }
 
-lsl_status rope_launch(uint16_t* x, int64_t T, int64_t ld, int n_heads, int head_dim, int seq, float theta,
-                       const lsl_rope_scaling* scaling, int inverse, hipStream_t s) {
+lsl_status rope_launch(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,
+                       float theta, const lsl_rope_scaling* scaling, int inverse, hipStream_t s) {
   if (head_dim % 8 || head_dim > 128)
     return set_error(LSL_ERR_UNSUPPORTED, "rope: head_dim %d (a multiple of 8, at most 128)", head_dim);
   if (T == 0) return LSL_OK;
   const RopeFreq fr = rope_freq(head_dim, (double)theta, scaling);
-  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((T + ROPE_ROWS - 1) / ROPE_ROWS)), dim3(256), 0, s, x, T, ld,
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)((T + ROPE_ROWS - 1) / ROPE_ROWS)), dim3(256), 0, s, x, y, T, ld,
                      n_heads, head_dim, seq, fr, inverse);
   return check_launch("rope");
 }

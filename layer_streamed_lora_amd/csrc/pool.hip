@@ -12,8 +12,19 @@
 // So compute on one slot overlaps the copy into the other, and no host thread
 // ever blocks. The state machine below rejects out-of-order use (STATE) before
 // anything is enqueued.
+//
+// Poison mode (LSL_POISON_SLOTS set to a non-zero value when the pool is
+// created): every load first fills the whole slot with 0xFF bytes on the copy
+// stream, after the wait for the slot's release and before the copy. A bf16
+// 0xFFFF is a NaN and an NF4 absmax of 0xFFFFFFFF too, so a kernel that reads
+// a slot outside its load/acquire/release window, or past the layer's bytes,
+// poisons its results instead of silently reading a stale layer: the pages
+// stress that streaming failures are silent ("Exact Layer Streaming ...",
+// abstract).
 #include "common.h"
 #include "api_util.h"
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 enum SlotState { SLOT_EMPTY = 0, SLOT_LOADED = 1, SLOT_ACQUIRED = 2, SLOT_RELEASED = 3 };
@@ -26,6 +37,7 @@ struct lsl_pool {
   std::vector<hipEvent_t> ready, freed;
   std::vector<int> state;
   std::vector<bool> free_recorded;
+  bool poison = false;
   // optional copy statistics
   std::vector<hipEvent_t> st_start, st_end;
   std::vector<size_t> st_bytes;
@@ -54,6 +66,7 @@ extern "C" lsl_status lsl_pool_create(lsl_pool** out, void* const* slot_ptrs, in
   p->freed.assign(n_slots, nullptr);
   p->state.assign(n_slots, SLOT_EMPTY);
   p->free_recorded.assign(n_slots, false);
+  if (const char* e = getenv("LSL_POISON_SLOTS")) p->poison = e[0] != '\0' && strcmp(e, "0") != 0;
   for (int i = 0; i < n_slots; ++i) {
     hipError_t e;
     // ordering only: no timestamps on the per-layer events (statistics use their own)
@@ -144,6 +157,8 @@ extern "C" lsl_status load_layer_async(lsl_pool* p, int32_t slot, const void* ho
   }
   if (p->free_recorded[slot] && (e = hipStreamWaitEvent(p->copy, p->freed[slot], 0)) != hipSuccess)
     return hip_fail("load_layer_async: hipStreamWaitEvent", e);
+  if (p->poison && (e = hipMemsetAsync(p->ptr[slot], 0xFF, p->slot_bytes, p->copy)) != hipSuccess)
+    return hip_fail("load_layer_async: hipMemsetAsync (poison)", e);
   const bool stat = p->st_count < (int)p->st_start.size();
   if (stat && (e = hipEventRecord(p->st_start[p->st_count], p->copy)) != hipSuccess) return hip_fail("hipEventRecord", e);
   if ((e = hipMemcpyAsync(p->ptr[slot], host_ptr, bytes, hipMemcpyHostToDevice, p->copy)) != hipSuccess)

@@ -32,8 +32,10 @@ lsl_status lora_tn_check(const LoraTn& d);
 lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y, hipStream_t s);
 lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,
                               int64_t T, int64_t H, float eps, uint16_t* dx, hipStream_t s);
-lsl_status rope_launch(uint16_t* x, int64_t T, int64_t ld, int n_heads, int head_dim, int seq, float theta,
-                       const lsl_rope_scaling* scaling, int inverse, hipStream_t s);
+// y = RoPE(x) for n_heads heads of head_dim from column 0 of each row (row
+// stride ld for both; y may be x)
+lsl_status rope_launch(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,
+                       float theta, const lsl_rope_scaling* scaling, int inverse, hipStream_t s);
 lsl_status swiglu_fwd_launch(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, hipStream_t s);
 lsl_status swiglu_bwd_launch(const uint16_t* gu, const uint16_t* da, int64_t T, int64_t I, uint16_t* dgu, hipStream_t s);
 }  // namespace lsl

@@ -158,6 +158,13 @@ def layer_workspace_bytes(cfg, batch, seq, mode):
     return lib().lsl_layer_workspace_bytes(C.byref(cfg), batch, seq, mode)
 
 
+def layer_workspace_map(cfg, batch, seq, mode):
+    """Byte offsets of the layer's intermediates inside its workspace (dict)."""
+    m = _abi.LayerWsMap()
+    _check("lsl_layer_workspace_map", lib().lsl_layer_workspace_map(C.byref(cfg), batch, seq, mode, C.byref(m)))
+    return {n: int(getattr(m, n)) for n in _abi.WS_MAP_FIELDS}
+
+
 def decoder_layer_fwd(cfg, blob, lora_set, x, batch, seq, out=None, ws=None, stream=None):
     """lora_set None: adapters off (the frozen base alone)."""
     if out is None:

@@ -32,6 +32,13 @@ def base_linear_fwd(x, w, rnd=round_bf16, bias=None):
     return rnd(y)
 
 
+def lora_adapter_grads(x, t, dy, u, scale):
+    """The adapter gradients of one LoRA linear from its forward input x,
+    t = x A^T, the loss gradient dy and u = dy B: dA = s u^T x, dB = s dy^T t
+    (unrounded; the chain rule through y = x W^T + s t B^T with t = x A^T)."""
+    return scale * (u.T @ x), scale * (dy.T @ t)
+
+
 def lora_linear_bwd(x, t, dy, w, a, b, scale, rnd=round_bf16, round_dx=True):
     """Returns (dx, dA, dB, u) for the loss gradient dy [T x out].
 
@@ -43,6 +50,5 @@ def lora_linear_bwd(x, t, dy, w, a, b, scale, rnd=round_bf16, round_dx=True):
     dx = dy @ w + scale * (u @ a)
     if round_dx:
         dx = rnd(dx)
-    da = scale * (u.T @ x)
-    db = scale * (dy.T @ t)
+    da, db = lora_adapter_grads(x, t, dy, u, scale)
     return dx, da, db, u

@@ -235,3 +235,45 @@ def test_size_limits_rejected_before_any_launch(L):
     assert b"4 GiB" in lib.lsl_last_error()
     assert lib.decoder_layer_bwd(C.byref(cfg), 256, C.byref(lo), 256, 256, 1, 160000, 256, C.byref(gr), 256, big,
                                  None) == _abi.LSL_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_layer_workspace_map_regions(L, mode):
+    """The layer's intermediates sit in 256-byte aligned, disjoint regions of
+    their sizes inside the workspace; the backward entries are 0 in the
+    forward mode."""
+    from layer_streamed_lora_amd import _abi
+    from layer_streamed_lora_amd import model as M
+    from synth.configs import LLAMA8B_LAYER
+    s = LLAMA8B_LAYER
+    batch, seq = 2, 300
+    T, H, I, r, Q, KV = batch * seq, s.hidden, s.inter, s.lora_r, s.q_dim, s.kv_dim
+    NQKV = Q + 2 * KV
+    cfg = M.layer_cfg(s)
+    m = M.layer_workspace_map(cfg, batch, seq, mode)
+    total = M.layer_workspace_bytes(cfg, batch, seq, mode)
+    size = {"n1": 2 * T * H, "t_qkv": 6 * T * r, "qkv": 2 * T * NQKV, "qk_rope": 2 * T * NQKV, "attn": 2 * T * Q,
+            "lse": 4 * batch * s.n_q * seq, "t_o": 2 * T * r, "h1": 2 * T * H, "n2": 2 * T * H, "t_gu": 4 * T * r,
+            "gu": 4 * T * I, "act": 2 * T * I, "t_down": 2 * T * r, "u_down": 2 * T * r, "d_act": 2 * T * I,
+            "d_gu": 4 * T * I, "u_gu": 4 * T * r, "d_n2": 2 * T * H, "d_h1": 2 * T * H, "u_o": 2 * T * r,
+            "d_attn": 2 * T * Q, "d_qk_rope": 2 * T * NQKV, "d_qkv": 2 * T * NQKV, "u_qkv": 6 * T * r,
+            "d_n1": 2 * T * H, "attn32": 4 * T * Q}
+    bwd = set(_abi.WS_MAP_FIELDS[13:])
+    regions = []
+    for n in _abi.WS_MAP_FIELDS:
+        if mode == _abi.MODE_FWD and n in bwd:
+            assert m[n] == 0, n
+            continue
+        assert m[n] % 256 == 0, n
+        regions.append((m[n], size[n], n))
+    regions.sort()
+    for (o, b, n), (o2, _, n2) in zip(regions, regions[1:]):
+        assert o + b <= o2, (n, n2)
+    assert regions[-1][0] + regions[-1][1] <= total
+    assert lib_status_bad_mode(L, cfg) == _abi.LSL_ERR_INVALID_ARG
+
+
+def lib_status_bad_mode(L, cfg):
+    from layer_streamed_lora_amd import _abi
+    out = _abi.LayerWsMap()
+    return L.lib().lsl_layer_workspace_map(C.byref(cfg), 1, 16, 2, C.byref(out))

@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 import synth
-from tests.gpu_util import dev_bf16, dev, host, assert_close, assert_close_chain
+from tests.gpu_util import dev_bf16, dev, host, assert_close_chain, assert_close_scaled
 
 pytestmark = pytest.mark.gpu
 
@@ -41,8 +41,9 @@ def test_ce_parity(gpu, T, H, V, gs):
     torch.cuda.synchronize()
     assert abs(loss.item() - loss_ref) <= 1e-5 * abs(loss_ref), (loss.item(), loss_ref)
     assert np.allclose(host(lse), lse_ref, rtol=1e-5, atol=0)
-    # dh is O(grad_scale / N_valid): judged scale-free (normwise and RMS-scaled) and by the plain bound
-    assert_close(host(dh), dh_ref, "ce dh")
+    # dh is O(grad_scale / N_valid): the per-element bound with its absolute term
+    # scaled to the tensor (the plain 1e-2 would be vacuous at that size)
+    assert_close_scaled(host(dh), dh_ref, "ce dh")
     assert_close_chain(host(dh), dh_ref, "ce dh (scale-free)")
     assert_close_chain(host(dh) * nv, dh_ref * nv, "ce dh * N_valid")
 
@@ -90,7 +91,7 @@ def test_ce_llama8b_head_sampled_rows(gpu):
     nv_all = int(np.sum(labels != -100))
     dh_ref = O.ce_loss_bwd(hd, wd, labels[rows], grad_scale=len(np.nonzero(labels[rows] != -100)[0]) / nv_all)
     assert np.allclose(host(lse)[rows], lse_ref, rtol=1e-5, atol=0)
-    assert_close(host(dh)[rows], dh_ref, "ce dh rows")
+    assert_close_scaled(host(dh)[rows], dh_ref, "ce dh rows")
     assert_close_chain(host(dh)[rows] * nv_all, dh_ref * nv_all, "ce dh rows * N_valid")
     assert np.all(host(dh)[T - 1] == 0)
 
