@@ -27,9 +27,12 @@ from tests.gpu_util import dev_bf16, host, assert_close_scaled, oracle_layer_wei
 pytestmark = pytest.mark.gpu
 
 
-def _region(ws, off, rows, cols, dtype=torch.bfloat16):
+def _region(ws, off, rows, cols, dtype=torch.bfloat16, use=None):
+    """[rows x cols] at byte offset off; use: the first `use` columns only (the
+    rest of the rows is never written and may hold any bits)."""
     n = rows * cols * (2 if dtype == torch.bfloat16 else 4)
-    return host(ws[off:off + n].view(dtype).view(rows, cols))
+    t = ws[off:off + n].view(dtype).view(rows, cols)
+    return host(t if use is None else t[:, :use])
 
 
 def _run(shape, batch, seq, wid):
@@ -73,8 +76,8 @@ def _check_steps(shape, batch, seq, wid):
     rnd = O.round_bf16
     wsb, mb = r["wsb"], r["mb"]
 
-    def g(name, cols, rows=T, dtype=torch.bfloat16):
-        return _region(wsb, mb[name], rows, cols, dtype)
+    def g(name, cols, rows=T, dtype=torch.bfloat16, use=None):
+        return _region(wsb, mb[name], rows, cols, dtype, use)
 
     # the recompute in the backward equals the forward call bit for bit
     for name, cols in (("n1", H), ("qkv", NQKV), ("attn", Q), ("h1", H), ("gu", 2 * I), ("act", I)):
@@ -91,7 +94,7 @@ def _check_steps(shape, batch, seq, wid):
     assert_close_scaled(g("t_qkv", 3 * rk), np.concatenate(ts, 1), "t_qkv")
     qkv = g("qkv", NQKV)
     assert_close_scaled(qkv, np.concatenate(ys, 1), "qkv")
-    qkr = g("qk_rope", NQKV)[:, :Q + KV]
+    qkr = g("qk_rope", NQKV, use=Q + KV)
     qr_ref = O.rope_apply(qkv[:, :Q].reshape(T, nq, d), pos, theta, scaling=sc).reshape(T, Q)
     kr_ref = O.rope_apply(qkv[:, Q:Q + KV].reshape(T, nkv, d), pos, theta, scaling=sc).reshape(T, KV)
     assert_close_scaled(qkr, np.concatenate([qr_ref, kr_ref], 1), "q, k after RoPE")
@@ -157,7 +160,7 @@ def _check_steps(shape, batch, seq, wid):
     d_attn = g("d_attn", Q)
     assert_close_scaled(d_attn, rnd(dxo), "d_attn")
     dqr, dkr, dv = O.attention_bwd(qr, kr, v, d_attn.reshape(T, nq, d), batch, seq)
-    dqkr = g("d_qk_rope", NQKV)
+    dqkr = g("d_qk_rope", NQKV, use=Q + KV)
     assert_close_scaled(dqkr[:, :Q], dqr.reshape(T, Q), "dq (before inverse RoPE)")
     assert_close_scaled(dqkr[:, Q:Q + KV], dkr.reshape(T, KV), "dk (before inverse RoPE)")
     d_qkv = g("d_qkv", NQKV)
