@@ -142,6 +142,20 @@ lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W,
                            const uint16_t* A, const uint16_t* B, int32_t r, float scale,
                            uint16_t* y, uint16_t* t_out, void* ws, size_t ws_bytes,
                            lsl_stream stream);
+/* The same forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; its scratch (the side product's and the
+ * GEMM's split partials, lsl_lora_linear_workspace_bytes' forward share) is a
+ * device array of lsl_noalloc_scratch_bytes() bytes (64 MiB) that the library
+ * holds on each GPU it runs on until the process ends. It calls no allocating
+ * routine. WORKSPACE if the shape needs more scratch than that. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (two streams,
+ * two threads) race and must be ordered by the caller. Results are bit for bit
+ * those of lora_linear_fwd. */
+lsl_status lora_linear_fwd_noalloc(const uint16_t* x, int64_t T, const lsl_weight* W,
+                                   const uint16_t* A, const uint16_t* B, int32_t r, float scale,
+                                   uint16_t* y, uint16_t* t_out, lsl_stream stream);
+size_t lsl_noalloc_scratch_bytes(void);
 /* u = bf16(dy B); dx = bf16(dy W + s u A) (dx may be NULL);
  * dA += s u^T x and dB += s dy^T t (float32, accumulated into the caller's
  * buffers in a fixed order). W gets no gradient. */

@@ -72,6 +72,8 @@ PROTOS = {
     "lsl_lora_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
     "lora_linear_fwd": (i32, [vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, sz, vp]),
     "lora_linear_bwd": (i32, [vp, vp, vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+    "lora_linear_fwd_noalloc": (i32, [vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp]),
+    "lsl_noalloc_scratch_bytes": (sz, []),
     "lsl_layer_layout_get": (i32, [C.POINTER(LayerCfg), C.POINTER(LayerLayout)]),
     "lsl_layer_workspace_bytes": (sz, [C.POINTER(LayerCfg), i32, i32, i32]),
     "lsl_layer_workspace_map": (i32, [C.POINTER(LayerCfg), i32, i32, i32, C.POINTER(LayerWsMap)]),

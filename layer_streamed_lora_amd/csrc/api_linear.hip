@@ -4,6 +4,13 @@
 #include "gemm.h"
 #include "small.h"
 #include "api_util.h"
+#include <mutex>
+
+// bytes of the allocation-free forward's scratch (64 MiB: the largest split
+// partials of a Llama-3.1-8B projection at 1024 tokens, its down projection's)
+#ifndef LSL_NOALLOC_SCRATCH_BYTES
+#define LSL_NOALLOC_SCRATCH_BYTES (64u << 20)
+#endif
 
 using namespace lsl;
 
@@ -130,6 +137,59 @@ extern "C" lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, cons
   if (dx) LSL_TRY(gemm_launch(g, s));
   LSL_TRY(lora_tn_launch(ta, s));
   return lora_tn_launch(tb, s);
+}
+
+// ---------------------------------------------------------------- allocation-free forward
+// lora_linear_fwd_noalloc: the same launches as lora_linear_fwd with the
+// workspace in a file-scope device array of LSL_NOALLOC_SCRATCH_BYTES (each GPU
+// the library runs on holds its own copy until the process ends). Host code
+// never passes the array's name to a kernel: its address on the current device
+// comes from hipGetSymbolAddress, looked up once per device on the first call.
+namespace lsl {
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)LSL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MAX_DEVICES];
+
+static lsl_status scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(LSL_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return set_error(LSL_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return set_error(LSL_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LSL_OK;
+}
+}  // namespace lsl
+
+extern "C" size_t lsl_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" lsl_status lora_linear_fwd_noalloc(const uint16_t* x, int64_t T, const lsl_weight* W, const uint16_t* A,
+                                              const uint16_t* B, int32_t r, float scale, uint16_t* y,
+                                              uint16_t* t_out, lsl_stream stream) {
+  const char* fn = "lora_linear_fwd_noalloc";
+  LSL_TRY(check_weight(W, fn));
+  if (T < 0) return set_error(LSL_ERR_INVALID_ARG, "%s: T < 0", fn);
+  if (!lora_rank_ok(r)) return set_error(LSL_ERR_UNSUPPORTED, "%s: rank %d must be a multiple of 8 in [8, 64]", fn, r);
+  if (T == 0) return LSL_OK;
+  const size_t need = linear_ws_fwd(T, W->n_out, W->k_in);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return set_error(LSL_ERR_WORKSPACE, "%s: this shape needs %zu bytes of scratch, more than the %zu the library holds",
+                     fn, need, NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  LSL_TRY(scratch_on_current_device(fn, &ws));
+  // nothing in the forward's scratch needs to start at zero: the side product's
+  // and the GEMM's split partials are written in full before they are read
+  return lora_linear_fwd(x, T, W, A, B, r, scale, y, t_out, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---------------------------------------------------------------- support ops

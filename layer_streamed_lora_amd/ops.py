@@ -162,6 +162,23 @@ def lora_linear_fwd(x, W, A, B, scale, ws=None, stream=None):
     return y, t
 
 
+def lora_linear_fwd_noalloc(x, W, A, B, scale, y=None, t=None, stream=None):
+    """lora_linear_fwd with the library's own device scratch (no workspace)."""
+    T = x.shape[0]
+    r = A.shape[0]
+    if y is None:
+        y = torch.empty((T, W.n_out), dtype=torch.bfloat16, device=x.device)
+    if t is None:
+        t = torch.empty((T, r), dtype=torch.bfloat16, device=x.device)
+    _check("lora_linear_fwd_noalloc", lib().lora_linear_fwd_noalloc(_p(x), T, C.byref(W.struct), _p(A), _p(B), r,
+                                                                    scale, _p(y), _p(t), _s(stream)))
+    return y, t
+
+
+def noalloc_scratch_bytes():
+    return lib().lsl_noalloc_scratch_bytes()
+
+
 def lora_linear_bwd(x, t, dy, W, A, B, scale, dA, dB, need_dx=True, ws=None, stream=None):
     T = x.shape[0]
     r = A.shape[0]
