@@ -489,6 +489,92 @@ def summarize_counters(fetch_dir, write_dir, args):
     print(json.dumps(doc, indent=1))
 
 
+def layer_only(args):
+    """One resident decoder layer of the workload's shape (seeded N(0, 0.02) base,
+    the benchmark's adapters) at batch x seq tokens: `steps` timed forward and
+    backward (with recompute) calls after `warmup` untimed ones. For kernel
+    traces and hardware counters of every kernel of a layer without building
+    the whole model. Prints one JSON line."""
+    import dataclasses
+    import torch
+    import synth
+    from layer_streamed_lora_amd import model as M, _abi
+    wl, shape, ms = workload(args.workload)
+    if args.layer_seq:
+        ms = dataclasses.replace(ms, batch=1, seq=args.layer_seq)
+    T = ms.batch * ms.seq
+    one = dataclasses.replace(ms, n_layers=1)
+    m = build_model(shape, one, "resident")
+    cfg, blob = m.cfg, m.blob_view(0)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn((T, shape.hidden), generator=g, device="cuda").to(torch.bfloat16)
+    dy = torch.randn((T, shape.hidden), generator=g, device="cuda").to(torch.bfloat16)
+    out, dx = torch.empty_like(x), torch.empty_like(x)
+    ws = torch.empty(M.layer_workspace_bytes(cfg, ms.batch, ms.seq, _abi.MODE_BWD), dtype=torch.uint8, device="cuda")
+    lo, gr = m.lora.lora_set(0), m.lora.lora_grads(0)
+
+    def fwd():
+        M.decoder_layer_fwd(cfg, blob, lo, x, ms.batch, ms.seq, out=out, ws=ws)
+
+    def bwd():
+        M.decoder_layer_bwd(cfg, blob, lo, x, dy, ms.batch, ms.seq, gr, dx=dx, ws=ws)
+    res = {"workload": f"one {args.workload} layer at {ms.batch}x{ms.seq} tokens, resident"}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"layer_{name}_ms"] = round(e0.elapsed_time(e1) / max(args.steps, 1), 4)
+        log(f"  layer {name}: {res[f'layer_{name}_ms']} ms")
+    print(json.dumps(res), flush=True)
+
+
+def summarize_pmc(dirs, args):
+    """Per-kernel averages of the hardware counters of one or more `rocprofv3
+    --pmc` runs (one row per kernel name, values per dispatch) and the derived
+    MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
+    LDS bank-conflict share (SQ_LDS_BANK_CONFLICT over SQ_ACTIVE_INST_LDS).
+    Kernels are told apart by name and grid size. rocprofv3 sums each counter
+    over its dimensions, so GRBM_GUI_ACTIVE (one clock count per XCD) is
+    divided by the XCD count before it is used as the dispatch's duration."""
+    import collections
+    simds = 4 * args.cus
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    names = []
+    for d in dirs:
+        for r in _rows(_find(d, "*counter_collection.csv")):
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("lsl::", "") + f" grid {_grid_items(r)}"
+            v = float(r["Counter_Value"])
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                v /= args.xcds
+            per[k][r["Counter_Name"]].append(v)
+            if r["Counter_Name"] not in names:
+                names.append(r["Counter_Name"])
+    cols = [n for n in names]
+    out = ["| kernel | dispatches | " + " | ".join(cols) + " | MFMA util | LDS conflict / LDS active |",
+           "|---|---:|" + "---:|" * len(cols) + "---:|---:|"]
+    rows = []
+    for k, c in per.items():
+        n = max(len(v) for v in c.values())
+        avg = {cn: (sum(c[cn]) / len(c[cn]) if c.get(cn) else None) for cn in cols}
+        util = (avg.get("SQ_VALU_MFMA_BUSY_CYCLES") / (avg["GRBM_GUI_ACTIVE"] * simds)
+                if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None and avg.get("GRBM_GUI_ACTIVE") else None)
+        confl = (avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_ACTIVE_INST_LDS"]
+                 if avg.get("SQ_LDS_BANK_CONFLICT") is not None and avg.get("SQ_ACTIVE_INST_LDS") else None)
+        rows.append((-(avg.get("GRBM_GUI_ACTIVE") or 0) * n, k, n, avg, util, confl))
+    rows.sort()
+    for _, k, n, avg, util, confl in rows[:args.top]:
+        vals = " | ".join("" if avg[cn] is None else f"{avg[cn]:.4g}" for cn in cols)
+        out.append(f"| `{k[:110]}` | {n} | {vals} | {'' if util is None else f'{util:.3f}'} | "
+                   f"{'' if confl is None else f'{confl:.3f}'} |")
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -513,7 +599,17 @@ def main():
     ap.add_argument("--summarize-copies", metavar="DIR",
                     help="summarise a rocprofv3 kernel + memory-copy trace of a --no-resident run and exit")
     ap.add_argument("--blob-bytes", type=int, default=0, help="layer blob size, for --summarize-copies")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time one resident layer's forward and backward (for traces and counters), then exit")
+    ap.add_argument("--layer-seq", type=int, default=0, help="tokens of --layer-only (default: the workload's)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="per-kernel averages of rocprofv3 --pmc runs (markdown), then exit")
+    ap.add_argument("--cus", type=int, default=256, help="compute units, for --summarize-pmc")
+    ap.add_argument("--xcds", type=int, default=8, help="accelerator dies (XCDs), for --summarize-pmc")
+    ap.add_argument("--top", type=int, default=30, help="kernels listed by --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc, args)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args)
     if args.summarize_copies:
@@ -535,6 +631,8 @@ def main():
         calib_copy()
     if args.t_sweep:
         return t_sweep(args, args.sizes)
+    if args.layer_only:
+        return layer_only(args)
     wl, shape, ms = workload(args.workload)
     T = ms.batch * ms.seq
     log(f"building {args.workload}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.wfmt} base")

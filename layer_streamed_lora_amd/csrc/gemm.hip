@@ -196,75 +196,83 @@ struct WLoader<LSL_WFMT_NF4, false, BN> : Nf4NkLoader<LSL_WFMT_NF4, BN> {};
 template <int BN>
 struct WLoader<LSL_WFMT_NF4DQ, false, BN> : Nf4NkLoader<LSL_WFMT_NF4DQ, BN> {};
 
-// bf16 stored [K x N] (row = reduction index): thread -> KR k-rows x 8 n-cols.
-// Columns past N read neighbouring data or zeros; their outputs are never stored.
+// The [K x N] weight tile of this kernel in LDS: [64 k][64 n], rows unpadded,
+// the 8-column chunk c of row r at chunk position c ^ kn64_swz(r). A
+// transposing read (4 rows x 4 chunks per 32 lanes, rows r0 .. r0 + 3 with r0
+// a multiple of 4, and rows r0 + 8 .. in the other half-wave) then touches 16
+// distinct 16-byte bank groups, and so does each loader store below (16 lanes:
+// the 8 chunks of an even and of an odd row).
+LSL_DEV int kn64_swz(int r) { return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1); }
+LSL_DEV int kn64_pos(int r, int c) { return r * 64 + 8 * (c ^ kn64_swz(r)); }
+
+// bf16 stored [K x N] (row = reduction index): thread -> rows tid / 8 and
+// tid / 8 + 32, columns 8 (tid % 8) .. + 7. Columns past N read zeros or
+// neighbouring data; their outputs are never stored.
 template <int BN>
 struct WLoader<LSL_WFMT_BF16, true, BN> {
-  static constexpr int KR = BN / 32, OG = BN / 8;  // k-rows per thread, n-groups per tile
-  uint32_t voff;
-  uint32_t w[KR][4];
+  static_assert(BN == 64, "the [K x N] tile layout is 64 columns wide");
+  uint32_t voff[2];
+  uint32_t w[2][4];
   LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) {
-    const int q = tid / OG, o = tid % OG;
-    voff = (uint32_t)(((int64_t)(q * KR) * a.N + n0 + o * 8) * 2);
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+      voff[rr] = (uint32_t)(((int64_t)((tid >> 3) + 32 * rr) * a.N + n0 + (tid & 7) * 8) * 2);
   }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
     const int64_t rows = a.kwrap ? a.kwrap : a.K;
     if (a.kwrap && k0 >= a.kwrap) k0 -= a.kwrap;  // K <= 2 kwrap (checked on the host)
-    // descriptor from row k0 + rr to the end of the matrix: the column offset
+    // descriptor from row k0 to the end of the matrix: the row and column offset
     // (in the vector offset) is range-checked
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb + k0 * a.N, (rows - k0) * a.N * 2);
 #pragma unroll
-    for (int rr = 0; rr < KR; ++rr) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb + (k0 + rr) * a.N, (rows - k0 - rr) * a.N * 2);
-      u32x4 v = bload16(rs, voff, 0);
+    for (int rr = 0; rr < 2; ++rr) {
+      u32x4 v = bload16(rs, voff[rr], 0);
       w[rr][0] = v[0]; w[rr][1] = v[1]; w[rr][2] = v[2]; w[rr][3] = v[3];
     }
   }
-  // row-major [k][n] tile (row stride BN + 8); the MFMA reads it transposed
   LSL_DEV void store(uint16_t* lds, const float*, int tid) const {
-    const int q = tid / OG, o = tid % OG;
 #pragma unroll
-    for (int rr = 0; rr < KR; ++rr)
-      *reinterpret_cast<u32x4*>(lds + (q * KR + rr) * (BN + 8) + o * 8) = u32x4{w[rr][0], w[rr][1], w[rr][2], w[rr][3]};
+    for (int rr = 0; rr < 2; ++rr)
+      *reinterpret_cast<u32x4*>(lds + kn64_pos((tid >> 3) + 32 * rr, tid & 7)) =
+          u32x4{w[rr][0], w[rr][1], w[rr][2], w[rr][3]};
   }
 };
 
-// NF4 stored [K x N]: thread -> KR k-rows x 8 n-cols (4 code bytes + absmax per
-// row); column groups past N are clamped to the last group (outputs not stored).
+// NF4 stored [K x N]: thread -> rows tid / 8 and tid / 8 + 32, columns
+// 8 (tid % 8) .. + 7 (4 code bytes and the absmax of each row); column groups
+// past N are clamped to the last group (outputs not stored).
 template <int WFMT, int BN>
 struct Nf4KnLoader {
-  static constexpr int KR = BN / 32, OG = BN / 8;
+  static_assert(BN == 64, "the [K x N] tile layout is 64 columns wide");
   const uint8_t* pc;
   int64_t ai;  // absmax index of this thread's first row and column block
   int64_t rowc, rowa;
-  uint32_t c[KR];
-  float am[KR];
+  uint32_t c[2];
+  float am[2];
   LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid) {
-    const int q = tid / OG, o = tid % OG;
-    const int64_t n = n0 + o * 8 < a.N ? n0 + o * 8 : a.N - 8;
+    const int64_t n = n0 + (tid & 7) * 8 < a.N ? n0 + (tid & 7) * 8 : a.N - 8;
     rowc = a.N >> 1;
     rowa = a.N >> 6;
-    pc = a.wq + (int64_t)(q * KR) * rowc + (n >> 1);
-    ai = (int64_t)(q * KR) * rowa + (n >> 6);
+    pc = a.wq + (int64_t)(tid >> 3) * rowc + (n >> 1);
+    ai = (int64_t)(tid >> 3) * rowa + (n >> 6);
   }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
 #pragma unroll
-    for (int rr = 0; rr < KR; ++rr) {
-      c[rr] = *reinterpret_cast<const uint32_t*>(pc + (k0 + rr) * rowc);
-      am[rr] = block_absmax<WFMT>(a, ai + (k0 + rr) * rowa);
+    for (int rr = 0; rr < 2; ++rr) {
+      c[rr] = *reinterpret_cast<const uint32_t*>(pc + (k0 + 32 * rr) * rowc);
+      am[rr] = block_absmax<WFMT>(a, ai + (k0 + 32 * rr) * rowa);
     }
   }
-  // row-major [k][n] tile (row stride BN + 8); the MFMA reads it transposed
   LSL_DEV void store(uint16_t* lds, const float* lut, int tid) const {
-    const int q = tid / OG, o = tid % OG;
 #pragma unroll
-    for (int rr = 0; rr < KR; ++rr) {
+    for (int rr = 0; rr < 2; ++rr) {
       uint32_t w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t b = c[rr] >> (8 * j);  // element 2j in the high nibble
         w[j] = pack2(lut[(b >> 4) & 15] * am[rr], lut[b & 15] * am[rr]);
       }
-      *reinterpret_cast<u32x4*>(lds + (q * KR + rr) * (BN + 8) + o * 8) = u32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4*>(lds + kn64_pos((tid >> 3) + 32 * rr, tid & 7)) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
 };
@@ -287,10 +295,10 @@ struct Geo {
 };
 
 // ksteps x 16-deep MFMA steps on LDS tiles: acc[ni][mi] += Wt-block[ni] x X-block[mi].
-// TRW: the weight tile is row-major [k][n] (row stride WLD) and read with
-// transposing LDS reads (natural k order, so the token tile is unchanged).
+// TRW: the weight tile is the swizzled [64 k][64 n] layout (kn64_pos) and read
+// with transposing LDS reads (natural k order, so the token tile is unchanged).
 // XSW: the token tile is the unpadded, swizzled [BM][64] layout (else [BM][LDSW]).
-template <int MI, bool TRW = false, int WLD = LDSW, bool XSW = false>
+template <int MI, bool TRW = false, bool XSW = false>
 LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x16 (&acc)[2][MI], int wn, int wm0, int lane,
                       int ksteps) {
   const int h8 = (lane >> 5) * 8, r32 = lane & 31;
@@ -301,10 +309,11 @@ LSL_DEV void mma_tile(const uint16_t* Ws, const uint16_t* Xs, f32x16 (&acc)[2][M
     for (int i = 0; i < 2; ++i) {
       if constexpr (TRW) {
         // lanes 16-31 / 48-63 take columns 16..31 of the block; each 16-lane group
-        // reads rows kofs .. kofs + 3 and kofs + 4 .. kofs + 7 of its 16 columns
-        const int j = lane & 15;
-        const uint16_t* p = Ws + (kofs + (j >> 2)) * WLD + wn * 64 + i * 32 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
-        const u32x2 x = ld_tr4(p), y = ld_tr4(p + 4 * WLD);
+        // reads rows kofs .. kofs + 3 and kofs + 4 .. kofs + 7 of its 16 columns:
+        // lane j gets row kofs + j / 4, columns 4 (j % 4) .. + 3 (half of a chunk)
+        const int j = lane & 15, r = kofs + (j >> 2);
+        const int c = wn * 8 + i * 4 + 2 * ((lane >> 4) & 1) + ((j & 3) >> 1), e = 4 * (j & 1);
+        const u32x2 x = ld_tr4(Ws + kn64_pos(r, c) + e), y = ld_tr4(Ws + kn64_pos(r + 4, c) + e);
         af[i] = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
       } else {
         af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wn * 64 + i * 32 + r32) * LDSW + kofs);
@@ -532,10 +541,10 @@ template <int WFMT, bool KN, int LORA, int EPI, int BN, int BM>
 __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const GemmKArgs a) {
   using G = Geo<BN, BM>;
   constexpr int MI = G::MI;
-  // weight tile: [BN][LDSW] (NK), or row-major [BK][BN + 8] read transposed (KN);
-  // the LoRA step reuses it as [BN][LDSW]. Token tile: swizzled [BM][64] (the
-  // LoRA step: [BM][LDSW]).
-  constexpr int WSZ = BN * LDSW > BK * (BN + 8) ? BN * LDSW : BK * (BN + 8);
+  // weight tile: [BN][LDSW] (NK), or the swizzled [BK][64] layout read
+  // transposed (KN); the LoRA step reuses it as [BN][LDSW]. Token tile:
+  // swizzled [BM][64] (the LoRA step: [BM][LDSW]).
+  constexpr int WSZ = BN * LDSW > BK * (BN + 32) ? BN * LDSW : BK * (BN + 32);
   __shared__ __attribute__((aligned(16))) uint16_t Ws[WSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[BM * LDSW];
   // NF4 codebook: 16 floats, so every lookup is a conflict-free broadcast read
@@ -602,7 +611,7 @@ __global__ __launch_bounds__(NTHREADS, LSL_GEMM_MINB) void gemm_kernel(const Gem
       xl.load(a.x, a.ldx, a.M, (int64_t)(kt0 + kt + 1) * BK);
       wl.load(a, (int64_t)(kt0 + kt + 1) * BK);
     }
-    mma_tile<MI, KN, BN + 8, true>(Ws, Xs, acc, wn, wm0, lane, 4);
+    mma_tile<MI, KN, true>(Ws, Xs, acc, wn, wm0, lane, 4);
     __syncthreads();
     if (more) {
       xstore(xl, Xs);
@@ -693,7 +702,7 @@ __global__ void gemm_split_reduce(const float* __restrict__ part, int S, int64_t
 namespace big {
 constexpr int BN = 256, BM = 256, NT = 512;
 constexpr int XSZ = BM * BK;  // token stage [256][64], swizzled
-constexpr int WSZ = BN * LDSW > BK * (BN + 8) ? BN * LDSW : BK * (BN + 8);
+constexpr int WSZ = BN * LDSW > BK * (BN + 32) ? BN * LDSW : BK * (BN + 32);
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -787,31 +796,68 @@ struct BigNf4Nk {
 template <> struct BigW<LSL_WFMT_NF4, false> : BigNf4Nk<LSL_WFMT_NF4> {};
 template <> struct BigW<LSL_WFMT_NF4DQ, false> : BigNf4Nk<LSL_WFMT_NF4DQ> {};
 
-// NF4 [K x N] (N % 64 == 0): thread -> k-row tid / 8, 16 code bytes = 32 columns
-// at n 32 (tid % 8), one absmax; stored row-major [k][n] (row stride BN + 8).
-// Column groups past N are clamped to the last group (outputs not stored).
+// The [K x N] weight tile in LDS: [64 k][256 n] with a row stride of KNW = 288
+// elements (row r starts 4 r 16-byte bank groups further on, modulo 16), the
+// 8-column chunk c of row r at chunk position c ^ 2 ((r >> 3) & 1). A
+// transposing read takes rows r0 .. r0 + 3 (r0 a multiple of 4) x 4 chunks in
+// lanes 0-31 and rows r0 + 8 .. r0 + 11 in lanes 32-63: both halves, and the
+// lanes 0-15 + 32-47 pairing too, touch 16 distinct bank groups, and every
+// offset but one base is an immediate. The loaders below give each thread one
+// chunk position in four rows, so every 16 lanes of a store write 16
+// consecutive chunks of one row: conflict-free too. Same size as [256][LDSW].
+constexpr int KNW = BN + 32;
+LSL_DEV int kn_pos(int r, int c) { return r * KNW + 8 * (c ^ (((r >> 3) & 1) << 1)); }
+// row of load i (0..3) of thread tid: wave w takes rows 8 w .. 8 w + 7, lanes
+// 0-31 the even and lanes 32-63 the odd ones; chunk tid % 32
+LSL_DEV int kn_row(int tid, int i) { return 8 * (tid >> 6) + 2 * i + ((tid >> 5) & 1); }
+
+// NF4 [K x N] (N % 64 == 0): thread -> chunk tid % 32 (8 columns, 4 code bytes
+// and their absmax) of the rows kn_row(tid, i). Column groups past N are
+// clamped to the last group (outputs not stored).
+// Codes and absmax are read through buffer descriptors over the whole matrix
+// with the lane's offset in the vector offset and the row's in the scalar
+// offset: every row read is inside the matrix and the columns are clamped, so
+// no range check is needed, and one 32-bit register per operand addresses all
+// four rows.
 template <int WFMT>
 struct BigNf4Kn {
-  static constexpr int kind = 0, nload = 2;
-  const uint8_t* pc;
-  int64_t ai, rowc, rowa;
-  u32x4 c;
-  float am;
+  // vector loads issued per load() (8, 12 for NF4DQ): the pipeline's wait for
+  // the token DMA may count fewer of them, never more
+  static constexpr int kind = 0, nload = 8;
+  uint32_t vc, va;  // byte offsets of the lane's codes and absmax (code) in row 0
+  uint32_t c[4];
+  float am[4];
   LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid, int, int) {
-    const int kr = tid >> 3, part = tid & 7;
-    const int64_t n = n0 + part * 32 < a.N ? n0 + part * 32 : a.N - 32;
-    rowc = a.N >> 1;
-    rowa = a.N >> 6;
-    pc = a.wq + kr * rowc + (n >> 1);
-    ai = kr * rowa + (n >> 6);
+    const int64_t n = n0 + (tid & 31) * 8 < a.N ? n0 + (tid & 31) * 8 : a.N - 8;
+    const int64_t row = kn_row(tid, 0);
+    vc = (uint32_t)(row * (a.N >> 1) + (n >> 1));
+    va = (uint32_t)((row * (a.N >> 6) + (n >> 6)) * (WFMT == LSL_WFMT_NF4DQ ? 1 : 4));
   }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
-    c = *reinterpret_cast<const u32x4*>(pc + k0 * rowc);
-    am = block_absmax<WFMT>(a, ai + k0 * rowa);
+    const int64_t rowc = a.N >> 1, rowa = a.N >> 6;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.wq, a.K * rowc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // rows kn_row(tid, 0) + 2 i
+      c[i] = bload4(rc, vc, (uint32_t)((k0 + 2 * i) * rowc));
+    if constexpr (WFMT == LSL_WFMT_NF4DQ) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.wq8, a.K * rowa);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t q = __builtin_amdgcn_raw_buffer_load_b8(rq, va, (uint32_t)((k0 + 2 * i) * rowa), 0);
+        const int64_t idx = (int64_t)va + (k0 + 2 * i) * rowa;  // flattened absmax index
+        am[i] = (float)q * a.wsc[idx >> 8];
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.wa, a.K * rowa * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am[i] = __uint_as_float(bload4(ra, va, (uint32_t)((k0 + 2 * i) * rowa * 4)));
+    }
   }
+  // quarter i: row kn_row(tid, i), its 8 codes' values, then the scaled bf16
+  // weights as one 16-byte LDS store
   LSL_DEV void fetch(int i, const float* lut, float (&v)[8]) const { nf4_fetch(c[i], lut, v); }
   LSL_DEV void emit(int i, const float (&v)[8], uint16_t* __restrict__ lds, int tid) const {
-    reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32)[i] = nf4_emit(v, am);
+    *reinterpret_cast<u32x4*>(lds + kn_pos(kn_row(tid, i), tid & 31)) = nf4_emit(v, am[i]);
   }
   LSL_DEV void store(uint16_t* __restrict__ lds, const float* lut, int tid) const {
 #pragma unroll
@@ -825,7 +871,7 @@ struct BigNf4Kn {
 template <> struct BigW<LSL_WFMT_NF4, true> : BigNf4Kn<LSL_WFMT_NF4> {};
 template <> struct BigW<LSL_WFMT_NF4DQ, true> : BigNf4Kn<LSL_WFMT_NF4DQ> {};
 
-// bf16 [K x N]: thread -> k-row tid / 8, 32 columns at n 32 (tid % 8) (4 x 16 B);
+// bf16 [K x N]: thread -> chunk tid % 32 (16 bytes) of the rows kn_row(tid, i);
 // columns past N read zeros (buffer range) or neighbouring data, never stored
 template <>
 struct BigW<LSL_WFMT_BF16, true> {
@@ -833,22 +879,22 @@ struct BigW<LSL_WFMT_BF16, true> {
   uint32_t voff;
   u32x4 v[4];
   LSL_DEV void init(const GemmKArgs& a, int64_t n0, int tid, int, int) {
-    voff = (uint32_t)((((int64_t)(tid >> 3)) * a.N + n0 + (tid & 7) * 32) * 2);
+    voff = (uint32_t)((((int64_t)kn_row(tid, 0)) * a.N + n0 + (tid & 31) * 8) * 2);
   }
   LSL_DEV void load(const GemmKArgs& a, int64_t k0) {
     // descriptor from row k0 to the end of the matrix: a column past N in the
     // last row reads zeros instead of the bytes after the matrix
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.wb + k0 * a.N, (a.K - k0) * a.N * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = bload16(rs, voff + 16 * i, 0);
+    for (int i = 0; i < 4; ++i) v[i] = bload16(rs, voff + (uint32_t)(2 * i * a.N * 2), 0);
   }
   LSL_DEV void fetch(int, const float*, float (&)[8]) const {}
   LSL_DEV void emit(int i, const float (&)[8], uint16_t* __restrict__ lds, int tid) const {
-    reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32)[i] = v[i];
+    *reinterpret_cast<u32x4*>(lds + kn_pos(kn_row(tid, i), tid & 31)) = v[i];
   }
   LSL_DEV void store(uint16_t* __restrict__ lds, const float*, int tid) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(lds + (tid >> 3) * (BN + 8) + (tid & 7) * 32)[i] = v[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lds + kn_pos(kn_row(tid, i), tid & 31)) = v[i];
   }
 };
 
@@ -865,7 +911,7 @@ struct BigW<LSL_WFMT_BF16, false> {
 
 // nsub 16-deep MFMA sub-steps: acc[ni][mi] += W-block[ni] x X-block[mi] for the
 // wave's 128 x 64 tile. WL: weight tile layout 0 padded [n][LDSW], 1 swizzled
-// [n][64], 2 row-major [k][BN + 8] read with transposing LDS reads.
+// [n][64], 2 the swizzled [k][256] layout (kn_pos) read with transposing LDS reads.
 struct NoPart {
   LSL_DEV void begin() const {}
   LSL_DEV void operator()(int) const {}
@@ -884,10 +930,11 @@ LSL_DEV void mma_big(const uint16_t* __restrict__ Ws, const uint16_t* __restrict
         af[i] = *reinterpret_cast<const bf16x8*>(Ws + row * BK + 8 * ((2 * s + h) ^ xswz(row)));
       } else {
         // lanes 16-31 / 48-63 take columns 16..31 of the block; each 16-lane group
-        // reads rows kofs .. kofs + 3 and kofs + 4 .. kofs + 7 of its 16 columns
-        const int j = lane & 15, kofs = 16 * s + 8 * h;
-        const uint16_t* p = Ws + (kofs + (j >> 2)) * (BN + 8) + wn * 128 + i * 32 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
-        const u32x2 lo = ld_tr4(p), hi = ld_tr4(p + 4 * (BN + 8));
+        // reads rows kofs .. kofs + 3 and kofs + 4 .. kofs + 7 of its 16 columns:
+        // lane j gets row kofs + j / 4, columns 4 (j % 4) .. + 3 (half of a chunk)
+        const int j = lane & 15, r = 16 * s + 8 * h + (j >> 2);
+        const int c = wn * 16 + i * 4 + 2 * ((lane >> 4) & 1) + ((j & 3) >> 1), e = 4 * (j & 1);
+        const u32x2 lo = ld_tr4(Ws + kn_pos(r, c) + e), hi = ld_tr4(Ws + kn_pos(r + 4, c) + e);
         af[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       }
     }
@@ -928,8 +975,8 @@ LSL_DEV void mma_big(const uint16_t* __restrict__ Ws, const uint16_t* __restrict
 
 // LoRA K-step operands: Ls = rows m0.. of la (k zero padded to 64) in the
 // swizzled token layout; Lt as in lora_stage, [BN][LDSW] for the forward (LORA
-// 1) and, for the input gradient (LORA 2), A_full's rows j < 64 as the row-major
-// [k][BN + 8] tile the KN main loop reads. 16-byte chunks, loads issued first.
+// 1) and, for the input gradient (LORA 2), A_full's rows j < 64 in the swizzled
+// [k][256] layout the KN main loop reads. 16-byte chunks, loads issued first.
 template <int LORA>
 LSL_DEV void lora_stage_big(const GemmKArgs& a, uint16_t* Ls, uint16_t* Lt, int64_t m0, int64_t n0, int tid) {
   constexpr int LC = BM * 8 / NT, TC = BN * 8 / NT;  // 4 and 4 chunks per thread
@@ -974,8 +1021,8 @@ LSL_DEV void lora_stage_big(const GemmKArgs& a, uint16_t* Ls, uint16_t* Lt, int6
   } else {
 #pragma unroll
     for (int q = 0; q < TC; ++q) {
-      const int c = tid + q * NT, j = c >> 5, nc = (c & 31) * 8;
-      *reinterpret_cast<u32x4*>(Lt + j * (BN + 8) + nc) = tv[q];
+      const int c = tid + q * NT, j = c >> 5;
+      *reinterpret_cast<u32x4*>(Lt + kn_pos(j, c & 31)) = tv[q];
     }
   }
 }
@@ -991,9 +1038,11 @@ LSL_DEV void order_point() {
 // after the tile DMA stay in flight across it)
 template <int N>
 LSL_DEV void tile_barrier() {
+  static_assert(N == 0 || N == 2 || N == 4 || N == 8, "tile_barrier: 0, 2, 4 or 8 loads");
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 }  // namespace big
@@ -1104,6 +1153,8 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
       if (next2) big::tile_barrier<2>(); else big::tile_barrier<0>();
     } else if constexpr (W::kind == 0 && W::nload == 4) {
       if (next2) big::tile_barrier<4>(); else big::tile_barrier<0>();
+    } else if constexpr (W::kind == 0 && W::nload == 8) {
+      if (next2) big::tile_barrier<8>(); else big::tile_barrier<0>();
     } else {
       big::tile_barrier<0>();
     }
