@@ -241,6 +241,61 @@ def nf4dq_leg(args, T_inputs_seed):
     return out
 
 
+# the pages' own figures for these workloads' shapes ("Exact Layer Streaming ...",
+# abstract): context only, other hardware and unstated sequence lengths
+LEG_CONTEXT = {
+    "qwen05b_bf16": {"pages_streamed_over_resident": 1.43,
+                     "pages_note": "0.5B model, the one size with a resident baseline on the pages' 4 GB laptop GPU"},
+    "qwen3b_bf16": {"pages_tok_s": 143.0,
+                    "pages_note": "Qwen2.5-3B, un-quantized bf16 base, layer-streamed, RTX 3050 Laptop 4 GB (2.15 GB peak)"},
+}
+
+
+def model_leg(name, args):
+    """One workload model streamed (2 slots) and resident with the same base:
+    bit-exactness of one optimizer step, then `steps` timed steps of each (after
+    one warm-up), and the layer copies of one step (copy-engine time)."""
+    import torch
+    import synth
+    from layer_streamed_lora_amd.trainer import StreamedLoraModel
+    wl, shape, ms = workload(name)
+    T = ms.batch * ms.seq
+    log(f"building {name}: {ms.n_layers} layers, {shape.wfmt} base, {ms.n_micro} x {ms.batch}x{ms.seq} tokens")
+    s_model = build_model(shape, ms, "streamed", seed=2024 + wl.wid)
+    r_model = StreamedLoraModel(shape, ms.n_layers, ms.vocab, ms.tied, ms.batch, ms.seq, mode="resident")
+    r_model.copy_base_from(s_model)
+    chunks = [synth.token_ids(T, ms.vocab, wl.wid, salt=i) for i in range(ms.n_micro)]
+    inputs = s_model.prepare_inputs(chunks)
+    ls, lr_ = s_model.step(inputs), r_model.step(inputs)
+    torch.cuda.synchronize()
+    exact = bool(torch.equal(ls, lr_) and torch.equal(s_model.lora.grad, r_model.lora.grad)
+                 and torch.equal(s_model.lora.master, r_model.lora.master) and torch.equal(s_model.ckpt, r_model.ckpt))
+    steps, warm = max(1, min(args.steps, 3)), 1
+    st = time_steps(s_model, inputs, steps, warm)
+    cs = time_steps(s_model, inputs, 1, 0, stats=True)
+    rt = time_steps(r_model, inputs, steps, warm)
+    ntok = T * ms.n_micro
+    out = {"workload": (f"{name}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.n_q}/{shape.n_kv} heads, "
+                        f"MLP {shape.inter}, vocab {ms.vocab}{' tied' if ms.tied else ''}, {shape.wfmt} base, "
+                        f"LoRA r{shape.lora_r}, {ms.n_micro} microbatch(es) of {ms.batch}x{ms.seq} tokens, AdamW"),
+           "streamed_ms_per_step": round(st["ms_per_step"], 3), "resident_ms_per_step": round(rt["ms_per_step"], 3),
+           "streamed_over_resident": round(st["ms_per_step"] / rt["ms_per_step"], 3),
+           "streamed_tok_s": round(ntok / (st["ms_per_step"] * 1e-3), 1),
+           "resident_tok_s": round(ntok / (rt["ms_per_step"] * 1e-3), 1),
+           "bit_exact_vs_resident": exact, "blob_bytes": s_model.blob_bytes,
+           "store_GB": round(s_model.blob_bytes * ms.n_layers / 1e9, 3),
+           "h2d_loads_per_step": cs.get("h2d_loads"), "h2d_bytes_per_step": cs.get("h2d_bytes"),
+           "h2d_GBps_copy_engine": cs.get("h2d_copy_s") and round(cs["h2d_bytes"] / cs["h2d_copy_s"] / 1e9, 2),
+           "h2d_GBps_over_step": cs.get("h2d_bytes") and round(cs["h2d_bytes"] / (st["ms_per_step"] * 1e-3) / 1e9, 2),
+           "steps": steps, "loss": round(st["loss"], 5), "context": LEG_CONTEXT.get(name)}
+    log(f"  {name}: streamed {st['ms_per_step']:.2f} ms, resident {rt['ms_per_step']:.2f} ms, "
+        f"ratio {out['streamed_over_resident']}, bit-exact {exact}")
+    del s_model, r_model, inputs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def counters_traffic():
     """HBM bytes per launch of the timed GEMM from committed rocprofv3 counters,
     if they were taken on the current kernel source (else None)."""
@@ -264,9 +319,14 @@ def cpu_baseline(shape, ms):
     import oracle as O
     import synth
     from synth.configs import PROJ_IN_OUT
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '?')} threads, "
+                             f"{i.get('architecture', '?')})" for i in info)
     except Exception:
         threads = len(os.sched_getaffinity(0))
     T = ms.batch * ms.seq
@@ -293,6 +353,7 @@ def cpu_baseline(shape, ms):
     t_ce = time.perf_counter() - t0
     step_s = ms.n_layers * (t_layer + 2 * t_deq) + t_ce * (T / ntok)
     return {"value": T * ms.n_micro / (step_s * ms.n_micro), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "blas": blas, "host_cpus": len(os.sched_getaffinity(0)),
             "sample": (f"1 of {ms.n_layers} layers fwd+bwd at {T} tokens ({t_layer:.1f} s) + its NF4 dequant x2 "
                        f"({2 * t_deq:.1f} s) + cross-entropy fwd+bwd on {ntok} of {T} tokens ({t_ce:.1f} s), "
                        f"scaled to {ms.n_layers} layers and {T} tokens (float64 numpy)"),
@@ -534,6 +595,69 @@ def layer_only(args):
     print(json.dumps(res), flush=True)
 
 
+def ce_only(args):
+    """The fused cross-entropy of the workload's head (T tokens, hidden H, vocab
+    V, its lm_head) on seeded inputs: `steps` timed forward + backward calls
+    after `warmup`, for traces and HBM counters. Prints one JSON line."""
+    import torch
+    from layer_streamed_lora_amd import ops
+    wl, shape, ms = workload(args.workload)
+    T, H, V = ms.batch * ms.seq, shape.hidden, ms.vocab
+    g = torch.Generator(device="cuda").manual_seed(11)
+    h = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    labels = torch.randint(0, V, (T,), generator=g, device="cuda", dtype=torch.int32)
+    ws = torch.empty(ops.ce_workspace_bytes(T, H, V), dtype=torch.uint8, device="cuda")
+
+    def run():
+        loss, lse = ops.fused_ce_loss_fwd(h, w, labels, ws=ws)
+        ops.fused_ce_loss_bwd(h, w, labels, lse, ws=ws)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / max(args.steps, 1)
+    print(json.dumps({"workload": f"fused CE of {args.workload}: T {T}, H {H}, V {V}", "fwd_bwd_ms": round(ms_call, 4),
+                      "logits_avoided_GB_naive_14B": round(14 * T * V / 1e9, 3)}), flush=True)
+
+
+def summarize_ce_bytes(fetch_dir, write_dir, args):
+    """HBM bytes per logit element of the fused cross-entropy (forward and
+    backward) from two rocprofv3 --pmc runs of `--ce-only --calib-copy`
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), scaled by what the same
+    counters read for the calibration copy. The CE kernels of one call are the
+    lm_head GEMM passes and the small reductions around them."""
+    wl, shape, ms = workload(args.workload)
+    T, H, V = ms.batch * ms.seq, shape.hidden, ms.vocab
+    ce_names = ("gemm_big_kernel<1", "gemm_kernel<1", "ce_")
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _rows(_find(d, "*counter_collection.csv")) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]
+                and _grid_items(r) >= 1 << 20]
+        ce = [r for r in rows if any(n in r["Kernel_Name"] for n in ce_names)]
+        if not copy or not ce:
+            sys.exit(f"{counter}: copy dispatches {len(copy)}, CE dispatches {len(ce)}")
+        scale = (CALIB_MIB << 20) / (sum(copy) / len(copy) * 1024.0)
+        calls = args.steps + args.warmup
+        per_kernel = {}
+        for r in ce:
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("lsl::", "")
+            per_kernel[k] = per_kernel.get(k, 0.0) + float(r["Counter_Value"]) * 1024.0 * scale / calls
+        res[counter] = {"scale": scale, "bytes_per_call": sum(per_kernel.values()), "per_kernel": per_kernel}
+    total = res["FETCH_SIZE"]["bytes_per_call"] + res["WRITE_SIZE"]["bytes_per_call"]
+    doc = {"workload": f"fused CE, T {T}, H {H}, V {V} (forward + backward)", "counters": res,
+           "hbm_bytes_per_call": round(total), "bytes_per_logit_element": round(total / (T * V), 3),
+           "lm_head_bytes_per_call_algorithmic": 3 * V * H * 2,
+           "pages_naive_bytes_per_logit_element": 14, "commands": args.commands}
+    print(json.dumps(doc, indent=1))
+
+
 def summarize_pmc(dirs, args):
     """Per-kernel averages of the hardware counters of one or more `rocprofv3
     --pmc` runs (one row per kernel name, values per dispatch) and the derived
@@ -586,6 +710,8 @@ def main():
     ap.add_argument("--no-nf4dq", action="store_true", help="skip the double-quantized-absmax variant")
     ap.add_argument("--no-reference", action="store_true", help="skip the adapter-off reference forward")
     ap.add_argument("--no-large-t", action="store_true", help="skip the 8 x 1024-token streamed/resident point")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the Qwen-0.5B and Qwen-3B streamed/resident legs")
     ap.add_argument("--t-sweep", action="store_true",
                     help="streamed vs resident step time from 1k to 16k tokens per layer visit, then exit")
     ap.add_argument("--sizes", type=int, nargs="*", default=[1024, 2048, 4096, 8192, 16384],
@@ -602,6 +728,10 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="time one resident layer's forward and backward (for traces and counters), then exit")
     ap.add_argument("--layer-seq", type=int, default=0, help="tokens of --layer-only (default: the workload's)")
+    ap.add_argument("--ce-only", action="store_true",
+                    help="time the fused cross-entropy of the workload's head (for counters), then exit")
+    ap.add_argument("--summarize-ce-bytes", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="HBM bytes per logit element of two --ce-only --pmc runs, then exit")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="per-kernel averages of rocprofv3 --pmc runs (markdown), then exit")
     ap.add_argument("--cus", type=int, default=256, help="compute units, for --summarize-pmc")
@@ -610,6 +740,8 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc, args)
+    if args.summarize_ce_bytes:
+        return summarize_ce_bytes(*args.summarize_ce_bytes, args)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args)
     if args.summarize_copies:
@@ -633,6 +765,8 @@ def main():
         return t_sweep(args, args.sizes)
     if args.layer_only:
         return layer_only(args)
+    if args.ce_only:
+        return ce_only(args)
     wl, shape, ms = workload(args.workload)
     T = ms.batch * ms.seq
     log(f"building {args.workload}: {ms.n_layers} layers, hidden {shape.hidden}, {shape.wfmt} base")
@@ -707,6 +841,10 @@ def main():
         del s_model
         torch.cuda.empty_cache()
         large_t = t_sweep(args, [8192], emit=False)[0]
+    # the bf16-base workloads the pages quote (streaming overhead at 0.5B, tok/s at 3B)
+    legs = None
+    if not args.no_legs and args.workload == "llama8b_nf4":
+        legs = {n: model_leg(n, args) for n in ("qwen05b_bf16", "qwen3b_bf16")}
 
     tok_s = T * ms.n_micro / (res["ms_per_step"] * 1e-3)
     flops = step_flops(shape, ms)
@@ -748,6 +886,7 @@ def main():
                             "pages_peak_vram_GB": 3.32},
         "loss": round(res["loss"], 5),
         "nf4dq": variant,
+        "legs": legs,
         "reference_forward": reference and {
             "what": "adapter-off streamed forward + per-token log-probs (preference reference)",
             "ms": round(reference["ms"], 3), "tok_s": round(T * ms.n_micro / (reference["ms"] * 1e-3), 2),

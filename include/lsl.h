@@ -137,6 +137,10 @@ typedef struct {
  * accumulation, one rounding). r is a multiple of 8 in [8, 64]; T >= 0 is any token count.
  */
 size_t lsl_lora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in, int32_t r);
+/* Byte offset (a multiple of 256) in lora_linear_bwd's workspace where the call
+ * leaves u = bf16(dy B) [T x r] (row-major), for callers that check or reuse it;
+ * valid until the workspace is used again. */
+size_t lsl_lora_linear_bwd_u_offset(int64_t T, int64_t n_out, int64_t k_in);
 /* x [T x k_in], y [T x n_out], t_out [T x r] (kept for the backward). */
 lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W,
                            const uint16_t* A, const uint16_t* B, int32_t r, float scale,
@@ -145,8 +149,9 @@ lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W,
 /* The same forward for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no workspace argument; its scratch (the side product's and the
- * GEMM's split partials, lsl_lora_linear_workspace_bytes' forward share) is a
- * device array of lsl_noalloc_scratch_bytes() bytes (64 MiB) that the library
+ * GEMM's split partials and their arrival counts, lsl_lora_linear_workspace_bytes'
+ * forward share) is a
+ * device array of lsl_noalloc_scratch_bytes() bytes (88 MiB + 64 KiB) that the library
  * holds on each GPU it runs on until the process ends. It calls no allocating
  * routine. WORKSPACE if the shape needs more scratch than that. Every call on
  * one GPU shares that GPU's array: calls that overlap on one GPU (two streams,

@@ -70,6 +70,7 @@ PROTOS = {
     "lsl_nf4dq_quantize_absmax": (i32, [vp, i64, vp, vp, vp]),
     "lsl_nf4dq_dequant": (i32, [vp, vp, vp, i64, i64, vp, vp]),
     "lsl_lora_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
+    "lsl_lora_linear_bwd_u_offset": (sz, [i64, i64, i64]),
     "lora_linear_fwd": (i32, [vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, sz, vp]),
     "lora_linear_bwd": (i32, [vp, vp, vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
     "lora_linear_fwd_noalloc": (i32, [vp, i64, C.POINTER(Weight), vp, vp, i32, f32, vp, vp, vp]),

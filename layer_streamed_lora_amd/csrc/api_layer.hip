@@ -129,7 +129,7 @@ static void layout_of(const lsl_layer_cfg* c, lsl_layer_layout* L) {
 struct Plan {
   size_t n1, tqkv, qkv, qkr, o, lse, to, h1, n2, tgu, gu, a, td;                    // forward
   size_t ud, da, dgu, ugu, dn2, dh1, uo, dob, dqkr, dqkv, uqkv, dn1, attn_ws, o32;  // backward
-  size_t part, total;
+  size_t part, cnt, ncnt, total;
 };
 
 static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
@@ -152,7 +152,9 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
   p.a = take(T * d.I * 2);
   p.td = take(T * d.r * 2);
   // one region reused in turn by LoRA split partials and GEMM split-K partials
-  size_t part = std::max({lora_nt_ws_bytes(d.T, d.H), lora_nt_ws_bytes(d.T, d.Q), lora_nt_ws_bytes(d.T, d.I),
+  const int r = d.r;
+  size_t part = std::max({lora_nt_ws_bytes(d.T, d.H, 3 * r), lora_nt_ws_bytes(d.T, d.Q, r),
+                          lora_nt_ws_bytes(d.T, d.H, 2 * r), lora_nt_ws_bytes(d.T, d.I, r),
                           gemm_split_bytes(d.T, d.NQKV, d.H), gemm_split_bytes(d.T, d.H, d.Q),
                           gemm_split_bytes(d.T, 2 * d.I, d.H), gemm_split_bytes(d.T, d.H, d.I)});
   if (mode == LSL_MODE_BWD) {
@@ -170,13 +172,24 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
     p.dn1 = take(T * d.H * 2);
     p.attn_ws = take(lsl_attention_workspace_bytes(batch, seq, c->n_q, c->n_kv, c->head_dim));
     p.o32 = take(T * d.Q * 4);
-    part = std::max({part, lora_nt_ws_bytes(d.T, d.NQKV), lora_nt_ws_bytes(d.T, 2 * d.I),
-                     lora_tn_ws_bytes(d.T, d.H), lora_tn_ws_bytes(d.T, d.Q), lora_tn_ws_bytes(d.T, d.I),
-                     lora_tn_ws_bytes(d.T, d.NQKV), lora_tn_ws_bytes(d.T, 2 * d.I),
+    part = std::max({part, lora_nt_ws_bytes(d.T, d.NQKV, 3 * r), lora_nt_ws_bytes(d.T, d.H, r),
+                     lora_nt_ws_bytes(d.T, 2 * d.I, 2 * r),
+                     lora_tn_ws_bytes(d.T, d.H, 3 * r), lora_tn_ws_bytes(d.T, d.Q, r), lora_tn_ws_bytes(d.T, d.H, 2 * r),
+                     lora_tn_ws_bytes(d.T, d.I, r), lora_tn_ws_bytes(d.T, d.NQKV, 3 * r), lora_tn_ws_bytes(d.T, d.H, r),
+                     lora_tn_ws_bytes(d.T, 2 * d.I, 2 * r),
                      gemm_split_bytes(d.T, d.H, d.NQKV), gemm_split_bytes(d.T, d.Q, d.H),
                      gemm_split_bytes(d.T, d.H, 2 * d.I), gemm_split_bytes(d.T, d.I, d.H)});
   }
   p.part = take(part);
+  // the arrival counts of the side products and of the stream-K GEMMs: a region
+  // of their own (zeroed by the layer's first RMSNorm launch, left zero by every
+  // launch that uses it; the launches that share it run one after another)
+  p.ncnt = std::max({lora_counts_needed(d.T, std::max({d.NQKV, 2 * d.I, d.H, d.Q, d.I})),
+                     gemm_counts_needed(d.T, d.NQKV, d.H), gemm_counts_needed(d.T, d.H, d.Q),
+                     gemm_counts_needed(d.T, 2 * d.I, d.H), gemm_counts_needed(d.T, d.H, d.I),
+                     gemm_counts_needed(d.T, d.H, d.NQKV), gemm_counts_needed(d.T, d.Q, d.H),
+                     gemm_counts_needed(d.T, d.H, 2 * d.I), gemm_counts_needed(d.T, d.I, d.H)});
+  p.cnt = take(p.ncnt * sizeof(unsigned));
   p.total = off;
   return p;
 }
@@ -217,7 +230,7 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
 // dry: only check every launch's conditions (nothing is enqueued).
 static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    int i, const uint16_t* x, uint16_t* t, uint16_t* y, const uint16_t* res,
-                                   float* part, hipStream_t s, bool dry) {
+                                   float* part, unsigned* cnt, hipStream_t s, bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -225,7 +238,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   if (lo) {  // adapters on: t = x A^T first, then the GEMM's LoRA K-step
     LoraNt nt;
     nt.p = x; nt.ldp = k; nt.T = d.T; nt.K = k; nt.kl = kl; nt.a_full = lo->A[i];
-    nt.out = t; nt.ldo = kl; nt.ws = part;
+    nt.out = t; nt.ldo = kl; nt.ws = part; nt.cnt = cnt;
     LSL_TRY(dry ? lora_nt_check(nt) : lora_nt_launch(nt, s));
   }
   if (!y) return LSL_OK;
@@ -238,7 +251,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   else if (i == LSL_M_GU) { g.seg_end[0] = d.I; g.seg_end[1] = 2 * d.I; }
   else g.seg_end[0] = n;
   g.scale = c->lora_scale;
-  g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part;
+  g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part; g.cnt = cnt;
   if (i == LSL_M_QKV) g.bias = W.qkv_bias;
   if (dry) return gemm_check(g);
   timing_mark(1 + i, true, s);
@@ -251,8 +264,8 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
 // dA += s u^T x; dB += s dy^T t (per projection).
 static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    const lsl_lora_grads* gr, int i, const uint16_t* x, const uint16_t* t,
-                                   const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, hipStream_t s,
-                                   bool dry) {
+                                   const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, unsigned* cnt,
+                                   hipStream_t s, bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -263,7 +276,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
   LoraNt nt;
   nt.p = dy; nt.ldp = n; nt.T = d.T; nt.K = n; nt.kl = kl; nt.b_full = lo->B[i]; nt.r = d.r; nt.nseg = nseg;
   for (int q = 0; q < 4; ++q) nt.seg_end[q] = se[q];
-  nt.out = u; nt.ldo = kl; nt.ws = part;
+  nt.out = u; nt.ldo = kl; nt.ws = part; nt.cnt = cnt;
   LSL_TRY(dry ? lora_nt_check(nt) : lora_nt_launch(nt, s));
   if (dx) {
     GemmDesc g;
@@ -271,7 +284,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
     g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i]; g.wq8 = W.wq8[i]; g.wsc = W.wsc[i];
     g.M = d.T; g.N = k; g.K = n;
     g.lora = 2; g.la = u; g.ldla = kl; g.kl = kl; g.lb = lo->A[i]; g.r = d.r;
-    g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part;
+    g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part; g.cnt = cnt;
     if (dry) {
       LSL_TRY(gemm_check(g));
     } else {
@@ -283,13 +296,13 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
   }
   LoraTn ta;
   ta.p = x; ta.ldp = k; ta.q = u; ta.ldq = kl; ta.T = d.T; ta.W = k; ta.kl = kl;
-  ta.scale = c->lora_scale; ta.dA = gr->dA[i]; ta.ws = part;
+  ta.scale = c->lora_scale; ta.dA = gr->dA[i]; ta.ws = part; ta.cnt = cnt;
   LSL_TRY(dry ? lora_tn_check(ta) : lora_tn_launch(ta, s));
   LoraTn tb;
   tb.p = dy; tb.ldp = n; tb.q = t; tb.ldq = kl; tb.T = d.T; tb.W = n; tb.kl = kl;
   tb.scale = c->lora_scale; tb.dB = gr->dB[i]; tb.r = d.r; tb.nseg = nseg;
   for (int q = 0; q < 4; ++q) tb.seg_end[q] = se[q];
-  tb.ws = part;
+  tb.ws = part; tb.cnt = cnt;
   return dry ? lora_tn_check(tb) : lora_tn_launch(tb, s);
 }
 
@@ -307,26 +320,28 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   uint16_t* n2 = (uint16_t*)(ws + p.n2);
   uint16_t* gu = (uint16_t*)(ws + p.gu);
   uint16_t* a = (uint16_t*)(ws + p.a);
+  unsigned* cnt = (unsigned*)(ws + p.cnt);
   if (dry) {
-    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s, true));
-    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s, true));
-    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, s, true));
-    return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, s, true);
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, cnt, s, true));
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, cnt, s, true));
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, cnt, s, true));
+    return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, cnt, s, true);
   }
-  LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, s, false));
+  // (also zeroes the arrival counts every later side product of the call uses)
+  LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s, cnt, (int)p.ncnt));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, cnt, s, false));
   // q and k heads are adjacent in each row and share the frequencies: one launch
   uint16_t* qkr = (uint16_t*)(ws + p.qkr);
   LSL_TRY(rope_launch(qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(lsl_attention_fwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, s, false));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, cnt, s, false));
   LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, s, false));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, cnt, s, false));
   LSL_TRY(swiglu_fwd_launch(gu, d.T, d.I, a, s));
   // out == nullptr (the backward's recompute): the layer output itself is not
   // needed, only the LoRA product t of the down projection (for its dB)
-  return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, s, false);
+  return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, cnt, s, false);
 }
 
 // Backward with recompute. dry: check every GEMM's and side product's
@@ -341,6 +356,7 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
   uint16_t* dn1 = (uint16_t*)(w + p.dn1);
   LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, (float*)(w + p.o32), s, dry));
   float* part = (float*)(w + p.part);
+  unsigned* cnt = (unsigned*)(w + p.cnt);
   uint16_t* qkv = (uint16_t*)(w + p.qkv);
   uint16_t* qkr = (uint16_t*)(w + p.qkr);
   uint16_t* dqkr = (uint16_t*)(w + p.dqkr);
@@ -352,14 +368,14 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
   uint16_t* dob = (uint16_t*)(w + p.dob);
   // MLP
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_DOWN, (uint16_t*)(w + p.a), (uint16_t*)(w + p.td), dy,
-                           (uint16_t*)(w + p.ud), da, part, s, dry));
+                           (uint16_t*)(w + p.ud), da, part, cnt, s, dry));
   if (!dry) LSL_TRY(swiglu_bwd_launch((uint16_t*)(w + p.gu), da, d.T, d.I, dgu, s));
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), (uint16_t*)(w + p.tgu), dgu,
-                           (uint16_t*)(w + p.ugu), dn2, part, s, dry));
+                           (uint16_t*)(w + p.ugu), dn2, part, cnt, s, dry));
   if (!dry) LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
   // attention block
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), (uint16_t*)(w + p.to), dh1,
-                           (uint16_t*)(w + p.uo), dob, part, s, dry));
+                           (uint16_t*)(w + p.uo), dob, part, cnt, s, dry));
   if (!dry) {
     LSL_TRY(lsl_attention_bwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
                               (const float*)(w + p.o32), d.NQKV, d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d,
@@ -368,7 +384,7 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
                         1, s));
   }
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
-                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, s, dry));
+                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, cnt, s, dry));
   if (dx && !dry) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
   return LSL_OK;
 }

@@ -6,10 +6,11 @@
 #include "api_util.h"
 #include <mutex>
 
-// bytes of the allocation-free forward's scratch (64 MiB: the largest split
-// partials of a Llama-3.1-8B projection at 1024 tokens, its down projection's)
+// bytes of the allocation-free forward's scratch: 88 MiB, the largest stream-K
+// partials of a Llama-3.1-8B projection at 1024 tokens (q|k|v: 351 slots of
+// 256 KiB), plus 64 KiB for the arrival counts
 #ifndef LSL_NOALLOC_SCRATCH_BYTES
-#define LSL_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define LSL_NOALLOC_SCRATCH_BYTES ((88u << 20) + (64u << 10))
 #endif
 
 using namespace lsl;
@@ -18,19 +19,27 @@ namespace lsl {
 
 bool lora_rank_ok(int32_t r) { return r >= 8 && r <= 64 && r % 8 == 0; }
 
-// fwd: the t = x A^T partials, then the GEMM's split-K partials (in turn)
-size_t linear_ws_fwd(int64_t T, int64_t N, int64_t K) {
-  return std::max(lora_nt_ws_bytes(T, K), gemm_split_bytes(T, N, K));
+// Workspace of the LoRA linear: the arrival counts of the side products and of
+// the GEMM (zeroed at the start of each call), then (bwd) u = dy B [T x r] bf16,
+// then one region reused in turn by the side products' partials and the GEMM's
+// split-K / stream-K partials.
+static size_t linear_counts(int64_t T, int64_t N, int64_t K) {
+  return std::max({lora_counts_needed(T, std::max(N, K)), gemm_counts_needed(T, N, K), gemm_counts_needed(T, K, N)});
+}
+static size_t linear_counts_bytes(int64_t T, int64_t N, int64_t K) {
+  return align256(linear_counts(T, N, K) * sizeof(unsigned));
 }
 
-// bwd: u = dy B [T x r] bf16, then one region reused in turn by the u partials,
-// the dX GEMM's split-K partials and the dA / dB partials
+size_t linear_ws_fwd(int64_t T, int64_t N, int64_t K, int r) {
+  return linear_counts_bytes(T, N, K) + std::max(lora_nt_ws_bytes(T, K, r), gemm_split_bytes(T, N, K));
+}
+
 size_t linear_ws_bwd(int64_t T, int64_t N, int64_t K, int r) {
-  size_t part = lora_nt_ws_bytes(T, N);
+  size_t part = lora_nt_ws_bytes(T, N, r);
   part = std::max(part, gemm_split_bytes(T, K, N));
-  part = std::max(part, lora_tn_ws_bytes(T, K));
-  part = std::max(part, lora_tn_ws_bytes(T, N));
-  return align256((size_t)T * r * 2) + part;
+  part = std::max(part, lora_tn_ws_bytes(T, K, r));
+  part = std::max(part, lora_tn_ws_bytes(T, N, r));
+  return linear_counts_bytes(T, N, K) + align256((size_t)T * r * 2) + part;
 }
 
 static lsl_status check_weight(const lsl_weight* W, const char* fn) {
@@ -64,9 +73,13 @@ static void weight_into(GemmDesc& g, const lsl_weight* W) {
 
 }  // namespace lsl
 
+extern "C" size_t lsl_lora_linear_bwd_u_offset(int64_t T, int64_t n_out, int64_t k_in) {
+  return T > 0 && n_out > 0 && k_in > 0 ? linear_counts_bytes(T, n_out, k_in) : 0;
+}
+
 extern "C" size_t lsl_lora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in, int32_t r) {
   if (T < 0 || n_out <= 0 || k_in <= 0 || !lora_rank_ok(r)) return 0;
-  return std::max(linear_ws_fwd(T, n_out, k_in), linear_ws_bwd(T, n_out, k_in, r));
+  return std::max(linear_ws_fwd(T, n_out, k_in, r), linear_ws_bwd(T, n_out, k_in, r));
 }
 
 extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_weight* W, const uint16_t* A,
@@ -78,21 +91,25 @@ extern "C" lsl_status lora_linear_fwd(const uint16_t* x, int64_t T, const lsl_we
   if (!lora_rank_ok(r)) return set_error(LSL_ERR_UNSUPPORTED, "%s: rank %d must be a multiple of 8 in [8, 64]", fn, r);
   if (T == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x, A, B, y, t_out}));
-  const size_t need = linear_ws_fwd(T, W->n_out, W->k_in);
-  if (ws_bytes < need || (need && (!ws || !aligned(ws, 256))))
+  const size_t need = linear_ws_fwd(T, W->n_out, W->k_in, r);
+  if (ws_bytes < need || !ws || !aligned(ws, 256))
     return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
+  const size_t ncnt = linear_counts(T, W->n_out, W->k_in);
+  unsigned* cnt = (unsigned*)ws;
+  float* part = (float*)((char*)ws + linear_counts_bytes(T, W->n_out, W->k_in));
   LoraNt nt;
   nt.p = x; nt.ldp = W->k_in; nt.T = T; nt.K = W->k_in; nt.kl = r; nt.a_full = A;
-  nt.out = t_out; nt.ldo = r; nt.ws = (float*)ws;
+  nt.out = t_out; nt.ldo = r; nt.ws = part; nt.cnt = cnt;
   GemmDesc g;
   g.x = x; g.ldx = W->k_in; weight_into(g, W); g.kn = false;
   g.M = T; g.N = W->n_out; g.K = W->k_in;
   g.lora = 1; g.la = t_out; g.ldla = r; g.kl = r; g.lb = B; g.r = r; g.nseg = 1; g.seg_end[0] = W->n_out;
-  g.scale = scale; g.y = y; g.ldy = W->n_out; g.split_ws = (float*)ws; g.bias = W->bias;
+  g.scale = scale; g.y = y; g.ldy = W->n_out; g.split_ws = part; g.cnt = cnt; g.bias = W->bias;
   // every launch's conditions first, so that a rejected call enqueues nothing
   LSL_TRY(lora_nt_check(nt));
   LSL_TRY(gemm_check(g));
+  LSL_TRY(lora_counts_zero(cnt, ncnt, s));
   LSL_TRY(lora_nt_launch(nt, s));
   return gemm_launch(g, s);
 }
@@ -113,26 +130,30 @@ extern "C" lsl_status lora_linear_bwd(const uint16_t* x, const uint16_t* t, cons
     return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu (or not 256-byte aligned)", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   const int64_t N = W->n_out, K = W->k_in;
-  uint16_t* u = (uint16_t*)ws;
-  float* part = (float*)((char*)ws + align256((size_t)T * r * 2));
+  const size_t ncnt = linear_counts(T, N, K);
+  unsigned* cnt = (unsigned*)ws;
+  uint16_t* u = (uint16_t*)((char*)ws + linear_counts_bytes(T, N, K));
+  float* part = (float*)((char*)u + align256((size_t)T * r * 2));
   LoraNt nt;
   nt.p = dy; nt.ldp = N; nt.T = T; nt.K = N; nt.kl = r; nt.b_full = B; nt.r = r; nt.nseg = 1; nt.seg_end[0] = N;
-  nt.out = u; nt.ldo = r; nt.ws = part;
+  nt.out = u; nt.ldo = r; nt.ws = part; nt.cnt = cnt;
   GemmDesc g;
   g.x = dy; g.ldx = N; weight_into(g, W); g.kn = true;
   g.M = T; g.N = K; g.K = N;
   g.lora = 2; g.la = u; g.ldla = r; g.kl = r; g.lb = A; g.r = r;
-  g.scale = scale; g.y = dx; g.ldy = K; g.split_ws = part;
+  g.scale = scale; g.y = dx; g.ldy = K; g.split_ws = part; g.cnt = cnt;
   LoraTn ta;
   ta.p = x; ta.ldp = K; ta.q = u; ta.ldq = r; ta.T = T; ta.W = K; ta.kl = r; ta.scale = scale; ta.dA = dA; ta.ws = part;
+  ta.cnt = cnt;
   LoraTn tb;
   tb.p = dy; tb.ldp = N; tb.q = t; tb.ldq = r; tb.T = T; tb.W = N; tb.kl = r; tb.scale = scale; tb.dB = dB;
-  tb.r = r; tb.nseg = 1; tb.seg_end[0] = N; tb.ws = part;
+  tb.r = r; tb.nseg = 1; tb.seg_end[0] = N; tb.ws = part; tb.cnt = cnt;
   // every launch's conditions first, so that a rejected call enqueues nothing
   LSL_TRY(lora_nt_check(nt));
   if (dx) LSL_TRY(gemm_check(g));
   LSL_TRY(lora_tn_check(ta));
   LSL_TRY(lora_tn_check(tb));
+  LSL_TRY(lora_counts_zero(cnt, ncnt, s));
   LSL_TRY(lora_nt_launch(nt, s));
   if (dx) LSL_TRY(gemm_launch(g, s));
   LSL_TRY(lora_tn_launch(ta, s));
@@ -181,14 +202,15 @@ extern "C" lsl_status lora_linear_fwd_noalloc(const uint16_t* x, int64_t T, cons
   if (T < 0) return set_error(LSL_ERR_INVALID_ARG, "%s: T < 0", fn);
   if (!lora_rank_ok(r)) return set_error(LSL_ERR_UNSUPPORTED, "%s: rank %d must be a multiple of 8 in [8, 64]", fn, r);
   if (T == 0) return LSL_OK;
-  const size_t need = linear_ws_fwd(T, W->n_out, W->k_in);
+  const size_t need = linear_ws_fwd(T, W->n_out, W->k_in, r);
   if (need > NOALLOC_SCRATCH_BYTES)
     return set_error(LSL_ERR_WORKSPACE, "%s: this shape needs %zu bytes of scratch, more than the %zu the library holds",
                      fn, need, NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
   LSL_TRY(scratch_on_current_device(fn, &ws));
-  // nothing in the forward's scratch needs to start at zero: the side product's
-  // and the GEMM's split partials are written in full before they are read
+  // the side product's arrival counts, which must start at zero, are zeroed by
+  // lora_linear_fwd at its start; its split partials are written in full
+  // before they are read
   return lora_linear_fwd(x, T, W, A, B, r, scale, y, t_out, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 

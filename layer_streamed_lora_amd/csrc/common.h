@@ -57,6 +57,42 @@ LSL_DEV bf16x8 ld_tr8(const uint16_t* tile, int ld, int r0, int c0, int lane) {
   return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
 }
 
+// Fixed-order reductions across workgroups without a second kernel. The
+// workgroups that share an output tile store float32 partials with
+// device-coherent stores (wt_store4: the sc1 cache policy, the one the gfx942
+// memory model gives device-scope atomic stores, which write through the XCD's
+// L2), then call last_arrival. It returns true (in every thread) in the
+// workgroup that arrives last; that one reads the partials back with
+// device-coherent loads (wt_load4, likewise never served from a stale L2 line)
+// and adds them in a fixed order, so the bits do not depend on the arrival
+// order. The count (zero before the first arrival) is reset for the next
+// launch. A device-scope fence would make plain stores visible too, but on this
+// chip it writes back and invalidates the XCD's whole L2, and hundreds of
+// workgroups fencing at once cost more than the work they hand over.
+constexpr int CPOL_SC1 = 16;  // buffer instruction cache-policy bit: sc1 (device scope)
+LSL_DEV __amdgpu_buffer_rsrc_t wt_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+LSL_DEV void wt_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, CPOL_SC1);
+}
+LSL_DEV f32x4 wt_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, CPOL_SC1));
+}
+LSL_DEV bool last_arrival(unsigned* cnt, int S) {
+  __shared__ unsigned prev;
+  // this thread's partial stores are complete (written through) before the
+  // workgroup arrives
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (unsigned)S - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return prev == (unsigned)S - 1;
+}
+
 // Host-side status plumbing shared by every translation unit.
 #include "../../include/lsl.h"
 namespace lsl {

@@ -16,7 +16,10 @@ constexpr int RMS_CHUNKS = 16;
 
 // y = bf16(x * r * w), r = 1 / sqrt(mean(x^2) + eps)
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          int64_t T, int64_t H, float eps, uint16_t* __restrict__ y) {
+                                                          int64_t T, int64_t H, float eps, uint16_t* __restrict__ y,
+                                                          unsigned* __restrict__ zero, int nzero) {
+  if (blockIdx.x == 0)  // side job: zero the caller's nzero words
+    for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0u;
   int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (row >= T) return;
@@ -89,10 +92,12 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __rest
   }
 }
 
-lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y, hipStream_t s) {
+lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                              hipStream_t s, unsigned* zero, int nzero) {
   if (H > 512 * RMS_CHUNKS) return set_error(LSL_ERR_UNSUPPORTED, "rmsnorm: hidden %lld > %d", (long long)H, 512 * RMS_CHUNKS);
   if (T == 0) return LSL_OK;
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, w, T, H, eps, y);
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, w, T, H, eps, y, zero,
+                     zero ? nzero : 0);
   return check_launch("rmsnorm_fwd");
 }
 lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,

@@ -27,8 +27,11 @@ struct GemmDesc {
   // into out32 + s * o32_split (y must be NULL; the caller adds the splits)
   int acc_splits = 1; int64_t o32_split = 0;
   int64_t kwrap = 0;
-  // split-K scratch for the bf16 epilogue: gemm_split_bytes(M, N, K) bytes
+  // split-K / stream-K scratch for the bf16 epilogue: gemm_split_bytes(M, N, K)
+  // bytes; stream-K also takes gemm_counts_needed(M, N, K) arrival counts,
+  // zero before the first launch and left zero by every launch
   float* split_ws = nullptr;
+  unsigned* cnt = nullptr;
 };
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
 // The conditions gemm_launch rejects, checked without launching anything.
@@ -37,6 +40,7 @@ lsl_status gemm_check(const GemmDesc& d);
 // the float32 scratch they need (0 when the GEMM is not split).
 int gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
+size_t gemm_counts_needed(int64_t M, int64_t N, int64_t K);
 // Tile shape gemm_launch picks for an M x N output (bn weight rows, bm tokens).
 void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm);
 // cross-entropy GEMMs: whether the logits passes of an M x N x K problem run in

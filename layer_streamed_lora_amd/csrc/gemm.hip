@@ -63,7 +63,9 @@ struct GemmKArgs {
   float* out32; int64_t ldo32; int first; int64_t o32_split;  // split s accumulates at out32 + s o32_split
   int64_t kwrap;             // KN operand: reduction index k reads weight row k mod kwrap (K <= 2 kwrap)
   int ksplit; int kt_per_split;  // split-K: workgroup b takes split b / (tiles_m tiles_n)
-  float* spart;                  // float32 partials [ksplit][M][N]
+  float* spart;                  // float32 partials [ksplit][M][N]; stream-K: tile slots
+  int sk_g;                      // stream-K (large tile): number of workgroups, 0 when off
+  unsigned* cnt;                 // stream-K: per-tile arrival counts (zero between launches)
 };
 
 enum { EPI_BF16 = 0, EPI_LSE = 1, EPI_CEGRAD = 2, EPI_ACC32 = 3 };
@@ -1047,28 +1049,25 @@ LSL_DEV void tile_barrier() {
 
 }  // namespace big
 
-template <int WFMT, bool KN, int LORA, int EPI = EPI_BF16>
-__global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a) {
-  using namespace big;
+namespace big {
+
+// The LDS stages of one workgroup.
+struct Smem {
+  uint16_t* xs0; uint16_t* xs1; uint16_t* ws0; uint16_t* ws1; const float* lut;
+};
+
+// acc = the sum over reduction steps [kb, kb + nsteps) of output tile (m0, n0),
+// plus s * (L Lt^T) when kb == 0 and the GEMM has a LoRA term. On return every
+// wave has passed the last step's barrier, so both stages are free again.
+template <int WFMT, bool KN, int LORA>
+LSL_DEV void tile_steps(const GemmKArgs& a, int64_t m0, int64_t n0, int kb, int nsteps, f32x16 (&acc)[4][2],
+                        const Smem& sm, int tid) {
   using W = BigW<WFMT, KN>;
   constexpr int WL = KN ? 2 : (W::kind == 1 ? 1 : 0);
-  __shared__ __attribute__((aligned(16))) uint16_t Xs0[XSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Xs1[XSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws0[WSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws1[WSZ];
-  __shared__ float lut[16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
-  int tm, tn;
-  const int ntiles = a.tiles_m * a.tiles_n;
-  const int split = (int)blockIdx.x / ntiles;  // split-K: reduction steps [kt0, kt0 + KT)
-  tile_coords((int)blockIdx.x - split * ntiles, a.tiles_m, a.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  if constexpr (WFMT != LSL_WFMT_BF16)
-    if (tid < 16) lut[tid] = a.cb[tid];
-
-  f32x16 acc[4][2];
+  uint16_t* const Xs0 = sm.xs0; uint16_t* const Xs1 = sm.xs1;
+  uint16_t* const Ws0 = sm.ws0; uint16_t* const Ws1 = sm.ws1;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1076,9 +1075,8 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int kt0 = split * a.kt_per_split;
-  const int KT = min((int)(a.K / BK) - kt0, a.kt_per_split);
-  const int64_t k0 = (int64_t)kt0 * BK;
+  const int KT = nsteps;
+  const int64_t k0 = (int64_t)kb * BK;
   TileDma xd;
   xd.init(a.ldx, m0, 0, wave, lane);
   W wl;
@@ -1088,9 +1086,10 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
   if constexpr (W::kind == 1) wl.issue(a, k0, Ws0);
   else wl.load(a, k0);
 
-  // LoRA K-step first (split 0), on the second stage's buffers: the
-  // accumulators start as s * (L Lt^T)
-  if constexpr (LORA != 0) if (split == 0) {
+  // the LoRA K-step (with the tile's first reduction step), on the second
+  // stage's buffers: the accumulators start as s * (L Lt^T)
+  const bool lora_here = LORA != 0 && kb == 0;
+  if constexpr (LORA != 0) if (lora_here) {
     lora_stage_big<LORA>(a, Xs1, Ws1, m0, n0, tid);
     __syncthreads();
     mma_big<LORA == 1 ? 0 : 2>(Ws1, Xs1, acc, wn, wm, lane, (a.kl + 15) / 16);
@@ -1106,11 +1105,11 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
 
   // prologue: step 0 into stage 0; codes of step 1 into registers
   if constexpr (W::kind == 0) {
-    if (LORA == 0 || split != 0) __syncthreads();  // lut visible (the LoRA step's barrier did it otherwise)
-    wl.store(Ws0, lut, tid);
+    if (!lora_here) __syncthreads();  // lut visible (the LoRA step's barrier did it otherwise)
+    wl.store(Ws0, sm.lut, tid);
     if (KT > 1) wl.load(a, k0 + BK);
   }
-  big::tile_barrier<0>();
+  tile_barrier<0>();
   auto step = [&](int kt, const uint16_t* __restrict__ xc, const uint16_t* __restrict__ wc, uint16_t* __restrict__ xn,
                   uint16_t* __restrict__ wnx) {
     const bool next = kt + 1 < KT, next2 = kt + 2 < KT;
@@ -1128,7 +1127,7 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
       if (next) xd.issue(a.x, a.ldx, a.M, k0 + (int64_t)(kt + 1) * BK, xn);
       if (next2) {
         // the weight loads must issue after the DMA: the barrier below counts them
-        big::order_point();
+        order_point();
         wl.load(a, k0 + (int64_t)(kt + 2) * BK);
       }
       // quarter q's codebook values are read one sub-step before they are scaled
@@ -1144,28 +1143,195 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
           if (q + 1 < 4) w.fetch(q + 1, lut, v[(q + 1) & 1]);
           w.emit(q, v[q & 1], dst, tid);
         }
-      } part{cur, lut, wnx, tid, {}};
+      } part{cur, sm.lut, wnx, tid, {}};
       mma_big<WL>(wc, xc, acc, wn, wm, lane, 4, part);
     }
     // the DMA of step kt + 1 is complete once at most the weight loads issued
     // after it (step kt + 2) are outstanding
     if constexpr (W::kind == 0 && W::nload == 2) {
-      if (next2) big::tile_barrier<2>(); else big::tile_barrier<0>();
+      if (next2) tile_barrier<2>(); else tile_barrier<0>();
     } else if constexpr (W::kind == 0 && W::nload == 4) {
-      if (next2) big::tile_barrier<4>(); else big::tile_barrier<0>();
+      if (next2) tile_barrier<4>(); else tile_barrier<0>();
     } else if constexpr (W::kind == 0 && W::nload == 8) {
-      if (next2) big::tile_barrier<8>(); else big::tile_barrier<0>();
+      if (next2) tile_barrier<8>(); else tile_barrier<0>();
     } else {
-      big::tile_barrier<0>();
+      tile_barrier<0>();
     }
   };
   for (int kt = 0; kt < KT; kt += 2) {
     step(kt, Xs0, Ws0, Xs1, Ws1);
     if (kt + 1 < KT) step(kt + 1, Xs1, Ws1, Xs0, Ws0);
   }
+}
+
+// bf16 epilogue of a finished tile (bias, residual), or its float32 split-K
+// partial at `part` (row-major [M][N]) when part != NULL, for the column blocks
+// ni0 .. ni0 + NI - 1 held in v[0 .. NI - 1]. Block (ni, mi), q < 4: the lane
+// holds C[m][n .. n + 3] with m = m0 + 64 wm + 32 mi + lane % 32,
+// n = n0 + 128 wn + 32 ni + 8 q + 4 (lane / 32).
+template <int NI>
+LSL_DEV void store_tile_bf16(const GemmKArgs& a, const f32x16 (&acc)[NI][2], int ni0, int64_t m0, int64_t n0, int tid,
+                             float* part) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t mb = m0 + (wave >> 1) * 64 + (lane & 31);
+  const int64_t nb = n0 + (wave & 1) * 128 + (lane >> 5) * 4;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = nb + (ni0 + ni) * 32 + 8 * q;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int64_t m = mb + mi * 32;
+        if (m >= a.M) continue;
+        const f32x16& v = acc[ni][mi];
+        if (part)
+          *reinterpret_cast<f32x4*>(part + m * a.N + n) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+        else
+          store_bf16x4(a, m, n, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+    }
+}
+
+// Stream-K partial slots hold a tile's accumulators in register order: float4
+// group g of thread t at (g NT + t) * 4, so every store and load is a
+// contiguous 16-byte access per lane. They are written and read through
+// (wt_store4 / wt_load4): the slot region is handed between workgroups on
+// different XCDs within the launch.
+constexpr int SLOT = BM * BN;
+LSL_DEV void slot_store(__amdgpu_buffer_rsrc_t rs, int slot, const f32x16 (&acc)[4][2], int tid) {
+  const uint32_t so = (uint32_t)slot * SLOT * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int g = (i * 2 + j) * 4 + q;
+        const f32x16& v = acc[i][j];
+        wt_store4(rs, (uint32_t)(g * NT + tid) * 16, so, f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]});
+      }
+}
+
+// The last arrival's sum of a split tile: the partials in slots s0 .. s0 + nseg - 1,
+// added in that order, then the bf16 epilogue; one half of the tile (column
+// blocks 2 h, 2 h + 1) at a time, 16 loads in flight per slot.
+LSL_DEV void sk_fixup(const GemmKArgs& a, __amdgpu_buffer_rsrc_t rs, int s0, int nseg, int64_t m0, int64_t n0,
+                      int tid) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f32x16 sum[2][2];
+    for (int v = 0; v < nseg; ++v) {
+      const uint32_t so = (uint32_t)(s0 + v) * SLOT * 4;
+      f32x4 p[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) p[c] = wt_load4(rs, (uint32_t)((h * 16 + c) * NT + tid) * 16, so);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int i = c >> 3, j = (c >> 2) & 1, q = c & 3;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[i][j][4 * q + e] = v == 0 ? p[c][e] : sum[i][j][4 * q + e] + p[c][e];
+      }
+    }
+    store_tile_bf16<2>(a, sum, 2 * h, m0, n0, tid, nullptr);
+  }
+}
+
+// Stream-K schedule: the reduction steps of all tiles, tile after tile, form
+// one range of U = tiles * KT units that G workgroups split evenly; workgroup w
+// takes units [U w / G, U (w + 1) / G). owner(u) is the workgroup whose range
+// holds unit u.
+LSL_DEV int sk_owner(int u, int U, int G) { return ((u + 1) * G - 1) / U; }
+
+}  // namespace big
+
+// Stream-K over a.sk_g workgroups (bf16 epilogue): workgroup w (the dispatch
+// order deals blocks to the XCDs in turn, so w gives each XCD a contiguous range
+// of units) walks its units tile by tile. Tile t is (tm, tn) = (t % tiles_m,
+// t / tiles_m): an XCD's tiles share weight tiles. A tile split over several
+// workgroups is summed by the one that arrives last, in workgroup order.
+template <int WFMT, bool KN, int LORA>
+__global__ __launch_bounds__(big::NT, 1) void gemm_sk_kernel(const GemmKArgs a) {
+  using namespace big;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs0[XSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs1[XSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws0[WSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws1[WSZ];
+  __shared__ float lut[16];
+  const Smem sm{Xs0, Xs1, Ws0, Ws1, lut};
+  if constexpr (WFMT != LSL_WFMT_BF16)
+    if (threadIdx.x < 16) lut[threadIdx.x] = a.cb[threadIdx.x];
+  f32x16 acc[4][2];
+  const int KTall = (int)(a.K / BK);
+  const int G = a.sk_g, b = (int)blockIdx.x;
+  const int w = (b & 7) * (G >> 3) + (b >> 3);
+  // U G < 2^31 (checked on the host)
+  const int U = a.tiles_m * a.tiles_n * KTall;
+  // the slots: (G + tiles - 1) x 256 KiB, below 4 GiB (tiles < G)
+  const __amdgpu_buffer_rsrc_t rs = wt_rsrc(a.spart, (int64_t)(G + a.tiles_m * a.tiles_n - 1) * SLOT * 4);
+  const int ue = U * (w + 1) / G;
+  // tiles whose partials this workgroup adds up (it arrived last), summed after
+  // its own segments so that the sum's registers are not live in the loop; with
+  // fewer tiles than workgroups a workgroup has at most two segments
+  int fix_t[2], fix_f[2], fix_n[2], nfix = 0;
+  for (int u = U * w / G; u < ue;) {
+    // thread-index arithmetic is redone per segment instead of being held in
+    // registers across the loop (which would spill)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int t = u / KTall;
+    const int kb = u - t * KTall;
+    const int ke = min(KTall, kb + (ue - u));
+    const int64_t m0 = (int64_t)(t % a.tiles_m) * BM, n0 = (int64_t)(t / a.tiles_m) * BN;
+    tile_steps<WFMT, KN, LORA>(a, m0, n0, kb, ke - kb, acc, sm, tid);
+    u += ke - kb;
+    if (kb == 0 && ke == KTall) {
+      store_tile_bf16<4>(a, acc, 0, m0, n0, tid, nullptr);
+      continue;
+    }
+    // workgroups f .. l share tile t; their partials sit in slots f + t .. l + t
+    slot_store(rs, w + t, acc, tid);
+    const int f = sk_owner(t * KTall, U, G), l = sk_owner(t * KTall + KTall - 1, U, G);
+    if (last_arrival(a.cnt + t, l - f + 1) && nfix < 2) {
+      fix_t[nfix] = t; fix_f[nfix] = f; fix_n[nfix] = l - f + 1;
+      ++nfix;
+    }
+  }
+  const int tid = threadIdx.x;
+  for (int i = 0; i < nfix; ++i) {
+    const int t = fix_t[i];
+    sk_fixup(a, rs, fix_f[i] + t, fix_n[i], (int64_t)(t % a.tiles_m) * BM, (int64_t)(t / a.tiles_m) * BN, tid);
+  }
+}
+
+template <int WFMT, bool KN, int LORA, int EPI = EPI_BF16>
+__global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a) {
+  using namespace big;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs0[XSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs1[XSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws0[WSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws1[WSZ];
+  __shared__ float lut[16];
+  const Smem sm{Xs0, Xs1, Ws0, Ws1, lut};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if constexpr (WFMT != LSL_WFMT_BF16)
+    if (tid < 16) lut[tid] = a.cb[tid];
+  f32x16 acc[4][2];
+  const int KTall = (int)(a.K / BK);
+
+  int tm, tn;
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int split = (int)blockIdx.x / ntiles;  // split-K: reduction steps [kt0, kt0 + KT)
+  tile_coords((int)blockIdx.x - split * ntiles, a.tiles_m, a.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int kt0 = split * a.kt_per_split;
+  tile_steps<WFMT, KN, LORA>(a, m0, n0, kt0, min(KTall - kt0, a.kt_per_split), acc, sm, tid);
 
   // epilogue: block (ni, mi), q < 4: the lane holds C[m][n .. n + 3] with
   // m = m0 + 64 wm + 32 mi + lane % 32, n = n0 + 128 wn + 32 ni + 8 q + 4 (lane / 32)
+  const int wn = wave & 1, wm = wave >> 1;
   const int64_t mb = m0 + wm * 64 + (lane & 31);
   const int64_t nb = n0 + wn * 128 + (lane >> 5) * 4;
   if constexpr (EPI == EPI_LSE) {
@@ -1202,24 +1368,7 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_big_kernel(const GemmKArgs a)
     return;
   }
   // split-K: this split's float32 partial (gemm_split_reduce adds the splits in order)
-  float* part = a.ksplit > 1 ? a.spart + (int64_t)split * a.M * a.N : nullptr;
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = nb + ni * 32 + 8 * q;
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int64_t m = mb + mi * 32;
-        if (m >= a.M) continue;
-        const f32x16& v = acc[ni][mi];
-        if (part)
-          *reinterpret_cast<f32x4*>(part + m * a.N + n) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-        else
-          store_bf16x4(a, m, n, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-      }
-    }
+  store_tile_bf16<4>(a, acc, 0, m0, n0, tid, a.ksplit > 1 ? a.spart + (int64_t)split * a.M * a.N : nullptr);
 }
 
 template <int WFMT, bool KN, int BN, int BM>
@@ -1303,58 +1452,70 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
 #ifndef LSL_BIG_MIN_TILES
 #define LSL_BIG_MIN_TILES 192
 #endif
-// GEMMs with fewer tiles but a long reduction take the large tile too, with the
-// reduction split so that about BIG_SPLIT_TARGET workgroups run, each at least
-// BIG_SPLIT_MIN_STEPS K-steps. Measured at 1024 tokens on the Llama-8B layer:
-// the down projection forward (K 14336, four splits) 182 -> 156 us and the
-// gate|up input gradient (K 28672, four splits) 355 -> 302 us.
-#ifndef LSL_BIG_SPLIT_MIN_TILES
-#define LSL_BIG_SPLIT_MIN_TILES 32
+// Stream-K in the large tile: when the tiles fill less than BIG_MIN_TILES of
+// the SK_G workgroups (one per CU), the reduction steps of all tiles are dealt
+// out evenly to SK_G workgroups instead, as long as each gets at least
+// SK_MIN_STEPS steps. Each split tile costs a float32 partial per segment (256
+// KiB, written and read back once through one CU), about 30 us per launch in
+// all; at 1024 tokens of the Llama-8B layer that pays off from about 20 steps
+// per workgroup: q|k|v forward 89 -> 87 us and input gradient 92 -> 82 us
+// (24 steps each), against 65 -> 75 us for the o projection (16 steps), which
+// keeps the 64-row tiles with split-K, and 138 -> 160 us for the down
+// projection's input gradient (224 tiles), which keeps one tile per workgroup.
+// SK_G is the CU count of MI355X, so that the plan depends on the GEMM's shape only.
+#ifndef LSL_SK_G
+#define LSL_SK_G 256
 #endif
-#ifndef LSL_BIG_SPLIT_MIN_STEPS
-#define LSL_BIG_SPLIT_MIN_STEPS 48
+#ifndef LSL_SK_MIN_STEPS
+#define LSL_SK_MIN_STEPS 20
 #endif
-#ifndef LSL_BIG_SPLIT_TARGET
-#define LSL_BIG_SPLIT_TARGET 256
-#endif
-// 0: the 64-row tiles; 1: the large tile, unsplit; S > 1: the large tile, S splits
+static_assert(LSL_SK_G % 8 == 0, "stream-K workgroups are dealt to 8 XCDs");
+static_assert(LSL_BIG_MIN_TILES <= LSL_SK_G, "stream-K takes fewer tiles than workgroups");
+// 0: the 64-row tiles; 1: the large tile, one workgroup per tile; -1: the
+// large tile, stream-K over LSL_SK_G workgroups
 static int gemm_big_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
   if (tiles == 0) return 0;
-  if (tiles >= LSL_BIG_MIN_TILES) return 1;
-  if (tiles < LSL_BIG_SPLIT_MIN_TILES) return 0;
-  const int64_t steps = K / BK;
-  int64_t S = (LSL_BIG_SPLIT_TARGET + tiles - 1) / tiles;
-  if (S > steps / LSL_BIG_SPLIT_MIN_STEPS) S = steps / LSL_BIG_SPLIT_MIN_STEPS;
-  if (S < 2) return 0;
-  const int64_t per = (steps + S - 1) / S;
-  S = (steps + per - 1) / per;
-  // the splits must fill the chip as well as an unsplit large-tile GEMM does
-  // (the input gradient of q|k|v at 1024 tokens, 64 tiles x 2 splits, is
-  // slower than the 64-row tiles)
-  return tiles * S >= LSL_BIG_MIN_TILES ? (int)S : 0;
+  const int64_t units = tiles * (K / BK);
+  // (fewer tiles than workgroups: a workgroup's units span at most two tiles;
+  // units * SK_G < 2^31 keeps the kernel's unit arithmetic in 32 bits)
+  if (tiles < LSL_BIG_MIN_TILES && units >= (int64_t)LSL_SK_MIN_STEPS * LSL_SK_G &&
+      units * LSL_SK_G < ((int64_t)1 << 31))
+    return -1;
+  return tiles >= LSL_BIG_MIN_TILES ? 1 : 0;
+}
+
+size_t gemm_counts_needed(int64_t M, int64_t N, int64_t K) {
+  if (gemm_big_plan(M, N, K) != -1) return 0;
+  return (size_t)(((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN));
 }
 
 template <int WFMT, bool KN>
 static void launch_big(const GemmKArgs& a, int lora, hipStream_t s, dim3 grid) {
+  if (a.sk_g) {
+    if (lora == 0) hipLaunchKernelGGL((gemm_sk_kernel<WFMT, KN, 0>), grid, dim3(big::NT), 0, s, a);
+    else if (lora == 1) hipLaunchKernelGGL((gemm_sk_kernel<WFMT, KN, 1>), grid, dim3(big::NT), 0, s, a);
+    else hipLaunchKernelGGL((gemm_sk_kernel<WFMT, KN, 2>), grid, dim3(big::NT), 0, s, a);
+    return;
+  }
   if (lora == 0) hipLaunchKernelGGL((gemm_big_kernel<WFMT, KN, 0>), grid, dim3(big::NT), 0, s, a);
   else if (lora == 1) hipLaunchKernelGGL((gemm_big_kernel<WFMT, KN, 1>), grid, dim3(big::NT), 0, s, a);
   else hipLaunchKernelGGL((gemm_big_kernel<WFMT, KN, 2>), grid, dim3(big::NT), 0, s, a);
 }
 
-static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s, int S) {
+static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s, int plan) {
   a.tiles_m = (int)((d.M + big::BM - 1) / big::BM);
   a.tiles_n = (int)((d.N + big::BN - 1) / big::BN);
-  const int KT = (int)(d.K / BK);
   a.ksplit = 1;
-  a.kt_per_split = KT;
-  if (S > 1) {
-    if (!d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
-    a.kt_per_split = (KT + S - 1) / S;
-    a.ksplit = (KT + a.kt_per_split - 1) / a.kt_per_split;
+  a.kt_per_split = (int)(d.K / BK);
+  a.sk_g = 0;
+  dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  if (plan == -1) {
+    a.sk_g = LSL_SK_G;
     a.spart = d.split_ws;
+    a.cnt = d.cnt;
+    grid = dim3(LSL_SK_G);
   }
-  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n * a.ksplit));
   if (d.wfmt == LSL_WFMT_NF4) {
     if (d.kn) launch_big<LSL_WFMT_NF4, true>(a, d.lora, s, grid);
     else launch_big<LSL_WFMT_NF4, false>(a, d.lora, s, grid);
@@ -1365,18 +1526,16 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s,
     if (d.kn) launch_big<LSL_WFMT_BF16, true>(a, d.lora, s, grid);
     else launch_big<LSL_WFMT_BF16, false>(a, d.lora, s, grid);
   }
-  if (a.ksplit > 1) {
-    const int64_t n4 = d.M * d.N / 4;
-    hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
-                       a.ksplit, d.M, d.N, d.bias, d.res, d.ldres, d.y, d.ldy);
-  }
   return check_launch("gemm(256 x 256 tiles)");
 }
 
 // Cross-entropy GEMMs (bf16 weight, no LoRA) in the large tile: the logits
 // passes (forward log-sum-exp, gradient chunk) when the vocabulary gives enough
 // tiles unsplit, the dH accumulation when its splits fill the chip.
-bool gemm_ce_big(int64_t M, int64_t N, int64_t K) { return gemm_big_plan(M, N, K) == 1; }
+bool gemm_ce_big(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  return ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN) >= LSL_BIG_MIN_TILES;
+}
 
 int gemm_ce_tile_n(int64_t M, int64_t N, int64_t K) {
   if (gemm_ce_big(M, N, K)) return big::BN;
@@ -1385,6 +1544,18 @@ int gemm_ce_tile_n(int64_t M, int64_t N, int64_t K) {
   return bn;
 }
 
+// The float32 dH accumulation of the cross-entropy backward takes the large
+// tile with its reduction split so that about BIG_SPLIT_TARGET workgroups run,
+// each at least BIG_SPLIT_MIN_STEPS K-steps, when the splits fill the chip.
+#ifndef LSL_BIG_SPLIT_MIN_TILES
+#define LSL_BIG_SPLIT_MIN_TILES 32
+#endif
+#ifndef LSL_BIG_SPLIT_MIN_STEPS
+#define LSL_BIG_SPLIT_MIN_STEPS 48
+#endif
+#ifndef LSL_BIG_SPLIT_TARGET
+#define LSL_BIG_SPLIT_TARGET 256
+#endif
 static bool acc32_big(int64_t M, int64_t N, int S) {
   const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
   return tiles >= LSL_BIG_SPLIT_MIN_TILES && tiles * S >= LSL_BIG_MIN_TILES;
@@ -1447,7 +1618,7 @@ int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t steps = K / BK;
   if (tiles == 0) return 1;  // empty output
-  if (const int b = gemm_big_plan(M, N, K)) return b;
+  if (gemm_big_plan(M, N, K) != 0) return 1;  // the large tile has no separate reduction pass
   int64_t S = (LSL_SPLIT_TARGET + tiles - 1) / tiles;
   if (S > steps / LSL_SPLIT_MIN_STEPS) S = steps / LSL_SPLIT_MIN_STEPS;
   if (S < 2) return 1;
@@ -1456,6 +1627,9 @@ int gemm_splits(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  // stream-K: workgroup w's partial of tile t sits in slot w + t (the sum
+  // rises by at least one from each segment of the schedule to the next)
+  if (const size_t tiles = gemm_counts_needed(M, N, K)) return (LSL_SK_G + tiles - 1) * big::SLOT * sizeof(float);
   const int S = gemm_splits(M, N, K);
   return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
 }
@@ -1478,7 +1652,8 @@ lsl_status gemm_check(const GemmDesc& d) {
   if ((d.M + 256) * d.ldx * 2 > lim || (d.N + 128) * d.K * 2 > lim)
     return set_error(LSL_ERR_UNSUPPORTED, "gemm: operand larger than 4 GiB");
   if (d.epi == EPI_BF16) {
-    if (gemm_splits(d.M, d.N, d.K) > 1 && !d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
+    if (gemm_split_bytes(d.M, d.N, d.K) && !d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
+    if (gemm_counts_needed(d.M, d.N, d.K) && !d.cnt) return set_error(LSL_ERR_WORKSPACE, "gemm: stream-K arrival counts missing");
     return LSL_OK;
   }
   if (d.wfmt != LSL_WFMT_BF16 || d.lora) return set_error(LSL_ERR_UNSUPPORTED, "gemm: CE epilogues take a bf16 weight");

@@ -1,5 +1,5 @@
 // The rank-r side products of LoRA on bf16 MFMA, with fixed-order split
-// reductions (no atomics, so every run gives the same bits).
+// reductions (no floating-point atomics, so every run gives the same bits).
 //
 //   NT  (t, u):   C[t][j] = sum_k P[t][k] R[j][k]          P [T x K], j < kl <= 64
 //        t = x A^T           R = A_full [kl x K]
@@ -7,119 +7,154 @@
 //   TN  (dA, dB): C[a][j] = sum_t P[t][a] Q[t][j]          P [T x W], Q [T x kl]
 //        dA[j][k] += s C[k][j]              (P = x,  Q = u)
 //        dB[n][i] += s C[n][p(n) r + i]     (P = dy, Q = t)
-// The first kernel of each pair writes float32 partial sums per split of the
-// reduction; the second adds the splits in index order and writes the result.
+//
+// Both are short, bandwidth-bound reductions at a few thousand tokens, so they
+// are split over many workgroups (NT over K, TN over T). Each workgroup writes
+// a float32 partial sum in its registers' order (one contiguous 16-byte store
+// per lane and float4, written through to the device's coherence point); the
+// workgroup that finishes last for a tile (an integer arrival count per tile)
+// reads the tile's partials back in the same order, many loads in flight, adds
+// them in split order and writes the result, so no second kernel runs and the
+// bits do not depend on which workgroup finished last. The arrival counts live
+// in a caller-provided region that must be zero before the first launch; each
+// launch leaves it zero.
 #include "common.h"
 #include "small.h"
 #include "api_util.h"
 
 namespace lsl {
 
-constexpr int SK_LDS = 72;  // LDS row stride (64 + 8 elements)
-
 LSL_DEV f32x4 mfma16s(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-struct NtArgs {
-  const uint16_t* p; int64_t ldp;   // [T x K]
-  const uint16_t* rt;               // R [kl x K], row stride K (A_full, or the masked B transposed)
-  int64_t T, K; int kl;
-  int64_t k_per_split;              // multiple of 256
-  float* part;                      // [S][T][kl] float32 partial sums (S > 1)
-  uint16_t* out; int64_t ldo;       // S == 1: the bf16 result [T x kl]
-};
-
-// Raw buffer loads: bytes past the descriptor's end read as zeros.
+// Raw buffer loads: lanes whose (vector) offset is at or past the end read zeros.
 LSL_DEV __amdgpu_buffer_rsrc_t small_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
 }
 
+// ---------------------------------------------------------------- NT
+struct NtArgs {
+  const uint16_t* p; int64_t ldp;   // [T x K]
+  const uint16_t* rt;               // R [kl x K], row stride K (A_full, or the masked B transposed)
+  int64_t T, K; int kl;
+  int S, steps;                     // K split S ways, `steps` 64-wide steps each
+  float* part;                      // S > 1: one NT_SLOT float32 slot per (64-row tile, split)
+  unsigned* cnt;                    // one arrival count per 64-row tile (S > 1)
+  uint16_t* out; int64_t ldo;       // the bf16 result [T x kl]
+};
+
+// a partial slot: the 64 x 64 float32 tile, lane l of wave w holding row block
+// rb at float4 ((4 w + rb) 64 + l)
+constexpr int NT_SLOT = 64 * 64;
+
 // C[t][j] = sum_k P[t][k] R[j][k] for a 64-row tile and one split of K.
-// grid (ceil(T/64), S), 4 waves; wave w takes the split's 64-wide K-steps
-// w, w + 4, ... for all 64 rows and all kl columns, loading both operands from
-// global memory (L2) straight into MFMA registers (each P element is read once;
-// R is small and shared). The four waves' sums are added in wave order in LDS.
-template <bool DIRECT>
-__global__ __launch_bounds__(256) void lora_nt_kernel(const NtArgs a) {
-  __shared__ f32x4 red[3][4][4][64];
-  // the wave index is uniform in a wave: as a scalar, the K loop and the buffer
-  // loads' offsets stay scalar (no per-lane loop around every load)
+// grid (ceil(T/64), S), 4 waves; wave w takes the split's steps w, w + 4, ...,
+// in halves of 32 k, the next half's 8 loads in flight during the current
+// half's MFMAs (operands straight from L2 into MFMA registers: each P element
+// is read once, R is small and shared). The waves' sums are added in wave order through LDS, wave
+// w then holding the tile's columns 16 w .. 16 w + 15: with one split that is
+// the result, else a partial for the last-arriving workgroup of the tile.
+__global__ __launch_bounds__(256, 2) void lora_nt_kernel(const NtArgs a) {
+  __shared__ f32x4 red[4][4][4][64];  // [wave][j block][row block][lane]
+  // the wave index is uniform in a wave: as a scalar, the buffer loads' offsets stay scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t t0 = (int64_t)blockIdx.x * 64;
-  const int64_t kbeg = (int64_t)blockIdx.y * a.k_per_split;
-  const int64_t kend = kbeg + a.k_per_split < a.K ? kbeg + a.k_per_split : a.K;
-  const __amdgpu_buffer_rsrc_t rp = small_rsrc(a.p, a.T * a.ldp * 2);
-  const __amdgpu_buffer_rsrc_t rr = small_rsrc(a.rt, (int64_t)a.kl * a.K * 2);
-  uint32_t po[4], ro[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    po[i] = (uint32_t)(((t0 + i * 16 + c16) * a.ldp + g * 8) * 2);   // rows >= T read zeros
-    ro[i] = (uint32_t)(((int64_t)(i * 16 + c16) * a.K + g * 8) * 2);  // rows >= kl read zeros
-  }
+  const int KT = (int)(a.K / 64);
+  const int sb = (int)blockIdx.y * a.steps, se = min(KT, sb + a.steps);
   f32x4 acc[4][4];  // [j block][row block]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = kbeg + wave * 64; k0 < kend; k0 += 256) {
+  const __amdgpu_buffer_rsrc_t rp = small_rsrc(a.p, a.T * a.ldp * 2);
+  const __amdgpu_buffer_rsrc_t rr = small_rsrc(a.rt, (int64_t)a.kl * a.K * 2);
+  // rows >= T and R rows >= kl read zeros (the row is in the vector offset, the
+  // step's k in the scalar one)
+  uint32_t pv[4], rv[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint32_t so = (uint32_t)((k0 + ks * 32) * 2);
-      bf16x8 pf[4], rf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rp, po[i], so, 0));
-        rf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rr, ro[i], so, 0));
-      }
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[jb][rb] = mfma16s(rf[jb], pf[rb], acc[jb][rb]);
-    }
+  for (int i = 0; i < 4; ++i) {
+    pv[i] = (uint32_t)(((t0 + i * 16 + c16) * a.ldp + g * 8) * 2);
+    rv[i] = (uint32_t)(((int64_t)(i * 16 + c16) * a.K + g * 8) * 2);
   }
-  if (wave > 0)
+  // half-steps (32 of the step's 64 k): h -> step sb + wave + 4 (h / 2), half h % 2;
+  // the next half's 8 loads are in flight during the current half's MFMAs
+  auto load = [&](int h, bf16x8 (&pf)[4], bf16x8 (&rf)[4]) {
+    const uint32_t so = (uint32_t)(((sb + wave + 4 * (h >> 1)) * 64 + (h & 1) * 32) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rp, pv[i], so, 0));
+      rf[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rr, rv[i], so, 0));
+    }
+  };
+  auto mma = [&](const bf16x8 (&pf)[4], const bf16x8 (&rf)[4]) {
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) red[wave - 1][jb][rb][lane] = acc[jb][rb];
+      for (int rb = 0; rb < 4; ++rb) acc[jb][rb] = mfma16s(rf[jb], pf[rb], acc[jb][rb]);
+  };
+  const int H = sb + wave < se ? 2 * ((se - sb - wave + 3) / 4) : 0;  // even
+  bf16x8 pa[4], ra[4], pb[4], rb_[4];
+  if (H > 0) load(0, pa, ra);
+  for (int h = 0; h < H; h += 2) {
+    load(h + 1, pb, rb_);
+    mma(pa, ra);
+    if (h + 2 < H) load(h + 2, pa, ra);
+    mma(pb, rb_);
+  }
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) red[wave][jb][rb][lane] = acc[jb][rb];
   __syncthreads();
-  if (wave != 0) return;
-  // lane holds C[j = 16 jb + 4 g + i][t = t0 + 16 rb + c16]
+  // wave w, lane: C[j = 16 w + 4 g + i][t = t0 + 16 rb + c16], the waves added in order
+  f32x4 v[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int j = jb * 16 + g * 4;
-    if (j >= a.kl) continue;
+  for (int rb = 0; rb < 4; ++rb) {
+    v[rb] = red[0][wave][rb][lane];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int64_t t = t0 + rb * 16 + c16;
-      f32x4 v = acc[jb][rb];
-#pragma unroll
-      for (int w = 0; w < 3; ++w) {
-        const f32x4 q = red[w][jb][rb][lane];
-        v = f32x4{v[0] + q[0], v[1] + q[1], v[2] + q[2], v[3] + q[3]};
-      }
-      if (t >= a.T) continue;
-      if (DIRECT) *reinterpret_cast<u32x2*>(a.out + t * a.ldo + j) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
-      else *reinterpret_cast<f32x4*>(a.part + ((int64_t)blockIdx.y * a.T + t) * a.kl + j) = v;
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 q = red[w][wave][rb][lane];
+      v[rb] = f32x4{v[rb][0] + q[0], v[rb][1] + q[1], v[rb][2] + q[2], v[rb][3] + q[3]};
     }
   }
-}
-
-// out[t][j] = bf16(sum over splits in order); 4 values per thread
-__global__ void nt_reduce_kernel(const float* __restrict__ part, int S, int64_t T, int kl, uint16_t* __restrict__ out,
-                                 int64_t ldo) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i >= T * kl) return;
-  const int64_t t = i / kl;
-  const int j = (int)(i - t * kl);
-  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
-  for (int k = 1; k < S; ++k) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(part + (int64_t)k * T * kl + i);
-    v = f32x4{v[0] + q[0], v[1] + q[1], v[2] + q[2], v[3] + q[3]};
+  const int j = wave * 16 + g * 4;
+  const bool live = wave * 16 < a.kl;  // (uniform in the wave)
+  if (a.S > 1) {
+    const __amdgpu_buffer_rsrc_t rs = wt_rsrc(a.part, (int64_t)gridDim.x * a.S * NT_SLOT * 4);
+    const uint32_t so = (blockIdx.x * (uint32_t)a.S + blockIdx.y) * NT_SLOT * 4;
+    if (live)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) wt_store4(rs, (uint32_t)((wave * 4 + rb) * 64 + lane) * 16, so, v[rb]);
+    if (!last_arrival(a.cnt + blockIdx.x, a.S)) return;
+    if (!live) return;
+    // the tile's S partials in split order, two splits' loads in flight at a time
+    const uint32_t s0 = blockIdx.x * (uint32_t)a.S * NT_SLOT * 4;
+    for (int sp = 0; sp < a.S; sp += 2) {
+      f32x4 q[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (sp + u < a.S)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            q[u][rb] = wt_load4(rs, (uint32_t)((wave * 4 + rb) * 64 + lane) * 16, s0 + (uint32_t)(sp + u) * NT_SLOT * 4);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (sp + u < a.S)
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            v[rb] = sp + u == 0 ? q[u][rb]
+                                : f32x4{v[rb][0] + q[u][rb][0], v[rb][1] + q[u][rb][1], v[rb][2] + q[u][rb][2],
+                                        v[rb][3] + q[u][rb][3]};
+    }
   }
-  *reinterpret_cast<u32x2*>(out + t * ldo + j) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+  if (!live || j >= a.kl) return;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int64_t t = t0 + rb * 16 + c16;
+    if (t < a.T) *reinterpret_cast<u32x2*>(a.out + t * a.ldo + j) = u32x2{pack2(v[rb][0], v[rb][1]), pack2(v[rb][2], v[rb][3])};
+  }
 }
 
 // Masked transpose of B_full [K x r] for u = dy B: bt[j][k] = B[k][j % r] when
@@ -142,23 +177,43 @@ __global__ void lora_bt_kernel(const uint16_t* __restrict__ b, int r, int kl, in
   *reinterpret_cast<u32x4*>(bt + (int64_t)j * K + k) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// ---------------------------------------------------------------- TN
 struct TnArgs {
   const uint16_t* p; int64_t ldp;  // [T x W]
   const uint16_t* q; int64_t ldq;  // [T x kl]
   int64_t T, W; int kl;
-  int64_t t_per_split;
-  float* part;                     // [S][W][kl] (S > 1)
-  // S == 1: the result goes straight to dA [kl x W] or dB [W x r] (+= scale C)
+  int64_t t_per_split; int S;
+  float* part;                     // S > 1: one TN_SLOT float32 slot per (128-column tile, split)
+  unsigned* cnt;                   // one arrival count per 128-column tile (S > 1)
+  // the result goes to dA [kl x W] or dB [W x r] (+= scale C)
   float* dA; float* dB; float scale; int r; int nseg; SegEnds seg;
 };
+
+// The tiles are stored row-major [64 t][cols] as loaded (one 16-byte store per
+// chunk) and the MFMA operands, whose reduction index t runs down the rows, are
+// read with transposing LDS reads (ld_tr8; both operands in the same permuted
+// t order). Row strides: 144 elements for P (128 columns) and 80 for Q (64),
+// 8 dwords past a multiple of 64 banks, so the 8 rows x 32 bytes of a
+// transposing read's half-wave fall in distinct banks; a 16-lane store covers
+// one P row, or two Q rows 4 apart (32 banks apart).
+constexpr int TN_LDP = 144, TN_LDQ = 80;
+// a partial slot: the workgroup's accumulators, float4 (i, j) of thread tid at
+// ((2 i + j) 256 + tid)
+constexpr int TN_SLOT = 8 * 256 * 4;
+// Q row of load rr (0, 1) of thread tid: rows 0, 4, 1, 5, 2, 6, 3, 7 (+ 8 (tid / 64)) for
+// tid / 8 = 0..7 of each wave, and 32 more for rr = 1
+LSL_DEV int tn_qrow(int tid, int rr) {
+  const int qq = tid >> 3;
+  return 8 * (qq >> 3) + ((qq >> 1) & 3) + 4 * (qq & 1) + 32 * rr;
+}
 
 // grid: (ceil(W/128), S). 4 waves, wave w owns columns a = 32w..32w+31 of the tile.
 // BUF: the split's rows are read through buffer descriptors (its bytes below
 // 4 GiB): no per-load bounds branches.
-template <bool DIRECT, bool BUF>
+template <bool BUF>
 __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[128 * SK_LDS];  // [a][t]
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * SK_LDS];   // [j][t]
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[64 * TN_LDP];  // [t][a]
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * TN_LDQ];  // [t][j]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t a0 = (int64_t)blockIdx.x * 128;
   const int64_t tbeg = (int64_t)blockIdx.y * a.t_per_split;
@@ -167,12 +222,13 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // thread -> P: 4 t-rows x 8 a-cols; Q: 2 t-rows x 8 j-cols. The global loads
-  // run two 64-token steps ahead of the MFMAs, in two register sets. With BUF,
-  // rows past the split's end read zeros (t_per_split is a multiple of 64, so
-  // that happens only past T); columns past W or kl read neighbouring data or
-  // zeros and feed only outputs that are never stored.
-  const int pq = tid >> 4, po = tid & 15, qq = tid >> 3, qo = tid & 7;
+  // thread -> P: rows 4 (tid / 16) + rr (rr < 4), 8 a-columns at 8 (tid % 16);
+  // Q: rows tn_qrow(tid, rr) (rr < 2), 8 j-columns at 8 (tid % 8). The global
+  // loads run two 64-token steps ahead of the MFMAs, in two register sets. With
+  // BUF, rows past the split's end read zeros (t_per_split is a multiple of 64,
+  // so that happens only past T); columns past W or kl read neighbouring data
+  // or zeros and feed only outputs that are never stored.
+  const int pq = tid >> 4, po = tid & 15, qo = tid & 7;
   const int64_t ac = a0 + po * 8;
   // (unused without BUF)
   const __amdgpu_buffer_rsrc_t rsp = small_rsrc(a.p + tbeg * a.ldp, (tend - tbeg) * a.ldp * 2);
@@ -182,7 +238,7 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) pofs[rr] = (uint32_t)(((int64_t)(pq * 4 + rr) * a.ldp + ac) * 2);
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) qofs[rr] = (uint32_t)(((int64_t)(qq * 2 + rr) * a.ldq + qo * 8) * 2);
+    for (int rr = 0; rr < 2; ++rr) qofs[rr] = (uint32_t)(((int64_t)tn_qrow(tid, rr) * a.ldq + qo * 8) * 2);
   }
   auto gload = [&](int64_t tt, u32x4 (&rp)[4], u32x4 (&rq)[2]) {
     if constexpr (BUF) {
@@ -201,7 +257,7 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
       }
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
-        const int64_t t = tt + qq * 2 + rr;
+        const int64_t t = tt + tn_qrow(tid, rr);
         rq[rr] = (t < tend && qo * 8 < a.kl) ? *reinterpret_cast<const u32x4*>(a.q + t * a.ldq + qo * 8)
                                              : u32x4{0, 0, 0, 0};
       }
@@ -213,32 +269,21 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
     // (nothing of this step moves into the previous one, where it would wait for
     // loads that are still in flight)
     __builtin_amdgcn_sched_barrier(0);
-    // both tiles stored transposed ([col][t])
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      uint32_t e[4];
+    for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<u32x4*>(Ps + (pq * 4 + rr) * TN_LDP + po * 8) = rp[rr];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) e[rr] = (cc & 1) ? (rp[rr][cc >> 1] >> 16) : (rp[rr][cc >> 1] & 0xFFFFu);
-      *reinterpret_cast<u32x2*>(Ps + (po * 8 + cc) * SK_LDS + pq * 4) = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-    }
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const uint32_t e0 = (cc & 1) ? (rq[0][cc >> 1] >> 16) : (rq[0][cc >> 1] & 0xFFFFu);
-      const uint32_t e1 = (cc & 1) ? (rq[1][cc >> 1] >> 16) : (rq[1][cc >> 1] & 0xFFFFu);
-      *reinterpret_cast<uint32_t*>(Qs + (qo * 8 + cc) * SK_LDS + qq * 2) = e0 | (e1 << 16);
-    }
+    for (int rr = 0; rr < 2; ++rr) *reinterpret_cast<u32x4*>(Qs + tn_qrow(tid, rr) * TN_LDQ + qo * 8) = rq[rr];
     __syncthreads();
     // unconditional, so that every step has the same loads in flight and each
     // wait covers only the older register set (past the split: zeros, unused)
     gload(tt + 128, rp, rq);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      int kofs = ks * 32 + (lane >> 4) * 8;
+    for (int kk = 0; kk < 2; ++kk) {
       bf16x8 qf[4], pf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qf[i] = *reinterpret_cast<const bf16x8*>(Qs + (i * 16 + (lane & 15)) * SK_LDS + kofs);
+      for (int i = 0; i < 4; ++i) qf[i] = ld_tr8(Qs, TN_LDQ, kk * 32, i * 16, lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) pf[i] = *reinterpret_cast<const bf16x8*>(Ps + (wave * 32 + i * 16 + (lane & 15)) * SK_LDS + kofs);
+      for (int i = 0; i < 2; ++i) pf[i] = ld_tr8(Ps, TN_LDP, kk * 32, wave * 32 + i * 16, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -258,26 +303,52 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
     step(tt + 64, rpb, rqb);
   }
   if (tt < tend) step(tt, rpa, rqa);
-  // lane holds C[a][c..c+3], c = 16 i + 4 (lane >> 4)
-  float* dst = a.part + (int64_t)blockIdx.y * a.W * a.kl;
+  // lane holds C[a][c..c+3], a = a0 + 32 wave + 16 j + lane % 16, c = 16 i + 4 (lane / 16)
+  if (a.S > 1) {
+    const __amdgpu_buffer_rsrc_t rs = wt_rsrc(a.part, (int64_t)gridDim.x * a.S * TN_SLOT * 4);
+    const uint32_t s0 = blockIdx.x * (uint32_t)a.S * TN_SLOT * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        wt_store4(rs, (uint32_t)((2 * i + j) * 256 + tid) * 16, s0 + blockIdx.y * (uint32_t)TN_SLOT * 4, acc[i][j]);
+    if (!last_arrival(a.cnt + blockIdx.x, a.S)) return;
+    // the tile's S partials in split order, two splits' loads in flight at a time
+    for (int sp = 0; sp < a.S; sp += 2) {
+      f32x4 q[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (sp + u < a.S)
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            q[u][c] = wt_load4(rs, (uint32_t)(c * 256 + tid) * 16, s0 + (uint32_t)(sp + u) * TN_SLOT * 4);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (sp + u < a.S)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            f32x4& d = acc[c >> 1][c & 1];
+            d = sp + u == 0 ? q[u][c] : f32x4{d[0] + q[u][c][0], d[1] + q[u][c][1], d[2] + q[u][c][2], d[3] + q[u][c][3]};
+          }
+    }
+  }
+  // the tile's sum, scaled, into dA / dB
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    int64_t ac = a0 + wave * 32 + j * 16 + (lane & 15);
-    if (ac >= a.W) continue;
+    const int64_t aa = a0 + wave * 32 + j * 16 + (lane & 15);
+    if (aa >= a.W) continue;
     int p = 0;
-    if (DIRECT && a.dB)
-      while (p < a.nseg - 1 && ac >= a.seg.e[p]) ++p;
+    if (a.dB)
+      while (p < a.nseg - 1 && aa >= a.seg.e[p]) ++p;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = i * 16 + (lane >> 4) * 4;
       if (c >= a.kl) continue;
-      if (!DIRECT) {
-        *reinterpret_cast<f32x4*>(dst + ac * a.kl + c) = acc[i][j];
-      } else if (a.dA) {
+      if (a.dA) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a.dA[(int64_t)(c + e) * a.W + ac] += a.scale * acc[i][j][e];
+        for (int e = 0; e < 4; ++e) a.dA[(int64_t)(c + e) * a.W + aa] += a.scale * acc[i][j][e];
       } else if (c >= p * a.r && c < (p + 1) * a.r) {
-        f32x4* d = reinterpret_cast<f32x4*>(a.dB + ac * a.r + (c - p * a.r));
+        f32x4* d = reinterpret_cast<f32x4*>(a.dB + aa * a.r + (c - p * a.r));
         f32x4 v = *d;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += a.scale * acc[i][j][e];
@@ -287,70 +358,70 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
   }
 }
 
-// dA[j][k] += s * sum_s part[s][k][j]
-__global__ void tn_reduce_dA_kernel(const float* __restrict__ part, int S, int64_t W, int kl, float scale, float* __restrict__ dA) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= W * kl) return;
-  int j = (int)(i / W); int64_t k = i - (int64_t)j * W;
-  float s = 0.f;
-  for (int q = 0; q < S; ++q) s += part[((int64_t)q * W + k) * kl + j];
-  dA[i] += scale * s;
-}
-
-// dB[n][i] += s * sum_s part[s][n][p(n) r + i]
-__global__ void tn_reduce_dB_kernel(const float* __restrict__ part, int S, int64_t W, int kl, int r, int nseg,
-                                    SegEnds seg, float scale, float* __restrict__ dB) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= W * r) return;
-  int64_t n = idx / r; int i = (int)(idx - n * r);
-  int p = 0;
-  while (p < nseg - 1 && n >= seg.e[p]) ++p;
-  int j = p * r + i;
-  float s = 0.f;
-  for (int q = 0; q < S; ++q) s += part[((int64_t)q * W + n) * kl + j];
-  dB[idx] += scale * s;
+// zero n 32-bit words (the arrival counts, before a call's first split launch)
+__global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------- host side
-// Splits of the reduction so that about `target_blocks` workgroups run, each
-// taking at least `min_steps` 64-wide steps of the reduction.
-static int pick_splits(int64_t tiles, int64_t red, int64_t target_blocks, int64_t min_steps) {
-  if (tiles <= 0) return 1;  // empty output
-  int64_t steps = (red + 63) / 64;
-  int64_t s = (target_blocks + tiles - 1) / tiles;
-  int64_t cap = steps / min_steps;
-  if (s > cap) s = cap;
+// NT: K split so that about NT_TARGET workgroups run (at most NT_MAX_S splits,
+// at least one 64-wide step per wave)
+constexpr int64_t NT_TARGET = 384, NT_MAX_S = 16;
+static void nt_plan(int64_t T, int64_t K, int& S, int& steps) {
+  const int64_t tiles = (T + 63) / 64, KT = K / 64;
+  S = 1;
+  steps = (int)KT;
+  if (tiles <= 0 || KT <= 0) return;
+  int64_t s = (NT_TARGET + tiles - 1) / tiles;
+  if (s > NT_MAX_S) s = NT_MAX_S;
+  if (s > KT / 4) s = KT / 4;
   if (s < 1) s = 1;
-  return (int)s;
+  steps = (int)((KT + s - 1) / s);
+  S = (int)((KT + steps - 1) / steps);
 }
-constexpr int64_t TN_TARGET = 256, TN_MIN_STEPS = 4;
-
-// NT splits: about NT_BLOCKS workgroups of 64 rows, each split at least
-// NT_MIN_K of K (so that each of its four waves takes NT_MIN_K / 256 steps)
-#ifndef LSL_NT_BLOCKS
-#define LSL_NT_BLOCKS 256
-#endif
-#ifndef LSL_NT_MIN_K
-#define LSL_NT_MIN_K 1024
-#endif
 static int nt_splits(int64_t T, int64_t K) {
-  const int64_t tiles = (T + 63) / 64;
-  if (tiles == 0) return 1;  // no tokens
-  int64_t S = (LSL_NT_BLOCKS + tiles - 1) / tiles;
-  if (S > K / LSL_NT_MIN_K) S = K / LSL_NT_MIN_K;
-  return S < 1 ? 1 : (int)S;
+  int S, steps;
+  nt_plan(T, K, S, steps);
+  return S;
 }
 
-// [masked B^T, kl <= 64 rows] + [S][T][kl] partials
-size_t lora_nt_ws_bytes(int64_t T, int64_t K) {
+// TN: splits of T so that about TN_TARGET workgroups run, each taking at least
+// TN_MIN_STEPS 64-token steps
+constexpr int64_t TN_TARGET = 256, TN_MIN_STEPS = 4;
+static int tn_splits(int64_t W, int64_t T) {
+  const int64_t tiles = (W + 127) / 128;
+  const int64_t steps = (T + 63) / 64;
+  if (tiles <= 0 || steps <= 0) return 1;  // empty output or no tokens
+  int64_t s = (TN_TARGET + tiles - 1) / tiles;
+  if (s > steps / TN_MIN_STEPS) s = steps / TN_MIN_STEPS;
+  if (s < 1) s = 1;
+  const int64_t per = (steps + s - 1) / s;
+  return (int)((steps + per - 1) / per);
+}
+
+size_t lora_counts_needed(int64_t T, int64_t W) {
+  const int64_t a = (T + 63) / 64, b = (W + 127) / 128;
+  return (size_t)(a > b ? a : b);
+}
+
+// [masked B^T, kl <= 64 rows] + the partial slots
+size_t lora_nt_ws_bytes(int64_t T, int64_t K, int kl) {
+  (void)kl;
   const int S = nt_splits(T, K);
-  return align256((size_t)64 * K * 2) + (S > 1 ? (size_t)S * T * 64 * sizeof(float) : 0);
+  return align256((size_t)64 * K * 2) + (S > 1 ? (size_t)((T + 63) / 64) * S * NT_SLOT * sizeof(float) : 0);
 }
 
-size_t lora_tn_ws_bytes(int64_t T, int64_t W) {
-  int64_t tiles = (W + 127) / 128;
-  int S = pick_splits(tiles, T, TN_TARGET, TN_MIN_STEPS);
-  return S > 1 ? (size_t)S * W * 64 * sizeof(float) : 0;
+size_t lora_tn_ws_bytes(int64_t T, int64_t W, int kl) {
+  (void)kl;
+  const int S = tn_splits(W, T);
+  return S > 1 ? (size_t)((W + 127) / 128) * S * TN_SLOT * sizeof(float) : 0;
+}
+
+lsl_status lora_counts_zero(unsigned* cnt, size_t n, hipStream_t s) {
+  if (n == 0) return LSL_OK;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cnt, (int)n);
+  return check_launch("lora_counts_zero");
 }
 
 lsl_status lora_nt_check(const LoraNt& d) {
@@ -359,6 +430,7 @@ lsl_status lora_nt_check(const LoraNt& d) {
     return set_error(LSL_ERR_UNSUPPORTED, "lora side product: K %% 64 and kl in [8, 64] multiple of 8 required");
   if ((d.T + 64) * d.ldp * 2 >= ((int64_t)1 << 32))
     return set_error(LSL_ERR_UNSUPPORTED, "lora side product: operand larger than 4 GiB");
+  if (nt_splits(d.T, d.K) > 1 && !d.cnt) return set_error(LSL_ERR_WORKSPACE, "lora side product: no arrival counts");
   return LSL_OK;
 }
 
@@ -366,6 +438,7 @@ lsl_status lora_tn_check(const LoraTn& d) {
   if (d.W == 0) return LSL_OK;
   if (d.kl <= 0 || d.kl > 64 || d.kl % 8 || d.W % 8)
     return set_error(LSL_ERR_UNSUPPORTED, "lora grad: kl in [8, 64] multiple of 8 and W %% 8 required");
+  if (d.T > 0 && tn_splits(d.W, d.T) > 1 && !d.cnt) return set_error(LSL_ERR_WORKSPACE, "lora grad: no arrival counts");
   return LSL_OK;
 }
 
@@ -387,19 +460,9 @@ lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
     a.rt = d.a_full;
   }
   a.part = (float*)(ws + align256((size_t)64 * d.K * 2));
-  const int64_t tiles = (d.T + 63) / 64;
-  int S = nt_splits(d.T, d.K);
-  const int64_t per = (d.K / S + 255) / 256 * 256;
-  S = (int)((d.K + per - 1) / per);
-  a.k_per_split = per;
-  if (S == 1) {
-    hipLaunchKernelGGL(lora_nt_kernel<true>, dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
-    return check_launch("lora_nt");
-  }
-  hipLaunchKernelGGL(lora_nt_kernel<false>, dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
-  const int64_t n4 = d.T * d.kl / 4;
-  hipLaunchKernelGGL(nt_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.part, S,
-                     d.T, d.kl, d.out, d.ldo);
+  a.cnt = d.cnt;
+  nt_plan(d.T, d.K, a.S, a.steps);
+  hipLaunchKernelGGL(lora_nt_kernel, dim3((unsigned)((d.T + 63) / 64), (unsigned)a.S), dim3(256), 0, s, a);
   return check_launch("lora_nt");
 }
 
@@ -407,36 +470,22 @@ lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
   if (d.W == 0) return LSL_OK;
   LSL_TRY(lora_tn_check(d));
   if (d.T == 0) return LSL_OK;
-  int64_t tiles = (d.W + 127) / 128;
-  int S = pick_splits(tiles, d.T, TN_TARGET, TN_MIN_STEPS);
-  int64_t steps = (d.T + 63) / 64;
-  int64_t per = ((steps + S - 1) / S) * 64;
-  S = (int)((d.T + per - 1) / per);
+  const int64_t tiles = (d.W + 127) / 128;
+  const int S = tn_splits(d.W, d.T);
+  const int64_t steps = (d.T + 63) / 64;
+  const int64_t per = ((steps + S - 1) / S) * 64;
   TnArgs a{};
   a.p = d.p; a.ldp = d.ldp; a.q = d.q; a.ldq = d.ldq; a.T = d.T; a.W = d.W; a.kl = d.kl;
-  a.t_per_split = per; a.part = d.ws;
+  a.t_per_split = per; a.S = S; a.part = d.ws; a.cnt = d.cnt;
   a.dA = d.dA; a.dB = d.dA ? nullptr : d.dB; a.scale = d.scale; a.r = d.r; a.nseg = d.nseg;
   for (int i = 0; i < 4; ++i) a.seg.e[i] = d.seg_end[i];
   // buffer descriptors address a split's rows with 32-bit offsets
   const int64_t lim = (int64_t)1 << 32;
   // (the loads run up to two steps past a split's rows)
   const bool buf = (per + 192) * d.ldp * 2 < lim && (per + 192) * d.ldq * 2 < lim;
-  if (S == 1) {
-    if (buf) hipLaunchKernelGGL((lora_tn_kernel<true, true>), dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((lora_tn_kernel<true, false>), dim3((unsigned)tiles, 1), dim3(256), 0, s, a);
-    return check_launch("lora_tn");
-  }
-  if (buf) hipLaunchKernelGGL((lora_tn_kernel<false, true>), dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((lora_tn_kernel<false, false>), dim3((unsigned)tiles, (unsigned)S), dim3(256), 0, s, a);
-  if (d.dA) {
-    int64_t n = d.W * d.kl;
-    hipLaunchKernelGGL(tn_reduce_dA_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float*)d.ws, S, d.W, d.kl, d.scale, d.dA);
-  } else {
-    int64_t n = d.W * d.r;
-    hipLaunchKernelGGL(tn_reduce_dB_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float*)d.ws, S, d.W, d.kl, d.r, d.nseg, a.seg, d.scale, d.dB);
-  }
+  const dim3 grid((unsigned)tiles, (unsigned)S);
+  if (buf) hipLaunchKernelGGL((lora_tn_kernel<true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((lora_tn_kernel<false>), grid, dim3(256), 0, s, a);
   return check_launch("lora_tn");
 }
 

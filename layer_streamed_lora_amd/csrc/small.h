@@ -6,12 +6,15 @@ struct SegEnds { int64_t e[4]; };
 
 // C[t][j] = sum_k p[t][k] R[j][k] -> out bf16 [T x kl]; R = a_full [kl x K], or
 // (b_full != NULL) the projection-masked B_full [K x r].
+// ws: lora_nt_ws_bytes(T, K, kl) bytes; cnt: lora_counts_needed(T, .) arrival
+// counts, zero before the call's first launch (each launch leaves them zero).
 struct LoraNt {
   const uint16_t* p = nullptr; int64_t ldp = 0; int64_t T = 0, K = 0; int kl = 0;
   const uint16_t* a_full = nullptr;
   const uint16_t* b_full = nullptr; int r = 0; int nseg = 1; int64_t seg_end[4] = {0, 0, 0, 0};
   uint16_t* out = nullptr; int64_t ldo = 0;
   float* ws = nullptr;
+  unsigned* cnt = nullptr;
 };
 // C[a][j] = sum_t p[t][a] q[t][j]; dA [kl x W] += s C^T, or dB [W x r] += s C (projection-selected)
 struct LoraTn {
@@ -20,16 +23,24 @@ struct LoraTn {
   float scale = 0.f; float* dA = nullptr; float* dB = nullptr;
   int r = 0; int nseg = 1; int64_t seg_end[4] = {0, 0, 0, 0};
   float* ws = nullptr;
+  unsigned* cnt = nullptr;
 };
-size_t lora_nt_ws_bytes(int64_t T, int64_t K);
-size_t lora_tn_ws_bytes(int64_t T, int64_t W);
+size_t lora_nt_ws_bytes(int64_t T, int64_t K, int kl);
+size_t lora_tn_ws_bytes(int64_t T, int64_t W, int kl);
+// arrival counts a side product of T tokens and output width W (K for NT) may use
+size_t lora_counts_needed(int64_t T, int64_t W);
+// zero n counts (a fill kernel on the stream)
+lsl_status lora_counts_zero(unsigned* cnt, size_t n, hipStream_t s);
 lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s);
 lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s);
 // the conditions the launches reject, checked without launching anything
 lsl_status lora_nt_check(const LoraNt& d);
 lsl_status lora_tn_check(const LoraTn& d);
 
-lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y, hipStream_t s);
+// zero (may be NULL): nzero 32-bit words the launch also sets to 0 (the layer's
+// arrival counts, so that they need no launch of their own)
+lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                              hipStream_t s, unsigned* zero = nullptr, int nzero = 0);
 lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,
                               int64_t T, int64_t H, float eps, uint16_t* dx, hipStream_t s);
 // y = RoPE(x) for n_heads heads of head_dim from column 0 of each row (row

@@ -179,6 +179,12 @@ def noalloc_scratch_bytes():
     return lib().lsl_noalloc_scratch_bytes()
 
 
+def lora_linear_bwd_u(ws, T, W, r):
+    """The u = bf16(dy B) [T x r] that lora_linear_bwd left in its workspace ws."""
+    off = lib().lsl_lora_linear_bwd_u_offset(T, W.n_out, W.k_in)
+    return ws[off:off + T * r * 2].view(torch.bfloat16).view(T, r)
+
+
 def lora_linear_bwd(x, t, dy, W, A, B, scale, dA, dB, need_dx=True, ws=None, stream=None):
     T = x.shape[0]
     r = A.shape[0]

@@ -34,7 +34,7 @@ count of the double-quantized NF4 store (tests/golden/pages_store_sizes.json).
 """
 from .bf16 import round_bf16, identity, bf16_bits, from_bf16_bits  # noqa: F401
 from .nf4 import nf4_codebook, nf4_quantize, nf4_dequant  # noqa: F401
-from .lora import lora_linear_fwd, lora_linear_bwd  # noqa: F401
+from .lora import lora_linear_fwd, lora_linear_bwd, lora_adapter_grads  # noqa: F401
 from .layer import (  # noqa: F401
     rmsnorm_fwd, rmsnorm_bwd, rope_apply, rope_inv_freq, attention_fwd, attention_bwd,
     swiglu_fwd, swiglu_bwd, decoder_layer_fwd, decoder_layer_bwd,

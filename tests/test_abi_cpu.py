@@ -96,6 +96,20 @@ def test_workspace_sizes_are_deterministic(L):
     assert L.lora_linear_workspace_bytes(512, 4096, 4096, 12) == 0
 
 
+def test_linear_workspace_covers_stream_k_and_u(L):
+    """A GEMM with fewer 256 x 256 output tiles than the 256 stream-K
+    workgroups (1024 tokens of a 6144 x 4096 projection: 96 tiles) keeps one
+    float32 tile of partials per slot, 256 + 96 - 1 slots; the backward's u
+    [T x r] region lies inside the workspace, 256-byte aligned."""
+    lib = L.lib()
+    T, n_out, k_in, r = 1024, 6144, 4096, 16
+    ws = L.lora_linear_workspace_bytes(T, n_out, k_in, r)
+    assert ws >= (256 + 96 - 1) * 256 * 256 * 4
+    off = lib.lsl_lora_linear_bwd_u_offset(T, n_out, k_in)
+    assert off % 256 == 0 and 0 < off and off + T * r * 2 <= ws
+    assert lib.lsl_lora_linear_bwd_u_offset(0, n_out, k_in) == 0
+
+
 def test_nf4dq_validation(L):
     from layer_streamed_lora_amd import _abi
     lib = L.lib()

@@ -9,10 +9,13 @@ term scaled down for tensors whose RMS is below 1 (tests/gpu_util.py,
 assert_close_scaled); float32 adapter gradients and the attention statistics
 are held to the same bound or tighter. Two outputs pass two rounding points
 each because the first one is not stored (h1 = bf16(x + bf16(o projection))
-and the layer output likewise); there the oracle rounds at both points too.
+and the layer output likewise); there the oracle rounds at both points too, and
+the bound adds 2e-2 times the first sum's magnitude, the scale of its rounding
+error (where x and the projection cancel, the output is far smaller).
 The Llama-3.1-8B layer runs at seq 512
-and at 1024 tokens, the dispatch the benchmark times (the down projection's
-forward and the gate|up input gradient in split-K large tiles)."""
+and at 1024 tokens, the dispatch the benchmark times (the forward of q|k|v, o
+and the down projection and all four input gradients in stream-K large tiles,
+the gate|up forward one large tile per workgroup)."""
 import dataclasses
 
 import numpy as np
@@ -109,7 +112,7 @@ def _check_steps(shape, batch, seq, wid):
     y_o, t_o = O.lora_linear_fwd(attn, wd["o"], ld["A_o"], ld["B_o"], s)
     assert_close_scaled(g("t_o", rk), t_o, "t_o")
     h1 = g("h1", H)
-    assert_close_scaled(h1, rnd(x + y_o), "h1 = x + o projection")
+    assert_close_scaled(h1, rnd(x + y_o), "h1 = x + o projection", inter=y_o)
     n2 = g("n2", H)
     assert_close_scaled(n2, O.rmsnorm_fwd(h1, wd["norm2"], eps), "n2")
     yg, tg = O.lora_linear_fwd(n2, wd["gate"], ld["A_gate"], ld["B_gate"], s)
@@ -121,7 +124,7 @@ def _check_steps(shape, batch, seq, wid):
     assert_close_scaled(act, O.swiglu_fwd(gu[:, :I], gu[:, I:]), "swiglu")
     y_d, t_d = O.lora_linear_fwd(act, wd["down"], ld["A_down"], ld["B_down"], s)
     assert_close_scaled(g("t_down", rk), t_d, "t_down")
-    assert_close_scaled(r["out"], rnd(h1 + y_d), "layer output = h1 + down projection")
+    assert_close_scaled(r["out"], rnd(h1 + y_d), "layer output = h1 + down projection", inter=y_d)
 
     # ---- backward (and the float32 adapter gradients of each projection)
     grads = r["grads"]

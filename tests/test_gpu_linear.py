@@ -105,11 +105,15 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1024, 24576, 64, 8, "bf16"),
     (1, 64, 98304, 8, "nf4"),
     (1, 98304, 64, 8, "bf16"),
-    # fewer large tiles but a long reduction: the large tile with split-K (forward
-    # here; the input gradient of the same linear has 224 tiles, unsplit)
+    # fewer than 192 large tiles but at least 20 x 256 K-steps in all: stream-K
+    # over 256 workgroups, split tiles summed by the last arrival (the forward
+    # here; the input gradient has 192 tiles or more, one per workgroup)
     (1024, 14336, 2048, 16, "nf4"),
-    (1000, 2048, 14336, 8, "bf16"),   # input gradient split, ragged tokens
     (1100, 12288, 2048, 16, "nf4dq"),
+    (1000, 2048, 14336, 8, "bf16"),   # the input gradient in stream-K, ragged tokens
+    (1024, 12288, 2112, 16, "nf4"),   # ragged weight rows (last tile 64 of 256), 27 steps per workgroup
+    (512, 16384, 4096, 16, "bf16"),   # 32 steps per workgroup: forward tiles split exactly 8 ways;
+                                      # input gradient two whole tiles per workgroup, nothing split
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
@@ -121,16 +125,22 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
         W = gpu.FrozenWeight.dense(dev_bf16(w))
     xd, ad, bd, dyd = (v.astype(np.float64) for v in (x, a, b, dy))
     y_ref, t_ref = O.lora_linear_fwd(xd, wd, ad, bd, s)
-    dx_ref, da_ref, db_ref, _ = O.lora_linear_bwd(xd, t_ref, dyd, wd, ad, bd, s)
+    dx_ref, _, _, u_ref = O.lora_linear_bwd(xd, t_ref, dyd, wd, ad, bd, s)
     X, A, B, DY = dev_bf16(x), dev_bf16(a), dev_bf16(b), dev_bf16(dy)
     y, t = gpu.lora_linear_fwd(X, W, A, B, s)
     dA = torch.zeros((r, fin), dtype=torch.float32, device="cuda")
     dB = torch.zeros((fout, r), dtype=torch.float32, device="cuda")
-    dx = gpu.lora_linear_bwd(X, t, DY, W, A, B, s, dA, dB)
+    ws = torch.empty(gpu.lora_linear_workspace_bytes(T, fout, fin, r), dtype=torch.uint8, device="cuda")
+    dx = gpu.lora_linear_bwd(X, t, DY, W, A, B, s, dA, dB, ws=ws)
+    u = gpu.lora_linear_bwd_u(ws, T, W, r).clone()
     torch.cuda.synchronize()
     assert_close(host(t), t_ref, "t")
+    assert_close(host(u), u_ref, "u")
     assert_close(host(y), y_ref, "y")
     assert_close(host(dx), dx_ref, "dx")
+    # the adapter gradients from the GPU's own bf16 t and u (a one-ulp rounding
+    # difference in one of them moves a whole row of dA or dB)
+    da_ref, db_ref = O.lora_adapter_grads(xd, host(t), dyd, host(u), s)
     assert_close(host(dA), da_ref, "dA")
     assert_close(host(dB), db_ref, "dB")
     # gradients accumulate (+=) in a fixed order: a second call doubles them exactly
@@ -141,10 +151,44 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
 
 
 @pytest.mark.parametrize("T,fin,fout,r,fmt", [
+    (1024, 12288, 2112, 16, "nf4"),   # stream-K forward, split side products
+    (300, 16384, 4096, 16, "bf16"),   # ragged tokens, stream-K both ways
+])
+def test_split_partials_do_not_leak_between_calls(gpu, T, fin, fout, r, fmt):
+    """Two calls with different inputs on one workspace: the second call's
+    split partials land where the first call's still sit, and its results match
+    the oracle for its own inputs (a partial read from the first call would
+    not)."""
+    ws_f = torch.empty(gpu.lora_linear_workspace_bytes(T, fout, fin, r), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty_like(ws_f)
+    for wid in (5, 6):
+        x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, wid, fmt)
+        wd = oracle_weight(w, fmt)
+        W = gpu.FrozenWeight.nf4(dev_bf16(w)) if fmt == "nf4" else gpu.FrozenWeight.dense(dev_bf16(w))
+        xd, ad, bd, dyd = (v.astype(np.float64) for v in (x, a, b, dy))
+        X, A, B, DY = dev_bf16(x), dev_bf16(a), dev_bf16(b), dev_bf16(dy)
+        y, t = gpu.lora_linear_fwd(X, W, A, B, s, ws=ws_f)
+        dA = torch.zeros((r, fin), dtype=torch.float32, device="cuda")
+        dB = torch.zeros((fout, r), dtype=torch.float32, device="cuda")
+        dx = gpu.lora_linear_bwd(X, t, DY, W, A, B, s, dA, dB, ws=ws_b)
+        u = gpu.lora_linear_bwd_u(ws_b, T, W, r).clone()
+        torch.cuda.synchronize()
+        y_ref, t_ref = O.lora_linear_fwd(xd, wd, ad, bd, s)
+        dx_ref, _, _, u_ref = O.lora_linear_bwd(xd, t_ref, dyd, wd, ad, bd, s)
+        assert_close(host(t), t_ref, f"t, call {wid}")
+        assert_close(host(y), y_ref, f"y, call {wid}")
+        assert_close(host(u), u_ref, f"u, call {wid}")
+        assert_close(host(dx), dx_ref, f"dx, call {wid}")
+        da_ref, db_ref = O.lora_adapter_grads(xd, host(t), dyd, host(u), s)
+        assert_close(host(dA), da_ref, f"dA, call {wid}")
+        assert_close(host(dB), db_ref, f"dB, call {wid}")
+
+
+@pytest.mark.parametrize("T,fin,fout,r,fmt", [
     (200, 320, 448, 16, "bf16"),      # ragged, unsplit GEMM
     (64, 4096, 512, 16, "nf4"),       # few output tiles: split-K path, bias added in the split reduce
     (1100, 256, 24576, 16, "nf4"),    # 256 x 256 tiles
-    (1024, 14336, 2048, 16, "nf4"),   # 256 x 256 tiles with split-K, bias added in the split reduce
+    (1024, 14336, 2048, 16, "nf4"),   # stream-K: the bias added by the last arrival
 ])
 def test_lora_linear_bias(gpu, T, fin, fout, r, fmt):
     """A frozen bias joins the forward sum before its single rounding; the
