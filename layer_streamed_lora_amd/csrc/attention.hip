@@ -24,6 +24,15 @@ namespace lsl {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// Block -> work item: the hardware deals consecutive blocks to the 8 XCDs in
+// turn; XCD x gets the items [x n / 8, (x + 1) n / 8) (rounded), so that the
+// blocks of one (sequence, kv head), which read the same K and V tiles, share
+// an XCD's L2 instead of every XCD caching every head.
+LSL_DEV int xcd_item(int b, int n) {
+  const int per = n >> 3, rem = n & 7, x = b & 7, i = b >> 3;
+  return x * per + min(x, rem) + i;
+}
+
 struct AttnArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
   int64_t ldq, ldk;
@@ -91,6 +100,49 @@ struct TileStage {
   }
 };
 
+// The same 64-row tile stage through a buffer descriptor over the sequence's
+// rows: the per-thread offsets are set up once and a tile adds one scalar row
+// offset; rows at or past the end read zeros (they meet only masked scores or
+// zero probabilities).
+template <int D, int NT>
+struct BufTileStage {
+  static constexpr int CHUNKS = 64 * D / 8;
+  static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff[CPT];
+  u32x4 v[CPT];
+  // src: row 0 of the sequence (head column offset included), rows rows of stride ld
+  LSL_DEV void init(const uint16_t* src, int64_t ld, int rows, int tid) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0,
+                                           (int)(uint32_t)((int64_t)rows * ld * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      voff[i] = (uint32_t)((row * ld + col) * 2);
+    }
+  }
+  // rows r0 .. r0 + 63; r0 ld 2 is added to the vector offset, which the range
+  // check covers
+  LSL_DEV void load(int64_t ld, int r0, int tid) {
+    const uint32_t o = (uint32_t)(r0 * ld * 2);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (CHUNKS % NT == 0 || tid + i * NT < CHUNKS)
+        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + o, 0, 0));
+  }
+  LSL_DEV void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(dst + row * (D + 8) + col) = v[i];
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------- forward
 // grid (ceil(seq / (16 NQS)), n_kv, batch), block group*64 threads; wave = query
 // head, 16 NQS queries per wave.
@@ -100,8 +152,11 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (latest) query tiles first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  // item (b n_kv + kvh) n_qt + n_qt - 1 - qt: heaviest (latest) query tiles first
+  const int n_qt = (a.seq + QT - 1) / QT;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int bk = item / n_qt, qt = n_qt - 1 - (item - bk * n_qt);
+  const int kvh = bk % a.n_kv, b = bk / a.n_kv;
   const int h = kvh * a.group + wave;
   const int q0 = qt * QT;
   const int64_t rowbase = (int64_t)b * a.seq;
@@ -128,17 +183,19 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
 
   const int qmax = min(q0 + QT - 1, a.seq - 1);
   const int ntiles = qmax / 64 + 1;
-  TileStage<D, 64 * NW> kst, vst;
-  kst.load(kp, a.ldk, 0, a.seq, tid);
-  vst.load(vp, a.ldk, 0, a.seq, tid);
+  BufTileStage<D, 64 * NW> kst, vst;
+  kst.init(kp, a.ldk, a.seq, tid);
+  vst.init(vp, a.ldk, a.seq, tid);
+  kst.load(a.ldk, 0, tid);
+  vst.load(a.ldk, 0, tid);
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * 64;
     kst.store(Ks, tid);
     vst.store(Vs, tid);
     __syncthreads();
     if (j + 1 < ntiles) {
-      kst.load(kp, a.ldk, kv0 + 64, a.seq, tid);
-      vst.load(vp, a.ldk, kv0 + 64, a.seq, tid);
+      kst.load(a.ldk, kv0 + 64, tid);
+      vst.load(a.ldk, kv0 + 64, tid);
     }
     // S^T: lane holds kv = kv0 + kvs*16 + 4g + i, q = q0 + qs*16 + c16
     f32x4 sc[4][NQS];
@@ -153,39 +210,51 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
         for (int qs = 0; qs < NQS; ++qs) sc[kvs][qs] = mfma(kf, qf[qs][ks], sc[kvs][qs]);
       }
     }
+    // only the tiles that reach the diagonal (or the sequence's end) are masked:
+    // below it every key kv <= kv0 + 63 < q0 <= q is visible and inside the sequence
+    const bool diag = kv0 + 63 > q0;
     bf16x8 pf[NQS][2], pl[NQS][2];
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       const int q = q0 + qs * 16 + c16;
-      float mt = -INFINITY;
+      if (diag) {
 #pragma unroll
-      for (int kvs = 0; kvs < 4; ++kvs)
+        for (int kvs = 0; kvs < 4; ++kvs)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kv = kv0 + kvs * 16 + g * 4 + i;
-          const float x = (kv <= q && kv < a.seq) ? sc[kvs][qs][i] * a.scale_log2 : -INFINITY;
-          sc[kvs][qs][i] = x;
-          mt = fmaxf(mt, x);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int kv = kv0 + kvs * 16 + g * 4 + i;
+            if (!(kv <= q && kv < a.seq)) sc[kvs][qs][i] = -INFINITY;
+          }
+      }
+      // the row maximum of the raw scores, scaled once (scaling by a positive
+      // constant commutes with the maximum)
+      float mt = fmaxf(fmaxf(sc[0][qs][0], sc[0][qs][1]), fmaxf(sc[0][qs][2], sc[0][qs][3]));
+#pragma unroll
+      for (int kvs = 1; kvs < 4; ++kvs)
+        mt = fmaxf(mt, fmaxf(fmaxf(sc[kvs][qs][0], sc[kvs][qs][1]), fmaxf(sc[kvs][qs][2], sc[kvs][qs][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m[qs], mt);  // finite: key 0 is visible to every query
-      const float alpha = exp2_ftz(m[qs] - mn);
-      m[qs] = mn;
+      const float mn = fmaxf(m[qs], mt * a.scale_log2);  // finite: key 0 is visible to every query
       float ls = 0.f;
 #pragma unroll
       for (int kvs = 0; kvs < 4; ++kvs)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = exp2_ftz(sc[kvs][qs][i] - mn);
+          const float pv = exp2_ftz(fmaf(sc[kvs][qs][i], a.scale_log2, -mn));
           sc[kvs][qs][i] = pv;
           ls += pv;
         }
-      l[qs] = l[qs] * alpha + ls;
+      // the running sums rescale only where some lane's maximum moved (exp2(0) = 1)
+      if (__builtin_amdgcn_ballot_w64(mn != m[qs])) {
+        const float alpha = exp2_ftz(m[qs] - mn);
+        l[qs] *= alpha;
 #pragma unroll
-      for (int ds = 0; ds < D / 16; ++ds)
+        for (int ds = 0; ds < D / 16; ++ds)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[ds][qs][i] *= alpha;
+          for (int i = 0; i < 4; ++i) o[ds][qs][i] *= alpha;
+      }
+      m[qs] = mn;
+      l[qs] += ls;
       split8(sc[0][qs], sc[1][qs], pf[qs][0], pl[qs][0]);
       split8(sc[2][qs], sc[3][qs], pf[qs][1], pl[qs][1]);
     }
@@ -274,8 +343,12 @@ __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
   __shared__ float lse_s[4][DKV_QT], dsum_s[4][DKV_QT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int HG = blockDim.x >> 7, hg = wave >> 1, ws = wave & 1, htid = tid & 127;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const int kv0 = blockIdx.x * 32;  // heaviest (earliest) key tiles are dispatched first
+  // item (b n_kv + kvh) n_kt + kt: heaviest (earliest) key tiles first
+  const int n_kt = (a.seq + 31) / 32;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int bk = item / n_kt;
+  const int kv0 = (item - bk * n_kt) * 32;
+  const int kvh = bk % a.n_kv, b = bk / a.n_kv;
   const int64_t rowbase = (int64_t)b * a.seq;
   const int g = lane >> 4, c16 = lane & 15;
   const int mykv = kv0 + ws * 16 + c16;
@@ -339,6 +412,10 @@ __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
     __syncthreads();
     if (it + 1 < iters) fetch(it + 1);
     if (act) {
+      // only query tiles that reach the diagonal or the sequence's end are
+      // masked: elsewhere every query q >= q0 >= kv0 + 31 sees every key of the
+      // tile and is inside the sequence
+      const bool diag = q0 < kv0 + 31 || q0 + DKV_QT > a.seq;
       // S[q][kv], dP[q][kv] for 64 queries: lane holds q = qs*16 + 4g + i, kv = mykv
       f32x4 p[4], ds[4];
 #pragma unroll
@@ -353,8 +430,9 @@ __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int ql = qs * 16 + g * 4 + i;
           const int q = q0 + ql;
-          const bool keep = mykv <= q && q < a.seq && mykv < a.seq;
-          const float pv = exp2_ftz(keep ? sv[i] * a.scale_log2 - lse_s[hg][ql] : -INFINITY);
+          float x = fmaf(sv[i], a.scale_log2, -lse_s[hg][ql]);
+          if (diag && !(mykv <= q && q < a.seq && mykv < a.seq)) x = -INFINITY;
+          const float pv = exp2_ftz(x);
           p[qs][i] = pv;
           ds[qs][i] = pv * (dp[i] - dsum_s[hg][ql]);
         }
@@ -422,8 +500,10 @@ __global__ __launch_bounds__(64 * NW) void attn_dq_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = gridDim.x - 1 - blockIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int n_qt = (a.seq + QT - 1) / QT;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int bk = item / n_qt, qt = n_qt - 1 - (item - bk * n_qt);
+  const int kvh = bk % a.n_kv, b = bk / a.n_kv;
   const int h = kvh * a.group + wave;
   const int q0 = qt * QT;
   const int64_t rowbase = (int64_t)b * a.seq;
@@ -484,6 +564,9 @@ __global__ __launch_bounds__(64 * NW) void attn_dq_kernel(const AttnArgs a) {
         }
       }
     }
+    // only key tiles that reach the diagonal (or query rows past the sequence's
+    // end) are masked: below it every key kv <= kv0 + 63 < q0 <= q is visible
+    const bool diag = kv0 + 63 > q0 || q0 + QT > a.seq;
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       const int q = q0 + qs * 16 + c16;
@@ -492,8 +575,9 @@ __global__ __launch_bounds__(64 * NW) void attn_dq_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int kv = kv0 + kvs * 16 + g * 4 + i;
-          const bool keep = kv <= q && kv < a.seq && q < a.seq;
-          const float pv = exp2_ftz(keep ? sc[kvs][qs][i] * a.scale_log2 - lse2[qs] : -INFINITY);
+          float x = fmaf(sc[kvs][qs][i], a.scale_log2, -lse2[qs]);
+          if (diag && !(kv <= q && kv < a.seq && q < a.seq)) x = -INFINITY;
+          const float pv = exp2_ftz(x);
           sc[kvs][qs][i] = pv * (dp[kvs][qs][i] - dsm[qs]);
         }
       split8(sc[0][qs], sc[1][qs], dsf[qs][0], dsl[qs][0]);
@@ -564,6 +648,9 @@ static lsl_status attn_check(const char* fn, int64_t ldq, int64_t ldk, int batch
     return set_error(LSL_ERR_INVALID_ARG, "%s: bad head counts (n_q %% n_kv must be 0)", fn);
   if (d != 64 && d != 128) return set_error(LSL_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, d);
   if (n_q / n_kv > 8) return set_error(LSL_ERR_UNSUPPORTED, "%s: more than 8 query heads per kv head", fn);
+  // one-dimensional grids of (query or key tiles) x kv heads x sequences
+  if ((int64_t)((seq + 15) / 16) * n_kv * batch >= ((int64_t)1 << 31))
+    return set_error(LSL_ERR_UNSUPPORTED, "%s: too many tiles for one grid", fn);
   if (ldq < (int64_t)n_q * d || ldk < (int64_t)n_kv * d || ldq % 8 || ldk % 8)
     return set_error(LSL_ERR_INVALID_ARG, "%s: leading dimensions too small or not multiples of 8", fn);
   return LSL_OK;
@@ -572,7 +659,7 @@ static lsl_status attn_check(const char* fn, int64_t ldq, int64_t ldk, int batch
 lsl_status attention_fwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
   AttnArgs a = a0;
   if ((int64_t)a.batch * a.seq == 0) return LSL_OK;
-  dim3 grid((unsigned)((a.seq + ATT_QT - 1) / ATT_QT), (unsigned)a.n_kv, (unsigned)a.batch);
+  dim3 grid((unsigned)(((a.seq + ATT_QT - 1) / ATT_QT) * a.n_kv * a.batch));
   dim3 block((unsigned)(64 * a.group));
   if (d == 128) launch_by_group<FwdKernel, 128>(a.group, grid, block, s, a);
   else launch_by_group<FwdKernel, 64>(a.group, grid, block, s, a);
@@ -587,11 +674,11 @@ lsl_status attention_bwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
   if (d == 128) hipLaunchKernelGGL(attn_dsum_kernel<128>, gs, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_dsum_kernel<64>, gs, dim3(256), 0, s, a);
   a.dsum = a.dsum_out;
-  dim3 gk((unsigned)((a.seq + 31) / 32), (unsigned)a.n_kv, (unsigned)a.batch);
+  dim3 gk((unsigned)(((a.seq + 31) / 32) * a.n_kv * a.batch));
   dim3 bk((unsigned)(128 * std::min(a.group, 4)));
   if (d == 128) hipLaunchKernelGGL(attn_dkv_kernel<128>, gk, bk, 0, s, a);
   else hipLaunchKernelGGL(attn_dkv_kernel<64>, gk, bk, 0, s, a);
-  dim3 gq((unsigned)((a.seq + ATT_QT - 1) / ATT_QT), (unsigned)a.n_kv, (unsigned)a.batch);
+  dim3 gq((unsigned)(((a.seq + ATT_QT - 1) / ATT_QT) * a.n_kv * a.batch));
   if (d == 128) launch_by_group<DqKernel, 128>(a.group, gq, dim3(64 * a.group), s, a);
   else launch_by_group<DqKernel, 64>(a.group, gq, dim3(64 * a.group), s, a);
   return check_launch("attention_bwd");
