@@ -432,7 +432,7 @@ def hbm_kernels(shape, ms):
         ("lsl::rmsnorm_bwd_kernel", 4 * T * H * 2 + 2 * H, "x, dy, residual gradient read, dx written"),
         ("lsl::swiglu_fwd_kernel", 3 * T * I * 2, "gate|up read, a written"),
         ("lsl::swiglu_bwd_kernel", 5 * T * I * 2, "gate|up and da read, dgate|dup written"),
-        ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2 // 2, "q or k heads read and written in place (mean of the two)"),
+        ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2 // 2, "q or k heads read, rotated copy written (mean of the two)"),
         ("lsl::adamw_kernel", n_params * (4 * 4 + 3 * 4 + 2), "master, grad, m, v read; master, m, v, bf16 copy written"),
     ]
 
@@ -660,11 +660,15 @@ def summarize_ce_bytes(fetch_dir, write_dir, args):
 
 def summarize_pmc(dirs, args):
     """Per-kernel averages of the hardware counters of one or more `rocprofv3
-    --pmc` runs (one row per kernel name, values per dispatch) and the derived
-    MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and
-    LDS bank-conflict share (SQ_LDS_BANK_CONFLICT over SQ_ACTIVE_INST_LDS).
-    Kernels are told apart by name and grid size. rocprofv3 sums each counter
-    over its dimensions, so GRBM_GUI_ACTIVE (one clock count per XCD) is
+    --pmc` runs of this library's kernels (one row per kernel name and grid,
+    values per dispatch), with derived ratios where their counters are present:
+    MFMA utilisation (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs),
+    the share of that time with VALU work issued beside it
+    (SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES), VALU instructions
+    per MFMA instruction, the LDS bank-conflict share (SQ_LDS_BANK_CONFLICT over
+    SQ_ACTIVE_INST_LDS) and the wave-state shares (waiting on a counter,
+    waiting to issue, issuing; over SQ_WAVE_CYCLES). rocprofv3 sums each
+    counter over its dimensions, so GRBM_GUI_ACTIVE (one clock count per XCD) is
     divided by the XCD count before it is used as the dispatch's duration."""
     import collections
     simds = 4 * args.cus
@@ -672,6 +676,8 @@ def summarize_pmc(dirs, args):
     names = []
     for d in dirs:
         for r in _rows(_find(d, "*counter_collection.csv")):
+            if "lsl::" not in r["Kernel_Name"]:
+                continue  # torch's and the runtime's own kernels
             k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("lsl::", "") + f" grid {_grid_items(r)}"
             v = float(r["Counter_Value"])
             if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
@@ -679,23 +685,32 @@ def summarize_pmc(dirs, args):
             per[k][r["Counter_Name"]].append(v)
             if r["Counter_Name"] not in names:
                 names.append(r["Counter_Name"])
-    cols = [n for n in names]
-    out = ["| kernel | dispatches | " + " | ".join(cols) + " | MFMA util | LDS conflict / LDS active |",
-           "|---|---:|" + "---:|" * len(cols) + "---:|---:|"]
+
+    def ratio(avg, num, den, scale=1.0):
+        return avg[num] / (avg[den] * scale) if avg.get(num) is not None and avg.get(den) else None
+    derived = [("MFMA util", lambda a: ratio(a, "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", simds)),
+               ("VALU beside MFMA", lambda a: ratio(a, "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES")),
+               ("VALU / MFMA instr", lambda a: ratio(a, "SQ_INSTS_VALU", "SQ_INSTS_MFMA")),
+               ("LDS conflict / LDS active", lambda a: ratio(a, "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS")),
+               ("waiting", lambda a: ratio(a, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+               ("waiting to issue", lambda a: ratio(a, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+               ("issuing", lambda a: ratio(a, "SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"))]
     rows = []
     for k, c in per.items():
         n = max(len(v) for v in c.values())
-        avg = {cn: (sum(c[cn]) / len(c[cn]) if c.get(cn) else None) for cn in cols}
-        util = (avg.get("SQ_VALU_MFMA_BUSY_CYCLES") / (avg["GRBM_GUI_ACTIVE"] * simds)
-                if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None and avg.get("GRBM_GUI_ACTIVE") else None)
-        confl = (avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_ACTIVE_INST_LDS"]
-                 if avg.get("SQ_LDS_BANK_CONFLICT") is not None and avg.get("SQ_ACTIVE_INST_LDS") else None)
-        rows.append((-(avg.get("GRBM_GUI_ACTIVE") or 0) * n, k, n, avg, util, confl))
+        avg = {cn: (sum(c[cn]) / len(c[cn]) if c.get(cn) else None) for cn in names}
+        dv = [(dn, f(avg)) for dn, f in derived]
+        key = avg.get("GRBM_GUI_ACTIVE") or avg.get("SQ_WAVE_CYCLES") or 0
+        rows.append((-key * n, k, n, avg, dv))
     rows.sort()
-    for _, k, n, avg, util, confl in rows[:args.top]:
-        vals = " | ".join("" if avg[cn] is None else f"{avg[cn]:.4g}" for cn in cols)
-        out.append(f"| `{k[:110]}` | {n} | {vals} | {'' if util is None else f'{util:.3f}'} | "
-                   f"{'' if confl is None else f'{confl:.3f}'} |")
+    shown = [dn for dn, _ in derived if any(v is not None for _, _, _, _, dv in rows for d2, v in dv if d2 == dn)]
+    out = ["| kernel | dispatches | " + " | ".join(names + shown) + " |",
+           "|---|---:|" + "---:|" * (len(names) + len(shown))]
+    for _, k, n, avg, dv in rows[:args.top]:
+        vals = ["" if avg[cn] is None else f"{avg[cn]:.4g}" for cn in names]
+        dd = dict(dv)
+        vals += ["" if dd[dn] is None else f"{dd[dn]:.3f}" for dn in shown]
+        out.append(f"| `{k[:110]}` | {n} | " + " | ".join(vals) + " |")
     print("\n".join(out))
 
 

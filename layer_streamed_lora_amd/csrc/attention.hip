@@ -131,13 +131,14 @@ struct BufTileStage {
       if (CHUNKS % NT == 0 || tid + i * NT < CHUNKS)
         v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + o, 0, 0));
   }
+  template <int LDD>
   LSL_DEV void store(uint16_t* dst, int tid) const {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + i * NT;
       if (CHUNKS % NT == 0 || c < CHUNKS) {
         const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(dst + row * (D + 8) + col) = v[i];
+        *reinterpret_cast<u32x4*>(dst + row * LDD + col) = v[i];
       }
     }
   }
@@ -148,9 +149,12 @@ struct BufTileStage {
 // head, 16 NQS queries per wave.
 template <int D, int NQS, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
-  constexpr int QT = 16 * NQS, LD = D + 8;
+  // K rows are read 16 at a time in 16-byte chunks (a 16-byte skew per row
+  // spreads 16 rows over all banks); V is read with transposing reads of 8
+  // rows x 32 bytes per half-wave (a 32-byte skew per row spreads those)
+  constexpr int QT = 16 * NQS, LD = D + 8, LDV = D + 16;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LDV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // item (b n_kv + kvh) n_qt + n_qt - 1 - qt: heaviest (latest) query tiles first
   const int n_qt = (a.seq + QT - 1) / QT;
@@ -190,8 +194,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
   vst.load(a.ldk, 0, tid);
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * 64;
-    kst.store(Ks, tid);
-    vst.store(Vs, tid);
+    kst.template store<LD>(Ks, tid);
+    vst.template store<LDV>(Vs, tid);
     __syncthreads();
     if (j + 1 < ntiles) {
       kst.load(a.ldk, kv0 + 64, tid);
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
     for (int ds = 0; ds < D / 16; ++ds) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 vf = ld_tr8(Vs, LD, kk * 32, ds * 16, lane);
+        const bf16x8 vf = ld_tr8(Vs, LDV, kk * 32, ds * 16, lane);
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs) {
           o[ds][qs] = mfma(vf, pf[qs][kk], o[ds][qs]);
