@@ -18,6 +18,9 @@ pytestmark = pytest.mark.gpu
     (1, 512, 32, 8, 128),   # one Llama-3.1-8B layer at seq 512
     (3, 1, 4, 2, 64),       # one token per sequence
     (1, 2048, 8, 2, 128),   # a long sequence: 32 key tiles in the backward
+    (1, 1024, 32, 8, 128),  # the benchmark's layer at 1024 tokens
+    (2, 700, 4, 2, 64),     # ragged, two sequences
+    (1, 577, 3, 1, 128),    # group of 3, a partly filled last key tile
 ])
 def test_attention_parity(gpu, batch, seq, nq, nkv, d):
     T = batch * seq
@@ -53,3 +56,19 @@ def test_attention_strided_views(gpu):
     o_ref, _ = O.attention_fwd(qd[:, : nq * d].reshape(T, nq, d), qd[:, nq * d:(nq + nkv) * d].reshape(T, nkv, d),
                                qd[:, (nq + nkv) * d:].reshape(T, nkv, d), batch, seq)
     assert_close(host(o), o_ref.reshape(T, -1), "attn o (strided)")
+
+
+def test_attention_forward_is_deterministic(gpu):
+    """Repeated forward calls give identical bits (output, its float32 copy and
+    the log-sum-exp)."""
+    batch, seq, nq, nkv, d = 1, 1024, 8, 2, 128
+    T = batch * seq
+    g = torch.Generator(device="cuda").manual_seed(7)
+    Q = torch.randn(T, nq * d, device="cuda", generator=g).to(torch.bfloat16)
+    K = torch.randn(T, nkv * d, device="cuda", generator=g).to(torch.bfloat16)
+    V = torch.randn(T, nkv * d, device="cuda", generator=g).to(torch.bfloat16)
+    o0, lse0, o320 = gpu.attention_fwd(Q, K, V, batch, seq, nq, nkv, d, want_o32=True)
+    for _ in range(3):
+        o1, lse1, o321 = gpu.attention_fwd(Q, K, V, batch, seq, nq, nkv, d, want_o32=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(lse0, lse1) and torch.equal(o320, o321)
