@@ -129,18 +129,19 @@ __global__ __launch_bounds__(256, 2) void lora_nt_kernel(const NtArgs a) {
       for (int rb = 0; rb < 4; ++rb) wt_store4(rs, (uint32_t)((wave * 4 + rb) * 64 + lane) * 16, so, v[rb]);
     if (!last_arrival(a.cnt + blockIdx.x, a.S)) return;
     if (!live) return;
-    // the tile's S partials in split order, two splits' loads in flight at a time
+    // the tile's S partials in split order, eight splits' loads in flight at a
+    // time (the loop's registers are free by now)
     const uint32_t s0 = blockIdx.x * (uint32_t)a.S * NT_SLOT * 4;
-    for (int sp = 0; sp < a.S; sp += 2) {
-      f32x4 q[2][4];
+    for (int sp = 0; sp < a.S; sp += 8) {
+      f32x4 q[8][4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 8; ++u)
         if (sp + u < a.S)
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
             q[u][rb] = wt_load4(rs, (uint32_t)((wave * 4 + rb) * 64 + lane) * 16, s0 + (uint32_t)(sp + u) * NT_SLOT * 4);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 8; ++u)
         if (sp + u < a.S)
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
