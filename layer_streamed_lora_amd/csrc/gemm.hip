@@ -1220,23 +1220,32 @@ LSL_DEV void slot_store(__amdgpu_buffer_rsrc_t rs, int slot, const f32x16 (&acc)
 
 // The last arrival's sum of a split tile: the partials in slots s0 .. s0 + nseg - 1,
 // added in that order, then the bf16 epilogue; one half of the tile (column
-// blocks 2 h, 2 h + 1) at a time, 16 loads in flight per slot.
+// blocks 2 h, 2 h + 1) at a time, two slots' 32 loads in flight per lane (the
+// segment loop's registers are free by now).
 LSL_DEV void sk_fixup(const GemmKArgs& a, __amdgpu_buffer_rsrc_t rs, int s0, int nseg, int64_t m0, int64_t n0,
                       int tid) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     f32x16 sum[2][2];
-    for (int v = 0; v < nseg; ++v) {
-      const uint32_t so = (uint32_t)(s0 + v) * SLOT * 4;
-      f32x4 p[16];
+    for (int v = 0; v < nseg; v += 2) {
+      f32x4 p[2][16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) p[c] = wt_load4(rs, (uint32_t)((h * 16 + c) * NT + tid) * 16, so);
+      for (int u = 0; u < 2; ++u)
+        if (v + u < nseg) {
+          const uint32_t so = (uint32_t)(s0 + v + u) * SLOT * 4;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const int i = c >> 3, j = (c >> 2) & 1, q = c & 3;
+          for (int c = 0; c < 16; ++c) p[u][c] = wt_load4(rs, (uint32_t)((h * 16 + c) * NT + tid) * 16, so);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sum[i][j][4 * q + e] = v == 0 ? p[c][e] : sum[i][j][4 * q + e] + p[c][e];
-      }
+      for (int u = 0; u < 2; ++u)
+        if (v + u < nseg)
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const int i = c >> 3, j = (c >> 2) & 1, q = c & 3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sum[i][j][4 * q + e] = v + u == 0 ? p[u][c][e] : sum[i][j][4 * q + e] + p[u][c][e];
+          }
     }
     store_tile_bf16<2>(a, sum, 2 * h, m0, n0, tid, nullptr);
   }
