@@ -22,13 +22,15 @@
  *    packed unless a leading dimension is given. Device pointers to bf16 data
  *    must be 16-byte aligned, float/int32 vectors (labels, lse, loss) 4-byte
  *    aligned (INVALID_ARG otherwise; there is no slower fallback path).
- *  - Kernel selection (tile shapes, splits, chunking) depends only on the shapes
- *    passed, never on pointer values, residency or the stream, so a streamed and
- *    a resident run execute identical arithmetic and produce identical bits.
- *    No result is reduced with floating-point atomics.
- *  - The caller owns every buffer. The library keeps no device state; a pool
- *    object owns only its HIP events (the optional GEMM timing below is the one
- *    piece of process-global state).
+ *  - Kernel selection (tile shapes, splits, stream-K schedule, chunking) depends
+ *    only on the shapes passed, never on pointer values, residency, the stream or
+ *    the device, so a streamed and a resident run execute identical arithmetic
+ *    and produce identical bits. No result is reduced with floating-point
+ *    atomics: split partials are added in a fixed order, by a second kernel or
+ *    by the workgroup that arrives last on a per-tile count (integer atomics).
+ *  - The caller owns every buffer. The library keeps no device state beyond the
+ *    allocation-free forward's scratch array; a pool object owns only its HIP
+ *    events; the optional GEMM timing below is per calling thread.
  */
 #ifndef LSL_H
 #define LSL_H
@@ -339,8 +341,9 @@ lsl_status lsl_pool_stats_read(lsl_pool* pool, int32_t* loads, double* bytes, do
 /* ------------------------------------------------------------------ timing
  * Optional measurement of one GEMM of the decoder layer for roofline reports:
  * while enabled, decoder_layer_fwd/bwd record HIP events on their stream
- * around each launch of the selected GEMM (at most max_launches). This is the
- * only process-global state of the library; it is off by default.
+ * around each launch of the selected GEMM (at most max_launches). The switch
+ * and its events belong to the calling thread (layer calls made on other
+ * threads neither see nor touch them); it is off by default.
  * which: 1..4 forward GEMM of group LSL_M_QKV..LSL_M_DOWN (+1),
  *        5..8 input-gradient GEMM of the same groups. */
 lsl_status lsl_timing_enable(int32_t which, int32_t max_launches);

@@ -657,6 +657,9 @@ static lsl_status attn_check(const char* fn, int64_t ldq, int64_t ldk, int batch
     return set_error(LSL_ERR_UNSUPPORTED, "%s: too many tiles for one grid", fn);
   if (ldq < (int64_t)n_q * d || ldk < (int64_t)n_kv * d || ldq % 8 || ldk % 8)
     return set_error(LSL_ERR_INVALID_ARG, "%s: leading dimensions too small or not multiples of 8", fn);
+  // the forward reads a sequence's K and V rows through 32-bit buffer offsets
+  if ((int64_t)seq * ldk * 2 >= ((int64_t)1 << 32))
+    return set_error(LSL_ERR_UNSUPPORTED, "%s: one sequence's K or V rows exceed 4 GiB", fn);
   return LSL_OK;
 }
 

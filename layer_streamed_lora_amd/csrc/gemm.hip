@@ -1307,6 +1307,8 @@ __global__ __launch_bounds__(big::NT, 1) void gemm_sk_kernel(const GemmKArgs a) 
     // workgroups f .. l share tile t; their partials sit in slots f + t .. l + t
     slot_store(rs, w + t, acc, tid);
     const int f = sk_owner(t * KTall, U, G), l = sk_owner(t * KTall + KTall - 1, U, G);
+    // (nfix < 2 always: the host launches stream-K only with fewer tiles than
+    // workgroups, and a workgroup's units then span at most two tiles)
     if (last_arrival(a.cnt + t, l - f + 1) && nfix < 2) {
       fix_t[nfix] = t; fix_f[nfix] = f; fix_n[nfix] = l - f + 1;
       ++nfix;
@@ -1526,6 +1528,9 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s,
   a.sk_g = 0;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
   if (plan == -1) {
+    // at most two segments per workgroup (the kernel keeps two pending sums)
+    if ((int64_t)a.tiles_m * a.tiles_n >= LSL_SK_G)
+      return set_error(LSL_ERR_UNSUPPORTED, "gemm: stream-K needs fewer tiles than workgroups");
     a.sk_g = LSL_SK_G;
     a.spart = d.split_ws;
     a.cnt = d.cnt;
