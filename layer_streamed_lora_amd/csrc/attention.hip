@@ -1,9 +1,9 @@
 // Causal grouped-query attention on gfx950 bf16 MFMA (16x16x32), head_dim 64 or 128.
 //
 // Forward (one pass, online softmax): a workgroup holds one (sequence, kv head,
-// 32-query tile); its G waves are the G query heads of that kv head, so the K/V
-// tiles staged in LDS are shared by the whole group and all waves see the same
-// causal range. Scores are computed transposed (S^T = K Q^T) so that each lane
+// 16-query tile); its waves are the G query heads of that kv head (two per head
+// at head_dim 128, each on half of every key tile), so the K/V tiles staged in
+// LDS are shared by the whole group and all waves see the same causal range. Scores are computed transposed (S^T = K Q^T) so that each lane
 // owns one query column: the running max/sum of the online softmax need one
 // value per lane, and the probabilities feed the P V product straight from
 // registers (the reduction index of an MFMA may be permuted freely as long as
@@ -297,6 +297,289 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(const AttnArgs a) {
             f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
     }
     if (g == 0) a.lse_out[((int64_t)b * a.n_q + h) * a.seq + q] = (m[qs] + log2f(lt)) * LN2;
+  }
+}
+
+// ---------------------------------------------------------------- forward, head_dim 128
+// The same work split, with the K and V tiles moved global -> LDS by buffer loads
+// that write LDS directly (no registers, no LDS store instructions), in two
+// stages, and one barrier per 64-key tile. Rows are unpadded (256 bytes); the
+// 16-byte chunk c of row r sits at position c ^ kv_sw(r). kv_sw is linear over
+// the bits of r mod 16 (images 8, 4, 3, 6 of bits 0-3); with it both the row-wise
+// K reads (16 rows, chunks ks*4 + g) and the transposing V reads (4 rows x two
+// chunks per 16 lanes) ran with no LDS bank-conflict cycles on gfx950
+// (SQ_LDS_BANK_CONFLICT), where rows padded by 16 bytes, the identity or a
+// (r mod 8) << 1 swizzle left conflicts in one of the two.
+LSL_DEV int kv_sw(int r) { return ((r & 1) ? 8 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 3 : 0) ^ ((r & 8) ? 6 : 0); }
+
+typedef __attribute__((address_space(3))) void att_lds_void;
+
+// one 64 x 128 tile = 16 loads of 4 rows (64 lanes x 16 bytes each); wave w
+// issues loads w, w + NW, ... of K and of V. Lane l of load i fills position
+// l % 16 of row 4 i + l / 16, i.e. global chunk (l % 16) ^ kv_sw(row).
+template <int NW>
+struct KvDma {
+  static constexpr int PER = (16 + NW - 1) / NW;
+  uint32_t voff[PER];
+  int wave;
+  LSL_DEV void init(int64_t ld, int w, int lane) {
+    wave = w;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int r = 4 * (w + i * NW) + (lane >> 4);
+      voff[i] = (uint32_t)(((int64_t)r * ld + (((lane & 15) ^ kv_sw(r)) * 8)) * 2);
+    }
+  }
+  // tile rows r0 .. r0 + 63: r0 ld 2 goes into the vector offset, which the
+  // descriptor's range check covers (rows at or past the end read zeros)
+  LSL_DEV void issue(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, uint32_t r0off, uint16_t* ks,
+                     uint16_t* vs) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ins = wave + i * NW;
+      if (ins < 16) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (att_lds_void*)(ks + ins * 512), 16, voff[i] + r0off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (att_lds_void*)(vs + ins * 512), 16, voff[i] + r0off, 0, 0, 0);
+      }
+    }
+#else
+    (void)rk; (void)rv; (void)r0off; (void)ks; (void)vs;
+#endif
+  }
+};
+
+// V^T operand from the swizzled V tile (as ld_tr8: lane l, g = l / 16, gets
+// column c0 + l % 16 at rows r0 + 4 g + s and r0 + 16 + 4 g + s, s < 4)
+LSL_DEV bf16x8 ld_tr8_sw(const uint16_t* tile, int r0, int c0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int r = r0 + 4 * g + (j >> 2);
+  const int chunk = (c0 >> 3) + ((j & 3) >> 1);
+  const uint16_t* p = tile + r * 128 + ((chunk ^ kv_sw(r)) << 3) + 4 * (j & 1);
+  const u32x2 x = ld_tr4(p), y = ld_tr4(p + 16 * 128);  // kv_sw(r + 16) = kv_sw(r)
+  return __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], y[0], y[1]});
+}
+
+// the causal mask of a diagonal tile: score kb*16 + 4g + i of the lane (from the
+// wave's first key) is visible when that offset is at most lim (the lane's last
+// visible key, its query or the sequence's last key, minus the wave's first key
+// and 4g)
+template <int KB>
+LSL_DEV void mask_tile(f32x4 (&sc)[KB], int lim) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (kb * 16 + i > lim) sc[kb][i] = -INFINITY;
+}
+// maximum / sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four row groups of
+// a 16 x 16 block) by two cross-row swaps
+LSL_DEV float max_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+LSL_DEV float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The running maximum is moved (and O, l rescaled) only when a tile's maximum
+// exceeds it by more than 2^RESCALE_LOG2 in probability: until then the
+// probabilities are taken against the old maximum and stay below 2^8, far from
+// float32 or bf16 overflow; the log-sum-exp m + log2(l) is the same either way.
+constexpr float RESCALE_LOG2 = 8.f;
+
+// grid (ceil(seq / 16), n_kv, batch) as one dimension, block NW KH waves: wave
+// w = kh NW + hw is query head hw of the kv head for keys kv0 + 64 kh / KH ..
+// of each 64-key tile (KH = 2: each wave takes half of every tile, and the two
+// halves' (max, sum, output) are merged at the end in a fixed order).
+template <int NW, int KH>
+__global__ __launch_bounds__(64 * NW * KH) void attn_fwd_dma_kernel(const AttnArgs a) {
+  constexpr int D = 128, QT = 16, NWT = NW * KH, KB = 4 / KH;  // 16-key blocks per wave and tile
+  // two stages as separate arrays: the stage being read and the one being
+  // filled are distinct objects, so reads of one need not wait for the other's loads
+  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[64 * D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wave % NW, kh = wave / NW;
+  // item (b n_kv + kvh) n_qt + n_qt - 1 - qt: heaviest (latest) query tiles first
+  const int n_qt = (a.seq + QT - 1) / QT;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int bk = item / n_qt, qt = n_qt - 1 - (item - bk * n_qt);
+  const int kvh = bk % a.n_kv, b = bk / a.n_kv;
+  const int h = kvh * a.group + hw;
+  const int q0 = qt * QT;
+  const int64_t rowbase = (int64_t)b * a.seq;
+  const uint16_t* qp = a.q + rowbase * a.ldq + (int64_t)h * D;
+  const uint16_t* kp = a.k + rowbase * a.ldk + (int64_t)kvh * D;
+  const uint16_t* vp = a.v + rowbase * a.ldk + (int64_t)kvh * D;
+  const int g = lane >> 4, c16 = lane & 15;
+
+  const int qmax = min(q0 + QT - 1, a.seq - 1);
+  const int ntiles = qmax / 64 + 1;
+  const uint32_t seqbytes = (uint32_t)((int64_t)a.seq * a.ldk * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), (short)0, (int)seqbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), (short)0, (int)seqbytes, 0x00020000);
+  KvDma<NWT> dma;
+  dma.init(a.ldk, wave, lane);
+  dma.issue(rk, rv, 0, K0, V0);
+
+  bf16x8 qf[D / 32];
+  {
+    const int64_t q = min(q0 + c16, a.seq - 1);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[ks] = ld8(qp + q * a.ldq + ks * 32 + g * 8);
+  }
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // running maximum (scaled by log2 e / sqrt d) and the lane's partial sum
+  const int q = q0 + c16;
+  const int qlast = min(q, a.seq - 1);  // the lane's last visible key
+
+  // one 64-key tile from stage (K, V) while the next tile's loads fill (Kn, Vn)
+  auto tile = [&](const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* Kn, uint16_t* Vn,
+                  int j) {
+    const int kv0 = j * 64, kb0 = kv0 + kh * 16 * KB;  // the wave's first key
+    // this wave's loads of tile j (and the queries) are done; after the barrier
+    // every wave's are, and every wave has finished reading (Kn, Vn)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + 1 < ntiles) dma.issue(rk, rv, (uint32_t)((int64_t)(kv0 + 64) * a.ldk * 2), Kn, Vn);
+    if (kb0 > qmax) return;  // no key of this wave's part is visible to the tile's queries
+    // S^T: lane holds kv = kb0 + kb*16 + 4g + i, q = q0 + c16
+    f32x4 sc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = kh * 16 * KB + kb * 16 + c16;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const bf16x8 kf = ld8(K + row * D + (((ks * 4 + g) ^ kv_sw(row)) << 3));
+        sc[kb] = mfma(kf, qf[ks], sc[kb]);
+      }
+    }
+    // only the parts that reach the diagonal (or the sequence's end) are masked
+    if (kb0 + 16 * KB - 1 > q0) mask_tile<KB>(sc, qlast - kb0 - 4 * g);
+    float mt = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb) mt = fmaxf(mt, fmaxf(fmaxf(sc[kb][0], sc[kb][1]), fmaxf(sc[kb][2], sc[kb][3])));
+    mt = max_rows4(mt) * a.scale_log2;  // -inf where the lane's query sees none of these keys
+    if (__builtin_amdgcn_ballot_w64(mt > m + RESCALE_LOG2)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = mn == -INFINITY ? 1.f : exp2_ftz(m - mn);  // exp2(-inf) = 0 from a first maximum
+      l *= alpha;
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[ds][i] *= alpha;
+      m = mn;
+    }
+    // a lane that has seen no visible key has only -inf scores: 2^-inf = 0
+    const float mref = m == -INFINITY ? 0.f : m;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = exp2_ftz(fmaf(sc[kb][i], a.scale_log2, -mref));
+        sc[kb][i] = pv;
+        ls += pv;
+      }
+    l += ls;
+    bf16x8 pf[KB / 2], pl[KB / 2];
+#pragma unroll
+    for (int kk = 0; kk < KB / 2; ++kk) split8(sc[2 * kk], sc[2 * kk + 1], pf[kk], pl[kk]);
+    // O^T += V^T P^T over the wave's keys (the permuted order of pf), with P as a
+    // hi + lo pair of bf16 values: O then carries about 16 significant bits of P,
+    // so the backward's rowsum(dO O) is accurate where dP - rowsum cancels
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+      for (int kk = 0; kk < KB / 2; ++kk) {
+        const bf16x8 vf = ld_tr8_sw(V, kh * 16 * KB + kk * 32, ds * 16, lane);
+        o[ds] = mfma(vf, pf[kk], o[ds]);
+        o[ds] = mfma(vf, pl[kk], o[ds]);
+      }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(K0, V0, K1, V1, j);
+    if (j + 1 < ntiles) tile(K1, V1, K0, V0, j + 1);
+  }
+  if constexpr (KH == 2) {
+    // the second half's (max, partial sums, output) through LDS, in register
+    // order (K0 / K1 hold the outputs of heads 0-1 / 2-3 of each group of four)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(NW <= 8, "attn_fwd_dma_kernel: 8 query heads per kv head at most");
+    float* red = reinterpret_cast<float*>((hw & 2) ? K1 : K0) + (hw & 1) * (D / 16) * 4 * 64;
+    float* redml = reinterpret_cast<float*>(V0) + hw * 128;
+    if (hw < 4) {
+      if (kh == 1) {
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[(ds * 4 + i) * 64 + lane] = o[ds][i];
+        redml[lane] = m;
+        redml[64 + lane] = l;
+      }
+    }
+    __syncthreads();
+    if (hw < 4 && kh == 0) {
+      const float m1 = redml[lane], l1 = redml[64 + lane];
+      const float mn = fmaxf(m, m1);  // finite: key 0 is in the first half of tile 0
+      const float a0 = exp2_ftz(m - mn), a1 = m1 == -INFINITY ? 0.f : exp2_ftz(m1 - mn);
+      l = l * a0 + l1 * a1;
+#pragma unroll
+      for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[ds][i] = o[ds][i] * a0 + red[(ds * 4 + i) * 64 + lane] * a1;
+      m = mn;
+    }
+    if constexpr (NW > 4) {
+      // heads 4..7: a second round through the same buffers
+      __syncthreads();
+      if (hw >= 4 && kh == 1) {
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[(ds * 4 + i) * 64 + lane] = o[ds][i];
+        redml[lane] = m;
+        redml[64 + lane] = l;
+      }
+      __syncthreads();
+      if (hw >= 4 && kh == 0) {
+        const float m1 = redml[lane], l1 = redml[64 + lane];
+        const float mn = fmaxf(m, m1);
+        const float a0 = exp2_ftz(m - mn), a1 = m1 == -INFINITY ? 0.f : exp2_ftz(m1 - mn);
+        l = l * a0 + l1 * a1;
+#pragma unroll
+        for (int ds = 0; ds < D / 16; ++ds)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[ds][i] = o[ds][i] * a0 + red[(ds * 4 + i) * 64 + lane] * a1;
+        m = mn;
+      }
+    }
+    if (kh == 1) return;
+  }
+  const float lt = sum_rows4(l);
+  if (q < a.seq) {
+    const float inv = 1.0f / lt;
+    uint16_t* op = a.out + (rowbase + q) * a.ldo + (int64_t)h * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const f32x4& r = o[ds];
+      *reinterpret_cast<u32x2*>(op + ds * 16 + g * 4) = u32x2{pack2(r[0] * inv, r[1] * inv), pack2(r[2] * inv, r[3] * inv)};
+      if (a.o32)
+        *reinterpret_cast<f32x4*>(a.o32 + (rowbase + q) * ((int64_t)a.n_q * D) + (int64_t)h * D + ds * 16 + g * 4) =
+            f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+    }
+    if (g == 0) a.lse_out[((int64_t)b * a.n_q + h) * a.seq + q] = (m + log2f(lt)) * LN2;
   }
 }
 
@@ -624,7 +907,10 @@ constexpr int ATT_QT = LSL_ATT_QT;  // queries per wave in the forward and dQ ke
 
 struct FwdKernel {
   template <int D, int NW> static void launch(dim3 g, dim3 b, hipStream_t s, const AttnArgs& a) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, ATT_QT / 16, NW>), g, b, 0, s, a);
+    if constexpr (D == 128 && ATT_QT == 16)
+      hipLaunchKernelGGL((attn_fwd_dma_kernel<NW, 2>), g, dim3(b.x * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<D, ATT_QT / 16, NW>), g, b, 0, s, a);
   }
 };
 struct DqKernel {

@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
     (1, 1024, 32, 8, 128),  # the benchmark's layer at 1024 tokens
     (2, 700, 4, 2, 64),     # ragged, two sequences
     (1, 577, 3, 1, 128),    # group of 3, a partly filled last key tile
+    (1, 300, 7, 1, 128),    # group of 7 at head_dim 128
+    (2, 129, 2, 2, 128),    # one query head per kv head, two sequences, a one-row last key tile
+    (1, 33, 2, 1, 128),     # group of 2, a single partial tile
 ])
 def test_attention_parity(gpu, batch, seq, nq, nkv, d):
     T = batch * seq
@@ -43,9 +46,10 @@ def test_attention_parity(gpu, batch, seq, nq, nkv, d):
     assert_close(host(dv), dv_ref.reshape(T, -1), "attn dv")
 
 
-def test_attention_strided_views(gpu):
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_strided_views(gpu, d):
     """q, k, v as column slices of one fused qkv row (the layout the layer uses)."""
-    batch, seq, nq, nkv, d = 1, 80, 4, 2, 64
+    batch, seq, nq, nkv = 1, 80, 4, 2
     T, W = batch * seq, (nq + 2 * nkv) * d
     qkv = synth.activation((T, W), 31, "x")
     X = dev_bf16(qkv)
