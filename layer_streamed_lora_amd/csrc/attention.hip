@@ -624,7 +624,11 @@ __global__ void attn_dsum_kernel(const AttnArgs a) {
 constexpr int DKV_QT = 64;
 template <int D>
 __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
-  constexpr int LD = D + 8;
+  // head_dim 128: unpadded rows with the forward's chunk swizzle (conflict-free
+  // for the row-wise and the transposing reads); 64: rows padded by 16 bytes
+  constexpr bool SW = D == 128;
+  constexpr int LD = SW ? D : D + 8;
+  auto at = [](int row, int col) { return SW ? row * LD + (((col >> 3) ^ kv_sw(row)) << 3) + (col & 7) : row * LD + col; };
   constexpr int CH = DKV_QT * D / 8 / 128;  // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 2 * DKV_QT * LD];
   __shared__ float lse_s[4][DKV_QT], dsum_s[4][DKV_QT];
@@ -689,8 +693,8 @@ __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Qs + row * LD + col) = pq[c];
-      *reinterpret_cast<u32x4*>(Os + row * LD + col) = po[c];
+      *reinterpret_cast<u32x4*>(Qs + at(row, col)) = pq[c];
+      *reinterpret_cast<u32x4*>(Os + at(row, col)) = po[c];
     }
     if (htid < DKV_QT) {
       lse_s[hg][htid] = plse * LOG2E;
@@ -710,8 +714,9 @@ __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
         f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          sv = mfma(ld8(Qs + (qs * 16 + c16) * LD + ks * 32 + g * 8), kf[ks], sv);
-          dp = mfma(ld8(Os + (qs * 16 + c16) * LD + ks * 32 + g * 8), vf[ks], dp);
+          const int off = at(qs * 16 + c16, ks * 32 + g * 8);
+          sv = mfma(ld8(Qs + off), kf[ks], sv);
+          dp = mfma(ld8(Os + off), vf[ks], dp);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -734,8 +739,14 @@ __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
         split8(ds[2 * kk], ds[2 * kk + 1], sb, sl);
 #pragma unroll
         for (int dd = 0; dd < D / 16; ++dd) {
-          const bf16x8 oa = ld_tr8(Os, LD, kk * 32, dd * 16, lane);
-          const bf16x8 qa = ld_tr8(Qs, LD, kk * 32, dd * 16, lane);
+          bf16x8 oa, qa;
+          if constexpr (SW) {
+            oa = ld_tr8_sw(Os, kk * 32, dd * 16, lane);
+            qa = ld_tr8_sw(Qs, kk * 32, dd * 16, lane);
+          } else {
+            oa = ld_tr8(Os, LD, kk * 32, dd * 16, lane);
+            qa = ld_tr8(Qs, LD, kk * 32, dd * 16, lane);
+          }
           dv[dd] = mfma(oa, pb, dv[dd]);
           dv[dd] = mfma(oa, pl, dv[dd]);
           dk[dd] = mfma(qa, sb, dk[dd]);
@@ -899,6 +910,132 @@ __global__ __launch_bounds__(64 * NW) void attn_dq_kernel(const AttnArgs a) {
   }
 }
 
+// dQ at head_dim 128 with the forward's staging: K/V tiles by LDS-writing buffer
+// loads (two stages, the conflict-free chunk swizzle), two waves per query head,
+// each on half of every 64-key tile; the halves' dQ partials are added in order
+// at the end.
+template <int NW>
+__global__ __launch_bounds__(128 * NW) void attn_dq_dma_kernel(const AttnArgs a) {
+  constexpr int D = 128, QT = 16, KH = 2, NWT = NW * KH, KB = 4 / KH;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[64 * D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wave % NW, kh = wave / NW;
+  const int n_qt = (a.seq + QT - 1) / QT;
+  const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
+  const int bk = item / n_qt, qt = n_qt - 1 - (item - bk * n_qt);
+  const int kvh = bk % a.n_kv, b = bk / a.n_kv;
+  const int h = kvh * a.group + hw;
+  const int q0 = qt * QT;
+  const int64_t rowbase = (int64_t)b * a.seq;
+  const int g = lane >> 4, c16 = lane & 15;
+  const uint16_t* qp = a.q + rowbase * a.ldq + (int64_t)h * D;
+  const uint16_t* dop = a.dout + rowbase * a.ldo + (int64_t)h * D;
+  const uint16_t* kp = a.k + rowbase * a.ldk + (int64_t)kvh * D;
+  const uint16_t* vp = a.v + rowbase * a.ldk + (int64_t)kvh * D;
+
+  const int qmax = min(q0 + QT - 1, a.seq - 1);
+  const int ntiles = qmax / 64 + 1;
+  const uint32_t seqbytes = (uint32_t)((int64_t)a.seq * a.ldk * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp), (short)0, (int)seqbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp), (short)0, (int)seqbytes, 0x00020000);
+  KvDma<NWT> dma;
+  dma.init(a.ldk, wave, lane);
+  dma.issue(rk, rv, 0, K0, V0);
+
+  const int q = q0 + c16;
+  const int qc = min(q, a.seq - 1);
+  bf16x8 qf[D / 32], of[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    qf[ks] = ld8(qp + (int64_t)qc * a.ldq + ks * 32 + g * 8);
+    of[ks] = ld8(dop + (int64_t)qc * a.ldo + ks * 32 + g * 8);
+  }
+  const float lse2 = a.lse[((int64_t)b * a.n_q + h) * a.seq + qc] * LOG2E;
+  const float dsm = a.dsum[((int64_t)b * a.n_q + h) * a.seq + qc];
+  f32x4 dq[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) dq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the lane's last visible key; query rows past the sequence see none
+  const int qlast = q < a.seq ? q : -1;
+
+  auto tile = [&](const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* Kn, uint16_t* Vn,
+                  int j) {
+    const int kv0 = j * 64, kb0 = kv0 + kh * 16 * KB;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + 1 < ntiles) dma.issue(rk, rv, (uint32_t)((int64_t)(kv0 + 64) * a.ldk * 2), Kn, Vn);
+    if (kb0 > qmax) return;
+    // S^T and dP^T: lane holds kv = kb0 + kb*16 + 4g + i, q = q0 + c16
+    f32x4 sc[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      sc[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = kh * 16 * KB + kb * 16 + c16;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const int off = row * D + (((ks * 4 + g) ^ kv_sw(row)) << 3);
+        sc[kb] = mfma(ld8(K + off), qf[ks], sc[kb]);
+        dp[kb] = mfma(ld8(V + off), of[ks], dp[kb]);
+      }
+    }
+    if (kb0 + 16 * KB - 1 > q0 || q0 + QT > a.seq) mask_tile<KB>(sc, qlast - kb0 - 4 * g);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = exp2_ftz(fmaf(sc[kb][i], a.scale_log2, -lse2));
+        sc[kb][i] = pv * (dp[kb][i] - dsm);
+      }
+    bf16x8 dsf[KB / 2], dsl[KB / 2];
+#pragma unroll
+    for (int kk = 0; kk < KB / 2; ++kk) split8(sc[2 * kk], sc[2 * kk + 1], dsf[kk], dsl[kk]);
+    // dQ^T += K^T dS^T over the wave's keys (permuted like the forward's P V)
+#pragma unroll
+    for (int dd = 0; dd < D / 16; ++dd)
+#pragma unroll
+      for (int kk = 0; kk < KB / 2; ++kk) {
+        const bf16x8 ka = ld_tr8_sw(K, kh * 16 * KB + kk * 32, dd * 16, lane);
+        dq[dd] = mfma(ka, dsf[kk], dq[dd]);
+        dq[dd] = mfma(ka, dsl[kk], dq[dd]);
+      }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(K0, V0, K1, V1, j);
+    if (j + 1 < ntiles) tile(K1, V1, K0, V0, j + 1);
+  }
+  // the second half's partial through LDS in register order, added to the first's
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(NW <= 8, "attn_dq_dma_kernel: 8 query heads per kv head at most");
+#pragma unroll
+  for (int round = 0; round < (NW + 3) / 4; ++round) {
+    const bool mine = hw / 4 == round;
+    float* red = reinterpret_cast<float*>((hw & 2) ? K1 : K0) + (hw & 1) * (D / 16) * 4 * 64;
+    if (mine && kh == 1)
+#pragma unroll
+      for (int dd = 0; dd < D / 16; ++dd)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[(dd * 4 + i) * 64 + lane] = dq[dd][i];
+    __syncthreads();
+    if (mine && kh == 0)
+#pragma unroll
+      for (int dd = 0; dd < D / 16; ++dd)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dq[dd][i] += red[(dd * 4 + i) * 64 + lane];
+    __syncthreads();
+  }
+  if (kh == 1 || q >= a.seq) return;
+  uint16_t* dqp = a.out + (rowbase + q) * a.ldq + (int64_t)h * D;
+#pragma unroll
+  for (int dd = 0; dd < D / 16; ++dd) {
+    const f32x4& r = dq[dd];
+    *reinterpret_cast<u32x2*>(dqp + dd * 16 + g * 4) =
+        u32x2{pack2(r[0] * a.scale, r[1] * a.scale), pack2(r[2] * a.scale, r[3] * a.scale)};
+  }
+}
+
 // ---------------------------------------------------------------- host
 #ifndef LSL_ATT_QT
 #define LSL_ATT_QT 16
@@ -915,7 +1052,10 @@ struct FwdKernel {
 };
 struct DqKernel {
   template <int D, int NW> static void launch(dim3 g, dim3 b, hipStream_t s, const AttnArgs& a) {
-    hipLaunchKernelGGL((attn_dq_kernel<D, ATT_QT / 16, NW>), g, b, 0, s, a);
+    if constexpr (D == 128 && ATT_QT == 16)
+      hipLaunchKernelGGL((attn_dq_dma_kernel<NW>), g, dim3(b.x * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_dq_kernel<D, ATT_QT / 16, NW>), g, b, 0, s, a);
   }
 };
 // one instantiation per group size (1..8 query heads per kv head, checked by attn_check)
