@@ -412,7 +412,11 @@ size_t lsl_attention_workspace_bytes(int32_t batch, int32_t seq, int32_t n_q, in
                                      int32_t head_dim);
 /* Gradients of sum(dout * o): o, dout [T x ldo]; dq [T x ldq] like q; dk, dv
  * [T x ldk] like k (dk, dv summed over the heads of each group). o32 (may be
- * NULL) is the forward's float output; without it rowsum(dout * o) uses o. */
+ * NULL) is the forward's float output; without it rowsum(dout * o) uses o.
+ * ws: lsl_attention_workspace_bytes() bytes of device scratch (any contents; the
+ * call initialises what it needs): the row sums and, when the key tiles are few,
+ * the float32 partials of key tiles whose dK/dV work is split over workgroups
+ * (added in a fixed order, so the result does not depend on timing). */
 lsl_status lsl_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* o, const uint16_t* dout, const float* lse,
                              const float* o32, int64_t ldq, int64_t ldk, int64_t ldo, int32_t batch,

@@ -45,6 +45,9 @@ struct AttnArgs {
   int batch, seq, n_q, n_kv, group;
   float scale_log2;                          // log2(e) / sqrt(d)
   float scale;                               // 1 / sqrt(d)
+  // balanced dK/dV (dkv_balanced): float32 partial slots and one arrival count
+  // per (sequence, kv head, key tile), zeroed by the dsum kernel
+  float* dkv_part; unsigned* dkv_cnt;
 };
 
 LSL_DEV f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -587,6 +590,12 @@ __global__ __launch_bounds__(64 * NW * KH) void attn_fwd_dma_kernel(const AttnAr
 // D[b][h][q] = sum_d dO[q][d] * O[q][d]; one wave per (row, head).
 template <int D>
 __global__ void attn_dsum_kernel(const AttnArgs a) {
+  if (a.dkv_cnt) {
+    // the balanced dK/dV kernel's arrival counts start at zero
+    const int64_t n = (int64_t)a.batch * a.n_kv * ((a.seq + 31) / 32);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+      a.dkv_cnt[i] = 0u;
+  }
   int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   int64_t T = (int64_t)a.batch * a.seq;
@@ -615,178 +624,284 @@ __global__ void attn_dsum_kernel(const AttnArgs a) {
   }
 }
 
-// dK, dV for one 32-key tile of one kv head. grid (ceil(seq/32), n_kv, batch),
-// block 128 * HG threads with HG = min(group, 4) head groups of two waves; wave
-// (hg, w) owns keys kv0 + 16w .. +15 and the query heads hg, hg + HG, ... of the
-// kv head. Each head group walks 64-query tiles from the diagonal down (the next
-// tile is fetched into registers while the current one is computed); at the end
+// dK, dV for 32-key tiles of one kv head. block 128 * HG threads with HG =
+// min(group, 4) head groups of two waves; wave (hg, w) owns keys kv0 + 16w .. +15
+// and the query heads hg, hg + HG, ... of the kv head. A key tile's work is its
+// units (query head sub-group, 64-query tile from the diagonal down: the next
+// unit's tiles are fetched into registers while the current one is computed);
 // the head groups' partial dK/dV are added in head-group order through LDS.
+//
+// One workgroup per key tile (grid ceil(seq/32) x n_kv x batch as one
+// dimension, heaviest tiles first), or, BAL, the same number of workgroups per
+// (sequence, kv head) walking equal ranges of the units in key-tile order: the
+// first key tile of a sequence has all the query tiles and the last one, so at
+// one workgroup per CU the kernel would otherwise last as long as its heaviest
+// tile. A tile whose units span several workgroups is summed by the one that
+// arrives last, adding their float32 partials in workgroup order.
 constexpr int DKV_QT = 64;
-template <int D>
+LSL_DEV int dkv_owner(int u, int U, int G) { return (int)((((int64_t)u + 1) * G - 1) / U); }
+
+template <int D, bool BAL>
 __global__ __launch_bounds__(512) void attn_dkv_kernel(const AttnArgs a) {
   // head_dim 128: unpadded rows with the forward's chunk swizzle (conflict-free
   // for the row-wise and the transposing reads); 64: rows padded by 16 bytes
   constexpr bool SW = D == 128;
   constexpr int LD = SW ? D : D + 8;
+  constexpr int SLOT = 2 * 32 * D;  // a partial: dK^T and dV^T of the tile, in register order
   auto at = [](int row, int col) { return SW ? row * LD + (((col >> 3) ^ kv_sw(row)) << 3) + (col & 7) : row * LD + col; };
   constexpr int CH = DKV_QT * D / 8 / 128;  // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[4 * 2 * DKV_QT * LD];
   __shared__ float lse_s[4][DKV_QT], dsum_s[4][DKV_QT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int HG = blockDim.x >> 7, hg = wave >> 1, ws = wave & 1, htid = tid & 127;
-  // item (b n_kv + kvh) n_kt + kt: heaviest (earliest) key tiles first
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (a scalar)
+  const int HG = blockDim.x >> 7, hg = wave >> 1, ws = wave & 1;
   const int n_kt = (a.seq + 31) / 32;
   const int item = xcd_item((int)blockIdx.x, (int)gridDim.x);
-  const int bk = item / n_kt;
-  const int kv0 = (item - bk * n_kt) * 32;
+  const int bk = item / n_kt, wi = item - bk * n_kt;  // (sequence, kv head) block; index in it
   const int kvh = bk % a.n_kv, b = bk / a.n_kv;
   const int64_t rowbase = (int64_t)b * a.seq;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int mykv = kv0 + ws * 16 + c16;
   uint16_t* Qs = lds + hg * 2 * DKV_QT * LD;
   uint16_t* Os = Qs + DKV_QT * LD;
+  const int n_qt = (a.seq + DKV_QT - 1) / DKV_QT;
+  const int hq = (a.group + HG - 1) / HG;  // query head sub-groups per head group
+  // key tile kt's units: hq sub-groups x its query tiles from kt * 32 / 64 on
+  auto units = [&](int kt) { return hq * (n_qt - kt / 2); };
 
-  bf16x8 kf[D / 32], vf[D / 32];
-  {
-    const uint16_t* kp = a.k + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
-    const uint16_t* vp = a.v + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
+  f32x4 dk[D / 16], dv[D / 16];  // dK^T, dV^T: lane holds [d = dd*16 + 4g + i][kv = kv0 + 16 ws + c16]
+  // units [ia, ib) of key tile kt into dk, dv (summed over the head groups in
+  // the hg = 0 waves; LDS is free again when it returns)
+  auto segment = [&](int kt, int ia, int ib) {
+    // lane arithmetic redone per segment rather than held across the segment
+    // loop (which would spill)
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int lane = tid_o & 63, htid = tid_o & 127, g = lane >> 4, c16 = lane & 15;
+    const int kv0 = kt * 32;
+    const int mykv = kv0 + ws * 16 + c16;
+    bf16x8 kf[D / 32], vf[D / 32];
+    {
+      const uint16_t* kp = a.k + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
+      const uint16_t* vp = a.v + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      kf[ks] = mykv < a.seq ? ld8(kp + ks * 32 + g * 8) : bf16x8{};
-      vf[ks] = mykv < a.seq ? ld8(vp + ks * 32 + g * 8) : bf16x8{};
+      for (int ks = 0; ks < D / 32; ++ks) {
+        kf[ks] = mykv < a.seq ? ld8(kp + ks * 32 + g * 8) : bf16x8{};
+        vf[ks] = mykv < a.seq ? ld8(vp + ks * 32 + g * 8) : bf16x8{};
+      }
     }
-  }
-  f32x4 dk[D / 16], dv[D / 16];  // dK^T, dV^T: lane holds [d = dd*16 + 4g + i][kv = mykv]
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) dk[i] = dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int qt_begin = kv0 / DKV_QT;
-  const int nq = (a.seq + DKV_QT - 1) / DKV_QT - qt_begin;
-  const int iters = (a.group + HG - 1) / HG * nq;  // the same count for every head group
-  u32x4 pq[CH], po[CH];
-  float plse = 0.f, pds = 0.f;
-  // Prefetch into registers. Rows past the sequence and inactive head groups
-  // load a clamped in-range row (masked out in the compute), so the loads need
-  // no branches and nothing waits for them until the LDS store.
-  auto fetch = [&](int it) {
-    const int hl = min(hg + (it / nq) * HG, a.group - 1);
-    const int q0 = (qt_begin + it % nq) * DKV_QT;
-    const int h = kvh * a.group + hl;
+    for (int i = 0; i < D / 16; ++i) dk[i] = dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int qt_begin = kv0 / DKV_QT;
+    const int nq = n_qt - qt_begin;
+    u32x4 pq[CH], po[CH];
+    float plse = 0.f, pds = 0.f;
+    // Prefetch into registers. Rows past the sequence and inactive head groups
+    // load a clamped in-range row (masked out in the compute), so the loads need
+    // no branches and nothing waits for them until the LDS store.
+    auto fetch = [&](int it) {
+      const int hl = min(hg + (it / nq) * HG, a.group - 1);
+      const int q0 = (qt_begin + it % nq) * DKV_QT;
+      const int h = kvh * a.group + hl;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-      const int64_t q = min(q0 + row, a.seq - 1);
-      pq[c] = *reinterpret_cast<const u32x4*>(a.q + (rowbase + q) * a.ldq + (int64_t)h * D + col);
-      po[c] = *reinterpret_cast<const u32x4*>(a.dout + (rowbase + q) * a.ldo + (int64_t)h * D + col);
+      for (int c = 0; c < CH; ++c) {
+        const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
+        const int64_t q = min(q0 + row, a.seq - 1);
+        pq[c] = *reinterpret_cast<const u32x4*>(a.q + (rowbase + q) * a.ldq + (int64_t)h * D + col);
+        po[c] = *reinterpret_cast<const u32x4*>(a.dout + (rowbase + q) * a.ldo + (int64_t)h * D + col);
+      }
+      if (htid < DKV_QT) {
+        const int q = min(q0 + htid, a.seq - 1);
+        plse = a.lse[((int64_t)b * a.n_q + h) * a.seq + q];
+        pds = a.dsum[((int64_t)b * a.n_q + h) * a.seq + q];
+      }
+    };
+    fetch(ia);
+    for (int it = ia; it < ib; ++it) {
+      const bool act = hg + (it / nq) * HG < a.group;
+      const int q0 = (qt_begin + it % nq) * DKV_QT;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(Qs + at(row, col)) = pq[c];
+        *reinterpret_cast<u32x4*>(Os + at(row, col)) = po[c];
+      }
+      if (htid < DKV_QT) {
+        lse_s[hg][htid] = plse * LOG2E;
+        dsum_s[hg][htid] = pds;
+      }
+      __syncthreads();
+      if (it + 1 < ib) fetch(it + 1);
+      if (act) {
+        // only query tiles that reach the diagonal or the sequence's end are
+        // masked: elsewhere every query q >= q0 >= kv0 + 31 sees every key of the
+        // tile and is inside the sequence
+        const bool diag = q0 < kv0 + 31 || q0 + DKV_QT > a.seq;
+        // S[q][kv], dP[q][kv] for 64 queries: lane holds q = qs*16 + 4g + i, kv = mykv
+        f32x4 p[4], ds[4];
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+          f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const int off = at(qs * 16 + c16, ks * 32 + g * 8);
+            sv = mfma(ld8(Qs + off), kf[ks], sv);
+            dp = mfma(ld8(Os + off), vf[ks], dp);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ql = qs * 16 + g * 4 + i;
+            const int q = q0 + ql;
+            float x = fmaf(sv[i], a.scale_log2, -lse_s[hg][ql]);
+            if (diag && !(mykv <= q && q < a.seq && mykv < a.seq)) x = -INFINITY;
+            const float pv = exp2_ftz(x);
+            p[qs][i] = pv;
+            ds[qs][i] = pv * (dp[i] - dsum_s[hg][ql]);
+          }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS: reduction over the 64 queries in two
+        // 32-steps; the transposed operands come from the row-major tiles through
+        // transposing LDS reads, in the permuted order of the P / dS registers.
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 pb, pl, sb, sl;
+          split8(p[2 * kk], p[2 * kk + 1], pb, pl);
+          split8(ds[2 * kk], ds[2 * kk + 1], sb, sl);
+#pragma unroll
+          for (int dd = 0; dd < D / 16; ++dd) {
+            bf16x8 oa, qa;
+            if constexpr (SW) {
+              oa = ld_tr8_sw(Os, kk * 32, dd * 16, lane);
+              qa = ld_tr8_sw(Qs, kk * 32, dd * 16, lane);
+            } else {
+              oa = ld_tr8(Os, LD, kk * 32, dd * 16, lane);
+              qa = ld_tr8(Qs, LD, kk * 32, dd * 16, lane);
+            }
+            dv[dd] = mfma(oa, pb, dv[dd]);
+            dv[dd] = mfma(oa, pl, dv[dd]);
+            dk[dd] = mfma(qa, sb, dk[dd]);
+            dk[dd] = mfma(qa, sl, dk[dd]);
+          }
+        }
+      }
+      __syncthreads();
     }
-    if (htid < DKV_QT) {
-      const int q = min(q0 + htid, a.seq - 1);
-      plse = a.lse[((int64_t)b * a.n_q + h) * a.seq + q];
-      pds = a.dsum[((int64_t)b * a.n_q + h) * a.seq + q];
+    // add the head groups' partial sums in head-group order (LDS reused)
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    auto slot = [&](int h, int which, int dd) { return (((h - 1) * 2 + ws) * 2 + which) * (D / 16) * 64 + dd * 64 + lane; };
+    if (hg > 0) {
+#pragma unroll
+      for (int dd = 0; dd < D / 16; ++dd) {
+        red[slot(hg, 0, dd)] = dk[dd];
+        red[slot(hg, 1, dd)] = dv[dd];
+      }
+    }
+    __syncthreads();
+    if (hg == 0)
+      for (int h = 1; h < HG; ++h)
+#pragma unroll
+        for (int dd = 0; dd < D / 16; ++dd) {
+          const f32x4 rk = red[slot(h, 0, dd)], rv = red[slot(h, 1, dd)];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dk[dd][i] += rk[i];
+            dv[dd][i] += rv[i];
+          }
+        }
+    __syncthreads();
+  };
+  // the bf16 result of key tile kt from the hg = 0 waves' sums
+  auto write = [&](int kt) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int mykv = kt * 32 + ws * 16 + c16;
+    if (hg != 0 || mykv >= a.seq) return;
+    uint16_t* dkp = a.dk + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
+    uint16_t* dvp = a.dv + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
+#pragma unroll
+    for (int dd = 0; dd < D / 16; ++dd) {
+      const f32x4& rk = dk[dd];
+      const f32x4& rv = dv[dd];
+      *reinterpret_cast<u32x2*>(dkp + dd * 16 + g * 4) =
+          u32x2{pack2(rk[0] * a.scale, rk[1] * a.scale), pack2(rk[2] * a.scale, rk[3] * a.scale)};
+      *reinterpret_cast<u32x2*>(dvp + dd * 16 + g * 4) = u32x2{pack2(rv[0], rv[1]), pack2(rv[2], rv[3])};
     }
   };
 
-  fetch(0);
-  for (int it = 0; it < iters; ++it) {
-    const bool act = hg + (it / nq) * HG < a.group;
-    const int q0 = (qt_begin + it % nq) * DKV_QT;
+  if constexpr (!BAL) {
+    // one workgroup per key tile, the heaviest (earliest) first
+    segment(wi, 0, units(wi));
+    write(wi);
+  } else {
+    // equal ranges of the block's units, G = n_kt workgroups; the partials of
+    // key tile kt sit in slots f + kt .. l + kt of the block (f, l: its first and
+    // last workgroup), (2 n_kt - 1) slots per block
+    const int G = n_kt;
+    int U = 0;
+    for (int kt = 0; kt < n_kt; ++kt) U += units(kt);
+    const int ub = (int)((int64_t)U * wi / G), ue = (int)((int64_t)U * (wi + 1) / G);
+    float* part = a.dkv_part + (int64_t)bk * (2 * n_kt - 1) * SLOT;
+    unsigned* cnt = a.dkv_cnt + (int64_t)bk * n_kt;
+    const __amdgpu_buffer_rsrc_t rs = wt_rsrc(part, (int64_t)(2 * n_kt - 1) * SLOT * 4);
+    // the first key tile of the range and its first unit
+    int kt = 0, P = 0;
+    while (P + units(kt) <= ub) { P += units(kt); ++kt; }
+    // tiles whose partials this workgroup adds up (it arrived last): at most the
+    // first and the last of its range (the others in it are whole)
+    // (scalars, not an indexed array: an array indexed at run time lives in scratch)
+    int fix_t0 = -1, fix_f0 = 0, fix_n0 = 0, fix_t1 = -1, fix_f1 = 0, fix_n1 = 0;
+    for (int u = ub; u < ue; ++kt) {
+      const int I = units(kt);
+      const int ia = u - P, ib = min(I, ue - P);
+      segment(kt, ia, ib);
+      if (ia == 0 && ib == I) {
+        write(kt);
+      } else {
+        const int lane = threadIdx.x & 63;
+        if (hg == 0)
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int idx = htid + c * 128, row = idx / (D / 8), col = (idx % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Qs + at(row, col)) = pq[c];
-      *reinterpret_cast<u32x4*>(Os + at(row, col)) = po[c];
-    }
-    if (htid < DKV_QT) {
-      lse_s[hg][htid] = plse * LOG2E;
-      dsum_s[hg][htid] = pds;
-    }
-    __syncthreads();
-    if (it + 1 < iters) fetch(it + 1);
-    if (act) {
-      // only query tiles that reach the diagonal or the sequence's end are
-      // masked: elsewhere every query q >= q0 >= kv0 + 31 sees every key of the
-      // tile and is inside the sequence
-      const bool diag = q0 < kv0 + 31 || q0 + DKV_QT > a.seq;
-      // S[q][kv], dP[q][kv] for 64 queries: lane holds q = qs*16 + 4g + i, kv = mykv
-      f32x4 p[4], ds[4];
-#pragma unroll
-      for (int qs = 0; qs < 4; ++qs) {
-        f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const int off = at(qs * 16 + c16, ks * 32 + g * 8);
-          sv = mfma(ld8(Qs + off), kf[ks], sv);
-          dp = mfma(ld8(Os + off), vf[ks], dp);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ql = qs * 16 + g * 4 + i;
-          const int q = q0 + ql;
-          float x = fmaf(sv[i], a.scale_log2, -lse_s[hg][ql]);
-          if (diag && !(mykv <= q && q < a.seq && mykv < a.seq)) x = -INFINITY;
-          const float pv = exp2_ftz(x);
-          p[qs][i] = pv;
-          ds[qs][i] = pv * (dp[i] - dsum_s[hg][ql]);
-        }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS: reduction over the 64 queries in two
-      // 32-steps; the transposed operands come from the row-major tiles through
-      // transposing LDS reads, in the permuted order of the P / dS registers.
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 pb, pl, sb, sl;
-        split8(p[2 * kk], p[2 * kk + 1], pb, pl);
-        split8(ds[2 * kk], ds[2 * kk + 1], sb, sl);
-#pragma unroll
-        for (int dd = 0; dd < D / 16; ++dd) {
-          bf16x8 oa, qa;
-          if constexpr (SW) {
-            oa = ld_tr8_sw(Os, kk * 32, dd * 16, lane);
-            qa = ld_tr8_sw(Qs, kk * 32, dd * 16, lane);
-          } else {
-            oa = ld_tr8(Os, LD, kk * 32, dd * 16, lane);
-            qa = ld_tr8(Qs, LD, kk * 32, dd * 16, lane);
+          for (int dd = 0; dd < D / 16; ++dd) {
+            const uint32_t o = (uint32_t)((((ws * 2 + 0) * (D / 16) + dd) * 64 + lane) * 16);
+            const uint32_t o2 = (uint32_t)((((ws * 2 + 1) * (D / 16) + dd) * 64 + lane) * 16);
+            wt_store4(rs, o, (uint32_t)(wi + kt) * SLOT * 4, dk[dd]);
+            wt_store4(rs, o2, (uint32_t)(wi + kt) * SLOT * 4, dv[dd]);
           }
-          dv[dd] = mfma(oa, pb, dv[dd]);
-          dv[dd] = mfma(oa, pl, dv[dd]);
-          dk[dd] = mfma(qa, sb, dk[dd]);
-          dk[dd] = mfma(qa, sl, dk[dd]);
+        const int f = dkv_owner(P, U, G), l = dkv_owner(P + I - 1, U, G);
+        if (last_arrival(cnt + kt, l - f + 1)) {
+          if (fix_t0 < 0) { fix_t0 = kt; fix_f0 = f; fix_n0 = l - f + 1; }
+          else { fix_t1 = kt; fix_f1 = f; fix_n1 = l - f + 1; }
         }
       }
+      u = P + ib;
+      P += I;
     }
-    __syncthreads();
-  }
-  // add the head groups' partial sums in head-group order (LDS reused)
-  f32x4* red = reinterpret_cast<f32x4*>(lds);
-  auto slot = [&](int h, int which, int dd) { return (((h - 1) * 2 + ws) * 2 + which) * (D / 16) * 64 + dd * 64 + lane; };
-  if (hg > 0) {
+    // the tiles' partials added in workgroup order by all threads: thread tid
+    // takes float4 e = tid + 512 m of the slot, i.e. (half ws, dK or dV, dd, lane)
+    const int nthr = (int)blockDim.x;
+    for (int fi = 0; fi < 2; ++fi) {
+      const int t = fi == 0 ? fix_t0 : fix_t1;
+      if (t < 0) continue;
+      const int ff = fi == 0 ? fix_f0 : fix_f1, fn = fi == 0 ? fix_n0 : fix_n1;
+      constexpr int NE = SLOT / 4 / 128;  // float4 per thread at the smallest block (128 threads)
+      f32x4 v[NE];
+      for (int sp = 0; sp < fn; ++sp) {
+        const uint32_t so = (uint32_t)(ff + sp + t) * SLOT * 4;
 #pragma unroll
-    for (int dd = 0; dd < D / 16; ++dd) {
-      red[slot(hg, 0, dd)] = dk[dd];
-      red[slot(hg, 1, dd)] = dv[dd];
-    }
-  }
-  __syncthreads();
-  if (hg != 0 || mykv >= a.seq) return;
-  for (int h = 1; h < HG; ++h)
+        for (int m = 0; m < NE; ++m) {
+          if (tid + nthr * m >= SLOT / 4) break;
+          const f32x4 q = wt_load4(rs, (uint32_t)(tid + nthr * m) * 16, so);
+          v[m] = sp == 0 ? q : f32x4{v[m][0] + q[0], v[m][1] + q[1], v[m][2] + q[2], v[m][3] + q[3]};
+        }
+      }
 #pragma unroll
-    for (int dd = 0; dd < D / 16; ++dd) {
-      const f32x4 rk = red[slot(h, 0, dd)], rv = red[slot(h, 1, dd)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dk[dd][i] += rk[i];
-        dv[dd][i] += rv[i];
+      for (int m = 0; m < NE; ++m) {
+        const int e = tid + nthr * m;
+        if (e >= SLOT / 4) break;
+        const int ln = e & 63, dd = (e >> 6) % (D / 16), which = (e >> 6) / (D / 16) % 2, hw = (e >> 6) / (D / 16) / 2;
+        const int kv = t * 32 + hw * 16 + (ln & 15);
+        if (kv >= a.seq) continue;
+        const int d = dd * 16 + (ln >> 4) * 4;
+        const float sc = which == 0 ? a.scale : 1.f;
+        uint16_t* dst = (which == 0 ? a.dk : a.dv) + (rowbase + kv) * a.ldk + (int64_t)kvh * D + d;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack2(v[m][0] * sc, v[m][1] * sc), pack2(v[m][2] * sc, v[m][3] * sc)};
       }
     }
-  uint16_t* dkp = a.dk + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
-  uint16_t* dvp = a.dv + (rowbase + mykv) * a.ldk + (int64_t)kvh * D;
-#pragma unroll
-  for (int dd = 0; dd < D / 16; ++dd) {
-    const f32x4& rk = dk[dd];
-    const f32x4& rv = dv[dd];
-    *reinterpret_cast<u32x2*>(dkp + dd * 16 + g * 4) =
-        u32x2{pack2(rk[0] * a.scale, rk[1] * a.scale), pack2(rk[2] * a.scale, rk[3] * a.scale)};
-    *reinterpret_cast<u32x2*>(dvp + dd * 16 + g * 4) = u32x2{pack2(rv[0], rv[1]), pack2(rv[2], rv[3])};
   }
 }
 
@@ -1109,15 +1224,36 @@ lsl_status attention_bwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
   a.dsum = a.dsum_out;
   dim3 gk((unsigned)(((a.seq + 31) / 32) * a.n_kv * a.batch));
   dim3 bk((unsigned)(128 * std::min(a.group, 4)));
-  if (d == 128) hipLaunchKernelGGL(attn_dkv_kernel<128>, gk, bk, 0, s, a);
-  else hipLaunchKernelGGL(attn_dkv_kernel<64>, gk, bk, 0, s, a);
+  if (a.dkv_cnt) {
+    if (d == 128) hipLaunchKernelGGL((attn_dkv_kernel<128, true>), gk, bk, 0, s, a);
+    else hipLaunchKernelGGL((attn_dkv_kernel<64, true>), gk, bk, 0, s, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((attn_dkv_kernel<128, false>), gk, bk, 0, s, a);
+    else hipLaunchKernelGGL((attn_dkv_kernel<64, false>), gk, bk, 0, s, a);
+  }
   dim3 gq((unsigned)(((a.seq + ATT_QT - 1) / ATT_QT) * a.n_kv * a.batch));
   if (d == 128) launch_by_group<DqKernel, 128>(a.group, gq, dim3(64 * a.group), s, a);
   else launch_by_group<DqKernel, 64>(a.group, gq, dim3(64 * a.group), s, a);
   return check_launch("attention_bwd");
 }
 
-size_t attention_ws_bytes(int batch, int seq, int n_q) { return align256((size_t)batch * n_q * seq * sizeof(float)); }
+// The balanced dK/dV kernel runs when the key tiles are few (at most two per CU),
+// so that one workgroup per key tile would leave the kernel waiting on its
+// heaviest tiles; its scratch follows the row sums in the workspace.
+static bool dkv_balanced(int batch, int seq, int n_kv) {
+  const int64_t n_kt = (seq + 31) / 32;
+  return n_kt >= 2 && (int64_t)batch * n_kv * n_kt <= 512;
+}
+static size_t dkv_cnt_bytes(int batch, int seq, int n_kv) {
+  return align256((size_t)batch * n_kv * ((seq + 31) / 32) * sizeof(unsigned));
+}
+size_t attention_ws_bytes(int batch, int seq, int n_q, int n_kv, int d) {
+  size_t bytes = align256((size_t)batch * n_q * seq * sizeof(float));
+  if (dkv_balanced(batch, seq, n_kv))
+    bytes += dkv_cnt_bytes(batch, seq, n_kv) +
+             (size_t)batch * n_kv * (2 * ((seq + 31) / 32) - 1) * (2 * 32 * d) * sizeof(float);
+  return bytes;
+}
 
 }  // namespace lsl
 
@@ -1140,9 +1276,11 @@ extern "C" lsl_status lsl_attention_fwd(const uint16_t* q, const uint16_t* k, co
   return attention_fwd_launch(a, head_dim, (hipStream_t)stream);
 }
 
-extern "C" size_t lsl_attention_workspace_bytes(int32_t batch, int32_t seq, int32_t n_q, int32_t, int32_t) {
+extern "C" size_t lsl_attention_workspace_bytes(int32_t batch, int32_t seq, int32_t n_q, int32_t n_kv,
+                                                 int32_t head_dim) {
   if (batch < 0 || seq < 0 || n_q <= 0) return 0;
-  return attention_ws_bytes(batch, seq, n_q);
+  if (n_kv <= 0 || (head_dim != 64 && head_dim != 128)) return 0;
+  return attention_ws_bytes(batch, seq, n_q, n_kv, head_dim);
 }
 
 extern "C" lsl_status lsl_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
@@ -1155,9 +1293,14 @@ extern "C" lsl_status lsl_attention_bwd(const uint16_t* q, const uint16_t* k, co
   if (ldo < (int64_t)n_q * head_dim || ldo % 8) return set_error(LSL_ERR_INVALID_ARG, "%s: bad ldo", fn);
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {q, k, v, o, dout, lse, dq, dk, dv}));
-  size_t need = attention_ws_bytes(batch, seq, n_q);
+  size_t need = attention_ws_bytes(batch, seq, n_q, n_kv, head_dim);
   if (!ws || ws_bytes < need) return set_error(LSL_ERR_WORKSPACE, "%s: workspace %zu < %zu", fn, ws_bytes, need);
   AttnArgs a{};
+  if (dkv_balanced(batch, seq, n_kv)) {
+    char* w = (char*)ws + align256((size_t)batch * n_q * seq * sizeof(float));
+    a.dkv_cnt = (unsigned*)w;
+    a.dkv_part = (float*)(w + dkv_cnt_bytes(batch, seq, n_kv));
+  }
   a.q = q; a.k = k; a.v = v; a.ldq = ldq; a.ldk = ldk;
   a.o = o; a.dout = dout; a.ldo = ldo; a.lse = lse; a.dsum_out = (float*)ws; a.o32 = (float*)o32;
   a.out = dq; a.dk = dk; a.dv = dv;

@@ -211,6 +211,23 @@ def test_workspace_queries_with_zero_tokens(L):
     assert lib.lsl_attention_workspace_bytes(0, 0, 32, 8, 128) >= 0
 
 
+def test_attention_workspace_holds_the_balanced_dkv_scratch(L):
+    """The backward's workspace: the float32 row sums [batch x n_q x seq], and,
+    when the key tiles are few (batch x n_kv x ceil(seq / 32) <= 512, where the
+    dK/dV work is spread evenly over the workgroups), 256-byte-aligned arrival
+    counts (one per key tile) and 2 ceil(seq / 32) - 1 float32 partial slots of
+    2 x 32 x head_dim per (sequence, kv head)."""
+    lib = L.lib()
+    rows = 1 * 32 * 1024 * 4
+    cnt = 256 * ((8 * 32 * 4 + 255) // 256)
+    part = 8 * 63 * (2 * 32 * 128) * 4
+    assert lib.lsl_attention_workspace_bytes(1, 1024, 32, 8, 128) == rows + cnt + part
+    # 3 x 8 x 32 = 768 key tiles: one workgroup per key tile, row sums only
+    assert lib.lsl_attention_workspace_bytes(3, 1024, 8, 8, 128) == 3 * 8 * 1024 * 4
+    # a single key tile needs no balancing
+    assert lib.lsl_attention_workspace_bytes(1, 32, 4, 2, 64) == 256 * ((4 * 32 * 4 + 255) // 256)
+
+
 def test_size_limits_rejected_before_any_launch(L):
     """Shapes past the 32-bit buffer-offset limits are rejected by every entry
     point before its first launch (these calls would fail on any launch here,

@@ -24,6 +24,10 @@ pytestmark = pytest.mark.gpu
     (1, 300, 7, 1, 128),    # group of 7 at head_dim 128
     (2, 129, 2, 2, 128),    # one query head per kv head, two sequences, a one-row last key tile
     (1, 33, 2, 1, 128),     # group of 2, a single partial tile
+    # more than 512 key tiles in all: dK/dV with one workgroup per key tile (the
+    # cases above spread each kv head's dK/dV work evenly over its workgroups)
+    (3, 1024, 8, 8, 128),
+    (3, 1024, 16, 8, 64),
 ])
 def test_attention_parity(gpu, batch, seq, nq, nkv, d):
     T = batch * seq
@@ -76,3 +80,22 @@ def test_attention_forward_is_deterministic(gpu):
         o1, lse1, o321 = gpu.attention_fwd(Q, K, V, batch, seq, nq, nkv, d, want_o32=True)
         torch.cuda.synchronize()
         assert torch.equal(o0, o1) and torch.equal(lse0, lse1) and torch.equal(o320, o321)
+
+
+def test_attention_backward_is_deterministic(gpu):
+    """Repeated backward calls give identical bits: the Llama-8B layer's shape at
+    1024 tokens, whose dK/dV key tiles are split over several workgroups and
+    summed in workgroup order by whichever arrives last."""
+    batch, seq, nq, nkv, d = 1, 1024, 32, 8, 128
+    T = batch * seq
+    g = torch.Generator(device="cuda").manual_seed(11)
+    Q = torch.randn(T, nq * d, device="cuda", generator=g).to(torch.bfloat16)
+    K = torch.randn(T, nkv * d, device="cuda", generator=g).to(torch.bfloat16)
+    V = torch.randn(T, nkv * d, device="cuda", generator=g).to(torch.bfloat16)
+    DO = torch.randn(T, nq * d, device="cuda", generator=g).to(torch.bfloat16)
+    o, lse, o32 = gpu.attention_fwd(Q, K, V, batch, seq, nq, nkv, d, want_o32=True)
+    r0 = gpu.attention_bwd(Q, K, V, o, DO, lse, batch, seq, nq, nkv, d, o32=o32)
+    for _ in range(3):
+        r1 = gpu.attention_bwd(Q, K, V, o, DO, lse, batch, seq, nq, nkv, d, o32=o32)
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(r0, r1))
