@@ -460,15 +460,17 @@ def summarize_trace(d, args):
     half = ms.batch * shape.n_q * ms.seq * ms.seq * shape.head_dim  # 2 B nq S^2 d / 2 per product
     out += ["", "| attention kernel | calls | avg us | algorithmic GFLOP per launch | TF/s | of bf16 peak |",
             "|---|---:|---:|---:|---:|---:|"]
-    for prefix, nprod in (("void lsl::attn_fwd_kernel", 2), ("void lsl::attn_dkv_kernel", 4),
-                          ("void lsl::attn_dq_kernel", 3)):
-        ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
-              if r["Kernel_Name"].startswith(prefix)]
-        if not ds:
+    # (the kernel families: attn_fwd_kernel / attn_fwd_dma_kernel, attn_dkv_kernel, attn_dq_kernel /
+    # attn_dq_dma_kernel; the forward's launches include the reference forwards and the recomputation)
+    for prefix, nprod in (("void lsl::attn_fwd", 2), ("void lsl::attn_dkv", 4), ("void lsl::attn_dq", 3)):
+        rows = [r for r in trace if r["Kernel_Name"].startswith(prefix)]
+        if not rows:
             continue
+        ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+        names = sorted({r["Kernel_Name"].split("(")[0][5:] for r in rows})
         avg = sum(ds) / len(ds)
         fl = nprod * half
-        out.append(f"| `{prefix[5:]}` | {len(ds)} | {avg:.1f} | {fl / 1e9:.2f} | {fl / (avg * 1e-6) / 1e12:.0f} | "
+        out.append(f"| `{', '.join(names)}` | {len(ds)} | {avg:.1f} | {fl / 1e9:.2f} | {fl / (avg * 1e-6) / 1e12:.0f} | "
                    f"{fl / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.2f} |")
     # bandwidth-bound kernels: algorithmic bytes / average duration against the 8 TB/s HBM peak
     out += ["", "| bandwidth-bound kernel | calls | avg us | algorithmic bytes per launch | GB/s | of 8 TB/s | bytes |",
