@@ -1070,7 +1070,37 @@ __global__ __launch_bounds__(128 * NW) void attn_dq_dma_kernel(const AttnArgs a)
     of[ks] = ld8(dop + (int64_t)qc * a.ldo + ks * 32 + g * 8);
   }
   const float lse2 = a.lse[((int64_t)b * a.n_q + h) * a.seq + qc] * LOG2E;
-  const float dsm = a.dsum[((int64_t)b * a.n_q + h) * a.seq + qc];
+  // D_q = sum_d dO O (O from the forward's float32 copy when there is one), over
+  // the lane's 32 columns and then the query's four lanes; written for the dK/dV
+  // kernel, which runs after this one
+  float dsm = 0.f;
+  if (a.o32) {
+    const float* op = a.o32 + (rowbase + qc) * ((int64_t)a.n_q * D) + (int64_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(op + ks * 32 + g * 8);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(op + ks * 32 + g * 8 + 4);
+      const u32x4 dv = __builtin_bit_cast(u32x4, of[ks]);
+      dsm += o0[0] * lo_bf(dv[0]) + o0[1] * hi_bf(dv[0]) + o0[2] * lo_bf(dv[1]) + o0[3] * hi_bf(dv[1]);
+      dsm += o1[0] * lo_bf(dv[2]) + o1[1] * hi_bf(dv[2]) + o1[2] * lo_bf(dv[3]) + o1[3] * hi_bf(dv[3]);
+    }
+  } else {
+    const uint16_t* op = a.o + (rowbase + qc) * a.ldo + (int64_t)h * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(op + ks * 32 + g * 8);
+      const u32x4 dv = __builtin_bit_cast(u32x4, of[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsm += lo_bf(ov[e]) * lo_bf(dv[e]) + hi_bf(ov[e]) * hi_bf(dv[e]);
+    }
+  }
+  dsm = sum_rows4(dsm);
+  if (kh == 0 && g == 0 && q < a.seq) a.dsum_out[((int64_t)b * a.n_q + h) * a.seq + q] = dsm;
+  if (a.dkv_cnt && blockIdx.x == 0) {
+    // the balanced dK/dV kernel's arrival counts start at zero
+    const int64_t n = (int64_t)a.batch * a.n_kv * ((a.seq + 31) / 32);
+    for (int64_t i = tid; i < n; i += blockDim.x) a.dkv_cnt[i] = 0u;
+  }
   f32x4 dq[D / 16];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) dq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1218,9 +1248,16 @@ lsl_status attention_bwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
   AttnArgs a = a0;
   int64_t T = (int64_t)a.batch * a.seq;
   if (T == 0) return LSL_OK;
-  dim3 gs((unsigned)((T * a.n_q + 3) / 4));
-  if (d == 128) hipLaunchKernelGGL(attn_dsum_kernel<128>, gs, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(attn_dsum_kernel<64>, gs, dim3(256), 0, s, a);
+  dim3 gq((unsigned)(((a.seq + ATT_QT - 1) / ATT_QT) * a.n_kv * a.batch));
+  if (d == 128 && ATT_QT == 16) {
+    // the dQ kernel computes the row sums D itself (and zeroes the dK/dV
+    // arrival counts); the dK/dV kernel reads them after it
+    launch_by_group<DqKernel, 128>(a.group, gq, dim3(64 * a.group), s, a);
+  } else {
+    dim3 gs((unsigned)((T * a.n_q + 3) / 4));
+    if (d == 128) hipLaunchKernelGGL(attn_dsum_kernel<128>, gs, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_dsum_kernel<64>, gs, dim3(256), 0, s, a);
+  }
   a.dsum = a.dsum_out;
   dim3 gk((unsigned)(((a.seq + 31) / 32) * a.n_kv * a.batch));
   dim3 bk((unsigned)(128 * std::min(a.group, 4)));
@@ -1231,9 +1268,10 @@ lsl_status attention_bwd_launch(const AttnArgs& a0, int d, hipStream_t s) {
     if (d == 128) hipLaunchKernelGGL((attn_dkv_kernel<128, false>), gk, bk, 0, s, a);
     else hipLaunchKernelGGL((attn_dkv_kernel<64, false>), gk, bk, 0, s, a);
   }
-  dim3 gq((unsigned)(((a.seq + ATT_QT - 1) / ATT_QT) * a.n_kv * a.batch));
-  if (d == 128) launch_by_group<DqKernel, 128>(a.group, gq, dim3(64 * a.group), s, a);
-  else launch_by_group<DqKernel, 64>(a.group, gq, dim3(64 * a.group), s, a);
+  if (d == 64 || ATT_QT != 16) {
+    if (d == 128) launch_by_group<DqKernel, 128>(a.group, gq, dim3(64 * a.group), s, a);
+    else launch_by_group<DqKernel, 64>(a.group, gq, dim3(64 * a.group), s, a);
+  }
   return check_launch("attention_bwd");
 }
 
