@@ -126,6 +126,12 @@ static void layout_of(const lsl_layer_cfg* c, lsl_layer_layout* L) {
 // row stride; the v columns of qkr are unused); in the backward the attention
 // writes dq and dk into dqkr and dv into dqkv, whose q and k columns then take
 // the inverse RoPE of dqkr. So every rounding point keeps its own tensor.
+// workspace of two TN side products launched together (the first's partial
+// slots, 256-byte aligned, then the second's)
+static size_t tn2_ws(int64_t T, int64_t W0, int64_t W1, int kl) {
+  return align256(lora_tn_ws_bytes(T, W0, kl)) + lora_tn_ws_bytes(T, W1, kl);
+}
+
 struct Plan {
   size_t n1, tqkv, qkv, qkr, o, lse, to, h1, n2, tgu, gu, a, td;                    // forward
   size_t ud, da, dgu, ugu, dn2, dh1, uo, dob, dqkr, dqkv, uqkv, dn1, attn_ws, o32;  // backward
@@ -174,9 +180,8 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
     p.o32 = take(T * d.Q * 4);
     part = std::max({part, lora_nt_ws_bytes(d.T, d.NQKV, 3 * r), lora_nt_ws_bytes(d.T, d.H, r),
                      lora_nt_ws_bytes(d.T, 2 * d.I, 2 * r),
-                     lora_tn_ws_bytes(d.T, d.H, 3 * r), lora_tn_ws_bytes(d.T, d.Q, r), lora_tn_ws_bytes(d.T, d.H, 2 * r),
-                     lora_tn_ws_bytes(d.T, d.I, r), lora_tn_ws_bytes(d.T, d.NQKV, 3 * r), lora_tn_ws_bytes(d.T, d.H, r),
-                     lora_tn_ws_bytes(d.T, 2 * d.I, 2 * r),
+                     tn2_ws(d.T, d.H, d.NQKV, 3 * r), tn2_ws(d.T, d.Q, d.H, r), tn2_ws(d.T, d.H, 2 * d.I, 2 * r),
+                     tn2_ws(d.T, d.I, d.H, r),
                      gemm_split_bytes(d.T, d.H, d.NQKV), gemm_split_bytes(d.T, d.Q, d.H),
                      gemm_split_bytes(d.T, d.H, 2 * d.I), gemm_split_bytes(d.T, d.I, d.H)});
   }
@@ -185,6 +190,8 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
   // of their own (zeroed by the layer's first RMSNorm launch, left zero by every
   // launch that uses it; the launches that share it run one after another)
   p.ncnt = std::max({lora_counts_needed(d.T, std::max({d.NQKV, 2 * d.I, d.H, d.Q, d.I})),
+                     lora_tn_tiles(d.H) + lora_tn_tiles(d.NQKV), lora_tn_tiles(d.Q) + lora_tn_tiles(d.H),
+                     lora_tn_tiles(d.H) + lora_tn_tiles(2 * d.I), lora_tn_tiles(d.I) + lora_tn_tiles(d.H),
                      gemm_counts_needed(d.T, d.NQKV, d.H), gemm_counts_needed(d.T, d.H, d.Q),
                      gemm_counts_needed(d.T, 2 * d.I, d.H), gemm_counts_needed(d.T, d.H, d.I),
                      gemm_counts_needed(d.T, d.H, d.NQKV), gemm_counts_needed(d.T, d.Q, d.H),
@@ -294,16 +301,21 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
       LSL_TRY(st);
     }
   }
+  // dA and dB in one launch, each with its own partial slots and arrival counts
   LoraTn ta;
   ta.p = x; ta.ldp = k; ta.q = u; ta.ldq = kl; ta.T = d.T; ta.W = k; ta.kl = kl;
   ta.scale = c->lora_scale; ta.dA = gr->dA[i]; ta.ws = part; ta.cnt = cnt;
-  LSL_TRY(dry ? lora_tn_check(ta) : lora_tn_launch(ta, s));
   LoraTn tb;
   tb.p = dy; tb.ldp = n; tb.q = t; tb.ldq = kl; tb.T = d.T; tb.W = n; tb.kl = kl;
   tb.scale = c->lora_scale; tb.dB = gr->dB[i]; tb.r = d.r; tb.nseg = nseg;
   for (int q = 0; q < 4; ++q) tb.seg_end[q] = se[q];
-  tb.ws = part; tb.cnt = cnt;
-  return dry ? lora_tn_check(tb) : lora_tn_launch(tb, s);
+  tb.ws = (float*)((char*)part + align256(lora_tn_ws_bytes(d.T, k, kl)));
+  tb.cnt = cnt + lora_tn_tiles(k);
+  if (dry) {
+    LSL_TRY(lora_tn_check(ta));
+    return lora_tn_check(tb);
+  }
+  return lora_tn2_launch(ta, tb, s);
 }
 
 // dry: check the conditions of every GEMM and side product, enqueue nothing

@@ -208,16 +208,30 @@ LSL_DEV int tn_qrow(int tid, int rr) {
   return 8 * (qq >> 3) + ((qq >> 1) & 3) + 4 * (qq & 1) + 32 * rr;
 }
 
-// grid: (ceil(W/128), S). 4 waves, wave w owns columns a = 32w..32w+31 of the tile.
+// Up to two products in one launch (the adapter gradients dA and dB of one
+// projection need no ordering between them): grid = tiles0 S0 + tiles1 S1
+// workgroups in one dimension, workgroup b < tiles0 S0 taking tile b % tiles0,
+// split b / tiles0 of product 0, the rest likewise of product 1; each product
+// has its own partial slots and arrival counts.
+struct TnGroup {
+  TnArgs p[2];
+  int tiles[2];
+};
+// 4 waves, wave w owns columns a = 32w..32w+31 of the tile.
 // BUF: the split's rows are read through buffer descriptors (its bytes below
 // 4 GiB): no per-load bounds branches.
 template <bool BUF>
-__global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
+__global__ __launch_bounds__(256) void lora_tn_kernel(const TnGroup grp) {
   __shared__ __attribute__((aligned(16))) uint16_t Ps[64 * TN_LDP];  // [t][a]
   __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * TN_LDQ];  // [t][j]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t a0 = (int64_t)blockIdx.x * 128;
-  const int64_t tbeg = (int64_t)blockIdx.y * a.t_per_split;
+  const int n0 = grp.tiles[0] * grp.p[0].S;
+  const int pi = (int)blockIdx.x < n0 ? 0 : 1;  // (uniform in the workgroup)
+  const TnArgs& a = grp.p[pi];
+  const int bi = (int)blockIdx.x - (pi ? n0 : 0);
+  const int tile = bi % grp.tiles[pi], split = bi / grp.tiles[pi], ntiles = grp.tiles[pi];
+  const int64_t a0 = (int64_t)tile * 128;
+  const int64_t tbeg = (int64_t)split * a.t_per_split;
   const int64_t tend = tbeg + a.t_per_split < a.T ? tbeg + a.t_per_split : a.T;
   f32x4 acc[4][2];
 #pragma unroll
@@ -306,14 +320,14 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnArgs a) {
   if (tt < tend) step(tt, rpa, rqa);
   // lane holds C[a][c..c+3], a = a0 + 32 wave + 16 j + lane % 16, c = 16 i + 4 (lane / 16)
   if (a.S > 1) {
-    const __amdgpu_buffer_rsrc_t rs = wt_rsrc(a.part, (int64_t)gridDim.x * a.S * TN_SLOT * 4);
-    const uint32_t s0 = blockIdx.x * (uint32_t)a.S * TN_SLOT * 4;
+    const __amdgpu_buffer_rsrc_t rs = wt_rsrc(a.part, (int64_t)ntiles * a.S * TN_SLOT * 4);
+    const uint32_t s0 = (uint32_t)tile * (uint32_t)a.S * TN_SLOT * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        wt_store4(rs, (uint32_t)((2 * i + j) * 256 + tid) * 16, s0 + blockIdx.y * (uint32_t)TN_SLOT * 4, acc[i][j]);
-    if (!last_arrival(a.cnt + blockIdx.x, a.S)) return;
+        wt_store4(rs, (uint32_t)((2 * i + j) * 256 + tid) * 16, s0 + (uint32_t)split * TN_SLOT * 4, acc[i][j]);
+    if (!last_arrival(a.cnt + tile, a.S)) return;
     // the tile's S partials in split order, two splits' loads in flight at a time
     for (int sp = 0; sp < a.S; sp += 2) {
       f32x4 q[2][8];
@@ -467,11 +481,8 @@ lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s) {
   return check_launch("lora_nt");
 }
 
-lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
-  if (d.W == 0) return LSL_OK;
-  LSL_TRY(lora_tn_check(d));
-  if (d.T == 0) return LSL_OK;
-  const int64_t tiles = (d.W + 127) / 128;
+static TnArgs tn_args(const LoraTn& d, int& tiles, bool& buf) {
+  tiles = (int)((d.W + 127) / 128);
   const int S = tn_splits(d.W, d.T);
   const int64_t steps = (d.T + 63) / 64;
   const int64_t per = ((steps + S - 1) / S) * 64;
@@ -481,13 +492,42 @@ lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
   a.dA = d.dA; a.dB = d.dA ? nullptr : d.dB; a.scale = d.scale; a.r = d.r; a.nseg = d.nseg;
   for (int i = 0; i < 4; ++i) a.seg.e[i] = d.seg_end[i];
   // buffer descriptors address a split's rows with 32-bit offsets
-  const int64_t lim = (int64_t)1 << 32;
   // (the loads run up to two steps past a split's rows)
-  const bool buf = (per + 192) * d.ldp * 2 < lim && (per + 192) * d.ldq * 2 < lim;
-  const dim3 grid((unsigned)tiles, (unsigned)S);
-  if (buf) hipLaunchKernelGGL((lora_tn_kernel<true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((lora_tn_kernel<false>), grid, dim3(256), 0, s, a);
+  const int64_t lim = (int64_t)1 << 32;
+  buf = (per + 192) * d.ldp * 2 < lim && (per + 192) * d.ldq * 2 < lim;
+  return a;
+}
+
+static lsl_status tn_group_launch(TnGroup& g, int n, bool buf, hipStream_t s) {
+  const int64_t blocks = (int64_t)g.tiles[0] * g.p[0].S + (n > 1 ? (int64_t)g.tiles[1] * g.p[1].S : 0);
+  if (blocks >= ((int64_t)1 << 31)) return set_error(LSL_ERR_UNSUPPORTED, "lora grad: too many tiles");
+  if (buf) hipLaunchKernelGGL((lora_tn_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((lora_tn_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   return check_launch("lora_tn");
+}
+
+lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
+  if (d.W == 0) return LSL_OK;
+  LSL_TRY(lora_tn_check(d));
+  if (d.T == 0) return LSL_OK;
+  TnGroup g{};
+  bool buf;
+  g.p[0] = tn_args(d, g.tiles[0], buf);
+  return tn_group_launch(g, 1, buf, s);
+}
+
+size_t lora_tn_tiles(int64_t W) { return (size_t)((W + 127) / 128); }
+
+lsl_status lora_tn2_launch(const LoraTn& d0, const LoraTn& d1, hipStream_t s) {
+  LSL_TRY(lora_tn_check(d0));
+  LSL_TRY(lora_tn_check(d1));
+  if (d0.W == 0 || d0.T == 0) return lora_tn_launch(d1, s);
+  if (d1.W == 0 || d1.T == 0) return lora_tn_launch(d0, s);
+  TnGroup g{};
+  bool b0, b1;
+  g.p[0] = tn_args(d0, g.tiles[0], b0);
+  g.p[1] = tn_args(d1, g.tiles[1], b1);
+  return tn_group_launch(g, 2, b0 && b1, s);
 }
 
 }  // namespace lsl
