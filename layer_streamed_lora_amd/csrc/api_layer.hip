@@ -135,6 +135,7 @@ static size_t tn2_ws(int64_t T, int64_t W0, int64_t W1, int kl) {
 struct Plan {
   size_t n1, tqkv, qkv, qkr, o, lse, to, h1, n2, tgu, gu, a, td;                    // forward
   size_t ud, da, dgu, ugu, dn2, dh1, uo, dob, dqkr, dqkv, uqkv, dn1, attn_ws, o32;  // backward
+  size_t bt[4];                                                                   // backward: masked B^T
   size_t part, cnt, ncnt, total;
 };
 
@@ -178,6 +179,11 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
     p.dn1 = take(T * d.H * 2);
     p.attn_ws = take(lsl_attention_workspace_bytes(batch, seq, c->n_q, c->n_kv, c->head_dim));
     p.o32 = take(T * d.Q * 4);
+    // the masked B^T of the four projections (u = dy B), made once per backward
+    p.bt[LSL_M_QKV] = take((size_t)3 * d.r * d.NQKV * 2);
+    p.bt[LSL_M_O] = take((size_t)d.r * d.H * 2);
+    p.bt[LSL_M_GU] = take((size_t)2 * d.r * 2 * d.I * 2);
+    p.bt[LSL_M_DOWN] = take((size_t)d.r * d.H * 2);
     part = std::max({part, lora_nt_ws_bytes(d.T, d.NQKV, 3 * r), lora_nt_ws_bytes(d.T, d.H, r),
                      lora_nt_ws_bytes(d.T, 2 * d.I, 2 * r),
                      tn2_ws(d.T, d.H, d.NQKV, 3 * r), tn2_ws(d.T, d.Q, d.H, r), tn2_ws(d.T, d.H, 2 * d.I, 2 * r),
@@ -269,10 +275,11 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
 
 // Backward of one fused LoRA linear: u = dy B (per projection); dx = dy W + s u A;
 // dA += s u^T x; dB += s dy^T t (per projection).
+// bt: the projection's masked B^T, made beforehand (lora_bt_group_launch)
 static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    const lsl_lora_grads* gr, int i, const uint16_t* x, const uint16_t* t,
                                    const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, unsigned* cnt,
-                                   hipStream_t s, bool dry) {
+                                   const uint16_t* bt, hipStream_t s, bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -281,7 +288,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
   if (i == LSL_M_QKV) { se[0] = d.Q; se[1] = d.Q + d.KV; se[2] = d.NQKV; }
   else if (i == LSL_M_GU) { se[0] = d.I; se[1] = 2 * d.I; }
   LoraNt nt;
-  nt.p = dy; nt.ldp = n; nt.T = d.T; nt.K = n; nt.kl = kl; nt.b_full = lo->B[i]; nt.r = d.r; nt.nseg = nseg;
+  nt.p = dy; nt.ldp = n; nt.T = d.T; nt.K = n; nt.kl = kl; nt.a_full = bt; nt.r = d.r; nt.nseg = nseg;
   for (int q = 0; q < 4; ++q) nt.seg_end[q] = se[q];
   nt.out = u; nt.ldo = kl; nt.ws = part; nt.cnt = cnt;
   LSL_TRY(dry ? lora_nt_check(nt) : lora_nt_launch(nt, s));
@@ -378,16 +385,33 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
   uint16_t* dn2 = (uint16_t*)(w + p.dn2);
   uint16_t* dh1 = (uint16_t*)(w + p.dh1);
   uint16_t* dob = (uint16_t*)(w + p.dob);
+  const uint16_t* bt[4];
+  for (int i = 0; i < 4; ++i) bt[i] = (const uint16_t*)(w + p.bt[i]);
+  if (!dry) {
+    // the four projections' masked B^T for u = dy B, in one launch
+    LoraBt jobs[4];
+    for (int i = 0; i < 4; ++i) {
+      int64_t n, k;
+      mat_shape(d, i, n, k);
+      jobs[i].b_full = lora->B[i]; jobs[i].r = d.r; jobs[i].K = n; jobs[i].bt = (uint16_t*)(w + p.bt[i]);
+      jobs[i].nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
+      jobs[i].kl = jobs[i].nseg * d.r;
+      jobs[i].seg_end[0] = n;
+      if (i == LSL_M_QKV) { jobs[i].seg_end[0] = d.Q; jobs[i].seg_end[1] = d.Q + d.KV; jobs[i].seg_end[2] = d.NQKV; }
+      else if (i == LSL_M_GU) { jobs[i].seg_end[0] = d.I; jobs[i].seg_end[1] = 2 * d.I; }
+    }
+    LSL_TRY(lora_bt_group_launch(jobs, 4, s));
+  }
   // MLP
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_DOWN, (uint16_t*)(w + p.a), (uint16_t*)(w + p.td), dy,
-                           (uint16_t*)(w + p.ud), da, part, cnt, s, dry));
+                           (uint16_t*)(w + p.ud), da, part, cnt, bt[LSL_M_DOWN], s, dry));
   if (!dry) LSL_TRY(swiglu_bwd_launch((uint16_t*)(w + p.gu), da, d.T, d.I, dgu, s));
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), (uint16_t*)(w + p.tgu), dgu,
-                           (uint16_t*)(w + p.ugu), dn2, part, cnt, s, dry));
+                           (uint16_t*)(w + p.ugu), dn2, part, cnt, bt[LSL_M_GU], s, dry));
   if (!dry) LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
   // attention block
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), (uint16_t*)(w + p.to), dh1,
-                           (uint16_t*)(w + p.uo), dob, part, cnt, s, dry));
+                           (uint16_t*)(w + p.uo), dob, part, cnt, bt[LSL_M_O], s, dry));
   if (!dry) {
     LSL_TRY(lsl_attention_bwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
                               (const float*)(w + p.o32), d.NQKV, d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d,
@@ -396,7 +420,7 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
                         1, s));
   }
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
-                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, cnt, s, dry));
+                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, cnt, bt[LSL_M_QKV], s, dry));
   if (dx && !dry) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
   return LSL_OK;
 }

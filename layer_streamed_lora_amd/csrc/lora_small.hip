@@ -160,11 +160,9 @@ __global__ __launch_bounds__(256, 2) void lora_nt_kernel(const NtArgs a) {
 
 // Masked transpose of B_full [K x r] for u = dy B: bt[j][k] = B[k][j % r] when
 // j / r is the projection owning row k (else 0), j < kl. 8 k per thread.
-__global__ void lora_bt_kernel(const uint16_t* __restrict__ b, int r, int kl, int64_t K, int nseg, SegEnds seg,
-                               uint16_t* __restrict__ bt) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+LSL_DEV void bt_chunk(const uint16_t* __restrict__ b, int r, int kl, int64_t K, int nseg, const SegEnds& seg,
+                      uint16_t* __restrict__ bt, int64_t idx) {
   const int64_t kc = K / 8;
-  if (idx >= kl * kc) return;
   const int j = (int)(idx / kc);
   const int64_t k = (idx - (int64_t)j * kc) * 8;
   int p = 0;
@@ -176,6 +174,28 @@ __global__ void lora_bt_kernel(const uint16_t* __restrict__ b, int r, int kl, in
     for (int e = 0; e < 4; ++e) w[e] = (uint32_t)src[(2 * e) * r] | ((uint32_t)src[(2 * e + 1) * r] << 16);
   }
   *reinterpret_cast<u32x4*>(bt + (int64_t)j * K + k) = u32x4{w[0], w[1], w[2], w[3]};
+}
+__global__ void lora_bt_kernel(const uint16_t* __restrict__ b, int r, int kl, int64_t K, int nseg, SegEnds seg,
+                               uint16_t* __restrict__ bt) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= kl * (K / 8)) return;
+  bt_chunk(b, r, kl, K, nseg, seg, bt, idx);
+}
+// up to four transposes in one launch (thread idx: the jobs' chunks one after another)
+struct BtGroup {
+  const uint16_t* b[4]; int r[4], kl[4], nseg[4]; int64_t K[4]; SegEnds seg[4]; uint16_t* bt[4];
+  int n;
+};
+__global__ void lora_bt_group_kernel(const BtGroup g) {
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int i = 0; i < g.n; ++i) {
+    const int64_t n = (int64_t)g.kl[i] * (g.K[i] / 8);
+    if (idx < n) {
+      bt_chunk(g.b[i], g.r[i], g.kl[i], g.K[i], g.nseg[i], g.seg[i], g.bt[i], idx);
+      return;
+    }
+    idx -= n;
+  }
 }
 
 // ---------------------------------------------------------------- TN
@@ -517,6 +537,23 @@ lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
 }
 
 size_t lora_tn_tiles(int64_t W) { return (size_t)((W + 127) / 128); }
+
+lsl_status lora_bt_group_launch(const LoraBt* jobs, int n, hipStream_t s) {
+  if (n < 1 || n > 4) return set_error(LSL_ERR_INVALID_ARG, "lora_bt_group: 1..4 transposes");
+  BtGroup g{};
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const LoraBt& j = jobs[i];
+    if (j.K % 8 || j.kl <= 0 || j.kl > 64 || j.r <= 0) return set_error(LSL_ERR_UNSUPPORTED, "lora_bt_group: shape");
+    g.b[i] = j.b_full; g.r[i] = j.r; g.kl[i] = j.kl; g.nseg[i] = j.nseg; g.K[i] = j.K; g.bt[i] = j.bt;
+    for (int q = 0; q < 4; ++q) g.seg[i].e[q] = j.seg_end[q];
+    total += (int64_t)j.kl * (j.K / 8);
+  }
+  g.n = n;
+  if (total == 0) return LSL_OK;
+  hipLaunchKernelGGL(lora_bt_group_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, g);
+  return check_launch("lora_bt_group");
+}
 
 lsl_status lora_tn2_launch(const LoraTn& d0, const LoraTn& d1, hipStream_t s) {
   LSL_TRY(lora_tn_check(d0));

@@ -25,6 +25,16 @@ struct LoraTn {
   float* ws = nullptr;
   unsigned* cnt = nullptr;
 };
+// the projection-masked transpose bt [kl x K] of B_full [K x r] (bt[j][k] =
+// B[k][j % r] when row k belongs to projection j / r, else 0): the NT operand
+// R of u = dy B
+struct LoraBt {
+  const uint16_t* b_full = nullptr; int r = 0; int kl = 0; int64_t K = 0;
+  int nseg = 1; int64_t seg_end[4] = {0, 0, 0, 0};
+  uint16_t* bt = nullptr;
+};
+// up to four of them in one launch
+lsl_status lora_bt_group_launch(const LoraBt* jobs, int n, hipStream_t s);
 size_t lora_nt_ws_bytes(int64_t T, int64_t K, int kl);
 size_t lora_tn_ws_bytes(int64_t T, int64_t W, int kl);
 // arrival counts a side product of T tokens and output width W (K for NT) may use
