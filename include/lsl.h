@@ -246,7 +246,8 @@ size_t lsl_layer_workspace_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_
  * entries hold the recomputed forward (the down projection's output is not
  * recomputed) and the backward entries the backward's values. They stay valid
  * until the workspace is used again. Backward entries are 0 in mode
- * LSL_MODE_FWD; with the adapters off the t_* entries are not written. */
+ * LSL_MODE_FWD; with the adapters off, or with a t_keep buffer (which then
+ * holds them), the t_* entries are not written. */
 typedef struct {
   /* forward */
   uint64_t n1;        /* bf16 [T x hidden]  rmsnorm(x_in, norm1) */
@@ -279,21 +280,34 @@ typedef struct {
 } lsl_layer_ws_map;
 lsl_status lsl_layer_workspace_map(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq, int32_t mode,
                                    lsl_layer_ws_map* out);
-/* x_in, x_out [batch*seq x hidden] bf16. Nothing is saved: the caller keeps
- * x_in as the layer-boundary checkpoint for the backward. lora may be NULL:
- * the adapters are off and every projection is the frozen base alone (the
- * reference forward of preference training). */
+/* Bytes of a t_keep buffer: the four projections' LoRA products t = x A^T
+ * (q|k|v [T x 3r], o [T x r], gate|up [T x 2r], down [T x r], bf16, each
+ * region 256-byte aligned, in that order), 0 for an invalid cfg. */
+size_t lsl_layer_tkeep_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq);
+/* x_in, x_out [batch*seq x hidden] bf16. The caller keeps x_in as the
+ * layer-boundary checkpoint for the backward ("Exact Layer Streaming ...",
+ * abstract: the layer is recomputed in the backward). lora may be NULL: the
+ * adapters are off and every projection is the frozen base alone (the
+ * reference forward of preference training). t_keep may be NULL; otherwise
+ * (256-byte aligned, lsl_layer_tkeep_bytes bytes, ignored when lora is NULL)
+ * the forward leaves the rank-r products t = x A^T of the four projections
+ * there instead of in the workspace, for decoder_layer_bwd of the same input. */
 lsl_status decoder_layer_fwd(const lsl_layer_cfg* cfg, const void* layer_blob,
                              const lsl_lora_set* lora, const uint16_t* x_in, int32_t batch,
-                             int32_t seq, uint16_t* x_out, void* ws, size_t ws_bytes,
-                             lsl_stream stream);
+                             int32_t seq, uint16_t* x_out, uint16_t* t_keep, void* ws,
+                             size_t ws_bytes, lsl_stream stream);
 /* Recomputes the forward from x_in, then back-propagates dy. dx may be NULL
- * (first layer); adapter gradients are accumulated (+=) into grads. */
+ * (first layer); adapter gradients are accumulated (+=) into grads. With
+ * t_keep (as filled by decoder_layer_fwd for this x_in, lora, cfg, batch and
+ * seq) the recompute takes the products t from there instead of computing
+ * them again; the caller guarantees they are that forward's. The results are
+ * the same bits either way (t is computed by the same launches from the same
+ * bits); only the t_* workspace entries stay unwritten. */
 lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* layer_blob,
                              const lsl_lora_set* lora, const uint16_t* x_in, const uint16_t* dy,
                              int32_t batch, int32_t seq, uint16_t* dx,
-                             const lsl_lora_grads* grads, void* ws, size_t ws_bytes,
-                             lsl_stream stream);
+                             const lsl_lora_grads* grads, const uint16_t* t_keep, void* ws,
+                             size_t ws_bytes, lsl_stream stream);
 
 /* ------------------------------------------------------------------ layer pool
  * Two (or more) HBM slots, each holding one layer blob, filled from the pinned

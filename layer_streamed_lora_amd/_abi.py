@@ -78,9 +78,10 @@ PROTOS = {
     "lsl_layer_layout_get": (i32, [C.POINTER(LayerCfg), C.POINTER(LayerLayout)]),
     "lsl_layer_workspace_bytes": (sz, [C.POINTER(LayerCfg), i32, i32, i32]),
     "lsl_layer_workspace_map": (i32, [C.POINTER(LayerCfg), i32, i32, i32, C.POINTER(LayerWsMap)]),
-    "decoder_layer_fwd": (i32, [C.POINTER(LayerCfg), vp, C.POINTER(LoraSet), vp, i32, i32, vp, vp, sz, vp]),
+    "lsl_layer_tkeep_bytes": (sz, [C.POINTER(LayerCfg), i32, i32]),
+    "decoder_layer_fwd": (i32, [C.POINTER(LayerCfg), vp, C.POINTER(LoraSet), vp, i32, i32, vp, vp, vp, sz, vp]),
     "decoder_layer_bwd": (i32, [C.POINTER(LayerCfg), vp, C.POINTER(LoraSet), vp, vp, i32, i32, vp,
-                                C.POINTER(LoraGrads), vp, sz, vp]),
+                                C.POINTER(LoraGrads), vp, vp, sz, vp]),
     "lsl_pool_create": (i32, [C.POINTER(vp), C.POINTER(vp), i32, sz, vp]),
     "lsl_pool_destroy": (i32, [vp]),
     "load_layer_async": (i32, [vp, i32, vp, sz]),

@@ -121,17 +121,34 @@ static void layout_of(const lsl_layer_cfg* c, lsl_layer_layout* L) {
   L->total_bytes = off;
 }
 
+// The adapter gradients of the four projections (dA and dB each) run as one
+// launch at the end of the backward, product j with its partial slots at
+// ws_off[j] in the partial region (256-byte aligned, one after another) and
+// its arrival counts at cnt_off[j]. Product 2 i is dA of projection
+// 3 - i (dA [kl x k]: W = k), 2 i + 1 its dB (W = n), in the backward's order.
+struct TnPlan {
+  size_t ws_off[9];
+  size_t cnt_off[9];
+};
+static TnPlan tn_plan(const Dims& d) {
+  TnPlan t{};
+  for (int j = 0; j < 8; ++j) {
+    int64_t n, k;
+    const int i = 3 - j / 2;
+    mat_shape(d, i, n, k);
+    const int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
+    const int64_t W = (j & 1) ? n : k;
+    t.ws_off[j + 1] = t.ws_off[j] + align256(lora_tn_ws_bytes(d.T, W, nseg * d.r));
+    t.cnt_off[j + 1] = t.cnt_off[j] + lora_tn_tiles(W);
+  }
+  return t;
+}
+
 // Workspace plan (byte offsets, all 256-aligned).
 // qkv holds the q|k|v GEMM output and qkr its RoPE'd q and k columns (same
 // row stride; the v columns of qkr are unused); in the backward the attention
 // writes dq and dk into dqkr and dv into dqkv, whose q and k columns then take
 // the inverse RoPE of dqkr. So every rounding point keeps its own tensor.
-// workspace of two TN side products launched together (the first's partial
-// slots, 256-byte aligned, then the second's)
-static size_t tn2_ws(int64_t T, int64_t W0, int64_t W1, int kl) {
-  return align256(lora_tn_ws_bytes(T, W0, kl)) + lora_tn_ws_bytes(T, W1, kl);
-}
-
 struct Plan {
   size_t n1, tqkv, qkv, qkr, o, lse, to, h1, n2, tgu, gu, a, td;                    // forward
   size_t ud, da, dgu, ugu, dn2, dh1, uo, dob, dqkr, dqkv, uqkv, dn1, attn_ws, o32;  // backward
@@ -185,9 +202,7 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
     p.bt[LSL_M_GU] = take((size_t)2 * d.r * 2 * d.I * 2);
     p.bt[LSL_M_DOWN] = take((size_t)d.r * d.H * 2);
     part = std::max({part, lora_nt_ws_bytes(d.T, d.NQKV, 3 * r), lora_nt_ws_bytes(d.T, d.H, r),
-                     lora_nt_ws_bytes(d.T, 2 * d.I, 2 * r),
-                     tn2_ws(d.T, d.H, d.NQKV, 3 * r), tn2_ws(d.T, d.Q, d.H, r), tn2_ws(d.T, d.H, 2 * d.I, 2 * r),
-                     tn2_ws(d.T, d.I, d.H, r),
+                     lora_nt_ws_bytes(d.T, 2 * d.I, 2 * r), tn_plan(d).ws_off[8],
                      gemm_split_bytes(d.T, d.H, d.NQKV), gemm_split_bytes(d.T, d.Q, d.H),
                      gemm_split_bytes(d.T, d.H, 2 * d.I), gemm_split_bytes(d.T, d.I, d.H)});
   }
@@ -196,8 +211,7 @@ static Plan plan_of(const lsl_layer_cfg* c, int batch, int seq, int mode) {
   // of their own (zeroed by the layer's first RMSNorm launch, left zero by every
   // launch that uses it; the launches that share it run one after another)
   p.ncnt = std::max({lora_counts_needed(d.T, std::max({d.NQKV, 2 * d.I, d.H, d.Q, d.I})),
-                     lora_tn_tiles(d.H) + lora_tn_tiles(d.NQKV), lora_tn_tiles(d.Q) + lora_tn_tiles(d.H),
-                     lora_tn_tiles(d.H) + lora_tn_tiles(2 * d.I), lora_tn_tiles(d.I) + lora_tn_tiles(d.H),
+                     mode == LSL_MODE_BWD ? tn_plan(d).cnt_off[8] : (size_t)0,
                      gemm_counts_needed(d.T, d.NQKV, d.H), gemm_counts_needed(d.T, d.H, d.Q),
                      gemm_counts_needed(d.T, 2 * d.I, d.H), gemm_counts_needed(d.T, d.H, d.I),
                      gemm_counts_needed(d.T, d.H, d.NQKV), gemm_counts_needed(d.T, d.Q, d.H),
@@ -241,14 +255,16 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
 // Forward of one fused LoRA linear: t = x A^T, y = x W^T + s t B^T (+ res).
 // With y == nullptr only t is computed.
 // dry: only check every launch's conditions (nothing is enqueued).
+// t_ready: t already holds x A^T (kept from the forward of the same input), so
+// only the GEMM runs.
 static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
-                                   int i, const uint16_t* x, uint16_t* t, uint16_t* y, const uint16_t* res,
-                                   float* part, unsigned* cnt, hipStream_t s, bool dry) {
+                                   int i, const uint16_t* x, uint16_t* t, bool t_ready, uint16_t* y,
+                                   const uint16_t* res, float* part, unsigned* cnt, hipStream_t s, bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
   int kl = nseg * d.r;
-  if (lo) {  // adapters on: t = x A^T first, then the GEMM's LoRA K-step
+  if (lo && !t_ready) {  // adapters on: t = x A^T first, then the GEMM's LoRA K-step
     LoraNt nt;
     nt.p = x; nt.ldp = k; nt.T = d.T; nt.K = k; nt.kl = kl; nt.a_full = lo->A[i];
     nt.out = t; nt.ldo = kl; nt.ws = part; nt.cnt = cnt;
@@ -274,12 +290,15 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
 }
 
 // Backward of one fused LoRA linear: u = dy B (per projection); dx = dy W + s u A;
-// dA += s u^T x; dB += s dy^T t (per projection).
+// and the descriptors of dA += s u^T x and dB += s dy^T t (per projection) in
+// tn[0], tn[1], with their partial slots and counts at tws, tcnt (the caller
+// launches them with the other projections').
 // bt: the projection's masked B^T, made beforehand (lora_bt_group_launch)
 static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    const lsl_lora_grads* gr, int i, const uint16_t* x, const uint16_t* t,
                                    const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, unsigned* cnt,
-                                   const uint16_t* bt, hipStream_t s, bool dry) {
+                                   const uint16_t* bt, LoraTn (&tn)[2], float* const (&tws)[2],
+                                   unsigned* const (&tcnt)[2], hipStream_t s, bool dry) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -308,28 +327,28 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
       LSL_TRY(st);
     }
   }
-  // dA and dB in one launch, each with its own partial slots and arrival counts
-  LoraTn ta;
+  LoraTn& ta = tn[0];
+  ta = LoraTn{};
   ta.p = x; ta.ldp = k; ta.q = u; ta.ldq = kl; ta.T = d.T; ta.W = k; ta.kl = kl;
-  ta.scale = c->lora_scale; ta.dA = gr->dA[i]; ta.ws = part; ta.cnt = cnt;
-  LoraTn tb;
+  ta.scale = c->lora_scale; ta.dA = gr->dA[i]; ta.ws = tws[0]; ta.cnt = tcnt[0];
+  LoraTn& tb = tn[1];
+  tb = LoraTn{};
   tb.p = dy; tb.ldp = n; tb.q = t; tb.ldq = kl; tb.T = d.T; tb.W = n; tb.kl = kl;
   tb.scale = c->lora_scale; tb.dB = gr->dB[i]; tb.r = d.r; tb.nseg = nseg;
   for (int q = 0; q < 4; ++q) tb.seg_end[q] = se[q];
-  tb.ws = (float*)((char*)part + align256(lora_tn_ws_bytes(d.T, k, kl)));
-  tb.cnt = cnt + lora_tn_tiles(k);
-  if (dry) {
-    LSL_TRY(lora_tn_check(ta));
-    return lora_tn_check(tb);
-  }
-  return lora_tn2_launch(ta, tb, s);
+  tb.ws = tws[1]; tb.cnt = tcnt[1];
+  LSL_TRY(lora_tn_check(ta));
+  return lora_tn_check(tb);
 }
 
 // dry: check the conditions of every GEMM and side product, enqueue nothing
 // (the other kernels' conditions follow from check_cfg)
+// tp: where the four projections' t = x A^T go (the workspace, or the caller's
+// t_keep buffer); t_ready: they already hold them (the backward's recompute with
+// a t_keep buffer), so the side products are not computed again.
 static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, const lsl_lora_set* lo, const uint16_t* x,
-                                int batch, int seq, uint16_t* out, char* ws, const Plan& p, float* o32, hipStream_t s,
-                                bool dry = false) {
+                                int batch, int seq, uint16_t* out, char* ws, const Plan& p, uint16_t* const (&tp)[4],
+                                bool t_ready, float* o32, hipStream_t s, bool dry = false) {
   Dims d = dims_of(c, batch, seq);
   float* part = (float*)(ws + p.part);
   uint16_t* n1 = (uint16_t*)(ws + p.n1);
@@ -340,27 +359,50 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   uint16_t* gu = (uint16_t*)(ws + p.gu);
   uint16_t* a = (uint16_t*)(ws + p.a);
   unsigned* cnt = (unsigned*)(ws + p.cnt);
+  const bool tr = t_ready;
   if (dry) {
-    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, cnt, s, true));
-    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, cnt, s, true));
-    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, cnt, s, true));
-    return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, cnt, s, true);
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, tp[LSL_M_QKV], tr, qkv, nullptr, part, cnt, s, true));
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, tp[LSL_M_O], tr, h1, x, part, cnt, s, true));
+    LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, tp[LSL_M_GU], tr, gu, nullptr, part, cnt, s, true));
+    return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, tp[LSL_M_DOWN], tr, out, h1, part, cnt, s, true);
   }
   // (also zeroes the arrival counts every later side product of the call uses)
   LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s, cnt, (int)p.ncnt));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, (uint16_t*)(ws + p.tqkv), qkv, nullptr, part, cnt, s, false));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, tp[LSL_M_QKV], tr, qkv, nullptr, part, cnt, s, false));
   // q and k heads are adjacent in each row and share the frequencies: one launch
   uint16_t* qkr = (uint16_t*)(ws + p.qkr);
   LSL_TRY(rope_launch(qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(lsl_attention_fwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, (uint16_t*)(ws + p.to), h1, x, part, cnt, s, false));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, tp[LSL_M_O], tr, h1, x, part, cnt, s, false));
   LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, (uint16_t*)(ws + p.tgu), gu, nullptr, part, cnt, s, false));
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, tp[LSL_M_GU], tr, gu, nullptr, part, cnt, s, false));
   LSL_TRY(swiglu_fwd_launch(gu, d.T, d.I, a, s));
   // out == nullptr (the backward's recompute): the layer output itself is not
   // needed, only the LoRA product t of the down projection (for its dB)
-  return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, (uint16_t*)(ws + p.td), out, h1, part, cnt, s, false);
+  return fused_linear_fwd(c, d, W, lo, LSL_M_DOWN, a, tp[LSL_M_DOWN], tr, out, h1, part, cnt, s, false);
+}
+
+// Byte offsets of the four projections' t (q|k|v, o, gate|up, down: [T x 3r],
+// [T x r], [T x 2r], [T x r] bf16) inside a t_keep buffer; off[4] is its size.
+static void tkeep_offsets(const Dims& d, size_t (&off)[5]) {
+  const int nseg[4] = {3, 1, 2, 1};
+  off[0] = 0;
+  for (int i = 0; i < 4; ++i) off[i + 1] = off[i] + align256((size_t)d.T * nseg[i] * d.r * 2);
+}
+
+// the t pointers of a layer call: the caller's t_keep buffer, or the workspace
+static void t_ptrs(const Dims& d, char* ws, const Plan& p, uint16_t* t_keep, uint16_t* (&tp)[4]) {
+  if (t_keep) {
+    size_t off[5];
+    tkeep_offsets(d, off);
+    for (int i = 0; i < 4; ++i) tp[i] = (uint16_t*)((char*)t_keep + off[i]);
+  } else {
+    tp[LSL_M_QKV] = (uint16_t*)(ws + p.tqkv);
+    tp[LSL_M_O] = (uint16_t*)(ws + p.to);
+    tp[LSL_M_GU] = (uint16_t*)(ws + p.tgu);
+    tp[LSL_M_DOWN] = (uint16_t*)(ws + p.td);
+  }
 }
 
 // Backward with recompute. dry: check every GEMM's and side product's
@@ -368,12 +410,17 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
 // GEMM and the first RMSNorm's backward are skipped, as nothing reads dn1.
 static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, const lsl_lora_set* lora,
                                  const uint16_t* x_in, const uint16_t* dy, int batch, int seq, uint16_t* dx,
-                                 const lsl_lora_grads* grads, char* w, const Plan& p, hipStream_t s, bool dry) {
+                                 const lsl_lora_grads* grads, const uint16_t* t_keep, char* w, const Plan& p,
+                                 hipStream_t s, bool dry) {
   Dims d = dims_of(cfg, batch, seq);
   // recompute the forward up to what the backward reads (every intermediate
-  // except the layer output, whose down-projection GEMM is skipped)
+  // except the layer output, whose down-projection GEMM is skipped; the LoRA
+  // products t too unless the forward kept them)
   uint16_t* dn1 = (uint16_t*)(w + p.dn1);
-  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, (float*)(w + p.o32), s, dry));
+  uint16_t* tp[4];
+  t_ptrs(d, w, p, const_cast<uint16_t*>(t_keep), tp);
+  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, nullptr, w, p, tp, t_keep != nullptr, (float*)(w + p.o32), s,
+                        dry));
   float* part = (float*)(w + p.part);
   unsigned* cnt = (unsigned*)(w + p.cnt);
   uint16_t* qkv = (uint16_t*)(w + p.qkv);
@@ -402,16 +449,31 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
     }
     LSL_TRY(lora_bt_group_launch(jobs, 4, s));
   }
+  // the adapter gradients' descriptors, launched together at the end
+  LoraTn tn[4][2];
+  const TnPlan tnp = tn_plan(d);
+  auto tws = [&](int j) { return (float*)((char*)part + tnp.ws_off[j]); };
+  auto tcnt = [&](int j) { return cnt + tnp.cnt_off[j]; };
+  auto tn_args = [&](int i, float* (&ws2)[2], unsigned* (&c2)[2]) {
+    const int j = 2 * (3 - i);
+    ws2[0] = tws(j); ws2[1] = tws(j + 1); c2[0] = tcnt(j); c2[1] = tcnt(j + 1);
+  };
+  float* twsp[4][2];
+  unsigned* tcp[4][2];
+  for (int i = 0; i < 4; ++i) tn_args(i, twsp[i], tcp[i]);
   // MLP
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_DOWN, (uint16_t*)(w + p.a), (uint16_t*)(w + p.td), dy,
-                           (uint16_t*)(w + p.ud), da, part, cnt, bt[LSL_M_DOWN], s, dry));
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_DOWN, (uint16_t*)(w + p.a), tp[LSL_M_DOWN], dy,
+                           (uint16_t*)(w + p.ud), da, part, cnt, bt[LSL_M_DOWN], tn[0], twsp[LSL_M_DOWN],
+                           tcp[LSL_M_DOWN], s, dry));
   if (!dry) LSL_TRY(swiglu_bwd_launch((uint16_t*)(w + p.gu), da, d.T, d.I, dgu, s));
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), (uint16_t*)(w + p.tgu), dgu,
-                           (uint16_t*)(w + p.ugu), dn2, part, cnt, bt[LSL_M_GU], s, dry));
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), tp[LSL_M_GU], dgu,
+                           (uint16_t*)(w + p.ugu), dn2, part, cnt, bt[LSL_M_GU], tn[1], twsp[LSL_M_GU], tcp[LSL_M_GU],
+                           s, dry));
   if (!dry) LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
   // attention block
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), (uint16_t*)(w + p.to), dh1,
-                           (uint16_t*)(w + p.uo), dob, part, cnt, bt[LSL_M_O], s, dry));
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), tp[LSL_M_O], dh1,
+                           (uint16_t*)(w + p.uo), dob, part, cnt, bt[LSL_M_O], tn[2], twsp[LSL_M_O], tcp[LSL_M_O], s,
+                           dry));
   if (!dry) {
     LSL_TRY(lsl_attention_bwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, (uint16_t*)(w + p.o), dob, (float*)(w + p.lse),
                               (const float*)(w + p.o32), d.NQKV, d.NQKV, d.Q, batch, seq, cfg->n_q, cfg->n_kv, d.d,
@@ -419,9 +481,14 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
     LSL_TRY(rope_launch(dqkr, dqkv, d.T, d.NQKV, cfg->n_q + cfg->n_kv, d.d, seq, cfg->rope_theta, &cfg->rope_scaling,
                         1, s));
   }
-  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), (uint16_t*)(w + p.tqkv), dqkv,
-                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, cnt, bt[LSL_M_QKV], s, dry));
+  LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), tp[LSL_M_QKV], dqkv,
+                           (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, cnt, bt[LSL_M_QKV], tn[3],
+                           twsp[LSL_M_QKV], tcp[LSL_M_QKV], s, dry));
   if (dx && !dry) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
+  // dA and dB of all four projections in one launch: their inputs (the layer's
+  // activations, the u and t products and the output gradients) all stay in
+  // the workspace (or are the caller's dy) until the call ends
+  if (!dry) LSL_TRY(lora_tn_group_launch(&tn[0][0], 8, s));
   return LSL_OK;
 }
 
@@ -474,35 +541,48 @@ static lsl_status check_layer_call(const char* fn, const lsl_layer_cfg* cfg, con
   return LSL_OK;
 }
 
+extern "C" size_t lsl_layer_tkeep_bytes(const lsl_layer_cfg* cfg, int32_t batch, int32_t seq) {
+  if (check_cfg(cfg, "lsl_layer_tkeep_bytes") != LSL_OK || batch < 0 || seq < 0) return 0;
+  size_t off[5];
+  tkeep_offsets(dims_of(cfg, batch, seq), off);
+  return off[4];
+}
+
 extern "C" lsl_status decoder_layer_fwd(const lsl_layer_cfg* cfg, const void* layer_blob, const lsl_lora_set* lora,
-                                        const uint16_t* x_in, int32_t batch, int32_t seq, uint16_t* x_out, void* ws,
-                                        size_t ws_bytes, lsl_stream stream) {
+                                        const uint16_t* x_in, int32_t batch, int32_t seq, uint16_t* x_out,
+                                        uint16_t* t_keep, void* ws, size_t ws_bytes, lsl_stream stream) {
   const char* fn = "decoder_layer_fwd";
   LSL_TRY(check_layer_call(fn, cfg, layer_blob, lora, batch, seq, ws, ws_bytes, LSL_MODE_FWD));
+  if (t_keep && !aligned(t_keep, 256)) return set_error(LSL_ERR_INVALID_ARG, "%s: t_keep not 256-byte aligned", fn);
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x_in, x_out}));
   Plan p = plan_of(cfg, batch, seq, LSL_MODE_FWD);
   const LayerPtrs W = ptrs_of(cfg, layer_blob);
-  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, x_out, (char*)ws, p, nullptr, (hipStream_t)stream, true));
-  return layer_forward(cfg, W, lora, x_in, batch, seq, x_out, (char*)ws, p, nullptr, (hipStream_t)stream);
+  uint16_t* tp[4];
+  t_ptrs(dims_of(cfg, batch, seq), (char*)ws, p, lora ? t_keep : nullptr, tp);
+  const hipStream_t s = (hipStream_t)stream;
+  LSL_TRY(layer_forward(cfg, W, lora, x_in, batch, seq, x_out, (char*)ws, p, tp, false, nullptr, s, true));
+  return layer_forward(cfg, W, lora, x_in, batch, seq, x_out, (char*)ws, p, tp, false, nullptr, s);
 }
 
 extern "C" lsl_status decoder_layer_bwd(const lsl_layer_cfg* cfg, const void* layer_blob, const lsl_lora_set* lora,
                                         const uint16_t* x_in, const uint16_t* dy, int32_t batch, int32_t seq,
-                                        uint16_t* dx, const lsl_lora_grads* grads, void* ws, size_t ws_bytes,
-                                        lsl_stream stream) {
+                                        uint16_t* dx, const lsl_lora_grads* grads, const uint16_t* t_keep, void* ws,
+                                        size_t ws_bytes, lsl_stream stream) {
   const char* fn = "decoder_layer_bwd";
   LSL_TRY(check_layer_call(fn, cfg, layer_blob, lora, batch, seq, ws, ws_bytes, LSL_MODE_BWD));
   if (!grads) return set_error(LSL_ERR_INVALID_ARG, "%s: grads is NULL", fn);
   for (int i = 0; i < 4; ++i) LSL_TRY(check_ptrs(fn, {grads->dA[i], grads->dB[i]}));
+  if (t_keep && !aligned(t_keep, 256)) return set_error(LSL_ERR_INVALID_ARG, "%s: t_keep not 256-byte aligned", fn);
   if ((int64_t)batch * seq == 0) return LSL_OK;
   LSL_TRY(check_ptrs(fn, {x_in, dy}));
   if (dx && !aligned(dx, 16)) return set_error(LSL_ERR_INVALID_ARG, "%s: dx misaligned", fn);
   const Plan p = plan_of(cfg, batch, seq, LSL_MODE_BWD);
   const LayerPtrs W = ptrs_of(cfg, layer_blob);
+  const hipStream_t s = (hipStream_t)stream;
   // every launch's conditions first, so that a rejected call enqueues nothing
-  LSL_TRY(layer_backward(cfg, W, lora, x_in, dy, batch, seq, dx, grads, (char*)ws, p, (hipStream_t)stream, true));
-  return layer_backward(cfg, W, lora, x_in, dy, batch, seq, dx, grads, (char*)ws, p, (hipStream_t)stream, false);
+  LSL_TRY(layer_backward(cfg, W, lora, x_in, dy, batch, seq, dx, grads, t_keep, (char*)ws, p, s, true));
+  return layer_backward(cfg, W, lora, x_in, dy, batch, seq, dx, grads, t_keep, (char*)ws, p, s, false);
 }
 
 static void timing_free() {

@@ -228,14 +228,17 @@ LSL_DEV int tn_qrow(int tid, int rr) {
   return 8 * (qq >> 3) + ((qq >> 1) & 3) + 4 * (qq & 1) + 32 * rr;
 }
 
-// Up to two products in one launch (the adapter gradients dA and dB of one
-// projection need no ordering between them): grid = tiles0 S0 + tiles1 S1
-// workgroups in one dimension, workgroup b < tiles0 S0 taking tile b % tiles0,
-// split b / tiles0 of product 0, the rest likewise of product 1; each product
-// has its own partial slots and arrival counts.
+// Up to TN_GROUP_MAX products in one launch (the adapter gradients dA and dB of
+// a layer's projections need no ordering among them): grid = the sum of tiles_i
+// S_i workgroups in one dimension, product i taking workgroups [start_i,
+// start_i + tiles_i S_i), workgroup start_i + b tile b % tiles_i, split b /
+// tiles_i; each product has its own partial slots and arrival counts.
+constexpr int TN_GROUP_MAX = 8;
 struct TnGroup {
-  TnArgs p[2];
-  int tiles[2];
+  TnArgs p[TN_GROUP_MAX];
+  int tiles[TN_GROUP_MAX];
+  int start[TN_GROUP_MAX];
+  int n;
 };
 // 4 waves, wave w owns columns a = 32w..32w+31 of the tile.
 // BUF: the split's rows are read through buffer descriptors (its bytes below
@@ -245,10 +248,10 @@ __global__ __launch_bounds__(256) void lora_tn_kernel(const TnGroup grp) {
   __shared__ __attribute__((aligned(16))) uint16_t Ps[64 * TN_LDP];  // [t][a]
   __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * TN_LDQ];  // [t][j]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = grp.tiles[0] * grp.p[0].S;
-  const int pi = (int)blockIdx.x < n0 ? 0 : 1;  // (uniform in the workgroup)
+  int pi = 0;  // (uniform in the workgroup)
+  while (pi + 1 < grp.n && (int)blockIdx.x >= grp.start[pi + 1]) ++pi;
   const TnArgs& a = grp.p[pi];
-  const int bi = (int)blockIdx.x - (pi ? n0 : 0);
+  const int bi = (int)blockIdx.x - grp.start[pi];
   const int tile = bi % grp.tiles[pi], split = bi / grp.tiles[pi], ntiles = grp.tiles[pi];
   const int64_t a0 = (int64_t)tile * 128;
   const int64_t tbeg = (int64_t)split * a.t_per_split;
@@ -518,23 +521,29 @@ static TnArgs tn_args(const LoraTn& d, int& tiles, bool& buf) {
   return a;
 }
 
-static lsl_status tn_group_launch(TnGroup& g, int n, bool buf, hipStream_t s) {
-  const int64_t blocks = (int64_t)g.tiles[0] * g.p[0].S + (n > 1 ? (int64_t)g.tiles[1] * g.p[1].S : 0);
-  if (blocks >= ((int64_t)1 << 31)) return set_error(LSL_ERR_UNSUPPORTED, "lora grad: too many tiles");
+lsl_status lora_tn_group_launch(const LoraTn* d, int n, hipStream_t s) {
+  if (n < 0 || n > TN_GROUP_MAX) return set_error(LSL_ERR_INVALID_ARG, "lora grad: 0..%d products", TN_GROUP_MAX);
+  for (int i = 0; i < n; ++i) LSL_TRY(lora_tn_check(d[i]));
+  TnGroup g{};
+  bool buf = true;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].W == 0 || d[i].T == 0) continue;
+    bool b;
+    g.p[g.n] = tn_args(d[i], g.tiles[g.n], b);
+    buf = buf && b;
+    g.start[g.n] = (int)blocks;
+    blocks += (int64_t)g.tiles[g.n] * g.p[g.n].S;
+    if (blocks >= ((int64_t)1 << 31)) return set_error(LSL_ERR_UNSUPPORTED, "lora grad: too many tiles");
+    ++g.n;
+  }
+  if (g.n == 0) return LSL_OK;
   if (buf) hipLaunchKernelGGL((lora_tn_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   else hipLaunchKernelGGL((lora_tn_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, g);
   return check_launch("lora_tn");
 }
 
-lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) {
-  if (d.W == 0) return LSL_OK;
-  LSL_TRY(lora_tn_check(d));
-  if (d.T == 0) return LSL_OK;
-  TnGroup g{};
-  bool buf;
-  g.p[0] = tn_args(d, g.tiles[0], buf);
-  return tn_group_launch(g, 1, buf, s);
-}
+lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s) { return lora_tn_group_launch(&d, 1, s); }
 
 size_t lora_tn_tiles(int64_t W) { return (size_t)((W + 127) / 128); }
 
@@ -556,15 +565,8 @@ lsl_status lora_bt_group_launch(const LoraBt* jobs, int n, hipStream_t s) {
 }
 
 lsl_status lora_tn2_launch(const LoraTn& d0, const LoraTn& d1, hipStream_t s) {
-  LSL_TRY(lora_tn_check(d0));
-  LSL_TRY(lora_tn_check(d1));
-  if (d0.W == 0 || d0.T == 0) return lora_tn_launch(d1, s);
-  if (d1.W == 0 || d1.T == 0) return lora_tn_launch(d0, s);
-  TnGroup g{};
-  bool b0, b1;
-  g.p[0] = tn_args(d0, g.tiles[0], b0);
-  g.p[1] = tn_args(d1, g.tiles[1], b1);
-  return tn_group_launch(g, 2, b0 && b1, s);
+  const LoraTn d[2] = {d0, d1};
+  return lora_tn_group_launch(d, 2, s);
 }
 
 }  // namespace lsl

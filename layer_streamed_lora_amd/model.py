@@ -165,23 +165,31 @@ def layer_workspace_map(cfg, batch, seq, mode):
     return {n: int(getattr(m, n)) for n in _abi.WS_MAP_FIELDS}
 
 
-def decoder_layer_fwd(cfg, blob, lora_set, x, batch, seq, out=None, ws=None, stream=None):
-    """lora_set None: adapters off (the frozen base alone)."""
+def layer_tkeep_bytes(cfg, batch, seq):
+    """Bytes of a buffer that keeps the layer forward's LoRA products t for its backward."""
+    return int(lib().lsl_layer_tkeep_bytes(C.byref(cfg), batch, seq))
+
+
+def decoder_layer_fwd(cfg, blob, lora_set, x, batch, seq, out=None, ws=None, t_keep=None, stream=None):
+    """lora_set None: adapters off (the frozen base alone). t_keep: optional
+    uint8 device buffer of layer_tkeep_bytes that receives the products t."""
     if out is None:
         out = torch.empty_like(x)
     if ws is None:
         ws = torch.empty(layer_workspace_bytes(cfg, batch, seq, _abi.MODE_FWD), dtype=torch.uint8, device=x.device)
     lo = None if lora_set is None else C.byref(lora_set)
     _check("decoder_layer_fwd", lib().decoder_layer_fwd(C.byref(cfg), _p(blob), lo, _p(x), batch, seq,
-                                                        _p(out), _p(ws), ws.numel(), _s(stream)))
+                                                        _p(out), _p(t_keep), _p(ws), ws.numel(), _s(stream)))
     return out
 
 
-def decoder_layer_bwd(cfg, blob, lora_set, x, dy, batch, seq, grads, dx=True, ws=None, stream=None):
+def decoder_layer_bwd(cfg, blob, lora_set, x, dy, batch, seq, grads, dx=True, ws=None, t_keep=None, stream=None):
+    """t_keep: the buffer decoder_layer_fwd of the same x filled (the recompute
+    then takes t from it), or None (t recomputed)."""
     dxt = torch.empty_like(x) if dx is True else dx
     if ws is None:
         ws = torch.empty(layer_workspace_bytes(cfg, batch, seq, _abi.MODE_BWD), dtype=torch.uint8, device=x.device)
     _check("decoder_layer_bwd", lib().decoder_layer_bwd(C.byref(cfg), _p(blob), C.byref(lora_set), _p(x), _p(dy),
-                                                        batch, seq, _p(dxt), C.byref(grads), _p(ws), ws.numel(),
-                                                        _s(stream)))
+                                                        batch, seq, _p(dxt), C.byref(grads), _p(t_keep), _p(ws),
+                                                        ws.numel(), _s(stream)))
     return dxt

@@ -23,7 +23,7 @@ import numpy as np
 import torch
 
 from . import _abi
-from .model import LoraParams, layer_cfg, layer_layout, write_layer_blob, layer_workspace_bytes
+from .model import LoraParams, layer_cfg, layer_layout, write_layer_blob, layer_workspace_bytes, layer_tkeep_bytes
 from .ops import lib, _check, _p, _s, embed_fwd, rmsnorm_fwd, rmsnorm_bwd, fused_ce_loss_fwd, fused_ce_loss_bwd
 from .ops import ce_workspace_bytes, adamw_step
 
@@ -108,7 +108,10 @@ class StreamedLoraModel:
     mode: "streamed" (pinned host store + 2-slot pool) or "resident" (all
     blobs in HBM). Both share the same blob bytes, adapters and kernels."""
 
-    def __init__(self, shape, n_layers, vocab, tied, batch, seq, mode="streamed", device="cuda"):
+    def __init__(self, shape, n_layers, vocab, tied, batch, seq, mode="streamed", device="cuda", keep_t=True):
+        """keep_t: each layer's forward keeps its LoRA products t (rank-r per
+        token and projection) for the backward's recompute, which then skips
+        computing them again (the same bits either way)."""
         assert mode in ("streamed", "resident")
         self.shape, self.n_layers, self.vocab, self.tied = shape, n_layers, vocab, tied
         self.batch, self.seq, self.T = batch, seq, batch * seq
@@ -135,6 +138,8 @@ class StreamedLoraModel:
         self.ws = torch.empty(max(layer_workspace_bytes(self.cfg, batch, seq, _abi.MODE_BWD),
                                   ce_workspace_bytes(T, H, vocab), 256), dtype=torch.uint8, device=device)
         self.lse = torch.empty(T, dtype=torch.float32, device=device)
+        tk = layer_tkeep_bytes(self.cfg, batch, seq)  # a multiple of 256: every row stays aligned
+        self.tkeep = torch.empty((n_layers, tk), dtype=torch.uint8, device=device) if keep_t else None
         self.step_count = 0
         self.slot_layer = [None, None]
         self._released = [False, False]
@@ -198,6 +203,9 @@ class StreamedLoraModel:
         self.h2d_bytes += self.blob_bytes
         self.loads += 1
 
+    def _tkeep(self, layer):
+        return None if self.tkeep is None else self.tkeep[layer].data_ptr()
+
     def _done(self, slot):
         if slot is not None:
             self.pool.release(slot)
@@ -225,7 +233,7 @@ class StreamedLoraModel:
             ptr, slot = self._blob_ptr_for_visit(visits, i)
             _check("decoder_layer_fwd", lib().decoder_layer_fwd(
                 C.byref(cfg), ptr, C.byref(self.lora.lora_set(i)), _p(self.ckpt[i]), self.batch, self.seq,
-                _p(self.ckpt[i + 1]), _p(self.ws), self.ws.numel(), _s(stream)))
+                _p(self.ckpt[i + 1]), self._tkeep(i), _p(self.ws), self.ws.numel(), _s(stream)))
             self._done(slot)
         eps = self.shape.rms_eps
         _check("lsl_rmsnorm_fwd", lib().lsl_rmsnorm_fwd(_p(self.ckpt[L]), _p(self.final_norm), T, H, eps,
@@ -248,8 +256,8 @@ class StreamedLoraModel:
             dx = self.dh[1 - cur] if layer > 0 else None
             _check("decoder_layer_bwd", lib().decoder_layer_bwd(
                 C.byref(cfg), ptr, C.byref(self.lora.lora_set(layer)), _p(self.ckpt[layer]), _p(self.dh[cur]),
-                self.batch, self.seq, _p(dx), C.byref(self.lora.lora_grads(layer)), _p(self.ws), self.ws.numel(),
-                _s(stream)))
+                self.batch, self.seq, _p(dx), C.byref(self.lora.lora_grads(layer)), self._tkeep(layer), _p(self.ws),
+                self.ws.numel(), _s(stream)))
             self._done(slot)
             cur = 1 - cur
 
@@ -275,8 +283,8 @@ class StreamedLoraModel:
                 # ping-pong between two checkpoint rows: only the last hidden state is needed
                 src, dst = self.ckpt[i % 2], self.ckpt[(i + 1) % 2]
                 _check("decoder_layer_fwd", lib().decoder_layer_fwd(
-                    C.byref(cfg), ptr, None, _p(src), self.batch, self.seq, _p(dst), _p(self.ws), self.ws.numel(),
-                    _s(stream)))
+                    C.byref(cfg), ptr, None, _p(src), self.batch, self.seq, _p(dst), None, _p(self.ws),
+                    self.ws.numel(), _s(stream)))
                 self._done(slot)
             _check("lsl_rmsnorm_fwd", lib().lsl_rmsnorm_fwd(_p(self.ckpt[L % 2]), _p(self.final_norm), T, H,
                                                             self.shape.rms_eps, _p(self.hn), _s(stream)))

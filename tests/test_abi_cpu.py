@@ -47,7 +47,7 @@ def test_codebook_matches_oracle_bitwise(L):
 
 
 def test_abi_version(L):
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
 
 
 def _status(L, name, *args):
@@ -261,11 +261,20 @@ def test_size_limits_rejected_before_any_launch(L):
     cfg = M.layer_cfg(LLAMA8B_LAYER)
     lo = _abi.LoraSet((C.c_void_p * 4)(*[256] * 4), (C.c_void_p * 4)(*[256] * 4))
     gr = _abi.LoraGrads((C.c_void_p * 4)(*[256] * 4), (C.c_void_p * 4)(*[256] * 4))
-    assert lib.decoder_layer_fwd(C.byref(cfg), 256, C.byref(lo), 256, 1, 160000, 256, 256, big, None) == \
+    assert lib.decoder_layer_fwd(C.byref(cfg), 256, C.byref(lo), 256, 1, 160000, 256, None, 256, big, None) == \
         _abi.LSL_ERR_UNSUPPORTED
     assert b"4 GiB" in lib.lsl_last_error()
-    assert lib.decoder_layer_bwd(C.byref(cfg), 256, C.byref(lo), 256, 256, 1, 160000, 256, C.byref(gr), 256, big,
-                                 None) == _abi.LSL_ERR_UNSUPPORTED
+    assert lib.decoder_layer_bwd(C.byref(cfg), 256, C.byref(lo), 256, 256, 1, 160000, 256, C.byref(gr), None, 256,
+                                 big, None) == _abi.LSL_ERR_UNSUPPORTED
+    # a t_keep buffer must be 256-byte aligned (checked before anything else is looked at)
+    assert lib.decoder_layer_fwd(C.byref(cfg), 256, C.byref(lo), 256, 1, 16, 256, 272, 256, big, None) == \
+        _abi.LSL_ERR_INVALID_ARG
+    assert b"t_keep" in lib.lsl_last_error()
+    assert lib.decoder_layer_bwd(C.byref(cfg), 256, C.byref(lo), 256, 256, 1, 16, 256, C.byref(gr), 272, 256,
+                                 big, None) == _abi.LSL_ERR_INVALID_ARG
+    # its size: the four projections' products [T x 3r | r | 2r | r] bf16, regions 256-byte aligned
+    T, r = 300, LLAMA8B_LAYER.lora_r
+    assert M.layer_tkeep_bytes(cfg, 1, T) == sum((T * k * r * 2 + 255) // 256 * 256 for k in (3, 1, 2, 1))
 
 
 @pytest.mark.parametrize("mode", [0, 1])

@@ -114,6 +114,38 @@ def test_layer_deterministic_and_address_independent(gpu):
         assert torch.equal(outs[0], outs[i]) and torch.equal(dxs[0], dxs[i]) and torch.equal(grads[0], grads[i])
 
 
+@pytest.mark.parametrize("shape,batch,seq", [(SMALL_LAYER_NF4, 2, 40), (LLAMA8B_LAYER, 1, 1024)])
+def test_layer_kept_t_gives_the_same_bits(gpu, shape, batch, seq):
+    """A backward whose recompute takes the LoRA products t kept by the forward
+    (t_keep) gives the same bits as one that computes them again: dx, every
+    adapter gradient, and the kept t equal the workspace's recomputed t."""
+    from layer_streamed_lora_amd import _abi
+    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 47)
+    X, DY = dev_bf16(x), dev_bf16(dy)
+    tk = torch.full((M.layer_tkeep_bytes(cfg, batch, seq),), 0xFF, dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(M.layer_workspace_bytes(cfg, batch, seq, _abi.MODE_BWD), dtype=torch.uint8, device="cuda")
+    out0 = M.decoder_layer_fwd(cfg, blob, lp.lora_set(0), X, batch, seq)
+    out1 = M.decoder_layer_fwd(cfg, blob, lp.lora_set(0), X, batch, seq, t_keep=tk)
+    res = []
+    for keep in (None, tk):
+        lp.grad.zero_()
+        dx = M.decoder_layer_bwd(cfg, blob, lp.lora_set(0), X, DY, batch, seq, lp.lora_grads(0), ws=wsb, t_keep=keep)
+        res.append((dx, lp.grad.clone()))
+        if keep is None:  # the recomputed t of this workspace, to compare with the kept ones
+            m = M.layer_workspace_map(cfg, batch, seq, _abi.MODE_BWD)
+            T, r = batch * seq, shape.lora_r
+            t_ws = [wsb[m[n]:m[n] + T * k * r * 2].clone() for n, k in (("t_qkv", 3), ("t_o", 1), ("t_gu", 2),
+                                                                          ("t_down", 1))]
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    off = 0
+    for t, k in zip(t_ws, (3, 1, 2, 1)):
+        assert torch.equal(tk[off:off + t.numel()], t)
+        off += (t.numel() + 255) // 256 * 256
+    assert off == tk.numel()
+
+
 def test_layer_zero_b_gives_zero_dA(gpu):
     shape, batch, seq = SMALL_LAYER_BF16, 1, 64
     M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 44)

@@ -22,9 +22,9 @@ SMALL_NF4_SCALED = LayerShape(128, 2, 1, 64, 192, 1e-5, 500000.0, "nf4", 8, 16.0
                               rope_scaling=(8.0, 1.0, 4.0, 32.0))
 
 
-def build(shape, n_layers, vocab, tied, batch, seq, mode, wid):
+def build(shape, n_layers, vocab, tied, batch, seq, mode, wid, keep_t=True):
     from layer_streamed_lora_amd.trainer import StreamedLoraModel
-    m = StreamedLoraModel(shape, n_layers, vocab, tied, batch, seq, mode=mode)
+    m = StreamedLoraModel(shape, n_layers, vocab, tied, batch, seq, mode=mode, keep_t=keep_t)
     weights, loras = [], []
     for l in range(n_layers):
         w = synth.layer_weights(shape, wid, l, ones_norm=False)
@@ -82,14 +82,19 @@ def test_streamed_equals_resident_small(gpu, shape):
     n_layers, vocab, batch, seq, n_micro = 4, 640, 2, 64, 3
     s, *_ = build(shape, n_layers, vocab, False, batch, seq, "streamed", 71)
     r, *_ = build(shape, n_layers, vocab, False, batch, seq, "resident", 71)
+    # the backward recomputing the LoRA products t instead of taking them from
+    # the forward: the same bits
+    n, *_ = build(shape, n_layers, vocab, False, batch, seq, "streamed", 71, keep_t=False)
     for step in range(2):
         chunks = ids_for(vocab, batch, seq, n_micro, 71 + step)
         ls = s.step(s.prepare_inputs(chunks))
         lr = r.step(r.prepare_inputs(chunks))
+        ln = n.step(n.prepare_inputs(chunks))
         torch.cuda.synchronize()
-        assert torch.equal(ls, lr)
+        assert torch.equal(ls, lr) and torch.equal(ls, ln)
         assert torch.equal(s.ckpt, r.ckpt) and torch.equal(s.lse, r.lse)
         _assert_same_state(s, r)
+        _assert_same_state(s, n)
     # every layer's adapters received gradient (no severed path)
     for l in range(n_layers):
         for i in range(4):
@@ -297,10 +302,11 @@ def test_empty_inputs_are_no_ops(gpu):
     ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     for batch, seq in ((0, 16), (2, 0)):
         assert lib().decoder_layer_fwd(C.byref(cfg), blob.data_ptr(), C.byref(lp.lora_set(0)), sentinel.data_ptr(),
-                                       batch, seq, sentinel.data_ptr(), ws.data_ptr(), ws.numel(), None) == _abi.LSL_OK
+                                       batch, seq, sentinel.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                       None) == _abi.LSL_OK
         assert lib().decoder_layer_bwd(C.byref(cfg), blob.data_ptr(), C.byref(lp.lora_set(0)), sentinel.data_ptr(),
                                        sentinel.data_ptr(), batch, seq, sentinel.data_ptr(),
-                                       C.byref(lp.lora_grads(0)), ws.data_ptr(), ws.numel(), None) == _abi.LSL_OK
+                                       C.byref(lp.lora_grads(0)), None, ws.data_ptr(), ws.numel(), None) == _abi.LSL_OK
     loss = torch.full((1,), 5.0, dtype=torch.float32, device="cuda")
     w = torch.zeros((64, shape.hidden), dtype=torch.bfloat16, device="cuda")
     assert lib().fused_ce_loss_fwd(None, w.data_ptr(), None, 0, shape.hidden, 64, -100, loss.data_ptr(), None,
