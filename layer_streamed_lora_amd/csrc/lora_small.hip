@@ -405,7 +405,10 @@ __global__ void zero_u32_kernel(unsigned* __restrict__ p, int n) {
 // ---------------------------------------------------------------- host side
 // NT: K split so that about NT_TARGET workgroups run (at most NT_MAX_S splits,
 // at least one 64-wide step per wave)
-constexpr int64_t NT_TARGET = 384, NT_MAX_S = 16;
+#ifndef LSL_NT_TARGET
+#define LSL_NT_TARGET 384
+#endif
+constexpr int64_t NT_TARGET = LSL_NT_TARGET, NT_MAX_S = 16;
 static void nt_plan(int64_t T, int64_t K, int& S, int& steps) {
   const int64_t tiles = (T + 63) / 64, KT = K / 64;
   S = 1;
@@ -426,7 +429,10 @@ static int nt_splits(int64_t T, int64_t K) {
 
 // TN: splits of T so that about TN_TARGET workgroups run, each taking at least
 // TN_MIN_STEPS 64-token steps
-constexpr int64_t TN_TARGET = 256, TN_MIN_STEPS = 4;
+#ifndef LSL_TN_TARGET
+#define LSL_TN_TARGET 256
+#endif
+constexpr int64_t TN_TARGET = LSL_TN_TARGET, TN_MIN_STEPS = 4;
 static int tn_splits(int64_t W, int64_t T) {
   const int64_t tiles = (W + 127) / 128;
   const int64_t steps = (T + 63) / 64;

@@ -110,6 +110,15 @@ def test_linear_workspace_covers_stream_k_and_u(L):
     assert lib.lsl_lora_linear_bwd_u_offset(0, n_out, k_in) == 0
 
 
+def test_linear_workspace_split_k(L):
+    """A 64-row-tile GEMM with its reduction split (300 tokens of a 6144 x 4096
+    projection: 3 x 96 tiles, 2 splits) needs the splits' float32 partials,
+    not stream-K slots."""
+    T, n_out, k_in = 300, 6144, 4096
+    ws = L.lora_linear_workspace_bytes(T, n_out, k_in, 16)
+    assert 2 * T * n_out * 4 <= ws < 2 * T * n_out * 4 + (1 << 20)
+
+
 def test_nf4dq_validation(L):
     from layer_streamed_lora_amd import _abi
     lib = L.lib()

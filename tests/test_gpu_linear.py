@@ -153,6 +153,7 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
 @pytest.mark.parametrize("T,fin,fout,r,fmt", [
     (1024, 12288, 2112, 16, "nf4"),   # stream-K forward, split side products
     (300, 16384, 4096, 16, "bf16"),   # ragged tokens, stream-K both ways
+    (1024, 4096, 4096, 16, "nf4"),    # 64-row tiles, reduction split 3 ways (the o projection's shape)
 ])
 def test_split_partials_do_not_leak_between_calls(gpu, T, fin, fout, r, fmt):
     """Two calls with different inputs on one workspace: the second call's
