@@ -1488,8 +1488,27 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
 #endif
 static_assert(LSL_SK_G % 8 == 0, "stream-K workgroups are dealt to 8 XCDs");
 static_assert(LSL_BIG_MIN_TILES <= LSL_SK_G, "stream-K takes fewer tiles than workgroups");
+// Split-K in the large tile: a GEMM of at least 1024 tokens with too few tiles
+// for either of the above takes S = SK_G / tiles reduction splits (at least
+// BIG_KSPLIT_MIN_STEPS K-steps each) when that fills at least BIG_MIN_TILES
+// workgroups; each split's float32 partial is summed in split order by
+// gemm_split_reduce, which reads them with the whole chip. At 1024 tokens of
+// the Llama-8B layer: the o projection, forward and input gradient (64 tiles,
+// four splits of 16 K-steps).
+#ifndef LSL_BIG_KSPLIT_MIN_STEPS
+#define LSL_BIG_KSPLIT_MIN_STEPS 8
+#endif
+static int big_ksplit(int64_t M, int64_t tiles, int64_t K) {
+  if (tiles <= 0 || M < 1024) return 1;
+  int64_t S = LSL_SK_G / tiles;
+  const int64_t KT = K / BK;
+  if (S > KT / LSL_BIG_KSPLIT_MIN_STEPS) S = KT / LSL_BIG_KSPLIT_MIN_STEPS;
+  if (S < 2 || tiles * S < LSL_BIG_MIN_TILES) return 1;
+  const int64_t per = (KT + S - 1) / S;
+  return (int)((KT + per - 1) / per);
+}
 // 0: the 64-row tiles; 1: the large tile, one workgroup per tile; -1: the
-// large tile, stream-K over LSL_SK_G workgroups
+// large tile, stream-K over LSL_SK_G workgroups; 2: the large tile, split-K
 static int gemm_big_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
   if (tiles == 0) return 0;
@@ -1499,7 +1518,8 @@ static int gemm_big_plan(int64_t M, int64_t N, int64_t K) {
   if (tiles < LSL_BIG_MIN_TILES && units >= (int64_t)LSL_SK_MIN_STEPS * LSL_SK_G &&
       units * LSL_SK_G < ((int64_t)1 << 31))
     return -1;
-  return tiles >= LSL_BIG_MIN_TILES ? 1 : 0;
+  if (tiles >= LSL_BIG_MIN_TILES) return 1;
+  return big_ksplit(M, tiles, K) > 1 ? 2 : 0;
 }
 
 size_t gemm_counts_needed(int64_t M, int64_t N, int64_t K) {
@@ -1527,6 +1547,15 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s,
   a.kt_per_split = (int)(d.K / BK);
   a.sk_g = 0;
   dim3 grid((unsigned)(a.tiles_m * a.tiles_n));
+  if (plan == 2) {
+    const int S = big_ksplit(d.M, (int64_t)a.tiles_m * a.tiles_n, d.K);
+    const int KT = (int)(d.K / BK);
+    if (!d.split_ws) return set_error(LSL_ERR_WORKSPACE, "gemm: split-K scratch missing");
+    a.kt_per_split = (KT + S - 1) / S;
+    a.ksplit = (KT + a.kt_per_split - 1) / a.kt_per_split;
+    a.spart = d.split_ws;
+    grid = dim3((unsigned)(a.tiles_m * a.tiles_n * a.ksplit));
+  }
   if (plan == -1) {
     // at most two segments per workgroup (the kernel keeps two pending sums)
     if ((int64_t)a.tiles_m * a.tiles_n >= LSL_SK_G)
@@ -1545,6 +1574,11 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s,
   } else {
     if (d.kn) launch_big<LSL_WFMT_BF16, true>(a, d.lora, s, grid);
     else launch_big<LSL_WFMT_BF16, false>(a, d.lora, s, grid);
+  }
+  if (a.ksplit > 1) {
+    const int64_t n4 = d.M * d.N / 4;
+    hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
+                       a.ksplit, d.M, d.N, d.bias, d.res, d.ldres, d.y, d.ldy);
   }
   return check_launch("gemm(256 x 256 tiles)");
 }
@@ -1638,7 +1672,9 @@ int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t steps = K / BK;
   if (tiles == 0) return 1;  // empty output
-  if (gemm_big_plan(M, N, K) != 0) return 1;  // the large tile has no separate reduction pass
+  const int plan = gemm_big_plan(M, N, K);
+  if (plan == 2) return big_ksplit(M, ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN), K);
+  if (plan != 0) return 1;  // the large tile, unsplit or stream-K: no separate reduction pass
   int64_t S = (LSL_SPLIT_TARGET + tiles - 1) / tiles;
   if (S > steps / LSL_SPLIT_MIN_STEPS) S = steps / LSL_SPLIT_MIN_STEPS;
   if (S < 2) return 1;

@@ -114,6 +114,10 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1024, 12288, 2112, 16, "nf4"),   # ragged weight rows (last tile 64 of 256), 27 steps per workgroup
     (512, 16384, 4096, 16, "bf16"),   # 32 steps per workgroup: forward tiles split exactly 8 ways;
                                       # input gradient two whole tiles per workgroup, nothing split
+    # from 1024 tokens, too few tiles for stream-K: large tiles with the reduction
+    # split so that the splits fill the chip, partials summed by the reduce kernel
+    (1100, 4096, 4096, 16, "nf4dq"),  # 5 x 16 = 80 tiles, three splits of 22 K-steps, ragged tokens
+    (1024, 2048, 4096, 16, "bf16"),   # forward 64 tiles x 4 splits, input gradient 32 tiles x 8 splits
 ])
 def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
     x, dy, w, a, b, s = _linear_case(T, fin, fout, r, 2.0 * r, 1, fmt)
@@ -153,7 +157,7 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
 @pytest.mark.parametrize("T,fin,fout,r,fmt", [
     (1024, 12288, 2112, 16, "nf4"),   # stream-K forward, split side products
     (300, 16384, 4096, 16, "bf16"),   # ragged tokens, stream-K both ways
-    (1024, 4096, 4096, 16, "nf4"),    # 64-row tiles, reduction split 3 ways (the o projection's shape)
+    (1024, 4096, 4096, 16, "nf4"),    # the o projection's shape: large tiles, reduction split 4 ways
 ])
 def test_split_partials_do_not_leak_between_calls(gpu, T, fin, fout, r, fmt):
     """Two calls with different inputs on one workspace: the second call's
