@@ -13,9 +13,10 @@ and the layer output likewise); there the oracle rounds at both points too, and
 the bound adds 2e-2 times the first sum's magnitude, the scale of its rounding
 error (where x and the projection cancel, the output is far smaller).
 The Llama-3.1-8B layer runs at seq 512
-and at 1024 tokens, the dispatch the benchmark times (the forward of q|k|v, o
-and the down projection and all four input gradients in stream-K large tiles,
-the gate|up forward one large tile per workgroup)."""
+and at 1024 tokens, the dispatch the benchmark times (q|k|v and down forward and
+the q|k|v and gate|up input gradients in stream-K large tiles, the o projection
+both ways in large tiles with a split reduction, the gate|up forward and the
+down input gradient one large tile per workgroup)."""
 import dataclasses
 
 import numpy as np
