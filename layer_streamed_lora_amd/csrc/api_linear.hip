@@ -6,9 +6,11 @@
 #include "api_util.h"
 #include <mutex>
 
-// bytes of the allocation-free forward's scratch: 88 MiB, the largest stream-K
-// partials of a Llama-3.1-8B projection at 1024 tokens (q|k|v: 351 slots of
-// 256 KiB), plus 64 KiB for the arrival counts
+// bytes of the allocation-free forward's scratch: 88 MiB, the largest forward
+// partials of a Llama-3.1-8B projection up to 1024 tokens (q|k|v just below 1024
+// tokens: 351 stream-K slots of 256 KiB; from 1024 tokens the split partials
+// of o and down, four of 1024 x 4096 floats, take 64 MiB), plus 64 KiB for the
+// arrival counts
 #ifndef LSL_NOALLOC_SCRATCH_BYTES
 #define LSL_NOALLOC_SCRATCH_BYTES ((88u << 20) + (64u << 10))
 #endif

@@ -1470,16 +1470,18 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
 #define LSL_BIG_MIN_TILES 192
 #endif
 // Stream-K in the large tile: when the tiles fill less than BIG_MIN_TILES of
-// the SK_G workgroups (one per CU), the reduction steps of all tiles are dealt
-// out evenly to SK_G workgroups instead, as long as each gets at least
-// SK_MIN_STEPS steps. Each split tile costs a float32 partial per segment (256
-// KiB, written and read back once through one CU), about 30 us per launch in
-// all; at 1024 tokens of the Llama-8B layer that pays off from about 20 steps
-// per workgroup: q|k|v forward 89 -> 87 us and input gradient 92 -> 82 us
-// (24 steps each), against 65 -> 75 us for the o projection (16 steps), which
-// keeps the 64-row tiles with split-K, and 138 -> 160 us for the down
-// projection's input gradient (224 tiles), which keeps one tile per workgroup.
-// SK_G is the CU count of MI355X, so that the plan depends on the GEMM's shape only.
+// the SK_G workgroups (one per CU) and split-K (below) does not apply, the
+// reduction steps of all tiles are dealt out evenly to SK_G workgroups instead,
+// as long as each gets at least SK_MIN_STEPS steps. Each split tile costs a
+// float32 partial per segment (256 KiB, written and read back once through one
+// CU), about 30 us per launch in all. Measured at 1024 tokens of the Llama-8B
+// layer before split-K existed: q|k|v forward 89 -> 87 us and input gradient
+// 92 -> 82 us (24 steps each) against the 64-row tiles, but 65 -> 75 us for the
+// o projection (16 steps) and 138 -> 160 us for the down projection's input
+// gradient (224 tiles, one per workgroup). Since then it serves shapes below
+// 1024 tokens (the Llama-8B layer at 512 tokens: the down forward and the
+// gate|up and down input gradients). SK_G is the CU count of MI355X, so that
+// the plan depends on the GEMM's shape only.
 #ifndef LSL_SK_G
 #define LSL_SK_G 256
 #endif
@@ -1488,13 +1490,16 @@ void gemm_tile_shape(int64_t M, int64_t N, int& bn, int& bm) {
 #endif
 static_assert(LSL_SK_G % 8 == 0, "stream-K workgroups are dealt to 8 XCDs");
 static_assert(LSL_BIG_MIN_TILES <= LSL_SK_G, "stream-K takes fewer tiles than workgroups");
-// Split-K in the large tile: a GEMM of at least 1024 tokens with too few tiles
-// for either of the above takes S = SK_G / tiles reduction splits (at least
+// Split-K in the large tile: a GEMM of at least 1024 tokens with fewer than
+// BIG_MIN_TILES tiles takes S = SK_G / tiles reduction splits (at least
 // BIG_KSPLIT_MIN_STEPS K-steps each) when that fills at least BIG_MIN_TILES
 // workgroups; each split's float32 partial is summed in split order by
-// gemm_split_reduce, which reads them with the whole chip. At 1024 tokens of
-// the Llama-8B layer: the o projection, forward and input gradient (64 tiles,
-// four splits of 16 K-steps).
+// gemm_split_reduce, which reads them with the whole chip. This comes before
+// stream-K: at 1024 tokens of the Llama-8B layer (A/B on one box, HIP events)
+// the down forward went 159 -> 142 us, the q|k|v input gradient 83 -> 79 us and
+// the gate|up input gradient 254 -> 248 us against stream-K, and the o
+// projection 69.6 -> 66.5 us forward (69.2 -> 64.3 us input gradient) against
+// the 64-row tiles.
 #ifndef LSL_BIG_KSPLIT_MIN_STEPS
 #define LSL_BIG_KSPLIT_MIN_STEPS 8
 #endif
@@ -1512,14 +1517,13 @@ static int big_ksplit(int64_t M, int64_t tiles, int64_t K) {
 static int gemm_big_plan(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
   if (tiles == 0) return 0;
+  if (tiles >= LSL_BIG_MIN_TILES) return 1;
+  if (big_ksplit(M, tiles, K) > 1) return 2;
   const int64_t units = tiles * (K / BK);
   // (fewer tiles than workgroups: a workgroup's units span at most two tiles;
   // units * SK_G < 2^31 keeps the kernel's unit arithmetic in 32 bits)
-  if (tiles < LSL_BIG_MIN_TILES && units >= (int64_t)LSL_SK_MIN_STEPS * LSL_SK_G &&
-      units * LSL_SK_G < ((int64_t)1 << 31))
-    return -1;
-  if (tiles >= LSL_BIG_MIN_TILES) return 1;
-  return big_ksplit(M, tiles, K) > 1 ? 2 : 0;
+  if (units >= (int64_t)LSL_SK_MIN_STEPS * LSL_SK_G && units * LSL_SK_G < ((int64_t)1 << 31)) return -1;
+  return 0;
 }
 
 size_t gemm_counts_needed(int64_t M, int64_t N, int64_t K) {

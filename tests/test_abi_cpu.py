@@ -98,11 +98,11 @@ def test_workspace_sizes_are_deterministic(L):
 
 def test_linear_workspace_covers_stream_k_and_u(L):
     """A GEMM with fewer 256 x 256 output tiles than the 256 stream-K
-    workgroups (1024 tokens of a 6144 x 4096 projection: 96 tiles) keeps one
+    workgroups (1000 tokens of a 6144 x 4096 projection: 96 tiles) keeps one
     float32 tile of partials per slot, 256 + 96 - 1 slots; the backward's u
     [T x r] region lies inside the workspace, 256-byte aligned."""
     lib = L.lib()
-    T, n_out, k_in, r = 1024, 6144, 4096, 16
+    T, n_out, k_in, r = 1000, 6144, 4096, 16
     ws = L.lora_linear_workspace_bytes(T, n_out, k_in, r)
     assert ws >= (256 + 96 - 1) * 256 * 256 * 4
     off = lib.lsl_lora_linear_bwd_u_offset(T, n_out, k_in)

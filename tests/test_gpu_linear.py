@@ -105,17 +105,22 @@ def _linear_case(T, fin, fout, r, alpha, wid, fmt, b_zero=False):
     (1024, 24576, 64, 8, "bf16"),
     (1, 64, 98304, 8, "nf4"),
     (1, 98304, 64, 8, "bf16"),
-    # fewer than 192 large tiles but at least 20 x 256 K-steps in all: stream-K
-    # over 256 workgroups, split tiles summed by the last arrival (the forward
-    # here; the input gradient has 192 tiles or more, one per workgroup)
-    (1024, 14336, 2048, 16, "nf4"),
-    (1100, 12288, 2048, 16, "nf4dq"),
+    # below 1024 tokens, fewer than 192 large tiles but at least 20 x 256 K-steps
+    # in all: stream-K over 256 workgroups, split tiles summed by the last
+    # arrival (the forward here; the input gradient has 192 tiles or more, one
+    # per workgroup)
+    (1000, 14336, 2048, 16, "nf4"),
+    (900, 12288, 2048, 16, "nf4dq"),
     (1000, 2048, 14336, 8, "bf16"),   # the input gradient in stream-K, ragged tokens
-    (1024, 12288, 2112, 16, "nf4"),   # ragged weight rows (last tile 64 of 256), 27 steps per workgroup
+    (900, 12288, 2112, 16, "nf4"),    # ragged weight rows (last tile 64 of 256), 27 steps per workgroup
     (512, 16384, 4096, 16, "bf16"),   # 32 steps per workgroup: forward tiles split exactly 8 ways;
                                       # input gradient two whole tiles per workgroup, nothing split
-    # from 1024 tokens, too few tiles for stream-K: large tiles with the reduction
-    # split so that the splits fill the chip, partials summed by the reduce kernel
+    # from 1024 tokens the same kind of shapes take large tiles with the
+    # reduction split so that the splits fill the chip, partials summed in
+    # split order by the reduce kernel
+    (1024, 14336, 2048, 16, "nf4"),   # 32 tiles x 8 splits of 28 K-steps
+    (1100, 12288, 2048, 16, "nf4dq"), # 40 tiles x 6 splits, ragged tokens
+    (1024, 12288, 2112, 16, "nf4"),   # ragged weight rows, 36 tiles x 7 splits
     (1100, 4096, 4096, 16, "nf4dq"),  # 5 x 16 = 80 tiles, three splits of 22 K-steps, ragged tokens
     (1024, 2048, 4096, 16, "bf16"),   # forward 64 tiles x 4 splits, input gradient 32 tiles x 8 splits
 ])
@@ -155,7 +160,7 @@ def test_lora_linear_parity(gpu, T, fin, fout, r, fmt):
 
 
 @pytest.mark.parametrize("T,fin,fout,r,fmt", [
-    (1024, 12288, 2112, 16, "nf4"),   # stream-K forward, split side products
+    (1000, 12288, 2112, 16, "nf4"),   # stream-K forward, split side products
     (300, 16384, 4096, 16, "bf16"),   # ragged tokens, stream-K both ways
     (1024, 4096, 4096, 16, "nf4"),    # the o projection's shape: large tiles, reduction split 4 ways
 ])
@@ -193,7 +198,8 @@ def test_split_partials_do_not_leak_between_calls(gpu, T, fin, fout, r, fmt):
     (200, 320, 448, 16, "bf16"),      # ragged, unsplit GEMM
     (64, 4096, 512, 16, "nf4"),       # few output tiles: split-K path, bias added in the split reduce
     (1100, 256, 24576, 16, "nf4"),    # 256 x 256 tiles
-    (1024, 14336, 2048, 16, "nf4"),   # stream-K: the bias added by the last arrival
+    (1000, 14336, 2048, 16, "nf4"),   # stream-K: the bias added by the last arrival
+    (1024, 14336, 2048, 16, "nf4"),   # large tiles, split reduction: the bias added in the reduce
 ])
 def test_lora_linear_bias(gpu, T, fin, fout, r, fmt):
     """A frozen bias joins the forward sum before its single rounding; the
