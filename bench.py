@@ -432,7 +432,7 @@ def hbm_kernels(shape, ms):
         ("lsl::rmsnorm_bwd_kernel", 4 * T * H * 2 + 2 * H, "x, dy, residual gradient read, dx written"),
         ("lsl::swiglu_fwd_kernel", 3 * T * I * 2, "gate|up read, a written"),
         ("lsl::swiglu_bwd_kernel", 5 * T * I * 2, "gate|up and da read, dgate|dup written"),
-        ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2 // 2, "q or k heads read, rotated copy written (mean of the two)"),
+        ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2, "q and k heads read, rotated copy written (one launch)"),
         ("lsl::adamw_kernel", n_params * (4 * 4 + 3 * 4 + 2), "master, grad, m, v read; master, m, v, bf16 copy written"),
     ]
 
@@ -660,6 +660,53 @@ def summarize_ce_bytes(fetch_dir, write_dir, args):
     print(json.dumps(doc, indent=1))
 
 
+def summarize_hbm_bytes(fetch_dir, write_dir, args):
+    """HBM bytes per dispatch of the layer's bandwidth-bound kernels from two
+    rocprofv3 --pmc runs of `--layer-only --calib-copy` (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), scaled by what the same counters read for the
+    calibration copy, beside each kernel's algorithmic bytes; with --trace-dir
+    (a kernel-trace run of the same shapes) also the counter bytes over the
+    kernel's average duration. Prints a markdown table."""
+    wl, shape, ms = workload(args.workload)
+    kernels = [k for k in hbm_kernels(shape, ms) if "adamw" not in k[0]]
+    kernels.append(("lsl::gemm_split_reduce", None, "split partials read, bf16 result written"))
+    got = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _rows(_find(d, "*counter_collection.csv")) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "neg_kernel" in r["Kernel_Name"]
+                and _grid_items(r) >= 1 << 20]
+        if not copy:
+            sys.exit(f"{counter}: no calibration copy dispatch")
+        scale = (CALIB_MIB << 20) / (sum(copy) / len(copy) * 1024.0)
+        for prefix, _, _ in kernels:
+            vals = [float(r["Counter_Value"]) * 1024.0 * scale for r in rows if r["Kernel_Name"].startswith(prefix)]
+            if vals:
+                got.setdefault(prefix, {})[counter] = (sum(vals) / len(vals), len(vals), scale)
+    durs = {}
+    if args.trace_dir:
+        trace = _rows(_find(args.trace_dir, "*kernel_trace.csv"))
+        for prefix, _, _ in kernels:
+            ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace
+                  if r["Kernel_Name"].startswith(prefix)]
+            if ds:
+                durs[prefix] = sum(ds) / len(ds)
+    out = ["| kernel | dispatches | read MB | written MB | HBM MB per dispatch | algorithmic MB | "
+           "HBM / algorithmic | trace avg us | HBM GB/s | of 8 TB/s |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for prefix, alg, what in kernels:
+        g = got.get(prefix)
+        if not g or "FETCH_SIZE" not in g or "WRITE_SIZE" not in g:
+            continue
+        rd, wr = g["FETCH_SIZE"][0], g["WRITE_SIZE"][0]
+        tot = rd + wr
+        avg = durs.get(prefix)
+        gbs = tot / (avg * 1e-6) / 1e9 if avg else None
+        out.append(f"| `{prefix}` | {g['FETCH_SIZE'][1]} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {tot / 1e6:.1f} | "
+                   + (f"{alg / 1e6:.1f} | {tot / alg:.2f}" if alg else "- | -") + " | "
+                   + (f"{avg:.1f} | {gbs:.0f} | {gbs / 8000:.2f}" if avg else "- | - | -") + " |")
+    print("\n".join(out))
+
+
 def summarize_pmc(dirs, args):
     """Per-kernel averages of the hardware counters of one or more `rocprofv3
     --pmc` runs of this library's kernels (one row per kernel name and grid,
@@ -749,6 +796,10 @@ def main():
                     help="time the fused cross-entropy of the workload's head (for counters), then exit")
     ap.add_argument("--summarize-ce-bytes", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="HBM bytes per logit element of two --ce-only --pmc runs, then exit")
+    ap.add_argument("--summarize-hbm-bytes", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="HBM bytes of the layer's bandwidth-bound kernels from two --pmc runs of "
+                         "--layer-only --calib-copy, and exit")
+    ap.add_argument("--trace-dir", metavar="DIR", help="kernel-trace run for --summarize-hbm-bytes durations")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="per-kernel averages of rocprofv3 --pmc runs (markdown), then exit")
     ap.add_argument("--cus", type=int, default=256, help="compute units, for --summarize-pmc")
@@ -759,6 +810,8 @@ def main():
         return summarize_pmc(args.summarize_pmc, args)
     if args.summarize_ce_bytes:
         return summarize_ce_bytes(*args.summarize_ce_bytes, args)
+    if args.summarize_hbm_bytes:
+        return summarize_hbm_bytes(*args.summarize_hbm_bytes, args)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace, args)
     if args.summarize_copies:
