@@ -441,6 +441,9 @@ def summarize_trace(d, args):
     """Markdown summary of a `rocprofv3 --kernel-trace --stats -f csv` run: the
     top kernels by total time, and the timed GEMM's dispatches (by grid)."""
     wl, shape, ms = workload(args.workload)
+    if args.trace_tokens:  # the run's tokens per layer visit, in sequences of the workload's length
+        import dataclasses
+        ms = dataclasses.replace(ms, batch=args.trace_tokens // ms.seq)
     stats = _rows(_find(d, "*kernel_stats.csv"))
     out = ["| kernel | calls | total ms | avg us | % |", "|---|---:|---:|---:|---:|"]
     for r in stats[:25]:
@@ -800,6 +803,8 @@ def main():
                     help="HBM bytes of the layer's bandwidth-bound kernels from two --pmc runs of "
                          "--layer-only --calib-copy, and exit")
     ap.add_argument("--trace-dir", metavar="DIR", help="kernel-trace run for --summarize-hbm-bytes durations")
+    ap.add_argument("--trace-tokens", type=int, default=0,
+                    help="tokens per layer visit of the run --summarize-trace reads (default: the workload's)")
     ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
                     help="per-kernel averages of rocprofv3 --pmc runs (markdown), then exit")
     ap.add_argument("--cus", type=int, default=256, help="compute units, for --summarize-pmc")
