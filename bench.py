@@ -428,8 +428,10 @@ def hbm_kernels(shape, ms):
     nq, nkv, d = shape.n_q, shape.n_kv, shape.head_dim
     n_params = ms.n_layers * sum(shape.lora_r * (fin + fout) for fin, fout in PROJ_IN_OUT(shape).values())
     return [
-        ("lsl::rmsnorm_fwd_kernel", 2 * T * H * 2 + 2 * H, "x read, y written, bf16 [T x H]"),
-        ("lsl::rmsnorm_bwd_kernel", 4 * T * H * 2 + 2 * H, "x, dy, residual gradient read, dx written"),
+        ("void lsl::rmsnorm_fwd_kernel<false>", 2 * T * H * 2 + 2 * H, "x read, y written, bf16 [T x H]"),
+        ("void lsl::rmsnorm_bwd_kernel<false>", 4 * T * H * 2 + 2 * H, "x, dy, residual gradient read, dx written"),
+        ("void lsl::rmsnorm_fwd_kernel<true>", None, "split partials and residual read, h and y written"),
+        ("void lsl::rmsnorm_bwd_kernel<true>", None, "split partials, x, residual gradient read, dy and dx written"),
         ("lsl::swiglu_fwd_kernel", 3 * T * I * 2, "gate|up read, a written"),
         ("lsl::swiglu_bwd_kernel", 5 * T * I * 2, "gate|up and da read, dgate|dup written"),
         ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2, "q and k heads read, rotated copy written (one launch)"),
@@ -484,6 +486,9 @@ def summarize_trace(d, args):
         if not ds:
             continue
         avg = sum(ds) / len(ds)
+        if nbytes is None:  # bytes depend on the split count: see --summarize-hbm-bytes
+            out.append(f"| `{prefix}` | {len(ds)} | {avg:.1f} | - | - | - | {what} |")
+            continue
         gbs = nbytes / (avg * 1e-6) / 1e9
         out.append(f"| `{prefix}` | {len(ds)} | {avg:.1f} | {nbytes:,} | {gbs:.0f} | {gbs / 8000:.2f} | {what} |")
     print("\n".join(out))

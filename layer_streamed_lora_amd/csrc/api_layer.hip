@@ -257,9 +257,11 @@ static LayerPtrs ptrs_of(const lsl_layer_cfg* c, const void* blob) {
 // dry: only check every launch's conditions (nothing is enqueued).
 // t_ready: t already holds x A^T (kept from the forward of the same input), so
 // only the GEMM runs.
+// defer: a split GEMM leaves its float32 partials in part for the caller to sum.
 static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const LayerPtrs& W, const lsl_lora_set* lo,
                                    int i, const uint16_t* x, uint16_t* t, bool t_ready, uint16_t* y,
-                                   const uint16_t* res, float* part, unsigned* cnt, hipStream_t s, bool dry) {
+                                   const uint16_t* res, float* part, unsigned* cnt, hipStream_t s, bool dry,
+                                   bool defer = false) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -280,7 +282,7 @@ static lsl_status fused_linear_fwd(const lsl_layer_cfg* c, const Dims& d, const 
   else if (i == LSL_M_GU) { g.seg_end[0] = d.I; g.seg_end[1] = 2 * d.I; }
   else g.seg_end[0] = n;
   g.scale = c->lora_scale;
-  g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part; g.cnt = cnt;
+  g.y = y; g.ldy = n; g.res = res; g.ldres = n; g.split_ws = part; g.cnt = cnt; g.defer_reduce = defer;
   if (i == LSL_M_QKV) g.bias = W.qkv_bias;
   if (dry) return gemm_check(g);
   timing_mark(1 + i, true, s);
@@ -298,7 +300,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
                                    const lsl_lora_grads* gr, int i, const uint16_t* x, const uint16_t* t,
                                    const uint16_t* dy, uint16_t* u, uint16_t* dx, float* part, unsigned* cnt,
                                    const uint16_t* bt, LoraTn (&tn)[2], float* const (&tws)[2],
-                                   unsigned* const (&tcnt)[2], hipStream_t s, bool dry) {
+                                   unsigned* const (&tcnt)[2], hipStream_t s, bool dry, bool defer = false) {
   int64_t n, k;
   mat_shape(d, i, n, k);
   int nseg = i == LSL_M_QKV ? 3 : (i == LSL_M_GU ? 2 : 1);
@@ -317,7 +319,7 @@ static lsl_status fused_linear_bwd(const lsl_layer_cfg* c, const Dims& d, const 
     g.wb = W.wb[i]; g.wq = W.wq[i]; g.wa = W.wa[i]; g.wq8 = W.wq8[i]; g.wsc = W.wsc[i];
     g.M = d.T; g.N = k; g.K = n;
     g.lora = 2; g.la = u; g.ldla = kl; g.kl = kl; g.lb = lo->A[i]; g.r = d.r;
-    g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part; g.cnt = cnt;
+    g.scale = c->lora_scale; g.y = dx; g.ldy = k; g.split_ws = part; g.cnt = cnt; g.defer_reduce = defer;
     if (dry) {
       LSL_TRY(gemm_check(g));
     } else {
@@ -374,8 +376,12 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   LSL_TRY(rope_launch(qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(lsl_attention_fwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, tp[LSL_M_O], tr, h1, x, part, cnt, s, false));
-  LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
+  // a split o projection's partials are summed (with the residual) by the
+  // second RMSNorm, which writes h1 and n2
+  const int so = gemm_splits(d.T, d.H, d.Q);
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_O, o, tp[LSL_M_O], tr, h1, x, part, cnt, s, false, so > 1));
+  if (so > 1) LSL_TRY(rmsnorm_fwd_split_launch(part, so, nullptr, x, d.H, h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
+  else LSL_TRY(rmsnorm_fwd_launch(h1, W.norm2, d.T, d.H, c->rms_eps, n2, s));
   LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_GU, n2, tp[LSL_M_GU], tr, gu, nullptr, part, cnt, s, false));
   LSL_TRY(swiglu_fwd_launch(gu, d.T, d.I, a, s));
   // out == nullptr (the backward's recompute): the layer output itself is not
@@ -466,10 +472,16 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
                            (uint16_t*)(w + p.ud), da, part, cnt, bt[LSL_M_DOWN], tn[0], twsp[LSL_M_DOWN],
                            tcp[LSL_M_DOWN], s, dry));
   if (!dry) LSL_TRY(swiglu_bwd_launch((uint16_t*)(w + p.gu), da, d.T, d.I, dgu, s));
+  // a split input-gradient GEMM's partials are summed by the RMSNorm backward
+  // that follows it, which writes the GEMM's output (dn2, dn1) and its own
+  const int sgu = gemm_splits(d.T, d.H, 2 * d.I), sqkv = gemm_splits(d.T, d.H, d.NQKV);
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_GU, (uint16_t*)(w + p.n2), tp[LSL_M_GU], dgu,
                            (uint16_t*)(w + p.ugu), dn2, part, cnt, bt[LSL_M_GU], tn[1], twsp[LSL_M_GU], tcp[LSL_M_GU],
-                           s, dry));
-  if (!dry) LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
+                           s, dry, sgu > 1));
+  if (!dry && sgu > 1)
+    LSL_TRY(rmsnorm_bwd_split_launch((uint16_t*)(w + p.h1), W.norm2, part, sgu, dy, d.T, d.H, cfg->rms_eps, dn2, dh1, s));
+  else if (!dry)
+    LSL_TRY(rmsnorm_bwd_launch((uint16_t*)(w + p.h1), W.norm2, dn2, dy, d.T, d.H, cfg->rms_eps, dh1, s));
   // attention block
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_O, (uint16_t*)(w + p.o), tp[LSL_M_O], dh1,
                            (uint16_t*)(w + p.uo), dob, part, cnt, bt[LSL_M_O], tn[2], twsp[LSL_M_O], tcp[LSL_M_O], s,
@@ -483,8 +495,11 @@ static lsl_status layer_backward(const lsl_layer_cfg* cfg, const LayerPtrs& W, c
   }
   LSL_TRY(fused_linear_bwd(cfg, d, W, lora, grads, LSL_M_QKV, (uint16_t*)(w + p.n1), tp[LSL_M_QKV], dqkv,
                            (uint16_t*)(w + p.uqkv), dx ? dn1 : nullptr, part, cnt, bt[LSL_M_QKV], tn[3],
-                           twsp[LSL_M_QKV], tcp[LSL_M_QKV], s, dry));
-  if (dx && !dry) LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
+                           twsp[LSL_M_QKV], tcp[LSL_M_QKV], s, dry, sqkv > 1));
+  if (dx && !dry && sqkv > 1)
+    LSL_TRY(rmsnorm_bwd_split_launch(x_in, W.norm1, part, sqkv, dh1, d.T, d.H, cfg->rms_eps, dn1, dx, s));
+  else if (dx && !dry)
+    LSL_TRY(rmsnorm_bwd_launch(x_in, W.norm1, dn1, dh1, d.T, d.H, cfg->rms_eps, dx, s));
   // dA and dB of all four projections in one launch: their inputs (the layer's
   // activations, the u and t products and the output gradients) all stay in
   // the workspace (or are the caller's dy) until the call ends

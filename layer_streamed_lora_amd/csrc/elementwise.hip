@@ -3,108 +3,221 @@
 // row for the row reductions (wave64 shuffles, no LDS), 16-byte accesses.
 #include "common.h"
 #include "small.h"
+#include "api_util.h"
 #include <cmath>
 
 namespace lsl {
 
 // ---------------------------------------------------------------- RMSNorm
-// One wave per row. The forward holds the lane's 16-byte chunks of the row
-// (chunk c of lane L covers columns 8 (L + 64 c) .. + 7) in registers, so the
-// row is read from HBM once and all of its loads are in flight together (rows
-// up to 512 RMS_CHUNKS columns).
-constexpr int RMS_CHUNKS = 16;
+// One workgroup of RMS_THREADS threads per row. Thread t holds the row's
+// 16-byte chunks t, t + 256, ... (columns 8 (t + 256 k) .. + 7, rows up to
+// 256 * 8 * RMS_CHUNKS columns) in registers, so all of the row's loads are in
+// flight together. Row sums are taken per thread in chunk order, then over the
+// wave (butterfly), then over the four waves in wave order through LDS: the same
+// order in every RMSNorm kernel here, so a kernel that reads its input as split
+// partials gives the bits of the plain one.
+constexpr int RMS_THREADS = 256, RMS_CHUNKS = 4;
 
-// y = bf16(x * r * w), r = 1 / sqrt(mean(x^2) + eps)
-__global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          int64_t T, int64_t H, float eps, uint16_t* __restrict__ y,
-                                                          unsigned* __restrict__ zero, int nzero) {
-  if (blockIdx.x == 0)  // side job: zero the caller's nzero words
+LSL_DEV float row_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float t = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();  // red is written again by the next sum
+  return t;
+}
+
+// The split-K sum of a GEMM's output fused into the RMSNorm that reads it.
+// Eight columns of a row: the float32 partials of the S splits ([S][T][H] at
+// part) added in split order, the bias added, rounded to bf16, the residual
+// added and rounded again: the arithmetic of gemm_split_reduce, so the bf16
+// values are the ones that kernel stores.
+LSL_DEV u32x4 split_sum8(const float* __restrict__ part, int S, int64_t TH, int64_t off,
+                         const uint16_t* __restrict__ bias, const uint16_t* __restrict__ res, int64_t col) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(part + off), b = *reinterpret_cast<const f32x4*>(part + off + 4);
+  for (int sp = 1; sp < S; ++sp) {
+    const f32x4 p = *reinterpret_cast<const f32x4*>(part + sp * TH + off);
+    const f32x4 q = *reinterpret_cast<const f32x4*>(part + sp * TH + off + 4);
+    a = f32x4{a[0] + p[0], a[1] + p[1], a[2] + p[2], a[3] + p[3]};
+    b = f32x4{b[0] + q[0], b[1] + q[1], b[2] + q[2], b[3] + q[3]};
+  }
+  float e[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  if (bias) {
+    const u32x4 bb = *reinterpret_cast<const u32x4*>(bias + col);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { e[2 * j] += lo_bf(bb[j]); e[2 * j + 1] += hi_bf(bb[j]); }
+  }
+  if (res) {
+    const u32x4 rr = *reinterpret_cast<const u32x4*>(res);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[2 * j] = bf2f(f2bf(e[2 * j])) + lo_bf(rr[j]);
+      e[2 * j + 1] = bf2f(f2bf(e[2 * j + 1])) + hi_bf(rr[j]);
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack2(e[2 * j], e[2 * j + 1]);
+  return o;
+}
+
+// Where an RMSNorm kernel takes its input row: a bf16 tensor, or (SPLIT) the
+// split-K partials of the GEMM before it, summed as gemm_split_reduce would
+// (+ bias, + res) and written to `out` as that kernel would store them.
+struct RmsIn {
+  const uint16_t* x;                                  // bf16 [T x H] (not SPLIT)
+  const float* part; int S;                           // SPLIT: float32 [S][T][H]
+  const uint16_t* bias; const uint16_t* res; int64_t ldres;
+  uint16_t* out;                                      // SPLIT: the summed bf16 [T x H]
+};
+template <bool SPLIT>
+LSL_DEV u32x4 rms_load(const RmsIn& in, int64_t T, int64_t H, int64_t row, int64_t col) {
+  if constexpr (SPLIT) {
+    const u32x4 v = split_sum8(in.part, in.S, T * H, row * H + col, in.bias,
+                               in.res ? in.res + row * in.ldres + col : nullptr, col);
+    *reinterpret_cast<u32x4*>(in.out + row * H + col) = v;
+    return v;
+  } else {
+    return *reinterpret_cast<const u32x4*>(in.x + row * H + col);
+  }
+}
+
+// y = bf16(x * r * w), r = 1 / sqrt(mean(x^2) + eps). Side job of workgroup 0:
+// zero the caller's nzero words.
+template <bool SPLIT>
+__global__ __launch_bounds__(RMS_THREADS) void rmsnorm_fwd_kernel(const RmsIn in, const uint16_t* __restrict__ w,
+                                                                  int64_t T, int64_t H, float eps,
+                                                                  uint16_t* __restrict__ y, unsigned* __restrict__ zero,
+                                                                  int nzero) {
+  __shared__ float red[4];
+  if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0u;
-  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
-  if (row >= T) return;
-  const uint16_t* xr = x + row * H;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
   u32x4 v[RMS_CHUNKS];
 #pragma unroll
-  for (int c = 0; c < RMS_CHUNKS; ++c) {
-    const int64_t col = (int64_t)(lane + 64 * c) * 8;
-    if (col < H) v[c] = *reinterpret_cast<const u32x4*>(xr + col);
+  for (int k = 0; k < RMS_CHUNKS; ++k) {
+    const int64_t col = (int64_t)(tid + RMS_THREADS * k) * 8;
+    if (col < H) v[k] = rms_load<SPLIT>(in, T, H, row, col);
   }
   float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < RMS_CHUNKS; ++c)
-    if ((int64_t)(lane + 64 * c) * 8 < H)
+  for (int k = 0; k < RMS_CHUNKS; ++k)
+    if ((int64_t)(tid + RMS_THREADS * k) * 8 < H)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { float a = lo_bf(v[c][j]), b = hi_bf(v[c][j]); ss += a * a + b * b; }
-  ss = wave_sum(ss);
-  float r = 1.0f / sqrtf(ss / (float)H + eps);
+      for (int j = 0; j < 4; ++j) { float a = lo_bf(v[k][j]), b = hi_bf(v[k][j]); ss += a * a + b * b; }
+  ss = row_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
-  for (int c = 0; c < RMS_CHUNKS; ++c) {
-    const int64_t col = (int64_t)(lane + 64 * c) * 8;
+  for (int k = 0; k < RMS_CHUNKS; ++k) {
+    const int64_t col = (int64_t)(tid + RMS_THREADS * k) * 8;
     if (col >= H) continue;
-    u32x4 g = *reinterpret_cast<const u32x4*>(w + col);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(w + col);
     u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = pack2(lo_bf(v[c][j]) * r * lo_bf(g[j]), hi_bf(v[c][j]) * r * hi_bf(g[j]));
+    for (int j = 0; j < 4; ++j) o[j] = pack2(lo_bf(v[k][j]) * r * lo_bf(g[j]), hi_bf(v[k][j]) * r * hi_bf(g[j]));
     *reinterpret_cast<u32x4*>(y + row * H + col) = o;
   }
 }
 
-// dx = bf16(dres + r (w dy - x r^2 sum(x w dy) / H)). Two passes over the row
-// (the second from L2): holding x and dy in registers would halve occupancy.
-__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                          const uint16_t* __restrict__ dy, const uint16_t* __restrict__ dres,
-                                                          int64_t T, int64_t H, float eps, uint16_t* __restrict__ dx) {
-  int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
-  if (row >= T) return;
-  const uint16_t* xr = x + row * H;
-  const uint16_t* dr = dy + row * H;
+// dx = bf16(dres + r (w dy - x r^2 sum(x w dy) / H)); the row's x and dy chunks
+// stay in registers between the two passes.
+template <bool SPLIT>
+__global__ __launch_bounds__(RMS_THREADS) void rmsnorm_bwd_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ w, const RmsIn dyin,
+                                                                  const uint16_t* __restrict__ dres, int64_t T,
+                                                                  int64_t H, float eps, uint16_t* __restrict__ dx) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  u32x4 xv[RMS_CHUNKS], dv[RMS_CHUNKS];
   float ss = 0.f, sd = 0.f;
-  for (int64_t c = lane * 8; c < H; c += 512) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    u32x4 g = *reinterpret_cast<const u32x4*>(w + c);
-    u32x4 d = *reinterpret_cast<const u32x4*>(dr + c);
+#pragma unroll
+  for (int k = 0; k < RMS_CHUNKS; ++k) {
+    const int64_t c = (int64_t)(tid + RMS_THREADS * k) * 8;
+    if (c >= H) continue;
+    xv[k] = *reinterpret_cast<const u32x4*>(x + row * H + c);
+    dv[k] = rms_load<SPLIT>(dyin, T, H, row, c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(w + c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float a = lo_bf(v[j]), b = hi_bf(v[j]);
+      const float a = lo_bf(xv[k][j]), b = hi_bf(xv[k][j]);
       ss += a * a + b * b;
-      sd += a * lo_bf(g[j]) * lo_bf(d[j]) + b * hi_bf(g[j]) * hi_bf(d[j]);
+      sd += a * lo_bf(g[j]) * lo_bf(dv[k][j]) + b * hi_bf(g[j]) * hi_bf(dv[k][j]);
     }
   }
-  ss = wave_sum(ss);
-  sd = wave_sum(sd);
-  float r = 1.0f / sqrtf(ss / (float)H + eps);
-  float c2 = r * r * sd / (float)H;
-  for (int64_t c = lane * 8; c < H; c += 512) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    u32x4 g = *reinterpret_cast<const u32x4*>(w + c);
-    u32x4 d = *reinterpret_cast<const u32x4*>(dr + c);
-    u32x4 rs = dres ? *reinterpret_cast<const u32x4*>(dres + row * H + c) : u32x4{0, 0, 0, 0};
+  ss = row_sum(ss, red);
+  sd = row_sum(sd, red);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  const float c2 = r * r * sd / (float)H;
+#pragma unroll
+  for (int k = 0; k < RMS_CHUNKS; ++k) {
+    const int64_t c = (int64_t)(tid + RMS_THREADS * k) * 8;
+    if (c >= H) continue;
+    const u32x4 g = *reinterpret_cast<const u32x4*>(w + c);
+    const u32x4 rs = dres ? *reinterpret_cast<const u32x4*>(dres + row * H + c) : u32x4{0, 0, 0, 0};
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float e0 = lo_bf(rs[j]) + r * (lo_bf(g[j]) * lo_bf(d[j]) - lo_bf(v[j]) * c2);
-      float e1 = hi_bf(rs[j]) + r * (hi_bf(g[j]) * hi_bf(d[j]) - hi_bf(v[j]) * c2);
+      const float e0 = lo_bf(rs[j]) + r * (lo_bf(g[j]) * lo_bf(dv[k][j]) - lo_bf(xv[k][j]) * c2);
+      const float e1 = hi_bf(rs[j]) + r * (hi_bf(g[j]) * hi_bf(dv[k][j]) - hi_bf(xv[k][j]) * c2);
       o[j] = pack2(e0, e1);
     }
     *reinterpret_cast<u32x4*>(dx + row * H + c) = o;
   }
 }
 
+static lsl_status rms_check(int64_t H, const char* what, int64_t T = 0) {
+  if (H > (int64_t)RMS_THREADS * 8 * RMS_CHUNKS || H % 8)
+    return set_error(LSL_ERR_UNSUPPORTED, "%s: hidden %lld (a multiple of 8 up to %d)", what, (long long)H,
+                     RMS_THREADS * 8 * RMS_CHUNKS);
+  if (T >= ((int64_t)1 << 31)) return set_error(LSL_ERR_UNSUPPORTED, "%s: %lld rows (one workgroup each)", what, (long long)T);
+  return LSL_OK;
+}
+
 lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y,
                               hipStream_t s, unsigned* zero, int nzero) {
-  if (H > 512 * RMS_CHUNKS) return set_error(LSL_ERR_UNSUPPORTED, "rmsnorm: hidden %lld > %d", (long long)H, 512 * RMS_CHUNKS);
+  LSL_TRY(rms_check(H, "rmsnorm", T));
   if (T == 0) return LSL_OK;
-  hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, w, T, H, eps, y, zero,
+  RmsIn in{};
+  in.x = x;
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel<false>, dim3((unsigned)T), dim3(RMS_THREADS), 0, s, in, w, T, H, eps, y, zero,
                      zero ? nzero : 0);
   return check_launch("rmsnorm_fwd");
 }
 lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,
                               int64_t T, int64_t H, float eps, uint16_t* dx, hipStream_t s) {
+  LSL_TRY(rms_check(H, "rmsnorm backward", T));
   if (T == 0) return LSL_OK;
-  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, w, dy, dres, T, H, eps, dx);
+  RmsIn in{};
+  in.x = dy;
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel<false>, dim3((unsigned)T), dim3(RMS_THREADS), 0, s, x, w, in, dres, T, H, eps,
+                     dx);
   return check_launch("rmsnorm_bwd");
+}
+lsl_status rmsnorm_fwd_split_launch(const float* part, int S, const uint16_t* bias, const uint16_t* res, int64_t ldres,
+                                    uint16_t* h, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                                    hipStream_t s) {
+  LSL_TRY(rms_check(H, "rmsnorm (split sum)", T));
+  if (S < 1) return set_error(LSL_ERR_INVALID_ARG, "rmsnorm (split sum): %d splits", S);
+  if (T == 0) return LSL_OK;
+  RmsIn in{};
+  in.part = part; in.S = S; in.bias = bias; in.res = res; in.ldres = ldres; in.out = h;
+  hipLaunchKernelGGL(rmsnorm_fwd_kernel<true>, dim3((unsigned)T), dim3(RMS_THREADS), 0, s, in, w, T, H, eps, y,
+                     (unsigned*)nullptr, 0);
+  return check_launch("rmsnorm_fwd (split sum)");
+}
+lsl_status rmsnorm_bwd_split_launch(const uint16_t* x, const uint16_t* w, const float* part, int S,
+                                    const uint16_t* dres, int64_t T, int64_t H, float eps, uint16_t* dy_out,
+                                    uint16_t* dx, hipStream_t s) {
+  LSL_TRY(rms_check(H, "rmsnorm backward (split sum)", T));
+  if (S < 1) return set_error(LSL_ERR_INVALID_ARG, "rmsnorm backward (split sum): %d splits", S);
+  if (T == 0) return LSL_OK;
+  RmsIn in{};
+  in.part = part; in.S = S; in.out = dy_out;
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel<true>, dim3((unsigned)T), dim3(RMS_THREADS), 0, s, x, w, in, dres, T, H, eps,
+                     dx);
+  return check_launch("rmsnorm_bwd (split sum)");
 }
 
 // ---------------------------------------------------------------- RoPE

@@ -32,6 +32,10 @@ struct GemmDesc {
   // zero before the first launch and left zero by every launch
   float* split_ws = nullptr;
   unsigned* cnt = nullptr;
+  // bf16 epilogue with its reduction split into float32 partials (gemm_splits > 1):
+  // leave the partials in split_ws ([S][M][N]) and launch no reduce; the caller
+  // sums them (the RMSNorm kernels that take split partials)
+  bool defer_reduce = false;
 };
 lsl_status gemm_launch(const GemmDesc& d, hipStream_t s);
 // The conditions gemm_launch rejects, checked without launching anything.

@@ -1442,7 +1442,7 @@ static lsl_status launch_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s) {
     if (d.kn) launch_lora_variant<LSL_WFMT_BF16, true, BN, BM>(a, d.lora, s, grid);
     else launch_lora_variant<LSL_WFMT_BF16, false, BN, BM>(a, d.lora, s, grid);
   }
-  if (a.ksplit > 1) {
+  if (a.ksplit > 1 && !d.defer_reduce) {
     const int64_t n4 = d.M * d.N / 4;
     hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
                        a.ksplit, d.M, d.N, d.bias, d.res, d.ldres, d.y, d.ldy);
@@ -1579,7 +1579,7 @@ static lsl_status launch_big_cfg(const GemmDesc& d, GemmKArgs& a, hipStream_t s,
     if (d.kn) launch_big<LSL_WFMT_BF16, true>(a, d.lora, s, grid);
     else launch_big<LSL_WFMT_BF16, false>(a, d.lora, s, grid);
   }
-  if (a.ksplit > 1) {
+  if (a.ksplit > 1 && !d.defer_reduce) {
     const int64_t n4 = d.M * d.N / 4;
     hipLaunchKernelGGL(gemm_split_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, (const float*)a.spart,
                        a.ksplit, d.M, d.N, d.bias, d.res, d.ldres, d.y, d.ldy);

@@ -59,6 +59,17 @@ lsl_status rmsnorm_fwd_launch(const uint16_t* x, const uint16_t* w, int64_t T, i
                               hipStream_t s, unsigned* zero = nullptr, int nzero = 0);
 lsl_status rmsnorm_bwd_launch(const uint16_t* x, const uint16_t* w, const uint16_t* dy, const uint16_t* dres,
                               int64_t T, int64_t H, float eps, uint16_t* dx, hipStream_t s);
+// The same two RMSNorm steps reading their input as the float32 split-K partials
+// [S][T x H] of the GEMM before them (GemmDesc::defer_reduce): the input is summed
+// (+ bias, + res) exactly as gemm_split_reduce would store it, written to h /
+// dy_out, and normalised (forward) or back-propagated (backward) from those
+// bf16 values, so every output has the bits of the unfused pair of launches.
+lsl_status rmsnorm_fwd_split_launch(const float* part, int S, const uint16_t* bias, const uint16_t* res, int64_t ldres,
+                                    uint16_t* h, const uint16_t* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                                    hipStream_t s);
+lsl_status rmsnorm_bwd_split_launch(const uint16_t* x, const uint16_t* w, const float* part, int S,
+                                    const uint16_t* dres, int64_t T, int64_t H, float eps, uint16_t* dy_out,
+                                    uint16_t* dx, hipStream_t s);
 // y = RoPE(x) for n_heads heads of head_dim from column 0 of each row (row
 // stride ld for both; y may be x)
 lsl_status rope_launch(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,

@@ -146,6 +146,36 @@ def test_layer_kept_t_gives_the_same_bits(gpu, shape, batch, seq):
     assert off == tk.numel()
 
 
+def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu):
+    """At 1024 tokens the o projection and the gate|up and q|k|v input gradients
+    of the Llama-8B layer leave split partials that the RMSNorm after them sums:
+    the norms they write must be the standalone RMSNorm ops' bits on the bf16
+    tensors they write beside them (h1 -> n2; dn2 -> dh1; dn1 -> dx)."""
+    from layer_streamed_lora_amd import _abi
+    batch, seq = 1, 1024
+    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, LLAMA8B_LAYER, batch, seq, 48, ones_norm=False)
+    X, DY = dev_bf16(x), dev_bf16(dy)
+    T, H, eps = batch * seq, LLAMA8B_LAYER.hidden, LLAMA8B_LAYER.rms_eps
+    n1w, n2w = dev_bf16(w["norm1"]), dev_bf16(w["norm2"])
+    wsf = torch.empty(M.layer_workspace_bytes(cfg, batch, seq, _abi.MODE_FWD), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(M.layer_workspace_bytes(cfg, batch, seq, _abi.MODE_BWD), dtype=torch.uint8, device="cuda")
+
+    def region(ws, off):
+        return ws[off:off + T * H * 2].view(torch.bfloat16).view(T, H)
+    M.decoder_layer_fwd(cfg, blob, lp.lora_set(0), X, batch, seq, ws=wsf)
+    mf = M.layer_workspace_map(cfg, batch, seq, _abi.MODE_FWD)
+    h1, n2 = region(wsf, mf["h1"]).clone(), region(wsf, mf["n2"]).clone()
+    dx = M.decoder_layer_bwd(cfg, blob, lp.lora_set(0), X, DY, batch, seq, lp.lora_grads(0), ws=wsb)
+    mb = M.layer_workspace_map(cfg, batch, seq, _abi.MODE_BWD)
+    dn2, dh1, dn1 = (region(wsb, mb[k]).clone() for k in ("d_n2", "d_h1", "d_n1"))
+    torch.cuda.synchronize()
+    assert torch.equal(gpu.rmsnorm_fwd(h1, n2w, eps), n2)
+    assert torch.equal(gpu.rmsnorm_bwd(h1, n2w, dn2, eps, dres=DY), dh1)
+    assert torch.equal(gpu.rmsnorm_bwd(X, n1w, dn1, eps, dres=dh1), dx)
+    # the recomputed forward inside the backward wrote the same h1 and n2
+    assert torch.equal(region(wsb, mb["h1"]), h1) and torch.equal(region(wsb, mb["n2"]), n2)
+
+
 def test_layer_zero_b_gives_zero_dA(gpu):
     shape, batch, seq = SMALL_LAYER_BF16, 1, 64
     M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 44)
