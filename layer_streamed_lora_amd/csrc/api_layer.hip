@@ -370,10 +370,16 @@ static lsl_status layer_forward(const lsl_layer_cfg* c, const LayerPtrs& W, cons
   }
   // (also zeroes the arrival counts every later side product of the call uses)
   LSL_TRY(rmsnorm_fwd_launch(x, W.norm1, d.T, d.H, c->rms_eps, n1, s, cnt, (int)p.ncnt));
-  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, tp[LSL_M_QKV], tr, qkv, nullptr, part, cnt, s, false));
-  // q and k heads are adjacent in each row and share the frequencies: one launch
+  // q and k heads are adjacent in each row and share the frequencies: one
+  // launch; a split q|k|v projection's partials are summed by that launch
+  const int sqkv = gemm_splits(d.T, d.NQKV, d.H);
+  LSL_TRY(fused_linear_fwd(c, d, W, lo, LSL_M_QKV, n1, tp[LSL_M_QKV], tr, qkv, nullptr, part, cnt, s, false, sqkv > 1));
   uint16_t* qkr = (uint16_t*)(ws + p.qkr);
-  LSL_TRY(rope_launch(qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
+  if (sqkv > 1)
+    LSL_TRY(rope_split_launch(part, sqkv, W.qkv_bias, qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta,
+                              &c->rope_scaling, s));
+  else
+    LSL_TRY(rope_launch(qkv, qkr, d.T, d.NQKV, c->n_q + c->n_kv, d.d, seq, c->rope_theta, &c->rope_scaling, 0, s));
   LSL_TRY(lsl_attention_fwd(qkr, qkr + d.Q, qkv + d.Q + d.KV, d.NQKV, d.NQKV, batch, seq, c->n_q, c->n_kv, d.d, o,
                             d.Q, (float*)(ws + p.lse), o32, s));
   // a split o projection's partials are summed (with the residual) by the

@@ -294,6 +294,100 @@ __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* x, uint16_t* 
   }
 }
 
+// Four columns of a row of a split GEMM's output: the float32 partials of the S
+// splits ([S][T][ld] at part) added in split order and the bias added, as
+// gemm_split_reduce does before its rounding.
+LSL_DEV void split_sum4(const float* __restrict__ part, int S, int64_t Tld, int64_t off,
+                        const uint16_t* __restrict__ bias, int64_t col, float (&e)[4]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(part + off);
+  for (int sp = 1; sp < S; ++sp) {
+    const f32x4 p = *reinterpret_cast<const f32x4*>(part + sp * Tld + off);
+    a = f32x4{a[0] + p[0], a[1] + p[1], a[2] + p[2], a[3] + p[3]};
+  }
+  e[0] = a[0]; e[1] = a[1]; e[2] = a[2]; e[3] = a[3];
+  if (bias) {
+    const u32x2 b = *reinterpret_cast<const u32x2*>(bias + col);
+    e[0] += lo_bf(b[0]); e[1] += hi_bf(b[0]); e[2] += lo_bf(b[1]); e[3] += hi_bf(b[1]);
+  }
+}
+
+// The q|k|v projection's split-K sum fused with RoPE: every column of the
+// [T x ld] output is summed (+ bias) and rounded as gemm_split_reduce would
+// store it into qkv; the first n_heads heads of each row (q and k) are then
+// rotated from those bf16 values exactly as rope_kernel rotates them, into y.
+__global__ __launch_bounds__(256) void rope_split_kernel(const float* __restrict__ part, int S,
+                                                         const uint16_t* __restrict__ bias, uint16_t* __restrict__ qkv,
+                                                         uint16_t* __restrict__ y, int64_t T, int64_t ld, int n_heads,
+                                                         int head_dim, int seq, RopeFreq fr) {
+  __shared__ float cs[ROPE_ROWS][64], sn[ROPE_ROWS][64];
+  const int half = head_dim >> 1;
+  const int64_t r0 = (int64_t)blockIdx.x * ROPE_ROWS;
+  for (int t = threadIdx.x; t < ROPE_ROWS * half; t += blockDim.x) {
+    const int rr = t / half, i = t - rr * half;
+    const int64_t row = r0 + rr;
+    if (row >= T) continue;
+    const double ang = (double)(row % seq) * fr.inv[i];
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    cs[rr][i] = (float)cd;
+    sn[rr][i] = (float)sd;
+  }
+  __syncthreads();
+  const int64_t Tld = T * ld;
+  const int q4 = half >> 2;
+  const int per_row = n_heads * q4;
+  for (int t = threadIdx.x; t < ROPE_ROWS * per_row; t += blockDim.x) {
+    const int rr = t / per_row, rem = t - rr * per_row;
+    const int h = rem / q4, g = rem - h * q4;
+    const int64_t row = r0 + rr;
+    if (row >= T) continue;
+    const int64_t col = (int64_t)h * head_dim + 4 * g, off = row * ld + col;
+    float e1[4], e2[4];
+    split_sum4(part, S, Tld, off, bias, col, e1);
+    split_sum4(part, S, Tld, off + half, bias, col + half, e2);
+    const u32x2 a = u32x2{pack2(e1[0], e1[1]), pack2(e1[2], e1[3])};
+    const u32x2 b = u32x2{pack2(e2[0], e2[1]), pack2(e2[2], e2[3])};
+    *reinterpret_cast<u32x2*>(qkv + off) = a;
+    *reinterpret_cast<u32x2*>(qkv + off + half) = b;
+    float x1[4] = {lo_bf(a[0]), hi_bf(a[0]), lo_bf(a[1]), hi_bf(a[1])};
+    float x2[4] = {lo_bf(b[0]), hi_bf(b[0]), lo_bf(b[1]), hi_bf(b[1])};
+    float o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = cs[rr][4 * g + e], s = sn[rr][4 * g + e];
+      o1[e] = x1[e] * c - x2[e] * s;
+      o2[e] = x2[e] * c + x1[e] * s;
+    }
+    *reinterpret_cast<u32x2*>(y + off) = u32x2{pack2(o1[0], o1[1]), pack2(o1[2], o1[3])};
+    *reinterpret_cast<u32x2*>(y + off + half) = u32x2{pack2(o2[0], o2[1]), pack2(o2[2], o2[3])};
+  }
+  // the remaining columns (v): the sum alone
+  const int64_t c0 = (int64_t)n_heads * head_dim;
+  const int v4 = (int)((ld - c0) >> 2);
+  for (int t = threadIdx.x; t < ROPE_ROWS * v4; t += blockDim.x) {
+    const int rr = t / v4, g = t - rr * v4;
+    const int64_t row = r0 + rr;
+    if (row >= T) continue;
+    const int64_t col = c0 + 4 * (int64_t)g, off = row * ld + col;
+    float e[4];
+    split_sum4(part, S, Tld, off, bias, col, e);
+    *reinterpret_cast<u32x2*>(qkv + off) = u32x2{pack2(e[0], e[1]), pack2(e[2], e[3])};
+  }
+}
+
+lsl_status rope_split_launch(const float* part, int S, const uint16_t* bias, uint16_t* qkv, uint16_t* y, int64_t T,
+                             int64_t ld, int n_heads, int head_dim, int seq, float theta,
+                             const lsl_rope_scaling* scaling, hipStream_t s) {
+  if (head_dim % 8 || head_dim > 128 || ld % 4 || ld < (int64_t)n_heads * head_dim || S < 1)
+    return set_error(LSL_ERR_UNSUPPORTED, "rope (split sum): head_dim %d, ld %lld, %d splits", head_dim, (long long)ld,
+                     S);
+  if (T == 0) return LSL_OK;
+  const RopeFreq fr = rope_freq(head_dim, (double)theta, scaling);
+  hipLaunchKernelGGL(rope_split_kernel, dim3((unsigned)((T + ROPE_ROWS - 1) / ROPE_ROWS)), dim3(256), 0, s, part, S,
+                     bias, qkv, y, T, ld, n_heads, head_dim, seq, fr);
+  return check_launch("rope (split sum)");
+}
+
 lsl_status rope_launch(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,
                        float theta, const lsl_rope_scaling* scaling, int inverse, hipStream_t s) {
   if (head_dim % 8 || head_dim > 128)

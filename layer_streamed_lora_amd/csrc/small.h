@@ -74,6 +74,13 @@ lsl_status rmsnorm_bwd_split_launch(const uint16_t* x, const uint16_t* w, const 
 // stride ld for both; y may be x)
 lsl_status rope_launch(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads, int head_dim, int seq,
                        float theta, const lsl_rope_scaling* scaling, int inverse, hipStream_t s);
+// RoPE of the q|k|v projection read as its float32 split-K partials [S][T x ld]
+// (GemmDesc::defer_reduce): every column summed (+ bias) and rounded into qkv as
+// gemm_split_reduce would, the first n_heads heads rotated from those values
+// into y as rope_launch (forward) would.
+lsl_status rope_split_launch(const float* part, int S, const uint16_t* bias, uint16_t* qkv, uint16_t* y, int64_t T,
+                             int64_t ld, int n_heads, int head_dim, int seq, float theta,
+                             const lsl_rope_scaling* scaling, hipStream_t s);
 lsl_status swiglu_fwd_launch(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, hipStream_t s);
 lsl_status swiglu_bwd_launch(const uint16_t* gu, const uint16_t* da, int64_t T, int64_t I, uint16_t* dgu, hipStream_t s);
 }  // namespace lsl

@@ -147,10 +147,11 @@ def test_layer_kept_t_gives_the_same_bits(gpu, shape, batch, seq):
 
 
 def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu):
-    """At 1024 tokens the o projection and the gate|up and q|k|v input gradients
-    of the Llama-8B layer leave split partials that the RMSNorm after them sums:
-    the norms they write must be the standalone RMSNorm ops' bits on the bf16
-    tensors they write beside them (h1 -> n2; dn2 -> dh1; dn1 -> dx)."""
+    """At 1024 tokens the q|k|v and o projections and the gate|up and q|k|v input
+    gradients of the Llama-8B layer leave split partials that the RoPE or
+    RMSNorm after them sums: what those write must be the standalone RoPE and
+    RMSNorm ops' bits on the bf16 tensors they write beside them (qkv -> the
+    rotated q and k; h1 -> n2; dn2 -> dh1; dn1 -> dx)."""
     from layer_streamed_lora_amd import _abi
     batch, seq = 1, 1024
     M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, LLAMA8B_LAYER, batch, seq, 48, ones_norm=False)
@@ -165,10 +166,17 @@ def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu):
     M.decoder_layer_fwd(cfg, blob, lp.lora_set(0), X, batch, seq, ws=wsf)
     mf = M.layer_workspace_map(cfg, batch, seq, _abi.MODE_FWD)
     h1, n2 = region(wsf, mf["h1"]).clone(), region(wsf, mf["n2"]).clone()
+    sh = LLAMA8B_LAYER
+    nqkv = (sh.n_q + 2 * sh.n_kv) * sh.head_dim
+    qkv = wsf[mf["qkv"]:mf["qkv"] + T * nqkv * 2].view(torch.bfloat16).view(T, nqkv).clone()
+    qkr = wsf[mf["qk_rope"]:mf["qk_rope"] + T * nqkv * 2].view(torch.bfloat16).view(T, nqkv).clone()
+    nrot = (sh.n_q + sh.n_kv) * sh.head_dim
+    rot = gpu.rope(qkv.clone(), sh.n_q + sh.n_kv, sh.head_dim, seq, sh.rope_theta, scaling=sh.rope_scaling)
     dx = M.decoder_layer_bwd(cfg, blob, lp.lora_set(0), X, DY, batch, seq, lp.lora_grads(0), ws=wsb)
     mb = M.layer_workspace_map(cfg, batch, seq, _abi.MODE_BWD)
     dn2, dh1, dn1 = (region(wsb, mb[k]).clone() for k in ("d_n2", "d_h1", "d_n1"))
     torch.cuda.synchronize()
+    assert torch.equal(rot[:, :nrot], qkr[:, :nrot])
     assert torch.equal(gpu.rmsnorm_fwd(h1, n2w, eps), n2)
     assert torch.equal(gpu.rmsnorm_bwd(h1, n2w, dn2, eps, dres=DY), dh1)
     assert torch.equal(gpu.rmsnorm_bwd(X, n1w, dn1, eps, dres=dh1), dx)
