@@ -435,6 +435,7 @@ def hbm_kernels(shape, ms):
         ("lsl::swiglu_fwd_kernel", 3 * T * I * 2, "gate|up read, a written"),
         ("lsl::swiglu_bwd_kernel", 5 * T * I * 2, "gate|up and da read, dgate|dup written"),
         ("lsl::rope_kernel", (nq + nkv) * T * d * 2 * 2, "q and k heads read, rotated copy written (one launch)"),
+        ("lsl::rope_split_kernel", None, "split partials read, q|k|v and the rotated q and k written"),
         ("lsl::adamw_kernel", n_params * (4 * 4 + 3 * 4 + 2), "master, grad, m, v read; master, m, v, bf16 copy written"),
     ]
 
