@@ -570,9 +570,4 @@ lsl_status lora_bt_group_launch(const LoraBt* jobs, int n, hipStream_t s) {
   return check_launch("lora_bt_group");
 }
 
-lsl_status lora_tn2_launch(const LoraTn& d0, const LoraTn& d1, hipStream_t s) {
-  const LoraTn d[2] = {d0, d1};
-  return lora_tn_group_launch(d, 2, s);
-}
-
 }  // namespace lsl

@@ -43,10 +43,8 @@ size_t lora_counts_needed(int64_t T, int64_t W);
 lsl_status lora_counts_zero(unsigned* cnt, size_t n, hipStream_t s);
 lsl_status lora_nt_launch(const LoraNt& d, hipStream_t s);
 lsl_status lora_tn_launch(const LoraTn& d, hipStream_t s);
-// two TN products in one launch; each needs its own ws (lora_tn_ws_bytes) and
-// its own lora_tn_tiles(W) arrival counts
-lsl_status lora_tn2_launch(const LoraTn& d0, const LoraTn& d1, hipStream_t s);
-// up to eight TN products in one launch, each with its own ws and arrival counts
+// up to eight TN products in one launch; each needs its own ws (lora_tn_ws_bytes)
+// and its own lora_tn_tiles(W) arrival counts
 lsl_status lora_tn_group_launch(const LoraTn* d, int n, hipStream_t s);
 size_t lora_tn_tiles(int64_t W);
 // the conditions the launches reject, checked without launching anything
