@@ -146,7 +146,11 @@ def test_layer_kept_t_gives_the_same_bits(gpu, shape, batch, seq):
     assert off == tk.numel()
 
 
-def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu):
+@pytest.mark.parametrize("shape", [
+    LLAMA8B_LAYER,
+    dataclasses.replace(LLAMA8B_LAYER, qkv_bias=True, rope_scaling=LLAMA31_ROPE_SCALING),
+])
+def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu, shape):
     """At 1024 tokens the q|k|v and o projections and the gate|up and q|k|v input
     gradients of the Llama-8B layer leave split partials that the RoPE or
     RMSNorm after them sums: what those write must be the standalone RoPE and
@@ -154,9 +158,9 @@ def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu):
     rotated q and k; h1 -> n2; dn2 -> dh1; dn1 -> dx)."""
     from layer_streamed_lora_amd import _abi
     batch, seq = 1, 1024
-    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, LLAMA8B_LAYER, batch, seq, 48, ones_norm=False)
+    M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 48, ones_norm=False)
     X, DY = dev_bf16(x), dev_bf16(dy)
-    T, H, eps = batch * seq, LLAMA8B_LAYER.hidden, LLAMA8B_LAYER.rms_eps
+    T, H, eps = batch * seq, shape.hidden, shape.rms_eps
     n1w, n2w = dev_bf16(w["norm1"]), dev_bf16(w["norm2"])
     wsf = torch.empty(M.layer_workspace_bytes(cfg, batch, seq, _abi.MODE_FWD), dtype=torch.uint8, device="cuda")
     wsb = torch.empty(M.layer_workspace_bytes(cfg, batch, seq, _abi.MODE_BWD), dtype=torch.uint8, device="cuda")
@@ -166,7 +170,7 @@ def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu):
     M.decoder_layer_fwd(cfg, blob, lp.lora_set(0), X, batch, seq, ws=wsf)
     mf = M.layer_workspace_map(cfg, batch, seq, _abi.MODE_FWD)
     h1, n2 = region(wsf, mf["h1"]).clone(), region(wsf, mf["n2"]).clone()
-    sh = LLAMA8B_LAYER
+    sh = shape
     nqkv = (sh.n_q + 2 * sh.n_kv) * sh.head_dim
     qkv = wsf[mf["qkv"]:mf["qkv"] + T * nqkv * 2].view(torch.bfloat16).view(T, nqkv).clone()
     qkr = wsf[mf["qk_rope"]:mf["qk_rope"] + T * nqkv * 2].view(torch.bfloat16).view(T, nqkv).clone()

@@ -25,7 +25,7 @@ import torch
 
 import oracle as O
 import synth
-from synth.configs import SMALL_LAYER_NF4, SMALL_LAYER_BF16, SMALL_LAYER_NF4DQ, LLAMA8B_LAYER
+from synth.configs import SMALL_LAYER_NF4, SMALL_LAYER_BF16, SMALL_LAYER_NF4DQ, LLAMA8B_LAYER, LLAMA31_ROPE_SCALING
 from tests.gpu_util import dev_bf16, host, assert_close_scaled, oracle_layer_weights
 
 pytestmark = pytest.mark.gpu
@@ -196,8 +196,14 @@ def test_layer_steps_small(gpu, shape, batch, seq):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("seq", [512, 1024])
-def test_layer_steps_llama8b(gpu, seq):
+@pytest.mark.parametrize("shape,seq", [
+    (LLAMA8B_LAYER, 512),
+    (LLAMA8B_LAYER, 1024),
+    # the split q|k|v sum inside the RoPE launch, with a q|k|v bias and
+    # Llama-3.1's RoPE frequency scaling
+    (dataclasses.replace(LLAMA8B_LAYER, qkv_bias=True, rope_scaling=LLAMA31_ROPE_SCALING), 1024),
+])
+def test_layer_steps_llama8b(gpu, shape, seq):
     """The Llama-3.1-8B NF4 layer at batch 1 x seq 512 and x 1024 (the
     benchmark's dispatch), every rounding point."""
-    _check_steps(LLAMA8B_LAYER, 1, seq, 82)
+    _check_steps(shape, 1, seq, 82)
