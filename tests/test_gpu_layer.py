@@ -146,18 +146,19 @@ def test_layer_kept_t_gives_the_same_bits(gpu, shape, batch, seq):
     assert off == tk.numel()
 
 
-@pytest.mark.parametrize("shape", [
-    LLAMA8B_LAYER,
-    dataclasses.replace(LLAMA8B_LAYER, qkv_bias=True, rope_scaling=LLAMA31_ROPE_SCALING),
+@pytest.mark.parametrize("shape,seq", [
+    (LLAMA8B_LAYER, 1024),
+    (dataclasses.replace(LLAMA8B_LAYER, qkv_bias=True, rope_scaling=LLAMA31_ROPE_SCALING), 1024),
+    (LLAMA8B_LAYER, 1100),  # a ragged last token tile
 ])
-def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu, shape):
+def test_layer_split_sums_fused_into_norms_give_the_standalone_bits(gpu, shape, seq):
     """At 1024 tokens the q|k|v and o projections and the gate|up and q|k|v input
     gradients of the Llama-8B layer leave split partials that the RoPE or
     RMSNorm after them sums: what those write must be the standalone RoPE and
     RMSNorm ops' bits on the bf16 tensors they write beside them (qkv -> the
     rotated q and k; h1 -> n2; dn2 -> dh1; dn1 -> dx)."""
     from layer_streamed_lora_amd import _abi
-    batch, seq = 1, 1024
+    batch = 1
     M, cfg, blob, lp, w, lora, x, dy = _setup(gpu, shape, batch, seq, 48, ones_norm=False)
     X, DY = dev_bf16(x), dev_bf16(dy)
     T, H, eps = batch * seq, shape.hidden, shape.rms_eps

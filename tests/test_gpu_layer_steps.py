@@ -202,6 +202,9 @@ def test_layer_steps_small(gpu, shape, batch, seq):
     # the split q|k|v sum inside the RoPE launch, with a q|k|v bias and
     # Llama-3.1's RoPE frequency scaling
     (dataclasses.replace(LLAMA8B_LAYER, qkv_bias=True, rope_scaling=LLAMA31_ROPE_SCALING), 1024),
+    # a ragged last token tile (1100 = 4 x 256 + 76) in the split large tiles and
+    # the RoPE / RMSNorm launches that sum their partials
+    (LLAMA8B_LAYER, 1100),
 ])
 def test_layer_steps_llama8b(gpu, shape, seq):
     """The Llama-3.1-8B NF4 layer at batch 1 x seq 512 and x 1024 (the
