@@ -402,28 +402,31 @@ lsl_status rope_launch(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, in
 // ---------------------------------------------------------------- SwiGLU
 LSL_DEV float sigm(float g) { return 1.0f / (1.0f + expf(-g)); }
 
-__global__ void swiglu_fwd_kernel(const uint16_t* __restrict__ gu, int64_t T, int64_t I, uint16_t* __restrict__ a) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // one per 8 outputs
-  int64_t per = I / 8;
-  if (idx >= T * per) return;
-  int64_t t = idx / per, c = (idx - t * per) * 8;
-  u32x4 g = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + c);
-  u32x4 u = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + I + c);
-  u32x4 o;
+// Grid (ceil(I / 2048), rows): a thread takes 8 columns of one row (no index
+// division); rows past the grid's height are taken in steps of it.
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t* __restrict__ gu, int64_t T, int64_t I,
+                                                         uint16_t* __restrict__ a) {
+  const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (c >= I) return;
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    u32x4 g = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + c);
+    u32x4 u = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + I + c);
+    u32x4 o;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float g0 = lo_bf(g[j]), g1 = hi_bf(g[j]);
-    o[j] = pack2(g0 * sigm(g0) * lo_bf(u[j]), g1 * sigm(g1) * hi_bf(u[j]));
+    for (int j = 0; j < 4; ++j) {
+      float g0 = lo_bf(g[j]), g1 = hi_bf(g[j]);
+      o[j] = pack2(g0 * sigm(g0) * lo_bf(u[j]), g1 * sigm(g1) * hi_bf(u[j]));
+    }
+    *reinterpret_cast<u32x4*>(a + t * I + c) = o;
   }
-  *reinterpret_cast<u32x4*>(a + t * I + c) = o;
 }
 
-__global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ gu, const uint16_t* __restrict__ da, int64_t T, int64_t I,
-                                  uint16_t* __restrict__ dgu) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t per = I / 8;
-  if (idx >= T * per) return;
-  int64_t t = idx / per, c = (idx - t * per) * 8;
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restrict__ gu,
+                                                         const uint16_t* __restrict__ da, int64_t T, int64_t I,
+                                                         uint16_t* __restrict__ dgu) {
+  const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (c >= I) return;
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
   u32x4 g = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + c);
   u32x4 u = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + I + c);
   u32x4 d = *reinterpret_cast<const u32x4*>(da + t * I + c);
@@ -443,18 +446,20 @@ __global__ void swiglu_bwd_kernel(const uint16_t* __restrict__ gu, const uint16_
   }
   *reinterpret_cast<u32x4*>(dgu + t * 2 * I + c) = og;
   *reinterpret_cast<u32x4*>(dgu + t * 2 * I + I + c) = ou;
+  }
 }
 
+static dim3 swiglu_grid(int64_t T, int64_t I) {
+  return dim3((unsigned)((I / 8 + 255) / 256), (unsigned)(T < 65535 ? T : 65535));
+}
 lsl_status swiglu_fwd_launch(const uint16_t* gu, int64_t T, int64_t I, uint16_t* a, hipStream_t s) {
   if (T == 0) return LSL_OK;
-  int64_t n = T * (I / 8);
-  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, T, I, a);
+  hipLaunchKernelGGL(swiglu_fwd_kernel, swiglu_grid(T, I), dim3(256), 0, s, gu, T, I, a);
   return check_launch("swiglu_fwd");
 }
 lsl_status swiglu_bwd_launch(const uint16_t* gu, const uint16_t* da, int64_t T, int64_t I, uint16_t* dgu, hipStream_t s) {
   if (T == 0) return LSL_OK;
-  int64_t n = T * (I / 8);
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, gu, da, T, I, dgu);
+  hipLaunchKernelGGL(swiglu_bwd_kernel, swiglu_grid(T, I), dim3(256), 0, s, gu, da, T, I, dgu);
   return check_launch("swiglu_bwd");
 }
 
