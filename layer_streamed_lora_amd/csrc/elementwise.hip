@@ -427,25 +427,25 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restr
   const int64_t c = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (c >= I) return;
   for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
-  u32x4 g = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + c);
-  u32x4 u = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + I + c);
-  u32x4 d = *reinterpret_cast<const u32x4*>(da + t * I + c);
-  u32x4 og, ou;
+    u32x4 g = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + c);
+    u32x4 u = *reinterpret_cast<const u32x4*>(gu + t * 2 * I + I + c);
+    u32x4 d = *reinterpret_cast<const u32x4*>(da + t * I + c);
+    u32x4 og, ou;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float gg[2] = {lo_bf(g[j]), hi_bf(g[j])}, uu[2] = {lo_bf(u[j]), hi_bf(u[j])}, dd[2] = {lo_bf(d[j]), hi_bf(d[j])};
-    float rg[2], ru[2];
+    for (int j = 0; j < 4; ++j) {
+      float gg[2] = {lo_bf(g[j]), hi_bf(g[j])}, uu[2] = {lo_bf(u[j]), hi_bf(u[j])}, dd[2] = {lo_bf(d[j]), hi_bf(d[j])};
+      float rg[2], ru[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float sg = sigm(gg[e]);
-      rg[e] = dd[e] * uu[e] * sg * (1.0f + gg[e] * (1.0f - sg));
-      ru[e] = dd[e] * gg[e] * sg;
+      for (int e = 0; e < 2; ++e) {
+        float sg = sigm(gg[e]);
+        rg[e] = dd[e] * uu[e] * sg * (1.0f + gg[e] * (1.0f - sg));
+        ru[e] = dd[e] * gg[e] * sg;
+      }
+      og[j] = pack2(rg[0], rg[1]);
+      ou[j] = pack2(ru[0], ru[1]);
     }
-    og[j] = pack2(rg[0], rg[1]);
-    ou[j] = pack2(ru[0], ru[1]);
-  }
-  *reinterpret_cast<u32x4*>(dgu + t * 2 * I + c) = og;
-  *reinterpret_cast<u32x4*>(dgu + t * 2 * I + I + c) = ou;
+    *reinterpret_cast<u32x4*>(dgu + t * 2 * I + c) = og;
+    *reinterpret_cast<u32x4*>(dgu + t * 2 * I + I + c) = ou;
   }
 }
 

@@ -73,7 +73,7 @@ def test_rope_strided_heads_leave_other_columns(gpu):
     assert np.array_equal(host(X)[:, nh * d:], x[:, nh * d:])
 
 
-@pytest.mark.parametrize("T,I", [(33, 4864), (4, 64)])
+@pytest.mark.parametrize("T,I", [(33, 4864), (4, 64), (70001, 8)])
 def test_swiglu(gpu, T, I):
     gu = synth.activation((T, 2 * I), 10, "x", std=2.0)
     da = synth.activation((T, I), 10, "dy")
