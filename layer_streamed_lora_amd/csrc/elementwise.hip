@@ -252,7 +252,13 @@ static RopeFreq rope_freq(int head_dim, double theta, const lsl_rope_scaling* sc
   return fr;
 }
 
-constexpr int ROPE_ROWS = 4;
+// rows per workgroup: one row gives four times the workgroups of four rows and
+// a quarter of the dependent load/store rounds per thread, which the launch's
+// latency, not its bandwidth, pays for
+#ifndef LSL_ROPE_ROWS
+#define LSL_ROPE_ROWS 1
+#endif
+constexpr int ROPE_ROWS = LSL_ROPE_ROWS;
 
 __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* x, uint16_t* y, int64_t T, int64_t ld, int n_heads,
                                                    int head_dim, int seq, RopeFreq fr, int inverse) {
